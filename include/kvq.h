@@ -1,0 +1,282 @@
+/*
+ * kvq.h — C ABI of libkvq: KIVI-style asymmetric low-bit KV-cache quantization
+ * fused into single-token decode attention, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [KIVI]  "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
+ *           (repository digest of jy-yuan/KIVI): sections "核心能力" (core
+ *           capabilities), "Overview", "Example".
+ *   [KV1]   "KV1-1.2B-Instruct" model card (klein-ml/KV1-1.2B): sections
+ *           "Quantization Format: KV1.cpp BQ2_0", "Memory", "Quickstart".
+ *   [REC]   "KIVI asymmetric 2-bit KV (2-bit keys / 4-bit values) on
+ *           Llama-2-class GQA models" (inference-research record): "Methodology",
+ *           "notes".
+ *   [KVQ]   "KV Cache Quantization" (mohsenhariri/spectral-kv): "Quantize What
+ *           Counts", "Usage".
+ *
+ * ---------------------------------------------------------------------------
+ * THE METHOD
+ * ---------------------------------------------------------------------------
+ * Keys are quantized per channel: for every channel, a group of G consecutive
+ * tokens shares one (scale, min) pair.  Values are quantized per token: every
+ * token's head vector is cut into D/G groups of G consecutive channels, each
+ * with its own (scale, min).  Codes have b = 2 or 4 bits, chosen separately for
+ * keys and values.  The most recent tokens stay in an fp16 residual window of R
+ * tokens until the window is full; then it is quantized into packed groups.
+ * ([KIVI] core capabilities, Overview, Example: k_bits, v_bits, group_size,
+ * residual_length; [REC] notes: per-channel keys group outlier channels.)
+ *
+ * Group quantizer (affine, asymmetric; [KV1] Quantization Format gives the
+ * formula for b = 2 and states that the fp16-rounded scale and min are used for
+ * the codes; the general b form replaces 3 by 2^b - 1):
+ *   mn = min x_i, mx = max x_i            (x_i: the fp16 inputs widened to fp32;
+ *                                         a zero min or max is taken as +0)
+ *   d32 = (mx - mn) / (2^b - 1)           (IEEE fp32 subtract, then IEEE fp32
+ *                                          divide, round to nearest even)
+ *   scale = fp16(d32), min = fp16(mn)     (round to nearest even; min is exact;
+ *                                          a zero scale is stored as +0)
+ *   code_i = 0 if scale == 0, else clamp(rne(fp32(fp32(x_i - min) / scale)),
+ *                                        0, 2^b - 1)
+ *   dequantized x_i = code_i * scale + min          ([KV1] Dequantize)
+ *
+ * Flush timing (lazy): a token that arrives when the sequence already holds
+ * n_before > 0 tokens with n_before % R == 0 first triggers the quantization of
+ * positions [n_before - R, n_before) from the residual window into packed rows;
+ * then the new token goes to residual slot n_before % R.  So at attention time
+ * a sequence of n >= 1 tokens has
+ *   r(n)   = ((n - 1) % R) + 1   residual (fp16) tokens: positions [Lq, n)
+ *   Lq(n)  = n - r(n)            packed tokens: positions [0, Lq), Lq % R == 0
+ * and the current token is always in the residual window.
+ *
+ * Decode attention for query head h of sequence b (GQA: the KV head is
+ * h / (Hq / Hkv), i.e. consecutive query heads share one KV head):
+ *   s_t = sm_scale * q_h . k_t   for the n tokens t < n (dequantized keys for
+ *                                t < Lq, fp16 residual keys for t >= Lq)
+ *   out_h = sum_t softmax(s)_t * v_t     (fp32 accumulation, fp16 result)
+ * The result equals softmax attention over the dequantized cache ([KV1]
+ * Quickstart: quantizing each token once as it enters the cache and attending
+ * over the dequantized values gives the exact low-bit outputs).
+ *
+ * ---------------------------------------------------------------------------
+ * PACKED LAYOUT  (KVQ_LAYOUT_VERSION 1)
+ * ---------------------------------------------------------------------------
+ * Shapes use: B = batch, Hkv = KV heads, D = head_dim, G = group, R = residual,
+ * C = capacity (tokens per sequence), bK / bV = key / value bits.
+ * All arrays are dense, C-order, little-endian, caller-owned device memory.
+ *
+ *   k_codes  uint32 [B][Hkv][C][D*bK/32]          token-major rows.
+ *            Channel c of a token sits in bits ((c*bK) % 32) .. +bK-1 of word
+ *            (c*bK)/32 of the token's row, lowest channel in the lowest bits
+ *            (the code order of the 2-bit BQ2_0 block in [KV1] Quantization
+ *            Format, where the first of four codes takes the two lowest bits
+ *            of a byte; extended here to 4-bit fields).
+ *   k_meta   uint16 [B][Hkv][C/G][D][2]           fp16 (scale, min) of key group
+ *            j = tokens [jG, jG+G) and channel c; scale first, as the scale field precedes
+ *            the min field in the [KV1] BQ2_0 block.
+ *   v_codes  uint32 [B][Hkv][C/32][D][bV]         32-token blocks, channel-major
+ *            inside a block: word w of channel c in block k holds tokens
+ *            32k + tau with (tau*bV)/32 == w, token tau in bits
+ *            ((tau*bV) % 32) .. +bV-1 (lowest token in the lowest bits).
+ *   v_meta   uint16 [B][Hkv][C][D/G][2]           fp16 (scale, min) of token t,
+ *            channel group gamma = channels [gamma*G, gamma*G+G).
+ *   k_res,   uint16 [B][Hkv][R][D]                fp16 residual window; position
+ *   v_res                                         p lives in slot p % R.
+ *
+ * Constraints (checked, KVQ_ERR_GEOM / KVQ_ERR_BITS otherwise):
+ *   batch >= 1; n_kv_heads >= 1; n_q_heads % n_kv_heads == 0 and
+ *   n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; head_dim in {64, 128};
+ *   k_bits, v_bits in {2, 4}; group in {32, 64, 128}, group <= head_dim,
+ *   head_dim % group == 0; residual % group == 0; capacity % residual == 0;
+ *   capacity <= 2^24.
+ *
+ * ---------------------------------------------------------------------------
+ * CONVENTIONS
+ * ---------------------------------------------------------------------------
+ * Ownership: the caller allocates and frees every buffer.  libkvq never
+ *   allocates device memory, never frees, and keeps no pointer after a call
+ *   returns.  Its only state is a thread-local error string and a per-device
+ *   cache of the compute-unit count.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Every call only enqueues work on that stream and returns; nothing
+ *   synchronizes.  Faults inside kernels surface at the caller's next sync.
+ * Errors: every call returns an int status (KVQ_OK = 0, negative on error).
+ *   All checks are done on the host before anything is enqueued, so a failing
+ *   call has no effect.  kvq_last_error() gives the text of the last failure on
+ *   the calling thread.  Device data (seq_lens values) cannot be checked on the
+ *   host: out-of-range lengths are clamped inside the kernels so that no access
+ *   leaves the buffers, and the affected outputs are documented per call.
+ * Alignment: every device pointer must be 16-byte aligned (KVQ_ERR_ALIGN).
+ * Thread safety: calls may be made from several host threads; calls whose
+ *   device work overlaps on the same buffers race, as any kernels would.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_LAYOUT_VERSION 1
+#define KVQ_VBLOCK 32 /* tokens per v_codes block */
+
+enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = -1,      /* a required pointer is NULL */
+  KVQ_ERR_GEOM = -2,      /* geometry violates the constraints above */
+  KVQ_ERR_BITS = -3,      /* k_bits / v_bits not in {2, 4} */
+  KVQ_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned */
+  KVQ_ERR_WORKSPACE = -5, /* workspace missing or too small */
+  KVQ_ERR_RANGE = -6,     /* a token range / length argument is out of range */
+  KVQ_ERR_HIP = -7,       /* a HIP runtime call failed (text in kvq_last_error) */
+  KVQ_ERR_INTERNAL = -8   /* unexpected internal failure */
+};
+
+/* Geometry of one attention layer's cache. */
+typedef struct kvq_geom {
+  int32_t batch;      /* B: sequences */
+  int32_t n_q_heads;  /* Hq: query heads */
+  int32_t n_kv_heads; /* Hkv: KV heads; Hq / Hkv query heads share one */
+  int32_t head_dim;   /* D: 64 or 128 */
+  int32_t k_bits;     /* bK: 2 or 4 */
+  int32_t v_bits;     /* bV: 2 or 4 */
+  int32_t group;      /* G: tokens per key group = channels per value group */
+  int32_t residual;   /* R: fp16 residual window length, multiple of G */
+  int32_t capacity;   /* C: max tokens per sequence, multiple of R */
+} kvq_geom;
+
+/* The six device buffers of one layer's cache (layout above). */
+typedef struct kvq_cache {
+  uint32_t *k_codes;
+  uint32_t *v_codes;
+  uint16_t *k_meta;
+  uint16_t *v_meta;
+  uint16_t *k_res;
+  uint16_t *v_res;
+} kvq_cache;
+
+/* ----- version, errors, sizes (host only, no device work) ----------------- */
+
+int kvq_abi_version(void);    /* returns KVQ_ABI_VERSION */
+int kvq_layout_version(void); /* returns KVQ_LAYOUT_VERSION */
+
+/* Static text for a status code (never NULL). */
+const char *kvq_status_str(int status);
+
+/* Text describing the last failing call on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+/* Checks a geometry against the constraints above. */
+int kvq_validate_geom(const kvq_geom *geom);
+
+/* Byte sizes of the six cache buffers, in the order k_codes, v_codes, k_meta,
+ * v_meta, k_res, v_res.  out must hold 6 entries. */
+int kvq_cache_bytes(const kvq_geom *geom, size_t out[6]);
+
+/* Split-context sizing used by kvq_decode_attn for a launch whose longest
+ * sequence has max_seq_len tokens (1 <= max_seq_len <= capacity): the number of
+ * splits per (sequence, KV head) and the tokens per split (a multiple of G).
+ * Depends on the geometry, max_seq_len and the compute-unit count of the
+ * current device (queried once per device). */
+int kvq_decode_splits(const kvq_geom *geom, int32_t max_seq_len,
+                      int32_t *n_split, int32_t *split_tokens);
+
+/* Workspace bytes kvq_decode_attn needs for max_seq_len (0 when one split
+ * covers every sequence). */
+int kvq_decode_workspace_bytes(const kvq_geom *geom, int32_t max_seq_len,
+                               size_t *bytes);
+
+/* ----- quantization of a packed prefix ------------------------------------ */
+
+/* Per-channel key quantization of positions [pos0, pos0 + n_tok) of every
+ * sequence ([KIVI] core capabilities and Overview: keys per channel; [KV1]
+ * Quantization Format: the group quantizer).
+ *   k       device fp16 [B][Hkv][n_tok][D]: the keys of those positions.
+ *   pos0    first position; multiple of G.   n_tok: multiple of G, >= 0.
+ *   pos0 + n_tok <= capacity (KVQ_ERR_RANGE otherwise).
+ *   k_codes, k_meta: the cache buffers; rows [pos0, pos0+n_tok) of k_codes and
+ *   key groups [pos0/G, (pos0+n_tok)/G) of k_meta are written, nothing else. */
+int kvq_quantize_keys_perchannel(const kvq_geom *geom, const uint16_t *k,
+                                 int32_t pos0, int32_t n_tok,
+                                 uint32_t *k_codes, uint16_t *k_meta,
+                                 void *stream);
+
+/* Per-token value quantization of positions [pos0, pos0 + n_tok) ([KIVI] core
+ * capabilities and Overview: values per token).
+ *   v       device fp16 [B][Hkv][n_tok][D].
+ *   pos0, n_tok: multiples of KVQ_VBLOCK (32) and of G; pos0+n_tok <= capacity.
+ *   v_codes blocks [pos0/32, (pos0+n_tok)/32) and v_meta rows [pos0, pos0+n_tok)
+ *   are written, nothing else. */
+int kvq_quantize_values_pertoken(const kvq_geom *geom, const uint16_t *v,
+                                 int32_t pos0, int32_t n_tok,
+                                 uint32_t *v_codes, uint16_t *v_meta,
+                                 void *stream);
+
+/* Sets up every sequence of the cache as a prefix of n tokens, with the state
+ * the lazy flush rule gives after n single-token appends: positions [0, Lq(n))
+ * quantized (both calls above), positions [Lq(n), n) copied to residual slots
+ * p % R.  Lq(0) = 0.
+ *   k, v    device fp16 [B][Hkv][n][D].   0 <= n <= capacity. */
+int kvq_prefill(const kvq_geom *geom, const uint16_t *k, const uint16_t *v,
+                int32_t n, const kvq_cache *cache, void *stream);
+
+/* ----- decode step --------------------------------------------------------- */
+
+/* Appends one token per sequence ([KIVI] core capabilities: the recent tokens
+ * stay fp16; the window is flushed into packed groups when it is full).
+ *   k_new, v_new  device fp16 [B][Hkv][D]: the new token's key and value.
+ *   seq_lens      device int32 [B]: tokens each sequence holds BEFORE this
+ *                 token.  Not modified: the caller advances it (once per step,
+ *                 after every layer has appended).
+ * For every sequence with n = seq_lens[b]: if n > 0 and n % R == 0, positions
+ * [n - R, n) are quantized from the residual window into packed rows
+ * (bit-identical to kvq_quantize_* on the same tokens); then the new token is
+ * written to slot n % R.  A sequence with n < 0 or n >= capacity is left
+ * untouched (no write), which is the caller's error. */
+int kvq_append(const kvq_geom *geom, const uint16_t *k_new,
+               const uint16_t *v_new, const int32_t *seq_lens,
+               const kvq_cache *cache, void *stream);
+
+/* Single-token decode attention over the packed cache plus the residual window
+ * (split-context partial softmax, then a combine; GQA heads of one KV head are
+ * processed together).
+ *   q           device fp16 [B][Hq][D]: the current token's queries.
+ *   seq_lens    device int32 [B]: tokens per sequence INCLUDING the current one
+ *               (the current token must already be appended).
+ *   max_seq_len host int32: an upper bound of every seq_lens[b];
+ *               1 <= max_seq_len <= capacity.  Sizes the grid and workspace.
+ *   sm_scale    softmax scale (1/sqrt(D) for standard attention).
+ *   workspace   device memory of at least kvq_decode_workspace_bytes(geom,
+ *               max_seq_len) bytes (may be NULL when that is 0); contents on
+ *               entry do not matter; overwritten.
+ *   out         device fp16 [B][Hq][D].
+ * A sequence with seq_lens[b] == 0 gets out = 0.  A sequence whose length is
+ * negative or above max_seq_len or capacity gets out = NaN (no memory outside
+ * the buffers is read). */
+int kvq_decode_attn(const kvq_geom *geom, const uint16_t *q,
+                    const kvq_cache *cache, const int32_t *seq_lens,
+                    int32_t max_seq_len, float sm_scale, void *workspace,
+                    size_t workspace_bytes, uint16_t *out, void *stream);
+
+/* The two phases of kvq_decode_attn, for callers that time or schedule them
+ * apart.  kvq_decode_attn(...) == kvq_decode_partial(...) followed by
+ * kvq_decode_combine(...) on the same stream with the same arguments.
+ * kvq_decode_partial writes out directly (and kvq_decode_combine does nothing)
+ * when kvq_decode_splits() gives one split; otherwise it writes per-split
+ * (max, sum, weighted value) partials into the workspace. */
+int kvq_decode_partial(const kvq_geom *geom, const uint16_t *q,
+                       const kvq_cache *cache, const int32_t *seq_lens,
+                       int32_t max_seq_len, float sm_scale, void *workspace,
+                       size_t workspace_bytes, uint16_t *out, void *stream);
+int kvq_decode_combine(const kvq_geom *geom, const int32_t *seq_lens,
+                       int32_t max_seq_len, const void *workspace,
+                       size_t workspace_bytes, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* KVQ_H_ */

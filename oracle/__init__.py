@@ -1,0 +1,222 @@
+"""CPU oracle for KIVI-style quantized KV caches and decode attention.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the library under test never does.  The
+arithmetic lives in ``kvq_oracle.c`` (plain C, fp32 quantizer as the KV1 model
+card's "Quantization Format" section fixes it, fp64 dequantization and
+attention); this module only builds it and marshals numpy arrays.  Nothing here
+is shared with the GPU library: the packed layout and fp16 rounding are
+restated independently.
+
+Every function cites the page passage it follows in ``kvq_oracle.c``.  Pins
+(tests marked ``not gpu``) tie it to the pages and to independent mathematics.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+VBLOCK = 32  # tokens per value-code block (layout restated in kvq_oracle.c)
+
+
+def build(force: bool = True) -> str:
+    """Compiles liboracle.so with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = [
+            "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+            "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC,
+            "-o", _LIB + ".tmp", "-lm",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.orc_half_to_float.restype = ctypes.c_float
+        L.orc_half_to_float.argtypes = [ctypes.c_uint16]
+        L.orc_float_to_half.restype = ctypes.c_uint16
+        L.orc_float_to_half.argtypes = [ctypes.c_float]
+        L.orc_float_to_half_array.argtypes = [P, P, i64]
+        L.orc_half_to_float_array.argtypes = [P, P, i64]
+        L.orc_quantize_group.argtypes = [P, i64, i64, ctypes.c_int, P, P, P, i64]
+        L.orc_quantize_keys.argtypes = [ctypes.c_int] * 5 + [i64, P, i64, i64, P, P]
+        L.orc_quantize_values.argtypes = [ctypes.c_int] * 5 + [i64, P, i64, i64, P, P]
+        L.orc_packed_len.restype = i64
+        L.orc_packed_len.argtypes = [i64, ctypes.c_int]
+        L.orc_append.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 9
+        L.orc_cache_kv.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 6 + [i64, P, P]
+        L.orc_decode_attn.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 8 + [f64, P]
+        L.orc_max_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a: np.ndarray) -> np.ndarray:
+    """fp16 or uint16 array -> contiguous uint16 view."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+# ---------------------------------------------------------------- fp16 -----
+def float_to_half_bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib().orc_float_to_half_array(_p(x), _p(y), x.size)
+    return y
+
+
+def half_bits_to_float(h: np.ndarray) -> np.ndarray:
+    h = _u16(h)
+    y = np.empty(h.shape, np.float32)
+    lib().orc_half_to_float_array(_p(h), _p(y), h.size)
+    return y
+
+
+# ------------------------------------------------------------ quantizer ----
+def quantize_group(x: np.ndarray, bits: int):
+    """One group: returns (scale_bits, min_bits, codes uint8[n])."""
+    x = _u16(x).ravel().copy()
+    n = x.size
+    codes = np.zeros(n, np.uint8)
+    d = ctypes.c_uint16()
+    m = ctypes.c_uint16()
+    lib().orc_quantize_group(_p(x), n, 1, bits, ctypes.byref(d), ctypes.byref(m),
+                             _p(codes), 1)
+    return int(d.value), int(m.value), codes
+
+
+@dataclass
+class Geom:
+    """Cache geometry (the oracle's own restatement; plain ints)."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    k_bits: int
+    v_bits: int
+    group: int
+    residual: int
+    capacity: int
+
+
+class Cache:
+    """The six packed-cache arrays on the host, laid out as the specification
+    states (see kvq_oracle.c)."""
+
+    def __init__(self, g: Geom):
+        B, H, C, D = g.batch, g.n_kv_heads, g.capacity, g.head_dim
+        self.g = g
+        self.k_codes = np.zeros((B, H, C, D * g.k_bits // 32), np.uint32)
+        self.v_codes = np.zeros((B, H, C // VBLOCK, D, g.v_bits), np.uint32)
+        self.k_meta = np.zeros((B, H, C // g.group, D, 2), np.uint16)
+        self.v_meta = np.zeros((B, H, C, D // g.group, 2), np.uint16)
+        self.k_res = np.zeros((B, H, g.residual, D), np.uint16)
+        self.v_res = np.zeros((B, H, g.residual, D), np.uint16)
+
+    def arrays(self):
+        return (self.k_codes, self.v_codes, self.k_meta, self.v_meta,
+                self.k_res, self.v_res)
+
+
+def quantize_keys(g: Geom, cache: Cache, k: np.ndarray, pos0: int) -> None:
+    """k fp16 [B][Hkv][n_tok][D] -> key groups of positions [pos0, pos0+n_tok)."""
+    k = _u16(k)
+    n_tok = k.shape[2]
+    lib().orc_quantize_keys(g.batch, g.n_kv_heads, g.head_dim, g.k_bits, g.group,
+                            g.capacity, _p(k), pos0, n_tok, _p(cache.k_codes),
+                            _p(cache.k_meta))
+
+
+def quantize_values(g: Geom, cache: Cache, v: np.ndarray, pos0: int) -> None:
+    v = _u16(v)
+    n_tok = v.shape[2]
+    lib().orc_quantize_values(g.batch, g.n_kv_heads, g.head_dim, g.v_bits,
+                              g.group, g.capacity, _p(v), pos0, n_tok,
+                              _p(cache.v_codes), _p(cache.v_meta))
+
+
+def packed_len(n: int, R: int) -> int:
+    return int(lib().orc_packed_len(n, R))
+
+
+def prefill(g: Geom, cache: Cache, k: np.ndarray, v: np.ndarray, n: int) -> None:
+    """State after n single-token appends: [0, Lq) packed, [Lq, n) residual."""
+    k = _u16(k)
+    v = _u16(v)
+    lq = packed_len(n, g.residual)
+    if lq > 0:
+        quantize_keys(g, cache, np.ascontiguousarray(k[:, :, :lq]), 0)
+        quantize_values(g, cache, np.ascontiguousarray(v[:, :, :lq]), 0)
+    for t in range(lq, n):
+        cache.k_res[:, :, t % g.residual] = k[:, :, t]
+        cache.v_res[:, :, t % g.residual] = v[:, :, t]
+
+
+def append(g: Geom, cache: Cache, k_new: np.ndarray, v_new: np.ndarray,
+           seq_lens_before: np.ndarray) -> None:
+    k_new = _u16(k_new)
+    v_new = _u16(v_new)
+    sl = np.ascontiguousarray(seq_lens_before, dtype=np.int32)
+    lib().orc_append(g.batch, g.n_kv_heads, g.head_dim, g.k_bits, g.v_bits,
+                     g.group, g.residual, g.capacity, _p(k_new), _p(v_new),
+                     _p(sl), *[_p(a) for a in cache.arrays()])
+
+
+def cache_kv(g: Geom, cache: Cache, n: int):
+    """(K, V) fp64 [B][Hkv][n][D] as the cache represents positions < n."""
+    shape = (g.batch, g.n_kv_heads, n, g.head_dim)
+    ok = np.zeros(shape, np.float64)
+    ov = np.zeros(shape, np.float64)
+    lib().orc_cache_kv(g.batch, g.n_kv_heads, g.head_dim, g.k_bits, g.v_bits,
+                       g.group, g.residual, g.capacity,
+                       *[_p(a) for a in cache.arrays()], n, _p(ok), _p(ov))
+    return ok, ov
+
+
+def decode_attn(g: Geom, cache: Cache, q: np.ndarray, seq_lens: np.ndarray,
+                sm_scale: float) -> np.ndarray:
+    """fp64 [B][Hq][D] attention outputs; seq_lens include the current token."""
+    q = _u16(q)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.zeros((g.batch, g.n_q_heads, g.head_dim), np.float64)
+    lib().orc_decode_attn(g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim,
+                          g.k_bits, g.v_bits, g.group, g.residual, g.capacity,
+                          _p(q), *[_p(a) for a in cache.arrays()], _p(sl),
+                          float(sm_scale), _p(out))
+    return out
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(n)

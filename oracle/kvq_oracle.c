@@ -1,0 +1,477 @@
+/*
+ * kvq_oracle.c — plain, slow CPU oracle for KIVI-style quantized KV caches and
+ * single-token decode attention over them.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the GPU library: the packed layout is restated
+ * here from its written specification, and fp16 conversion is done in software.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [KIVI] "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
+ *          (repository digest): core capabilities (keys per channel, values per
+ *          token, fp16 residual window, 2/4 bits, group size), Overview,
+ *          Example (k_bits, v_bits, group_size, residual_length).
+ *   [KV1]  "KV1-1.2B-Instruct" model card: "Quantization Format: KV1.cpp BQ2_0"
+ *          (quantize in fp32, scale = (max-min)/(2^b-1), fp16-rounded scale and
+ *          min used for the codes, round half to even, clamp, dequantize as
+ *          code*scale+min, code order inside a byte), "Quickstart" (attending
+ *          over the once-quantized cache gives the exact low-bit result).
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - the code divides by the stored fp16 scale (KV1 states the fp16-rounded
+ *     scale and min are the ones used for the codes);
+ *   - a zero fp16 scale gives code 0 for every element (KV1's 1e-6 floor belongs
+ *     to its own format and is not applied);
+ *   - zero min / max are taken as +0 so that stored bits do not depend on order;
+ *   - lazy flush: a full residual window is quantized when the next token
+ *     arrives, so 1..R residual tokens are present at attention time;
+ *   - query head h uses KV head h / (Hq/Hkv);
+ *   - attention covers all n tokens, including the current one, no mask.
+ *
+ * Floating point: the quantizer runs in IEEE fp32 (the precision KV1 fixes for
+ * quantizing); dequantization and attention run in fp64.  Build with
+ * -O2 -fno-fast-math -ffp-contract=off so that gcc neither contracts nor
+ * reorders the fp32 steps.  OpenMP splits independent (sequence, KV head)
+ * units across threads; every unit's arithmetic is serial and deterministic.
+ *
+ * Parity pins (tests): exhaustive fp32->fp16 rounding against numpy; worked
+ * examples derived by hand; brute-force nearest-grid-point code selection in
+ * exact rational arithmetic; reconstruction bound; constant groups; KV1 BQ2_0
+ * byte order; byte accounting against the KV1 memory table; attention against
+ * torch float64 scaled_dot_product_attention and a naive loop; closed forms
+ * (q = 0, n = 1, identical rows, all-residual); incremental flushes equal to a
+ * bulk quantization.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_VBLOCK 32 /* tokens per value-code block in the packed layout */
+
+/* ------------------------------------------------------------------------ */
+/* fp16 <-> fp32 in software                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Widens IEEE binary16 bits to a float (exact). */
+float orc_half_to_float(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 0x1f;
+  int mant = h & 0x3ff;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)mant, -24); /* subnormal: mant * 2^-24 */
+  } else if (expo == 31) {
+    v = mant ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(mant + 1024), expo - 25); /* (1.mant) * 2^(expo-15) */
+  }
+  return (float)(sign ? -v : v);
+}
+
+/* Rounds a float to the nearest binary16, ties to even; returns the bits. */
+uint16_t orc_float_to_half(float f) {
+  uint32_t fbits;
+  memcpy(&fbits, &f, sizeof fbits);
+  uint16_t sign = (uint16_t)((fbits >> 16) & 0x8000u);
+  if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  double a = fabs((double)f);
+  if (a == 0.0) return sign;
+  /* 65504 is the largest finite half; its successor would be 65536, and the
+   * midpoint 65520 rounds to the even one (65536), i.e. overflows. */
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+
+  int e2; /* a = fr * 2^e2, 0.5 <= fr < 1, so 2^(e2-1) <= a < 2^e2 */
+  (void)frexp(a, &e2);
+  int e = e2 - 1; /* unbiased exponent of a */
+  double quantum = (e < -14) ? ldexp(1.0, -24) : ldexp(1.0, e - 10);
+
+  double n = a / quantum; /* exact: quantum is a power of two */
+  double fl = floor(n);
+  double frac = n - fl;
+  if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+  /* fl * quantum is the rounded magnitude */
+  if (e < -14) {
+    /* subnormal range; fl == 1024 is the smallest normal, whose bits are 0x400 */
+    return (uint16_t)(sign | (uint16_t)fl);
+  }
+  long m = (long)fl; /* in [1024, 2048] */
+  int expo = e + 15;
+  if (m == 2048) {
+    m = 1024;
+    expo += 1;
+  }
+  if (expo >= 31) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)(expo << 10) | (uint16_t)(m - 1024));
+}
+
+/* Vector helpers for the tests. */
+void orc_float_to_half_array(const float *x, uint16_t *y, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_float_to_half(x[i]);
+}
+void orc_half_to_float_array(const uint16_t *x, float *y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_half_to_float(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The group quantizer                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Round half to even of a non-negative-or-any float, written out. */
+static float round_half_even(float y) {
+  float fl = floorf(y);
+  float frac = y - fl; /* exact for |y| < 2^23 */
+  if (frac > 0.5f || (frac == 0.5f && fmodf(fl, 2.0f) != 0.0f)) fl += 1.0f;
+  return fl;
+}
+
+/*
+ * Quantizes n fp16 values x[0], x[stride], ... with b bits.
+ * Writes the fp16 bits of (scale, min) and one code per element
+ * (codes[i*code_stride]).  [KV1] Quantization Format, in fp32:
+ *   scale = fp16((max - min) / (2^b - 1)), min = fp16(min),
+ *   code = clamp(round_half_even((x - min) / scale), 0, 2^b - 1)
+ * with the fp16-rounded scale and min used for the codes; a zero scale gives
+ * code 0.
+ */
+void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
+                        uint16_t *scale_out, uint16_t *min_out, uint8_t *codes,
+                        int64_t code_stride) {
+  float mn = orc_half_to_float(x[0]);
+  float mx = mn;
+  for (int64_t i = 1; i < n; ++i) {
+    float v = orc_half_to_float(x[i * stride]);
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  if (mn == 0.0f) mn = 0.0f; /* -0 -> +0 */
+  if (mx == 0.0f) mx = 0.0f;
+
+  const float levels = (float)((1 << bits) - 1);
+  float range = mx - mn;     /* fp32 subtract */
+  float d32 = range / levels; /* fp32 divide */
+  uint16_t d16 = orc_float_to_half(d32);
+  if ((d16 & 0x7fffu) == 0) d16 = 0; /* zero scale stored as +0 */
+  uint16_t m16 = orc_float_to_half(mn);
+
+  float scale = orc_half_to_float(d16);
+  float minv = orc_half_to_float(m16);
+  for (int64_t i = 0; i < n; ++i) {
+    float code = 0.0f;
+    if (scale != 0.0f) {
+      float v = orc_half_to_float(x[i * stride]);
+      float y = (v - minv) / scale; /* fp32 subtract, fp32 divide */
+      code = round_half_even(y);
+      if (code < 0.0f) code = 0.0f;
+      if (code > levels) code = levels;
+    }
+    codes[i * code_stride] = (uint8_t)code;
+  }
+  *scale_out = d16;
+  *min_out = m16;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed layout (restated from its specification)                          */
+/*                                                                           */
+/* k_codes  u32 [B][Hkv][C][D*bK/32]: token rows, channel c in bits          */
+/*          (c*bK)%32.. of word (c*bK)/32, lowest channel lowest.            */
+/* k_meta   u16 [B][Hkv][C/G][D][2]: (scale, min) per key group and channel. */
+/* v_codes  u32 [B][Hkv][C/32][D][bV]: 32-token blocks; for channel c,       */
+/*          token tau of the block in bits (tau*bV)%32.. of word (tau*bV)/32.*/
+/* v_meta   u16 [B][Hkv][C][D/G][2]: (scale, min) per token, channel group.  */
+/* k_res, v_res u16 [B][Hkv][R][D]: position p in slot p % R.               */
+/* ------------------------------------------------------------------------ */
+
+static void put_field(uint32_t *word, int bit, int bits, uint32_t code) {
+  uint32_t mask = ((1u << bits) - 1u) << bit;
+  *word = (*word & ~mask) | ((code << bit) & mask);
+}
+
+static uint32_t get_field(uint32_t word, int bit, int bits) {
+  return (word >> bit) & ((1u << bits) - 1u);
+}
+
+/* Key code of token t, channel c of unit (b, h), from the packed rows. */
+static uint32_t key_code(const uint32_t *k_codes, int64_t unit, int64_t C,
+                         int D, int bK, int64_t t, int c) {
+  int64_t words = (int64_t)D * bK / 32;
+  const uint32_t *row = k_codes + (unit * C + t) * words;
+  return get_field(row[(c * bK) / 32], (c * bK) % 32, bK);
+}
+
+static uint32_t value_code(const uint32_t *v_codes, int64_t unit, int64_t C,
+                           int D, int bV, int64_t t, int c) {
+  int64_t blk = t / ORC_VBLOCK;
+  int tau = (int)(t % ORC_VBLOCK);
+  const uint32_t *field =
+      v_codes + ((unit * (C / ORC_VBLOCK) + blk) * D + c) * bV;
+  return get_field(field[(tau * bV) / 32], (tau * bV) % 32, bV);
+}
+
+/* Quantizes key groups of one unit from a source of token rows src[t*D + c]
+ * (fp16) whose first row is position pos0; n_tok tokens, multiples of G. */
+static void quantize_keys_unit(const uint16_t *src, int64_t pos0, int64_t n_tok,
+                               int D, int bK, int G, int64_t C, int64_t unit,
+                               uint32_t *k_codes, uint16_t *k_meta) {
+  int64_t words = (int64_t)D * bK / 32;
+  uint8_t *codes = (uint8_t *)malloc((size_t)G);
+  for (int64_t j0 = 0; j0 < n_tok; j0 += G) {
+    int64_t j = (pos0 + j0) / G; /* key group index */
+    for (int c = 0; c < D; ++c) {
+      uint16_t d16, m16;
+      /* per channel: the G tokens of the group ([KIVI] keys per channel) */
+      orc_quantize_group(src + j0 * D + c, G, D, bK, &d16, &m16, codes, 1);
+      uint16_t *meta = k_meta + ((unit * (C / G) + j) * D + c) * 2;
+      meta[0] = d16;
+      meta[1] = m16;
+      for (int i = 0; i < G; ++i) {
+        int64_t t = pos0 + j0 + i;
+        uint32_t *row = k_codes + (unit * C + t) * words;
+        put_field(&row[(c * bK) / 32], (c * bK) % 32, bK, codes[i]);
+      }
+    }
+  }
+  free(codes);
+}
+
+/* Quantizes value tokens of one unit; src[t*D + c] fp16, position pos0 first. */
+static void quantize_values_unit(const uint16_t *src, int64_t pos0,
+                                 int64_t n_tok, int D, int bV, int G, int64_t C,
+                                 int64_t unit, uint32_t *v_codes,
+                                 uint16_t *v_meta) {
+  uint8_t *codes = (uint8_t *)malloc((size_t)G);
+  int ngroups = D / G;
+  for (int64_t i = 0; i < n_tok; ++i) {
+    int64_t t = pos0 + i;
+    for (int gm = 0; gm < ngroups; ++gm) {
+      uint16_t d16, m16;
+      /* per token: G consecutive channels ([KIVI] values per token) */
+      orc_quantize_group(src + i * D + (int64_t)gm * G, G, 1, bV, &d16, &m16,
+                         codes, 1);
+      uint16_t *meta = v_meta + ((unit * C + t) * ngroups + gm) * 2;
+      meta[0] = d16;
+      meta[1] = m16;
+      for (int cc = 0; cc < G; ++cc) {
+        int c = gm * G + cc;
+        int64_t blk = t / ORC_VBLOCK;
+        int tau = (int)(t % ORC_VBLOCK);
+        uint32_t *field =
+            v_codes + ((unit * (C / ORC_VBLOCK) + blk) * D + c) * bV;
+        put_field(&field[(tau * bV) / 32], (tau * bV) % 32, bV, codes[cc]);
+      }
+    }
+  }
+  free(codes);
+}
+
+/* Bulk per-channel key quantization of positions [pos0, pos0+n_tok) of every
+ * unit; k is fp16 [B*Hkv][n_tok][D]. */
+void orc_quantize_keys(int B, int Hkv, int D, int bK, int G, int64_t C,
+                       const uint16_t *k, int64_t pos0, int64_t n_tok,
+                       uint32_t *k_codes, uint16_t *k_meta) {
+  int64_t units = (int64_t)B * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u)
+    quantize_keys_unit(k + u * n_tok * D, pos0, n_tok, D, bK, G, C, u, k_codes,
+                       k_meta);
+}
+
+/* Bulk per-token value quantization; v is fp16 [B*Hkv][n_tok][D]. */
+void orc_quantize_values(int B, int Hkv, int D, int bV, int G, int64_t C,
+                         const uint16_t *v, int64_t pos0, int64_t n_tok,
+                         uint32_t *v_codes, uint16_t *v_meta) {
+  int64_t units = (int64_t)B * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u)
+    quantize_values_unit(v + u * n_tok * D, pos0, n_tok, D, bV, G, C, u,
+                         v_codes, v_meta);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Residual window and lazy flush                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Number of packed tokens of a sequence holding n tokens (lazy flush): the
+ * residual keeps ((n-1) % R) + 1 tokens when n >= 1. */
+int64_t orc_packed_len(int64_t n, int R) {
+  if (n <= 0) return 0;
+  return n - (((n - 1) % R) + 1);
+}
+
+/* Appends one token per sequence.  seq_lens[b] = tokens held BEFORE the new
+ * one.  If that count n is positive and a multiple of R, positions [n-R, n) are
+ * quantized from the residual window first; then the new token goes to slot
+ * n % R.  ([KIVI] core capabilities: recent tokens kept in fp16.)
+ * k_new, v_new fp16 [B][Hkv][D]. */
+void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int R, int64_t C,
+                const uint16_t *k_new, const uint16_t *v_new,
+                const int32_t *seq_lens, uint32_t *k_codes, uint32_t *v_codes,
+                uint16_t *k_meta, uint16_t *v_meta, uint16_t *k_res,
+                uint16_t *v_res) {
+  int64_t units = (int64_t)B * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    int b = (int)(u / Hkv);
+    int64_t n = seq_lens[b];
+    if (n < 0 || n >= C) continue;
+    uint16_t *kr = k_res + u * R * D;
+    uint16_t *vr = v_res + u * R * D;
+    if (n > 0 && n % R == 0) {
+      /* slots 0..R-1 hold positions n-R .. n-1 in order */
+      quantize_keys_unit(kr, n - R, R, D, bK, G, C, u, k_codes, k_meta);
+      quantize_values_unit(vr, n - R, R, D, bV, G, C, u, v_codes, v_meta);
+    }
+    int64_t slot = n % R;
+    memcpy(kr + slot * D, k_new + u * D, (size_t)D * sizeof(uint16_t));
+    memcpy(vr + slot * D, v_new + u * D, (size_t)D * sizeof(uint16_t));
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantization (fp64, exact)                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Dequantized key of token t < packed length: code * scale + min ([KV1]
+ * Dequantize).  The product of a code below 16 and an fp16 scale, plus an fp16
+ * min, is exact in fp64. */
+static double dequant_key(const uint32_t *k_codes, const uint16_t *k_meta,
+                          int64_t unit, int64_t C, int D, int bK, int G,
+                          int64_t t, int c) {
+  const uint16_t *meta = k_meta + ((unit * (C / G) + t / G) * D + c) * 2;
+  double scale = orc_half_to_float(meta[0]);
+  double minv = orc_half_to_float(meta[1]);
+  return (double)key_code(k_codes, unit, C, D, bK, t, c) * scale + minv;
+}
+
+static double dequant_value(const uint32_t *v_codes, const uint16_t *v_meta,
+                            int64_t unit, int64_t C, int D, int bV, int G,
+                            int64_t t, int c) {
+  const uint16_t *meta = v_meta + ((unit * C + t) * (D / G) + c / G) * 2;
+  double scale = orc_half_to_float(meta[0]);
+  double minv = orc_half_to_float(meta[1]);
+  return (double)value_code(v_codes, unit, C, D, bV, t, c) * scale + minv;
+}
+
+/* Full-precision key/value of every position t < n of every unit as the cache
+ * represents it: dequantized for t < packed length, residual fp16 otherwise.
+ * out_k, out_v: fp64 [B*Hkv][n][D]. */
+void orc_cache_kv(int B, int Hkv, int D, int bK, int bV, int G, int R,
+                  int64_t C, const uint32_t *k_codes, const uint32_t *v_codes,
+                  const uint16_t *k_meta, const uint16_t *v_meta,
+                  const uint16_t *k_res, const uint16_t *v_res, int64_t n,
+                  double *out_k, double *out_v) {
+  int64_t units = (int64_t)B * Hkv;
+  int64_t lq = orc_packed_len(n, R);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    for (int64_t t = 0; t < n; ++t) {
+      for (int c = 0; c < D; ++c) {
+        double kv, vv;
+        if (t < lq) {
+          kv = dequant_key(k_codes, k_meta, u, C, D, bK, G, t, c);
+          vv = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
+        } else {
+          kv = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
+          vv = orc_half_to_float(v_res[(u * R + t % R) * D + c]);
+        }
+        out_k[(u * n + t) * D + c] = kv;
+        out_v[(u * n + t) * D + c] = vv;
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention (fp64)                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For every sequence b and query head h: with n = seq_lens[b] (tokens including
+ * the current one) and KV head h / (Hq/Hkv),
+ *   s_t = sm_scale * sum_c q[c] * k_t[c],  p = softmax(s),  out = sum_t p_t v_t
+ * over all n tokens (dequantized for t < packed length, fp16 residual for the
+ * rest), in fp64.  q fp16 [B][Hq][D]; out fp64 [B][Hq][D].  n == 0 gives 0.
+ */
+void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
+                     int R, int64_t C, const uint16_t *q,
+                     const uint32_t *k_codes, const uint32_t *v_codes,
+                     const uint16_t *k_meta, const uint16_t *v_meta,
+                     const uint16_t *k_res, const uint16_t *v_res,
+                     const int32_t *seq_lens, double sm_scale, double *out) {
+  int64_t units = (int64_t)B * Hkv;
+  int g = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    int b = (int)(u / Hkv);
+    int hkv = (int)(u % Hkv);
+    int64_t n = seq_lens[b];
+    if (n > C) n = C;
+    int64_t lq = orc_packed_len(n, R);
+    /* this unit's keys and values, as the cache represents them */
+    double *kk = (double *)malloc((size_t)(n > 0 ? n : 1) * D * sizeof(double));
+    double *vv = (double *)malloc((size_t)(n > 0 ? n : 1) * D * sizeof(double));
+    double *s = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    for (int64_t t = 0; t < n; ++t) {
+      for (int c = 0; c < D; ++c) {
+        if (t < lq) {
+          kk[t * D + c] = dequant_key(k_codes, k_meta, u, C, D, bK, G, t, c);
+          vv[t * D + c] = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
+        } else {
+          kk[t * D + c] = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
+          vv[t * D + c] = orc_half_to_float(v_res[(u * R + t % R) * D + c]);
+        }
+      }
+    }
+    for (int hh = 0; hh < g; ++hh) {
+      int h = hkv * g + hh;
+      const uint16_t *qh = q + ((int64_t)b * Hq + h) * D;
+      double *oh = out + ((int64_t)b * Hq + h) * D;
+      for (int c = 0; c < D; ++c) oh[c] = 0.0;
+      if (n <= 0) continue;
+      double smax = -INFINITY;
+      for (int64_t t = 0; t < n; ++t) {
+        double dot = 0.0;
+        for (int c = 0; c < D; ++c)
+          dot += (double)orc_half_to_float(qh[c]) * kk[t * D + c];
+        s[t] = sm_scale * dot;
+        if (s[t] > smax) smax = s[t];
+      }
+      double denom = 0.0;
+      for (int64_t t = 0; t < n; ++t) {
+        s[t] = exp(s[t] - smax);
+        denom += s[t];
+      }
+      for (int64_t t = 0; t < n; ++t) {
+        double p = s[t] / denom;
+        for (int c = 0; c < D; ++c) oh[c] += p * vv[t * D + c];
+      }
+    }
+    free(kk);
+    free(vv);
+    free(s);
+  }
+}
+
+/* Threads the OpenMP runtime will use for the parallel loops above. */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

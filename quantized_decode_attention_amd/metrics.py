@@ -1,0 +1,59 @@
+"""Byte accounting of the packed cache and of one decode step.
+
+Algorithmic bytes are the bytes the method itself must move: every packed code
+once, each key group's fp16 (scale, min) row once per G tokens, each token's
+value (scale, min) pairs once, the fp16 residual window, the query and the
+output.  Split partials and any re-reads are not counted (they count against
+the kernels).  The per-token formula reproduces the KV1 model card's "Memory"
+table (fp16 / 3.5-bit / BQ2_0 per token and at 8K and 32K context), which is
+the pin used by the tests.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def packed_bytes_per_token(head_dim: int, k_bits: int, v_bits: int, group: int) -> float:
+    """Bytes per packed token per KV head: codes, key meta amortized over the
+    group's G tokens (4 bytes per channel), value meta (4 bytes per group)."""
+    D, G = head_dim, group
+    return D * (k_bits + v_bits) / 8 + 4 * D / G + 4 * D / G
+
+
+def fp16_bytes_per_token(head_dim: int) -> int:
+    return 2 * 2 * head_dim
+
+
+def packed_len(n: int, residual: int) -> int:
+    """Packed tokens of a sequence of n tokens under the lazy flush rule."""
+    return 0 if n <= 0 else n - (((n - 1) % residual) + 1)
+
+
+def decode_step_bytes(seq_lens, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                      k_bits: int, v_bits: int, group: int, residual: int) -> float:
+    """Algorithmic bytes of one decode-attention launch over sequences of the
+    given lengths (current token included)."""
+    per_packed = packed_bytes_per_token(head_dim, k_bits, v_bits, group)
+    total = 0.0
+    for n in np.asarray(seq_lens).tolist():
+        lq = packed_len(int(n), residual)
+        r = int(n) - lq
+        total += n_kv_heads * (lq * per_packed + r * fp16_bytes_per_token(head_dim))
+    B = len(np.asarray(seq_lens))
+    total += 2 * 2 * B * n_q_heads * head_dim      # q in, out
+    total += 4 * B                                  # seq_lens
+    return total
+
+
+def append_bytes(batch: int, n_kv_heads: int, head_dim: int) -> int:
+    """Bytes of one append without a flush: new K, V read and written."""
+    return 2 * 2 * 2 * batch * n_kv_heads * head_dim
+
+
+def flush_bytes(n_flush_units: int, residual: int, head_dim: int, k_bits: int,
+                v_bits: int, group: int) -> float:
+    """Bytes of flushing R residual tokens of n units: fp16 window read, packed
+    rows written."""
+    return n_flush_units * residual * (
+        fp16_bytes_per_token(head_dim)
+        + packed_bytes_per_token(head_dim, k_bits, v_bits, group))

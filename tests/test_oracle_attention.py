@@ -1,0 +1,209 @@
+"""Pins of the oracle's cache state machine, dequantization and attention.
+
+Attention is pinned to torch's float64 scaled_dot_product_attention (a library
+routine) on the cache's dequantized K/V, to a naive pure-Python loop on tiny
+inputs, and to closed forms: q = 0 gives the mean of the values, one token gives
+that token's value, identical value rows give that row, and a cache that is all
+residual (n <= R) equals plain softmax attention on the fp16 inputs.  The cache
+state is pinned by the reconstruction bound against the raw inputs and by
+incremental appends (with their flushes) equalling a bulk quantization.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_decode_attention_amd import synth
+
+
+def _geom(orc, w, capacity, batch=None):
+    return orc.Geom(batch or w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                    w.k_bits, w.v_bits, w.group, w.residual, capacity)
+
+
+def _sdpa(q, k, v, scale):
+    """q [B][Hq][D], k/v [B][Hkv][n][D] float64 -> [B][Hq][D] (GQA by repeat)."""
+    g = q.shape[1] // k.shape[1]
+    qt = torch.from_numpy(q)[:, :, None, :]
+    kt = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    vt = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return o[:, :, 0, :].numpy()
+
+
+def _tiny_case(orc, n, B=1, Hq=4, Hkv=2, D=64, bK=2, bV=4, G=32, R=32, seed=5):
+    w = synth.Workload("t", 1, B, Hq, Hkv, D, bK, bV, G, R, n)
+    cap = ((n + R) // R + 1) * R
+    g = _geom(orc, w, cap)
+    rng = np.random.default_rng(seed)
+    k = (rng.standard_normal((B, Hkv, n, D)) * rng.lognormal(0, .5, (1, Hkv, 1, D))).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, n, D)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    cache = orc.Cache(g)
+    orc.prefill(g, cache, k, v, n)
+    return g, cache, k, v, q
+
+
+def test_attention_matches_torch_sdpa_config1(orc):
+    w = synth.WORKLOADS[1]
+    g = _geom(orc, w, 288)
+    k = synth.keys(w, w.context)
+    v = synth.values(w, w.context)
+    q = synth.queries(w)
+    cache = orc.Cache(g)
+    orc.prefill(g, cache, k, v, w.context)
+    assert orc.packed_len(w.context, w.residual) == 224
+    scale = 1 / math.sqrt(w.head_dim)
+    out = orc.decode_attn(g, cache, q, np.full(w.batch, w.context), scale)
+    kk, vv = orc.cache_kv(g, cache, w.context)
+    ref = _sdpa(q.astype(np.float64), kk, vv, scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def _varlen_cache(orc, g, k, v, lens):
+    """Batched cache whose sequence b holds lens[b] tokens (per-sequence
+    prefill into the shared arrays)."""
+    cache = orc.Cache(g)
+    for b, n in enumerate(lens):
+        gb = orc.Geom(1, g.n_q_heads, g.n_kv_heads, g.head_dim, g.k_bits, g.v_bits,
+                      g.group, g.residual, g.capacity)
+        cb = orc.Cache(gb)
+        orc.prefill(gb, cb, k[b:b + 1, :, :n], v[b:b + 1, :, :n], int(n))
+        for dst, src in zip(cache.arrays(), cb.arrays()):
+            dst[b] = src[0]
+    return cache
+
+
+@pytest.mark.parametrize("bK,bV", [(2, 2), (2, 4), (4, 2), (4, 4)])
+def test_attention_matches_torch_sdpa_gqa_varlen(orc, bK, bV):
+    n = 200
+    g, _, k, v, q = _tiny_case(orc, n, B=3, Hq=8, Hkv=2, bK=bK, bV=bV)
+    lens = [n, 77, 33]
+    cache = _varlen_cache(orc, g, k, v, lens)
+    scale = 0.125
+    out = orc.decode_attn(g, cache, q, np.array(lens), scale)
+    for b, nb in enumerate(lens):
+        gb = orc.Geom(1, 8, 2, 64, bK, bV, 32, 32, g.capacity)
+        cb = orc.Cache(gb)
+        orc.prefill(gb, cb, k[b:b + 1, :, :nb], v[b:b + 1, :, :nb], nb)
+        kk, vv = orc.cache_kv(gb, cb, nb)
+        ref = _sdpa(q[b:b + 1].astype(np.float64), kk, vv, scale)
+        np.testing.assert_allclose(out[b], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_naive_loop(orc):
+    """Pure-Python softmax attention over the cache's K/V, one head at a time."""
+    n = 70
+    g, cache, k, v, q = _tiny_case(orc, n, B=1, Hq=4, Hkv=2, D=64, bK=2, bV=2)
+    scale = 0.3
+    out = orc.decode_attn(g, cache, q, np.array([n]), scale)
+    kk, vv = orc.cache_kv(g, cache, n)
+    for h in range(4):
+        hk = h // 2
+        qh = [float(x) for x in q[0, h]]
+        s = [scale * sum(qh[c] * kk[0, hk, t, c] for c in range(64)) for t in range(n)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        o = [sum(e[t] / z * vv[0, hk, t, c] for t in range(n)) for c in range(64)]
+        np.testing.assert_allclose(out[0, h], o, rtol=1e-12, atol=1e-13)
+
+
+def test_cache_reconstructs_inputs(orc):
+    """Packed positions reconstruct within the quantizer's bound; residual ones
+    are the fp16 inputs bit for bit."""
+    n = 150
+    g, cache, k, v, q = _tiny_case(orc, n, B=2, Hq=4, Hkv=2, bK=2, bV=4)
+    lq = orc.packed_len(n, g.residual)
+    assert lq == 128
+    kk, vv = orc.cache_kv(g, cache, n)
+    np.testing.assert_array_equal(kk[:, :, lq:], k[:, :, lq:].astype(np.float64))
+    np.testing.assert_array_equal(vv[:, :, lq:], v[:, :, lq:].astype(np.float64))
+    kscale = cache.k_meta[..., 0].view(np.float16).astype(np.float64)  # [B][H][C/G][D]
+    vscale = cache.v_meta[..., 0].view(np.float16).astype(np.float64)  # [B][H][C][D/G]
+    kbound = np.repeat(kscale[:, :, :lq // 32], 32, axis=2) * 0.5 * (1 + 1e-2)
+    vbound = np.repeat(vscale[:, :, :lq], 32, axis=3) * 0.5 * (1 + 1e-2)
+    kerr = np.abs(kk[:, :, :lq] - k[:, :, :lq].astype(np.float64))
+    verr = np.abs(vv[:, :, :lq] - v[:, :, :lq].astype(np.float64))
+    assert np.all(kerr <= kbound + 1e-7)
+    assert np.all(verr <= vbound + 1e-7)
+
+
+def test_closed_forms(orc):
+    n = 90
+    g, cache, k, v, q = _tiny_case(orc, n, B=1, Hq=2, Hkv=1, D=64, bK=2, bV=2)
+    kk, vv = orc.cache_kv(g, cache, n)
+    # q = 0: uniform weights -> mean of the values
+    out = orc.decode_attn(g, cache, np.zeros_like(q), np.array([n]), 0.1)
+    np.testing.assert_allclose(out[0, 0], vv[0, 0].mean(axis=0), rtol=1e-12, atol=1e-14)
+    # one token: the output is that token's (fp16 residual) value
+    c1 = orc.Cache(g)
+    orc.prefill(g, c1, k[:, :, :1], v[:, :, :1], 1)
+    out1 = orc.decode_attn(g, c1, q, np.array([1]), 0.1)
+    np.testing.assert_array_equal(out1[0, 0], v[0, 0, 0].astype(np.float64))
+    # zero tokens: defined as zero
+    out0 = orc.decode_attn(g, cache, q, np.array([0]), 0.1)
+    assert np.all(out0 == 0)
+    # identical value rows -> that row, whatever the weights.  The row is on
+    # every group's 2-bit grid (values -1.5, -0.5, 0.5, 1.5 in each group), so
+    # packed and residual tokens represent it exactly.
+    row = ((np.arange(64) % 4) - 1.5).astype(np.float16)
+    vconst = np.broadcast_to(row, v.shape).copy()
+    c2 = orc.Cache(g)
+    orc.prefill(g, c2, k, vconst, n)
+    out2 = orc.decode_attn(g, c2, q, np.array([n]), 0.1)
+    np.testing.assert_allclose(out2[0], np.broadcast_to(row.astype(np.float64), (2, 64)),
+                               rtol=1e-14, atol=1e-14)
+
+
+def test_all_residual_equals_unquantized(orc):
+    """n <= R: nothing is packed; attention equals softmax attention on the raw
+    fp16 inputs."""
+    for n in (1, 17, 32):
+        g, cache, k, v, q = _tiny_case(orc, n, B=2, Hq=4, Hkv=2, R=32)
+        assert orc.packed_len(n, 32) == 0
+        out = orc.decode_attn(g, cache, q, np.array([n, n]), 0.125)
+        ref = _sdpa(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 0.125)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("bK,bV,G,R", [(2, 2, 32, 32), (2, 4, 32, 64), (4, 2, 64, 64)])
+def test_appends_equal_bulk_quantization(orc, bK, bV, G, R):
+    """Incremental appends (with lazy flushes) leave the same packed state as a
+    bulk quantization of the packed prefix, bit for bit, for every length."""
+    B, H, D = 3, 2, 64
+    steps = 3 * R + 5
+    cap = 4 * R
+    g = orc.Geom(B, H, H, D, bK, bV, G, R, cap)
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((B, H, steps, D)).astype(np.float16)
+    v = rng.standard_normal((B, H, steps, D)).astype(np.float16)
+    start = np.array([0, 5, R])          # sequences start at different lengths
+    inc = orc.Cache(g)
+    for b in range(B):
+        gb = orc.Geom(1, H, H, D, bK, bV, G, R, cap)
+        cb = orc.Cache(gb)
+        orc.prefill(gb, cb, k[b:b + 1], v[b:b + 1], int(start[b]))
+        for name, arr in zip(["k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res"],
+                             cb.arrays()):
+            getattr(inc, name)[b] = arr[0]
+    lens = start.copy()
+    for step in range(steps - R):
+        kn = np.stack([k[b, :, lens[b]] for b in range(B)])
+        vn = np.stack([v[b, :, lens[b]] for b in range(B)])
+        orc.append(g, inc, kn, vn, lens.astype(np.int32))
+        lens += 1
+        for b in range(B):
+            n = int(lens[b])
+            gb = orc.Geom(1, H, H, D, bK, bV, G, R, cap)
+            ref = orc.Cache(gb)
+            orc.prefill(gb, ref, k[b:b + 1], v[b:b + 1], n)
+            lq = orc.packed_len(n, R)
+            np.testing.assert_array_equal(inc.k_codes[b, :, :lq], ref.k_codes[0, :, :lq])
+            np.testing.assert_array_equal(inc.k_meta[b, :, :lq // G], ref.k_meta[0, :, :lq // G])
+            np.testing.assert_array_equal(inc.v_codes[b, :, :lq // 32], ref.v_codes[0, :, :lq // 32])
+            np.testing.assert_array_equal(inc.v_meta[b, :, :lq], ref.v_meta[0, :, :lq])
+            for t in range(lq, n):
+                np.testing.assert_array_equal(inc.k_res[b, :, t % R], k[b, :, t].view(np.uint16))
+                np.testing.assert_array_equal(inc.v_res[b, :, t % R], v[b, :, t].view(np.uint16))

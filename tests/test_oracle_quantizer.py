@@ -1,0 +1,251 @@
+"""Pins of the oracle's fp16 rounding, group quantizer and packed layout.
+
+Each check ties the oracle to something other than itself: torch's and numpy's
+own fp16 conversions, examples worked out by hand from the KV1 model card's
+"Quantization Format" section, a brute-force nearest-grid-point search in exact
+rational arithmetic, the reconstruction bound, and the BQ2_0 code order.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_decode_attention_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ fp16 ---------
+def test_half_to_float_all_patterns(orc):
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = orc.half_bits_to_float(h)
+    ref = h.view(np.float16).astype(np.float32)
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.array_equal(ours.view(np.uint32)[~both_nan],
+                          ref.view(np.uint32)[~both_nan])
+    assert both_nan.sum() == np.isnan(ref).sum()
+
+
+def test_float_to_half_exhaustive(orc):
+    """Every fp32 bit pattern rounds like torch's (hardware F16C) conversion."""
+    torch.set_num_threads(min(8, os.cpu_count() or 1))
+    chunk = 1 << 27
+    for start in range(0, 1 << 32, chunk):
+        bits = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        x = bits.view(np.float32)
+        ours = orc.float_to_half_bits(x)
+        ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy()
+        ref = ref.view(np.uint16)
+        nan = np.isnan(x)
+        # NaN payloads are not specified; both must be NaN
+        assert np.all((ours[nan] & 0x7c00) == 0x7c00) and np.all(ours[nan] & 0x3ff)
+        bad = np.flatnonzero((ours != ref) & ~nan)
+        assert bad.size == 0, (start, hex(bits[bad[0]]), hex(ours[bad[0]]),
+                               hex(ref[bad[0]]))
+
+
+def test_float_to_half_matches_numpy_sample(orc):
+    """A second, independent library on a sample (ties, subnormals, overflow)."""
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    edge = np.array([65504, 65519.996, 65520, 2.0**-24, 2.0**-25, 3 * 2.0**-26,
+                     2.0**-14, 2.0**-14 - 2.0**-25, 1 + 2.0**-11, 1 + 3 * 2.0**-11],
+                    dtype=np.float32)
+    x = np.concatenate([x, edge, -edge])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.float_to_half_bits(x), ref)
+
+
+# ------------------------------------------------------ worked examples ----
+def _parse_value(s: str) -> float:
+    return float.fromhex(s) if "0x" in s else float(s)
+
+
+def _golden_quantizer():
+    rows = []
+    with open(os.path.join(GOLDEN, "quantizer_worked_examples.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, bits, xs, scale, mn, codes, why = [p.strip() for p in line.split("|")]
+            rows.append((name, int(bits), [_parse_value(v) for v in xs.split()],
+                         int(scale, 16), int(mn, 16), [int(c) for c in codes.split()],
+                         why))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_quantizer(), ids=lambda r: r[0])
+def test_worked_examples(orc, row):
+    name, bits, xs, scale, mn, codes, why = row
+    x = np.array(xs, dtype=np.float64)
+    assert np.array_equal(x.astype(np.float16).astype(np.float64), x), "not fp16"
+    x16 = np.array(xs, dtype=np.float16)
+    # keep the sign of -0 from the text
+    for i, s in enumerate(xs):
+        if s == 0.0 and np.signbit(s):
+            x16[i] = np.float16(-0.0)
+    d, m, c = orc.quantize_group(x16, bits)
+    assert (d, m, list(c)) == (scale, mn, codes), why
+
+
+# ---------------------------------------------------- brute force ---------
+def _half_frac(bits: int) -> Fraction:
+    return Fraction(float(np.array([bits], np.uint16).view(np.float16)[0]))
+
+
+def _check_group_brute_force(orc, x16: np.ndarray, bits: int):
+    """Checks one group against exact rational arithmetic:
+    min is the exact minimum; the scale is the fp16 rounding of the exact
+    (max-min)/(2^b-1) (up to the fp32 intermediate); each code is the index of
+    the nearest grid point min + k*scale, ties to even k, except where the exact
+    quotient lies within 2^-18 of a half-integer (fp32 rounding may then pick the
+    other neighbour)."""
+    levels = (1 << bits) - 1
+    d, m, codes = orc.quantize_group(x16, bits)
+    xs = [Fraction(float(v)) for v in x16.astype(np.float32)]
+    mn, mx = min(xs), max(xs)
+    assert _half_frac(m) == mn
+    assert (m & 0x8000) == 0 or mn != 0
+    dq = _half_frac(d)
+    exact = (mx - mn) / levels
+    # the fp16 neighbours of the exact scale
+    if exact == 0:
+        assert d == 0
+    else:
+        e = float(exact)
+        lo = np.float16(e)
+        cands = {float(lo), float(np.nextafter(lo, np.float16(np.inf))),
+                 float(np.nextafter(lo, np.float16(0)))}
+        assert float(dq) in cands
+        # nearest one, unless the exact value is within an fp32 ulp of a midpoint
+        best = min(cands, key=lambda c: abs(Fraction(c) - exact))
+        if float(dq) != best:
+            mid = (Fraction(float(dq)) + Fraction(best)) / 2
+            assert abs(mid - exact) <= exact * Fraction(1, 1 << 23)
+    for xv, code in zip(xs, codes):
+        assert 0 <= code <= levels
+        if dq == 0:
+            assert code == 0
+            continue
+        y = (xv - mn) / dq
+        k = int(np.floor(float(y)))
+        frac = y - k
+        if frac > Fraction(1, 2):
+            near = k + 1
+        elif frac < Fraction(1, 2):
+            near = k
+        else:
+            near = k + (k % 2)
+        near = min(max(near, 0), levels)
+        if code != near:
+            assert abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 18), (xv, y, code)
+            assert abs(code - near) == 1
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_brute_force_synthetic_groups(orc, bits):
+    w = synth.WORKLOADS[3]
+    k = synth.keys(w, 64, batch=1)           # [1][8][64][128]
+    v = synth.values(w, 2, batch=1)
+    rng = np.random.default_rng(7)
+    groups = [k[0, h, :32, c] for h in range(2) for c in range(0, 128, 3)]
+    groups += [v[0, h, t, g * 32:(g + 1) * 32] for h in range(8) for t in range(2)
+               for g in range(4)]
+    # wide dynamic range and subnormal groups
+    for scale in [1e-7, 1e-5, 1e-3, 1.0, 100.0, 3e4]:
+        groups.append((rng.standard_normal(32) * scale).astype(np.float16))
+    groups.append(rng.integers(0, 12, size=32).astype(np.float16) * np.float16(2.0**-24))
+    for gvals in groups:
+        _check_group_brute_force(orc, np.ascontiguousarray(gvals), bits)
+
+
+def test_reconstruction_bound(orc):
+    """|x - xhat| <= scale/2 + (2^b-1)|d32 - scale| (+ fp32 rounding); exact
+    minimum; constant groups exact."""
+    rng = np.random.default_rng(3)
+    for bits in (2, 4):
+        levels = (1 << bits) - 1
+        for trial in range(300):
+            n = int(rng.choice([32, 64, 128]))
+            x16 = (rng.standard_normal(n) * 10 ** rng.uniform(-6, 4)).astype(np.float16)
+            if trial % 17 == 0:
+                x16[:] = x16[0]
+            d, m, codes = orc.quantize_group(x16, bits)
+            xs = x16.astype(np.float64)
+            dq = float(_half_frac(d))
+            mq = float(_half_frac(m))
+            xhat = codes.astype(np.float64) * dq + mq
+            d32 = float(np.float32(np.float32(xs.max()) - np.float32(xs.min())) /
+                        np.float32(levels))
+            if dq == 0:
+                bound = xs.max() - xs.min()
+            else:
+                bound = dq / 2 + levels * abs(d32 - dq) + 4 * np.spacing(np.float32(np.abs(xs).max()))
+            assert np.all(np.abs(xs - xhat) <= bound + 1e-300)
+            assert xhat[np.argmin(xs)] == xs.min()  # code 0 -> exact minimum
+            if np.all(xs == xs[0]):
+                assert np.all(xhat == xs)
+
+
+# ------------------------------------------------------------ layout -------
+def _golden_layout():
+    rows = []
+    with open(os.path.join(GOLDEN, "layout_worked_examples.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            t, bits, idx, word, hexv = [p.strip() for p in line.split("|")]
+            rows.append((t, int(bits), int(idx), int(word), int(hexv, 16)))
+    return rows
+
+
+def _pattern_cache(orc, bits):
+    g = orc.Geom(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, k_bits=bits,
+                 v_bits=bits, group=32, residual=32, capacity=64)
+    cache = orc.Cache(g)
+    t = np.arange(32)[:, None]
+    c = np.arange(64)[None, :]
+    x = ((t + c) % (1 << bits)).astype(np.float16)[None, None]
+    orc.quantize_keys(g, cache, x, 0)
+    orc.quantize_values(g, cache, x, 0)
+    return cache
+
+
+@pytest.mark.parametrize("row", _golden_layout(),
+                         ids=lambda r: "%s%d_%d_%d" % r[:4])
+def test_layout_worked_examples(orc, row):
+    tensor, bits, idx, word, expect = row
+    cache = _pattern_cache(orc, bits)
+    if tensor == "k":
+        got = int(cache.k_codes[0, 0, idx, word])
+        assert np.all(cache.k_meta[0, 0, 0, :, 0] == 0x3C00)
+        assert np.all(cache.k_meta[0, 0, 0, :, 1] == 0)
+    else:
+        got = int(cache.v_codes[0, 0, 0, idx, word])
+        assert np.all(cache.v_meta[0, 0, :32, :, 0] == 0x3C00)
+    assert got == expect, hex(got)
+
+
+def test_key_row_is_a_bq2_0_code_array(orc):
+    """At D = 64 and 2 bits, a packed key row's 16 bytes are the qs[] of a BQ2_0
+    block: byte i holds codes 4i..4i+3 with the first in the lowest two bits
+    (KV1 model card, "Quantization Format: KV1.cpp BQ2_0").  The codes come
+    from the group quantizer applied to each channel on its own, so the packer
+    is checked against the page's byte order, not against itself."""
+    g = orc.Geom(1, 1, 1, 64, 2, 2, 32, 32, 32)
+    cache = orc.Cache(g)
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((1, 1, 32, 64)).astype(np.float16)
+    orc.quantize_keys(g, cache, k, 0)
+    per_channel = np.stack([orc.quantize_group(np.ascontiguousarray(k[0, 0, :, c]), 2)[2]
+                            for c in range(64)], axis=1)       # [t][c]
+    for t in range(32):
+        q = per_channel[t].astype(np.int64)
+        qs = bytes(int(q[4 * i] | q[4 * i + 1] << 2 | q[4 * i + 2] << 4 | q[4 * i + 3] << 6)
+                   for i in range(16))
+        assert cache.k_codes[0, 0, t].tobytes() == qs
