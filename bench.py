@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of libkvq on one MI355X.
+
+A step is one pass of the whole decode hot path for one attention layer over a
+batch of sequences: kvq_append (the new token; a residual flush when a window
+is full) then kvq_decode_attn (split partials + combine).  Steps rotate over
+--layers independent layer caches (default 4, about 1.1 GB for the default
+workload) so the 256 MB Infinity Cache cannot serve a layer's packed cache from
+one step to the next: the bytes come from HBM, as in a real multi-layer model.
+
+Default workload: the Llama-3-8B-shaped GQA layer (32 query / 8 KV heads,
+head_dim 128, batch 32, context 8192, 2-bit keys / 4-bit values, G = 32,
+R = 128).  512 steps = 128 tokens per layer, so every layer does exactly one
+residual flush inside the timed region.
+
+Prints one JSON line: effective HBM GB/s of the whole step (algorithmic bytes /
+time), tokens/s, the roofline of the dominant kernel (decode partial: HIP
+events around each launch on the launch stream) and the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=512)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
+    p.add_argument("--layers", type=int, default=4, help="rotating layer caches")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_quant.hip", "kvq_internal.h"):
+        with open(os.path.join(ROOT, "quantized_decode_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per decode-partial launch from committed rocprofv3 --pmc
+    summaries, if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_partial_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_seconds: float):
+    """The oracle, as it stands, on a bounded sample of the workload: the first
+    few sequences of the batch, one decode step (append + attention) repeated
+    until about target_seconds have passed."""
+    import oracle
+    from quantized_decode_attention_amd import metrics, synth
+
+    bs = min(w.batch, 4)
+    n0 = w.context - 1
+    cap = synth.capacity_for(w, 64)
+    og = oracle.Geom(bs, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k_bits, w.v_bits,
+                     w.group, w.residual, cap)
+    k = synth.keys(w, n0, batch=bs)
+    v = synth.values(w, n0, batch=bs)
+    oc = oracle.Cache(og)
+    oracle.prefill(og, oc, k, v, n0)
+    del k, v
+    scale = 1.0 / math.sqrt(w.head_dim)
+    steps, nbytes, t_total = 0, 0.0, 0.0
+    lens = np.full(bs, n0, np.int32)
+    while t_total < target_seconds and steps < 64:
+        kn, vn, q = synth.step_token(w, steps, batch=bs)
+        t0 = time.perf_counter()
+        oracle.append(og, oc, kn, vn, lens)
+        _ = oracle.decode_attn(og, oc, q, lens + 1, scale)
+        t_total += time.perf_counter() - t0
+        nbytes += metrics.decode_step_bytes(lens + 1, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                            w.k_bits, w.v_bits, w.group, w.residual)
+        nbytes += metrics.append_bytes(bs, w.n_kv_heads, w.head_dim)
+        lens += 1
+        steps += 1
+    return {
+        "value": round(nbytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(bs * steps / t_total, 3),
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"{bs} of {w.batch} sequences at context {w.context}, {steps} decode "
+                   f"steps (append + attention), {t_total:.1f} s"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode "
+                          "path has no multi-GPU part (--gpus must be 1)"}))
+        sys.exit(2)
+    import torch
+
+    import quantized_decode_attention_amd as kvq
+    from quantized_decode_attention_amd import metrics, synth
+
+    w = synth.WORKLOADS[a.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = a.layers if w.layers == 1 else w.layers
+    total_steps = a.warmup + a.steps
+    per_layer_tokens = -(-total_steps // L)
+    cap = synth.capacity_for(w, per_layer_tokens + 1)
+    g = kvq.Geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k_bits, w.v_bits,
+                 w.group, w.residual, cap)
+
+    # sequence lengths before the first warmup step: the first timed step of
+    # each layer attends over the workload's context
+    base = synth.seq_lens(w)
+    if w.ctx_range is None:
+        start = base - 1 - (a.warmup + L - 1) // L
+        if w.cfg == 5:
+            start = np.full(w.batch, w.context, np.int32)
+    else:
+        start = base - 1
+    start = np.maximum(start, 1).astype(np.int32)
+    nmax0 = int(start.max())
+
+    print(f"[bench] workload {w.name}: {L} layer caches, capacity {cap}, "
+          f"start len {int(start.min())}..{nmax0}", file=sys.stderr, flush=True)
+    caches = [kvq.Cache(g, dev) for _ in range(L)]
+    # prefill every layer from the same seeded tensors (layer 0's draw)
+    k = synth.keys(w, nmax0)
+    v = synth.values(w, nmax0)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    del k, v
+    for c in caches:
+        if np.all(start == start[0]):
+            n = int(start[0])
+            kvq.kvq_prefill(g, kd[:, :, :n].contiguous(), vd[:, :, :n].contiguous(), n, c)
+        else:
+            for b in range(w.batch):
+                n = int(start[b])
+                sub = c.view(b, b + 1)
+                kvq.kvq_prefill(sub.g, kd[b:b + 1, :, :n].contiguous(),
+                                vd[b:b + 1, :, :n].contiguous(), n, sub)
+    del kd, vd
+    torch.cuda.synchronize()
+
+    # per-step inputs (a pool of seeded tokens) and lengths, all on device
+    pool = [tuple(torch.from_numpy(x).to(dev) for x in synth.step_token(w, s)) for s in range(8)]
+    lens_host = np.zeros((total_steps, 2, w.batch), np.int32)
+    cur = [start.copy() for _ in range(L)]
+    for s in range(total_steps):
+        l = s % L
+        lens_host[s, 0] = cur[l]
+        lens_host[s, 1] = cur[l] + 1
+        cur[l] = cur[l] + 1
+    lens_dev = torch.from_numpy(lens_host).to(dev)
+    max_len = int(lens_host[:, 1].max())
+    ws = kvq.alloc_workspace(g, max_len, dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    n_split, split_tokens = kvq.kvq_decode_splits(g, max_len)
+
+    # algorithmic bytes of every step
+    step_bytes, dec_bytes = [], []
+    for s in range(total_steps):
+        before, after = lens_host[s, 0], lens_host[s, 1]
+        db = metrics.decode_step_bytes(after, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                       w.k_bits, w.v_bits, w.group, w.residual)
+        flushing = int(np.sum((before > 0) & (before % w.residual == 0)))
+        sb = db + metrics.append_bytes(w.batch, w.n_kv_heads, w.head_dim)
+        sb += metrics.flush_bytes(flushing * w.n_kv_heads, w.residual, w.head_dim,
+                                  w.k_bits, w.v_bits, w.group)
+        step_bytes.append(sb)
+        dec_bytes.append(db)
+
+    stream = torch.cuda.current_stream()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+
+    def step(s, timed_idx=None):
+        l = s % L
+        kn, vn, q = pool[s % len(pool)]
+        c = caches[l]
+        kvq.kvq_append(g, kn, vn, lens_dev[s, 0], c, stream)
+        if timed_idx is not None:
+            ev_a[timed_idx].record(stream)
+        kvq.kvq_decode_partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+        if timed_idx is not None:
+            ev_b[timed_idx].record(stream)
+        kvq.kvq_decode_combine(g, lens_dev[s, 1], max_len, ws, out, stream)
+
+    for s in range(a.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    timed = slice(a.warmup, a.warmup + a.steps)
+    total_bytes = float(np.sum(step_bytes[timed]))
+    part_ms = np.array([ev_a[i].elapsed_time(ev_b[i]) for i in range(a.steps)])
+    part_avg_s = float(np.mean(part_ms)) / 1e3
+    dec_avg_bytes = float(np.mean(dec_bytes[timed]))
+    achieved = dec_avg_bytes / part_avg_s / 1e9
+    gbs = total_bytes / elapsed / 1e9
+    traffic = load_traffic(w.name)
+
+    rec = {
+        "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak) + tokens/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed / a.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; keys with per-channel lognormal scales and outlier "
+                "channels, values and queries N(0,1), fp16)",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim, "k_bits": w.k_bits, "v_bits": w.v_bits,
+            "group": w.group, "residual": w.residual,
+            "context_first_step": int(lens_host[a.warmup, 1].max()),
+            "context_last_step": int(lens_host[-1, 1].max()),
+            "rotating_layer_caches": L, "n_split": n_split, "split_tokens": split_tokens,
+            "step": "kvq_append (+flush when a window fills) + kvq_decode_attn, one layer",
+        },
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(w.batch * a.steps / elapsed, 1),
+        "tokens_per_s_unit": "decoded tokens per second through one layer",
+        "roofline": {
+            "kernel": "decode_partial",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(part_avg_s * 1e6, 3),
+            "algorithmic_bytes_per_launch": round(dec_avg_bytes),
+        },
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,328 @@
+"""ctypes binding of libkvq (argument marshalling only).
+
+Every function here has the name of a C entry point in include/kvq.h and does
+nothing but check the torch tensors it is handed (device, dtype, contiguity,
+shape), pass their data pointers and the current HIP stream, and turn a
+non-zero status into an exception.  All computation runs in the library's HIP
+kernels; there is no fallback.  PyTorch only provides device memory and
+streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+ABI_VERSION = 1
+LAYOUT_VERSION = 1
+VBLOCK = 32
+
+# status codes (include/kvq.h)
+KVQ_OK = 0
+KVQ_ERR_NULL = -1
+KVQ_ERR_GEOM = -2
+KVQ_ERR_BITS = -3
+KVQ_ERR_ALIGN = -4
+KVQ_ERR_WORKSPACE = -5
+KVQ_ERR_RANGE = -6
+KVQ_ERR_HIP = -7
+KVQ_ERR_INTERNAL = -8
+
+EXPORTS = [
+    "kvq_abi_version", "kvq_layout_version", "kvq_status_str", "kvq_last_error",
+    "kvq_validate_geom", "kvq_cache_bytes", "kvq_decode_splits",
+    "kvq_decode_workspace_bytes", "kvq_quantize_keys_perchannel",
+    "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append",
+    "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
+]
+
+
+class kvq_geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits",
+        "group", "residual", "capacity")]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res")]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what} failed: {detail or status_str(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the in-tree libkvq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -c "
+                "'import __graft_entry__; __graft_entry__.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        G = ctypes.POINTER(kvq_geom)
+        C = ctypes.POINTER(kvq_cache)
+        sig = {
+            "kvq_abi_version": (ctypes.c_int, []),
+            "kvq_layout_version": (ctypes.c_int, []),
+            "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+            "kvq_last_error": (ctypes.c_char_p, []),
+            "kvq_validate_geom": (ctypes.c_int, [G]),
+            "kvq_cache_bytes": (ctypes.c_int, [G, ctypes.POINTER(sz)]),
+            "kvq_decode_splits": (ctypes.c_int, [G, i32, ctypes.POINTER(i32),
+                                                 ctypes.POINTER(i32)]),
+            "kvq_decode_workspace_bytes": (ctypes.c_int, [G, i32, ctypes.POINTER(sz)]),
+            "kvq_quantize_keys_perchannel": (ctypes.c_int, [G, P, i32, i32, P, P, P]),
+            "kvq_quantize_values_pertoken": (ctypes.c_int, [G, P, i32, i32, P, P, P]),
+            "kvq_prefill": (ctypes.c_int, [G, P, P, i32, C, P]),
+            "kvq_append": (ctypes.c_int, [G, P, P, P, C, P]),
+            "kvq_decode_attn": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
+            "kvq_decode_partial": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
+            "kvq_decode_combine": (ctypes.c_int, [G, P, i32, P, sz, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().kvq_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().kvq_last_error().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != KVQ_OK:
+        raise KvqError(status, what, last_error())
+
+
+@dataclass(frozen=True)
+class Geom:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    k_bits: int
+    v_bits: int
+    group: int
+    residual: int
+    capacity: int
+
+    def c(self) -> kvq_geom:
+        return kvq_geom(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                        self.k_bits, self.v_bits, self.group, self.residual,
+                        self.capacity)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_F16 = (torch.float16, torch.int16)
+_I32 = (torch.int32,)
+
+
+# ---------------------------------------------------------------- queries --
+def kvq_abi_version() -> int:
+    return lib().kvq_abi_version()
+
+
+def kvq_layout_version() -> int:
+    return lib().kvq_layout_version()
+
+
+def kvq_validate_geom(g: Geom) -> None:
+    gc = g.c()
+    _check(lib().kvq_validate_geom(ctypes.byref(gc)), "kvq_validate_geom")
+
+
+def kvq_cache_bytes(g: Geom) -> list[int]:
+    gc = g.c()
+    out = (ctypes.c_size_t * 6)()
+    _check(lib().kvq_cache_bytes(ctypes.byref(gc), out), "kvq_cache_bytes")
+    return list(out)
+
+
+def kvq_decode_splits(g: Geom, max_seq_len: int) -> tuple[int, int]:
+    gc = g.c()
+    ns, st = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().kvq_decode_splits(ctypes.byref(gc), max_seq_len, ctypes.byref(ns),
+                                   ctypes.byref(st)), "kvq_decode_splits")
+    return ns.value, st.value
+
+
+def kvq_decode_workspace_bytes(g: Geom, max_seq_len: int) -> int:
+    gc = g.c()
+    out = ctypes.c_size_t()
+    _check(lib().kvq_decode_workspace_bytes(ctypes.byref(gc), max_seq_len,
+                                            ctypes.byref(out)), "kvq_decode_workspace_bytes")
+    return out.value
+
+
+# ------------------------------------------------------------------ cache --
+class Cache:
+    """The six cache buffers of one layer as torch device tensors (allocated
+    here with torch, sized by kvq_cache_bytes, laid out as include/kvq.h
+    specifies)."""
+
+    def __init__(self, g: Geom, device="cuda"):
+        B, H, C, D = g.batch, g.n_kv_heads, g.capacity, g.head_dim
+        self.g = g
+        z = dict(device=device)
+        self.k_codes = torch.zeros((B, H, C, D * g.k_bits // 32), dtype=torch.int32, **z)
+        self.v_codes = torch.zeros((B, H, C // VBLOCK, D, g.v_bits), dtype=torch.int32, **z)
+        self.k_meta = torch.zeros((B, H, C // g.group, D, 2), dtype=torch.int16, **z)
+        self.v_meta = torch.zeros((B, H, C, D // g.group, 2), dtype=torch.int16, **z)
+        self.k_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
+        self.v_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
+        sizes = kvq_cache_bytes(g)
+        for t, s in zip(self.tensors(), sizes):
+            assert t.numel() * t.element_size() == s
+
+    def tensors(self):
+        return (self.k_codes, self.v_codes, self.k_meta, self.v_meta, self.k_res,
+                self.v_res)
+
+    def view(self, b0: int, b1: int) -> "Cache":
+        """Sequences [b0, b1) as a cache of batch b1 - b0 sharing this memory
+        (the layout is batch-major, so a batch slice is one contiguous piece)."""
+        c = Cache.__new__(Cache)
+        c.g = Geom(b1 - b0, *[getattr(self.g, f) for f in (
+            "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits", "group",
+            "residual", "capacity")])
+        for name in ("k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res"):
+            setattr(c, name, getattr(self, name)[b0:b1])
+        return c
+
+    def c(self) -> kvq_cache:
+        return kvq_cache(*[t.data_ptr() for t in self.tensors()])
+
+
+def _cache_arg(cache: Cache):
+    for t in cache.tensors():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("cache tensors must be contiguous device tensors")
+    return cache.c()
+
+
+# ------------------------------------------------------------- operations --
+def kvq_quantize_keys_perchannel(g: Geom, k: torch.Tensor, pos0: int,
+                                 k_codes: torch.Tensor, k_meta: torch.Tensor,
+                                 stream=None) -> None:
+    n_tok = k.shape[2]
+    gc = g.c()
+    _check(lib().kvq_quantize_keys_perchannel(
+        ctypes.byref(gc),
+        _ptr(k, "k", _F16, (g.batch, g.n_kv_heads, n_tok, g.head_dim)), pos0, n_tok,
+        _ptr(k_codes, "k_codes"), _ptr(k_meta, "k_meta"), _stream(stream)),
+        "kvq_quantize_keys_perchannel")
+
+
+def kvq_quantize_values_pertoken(g: Geom, v: torch.Tensor, pos0: int,
+                                 v_codes: torch.Tensor, v_meta: torch.Tensor,
+                                 stream=None) -> None:
+    n_tok = v.shape[2]
+    gc = g.c()
+    _check(lib().kvq_quantize_values_pertoken(
+        ctypes.byref(gc),
+        _ptr(v, "v", _F16, (g.batch, g.n_kv_heads, n_tok, g.head_dim)), pos0, n_tok,
+        _ptr(v_codes, "v_codes"), _ptr(v_meta, "v_meta"), _stream(stream)),
+        "kvq_quantize_values_pertoken")
+
+
+def kvq_prefill(g: Geom, k: torch.Tensor, v: torch.Tensor, n: int, cache: Cache,
+                stream=None) -> None:
+    shape = (g.batch, g.n_kv_heads, n, g.head_dim)
+    gc = g.c()
+    cc = _cache_arg(cache)
+    _check(lib().kvq_prefill(ctypes.byref(gc), _ptr(k, "k", _F16, shape),
+                             _ptr(v, "v", _F16, shape), n, ctypes.byref(cc),
+                             _stream(stream)), "kvq_prefill")
+
+
+def kvq_append(g: Geom, k_new: torch.Tensor, v_new: torch.Tensor,
+               seq_lens: torch.Tensor, cache: Cache, stream=None) -> None:
+    shape = (g.batch, g.n_kv_heads, g.head_dim)
+    gc = g.c()
+    cc = _cache_arg(cache)
+    _check(lib().kvq_append(ctypes.byref(gc), _ptr(k_new, "k_new", _F16, shape),
+                            _ptr(v_new, "v_new", _F16, shape),
+                            _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
+                            ctypes.byref(cc), _stream(stream)), "kvq_append")
+
+
+def _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out):
+    gc = g.c()
+    cc = _cache_arg(cache)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (ctypes.byref(gc),
+            _ptr(q, "q", _F16, (g.batch, g.n_q_heads, g.head_dim)),
+            ctypes.byref(cc), _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
+            int(max_seq_len), float(sm_scale), _ptr(workspace, "workspace"),
+            ws_bytes, _ptr(out, "out", _F16, (g.batch, g.n_q_heads, g.head_dim))), (gc, cc)
+
+
+def kvq_decode_attn(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,
+                    max_seq_len: int, sm_scale: float, workspace: torch.Tensor | None,
+                    out: torch.Tensor, stream=None) -> None:
+    args, keep = _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
+    _check(lib().kvq_decode_attn(*args, _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_decode_partial(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,
+                       max_seq_len: int, sm_scale: float, workspace: torch.Tensor | None,
+                       out: torch.Tensor, stream=None) -> None:
+    args, keep = _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
+    _check(lib().kvq_decode_partial(*args, _stream(stream)), "kvq_decode_partial")
+
+
+def kvq_decode_combine(g: Geom, seq_lens: torch.Tensor, max_seq_len: int,
+                       workspace: torch.Tensor | None, out: torch.Tensor,
+                       stream=None) -> None:
+    gc = g.c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvq_decode_combine(
+        ctypes.byref(gc), _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(max_seq_len),
+        _ptr(workspace, "workspace"), ws_bytes,
+        _ptr(out, "out", _F16, (g.batch, g.n_q_heads, g.head_dim)), _stream(stream)),
+        "kvq_decode_combine")
+
+
+def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:
+    n = kvq_decode_workspace_bytes(g, max_seq_len)
+    if n == 0:
+        return None
+    return torch.empty(n // 4, dtype=torch.float32, device=device)

@@ -1,0 +1,55 @@
+"""Builds libkvq.so for gfx950 with hipcc (in-tree, next to this file).
+
+Flags: every HIP translation unit is compiled without packed-fp32 ops; the
+quantizer's unit additionally with -ffp-contract=off so its fp32 steps stay
+separate IEEE operations (bit-exact codes).  No fast-math anywhere.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libkvq.so")
+BUILD = os.path.join(HERE, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+ARCH = ["--offload-arch=gfx950"]
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+          "-I" + os.path.join(HERE, "..", "include"),
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+SOURCES = {
+    "kvq_quant.hip": ["-ffp-contract=off"],
+    "kvq_decode.hip": [],
+    "kvq_api.cpp": [],
+}
+
+
+def _compile(name: str, extra: list[str]) -> str:
+    src = os.path.join(CSRC, name)
+    obj = os.path.join(BUILD, name + ".o")
+    lang = ["-x", "hip"] if name.endswith(".hip") else []
+    cmd = [HIPCC, *ARCH, *COMMON, *extra, *lang, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on " + name)
+    return obj
+
+
+def build() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

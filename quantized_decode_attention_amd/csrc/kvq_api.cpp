@@ -1,0 +1,383 @@
+// kvq_api.cpp — host side of the libkvq C ABI: argument validation, size and
+// workspace queries, split sizing, kernel launches.  Every entry point only
+// enqueues work on the caller's stream; nothing here synchronizes or allocates.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_geom(const kvq_geom* g) {
+  if (!g) return fail(KVQ_ERR_NULL, "geometry is NULL");
+  if (g->k_bits != 2 && g->k_bits != 4)
+    return fail(KVQ_ERR_BITS, "k_bits must be 2 or 4 (got %d)", g->k_bits);
+  if (g->v_bits != 2 && g->v_bits != 4)
+    return fail(KVQ_ERR_BITS, "v_bits must be 2 or 4 (got %d)", g->v_bits);
+  if (g->batch < 1 || g->n_kv_heads < 1 || g->n_q_heads < 1)
+    return fail(KVQ_ERR_GEOM, "batch and head counts must be >= 1");
+  if (g->n_q_heads % g->n_kv_heads != 0)
+    return fail(KVQ_ERR_GEOM, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                g->n_q_heads, g->n_kv_heads);
+  const int gq = g->n_q_heads / g->n_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+    return fail(KVQ_ERR_GEOM, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", gq);
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(KVQ_ERR_GEOM, "head_dim must be 64 or 128 (got %d)", g->head_dim);
+  if (g->group != 32 && g->group != 64 && g->group != 128)
+    return fail(KVQ_ERR_GEOM, "group must be 32, 64 or 128 (got %d)", g->group);
+  if (g->group > g->head_dim || g->head_dim % g->group != 0)
+    return fail(KVQ_ERR_GEOM, "group (%d) must divide head_dim (%d)", g->group, g->head_dim);
+  if (g->residual < g->group || g->residual % g->group != 0)
+    return fail(KVQ_ERR_GEOM, "residual (%d) must be a positive multiple of group (%d)",
+                g->residual, g->group);
+  if (g->capacity < g->residual || g->capacity % g->residual != 0 || g->capacity > (1 << 24))
+    return fail(KVQ_ERR_GEOM, "capacity (%d) must be a multiple of residual (%d), <= 2^24",
+                g->capacity, g->residual);
+  return KVQ_OK;
+}
+
+int check_cache(const kvq_cache* c) {
+  if (!c) return fail(KVQ_ERR_NULL, "cache is NULL");
+  const void* p[6] = {c->k_codes, c->v_codes, c->k_meta, c->v_meta, c->k_res, c->v_res};
+  static const char* names[6] = {"k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res"};
+  for (int i = 0; i < 6; ++i) {
+    if (!p[i]) return fail(KVQ_ERR_NULL, "cache.%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(KVQ_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  return KVQ_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(KVQ_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(KVQ_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return KVQ_OK;
+}
+
+int packed_len(int n, int R) { return n <= 0 ? 0 : n - (((n - 1) % R) + 1); }
+
+// Compute units of the current device, cached per device.
+int cu_count(int* out) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return KVQ_OK;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  *out = cus;
+  return KVQ_OK;
+}
+
+// Split sizing: about four workgroups per compute unit over all (sequence, KV
+// head) units, at least 256 tokens per split, a multiple of the key group so
+// no key group straddles two splits.
+int splits_for(const kvq_geom* g, int32_t max_seq_len, int32_t* n_split,
+               int32_t* split_tokens) {
+  if (max_seq_len < 1 || max_seq_len > g->capacity)
+    return fail(KVQ_ERR_RANGE, "max_seq_len (%d) must be in [1, capacity=%d]",
+                max_seq_len, g->capacity);
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != KVQ_OK) return st;
+  const int64_t units = (int64_t)g->batch * g->n_kv_heads;
+  const int64_t target = 4 * (int64_t)cus;
+  int64_t tokens = ((int64_t)max_seq_len * units + target - 1) / target;
+  if (tokens < 256) tokens = 256;
+  const int64_t q = g->group;
+  tokens = (tokens + q - 1) / q * q;
+  if (tokens > max_seq_len) tokens = ((int64_t)max_seq_len + q - 1) / q * q;
+  *split_tokens = (int32_t)tokens;
+  *n_split = (int32_t)(((int64_t)max_seq_len + tokens - 1) / tokens);
+  return KVQ_OK;
+}
+
+int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
+                 const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                 void* workspace, size_t workspace_bytes, uint16_t* out,
+                 kvq::DecodeLaunch* L) {
+  int st = check_geom(geom);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if ((st = check_ptr(q, "q")) != KVQ_OK) return st;
+  if ((st = check_ptr(seq_lens, "seq_lens")) != KVQ_OK) return st;
+  if ((st = check_ptr(out, "out")) != KVQ_OK) return st;
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_huge_valf() ||
+      sm_scale == -__builtin_huge_valf())
+    return fail(KVQ_ERR_RANGE, "sm_scale must be finite");
+  int32_t n_split = 0, split_tokens = 0;
+  if ((st = splits_for(geom, max_seq_len, &n_split, &split_tokens)) != KVQ_OK) return st;
+  const size_t need = n_split > 1 ? (size_t)geom->batch * geom->n_q_heads * n_split *
+                                        (geom->head_dim + 2) * sizeof(float)
+                                  : 0;
+  if (need > 0) {
+    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  L->g = kvq::to_geom(*geom);
+  L->q = q;
+  L->cache = *cache;
+  L->seq_lens = seq_lens;
+  L->max_seq_len = max_seq_len;
+  L->n_split = n_split;
+  L->split_tokens = split_tokens;
+  L->scale_log2 = sm_scale * 1.4426950408889634f;
+  L->ws = static_cast<float*>(workspace);
+  L->out = out;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+int kvq_layout_version(void) { return KVQ_LAYOUT_VERSION; }
+
+const char* kvq_status_str(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer";
+    case KVQ_ERR_GEOM: return "invalid geometry";
+    case KVQ_ERR_BITS: return "unsupported bit width";
+    case KVQ_ERR_ALIGN: return "misaligned pointer";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_RANGE: return "argument out of range";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    case KVQ_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+int kvq_validate_geom(const kvq_geom* geom) {
+  try {
+    return check_geom(geom);
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_cache_bytes(const kvq_geom* geom, size_t out[6]) {
+  int st = check_geom(geom);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
+  const size_t B = geom->batch, H = geom->n_kv_heads, C = geom->capacity,
+               D = geom->head_dim, G = geom->group, R = geom->residual;
+  out[0] = B * H * C * (D * geom->k_bits / 32) * 4;               // k_codes
+  out[1] = B * H * (C / KVQ_VBLOCK) * D * geom->v_bits * 4;      // v_codes
+  out[2] = B * H * (C / G) * D * 2 * 2;                          // k_meta
+  out[3] = B * H * C * (D / G) * 2 * 2;                          // v_meta
+  out[4] = B * H * R * D * 2;                                    // k_res
+  out[5] = B * H * R * D * 2;                                    // v_res
+  return KVQ_OK;
+}
+
+int kvq_decode_splits(const kvq_geom* geom, int32_t max_seq_len, int32_t* n_split,
+                      int32_t* split_tokens) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!n_split || !split_tokens) return fail(KVQ_ERR_NULL, "output pointer is NULL");
+    return splits_for(geom, max_seq_len, n_split, split_tokens);
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_decode_workspace_bytes(const kvq_geom* geom, int32_t max_seq_len, size_t* bytes) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+    int32_t ns = 0, tok = 0;
+    if ((st = splits_for(geom, max_seq_len, &ns, &tok)) != KVQ_OK) return st;
+    *bytes = ns > 1 ? (size_t)geom->batch * geom->n_q_heads * ns * (geom->head_dim + 2) *
+                          sizeof(float)
+                    : 0;
+    return KVQ_OK;
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_quantize_keys_perchannel(const kvq_geom* geom, const uint16_t* k, int32_t pos0,
+                                 int32_t n_tok, uint32_t* k_codes, uint16_t* k_meta,
+                                 void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_ptr(k, "k")) != KVQ_OK) return st;
+    if ((st = check_ptr(k_codes, "k_codes")) != KVQ_OK) return st;
+    if ((st = check_ptr(k_meta, "k_meta")) != KVQ_OK) return st;
+    if (pos0 < 0 || n_tok < 0 || pos0 % geom->group || n_tok % geom->group ||
+        (int64_t)pos0 + n_tok > geom->capacity)
+      return fail(KVQ_ERR_RANGE, "pos0=%d n_tok=%d: need multiples of group=%d within capacity=%d",
+                  pos0, n_tok, geom->group, geom->capacity);
+    const kvq::Geom g = kvq::to_geom(*geom);
+    hipError_t e = kvq::launch_quantize_keys(g, k, (int64_t)n_tok * g.D, pos0, n_tok, k_codes,
+                                             k_meta, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "quantize_keys launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_quantize_values_pertoken(const kvq_geom* geom, const uint16_t* v, int32_t pos0,
+                                 int32_t n_tok, uint32_t* v_codes, uint16_t* v_meta,
+                                 void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_ptr(v, "v")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_codes, "v_codes")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_meta, "v_meta")) != KVQ_OK) return st;
+    if (pos0 < 0 || n_tok < 0 || pos0 % geom->group || n_tok % geom->group ||
+        pos0 % KVQ_VBLOCK || n_tok % KVQ_VBLOCK || (int64_t)pos0 + n_tok > geom->capacity)
+      return fail(KVQ_ERR_RANGE, "pos0=%d n_tok=%d: need multiples of group=%d and 32 within capacity=%d",
+                  pos0, n_tok, geom->group, geom->capacity);
+    const kvq::Geom g = kvq::to_geom(*geom);
+    hipError_t e = kvq::launch_quantize_values(g, v, (int64_t)n_tok * g.D, pos0, n_tok,
+                                               v_codes, v_meta, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "quantize_values launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_prefill(const kvq_geom* geom, const uint16_t* k, const uint16_t* v, int32_t n,
+                const kvq_cache* cache, void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(cache)) != KVQ_OK) return st;
+    if (n < 0 || n > geom->capacity)
+      return fail(KVQ_ERR_RANGE, "n=%d must be in [0, capacity=%d]", n, geom->capacity);
+    if (n == 0) return KVQ_OK;
+    if ((st = check_ptr(k, "k")) != KVQ_OK) return st;
+    if ((st = check_ptr(v, "v")) != KVQ_OK) return st;
+    const kvq::Geom g = kvq::to_geom(*geom);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int lq = packed_len(n, g.R);
+    const int64_t stride = (int64_t)n * g.D;
+    hipError_t e = kvq::launch_quantize_keys(g, k, stride, 0, lq, cache->k_codes, cache->k_meta, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill quantize_keys launch");
+    e = kvq::launch_quantize_values(g, v, stride, 0, lq, cache->v_codes, cache->v_meta, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill quantize_values launch");
+    e = kvq::launch_residual_copy(g, k + (int64_t)lq * g.D, v + (int64_t)lq * g.D, stride, lq,
+                                  n - lq, cache->k_res, cache->v_res, s);
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "prefill residual copy launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_append(const kvq_geom* geom, const uint16_t* k_new, const uint16_t* v_new,
+               const int32_t* seq_lens, const kvq_cache* cache, void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(cache)) != KVQ_OK) return st;
+    if ((st = check_ptr(k_new, "k_new")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_new, "v_new")) != KVQ_OK) return st;
+    if ((st = check_ptr(seq_lens, "seq_lens")) != KVQ_OK) return st;
+    hipError_t e = kvq::launch_append(kvq::to_geom(*geom), k_new, v_new, seq_lens, *cache,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "append launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_decode_partial(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
+                       const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                       void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
+  try {
+    kvq::DecodeLaunch L;
+    int st = decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                          workspace_bytes, out, &L);
+    if (st != KVQ_OK) return st;
+    hipError_t e = kvq::launch_decode_partial(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_partial launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_decode_combine(const kvq_geom* geom, const int32_t* seq_lens, int32_t max_seq_len,
+                       const void* workspace, size_t workspace_bytes, uint16_t* out,
+                       void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_ptr(seq_lens, "seq_lens")) != KVQ_OK) return st;
+    if ((st = check_ptr(out, "out")) != KVQ_OK) return st;
+    int32_t n_split = 0, split_tokens = 0;
+    if ((st = splits_for(geom, max_seq_len, &n_split, &split_tokens)) != KVQ_OK) return st;
+    if (n_split == 1) return KVQ_OK;
+    const size_t need = (size_t)geom->batch * geom->n_q_heads * n_split *
+                        (geom->head_dim + 2) * sizeof(float);
+    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    kvq::DecodeLaunch L{};
+    L.g = kvq::to_geom(*geom);
+    L.seq_lens = seq_lens;
+    L.max_seq_len = max_seq_len;
+    L.n_split = n_split;
+    L.split_tokens = split_tokens;
+    L.ws = const_cast<float*>(static_cast<const float*>(workspace));
+    L.out = out;
+    hipError_t e = kvq::launch_decode_combine(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
+                    const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                    void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
+  int st = kvq_decode_partial(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                              workspace_bytes, out, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_decode_combine(geom, seq_lens, max_seq_len, workspace, workspace_bytes, out,
+                            stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// kvq_internal.h — device helpers and launch declarations shared by the libkvq
+// translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kThreads = 256;   // threads per workgroup of every kernel
+constexpr int kVBlock = KVQ_VBLOCK;
+
+// fp16 bits -> fp32 (exact widening).
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+// Geometry as kernels see it (validated on the host).
+struct Geom {
+  int B, Hq, Hkv, D, bK, bV, G, R, C;
+};
+
+inline Geom to_geom(const kvq_geom& g) {
+  return Geom{g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, g.k_bits,
+              g.v_bits, g.group, g.residual, g.capacity};
+}
+
+// 64-bit element offsets into the cache buffers.
+__host__ __device__ inline int64_t kcodes_words(const Geom& g) {
+  return (int64_t)g.D * g.bK / 32;
+}
+
+// ---- launchers (defined in the .hip files; all enqueue only) -------------
+hipError_t launch_quantize_keys(const Geom& g, const uint16_t* src,
+                                int64_t src_unit_stride, int32_t pos0,
+                                int32_t n_tok, uint32_t* k_codes,
+                                uint16_t* k_meta, hipStream_t st);
+hipError_t launch_quantize_values(const Geom& g, const uint16_t* src,
+                                  int64_t src_unit_stride, int32_t pos0,
+                                  int32_t n_tok, uint32_t* v_codes,
+                                  uint16_t* v_meta, hipStream_t st);
+hipError_t launch_residual_copy(const Geom& g, const uint16_t* k,
+                                const uint16_t* v, int64_t src_unit_stride,
+                                int32_t pos0, int32_t n_tok, uint16_t* k_res,
+                                uint16_t* v_res, hipStream_t st);
+hipError_t launch_append(const Geom& g, const uint16_t* k_new,
+                         const uint16_t* v_new, const int32_t* seq_lens,
+                         const kvq_cache& cache, hipStream_t st);
+
+struct DecodeLaunch {
+  Geom g;
+  const uint16_t* q;
+  kvq_cache cache;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t n_split;
+  int32_t split_tokens;
+  float scale_log2;  // sm_scale * log2(e)
+  float* ws;         // partials [B][Hq][n_split][D + 2] (n_split > 1)
+  uint16_t* out;     // [B][Hq][D]
+};
+hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st);
+
+}  // namespace kvq

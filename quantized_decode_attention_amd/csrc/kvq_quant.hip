@@ -1,0 +1,280 @@
+// kvq_quant.hip — group quantization into the packed layout, residual append
+// with lazy flush, and the prefill residual copy (gfx950).
+//
+// The group quantizer follows the "Quantization Format: KV1.cpp BQ2_0" section
+// of the KV1-1.2B model card (affine codes, scale = (max - min) / (2^b - 1) in
+// fp32, scale and min rounded to fp16 and those rounded values used for the
+// codes, round half to even, clamp), generalised from 2 to b bits.  Keys are
+// grouped per channel over G tokens and values per token over G channels, as
+// the KIVI repository page ("core capabilities", "Overview") describes.
+//
+// Bit-exactness: this file is compiled with -ffp-contract=off and without
+// fast-math; '/' on float is the correctly rounded IEEE division, rintf is
+// v_rndne_f32 (ties to even) and the fp16 conversion rounds to nearest even.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kMaxG = 128;
+constexpr int kMaxD = 128;
+
+// Scale and min of one group from its fp32 min and max.
+struct GroupParams {
+  uint16_t d16, m16;
+  float scale, minv;
+};
+
+__device__ __forceinline__ GroupParams group_params(float mn, float mx,
+                                                    int bits) {
+  // a zero min or max is taken as +0 so the stored bits do not depend on the
+  // order in which -0 and +0 were seen
+  mn = (mn == 0.0f) ? 0.0f : mn;
+  mx = (mx == 0.0f) ? 0.0f : mx;
+  const float levels = (float)((1 << bits) - 1);
+  const float range = mx - mn;      // IEEE fp32 subtract
+  const float d32 = range / levels;  // IEEE fp32 divide
+  GroupParams p;
+  p.d16 = f2h(d32);
+  if ((p.d16 & 0x7fffu) == 0) p.d16 = 0;
+  p.m16 = f2h(mn);
+  p.scale = h2f(p.d16);
+  p.minv = h2f(p.m16);
+  return p;
+}
+
+__device__ __forceinline__ uint32_t group_code(float x, const GroupParams& p,
+                                               int bits) {
+  if (p.scale == 0.0f) return 0u;
+  const float y = (x - p.minv) / p.scale;  // fp32 subtract, IEEE divide
+  float r = rintf(y);                      // round half to even
+  const float levels = (float)((1 << bits) - 1);
+  r = fminf(fmaxf(r, 0.0f), levels);
+  return (uint32_t)r;
+}
+
+// Loads n_halves fp16 values (a multiple of 8, 16-byte aligned) into LDS.
+__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* src,
+                                          int n_halves) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(tile);
+  for (int i = threadIdx.x; i < n_halves / 8; i += blockDim.x) d[i] = s[i];
+}
+
+// One key group: G token rows of D channels at `src` (row-major), first
+// position `pos` (a multiple of G).  Per channel: min/max over the G tokens.
+template <int BITS>
+__device__ void key_group(const Geom& g, const uint16_t* src, int64_t unit,
+                          int32_t pos, uint32_t* k_codes, uint16_t* k_meta,
+                          uint16_t* tile, uint8_t* codes) {
+  const int G = g.G, D = g.D;
+  load_tile(tile, src, G * D);
+  __syncthreads();
+  uint32_t* meta32 = reinterpret_cast<uint32_t*>(k_meta);
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float mn = h2f(tile[c]), mx = mn;
+    for (int t = 1; t < G; ++t) {
+      const float v = h2f(tile[t * D + c]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    const GroupParams p = group_params(mn, mx, BITS);
+    meta32[(unit * (g.C / G) + pos / G) * D + c] =
+        (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
+    for (int t = 0; t < G; ++t)
+      codes[t * D + c] = (uint8_t)group_code(h2f(tile[t * D + c]), p, BITS);
+  }
+  __syncthreads();
+  constexpr int kPer = 32 / BITS;  // codes per word
+  const int W = D * BITS / 32;     // words per token row
+  uint32_t* rows = k_codes + (unit * g.C + pos) * W;
+  for (int i = threadIdx.x; i < G * W; i += blockDim.x) {
+    const int t = i / W, w = i % W;
+    const uint8_t* cc = codes + t * D + w * kPer;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) word |= (uint32_t)cc[k] << (k * BITS);
+    rows[i] = word;
+  }
+  __syncthreads();  // tile/codes are reused by the caller
+}
+
+// One 32-token value block: token rows at `src`, first position `pos` (a
+// multiple of 32).  Per token: D/G groups of G consecutive channels.
+template <int BITS>
+__device__ void value_block(const Geom& g, const uint16_t* src, int64_t unit,
+                            int32_t pos, uint32_t* v_codes, uint16_t* v_meta,
+                            uint16_t* tile, uint8_t* codes) {
+  const int G = g.G, D = g.D, NG = D / G;
+  load_tile(tile, src, kVBlock * D);
+  __syncthreads();
+  uint32_t* meta32 = reinterpret_cast<uint32_t*>(v_meta);
+  for (int i = threadIdx.x; i < kVBlock * NG; i += blockDim.x) {
+    const int t = i / NG, gm = i % NG;
+    const uint16_t* row = tile + t * D + gm * G;
+    float mn = h2f(row[0]), mx = mn;
+    for (int c = 1; c < G; ++c) {
+      const float v = h2f(row[c]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    const GroupParams p = group_params(mn, mx, BITS);
+    meta32[(unit * g.C + pos + t) * NG + gm] =
+        (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
+    for (int c = 0; c < G; ++c)
+      codes[t * D + gm * G + c] = (uint8_t)group_code(h2f(row[c]), p, BITS);
+  }
+  __syncthreads();
+  constexpr int kPer = 32 / BITS;  // tokens per word
+  uint32_t* blk = v_codes + ((unit * (g.C / kVBlock) + pos / kVBlock) * D) * BITS;
+  for (int i = threadIdx.x; i < D * BITS; i += blockDim.x) {
+    const int c = i / BITS, w = i % BITS;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      word |= (uint32_t)codes[(w * kPer + k) * D + c] << (k * BITS);
+    blk[i] = word;
+  }
+  __syncthreads();
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_keys_kernel(
+    Geom g, const uint16_t* __restrict__ src, int64_t src_unit_stride,
+    int32_t pos0, uint32_t* __restrict__ k_codes, uint16_t* __restrict__ k_meta) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kMaxG * kMaxD];
+  __shared__ uint8_t codes[kMaxG * kMaxD];
+  const int64_t unit = (int64_t)blockIdx.z * g.Hkv + blockIdx.y;
+  const int j = blockIdx.x;
+  key_group<BITS>(g, src + unit * src_unit_stride + (int64_t)j * g.G * g.D,
+                  unit, pos0 + j * g.G, k_codes, k_meta, tile, codes);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_values_kernel(
+    Geom g, const uint16_t* __restrict__ src, int64_t src_unit_stride,
+    int32_t pos0, uint32_t* __restrict__ v_codes, uint16_t* __restrict__ v_meta) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kVBlock * kMaxD];
+  __shared__ uint8_t codes[kVBlock * kMaxD];
+  const int64_t unit = (int64_t)blockIdx.z * g.Hkv + blockIdx.y;
+  const int blk = blockIdx.x;
+  value_block<BITS>(g, src + unit * src_unit_stride + (int64_t)blk * kVBlock * g.D,
+                    unit, pos0 + blk * kVBlock, v_codes, v_meta, tile, codes);
+}
+
+// Copies positions [pos0, pos0 + n_tok) of k and v ([unit][.][D] with the given
+// unit stride, first row = position pos0) to residual slots p % R.
+__global__ __launch_bounds__(kThreads) void residual_copy_kernel(
+    Geom g, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int64_t src_unit_stride, int32_t pos0, int32_t n_tok,
+    uint16_t* __restrict__ k_res, uint16_t* __restrict__ v_res) {
+  const int64_t vecs_per_row = g.D / 8;
+  const int64_t total = (int64_t)g.B * g.Hkv * n_tok * vecs_per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i % vecs_per_row;
+    const int64_t t = (i / vecs_per_row) % n_tok;
+    const int64_t unit = i / (vecs_per_row * n_tok);
+    const int64_t slot = (pos0 + t) % g.R;
+    const int64_t s = unit * src_unit_stride / 8 + t * vecs_per_row + e;
+    const int64_t d = (unit * g.R + slot) * vecs_per_row + e;
+    reinterpret_cast<uint4*>(k_res)[d] = reinterpret_cast<const uint4*>(k)[s];
+    reinterpret_cast<uint4*>(v_res)[d] = reinterpret_cast<const uint4*>(v)[s];
+  }
+}
+
+// One workgroup per (KV head, sequence).  Lazy flush, then the residual write.
+template <int BK, int BV>
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    Geom g, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ seq_lens, uint32_t* __restrict__ k_codes,
+    uint32_t* __restrict__ v_codes, uint16_t* __restrict__ k_meta,
+    uint16_t* __restrict__ v_meta, uint16_t* __restrict__ k_res,
+    uint16_t* __restrict__ v_res) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kMaxG * kMaxD];
+  __shared__ uint8_t codes[kMaxG * kMaxD];
+  const int b = blockIdx.y;
+  const int64_t unit = (int64_t)b * g.Hkv + blockIdx.x;
+  const int32_t n = seq_lens[b];
+  if (n < 0 || n >= g.C) return;  // caller error: leave the cache untouched
+  uint16_t* kr = k_res + unit * g.R * g.D;
+  uint16_t* vr = v_res + unit * g.R * g.D;
+  if (n > 0 && n % g.R == 0) {
+    // slots 0..R-1 hold positions n-R .. n-1 in order
+    for (int j = 0; j < g.R / g.G; ++j)
+      key_group<BK>(g, kr + (int64_t)j * g.G * g.D, unit, n - g.R + j * g.G,
+                    k_codes, k_meta, tile, codes);
+    for (int blk = 0; blk < g.R / kVBlock; ++blk)
+      value_block<BV>(g, vr + (int64_t)blk * kVBlock * g.D, unit,
+                      n - g.R + blk * kVBlock, v_codes, v_meta, tile, codes);
+    // every read of the window happened before the barriers in the helpers
+  }
+  const int64_t slot = n % g.R;
+  for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
+    kr[slot * g.D + c] = k_new[unit * g.D + c];
+    vr[slot * g.D + c] = v_new[unit * g.D + c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_keys(const Geom& g, const uint16_t* src,
+                                int64_t src_unit_stride, int32_t pos0,
+                                int32_t n_tok, uint32_t* k_codes,
+                                uint16_t* k_meta, hipStream_t st) {
+  if (n_tok == 0) return hipSuccess;
+  dim3 grid(n_tok / g.G, g.Hkv, g.B);
+  if (g.bK == 2)
+    quantize_keys_kernel<2><<<grid, kThreads, 0, st>>>(g, src, src_unit_stride,
+                                                        pos0, k_codes, k_meta);
+  else
+    quantize_keys_kernel<4><<<grid, kThreads, 0, st>>>(g, src, src_unit_stride,
+                                                        pos0, k_codes, k_meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_values(const Geom& g, const uint16_t* src,
+                                  int64_t src_unit_stride, int32_t pos0,
+                                  int32_t n_tok, uint32_t* v_codes,
+                                  uint16_t* v_meta, hipStream_t st) {
+  if (n_tok == 0) return hipSuccess;
+  dim3 grid(n_tok / kVBlock, g.Hkv, g.B);
+  if (g.bV == 2)
+    quantize_values_kernel<2><<<grid, kThreads, 0, st>>>(
+        g, src, src_unit_stride, pos0, v_codes, v_meta);
+  else
+    quantize_values_kernel<4><<<grid, kThreads, 0, st>>>(
+        g, src, src_unit_stride, pos0, v_codes, v_meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_copy(const Geom& g, const uint16_t* k,
+                                const uint16_t* v, int64_t src_unit_stride,
+                                int32_t pos0, int32_t n_tok, uint16_t* k_res,
+                                uint16_t* v_res, hipStream_t st) {
+  if (n_tok == 0) return hipSuccess;
+  const int64_t total = (int64_t)g.B * g.Hkv * n_tok * (g.D / 8);
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+  residual_copy_kernel<<<grid, kThreads, 0, st>>>(g, k, v, src_unit_stride,
+                                                  pos0, n_tok, k_res, v_res);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Geom& g, const uint16_t* k_new,
+                         const uint16_t* v_new, const int32_t* seq_lens,
+                         const kvq_cache& c, hipStream_t st) {
+  dim3 grid(g.Hkv, g.B);
+#define KVQ_APPEND(BK, BV)                                                    \
+  append_kernel<BK, BV><<<grid, kThreads, 0, st>>>(                           \
+      g, k_new, v_new, seq_lens, c.k_codes, c.v_codes, c.k_meta, c.v_meta,    \
+      c.k_res, c.v_res)
+  if (g.bK == 2 && g.bV == 2) KVQ_APPEND(2, 2);
+  else if (g.bK == 2 && g.bV == 4) KVQ_APPEND(2, 4);
+  else if (g.bK == 4 && g.bV == 2) KVQ_APPEND(4, 2);
+  else KVQ_APPEND(4, 4);
+#undef KVQ_APPEND
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/kvq.h declares, and
+reject invalid arguments with the documented status before any launch.  The
+byte sizes it reports are tied to the layout and to the KV1 model card's
+"Memory" table.  Calls with made-up pointers below are all invalid in some
+other argument, so none of them reaches a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_decode_attention_amd as kvq
+from quantized_decode_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_versions_and_status_strings():
+    assert kvq.kvq_abi_version() == kvq.ABI_VERSION == 1
+    assert kvq.kvq_layout_version() == kvq.LAYOUT_VERSION == 1
+    for s in range(-8, 1):
+        assert kvq.status_str(s) and kvq.status_str(s) != "unknown status"
+    assert kvq.status_str(5) == "unknown status"
+
+
+GOOD = dict(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128, k_bits=2, v_bits=4,
+            group=32, residual=128, capacity=1024)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k_bits", 3, -3), ("v_bits", 8, -3), ("batch", 0, -2), ("n_q_heads", 12, -2),
+    ("n_q_heads", 24, -2), ("head_dim", 96, -2), ("group", 16, -2), ("group", 48, -2),
+    ("residual", 48, -2), ("residual", 0, -2), ("capacity", 1000, -2),
+    ("capacity", 1 << 25, -2), ("n_kv_heads", 0, -2),
+])
+def test_geometry_validation(field, value, status):
+    kvq.kvq_validate_geom(kvq.Geom(**GOOD))
+    bad = dict(GOOD)
+    bad[field] = value
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_validate_geom(kvq.Geom(**bad))
+    assert e.value.status == status
+    assert kvq.last_error()
+
+
+def test_group_larger_than_head_dim():
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_validate_geom(kvq.Geom(**{**GOOD, "head_dim": 64, "group": 128,
+                                          "residual": 128}))
+    assert e.value.status == -2
+
+
+def test_cache_bytes_layout():
+    g = kvq.Geom(**GOOD)
+    kc, vc, km, vm, kr, vr = kvq.kvq_cache_bytes(g)
+    B, H, C, D = 2, 8, 1024, 128
+    assert kc == B * H * C * D * 2 // 8
+    assert vc == B * H * C * D * 4 // 8
+    assert km == B * H * (C // 32) * D * 4
+    assert vm == B * H * C * (D // 32) * 4
+    assert kr == vr == B * H * 128 * D * 2
+
+
+def test_cache_bytes_kv1_memory_table():
+    """At head dim 64, group 64, 2-bit keys and values, the packed part of the
+    cache for the KV1 model's 6 attention layers x 8 KV heads at 32K context is
+    the card's 60 MiB (KV1-1.2B card, "Memory"); 8K gives 15 MiB."""
+    for ctx, mib in ((32768, 60), (8192, 15)):
+        g = kvq.Geom(1, 32, 8, 64, 2, 2, 64, 64, ctx)
+        kc, vc, km, vm, kr, vr = kvq.kvq_cache_bytes(g)
+        assert 6 * (kc + vc + km + vm) == mib * 1024 * 1024
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    L = kvq.lib()
+    g = kvq.Geom(**GOOD).c()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)
+    # pos0 / n_tok not multiples of the group, or past capacity
+    assert L.kvq_quantize_keys_perchannel(ctypes.byref(g), fake, 16, 32, fake, fake, None) == -6
+    assert L.kvq_quantize_keys_perchannel(ctypes.byref(g), fake, 0, 33, fake, fake, None) == -6
+    assert L.kvq_quantize_keys_perchannel(ctypes.byref(g), fake, 1024, 32, fake, fake, None) == -6
+    assert L.kvq_quantize_values_pertoken(ctypes.byref(g), fake, -32, 32, fake, fake, None) == -6
+    # null / misaligned pointers
+    assert L.kvq_quantize_keys_perchannel(ctypes.byref(g), None, 0, 32, fake, fake, None) == -1
+    assert L.kvq_quantize_keys_perchannel(ctypes.byref(g), odd, 0, 32, fake, fake, None) == -4
+    c = _lib.kvq_cache(0x10000, 0x10000, 0x10000, None, 0x10000, 0x10000)
+    assert L.kvq_append(ctypes.byref(g), fake, fake, fake, ctypes.byref(c), None) == -1
+    c = _lib.kvq_cache(0x10000, 0x10000, 0x10008, 0x10000, 0x10000, 0x10000)
+    assert L.kvq_append(ctypes.byref(g), fake, fake, fake, ctypes.byref(c), None) == -4
+    assert "k_meta" in kvq.last_error()
+    # prefill length out of range
+    c = _lib.kvq_cache(*([0x10000] * 6))
+    assert L.kvq_prefill(ctypes.byref(g), fake, fake, 1025, ctypes.byref(c), None) == -6
+    # bad geometry is reported first
+    bad = kvq.Geom(**{**GOOD, "k_bits": 3}).c()
+    assert L.kvq_decode_attn(ctypes.byref(bad), fake, ctypes.byref(c), fake, 8, 0.1,
+                             None, 0, fake, None) == -3
+    # non-finite scale
+    assert L.kvq_decode_attn(ctypes.byref(g), fake, ctypes.byref(c), fake, 8,
+                             float("nan"), None, 0, fake, None) == -6
+    assert L.kvq_cache_bytes(None, None) == -1
