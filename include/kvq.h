@@ -77,8 +77,9 @@
  *            inside a block: word w of channel c in block k holds tokens
  *            32k + tau with (tau*bV)/32 == w, token tau in bits
  *            ((tau*bV) % 32) .. +bV-1 (lowest token in the lowest bits).
- *   v_meta   uint16 [B][Hkv][C][D/G][2]           fp16 (scale, min) of token t,
- *            channel group gamma = channels [gamma*G, gamma*G+G).
+ *   v_meta   uint16 [B][Hkv][C/32][D/G][32][2]    fp16 (scale, min) of token t,
+ *            channel group gamma = channels [gamma*G, gamma*G+G), stored in
+ *            32-token blocks: block t/32, then gamma, then token t % 32.
  *   k_res,   uint16 [B][Hkv][R][D]                fp16 residual window; position
  *   v_res                                         p lives in slot p % R.
  *
@@ -105,7 +106,8 @@
  *   the calling thread.  Device data (seq_lens values) cannot be checked on the
  *   host: out-of-range lengths are clamped inside the kernels so that no access
  *   leaves the buffers, and the affected outputs are documented per call.
- * Alignment: every device pointer must be 16-byte aligned (KVQ_ERR_ALIGN).
+ * Alignment: every device pointer must be 16-byte aligned, except seq_lens
+ *   (4-byte aligned) (KVQ_ERR_ALIGN).
  * Thread safety: calls may be made from several host threads; calls whose
  *   device work overlaps on the same buffers race, as any kernels would.
  */
@@ -184,8 +186,9 @@ int kvq_cache_bytes(const kvq_geom *geom, size_t out[6]);
 int kvq_decode_splits(const kvq_geom *geom, int32_t max_seq_len,
                       int32_t *n_split, int32_t *split_tokens);
 
-/* Workspace bytes kvq_decode_attn needs for max_seq_len (0 when one split
- * covers every sequence). */
+/* Workspace bytes kvq_decode_attn needs for max_seq_len: fp32 partials
+ * [B][Hq][n_split + 1][head_dim + 2] (one per split of the packed tokens and
+ * one for the residual window). */
 int kvq_decode_workspace_bytes(const kvq_geom *geom, int32_t max_seq_len,
                                size_t *bytes);
 
@@ -208,8 +211,8 @@ int kvq_quantize_keys_perchannel(const kvq_geom *geom, const uint16_t *k,
  * capabilities and Overview: values per token).
  *   v       device fp16 [B][Hkv][n_tok][D].
  *   pos0, n_tok: multiples of KVQ_VBLOCK (32) and of G; pos0+n_tok <= capacity.
- *   v_codes blocks [pos0/32, (pos0+n_tok)/32) and v_meta rows [pos0, pos0+n_tok)
- *   are written, nothing else. */
+ *   v_codes and v_meta blocks [pos0/32, (pos0+n_tok)/32) are written, nothing
+ *   else. */
 int kvq_quantize_values_pertoken(const kvq_geom *geom, const uint16_t *v,
                                  int32_t pos0, int32_t n_tok,
                                  uint32_t *v_codes, uint16_t *v_meta,
@@ -250,8 +253,8 @@ int kvq_append(const kvq_geom *geom, const uint16_t *k_new,
  *               1 <= max_seq_len <= capacity.  Sizes the grid and workspace.
  *   sm_scale    softmax scale (1/sqrt(D) for standard attention).
  *   workspace   device memory of at least kvq_decode_workspace_bytes(geom,
- *               max_seq_len) bytes (may be NULL when that is 0); contents on
- *               entry do not matter; overwritten.
+ *               max_seq_len) bytes, 16-byte aligned; contents on entry do not
+ *               matter; overwritten.
  *   out         device fp16 [B][Hq][D].
  * A sequence with seq_lens[b] == 0 gets out = 0.  A sequence whose length is
  * negative or above max_seq_len or capacity gets out = NaN (no memory outside
@@ -264,9 +267,9 @@ int kvq_decode_attn(const kvq_geom *geom, const uint16_t *q,
 /* The two phases of kvq_decode_attn, for callers that time or schedule them
  * apart.  kvq_decode_attn(...) == kvq_decode_partial(...) followed by
  * kvq_decode_combine(...) on the same stream with the same arguments.
- * kvq_decode_partial writes out directly (and kvq_decode_combine does nothing)
- * when kvq_decode_splits() gives one split; otherwise it writes per-split
- * (max, sum, weighted value) partials into the workspace. */
+ * kvq_decode_partial writes per-split (max, sum, weighted value sum) partials
+ * into the workspace and does not touch out; kvq_decode_combine merges them
+ * into out. */
 int kvq_decode_partial(const kvq_geom *geom, const uint16_t *q,
                        const kvq_cache *cache, const int32_t *seq_lens,
                        int32_t max_seq_len, float sm_scale, void *workspace,

@@ -137,7 +137,7 @@ class Cache:
         self.k_codes = np.zeros((B, H, C, D * g.k_bits // 32), np.uint32)
         self.v_codes = np.zeros((B, H, C // VBLOCK, D, g.v_bits), np.uint32)
         self.k_meta = np.zeros((B, H, C // g.group, D, 2), np.uint16)
-        self.v_meta = np.zeros((B, H, C, D // g.group, 2), np.uint16)
+        self.v_meta = np.zeros((B, H, C // VBLOCK, D // g.group, VBLOCK, 2), np.uint16)
         self.k_res = np.zeros((B, H, g.residual, D), np.uint16)
         self.v_res = np.zeros((B, H, g.residual, D), np.uint16)
 

@@ -185,7 +185,8 @@ void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
 /* k_meta   u16 [B][Hkv][C/G][D][2]: (scale, min) per key group and channel. */
 /* v_codes  u32 [B][Hkv][C/32][D][bV]: 32-token blocks; for channel c,       */
 /*          token tau of the block in bits (tau*bV)%32.. of word (tau*bV)/32.*/
-/* v_meta   u16 [B][Hkv][C][D/G][2]: (scale, min) per token, channel group.  */
+/* v_meta   u16 [B][Hkv][C/32][D/G][32][2]: (scale, min) per token and      */
+/*          channel group, in 32-token blocks (block, group, token).        */
 /* k_res, v_res u16 [B][Hkv][R][D]: position p in slot p % R.               */
 /* ------------------------------------------------------------------------ */
 
@@ -204,6 +205,14 @@ static uint32_t key_code(const uint32_t *k_codes, int64_t unit, int64_t C,
   int64_t words = (int64_t)D * bK / 32;
   const uint32_t *row = k_codes + (unit * C + t) * words;
   return get_field(row[(c * bK) / 32], (c * bK) % 32, bK);
+}
+
+/* Entry of (scale, min) for token t, channel group gm in v_meta. */
+static int64_t value_meta_index(int64_t unit, int64_t C, int D, int G,
+                                int64_t t, int gm) {
+  int64_t blk = t / ORC_VBLOCK;
+  return ((unit * (C / ORC_VBLOCK) + blk) * (D / G) + gm) * ORC_VBLOCK +
+         t % ORC_VBLOCK;
 }
 
 static uint32_t value_code(const uint32_t *v_codes, int64_t unit, int64_t C,
@@ -255,7 +264,7 @@ static void quantize_values_unit(const uint16_t *src, int64_t pos0,
       /* per token: G consecutive channels ([KIVI] values per token) */
       orc_quantize_group(src + i * D + (int64_t)gm * G, G, 1, bV, &d16, &m16,
                          codes, 1);
-      uint16_t *meta = v_meta + ((unit * C + t) * ngroups + gm) * 2;
+      uint16_t *meta = v_meta + value_meta_index(unit, C, D, G, t, gm) * 2;
       meta[0] = d16;
       meta[1] = m16;
       for (int cc = 0; cc < G; ++cc) {
@@ -353,7 +362,7 @@ static double dequant_key(const uint32_t *k_codes, const uint16_t *k_meta,
 static double dequant_value(const uint32_t *v_codes, const uint16_t *v_meta,
                             int64_t unit, int64_t C, int D, int bV, int G,
                             int64_t t, int c) {
-  const uint16_t *meta = v_meta + ((unit * C + t) * (D / G) + c / G) * 2;
+  const uint16_t *meta = v_meta + value_meta_index(unit, C, D, G, t, c / G) * 2;
   double scale = orc_half_to_float(meta[0]);
   double minv = orc_half_to_float(meta[1]);
   return (double)value_code(v_codes, unit, C, D, bV, t, c) * scale + minv;

@@ -205,7 +205,8 @@ class Cache:
         self.k_codes = torch.zeros((B, H, C, D * g.k_bits // 32), dtype=torch.int32, **z)
         self.v_codes = torch.zeros((B, H, C // VBLOCK, D, g.v_bits), dtype=torch.int32, **z)
         self.k_meta = torch.zeros((B, H, C // g.group, D, 2), dtype=torch.int16, **z)
-        self.v_meta = torch.zeros((B, H, C, D // g.group, 2), dtype=torch.int16, **z)
+        self.v_meta = torch.zeros((B, H, C // VBLOCK, D // g.group, VBLOCK, 2),
+                                  dtype=torch.int16, **z)
         self.k_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
         self.v_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
         sizes = kvq_cache_bytes(g)

@@ -78,6 +78,14 @@ int check_ptr(const void* p, const char* name) {
   return KVQ_OK;
 }
 
+// seq_lens is an int32 array; 4-byte alignment is enough.
+int check_lens(const int32_t* p) {
+  if (!p) return fail(KVQ_ERR_NULL, "seq_lens is NULL");
+  if (reinterpret_cast<uintptr_t>(p) & 3u)
+    return fail(KVQ_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  return KVQ_OK;
+}
+
 int packed_len(int n, int R) { return n <= 0 ? 0 : n - (((n - 1) % R) + 1); }
 
 // Compute units of the current device, cached per device.
@@ -123,6 +131,20 @@ int splits_for(const kvq_geom* g, int32_t max_seq_len, int32_t* n_split,
   return KVQ_OK;
 }
 
+// Partials: n_split packed splits plus the residual window, per query head.
+size_t workspace_need(const kvq_geom* g, int32_t n_split) {
+  return (size_t)g->batch * g->n_q_heads * (n_split + 1) * (g->head_dim + 2) * sizeof(float);
+}
+
+int check_workspace(const kvq_geom* g, int32_t n_split, const void* ws, size_t bytes) {
+  const size_t need = workspace_need(g, n_split);
+  if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, need);
+  return KVQ_OK;
+}
+
 int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
                  const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                  void* workspace, size_t workspace_bytes, uint16_t* out,
@@ -131,22 +153,14 @@ int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache
   if (st != KVQ_OK) return st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if ((st = check_ptr(q, "q")) != KVQ_OK) return st;
-  if ((st = check_ptr(seq_lens, "seq_lens")) != KVQ_OK) return st;
+  if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
   if ((st = check_ptr(out, "out")) != KVQ_OK) return st;
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_huge_valf() ||
       sm_scale == -__builtin_huge_valf())
     return fail(KVQ_ERR_RANGE, "sm_scale must be finite");
   int32_t n_split = 0, split_tokens = 0;
   if ((st = splits_for(geom, max_seq_len, &n_split, &split_tokens)) != KVQ_OK) return st;
-  const size_t need = n_split > 1 ? (size_t)geom->batch * geom->n_q_heads * n_split *
-                                        (geom->head_dim + 2) * sizeof(float)
-                                  : 0;
-  if (need > 0) {
-    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-    if (!aligned16(workspace)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  }
+  if ((st = check_workspace(geom, n_split, workspace, workspace_bytes)) != KVQ_OK) return st;
   L->g = kvq::to_geom(*geom);
   L->q = q;
   L->cache = *cache;
@@ -226,9 +240,7 @@ int kvq_decode_workspace_bytes(const kvq_geom* geom, int32_t max_seq_len, size_t
     if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
     int32_t ns = 0, tok = 0;
     if ((st = splits_for(geom, max_seq_len, &ns, &tok)) != KVQ_OK) return st;
-    *bytes = ns > 1 ? (size_t)geom->batch * geom->n_q_heads * ns * (geom->head_dim + 2) *
-                          sizeof(float)
-                    : 0;
+    *bytes = workspace_need(geom, ns);
     return KVQ_OK;
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");
@@ -314,7 +326,7 @@ int kvq_append(const kvq_geom* geom, const uint16_t* k_new, const uint16_t* v_ne
     if ((st = check_cache(cache)) != KVQ_OK) return st;
     if ((st = check_ptr(k_new, "k_new")) != KVQ_OK) return st;
     if ((st = check_ptr(v_new, "v_new")) != KVQ_OK) return st;
-    if ((st = check_ptr(seq_lens, "seq_lens")) != KVQ_OK) return st;
+    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
     hipError_t e = kvq::launch_append(kvq::to_geom(*geom), k_new, v_new, seq_lens, *cache,
                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "append launch");
@@ -344,17 +356,11 @@ int kvq_decode_combine(const kvq_geom* geom, const int32_t* seq_lens, int32_t ma
   try {
     int st = check_geom(geom);
     if (st != KVQ_OK) return st;
-    if ((st = check_ptr(seq_lens, "seq_lens")) != KVQ_OK) return st;
+    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
     if ((st = check_ptr(out, "out")) != KVQ_OK) return st;
     int32_t n_split = 0, split_tokens = 0;
     if ((st = splits_for(geom, max_seq_len, &n_split, &split_tokens)) != KVQ_OK) return st;
-    if (n_split == 1) return KVQ_OK;
-    const size_t need = (size_t)geom->batch * geom->n_q_heads * n_split *
-                        (geom->head_dim + 2) * sizeof(float);
-    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-    if (!aligned16(workspace)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if ((st = check_workspace(geom, n_split, workspace, workspace_bytes)) != KVQ_OK) return st;
     kvq::DecodeLaunch L{};
     L.g = kvq::to_geom(*geom);
     L.seq_lens = seq_lens;

@@ -1,214 +1,217 @@
 // kvq_decode.hip — single-token decode attention over the packed cache plus
 // the fp16 residual window: split-context partial softmax and combine (gfx950).
 //
-// What is computed (KIVI repository page, "Overview": attention over keys
-// quantized per channel and values quantized per token, with the recent tokens
-// kept in fp16; KV1-1.2B model card, "Quickstart": attending over the
-// dequantized cache gives the exact low-bit result):
+// What is computed (KIVI repository page, "Overview": attention with keys
+// quantized per channel and values per token, the recent tokens kept in fp16;
+// KV1-1.2B model card, "Quickstart": attending over the dequantized cache gives
+// the exact low-bit result):
 //   s_t = sm_scale * q . k_t,  out = sum_t softmax(s)_t v_t
 // with k_t = code * scale + min from the key group's per-channel (scale, min)
 // for packed tokens, the fp16 residual for the rest, and v_t likewise from the
 // token's per-group (scale, min).
 //
-// Per-group fold (algebra on the dequantizer): for key group j,
-//   q . k_t = sum_c (q_c * scale_jc) * code_tc + sum_c q_c * min_jc
-// so the query is scaled once per group and the codes enter the dot product as
-// small integers.  Scores are kept in log2 units (sm_scale * log2 e folded into
-// q) so the softmax uses exp2.
+// Algebra on the dequantizer (per key group j and value group gamma):
+//   q . k_t = sum_c (q_c scale_jc) code_tc + sum_c q_c min_jc
+//   sum_t p_t v_tc = sum_t (p_t scale_t,gamma) code_tc + sum_t p_t min_t,gamma
+// so both contractions run on the small integer codes.  On gfx950 they are done
+// by v_mfma_f32_16x16x32_f16 with the codes fed as fp16 subnormals (a code c
+// masked out of a packed word *is* the fp16 number c * 2^-24, which the matrix
+// cores multiply exactly) and the fp32 factors (q * scale, p * scale) split into
+// a high and a low fp16 part, two MFMAs accumulating into the same fp32 tile.
+// The scaled-query and weight operands are computed once per key group / per
+// 32-token chunk; everything per code is a shift and a mask.
 //
-// One workgroup = (split, KV head, sequence); the GQA query heads of the KV head
-// share every code and meta load.  A split covers `split_tokens` positions (a
-// multiple of G, so key groups never straddle splits); its partial is the
-// running (max, sum, weighted value sum) of an online softmax.
+// Work decomposition: one workgroup (4 waves) per (split, KV head, sequence)
+// over packed tokens; the GQA query heads of the KV head share every load.
+// Each wave runs an online softmax over a contiguous run of 32-token chunks;
+// the 4 wave states merge in LDS into one partial (max, sum, weighted values)
+// per query head.  One extra workgroup per (KV head, sequence) covers the
+// residual window with plain fp32 arithmetic.  The combine kernel merges
+// partials: M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i-M) / L.
+// Scores are kept in log2 units (sm_scale * log2 e folded into q).
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kChunk = 32;          // tokens per inner iteration (= value block)
-constexpr int kThreadsPerToken = 8;  // score lanes per token
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 32;  // tokens per chunk (= value block)
+constexpr int kWaves = kThreads / 64;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ int packed_len(int n, int R) {
   return n <= 0 ? 0 : n - (((n - 1) % R) + 1);
 }
 
-__device__ __forceinline__ float reduce_max32(float x) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float reduce_sum32(float x) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+__device__ __forceinline__ f4 mfma(const uint32_t (&a)[4], const uint32_t (&b)[4], f4 c) {
+  const u4 av = {a[0], a[1], a[2], a[3]};
+  const u4 bv = {b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, av),
+                                                __builtin_bit_cast(h8, bv), c, 0, 0, 0);
 }
 
-// `bits` consecutive-field codes of CPT channels starting at bit `bitoff` of a
-// token row, returned as the low CPT*BK bits of a 64-bit word.
-template <int CPT, int BK>
-__device__ __forceinline__ uint64_t load_key_slice(const uint32_t* row,
-                                                   int bitoff) {
-  constexpr int kBits = CPT * BK;
-  if constexpr (kBits == 64) {
-    const uint2 w = *reinterpret_cast<const uint2*>(row + bitoff / 32);
-    return (uint64_t)w.x | ((uint64_t)w.y << 32);
+// Two floats -> packed fp16 pair, rounded toward zero (hi part of a hi/lo
+// split; the lo part carries the remainder, so the rounding mode of the split
+// does not matter).
+__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float lo_half(uint32_t v) {
+  return (float)__builtin_bit_cast(h2, v)[0];
+}
+__device__ __forceinline__ float hi_half(uint32_t v) {
+  return (float)__builtin_bit_cast(h2, v)[1];
+}
+// hi/lo fp16 split of (a, b): a ~= hi.x + lo.x to ~2^-21 relative.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pk_rtz(a, b);
+  lo = pk_rtz(a - lo_half(hi), b - hi_half(hi));
+}
+
+__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, 64)); }
+__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, 64); }
+
+// ---------------------------------------------------------------------------
+// Token and channel permutations of the MFMA operands.
+//
+// Value side: the A operand of lane (channel c, lane group g) holds 8 codes of
+// channel c; element j is the chunk token tok_v(g, j).  It comes straight from
+// the packed value word(s): 4-bit words hold tokens 8w..8w+7 (nibble e = token
+// 8w+e), and one mask of (w >> 4e) with 0x000F000F yields tokens 8g+e and
+// 8g+4+e as an fp16 pair; 2-bit words hold 16 tokens and (w >> 2s) & 0x00030003
+// yields tokens s and s+8 of the word.
+// Key side: tile u (16 tokens) row r is token tok_v(r / 4, 4u + r % 4), so that
+// the score tile's output registers (lane group g, register r' of tile u) hold
+// exactly the tokens tok_v(g, 4u + r') that the value side wants in element
+// 4u + r' of its B operand: the scores never leave their lanes.
+// ---------------------------------------------------------------------------
+template <int BV>
+__device__ __forceinline__ constexpr int tok_v(int g, int j) {
+  const int e = j >> 1, par = j & 1;
+  return BV == 4 ? 8 * g + 4 * par + e : 16 * (g >> 1) + 8 * par + 4 * (g & 1) + e;
+}
+
+// First channel of the two 4-channel runs a key-side B fragment (lane group g,
+// k-chunk kc) covers; element 2e is channel run0 + e, element 2e+1 is channel
+// run0 + kOff + e.  Matches the unpack in unpack_keys().
+template <int D, int BK>
+__device__ __forceinline__ constexpr int key_run0(int g, int kc) {
+  return BK == 2 ? g * (D / 4) + 16 * (kc >> 1) + 4 * (kc & 1) : g * (D / 4) + 8 * kc;
+}
+template <int BK>
+constexpr int kKeyOff = BK == 2 ? 8 : 4;
+
+// Lane's slice of a key row: channels [g*D/4, (g+1)*D/4) -> KW words.
+template <int D, int BK>
+constexpr int kKW = (D / 4) * BK / 32;
+
+template <int D, int BK>
+__device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
+                                            uint32_t (&a)[D / 32][4]) {
+  if constexpr (BK == 2) {
+#pragma unroll
+    for (int wi = 0; wi < kKW<D, BK>; ++wi)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int ri = 8 * wi + s;
+        a[ri >> 2][ri & 3] = (w[wi] >> (2 * s)) & 0x00030003u;
+      }
   } else {
-    const uint32_t w = row[bitoff / 32];
-    return (uint64_t)(w >> (bitoff % 32));
+#pragma unroll
+    for (int wi = 0; wi < kKW<D, BK>; ++wi)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[wi][s] = (w[wi] >> (4 * s)) & 0x000F000Fu;
   }
 }
 
-template <int D, int BK, int BV, int GQ>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeLaunch L) {
-  constexpr int CPT = D / kThreadsPerToken;      // channels per score lane
-  constexpr int TPC = kThreads / D;              // threads per channel (V)
-  constexpr int HPT = (GQ + TPC - 1) / TPC;      // heads per V thread
-  constexpr int kMaxNG = D / 32;                 // value groups per token, max
-
-  __shared__ float qf[GQ][D];        // q * sm_scale * log2 e
-  __shared__ float qk[GQ][D];        // qf * key scale of the current group
-  __shared__ float beta[GQ];         // qf . key min of the current group
-  __shared__ float sc[GQ][kChunk];   // scores, then probabilities
-  __shared__ float2 vm[kChunk][kMaxNG];  // value (scale, min) of the chunk
-  __shared__ float m_run[GQ], l_run[GQ], alpha[GQ];
-
-  const Geom& g = L.g;
-  const int tid = threadIdx.x;
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int64_t unit = (int64_t)b * g.Hkv + hkv;
-  const int n = L.seq_lens[b];
-  const bool direct = (L.n_split == 1);
-  const int c_v = tid % D;      // channel of this thread in the V phase
-  const int hg = tid / D;       // head group of this thread in the V phase
-
-  if (n < 0 || n > g.C || n > L.max_seq_len || (n == 0)) {
-    // invalid length -> NaN; empty sequence -> 0 (combine does the same when
-    // there is more than one split)
-    if (direct) {
-      const uint16_t val = (n == 0) ? (uint16_t)0 : (uint16_t)0x7e00;
-      for (int i = tid; i < GQ * D; i += kThreads)
-        L.out[((int64_t)b * g.Hq + hkv * GQ) * D + i] = val;
-    }
-    return;
+template <int KW>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[KW]) {
+  if constexpr (KW == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (KW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = p[0];
   }
-  const int t_begin = split * L.split_tokens;
-  if (t_begin >= n) return;  // empty split: the combine ignores it
-  const int t_end = min(n, t_begin + L.split_tokens);
-  const int lq = packed_len(n, g.R);
-  const int NG = D / g.G;
+}
 
+// ---------------------------------------------------------------------------
+// Residual window (fp16 tokens [t_begin, t_end)), plain fp32 arithmetic over
+// the whole workgroup: 8 lanes per token for scores, one lane per (channel,
+// head group) for the weighted value sum.  Writes partial `part_idx`.
+// ---------------------------------------------------------------------------
+template <int D, int GQ>
+__device__ void residual_partial(const DecodeLaunch& L, int b, int hkv, int t_begin,
+                                 int t_end, int part_idx, float* smem) {
+  constexpr int kTPT = 8, CPT = D / kTPT;
+  constexpr int TPC = kThreads / D, HPT = (GQ + TPC - 1) / TPC;
+  const Geom& g = L.g;
+  float* qf = smem;                      // [GQ][D]
+  float* sc = qf + GQ * D;               // [GQ][kChunk]
+  float* m_run = sc + GQ * kChunk;       // [GQ]
+  float* l_run = m_run + GQ;
+  float* alpha = l_run + GQ;
+  const int tid = threadIdx.x;
+  const int64_t unit = (int64_t)b * g.Hkv + hkv;
   for (int i = tid; i < GQ * D; i += kThreads)
-    (&qf[0][0])[i] =
-        h2f(L.q[((int64_t)b * g.Hq + hkv * GQ) * D + i]) * L.scale_log2;
+    qf[i] = h2f(L.q[((int64_t)b * g.Hq + hkv * GQ) * D + i]) * L.scale_log2;
   if (tid < GQ) {
     m_run[tid] = kNegInf;
     l_run[tid] = 0.0f;
   }
+  const int c_v = tid % D, hg = tid / D;
   float o[HPT];
 #pragma unroll
   for (int i = 0; i < HPT; ++i) o[i] = 0.0f;
   __syncthreads();
-
-  const int tok = tid / kThreadsPerToken;  // score phase: token in chunk
-  const int sl = tid % kThreadsPerToken;   // score phase: channel slice
-  const uint32_t* kc_unit = L.cache.k_codes + unit * g.C * (D * BK / 32);
-  const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) +
-                          unit * (g.C / g.G) * D;
-  const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
-                          unit * g.C * NG;
-  const uint32_t* vc_unit = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
   const uint16_t* kr = L.cache.k_res + unit * g.R * D;
   const uint16_t* vr = L.cache.v_res + unit * g.R * D;
-
-  int cur_group = -1;
+  const int tok = tid / kTPT, sl = tid % kTPT;
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const bool packed = t0 < lq;  // chunks never straddle lq (both % 32 == 0)
-    if (packed) {
-      const int j = t0 / g.G;
-      if (j != cur_group) {
-        // fold the group's per-channel scale into q; min into beta
-        for (int i = tid; i < GQ * D; i += kThreads) {
-          const int c = i % D;
-          (&qk[0][0])[i] = (&qf[0][0])[i] * h2f((uint16_t)(kmeta[j * D + c] & 0xffffu));
-        }
-        const int wave = tid / 64, lane = tid % 64;
-        for (int h = wave; h < GQ; h += kThreads / 64) {
-          float acc = 0.0f;
-          for (int c = lane; c < D; c += 64)
-            acc += qf[h][c] * h2f((uint16_t)(kmeta[j * D + c] >> 16));
+    const int t = t0 + tok;
+    const bool valid = t < t_end;
+    float acc[GQ];
 #pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-          if (lane == 0) beta[h] = acc;
-        }
-        cur_group = j;
-      }
-      for (int i = tid; i < kChunk * NG; i += kThreads) {
-        const uint32_t mv = vmeta[(int64_t)(t0 + i / NG) * NG + i % NG];
-        vm[i / NG][i % NG] = make_float2(h2f((uint16_t)(mv & 0xffffu)),
-                                         h2f((uint16_t)(mv >> 16)));
-      }
-      __syncthreads();
-      // scores: 8 lanes per token, CPT channels each
-      const int t = t0 + tok;  // always < lq <= t_end here
-      const uint64_t bits = load_key_slice<CPT, BK>(
-          kc_unit + (int64_t)t * (D * BK / 32), sl * CPT * BK);
-      float acc[GQ];
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) acc[h] = 0.0f;
+    for (int h = 0; h < GQ; ++h) acc[h] = 0.0f;
+    if (valid) {
+      const uint16_t* krow = kr + (int64_t)(t % g.R) * D + sl * CPT;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const float code = (float)((bits >> (i * BK)) & ((1u << BK) - 1u));
+        const float kv = h2f(krow[i]);
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) acc[h] += qk[h][sl * CPT + i] * code;
-      }
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        acc[h] += __shfl_xor(acc[h], 1, 64);
-        acc[h] += __shfl_xor(acc[h], 2, 64);
-        acc[h] += __shfl_xor(acc[h], 4, 64);
-      }
-      if (sl == 0) {
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) sc[h][tok] = acc[h] + beta[h];
-      }
-    } else {
-      const int t = t0 + tok;
-      const bool valid = t < t_end;
-      float acc[GQ];
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) acc[h] = 0.0f;
-      if (valid) {
-        const uint16_t* krow = kr + (int64_t)(t % g.R) * D + sl * CPT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-          const float kv = h2f(krow[i]);
-#pragma unroll
-          for (int h = 0; h < GQ; ++h) acc[h] += qf[h][sl * CPT + i] * kv;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        acc[h] += __shfl_xor(acc[h], 1, 64);
-        acc[h] += __shfl_xor(acc[h], 2, 64);
-        acc[h] += __shfl_xor(acc[h], 4, 64);
-      }
-      if (sl == 0) {
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) sc[h][tok] = valid ? acc[h] : kNegInf;
+        for (int h = 0; h < GQ; ++h) acc[h] += qf[h * D + sl * CPT + i] * kv;
       }
     }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      acc[h] = xor_sum(acc[h], 1);
+      acc[h] = xor_sum(acc[h], 2);
+      acc[h] = xor_sum(acc[h], 4);
+    }
+    if (sl == 0) {
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) sc[h * kChunk + tok] = valid ? acc[h] : kNegInf;
+    }
     __syncthreads();
-    // online softmax over the chunk: 32 lanes per head
     for (int i = tid; i < GQ * kChunk; i += kThreads) {
       const int h = i / kChunk, tk = i % kChunk;
-      const float x = sc[h][tk];
-      const float cmax = reduce_max32(x);
+      const float x = sc[i];
+      float cmax = x;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) cmax = xor_max(cmax, off);
       const float m_old = m_run[h];
-      const float m_new = fmaxf(m_old, cmax);  // finite: one valid token
+      const float m_new = fmaxf(m_old, cmax);
       const float p = exp2f(x - m_new);
-      const float psum = reduce_sum32(p);
-      sc[h][tk] = p;
+      float psum = p;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) psum = xor_sum(psum, off);
+      sc[i] = p;
       if (tk == 0) {
         const float a = exp2f(m_old - m_new);
         alpha[h] = a;
@@ -217,63 +220,349 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeLaunch L
       }
     }
     __syncthreads();
-    // V accumulation: this thread owns channel c_v of heads hg*HPT + i
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       const int h = hg * HPT + i;
       if (h < GQ) o[i] *= alpha[h];
     }
-    if (packed) {
-      const uint32_t* w = vc_unit + ((int64_t)(t0 / kVBlock) * D + c_v) * BV;
-      uint32_t words[BV];
+    for (int tk = 0; tk < kChunk && t0 + tk < t_end; ++tk) {
+      const float vv = h2f(vr[(int64_t)((t0 + tk) % g.R) * D + c_v]);
 #pragma unroll
-      for (int k = 0; k < BV; ++k) words[k] = w[k];
-      const int gm = c_v / g.G;
-#pragma unroll
-      for (int tk = 0; tk < kChunk; ++tk) {
-        const uint32_t code =
-            (words[(tk * BV) / 32] >> ((tk * BV) % 32)) & ((1u << BV) - 1u);
-        const float2 sm = vm[tk][gm];
-        const float vv = (float)code * sm.x + sm.y;
-#pragma unroll
-        for (int i = 0; i < HPT; ++i) {
-          const int h = hg * HPT + i;
-          if (h < GQ) o[i] += sc[h][tk] * vv;
-        }
-      }
-    } else {
-      for (int tk = 0; tk < kChunk && t0 + tk < t_end; ++tk) {
-        const float vv = h2f(vr[(int64_t)((t0 + tk) % g.R) * D + c_v]);
-#pragma unroll
-        for (int i = 0; i < HPT; ++i) {
-          const int h = hg * HPT + i;
-          if (h < GQ) o[i] += sc[h][tk] * vv;
-        }
+      for (int i = 0; i < HPT; ++i) {
+        const int h = hg * HPT + i;
+        if (h < GQ) o[i] += sc[h * kChunk + tk] * vv;
       }
     }
     __syncthreads();
   }
-
 #pragma unroll
   for (int i = 0; i < HPT; ++i) {
     const int h = hg * HPT + i;
     if (h >= GQ) continue;
     const int64_t bh = (int64_t)b * g.Hq + hkv * GQ + h;
-    if (direct) {
-      L.out[bh * D + c_v] = f2h(o[i] / l_run[h]);
-    } else {
-      float* part = L.ws + (bh * L.n_split + split) * (D + 2);
-      part[c_v] = o[i];
-      if (c_v == 0) {
-        part[D] = m_run[h];
-        part[D + 1] = l_run[h];
-      }
+    float* part = L.ws + (bh * (L.n_split + 1) + part_idx) * (D + 2);
+    part[c_v] = o[i];
+    if (c_v == 0) {
+      part[D] = m_run[h];
+      part[D + 1] = l_run[h];
     }
   }
 }
 
-// Merges the splits of one (sequence, query head):
-//   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
+// ---------------------------------------------------------------------------
+// Packed tokens of one split: MFMA path.
+// ---------------------------------------------------------------------------
+template <int D, int BK, int BV, int GQ>
+struct Cfg {
+  static constexpr int KC = D / 32;             // k-chunks of a score tile
+  static constexpr int NT = D / 16;             // value channel tiles
+  static constexpr int KW = kKW<D, BK>;         // key words per lane and row
+  static constexpr int SL = 16 / GQ;            // MFMA columns per head
+  static constexpr int IPH = 4 * KC;            // fold items per head
+  static constexpr int ITEMS = GQ * IPH;        // fold items per key group
+  static constexpr int IPL = (ITEMS + 63) / 64;  // fold items per lane
+  static constexpr int MAXNF = (4 + SL - 1) / SL;  // value-B fragments (NG <= 4)
+  // LDS (bytes): per wave q' fragments [2][GQ][4][KC] x 16 B + beta [GQ] floats
+  static constexpr int kQB = 2 * GQ * 4 * KC * 16;
+  static constexpr int kWaveLds = kQB + 16 * ((GQ * 4 + 15) / 16);
+};
+
+template <int D, int BK, int BV, int GQ>
+__device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split, int t0,
+                               int t1, char* smem) {
+  using C = Cfg<D, BK, BV, GQ>;
+  constexpr int KC = C::KC, NT = C::NT, KW = C::KW, SL = C::SL, IPH = C::IPH;
+  constexpr int MAXNF = C::MAXNF;
+  const Geom& g = L.g;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, lg = lane >> 4;
+  const int hcol = col / SL, slot = col % SL;
+  const int64_t unit = (int64_t)b * g.Hkv + hkv;
+  const int G = g.G, NG = D / G;
+  const int NF = (NG + SL - 1) / SL;
+
+  // ---- shared memory: scaled query, exponents, per-wave fold buffers ----
+  float* qfs = reinterpret_cast<float*>(smem);            // [GQ][D] q * 2^-E
+  int* qexp = reinterpret_cast<int*>(qfs + GQ * D);       // [GQ]
+  char* wbase = smem + (GQ * D + 16) * 4;
+  uint4* qB = reinterpret_cast<uint4*>(wbase + wave * C::kWaveLds);  // [2][GQ][4][KC]
+  float* beta_l = reinterpret_cast<float*>(wbase + wave * C::kWaveLds + C::kQB);
+
+  for (int i = tid; i < GQ * D; i += kThreads)
+    qfs[i] = h2f(L.q[((int64_t)b * g.Hq + hkv * GQ) * D + i]) * L.scale_log2;
+  __syncthreads();
+  // per-head exponent E with max|qf| < 2^E, so that q * 2^-E * scale fits fp16
+  for (int h = wave; h < GQ; h += kWaves) {
+    float mx = 0.0f;
+    for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(qfs[h * D + c]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = xor_max(mx, off);
+    int e = 0;
+    if (mx > 0.0f) (void)frexpf(mx, &e);
+    if (lane == 0) qexp[h] = e;
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * D; i += kThreads) qfs[i] = ldexpf(qfs[i], -qexp[i / D]);
+  __syncthreads();
+
+  const int e_h = qexp[hcol];
+  const float kscale = ldexpf(1.0f, e_h + 24);  // codes are fp16 numbers c*2^-24
+  const float bscale = ldexpf(1.0f, e_h);
+
+  // ---- this wave's chunks ----
+  const int nchunks = (t1 - t0) / kChunk;
+  const int c_lo = t0 / kChunk + (nchunks * wave) / kWaves;
+  const int c_hi = t0 / kChunk + (nchunks * (wave + 1)) / kWaves;
+
+  const uint32_t* kcodes = L.cache.k_codes + unit * g.C * (D * BK / 32);
+  const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) +
+                          unit * (g.C / G) * D;
+  const uint32_t* vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
+  const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
+                          unit * (g.C / kVBlock) * NG * kVBlock;
+
+  // key rows this lane feeds (row = col of tile u) and its word offset
+  int krow[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) krow[u] = tok_v<BV>(col >> 2, 4 * u + (col & 3));
+  const int vword = BV == 4 ? lg : (lg >> 1);
+  const int vshift = BV == 4 ? 0 : 8 * (lg & 1);
+  const int vrun0 = tok_v<BV>(lg, 0);        // tokens of run A (elements 2e)
+  const int vrun1 = tok_v<BV>(lg, 1);        // tokens of run B (elements 2e+1)
+
+  f4 oacc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.0f;
+  float bias[MAXNF];
+#pragma unroll
+  for (int f = 0; f < MAXNF; ++f) bias[f] = 0.0f;
+
+  int cur_group = -1;
+  uint32_t bq[2][KC][4];  // q' hi / lo fragments of the current key group
+  float beta_c = 0.0f;    // beta' of this lane's head, scaled
+
+  for (int ch = c_lo; ch < c_hi; ++ch) {
+    const int tbase = ch * kChunk;
+    // ---------------- loads of this chunk ----------------
+    uint32_t kw[2][KW];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      load_words<KW>(kcodes + (int64_t)(tbase + krow[u]) * (D * BK / 32) + lg * KW, kw[u]);
+    uint32_t vw[NT];
+    const uint32_t* vblk = vcodes + (int64_t)ch * D * BV;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) vw[n] = vblk[(16 * n + col) * BV + vword];
+    uint32_t vmA[MAXNF][4], vmB[MAXNF][4];
+#pragma unroll
+    for (int f = 0; f < MAXNF; ++f) {
+      if (f < NF) {
+        const int gam = (f * SL + slot) % NG;
+        const uint32_t* m = vmeta + ((int64_t)ch * NG + gam) * kVBlock;
+        const uint4 a = *reinterpret_cast<const uint4*>(m + vrun0);
+        const uint4 c = *reinterpret_cast<const uint4*>(m + vrun1);
+        vmA[f][0] = a.x; vmA[f][1] = a.y; vmA[f][2] = a.z; vmA[f][3] = a.w;
+        vmB[f][0] = c.x; vmB[f][1] = c.y; vmB[f][2] = c.z; vmB[f][3] = c.w;
+      }
+    }
+
+    // ---------------- fold of a new key group ----------------
+    const int grp = tbase / G;
+    if (grp != cur_group) {
+      cur_group = grp;
+      const uint32_t* km = kmeta + (int64_t)grp * D;
+      for (int it0 = 0; it0 < C::IPL * 64; it0 += 64) {
+        const int it = it0 + lane;
+        float bpart = 0.0f;
+        if (it < C::ITEMS) {
+          const int h = it / IPH, r = it % IPH, gg = r / KC, kc = r % KC;
+          const int c0 = key_run0<D, BK>(gg, kc), c1 = c0 + kKeyOff<BK>;
+          const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + c0);
+          const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + c1);
+          const uint4 ma = *reinterpret_cast<const uint4*>(km + c0);
+          const uint4 mb = *reinterpret_cast<const uint4*>(km + c1);
+          const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qB4[4] = {qb.x, qb.y, qb.z, qb.w};
+          const uint32_t mA[4] = {ma.x, ma.y, ma.z, ma.w}, mB[4] = {mb.x, mb.y, mb.z, mb.w};
+          uint32_t hp[4], lp[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xa = qA[e] * h2f((uint16_t)(mA[e] & 0xffffu));
+            const float xb = qB4[e] * h2f((uint16_t)(mB[e] & 0xffffu));
+            split2(xa, xb, hp[e], lp[e]);
+            bpart += qA[e] * h2f((uint16_t)(mA[e] >> 16)) + qB4[e] * h2f((uint16_t)(mB[e] >> 16));
+          }
+          qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+          qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+        }
+#pragma unroll
+        for (int off = IPH / 2; off >= 1; off >>= 1) bpart = xor_sum(bpart, off);
+        if (it < C::ITEMS && (it % IPH) == 0) beta_l[it / IPH] = bpart;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 v = qB[((p * GQ + hcol) * 4 + lg) * KC + kc];
+          bq[p][kc][0] = v.x; bq[p][kc][1] = v.y; bq[p][kc][2] = v.z; bq[p][kc][3] = v.w;
+        }
+      beta_c = beta_l[hcol] * bscale;
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---------------- scores ----------------
+    float s[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t a[KC][4];
+      unpack_keys<D, BK>(kw[u], a);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        acc = mfma(a[kc], bq[0][kc], acc);
+        acc = mfma(a[kc], bq[1][kc], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[u][r] = acc[r] * kscale + beta_c;
+    }
+
+    // ---------------- online softmax ----------------
+    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    cm = xor_max(cm, 16);
+    cm = xor_max(cm, 32);
+    const float m_new = fmaxf(m_run, cm);
+    if (__any(m_new > m_run)) {
+      const float a = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= a;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) oacc[n] *= a;
+#pragma unroll
+      for (int f = 0; f < MAXNF; ++f) bias[f] *= a;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[u][r] = exp2f(s[u][r] - m_run);
+        l_run += p[u][r];
+      }
+
+    // ---------------- weighted value sum ----------------
+#pragma unroll
+    for (int f = 0; f < MAXNF; ++f) {
+      if (f >= NF) break;
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // elements 2i (run A, token tok_v(lg, 2i)) and 2i+1 (run B)
+        const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
+        const float xa = pa * h2f((uint16_t)(vmA[f][i] & 0xffffu));
+        const float xb = pb * h2f((uint16_t)(vmB[f][i] & 0xffffu));
+        split2(xa, xb, bh[i], bl[i]);
+        bias[f] += pa * h2f((uint16_t)(vmA[f][i] >> 16)) + pb * h2f((uint16_t)(vmB[f][i] >> 16));
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int gam = (16 * n) / G;
+        if (gam / SL != f) continue;
+        uint32_t a[4];
+        if constexpr (BV == 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = (vw[n] >> (4 * e)) & 0x000F000Fu;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = (vw[n] >> (vshift + 2 * e)) & 0x00030003u;
+        }
+        oacc[n] = mfma(a, bh, oacc[n]);
+        oacc[n] = mfma(a, bl, oacc[n]);
+      }
+    }
+  }
+
+  // ---------------- merge lane groups, then waves ----------------
+  l_run = xor_sum(l_run, 16);
+  l_run = xor_sum(l_run, 32);
+#pragma unroll
+  for (int f = 0; f < MAXNF; ++f) {
+    bias[f] = xor_sum(bias[f], 16);
+    bias[f] = xor_sum(bias[f], 32);
+  }
+  __syncthreads();  // fold buffers are reused for the merge below
+  float* cmb = reinterpret_cast<float*>(smem);  // [kWaves][GQ][D + 2]
+  float* mine = cmb + wave * GQ * (D + 2);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int gam = (16 * n) / G;
+    if (gam % SL != slot) continue;
+    const float bsum = bias[gam / SL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      mine[hcol * (D + 2) + 16 * n + 4 * lg + r] = oacc[n][r] * 16777216.0f + bsum;
+  }
+  if (lg == 0 && slot == 0) {
+    mine[hcol * (D + 2) + D] = m_run;
+    mine[hcol * (D + 2) + D + 1] = l_run;
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * D; i += kThreads) {
+    const int h = i / D, c = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cmb[(w * GQ + h) * (D + 2) + D]);
+    float Ls = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* s = cmb + (w * GQ + h) * (D + 2);
+      const float wt = (s[D] == kNegInf) ? 0.0f : exp2f(s[D] - M);
+      Ls += s[D + 1] * wt;
+      acc += s[c] * wt;
+    }
+    const int64_t bh = (int64_t)b * g.Hq + hkv * GQ + h;
+    float* part = L.ws + (bh * (L.n_split + 1) + split) * (D + 2);
+    part[c] = acc;
+    if (c == 0) {
+      part[D] = M;
+      part[D + 1] = Ls;
+    }
+  }
+}
+
+template <int D, int BK, int BV, int GQ>
+constexpr int kSmemBytes() {
+  using C = Cfg<D, BK, BV, GQ>;
+  constexpr int packed = (GQ * D + 16) * 4 + kWaves * C::kWaveLds;
+  constexpr int merge = kWaves * GQ * (D + 2) * 4;
+  constexpr int resid = (GQ * D + GQ * kChunk + 3 * GQ) * 4;
+  constexpr int m1 = packed > merge ? packed : merge;
+  return m1 > resid ? m1 : resid;
+}
+
+// grid: (n_split + 1, Hkv, B).  x < n_split: packed tokens of split x;
+// x == n_split: the residual window.
+template <int D, int BK, int BV, int GQ>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeLaunch L) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D, BK, BV, GQ>()];
+  const Geom& g = L.g;
+  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int n = L.seq_lens[b];
+  if (n <= 0 || n > g.C || n > L.max_seq_len) return;  // the combine writes 0 / NaN
+  const int lq = packed_len(n, g.R);
+  if (split == L.n_split) {
+    residual_partial<D, GQ>(L, b, hkv, lq, n, L.n_split, reinterpret_cast<float*>(smem));
+    return;
+  }
+  const int t0 = split * L.split_tokens;
+  const int t1 = min(lq, t0 + L.split_tokens);
+  if (t0 >= t1) return;  // no packed tokens here: the combine skips this split
+  packed_partial<D, BK, BV, GQ>(L, b, hkv, split, t0, t1, smem);
+}
+
+// Merges the partials of one (sequence, query head).
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeLaunch L) {
   const Geom& g = L.g;
@@ -281,20 +570,23 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeLaunch L) {
   const int64_t bh = (int64_t)b * g.Hq + h;
   const int n = L.seq_lens[b];
   if (n < 0 || n > g.C || n > L.max_seq_len) {
-    L.out[bh * D + c] = 0x7e00;  // NaN
+    L.out[bh * D + c] = 0x7e00;  // NaN: length outside [0, max_seq_len]
     return;
   }
   if (n == 0) {
     L.out[bh * D + c] = 0;
     return;
   }
-  const int ns = (n + L.split_tokens - 1) / L.split_tokens;
-  const float* part = L.ws + bh * L.n_split * (D + 2);
-  float M = kNegInf;
-  for (int i = 0; i < ns; ++i) M = fmaxf(M, part[i * (D + 2) + D]);
-  float Ls = 0.0f, acc = 0.0f;
-  for (int i = 0; i < ns; ++i) {
-    const float w = exp2f(part[i * (D + 2) + D] - M);
+  const int lq = packed_len(n, g.R);
+  const int nsp = (lq + L.split_tokens - 1) / L.split_tokens;  // packed splits used
+  const float* part = L.ws + bh * (L.n_split + 1) * (D + 2);
+  const float* res = part + L.n_split * (D + 2);
+  float M = res[D];
+  for (int i = 0; i < nsp; ++i) M = fmaxf(M, part[i * (D + 2) + D]);
+  float w = exp2f(res[D] - M);
+  float Ls = res[D + 1] * w, acc = res[c] * w;
+  for (int i = 0; i < nsp; ++i) {
+    w = exp2f(part[i * (D + 2) + D] - M);
     Ls += part[i * (D + 2) + D + 1] * w;
     acc += part[i * (D + 2) + c] * w;
   }
@@ -303,7 +595,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeLaunch L) {
 
 template <int D, int BK, int BV>
 hipError_t dispatch_gq(const DecodeLaunch& L, hipStream_t st) {
-  dim3 grid(L.n_split, L.g.Hkv, L.g.B);
+  dim3 grid(L.n_split + 1, L.g.Hkv, L.g.B);
   switch (L.g.Hq / L.g.Hkv) {
     case 1: decode_partial_kernel<D, BK, BV, 1><<<grid, kThreads, 0, st>>>(L); break;
     case 2: decode_partial_kernel<D, BK, BV, 2><<<grid, kThreads, 0, st>>>(L); break;
@@ -331,7 +623,6 @@ hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st) {
 }
 
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st) {
-  if (L.n_split == 1) return hipSuccess;
   dim3 grid(L.g.Hq, L.g.B);
   if (L.g.D == 64)
     decode_combine_kernel<64><<<grid, 64, 0, st>>>(L);

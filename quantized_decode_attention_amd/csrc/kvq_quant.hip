@@ -119,7 +119,7 @@ __device__ void value_block(const Geom& g, const uint16_t* src, int64_t unit,
       mx = fmaxf(mx, v);
     }
     const GroupParams p = group_params(mn, mx, BITS);
-    meta32[(unit * g.C + pos + t) * NG + gm] =
+    meta32[((unit * (g.C / kVBlock) + pos / kVBlock) * NG + gm) * kVBlock + t] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
     for (int c = 0; c < G; ++c)
       codes[t * D + gm * G + c] = (uint8_t)group_code(h2f(row[c]), p, BITS);

@@ -44,7 +44,7 @@ def assert_cache_equal(cache: kvq.Cache, oc: oracle.Cache, lens=None, what=""):
             "k_codes": (slice(b, b + 1), slice(None), slice(0, lq)),
             "k_meta": (slice(b, b + 1), slice(None), slice(0, lq // g.group)),
             "v_codes": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
-            "v_meta": (slice(b, b + 1), slice(None), slice(0, lq)),
+            "v_meta": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
         }
         for name, idx in sl.items():
             o = getattr(oc, name)[idx]

@@ -235,7 +235,7 @@ def test_workspace_errors():
     ns, st = kvq.kvq_decode_splits(g, 65536)
     assert ns > 1
     need = kvq.kvq_decode_workspace_bytes(g, 65536)
-    assert need == 4 * 32 * ns * 130 * 4
+    assert need == 4 * 32 * (ns + 1) * 130 * 4  # packed splits + residual partial
     cache = kvq.Cache(kvq.Geom(4, 32, 8, 128, 2, 4, 32, 128, 65536))
     q = torch.zeros((4, 32, 128), dtype=torch.float16, device="cuda")
     out = torch.empty_like(q)

@@ -227,7 +227,7 @@ def test_layout_worked_examples(orc, row):
         assert np.all(cache.k_meta[0, 0, 0, :, 1] == 0)
     else:
         got = int(cache.v_codes[0, 0, 0, idx, word])
-        assert np.all(cache.v_meta[0, 0, :32, :, 0] == 0x3C00)
+        assert np.all(cache.v_meta[0, 0, 0, :, :, 0] == 0x3C00)
     assert got == expect, hex(got)
 
 
