@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--layers", type=int, default=4, help="rotating layer caches")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (5 times); used to "
+                        "calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return p.parse_args()
 
 
@@ -121,6 +124,16 @@ def main():
 
     import quantized_decode_attention_amd as kvq
     from quantized_decode_attention_amd import metrics, synth
+
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
 
     w = synth.WORKLOADS[a.config]
     dev = torch.device("cuda:0")

@@ -23,7 +23,9 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = {
     "kvq_quant.hip": ["-ffp-contract=off"],
-    "kvq_decode.hip": [],
+    # MFMA accumulators in VGPRs: keeps the O tiles out of AGPR<->VGPR copies
+    # around the (rare) softmax rescale.
+    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "kvq_api.cpp": [],
 }
 

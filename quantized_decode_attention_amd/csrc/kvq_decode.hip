@@ -66,14 +66,49 @@ __device__ __forceinline__ float lo_half(uint32_t v) {
 __device__ __forceinline__ float hi_half(uint32_t v) {
   return (float)__builtin_bit_cast(h2, v)[1];
 }
-// hi/lo fp16 split of (a, b): a ~= hi.x + lo.x to ~2^-21 relative.
+// hi/lo fp16 split of (a, b): a ~= hi.x + lo.x to ~2^-21 relative.  The
+// remainders a - hi.x are exact fp32 subtractions, written as fmas of the fp16
+// half so that the compiler fuses the conversion (v_fma_mix_f32).
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = pk_rtz(a, b);
-  lo = pk_rtz(a - lo_half(hi), b - hi_half(hi));
+  const h2 hh = __builtin_bit_cast(h2, hi);
+  lo = pk_rtz(__builtin_fmaf((float)hh[0], -1.0f, a), __builtin_fmaf((float)hh[1], -1.0f, b));
+}
+
+// x * fp16 field of a packed (scale, min) word (+ acc), converted inside the
+// fma (v_fma_mix_f32).  The +0 addend keeps the fma from being folded into a
+// plain multiply that would need a separate conversion.
+__device__ __forceinline__ float mul_lo(float x, uint32_t w, float acc = 0.0f) {
+  return __builtin_fmaf(x, (float)__builtin_bit_cast(h2, w)[0], acc);
+}
+__device__ __forceinline__ float mul_hi(float x, uint32_t w, float acc = 0.0f) {
+  return __builtin_fmaf(x, (float)__builtin_bit_cast(h2, w)[1], acc);
 }
 
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, 64)); }
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, 64); }
+
+// DPP lane moves inside a row of 16 lanes (no LDS traffic).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                           kCtrl, 0xF, 0xF, true));
+}
+// Sum over aligned groups of n lanes (n = 8 or 16).  Rotations act on whole
+// 16-lane rows, so they serve n = 16; for n = 8 the 4-apart step is a lane
+// shuffle.
+template <int kN>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (kN >= 16) {
+    x += dpp<0x128>(x);  // row_ror:8  -> lanes i, i+8
+    x += dpp<0x124>(x);  // row_ror:4  -> lanes i, i+4, i+8, i+12
+  } else {
+    x = xor_sum(x, 4);
+  }
+  x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+  return x;
+}
 
 // ---------------------------------------------------------------------------
 // Token and channel permutations of the MFMA operands.
@@ -250,43 +285,286 @@ __device__ void residual_partial(const DecodeLaunch& L, int b, int hkv, int t_be
 }
 
 // ---------------------------------------------------------------------------
-// Packed tokens of one split: MFMA path.
+// Packed tokens of one split: MFMA path.  NG = head_dim / group is a template
+// parameter, so the key-group length G = D / NG and the value-tile -> group
+// mapping are compile-time constants (no branches around the accumulators).
 // ---------------------------------------------------------------------------
-template <int D, int BK, int BV, int GQ>
+template <int D, int BK, int BV, int GQ, int NG>
 struct Cfg {
-  static constexpr int KC = D / 32;             // k-chunks of a score tile
-  static constexpr int NT = D / 16;             // value channel tiles
-  static constexpr int KW = kKW<D, BK>;         // key words per lane and row
-  static constexpr int SL = 16 / GQ;            // MFMA columns per head
-  static constexpr int IPH = 4 * KC;            // fold items per head
-  static constexpr int ITEMS = GQ * IPH;        // fold items per key group
-  static constexpr int IPL = (ITEMS + 63) / 64;  // fold items per lane
-  static constexpr int MAXNF = (4 + SL - 1) / SL;  // value-B fragments (NG <= 4)
-  // LDS (bytes): per wave q' fragments [2][GQ][4][KC] x 16 B + beta [GQ] floats
+  static constexpr int G = D / NG;
+  static constexpr int KC = D / 32;               // k-chunks of a score tile
+  static constexpr int NT = D / 16;               // value channel tiles
+  static constexpr int KW = kKW<D, BK>;           // key words per lane and row
+  static constexpr int WR = D * BK / 32;          // words per key row
+  static constexpr int SL = 16 / GQ;              // MFMA columns per head
+  static constexpr int NF = (NG + SL - 1) / SL;   // value-side B fragments
+  static constexpr int IPH = 4 * KC;              // fold items per head
+  static constexpr int ITEMS = GQ * IPH;          // fold items per key group
+  static constexpr int IPL = (ITEMS + 63) / 64;   // fold items per lane
+  // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ]
   static constexpr int kQB = 2 * GQ * 4 * KC * 16;
   static constexpr int kWaveLds = kQB + 16 * ((GQ * 4 + 15) / 16);
+  static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
 };
 
-template <int D, int BK, int BV, int GQ>
+// Loads of one 32-token chunk (a lane's share).
+template <int D, int BK, int BV, int GQ, int NG>
+struct Raw {
+  using C = Cfg<D, BK, BV, GQ, NG>;
+  uint32_t kw[2][C::KW];              // key code words of score tiles 0, 1
+  uint32_t vw[C::NT];                 // value code word per channel tile
+  uint32_t vmA[C::NF][4], vmB[C::NF][4];  // value (scale, min) of the B elements
+};
+
+template <int D, int BK, int BV, int GQ, int NG>
+struct PackedWave {
+  using C = Cfg<D, BK, BV, GQ, NG>;
+  using R = Raw<D, BK, BV, GQ, NG>;
+  static constexpr int KC = C::KC, NT = C::NT, KW = C::KW, WR = C::WR, SL = C::SL;
+  static constexpr int NF = C::NF, IPH = C::IPH, IPL = C::IPL, G = C::G;
+  // With two or more MFMA columns per head, the hi and lo parts of q' go to
+  // neighbouring columns (one MFMA per k-chunk, one DPP add to recombine);
+  // with one column per head they are two MFMAs into the same accumulator.
+  static constexpr bool kColSplit = SL >= 2;
+  static constexpr int KP = kColSplit ? 1 : 2;  // q' parts held per lane
+
+  // wave-uniform bases
+  const uint32_t* kcodes;
+  const uint32_t* kmeta;
+  const uint32_t* vcodes;
+  const uint32_t* vmeta;
+  const float* qfs;
+  uint4* qB;
+  float* beta_l;
+  int c_lo, c_hi;
+  // lane constants
+  int lane, col, lg, hcol, slot;
+  int koff[2];
+  int voff;
+  int vmoff[NF][2];
+  int kmoff[IPL][2];
+  int fitem[IPL];
+  float kscale, bscale;
+  // state
+  f4 oacc[NT];
+  float m_run, l_run;
+  float bias[NF];
+  uint32_t bq[KP][KC][4];
+  uint4 kmA[IPL], kmB[IPL];  // key (scale, min) for the next fold
+  float beta_c;
+  int cur_group;
+
+  __device__ void init(int lane_) {
+    lane = lane_;
+    col = lane & 15;
+    lg = lane >> 4;
+    hcol = col / SL;
+    slot = col % SL;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      koff[u] = tok_v<BV>(col >> 2, 4 * u + (col & 3)) * WR + lg * KW;
+    voff = col * BV + (BV == 4 ? lg : (lg >> 1));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int gm = (f * SL + slot) % NG;
+      vmoff[f][0] = gm * kVBlock + tok_v<BV>(lg, 0);
+      vmoff[f][1] = gm * kVBlock + tok_v<BV>(lg, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) {
+      const int it = lane + 64 * i;
+      fitem[i] = it;
+      const int r = it % IPH, gg = r / KC, kc = r % KC;
+      kmoff[i][0] = key_run0<D, BK>(gg, kc);
+      kmoff[i][1] = kmoff[i][0] + kKeyOff<BK>;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
+    m_run = kNegInf;
+    l_run = 0.0f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) bias[f] = 0.0f;
+    beta_c = 0.0f;
+    cur_group = -1;
+  }
+
+  __device__ __forceinline__ void load(int ch, R& r) const {
+    const uint32_t* kc = kcodes + (int64_t)ch * kChunk * WR;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) load_words<KW>(kc + koff[u], r.kw[u]);
+    const uint32_t* vc = vcodes + (int64_t)ch * D * BV;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) r.vw[n] = vc[voff + 16 * n * BV];
+    const uint32_t* vm = vmeta + (int64_t)ch * NG * kVBlock;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint4 a = *reinterpret_cast<const uint4*>(vm + vmoff[f][0]);
+      const uint4 c = *reinterpret_cast<const uint4*>(vm + vmoff[f][1]);
+      r.vmA[f][0] = a.x; r.vmA[f][1] = a.y; r.vmA[f][2] = a.z; r.vmA[f][3] = a.w;
+      r.vmB[f][0] = c.x; r.vmB[f][1] = c.y; r.vmB[f][2] = c.z; r.vmB[f][3] = c.w;
+    }
+  }
+
+  // Key meta of group grp for the next fold.
+  __device__ __forceinline__ void load_kmeta(int grp) {
+    const uint32_t* km = kmeta + (int64_t)grp * D;
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) {
+      if (fitem[i] < C::ITEMS) {
+        kmA[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][0]);
+        kmB[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][1]);
+      }
+    }
+  }
+
+  // q' = q * 2^-E * key scale (hi/lo fp16 fragments in LDS) and beta' =
+  // q * 2^-E . key min, for the key group starting in this chunk.
+  __device__ __forceinline__ void fold() {
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) {
+      const int it = fitem[i];
+      float bpart = 0.0f;
+      if (it < C::ITEMS) {
+        const int h = it / IPH, rr = it % IPH, gg = rr / KC, kc = rr % KC;
+        const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][0]);
+        const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][1]);
+        const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qBv[4] = {qb.x, qb.y, qb.z, qb.w};
+        const uint32_t mA[4] = {kmA[i].x, kmA[i].y, kmA[i].z, kmA[i].w};
+        const uint32_t mB[4] = {kmB[i].x, kmB[i].y, kmB[i].z, kmB[i].w};
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), hp[e], lp[e]);
+          bpart = mul_hi(qA[e], mA[e], bpart);
+          bpart = mul_hi(qBv[e], mB[e], bpart);
+        }
+        qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+        qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+      }
+      bpart = group_sum<IPH>(bpart);
+      if (it < C::ITEMS && (it % IPH) == 0) beta_l[it / IPH] = bpart;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int p = 0; p < KP; ++p)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int part = kColSplit ? (slot & 1) : p;
+        const uint4 v = qB[((part * GQ + hcol) * 4 + lg) * KC + kc];
+        bq[p][kc][0] = v.x; bq[p][kc][1] = v.y; bq[p][kc][2] = v.z; bq[p][kc][3] = v.w;
+      }
+    beta_c = beta_l[hcol] * bscale;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  __device__ __forceinline__ void process(int ch, const R& r) {
+    const int grp = (ch * kChunk) / G;
+    if (grp != cur_group) {
+      cur_group = grp;
+      fold();
+    }
+    // key meta of the next chunk's group loads while this chunk runs; it is
+    // issued unconditionally (the group index is clamped by the caller's
+    // chunk range) so the memory counters stay exact on every path.
+    load_kmeta(((ch + 1 < c_hi ? ch + 1 : ch) * kChunk) / G);
+    // scores: s = 2^(E+24) * (codes x q') + beta
+    float s[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t a[KC][4];
+      unpack_keys<D, BK>(r.kw[u], a);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        acc = mfma(a[kc], bq[0][kc], acc);
+        if constexpr (!kColSplit) acc = mfma(a[kc], bq[1][kc], acc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = acc[q];
+        if constexpr (kColSplit) {
+          // hi column + lo column (lanes col and col ^ 1 of a quad)
+          x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                   __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+        }
+        s[u][q] = __builtin_fmaf(x, kscale, beta_c);
+      }
+    }
+    // online softmax (exact running max; rescale only when it grows).  Each
+    // lane tests its own 8 scores; the cross-lane maximum is only formed on
+    // the (rare) path where some lane sees a larger score.
+    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    if (__any(cm > m_run)) {
+      cm = xor_max(cm, 16);
+      cm = xor_max(cm, 32);
+      const float m_new = fmaxf(m_run, cm);
+      const float a = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= a;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) oacc[n] *= a;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) bias[f] *= a;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p[u][q] = exp2f(s[u][q] - m_run);
+        l_run += p[u][q];
+      }
+    // weighted value sum
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // elements 2i (run A) and 2i+1 (run B) = score tile i/2, rows 2(i%2), +1
+        const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
+        split2(mul_lo(pa, r.vmA[f][i]), mul_lo(pb, r.vmB[f][i]), bh[i], bl[i]);
+        bias[f] = mul_hi(pa, r.vmA[f][i], bias[f]);
+        bias[f] = mul_hi(pb, r.vmB[f][i], bias[f]);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        if (C::gam(n) / SL != f) continue;  // compile-time
+        uint32_t a[4];
+        if constexpr (BV == 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = (r.vw[n] >> (4 * e)) & 0x000F000Fu;
+        } else {
+          const int sh = 8 * (lg & 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = (r.vw[n] >> (sh + 2 * e)) & 0x00030003u;
+        }
+        oacc[n] = mfma(a, bh, oacc[n]);
+        oacc[n] = mfma(a, bl, oacc[n]);
+      }
+    }
+  }
+};
+
+template <int D, int BK, int BV, int GQ, int NG>
 __device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split, int t0,
                                int t1, char* smem) {
-  using C = Cfg<D, BK, BV, GQ>;
-  constexpr int KC = C::KC, NT = C::NT, KW = C::KW, SL = C::SL, IPH = C::IPH;
-  constexpr int MAXNF = C::MAXNF;
+  using C = Cfg<D, BK, BV, GQ, NG>;
+  using W = PackedWave<D, BK, BV, GQ, NG>;
+  using R = Raw<D, BK, BV, GQ, NG>;
+  constexpr int NT = C::NT, SL = C::SL, NF = C::NF;
   const Geom& g = L.g;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, lg = lane >> 4;
-  const int hcol = col / SL, slot = col % SL;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t unit = (int64_t)b * g.Hkv + hkv;
-  const int G = g.G, NG = D / G;
-  const int NF = (NG + SL - 1) / SL;
 
-  // ---- shared memory: scaled query, exponents, per-wave fold buffers ----
   float* qfs = reinterpret_cast<float*>(smem);            // [GQ][D] q * 2^-E
   int* qexp = reinterpret_cast<int*>(qfs + GQ * D);       // [GQ]
-  char* wbase = smem + (GQ * D + 16) * 4;
-  uint4* qB = reinterpret_cast<uint4*>(wbase + wave * C::kWaveLds);  // [2][GQ][4][KC]
-  float* beta_l = reinterpret_cast<float*>(wbase + wave * C::kWaveLds + C::kQB);
+  char* wbase = smem + (GQ * D + 16) * 4 + wave * C::kWaveLds;
 
   for (int i = tid; i < GQ * D; i += kThreads)
     qfs[i] = h2f(L.q[((int64_t)b * g.Hq + hkv * GQ) * D + i]) * L.scale_log2;
@@ -305,191 +583,50 @@ __device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split,
   for (int i = tid; i < GQ * D; i += kThreads) qfs[i] = ldexpf(qfs[i], -qexp[i / D]);
   __syncthreads();
 
-  const int e_h = qexp[hcol];
-  const float kscale = ldexpf(1.0f, e_h + 24);  // codes are fp16 numbers c*2^-24
-  const float bscale = ldexpf(1.0f, e_h);
-
-  // ---- this wave's chunks ----
+  W w;
+  w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
+  w.kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) + unit * (g.C / C::G) * D;
+  w.vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
+  w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
+            unit * (g.C / kVBlock) * NG * kVBlock;
+  w.qfs = qfs;
+  w.qB = reinterpret_cast<uint4*>(wbase);
+  w.beta_l = reinterpret_cast<float*>(wbase + C::kQB);
   const int nchunks = (t1 - t0) / kChunk;
   const int c_lo = t0 / kChunk + (nchunks * wave) / kWaves;
   const int c_hi = t0 / kChunk + (nchunks * (wave + 1)) / kWaves;
+  w.c_lo = c_lo;
+  w.c_hi = c_hi;
+  w.init(lane);
+  const int e_h = qexp[w.hcol];
+  w.kscale = ldexpf(1.0f, e_h + 24);  // codes are the fp16 numbers c * 2^-24
+  w.bscale = ldexpf(1.0f, e_h);
 
-  const uint32_t* kcodes = L.cache.k_codes + unit * g.C * (D * BK / 32);
-  const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) +
-                          unit * (g.C / G) * D;
-  const uint32_t* vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
-  const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
-                          unit * (g.C / kVBlock) * NG * kVBlock;
-
-  // key rows this lane feeds (row = col of tile u) and its word offset
-  int krow[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) krow[u] = tok_v<BV>(col >> 2, 4 * u + (col & 3));
-  const int vword = BV == 4 ? lg : (lg >> 1);
-  const int vshift = BV == 4 ? 0 : 8 * (lg & 1);
-  const int vrun0 = tok_v<BV>(lg, 0);        // tokens of run A (elements 2e)
-  const int vrun1 = tok_v<BV>(lg, 1);        // tokens of run B (elements 2e+1)
-
-  f4 oacc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.0f;
-  float bias[MAXNF];
-#pragma unroll
-  for (int f = 0; f < MAXNF; ++f) bias[f] = 0.0f;
-
-  int cur_group = -1;
-  uint32_t bq[2][KC][4];  // q' hi / lo fragments of the current key group
-  float beta_c = 0.0f;    // beta' of this lane's head, scaled
-
-  for (int ch = c_lo; ch < c_hi; ++ch) {
-    const int tbase = ch * kChunk;
-    // ---------------- loads of this chunk ----------------
-    uint32_t kw[2][KW];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      load_words<KW>(kcodes + (int64_t)(tbase + krow[u]) * (D * BK / 32) + lg * KW, kw[u]);
-    uint32_t vw[NT];
-    const uint32_t* vblk = vcodes + (int64_t)ch * D * BV;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) vw[n] = vblk[(16 * n + col) * BV + vword];
-    uint32_t vmA[MAXNF][4], vmB[MAXNF][4];
-#pragma unroll
-    for (int f = 0; f < MAXNF; ++f) {
-      if (f < NF) {
-        const int gam = (f * SL + slot) % NG;
-        const uint32_t* m = vmeta + ((int64_t)ch * NG + gam) * kVBlock;
-        const uint4 a = *reinterpret_cast<const uint4*>(m + vrun0);
-        const uint4 c = *reinterpret_cast<const uint4*>(m + vrun1);
-        vmA[f][0] = a.x; vmA[f][1] = a.y; vmA[f][2] = a.z; vmA[f][3] = a.w;
-        vmB[f][0] = c.x; vmB[f][1] = c.y; vmB[f][2] = c.z; vmB[f][3] = c.w;
-      }
-    }
-
-    // ---------------- fold of a new key group ----------------
-    const int grp = tbase / G;
-    if (grp != cur_group) {
-      cur_group = grp;
-      const uint32_t* km = kmeta + (int64_t)grp * D;
-      for (int it0 = 0; it0 < C::IPL * 64; it0 += 64) {
-        const int it = it0 + lane;
-        float bpart = 0.0f;
-        if (it < C::ITEMS) {
-          const int h = it / IPH, r = it % IPH, gg = r / KC, kc = r % KC;
-          const int c0 = key_run0<D, BK>(gg, kc), c1 = c0 + kKeyOff<BK>;
-          const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + c0);
-          const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + c1);
-          const uint4 ma = *reinterpret_cast<const uint4*>(km + c0);
-          const uint4 mb = *reinterpret_cast<const uint4*>(km + c1);
-          const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qB4[4] = {qb.x, qb.y, qb.z, qb.w};
-          const uint32_t mA[4] = {ma.x, ma.y, ma.z, ma.w}, mB[4] = {mb.x, mb.y, mb.z, mb.w};
-          uint32_t hp[4], lp[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float xa = qA[e] * h2f((uint16_t)(mA[e] & 0xffffu));
-            const float xb = qB4[e] * h2f((uint16_t)(mB[e] & 0xffffu));
-            split2(xa, xb, hp[e], lp[e]);
-            bpart += qA[e] * h2f((uint16_t)(mA[e] >> 16)) + qB4[e] * h2f((uint16_t)(mB[e] >> 16));
-          }
-          qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
-          qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
-        }
-#pragma unroll
-        for (int off = IPH / 2; off >= 1; off >>= 1) bpart = xor_sum(bpart, off);
-        if (it < C::ITEMS && (it % IPH) == 0) beta_l[it / IPH] = bpart;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const uint4 v = qB[((p * GQ + hcol) * 4 + lg) * KC + kc];
-          bq[p][kc][0] = v.x; bq[p][kc][1] = v.y; bq[p][kc][2] = v.z; bq[p][kc][3] = v.w;
-        }
-      beta_c = beta_l[hcol] * bscale;
-      __builtin_amdgcn_wave_barrier();
-    }
-
-    // ---------------- scores ----------------
-    float s[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      uint32_t a[KC][4];
-      unpack_keys<D, BK>(kw[u], a);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        acc = mfma(a[kc], bq[0][kc], acc);
-        acc = mfma(a[kc], bq[1][kc], acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[u][r] = acc[r] * kscale + beta_c;
-    }
-
-    // ---------------- online softmax ----------------
-    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    cm = xor_max(cm, 16);
-    cm = xor_max(cm, 32);
-    const float m_new = fmaxf(m_run, cm);
-    if (__any(m_new > m_run)) {
-      const float a = exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= a;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) oacc[n] *= a;
-#pragma unroll
-      for (int f = 0; f < MAXNF; ++f) bias[f] *= a;
-    }
-    float p[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[u][r] = exp2f(s[u][r] - m_run);
-        l_run += p[u][r];
-      }
-
-    // ---------------- weighted value sum ----------------
-#pragma unroll
-    for (int f = 0; f < MAXNF; ++f) {
-      if (f >= NF) break;
-      uint32_t bh[4], bl[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // elements 2i (run A, token tok_v(lg, 2i)) and 2i+1 (run B)
-        const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
-        const float xa = pa * h2f((uint16_t)(vmA[f][i] & 0xffffu));
-        const float xb = pb * h2f((uint16_t)(vmB[f][i] & 0xffffu));
-        split2(xa, xb, bh[i], bl[i]);
-        bias[f] += pa * h2f((uint16_t)(vmA[f][i] >> 16)) + pb * h2f((uint16_t)(vmB[f][i] >> 16));
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int gam = (16 * n) / G;
-        if (gam / SL != f) continue;
-        uint32_t a[4];
-        if constexpr (BV == 4) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = (vw[n] >> (4 * e)) & 0x000F000Fu;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = (vw[n] >> (vshift + 2 * e)) & 0x00030003u;
-        }
-        oacc[n] = mfma(a, bh, oacc[n]);
-        oacc[n] = mfma(a, bl, oacc[n]);
-      }
+  // two chunk buffers: the next chunk's loads are in flight while one is
+  // used.  Prefetches past the wave's last chunk re-load that chunk (always in
+  // bounds) instead of being skipped, so no load sits under a branch.
+  R ra, rb;
+  if (c_lo < c_hi) {
+    const int last = c_hi - 1;
+    w.load_kmeta((c_lo * kChunk) / C::G);
+    w.load(c_lo, ra);
+    for (int ch = c_lo; ch < c_hi; ch += 2) {
+      w.load(min(ch + 1, last), rb);
+      w.process(ch, ra);
+      if (ch + 1 >= c_hi) break;
+      w.load(min(ch + 2, last), ra);
+      w.process(ch + 1, rb);
     }
   }
 
   // ---------------- merge lane groups, then waves ----------------
+  float l_run = w.l_run;
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);
+  float bias[NF];
 #pragma unroll
-  for (int f = 0; f < MAXNF; ++f) {
-    bias[f] = xor_sum(bias[f], 16);
+  for (int f = 0; f < NF; ++f) {
+    bias[f] = xor_sum(w.bias[f], 16);
     bias[f] = xor_sum(bias[f], 32);
   }
   __syncthreads();  // fold buffers are reused for the merge below
@@ -497,30 +634,30 @@ __device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split,
   float* mine = cmb + wave * GQ * (D + 2);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const int gam = (16 * n) / G;
-    if (gam % SL != slot) continue;
-    const float bsum = bias[gam / SL];
+    const int gm = C::gam(n);
+    if (gm % SL != w.slot) continue;
+    const float bsum = bias[gm / SL];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      mine[hcol * (D + 2) + 16 * n + 4 * lg + r] = oacc[n][r] * 16777216.0f + bsum;
+    for (int q = 0; q < 4; ++q)
+      mine[w.hcol * (D + 2) + 16 * n + 4 * w.lg + q] = w.oacc[n][q] * 16777216.0f + bsum;
   }
-  if (lg == 0 && slot == 0) {
-    mine[hcol * (D + 2) + D] = m_run;
-    mine[hcol * (D + 2) + D + 1] = l_run;
+  if (w.lg == 0 && w.slot == 0) {
+    mine[w.hcol * (D + 2) + D] = w.m_run;
+    mine[w.hcol * (D + 2) + D + 1] = l_run;
   }
   __syncthreads();
   for (int i = tid; i < GQ * D; i += kThreads) {
     const int h = i / D, c = i % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cmb[(w * GQ + h) * (D + 2) + D]);
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, cmb[(v * GQ + h) * (D + 2) + D]);
     float Ls = 0.0f, acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* s = cmb + (w * GQ + h) * (D + 2);
-      const float wt = (s[D] == kNegInf) ? 0.0f : exp2f(s[D] - M);
-      Ls += s[D + 1] * wt;
-      acc += s[c] * wt;
+    for (int v = 0; v < kWaves; ++v) {
+      const float* sv = cmb + (v * GQ + h) * (D + 2);
+      const float wt = (sv[D] == kNegInf) ? 0.0f : exp2f(sv[D] - M);
+      Ls += sv[D + 1] * wt;
+      acc += sv[c] * wt;
     }
     const int64_t bh = (int64_t)b * g.Hq + hkv * GQ + h;
     float* part = L.ws + (bh * (L.n_split + 1) + split) * (D + 2);
@@ -532,9 +669,9 @@ __device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split,
   }
 }
 
-template <int D, int BK, int BV, int GQ>
+template <int D, int BK, int BV, int GQ, int NG>
 constexpr int kSmemBytes() {
-  using C = Cfg<D, BK, BV, GQ>;
+  using C = Cfg<D, BK, BV, GQ, NG>;
   constexpr int packed = (GQ * D + 16) * 4 + kWaves * C::kWaveLds;
   constexpr int merge = kWaves * GQ * (D + 2) * 4;
   constexpr int resid = (GQ * D + GQ * kChunk + 3 * GQ) * 4;
@@ -544,9 +681,9 @@ constexpr int kSmemBytes() {
 
 // grid: (n_split + 1, Hkv, B).  x < n_split: packed tokens of split x;
 // x == n_split: the residual window.
-template <int D, int BK, int BV, int GQ>
+template <int D, int BK, int BV, int GQ, int NG>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeLaunch L) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D, BK, BV, GQ>()];
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D, BK, BV, GQ, NG>()];
   const Geom& g = L.g;
   const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int n = L.seq_lens[b];
@@ -559,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeLaunch L
   const int t0 = split * L.split_tokens;
   const int t1 = min(lq, t0 + L.split_tokens);
   if (t0 >= t1) return;  // no packed tokens here: the combine skips this split
-  packed_partial<D, BK, BV, GQ>(L, b, hkv, split, t0, t1, smem);
+  packed_partial<D, BK, BV, GQ, NG>(L, b, hkv, split, t0, t1, smem);
 }
 
 // Merges the partials of one (sequence, query head).
@@ -593,18 +730,33 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeLaunch L) {
   L.out[bh * D + c] = f2h(acc / Ls);
 }
 
+template <int D, int BK, int BV, int GQ>
+hipError_t dispatch_ng(const DecodeLaunch& L, dim3 grid, hipStream_t st) {
+  switch (D / L.g.G) {
+    case 1: decode_partial_kernel<D, BK, BV, GQ, 1><<<grid, kThreads, 0, st>>>(L); break;
+    case 2: decode_partial_kernel<D, BK, BV, GQ, 2><<<grid, kThreads, 0, st>>>(L); break;
+    case 4:
+      if constexpr (D == 128) {
+        decode_partial_kernel<D, BK, BV, GQ, 4><<<grid, kThreads, 0, st>>>(L);
+        break;
+      }
+      [[fallthrough]];
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int BK, int BV>
 hipError_t dispatch_gq(const DecodeLaunch& L, hipStream_t st) {
   dim3 grid(L.n_split + 1, L.g.Hkv, L.g.B);
   switch (L.g.Hq / L.g.Hkv) {
-    case 1: decode_partial_kernel<D, BK, BV, 1><<<grid, kThreads, 0, st>>>(L); break;
-    case 2: decode_partial_kernel<D, BK, BV, 2><<<grid, kThreads, 0, st>>>(L); break;
-    case 4: decode_partial_kernel<D, BK, BV, 4><<<grid, kThreads, 0, st>>>(L); break;
-    case 8: decode_partial_kernel<D, BK, BV, 8><<<grid, kThreads, 0, st>>>(L); break;
-    case 16: decode_partial_kernel<D, BK, BV, 16><<<grid, kThreads, 0, st>>>(L); break;
+    case 1: return dispatch_ng<D, BK, BV, 1>(L, grid, st);
+    case 2: return dispatch_ng<D, BK, BV, 2>(L, grid, st);
+    case 4: return dispatch_ng<D, BK, BV, 4>(L, grid, st);
+    case 8: return dispatch_ng<D, BK, BV, 8>(L, grid, st);
+    case 16: return dispatch_ng<D, BK, BV, 16>(L, grid, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int D>
