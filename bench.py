@@ -192,7 +192,7 @@ def main():
     ws = kvq.alloc_workspace(g, max_len, dev)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
     scale = 1.0 / math.sqrt(w.head_dim)
-    n_split, split_tokens = kvq.kvq_decode_splits(g, max_len)
+    n_workers = kvq.kvq_decode_workers(g)
 
     # algorithmic bytes of every step
     step_bytes, dec_bytes = [], []
@@ -221,7 +221,7 @@ def main():
         kvq.kvq_decode_partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
         if timed_idx is not None:
             ev_b[timed_idx].record(stream)
-        kvq.kvq_decode_combine(g, lens_dev[s, 1], max_len, ws, out, stream)
+        kvq.kvq_decode_combine(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
 
     for s in range(a.warmup):
         step(s)
@@ -262,7 +262,7 @@ def main():
             "group": w.group, "residual": w.residual,
             "context_first_step": int(lens_host[a.warmup, 1].max()),
             "context_last_step": int(lens_host[-1, 1].max()),
-            "rotating_layer_caches": L, "n_split": n_split, "split_tokens": split_tokens,
+            "rotating_layer_caches": L, "decode_worker_waves": n_workers,
             "step": "kvq_append (+flush when a window fills) + kvq_decode_attn, one layer",
         },
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),

@@ -178,17 +178,17 @@ int kvq_validate_geom(const kvq_geom *geom);
  * v_meta, k_res, v_res.  out must hold 6 entries. */
 int kvq_cache_bytes(const kvq_geom *geom, size_t out[6]);
 
-/* Split-context sizing used by kvq_decode_attn for a launch whose longest
- * sequence has max_seq_len tokens (1 <= max_seq_len <= capacity): the number of
- * splits per (sequence, KV head) and the tokens per split (a multiple of G).
- * Depends on the geometry, max_seq_len and the compute-unit count of the
- * current device (queried once per device). */
-int kvq_decode_splits(const kvq_geom *geom, int32_t max_seq_len,
-                      int32_t *n_split, int32_t *split_tokens);
+/* Worker waves of the decode partial kernel on the current device: the
+ * waves the GPU keeps resident at once for this geometry (from the kernel's
+ * register and LDS use, times the compute-unit count; queried once per device).
+ * The packed 32-token chunks of all (sequence, KV head) units are split into
+ * that many equal contiguous shares, one per wave (split-context attention with
+ * balanced splits for any mix of sequence lengths). */
+int kvq_decode_workers(const kvq_geom *geom, int32_t *n_workers);
 
-/* Workspace bytes kvq_decode_attn needs for max_seq_len: fp32 partials
- * [B][Hq][n_split + 1][head_dim + 2] (one per split of the packed tokens and
- * one for the residual window). */
+/* Workspace bytes kvq_decode_attn needs: fp32 partials, one per (worker wave,
+ * unit) pair a launch produces, at most kvq_decode_workers() + B * Hkv of them,
+ * each [Hq/Hkv][head_dim + 4].  max_seq_len is range-checked only. */
 int kvq_decode_workspace_bytes(const kvq_geom *geom, int32_t max_seq_len,
                                size_t *bytes);
 
@@ -244,13 +244,14 @@ int kvq_append(const kvq_geom *geom, const uint16_t *k_new,
                const kvq_cache *cache, void *stream);
 
 /* Single-token decode attention over the packed cache plus the residual window
- * (split-context partial softmax, then a combine; GQA heads of one KV head are
- * processed together).
+ * (split-context partial softmax over the packed tokens, then a combine that
+ * also covers the fp16 residual window; GQA heads of one KV head are processed
+ * together).
  *   q           device fp16 [B][Hq][D]: the current token's queries.
  *   seq_lens    device int32 [B]: tokens per sequence INCLUDING the current one
  *               (the current token must already be appended).
  *   max_seq_len host int32: an upper bound of every seq_lens[b];
- *               1 <= max_seq_len <= capacity.  Sizes the grid and workspace.
+ *               1 <= max_seq_len <= capacity.
  *   sm_scale    softmax scale (1/sqrt(D) for standard attention).
  *   workspace   device memory of at least kvq_decode_workspace_bytes(geom,
  *               max_seq_len) bytes, 16-byte aligned; contents on entry do not
@@ -267,16 +268,19 @@ int kvq_decode_attn(const kvq_geom *geom, const uint16_t *q,
 /* The two phases of kvq_decode_attn, for callers that time or schedule them
  * apart.  kvq_decode_attn(...) == kvq_decode_partial(...) followed by
  * kvq_decode_combine(...) on the same stream with the same arguments.
- * kvq_decode_partial writes per-split (max, sum, weighted value sum) partials
- * into the workspace and does not touch out; kvq_decode_combine merges them
- * into out. */
+ * kvq_decode_partial covers the packed tokens, writing (max, sum, weighted
+ * value sum) partials into the workspace, and does not touch out;
+ * kvq_decode_combine attends over the residual window, merges it with the
+ * partials and writes out. */
 int kvq_decode_partial(const kvq_geom *geom, const uint16_t *q,
                        const kvq_cache *cache, const int32_t *seq_lens,
                        int32_t max_seq_len, float sm_scale, void *workspace,
                        size_t workspace_bytes, uint16_t *out, void *stream);
-int kvq_decode_combine(const kvq_geom *geom, const int32_t *seq_lens,
-                       int32_t max_seq_len, const void *workspace,
-                       size_t workspace_bytes, uint16_t *out, void *stream);
+int kvq_decode_combine(const kvq_geom *geom, const uint16_t *q,
+                       const kvq_cache *cache, const int32_t *seq_lens,
+                       int32_t max_seq_len, float sm_scale,
+                       const void *workspace, size_t workspace_bytes,
+                       uint16_t *out, void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -35,7 +35,7 @@ KVQ_ERR_INTERNAL = -8
 
 EXPORTS = [
     "kvq_abi_version", "kvq_layout_version", "kvq_status_str", "kvq_last_error",
-    "kvq_validate_geom", "kvq_cache_bytes", "kvq_decode_splits",
+    "kvq_validate_geom", "kvq_cache_bytes", "kvq_decode_workers",
     "kvq_decode_workspace_bytes", "kvq_quantize_keys_perchannel",
     "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append",
     "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
@@ -81,8 +81,7 @@ def lib() -> ctypes.CDLL:
             "kvq_last_error": (ctypes.c_char_p, []),
             "kvq_validate_geom": (ctypes.c_int, [G]),
             "kvq_cache_bytes": (ctypes.c_int, [G, ctypes.POINTER(sz)]),
-            "kvq_decode_splits": (ctypes.c_int, [G, i32, ctypes.POINTER(i32),
-                                                 ctypes.POINTER(i32)]),
+            "kvq_decode_workers": (ctypes.c_int, [G, ctypes.POINTER(i32)]),
             "kvq_decode_workspace_bytes": (ctypes.c_int, [G, i32, ctypes.POINTER(sz)]),
             "kvq_quantize_keys_perchannel": (ctypes.c_int, [G, P, i32, i32, P, P, P]),
             "kvq_quantize_values_pertoken": (ctypes.c_int, [G, P, i32, i32, P, P, P]),
@@ -90,7 +89,7 @@ def lib() -> ctypes.CDLL:
             "kvq_append": (ctypes.c_int, [G, P, P, P, C, P]),
             "kvq_decode_attn": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_partial": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
-            "kvq_decode_combine": (ctypes.c_int, [G, P, i32, P, sz, P, P]),
+            "kvq_decode_combine": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -176,12 +175,12 @@ def kvq_cache_bytes(g: Geom) -> list[int]:
     return list(out)
 
 
-def kvq_decode_splits(g: Geom, max_seq_len: int) -> tuple[int, int]:
+def kvq_decode_workers(g: Geom) -> int:
     gc = g.c()
-    ns, st = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().kvq_decode_splits(ctypes.byref(gc), max_seq_len, ctypes.byref(ns),
-                                   ctypes.byref(st)), "kvq_decode_splits")
-    return ns.value, st.value
+    nw = ctypes.c_int32()
+    _check(lib().kvq_decode_workers(ctypes.byref(gc), ctypes.byref(nw)),
+           "kvq_decode_workers")
+    return nw.value
 
 
 def kvq_decode_workspace_bytes(g: Geom, max_seq_len: int) -> int:
@@ -310,16 +309,11 @@ def kvq_decode_partial(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.T
     _check(lib().kvq_decode_partial(*args, _stream(stream)), "kvq_decode_partial")
 
 
-def kvq_decode_combine(g: Geom, seq_lens: torch.Tensor, max_seq_len: int,
-                       workspace: torch.Tensor | None, out: torch.Tensor,
-                       stream=None) -> None:
-    gc = g.c()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().kvq_decode_combine(
-        ctypes.byref(gc), _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(max_seq_len),
-        _ptr(workspace, "workspace"), ws_bytes,
-        _ptr(out, "out", _F16, (g.batch, g.n_q_heads, g.head_dim)), _stream(stream)),
-        "kvq_decode_combine")
+def kvq_decode_combine(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,
+                       max_seq_len: int, sm_scale: float, workspace: torch.Tensor | None,
+                       out: torch.Tensor, stream=None) -> None:
+    args, keep = _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
+    _check(lib().kvq_decode_combine(*args, _stream(stream)), "kvq_decode_combine")
 
 
 def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:

@@ -108,36 +108,35 @@ int cu_count(int* out) {
   return KVQ_OK;
 }
 
-// Split sizing: about four workgroups per compute unit over all (sequence, KV
-// head) units, at least 256 tokens per split, a multiple of the key group so
-// no key group straddles two splits.
-int splits_for(const kvq_geom* g, int32_t max_seq_len, int32_t* n_split,
-               int32_t* split_tokens) {
-  if (max_seq_len < 1 || max_seq_len > g->capacity)
-    return fail(KVQ_ERR_RANGE, "max_seq_len (%d) must be in [1, capacity=%d]",
-                max_seq_len, g->capacity);
+// Worker waves of the persistent partial kernel (resident waves x CUs).
+int workers_for(const kvq_geom* g, int32_t* n_workers) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != KVQ_OK) return st;
-  const int64_t units = (int64_t)g->batch * g->n_kv_heads;
-  const int64_t target = 4 * (int64_t)cus;
-  int64_t tokens = ((int64_t)max_seq_len * units + target - 1) / target;
-  if (tokens < 256) tokens = 256;
-  const int64_t q = g->group;
-  tokens = (tokens + q - 1) / q * q;
-  if (tokens > max_seq_len) tokens = ((int64_t)max_seq_len + q - 1) / q * q;
-  *split_tokens = (int32_t)tokens;
-  *n_split = (int32_t)(((int64_t)max_seq_len + tokens - 1) / tokens);
+  int w = 0;
+  hipError_t e = kvq::decode_workers(kvq::to_geom(*g), cus, &w);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query");
+  *n_workers = w;
   return KVQ_OK;
 }
 
-// Partials: n_split packed splits plus the residual window, per query head.
-size_t workspace_need(const kvq_geom* g, int32_t n_split) {
-  return (size_t)g->batch * g->n_q_heads * (n_split + 1) * (g->head_dim + 2) * sizeof(float);
+int check_max_len(const kvq_geom* g, int32_t max_seq_len) {
+  if (max_seq_len < 1 || max_seq_len > g->capacity)
+    return fail(KVQ_ERR_RANGE, "max_seq_len (%d) must be in [1, capacity=%d]",
+                max_seq_len, g->capacity);
+  return KVQ_OK;
 }
 
-int check_workspace(const kvq_geom* g, int32_t n_split, const void* ws, size_t bytes) {
-  const size_t need = workspace_need(g, n_split);
+// Partials: one per (worker wave, unit) pair that occurs, at most
+// n_workers + B*Hkv, each [Hq/Hkv][head_dim + 4] floats.
+size_t workspace_need(const kvq_geom* g, int32_t n_workers) {
+  const size_t gq = g->n_q_heads / g->n_kv_heads;
+  return ((size_t)n_workers + (size_t)g->batch * g->n_kv_heads) * gq *
+         (g->head_dim + 4) * sizeof(float);
+}
+
+int check_workspace(const kvq_geom* g, int32_t n_workers, const void* ws, size_t bytes) {
+  const size_t need = workspace_need(g, n_workers);
   if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (bytes < need)
@@ -158,16 +157,22 @@ int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_huge_valf() ||
       sm_scale == -__builtin_huge_valf())
     return fail(KVQ_ERR_RANGE, "sm_scale must be finite");
-  int32_t n_split = 0, split_tokens = 0;
-  if ((st = splits_for(geom, max_seq_len, &n_split, &split_tokens)) != KVQ_OK) return st;
-  if ((st = check_workspace(geom, n_split, workspace, workspace_bytes)) != KVQ_OK) return st;
+  if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
+  int32_t n_workers = 0;
+  if ((st = workers_for(geom, &n_workers)) != KVQ_OK) return st;
+  if ((st = check_workspace(geom, n_workers, workspace, workspace_bytes)) != KVQ_OK) return st;
   L->g = kvq::to_geom(*geom);
   L->q = q;
   L->cache = *cache;
   L->seq_lens = seq_lens;
   L->max_seq_len = max_seq_len;
-  L->n_split = n_split;
-  L->split_tokens = split_tokens;
+  L->n_workers = n_workers;
+  {
+    // a residual (fp16) chunk moves rw times the bytes of a packed chunk
+    const int64_t D = geom->head_dim;
+    const int64_t packed = D * (geom->k_bits + geom->v_bits) / 8 + 8 * D / geom->group;
+    L->rw = (int32_t)((4 * D + packed - 1) / packed);
+  }
   L->scale_log2 = sm_scale * 1.4426950408889634f;
   L->ws = static_cast<float*>(workspace);
   L->out = out;
@@ -221,13 +226,12 @@ int kvq_cache_bytes(const kvq_geom* geom, size_t out[6]) {
   return KVQ_OK;
 }
 
-int kvq_decode_splits(const kvq_geom* geom, int32_t max_seq_len, int32_t* n_split,
-                      int32_t* split_tokens) {
+int kvq_decode_workers(const kvq_geom* geom, int32_t* n_workers) {
   try {
     int st = check_geom(geom);
     if (st != KVQ_OK) return st;
-    if (!n_split || !split_tokens) return fail(KVQ_ERR_NULL, "output pointer is NULL");
-    return splits_for(geom, max_seq_len, n_split, split_tokens);
+    if (!n_workers) return fail(KVQ_ERR_NULL, "n_workers is NULL");
+    return workers_for(geom, n_workers);
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");
   }
@@ -238,9 +242,10 @@ int kvq_decode_workspace_bytes(const kvq_geom* geom, int32_t max_seq_len, size_t
     int st = check_geom(geom);
     if (st != KVQ_OK) return st;
     if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
-    int32_t ns = 0, tok = 0;
-    if ((st = splits_for(geom, max_seq_len, &ns, &tok)) != KVQ_OK) return st;
-    *bytes = workspace_need(geom, ns);
+    if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
+    int32_t nw = 0;
+    if ((st = workers_for(geom, &nw)) != KVQ_OK) return st;
+    *bytes = workspace_need(geom, nw);
     return KVQ_OK;
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");
@@ -350,25 +355,15 @@ int kvq_decode_partial(const kvq_geom* geom, const uint16_t* q, const kvq_cache*
   }
 }
 
-int kvq_decode_combine(const kvq_geom* geom, const int32_t* seq_lens, int32_t max_seq_len,
+int kvq_decode_combine(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
+                       const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                        const void* workspace, size_t workspace_bytes, uint16_t* out,
                        void* stream) {
   try {
-    int st = check_geom(geom);
+    kvq::DecodeLaunch L;
+    int st = decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale,
+                          const_cast<void*>(workspace), workspace_bytes, out, &L);
     if (st != KVQ_OK) return st;
-    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
-    if ((st = check_ptr(out, "out")) != KVQ_OK) return st;
-    int32_t n_split = 0, split_tokens = 0;
-    if ((st = splits_for(geom, max_seq_len, &n_split, &split_tokens)) != KVQ_OK) return st;
-    if ((st = check_workspace(geom, n_split, workspace, workspace_bytes)) != KVQ_OK) return st;
-    kvq::DecodeLaunch L{};
-    L.g = kvq::to_geom(*geom);
-    L.seq_lens = seq_lens;
-    L.max_seq_len = max_seq_len;
-    L.n_split = n_split;
-    L.split_tokens = split_tokens;
-    L.ws = const_cast<float*>(static_cast<const float*>(workspace));
-    L.out = out;
     hipError_t e = kvq::launch_decode_combine(L, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
   } catch (...) {
@@ -382,8 +377,8 @@ int kvq_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_cache* ca
   int st = kvq_decode_partial(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
                               workspace_bytes, out, stream);
   if (st != KVQ_OK) return st;
-  return kvq_decode_combine(geom, seq_lens, max_seq_len, workspace, workspace_bytes, out,
-                            stream);
+  return kvq_decode_combine(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                            workspace_bytes, out, stream);
 }
 
 }  // extern "C"

@@ -21,13 +21,15 @@
 // The scaled-query and weight operands are computed once per key group / per
 // 32-token chunk; everything per code is a shift and a mask.
 //
-// Work decomposition: one workgroup (4 waves) per (split, KV head, sequence)
-// over packed tokens; the GQA query heads of the KV head share every load.
-// Each wave runs an online softmax over a contiguous run of 32-token chunks;
-// the 4 wave states merge in LDS into one partial (max, sum, weighted values)
-// per query head.  One extra workgroup per (KV head, sequence) covers the
-// residual window with plain fp32 arithmetic.  The combine kernel merges
-// partials: M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i-M) / L.
+// Work decomposition: a persistent grid of single-wave workgroups, as many
+// as the GPU keeps resident at once.  The packed 32-token chunks of all
+// (sequence, KV head) units form one flat list; every wave takes an equal
+// contiguous share of it (so any mix of sequence lengths is balanced) and runs
+// an online softmax over it, writing one partial (max, sum, weighted values)
+// per unit its share touches.  The GQA query heads of a KV head share every
+// load.  The combine kernel (one workgroup per unit) attends over the fp16
+// residual window and merges it with the unit's partials:
+//   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
 // Scores are kept in log2 units (sm_scale * log2 e folded into q).
 #include "kvq_internal.h"
 
@@ -173,114 +175,6 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[KW])
     w[0] = v.x; w[1] = v.y;
   } else {
     w[0] = p[0];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Residual window (fp16 tokens [t_begin, t_end)), plain fp32 arithmetic over
-// the whole workgroup: 8 lanes per token for scores, one lane per (channel,
-// head group) for the weighted value sum.  Writes partial `part_idx`.
-// ---------------------------------------------------------------------------
-template <int D, int GQ>
-__device__ void residual_partial(const DecodeLaunch& L, int b, int hkv, int t_begin,
-                                 int t_end, int part_idx, float* smem) {
-  constexpr int kTPT = 8, CPT = D / kTPT;
-  constexpr int TPC = kThreads / D, HPT = (GQ + TPC - 1) / TPC;
-  const Geom& g = L.g;
-  float* qf = smem;                      // [GQ][D]
-  float* sc = qf + GQ * D;               // [GQ][kChunk]
-  float* m_run = sc + GQ * kChunk;       // [GQ]
-  float* l_run = m_run + GQ;
-  float* alpha = l_run + GQ;
-  const int tid = threadIdx.x;
-  const int64_t unit = (int64_t)b * g.Hkv + hkv;
-  for (int i = tid; i < GQ * D; i += kThreads)
-    qf[i] = h2f(L.q[((int64_t)b * g.Hq + hkv * GQ) * D + i]) * L.scale_log2;
-  if (tid < GQ) {
-    m_run[tid] = kNegInf;
-    l_run[tid] = 0.0f;
-  }
-  const int c_v = tid % D, hg = tid / D;
-  float o[HPT];
-#pragma unroll
-  for (int i = 0; i < HPT; ++i) o[i] = 0.0f;
-  __syncthreads();
-  const uint16_t* kr = L.cache.k_res + unit * g.R * D;
-  const uint16_t* vr = L.cache.v_res + unit * g.R * D;
-  const int tok = tid / kTPT, sl = tid % kTPT;
-  for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int t = t0 + tok;
-    const bool valid = t < t_end;
-    float acc[GQ];
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) acc[h] = 0.0f;
-    if (valid) {
-      const uint16_t* krow = kr + (int64_t)(t % g.R) * D + sl * CPT;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const float kv = h2f(krow[i]);
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) acc[h] += qf[h * D + sl * CPT + i] * kv;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      acc[h] = xor_sum(acc[h], 1);
-      acc[h] = xor_sum(acc[h], 2);
-      acc[h] = xor_sum(acc[h], 4);
-    }
-    if (sl == 0) {
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) sc[h * kChunk + tok] = valid ? acc[h] : kNegInf;
-    }
-    __syncthreads();
-    for (int i = tid; i < GQ * kChunk; i += kThreads) {
-      const int h = i / kChunk, tk = i % kChunk;
-      const float x = sc[i];
-      float cmax = x;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) cmax = xor_max(cmax, off);
-      const float m_old = m_run[h];
-      const float m_new = fmaxf(m_old, cmax);
-      const float p = exp2f(x - m_new);
-      float psum = p;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) psum = xor_sum(psum, off);
-      sc[i] = p;
-      if (tk == 0) {
-        const float a = exp2f(m_old - m_new);
-        alpha[h] = a;
-        l_run[h] = l_run[h] * a + psum;
-        m_run[h] = m_new;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < HPT; ++i) {
-      const int h = hg * HPT + i;
-      if (h < GQ) o[i] *= alpha[h];
-    }
-    for (int tk = 0; tk < kChunk && t0 + tk < t_end; ++tk) {
-      const float vv = h2f(vr[(int64_t)((t0 + tk) % g.R) * D + c_v]);
-#pragma unroll
-      for (int i = 0; i < HPT; ++i) {
-        const int h = hg * HPT + i;
-        if (h < GQ) o[i] += sc[h * kChunk + tk] * vv;
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < HPT; ++i) {
-    const int h = hg * HPT + i;
-    if (h >= GQ) continue;
-    const int64_t bh = (int64_t)b * g.Hq + hkv * GQ + h;
-    float* part = L.ws + (bh * (L.n_split + 1) + part_idx) * (D + 2);
-    part[c_v] = o[i];
-    if (c_v == 0) {
-      part[D] = m_run[h];
-      part[D + 1] = l_run[h];
-    }
   }
 }
 
@@ -461,6 +355,144 @@ struct PackedWave {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  // Online softmax over a chunk's scores (exact running max; rescale only
+  // when it grows).  Each lane tests its own 8 scores; the cross-lane maximum
+  // is only formed on the (rare) path where some lane sees a larger score.
+  __device__ __forceinline__ void softmax(const float (&s)[2][4], float (&p)[2][4]) {
+    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    if (__any(cm > m_run)) {
+      cm = xor_max(cm, 16);
+      cm = xor_max(cm, 32);
+      const float m_new = fmaxf(m_run, cm);
+      const float a = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= a;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) oacc[n] *= a;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) bias[f] *= a;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p[u][q] = exp2f(s[u][q] - m_run);
+        l_run += p[u][q];
+      }
+  }
+
+  // Switch to the residual window: bring the packed accumulation to real scale
+  // (codes were fp16 numbers c * 2^-24) with its value-min term added, and set
+  // the key-side B fragments to q * 2^-E in natural channel order (element j of
+  // lane group g, k-chunk kc = channel 32 kc + 8 g + j), hi or lo part.
+  __device__ __forceinline__ void enter_residual() {
+    // the value-min term is summed over the four lane groups (token subsets)
+    float btot[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) btot[f] = xor_sum(xor_sum(bias[f], 16), 32);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float bsum = btot[C::gam(n) / SL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], 16777216.0f, bsum);
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) bias[f] = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg);
+      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg + 4);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t hi, lo;
+        split2(qv[2 * i], qv[2 * i + 1], hi, lo);
+        if constexpr (kColSplit) {
+          bq[0][kc][i] = (slot & 1) ? lo : hi;
+        } else {
+          bq[0][kc][i] = hi;
+          bq[1][kc][i] = lo;
+        }
+      }
+    }
+    cur_group = -1;
+  }
+
+  // Residual chunk: fp16 tokens t0 + [0, 32) of the window (those >= n_tok
+  // masked), keys straight from the window rows, values transposed through
+  // the wave's LDS buffer vbuf [32][D].
+  __device__ __forceinline__ void process_residual(int t0, int n_tok, int R,
+                                                   const uint16_t* kres,
+                                                   const uint16_t* vres, uint16_t* vbuf) {
+    // stage values: lane -> token lane/2, half of the channels
+    {
+      const int tk = lane >> 1, t = t0 + tk;
+      constexpr int V4 = D / 16;  // uint4 per half row
+      uint4* dst = reinterpret_cast<uint4*>(vbuf + tk * D + (lane & 1) * (D / 2));
+      if (t < n_tok) {
+        const uint4* src = reinterpret_cast<const uint4*>(vres + (int64_t)(t % R) * D +
+                                                          (lane & 1) * (D / 2));
+#pragma unroll
+        for (int v = 0; v < V4; ++v) dst[v] = src[v];
+      } else {
+#pragma unroll
+        for (int v = 0; v < V4; ++v) dst[v] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    // scores: tile u row r = token tok_v<4>(r/4, 4u + r%4)
+    const float kscale_r = bscale;  // keys are real fp16 values here
+    float s[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tin = t0 + tok_v<4>(col >> 2, 4 * u + (col & 3));
+      const int slot_in = (tin < n_tok ? tin : n_tok - 1) % R;
+      const uint4* krow = reinterpret_cast<const uint4*>(kres + (int64_t)slot_in * D);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint4 kv = krow[4 * kc + lg];
+        const uint32_t a[4] = {kv.x, kv.y, kv.z, kv.w};
+        acc = mfma(a, bq[0][kc], acc);
+        if constexpr (!kColSplit) acc = mfma(a, bq[1][kc], acc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = acc[q];
+        if constexpr (kColSplit) {
+          x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                   __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+        }
+        const bool valid = t0 + tok_v<4>(lg, 4 * u + q) < n_tok;
+        s[u][q] = valid ? x * kscale_r : kNegInf;
+      }
+    }
+    float p[2][4];
+    softmax(s, p);
+    uint32_t bh[4], bl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], bh[i], bl[i]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      uint32_t a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo16 = vbuf[tok_v<4>(lg, 2 * i) * D + 16 * n + col];
+        const uint32_t hi16 = vbuf[tok_v<4>(lg, 2 * i + 1) * D + 16 * n + col];
+        a[i] = lo16 | (hi16 << 16);
+      }
+      oacc[n] = mfma(a, bh, oacc[n]);
+      oacc[n] = mfma(a, bl, oacc[n]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
   __device__ __forceinline__ void process(int ch, const R& r) {
     const int grp = (ch * kChunk) / G;
     if (grp != cur_group) {
@@ -494,31 +526,8 @@ struct PackedWave {
         s[u][q] = __builtin_fmaf(x, kscale, beta_c);
       }
     }
-    // online softmax (exact running max; rescale only when it grows).  Each
-    // lane tests its own 8 scores; the cross-lane maximum is only formed on
-    // the (rare) path where some lane sees a larger score.
-    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    if (__any(cm > m_run)) {
-      cm = xor_max(cm, 16);
-      cm = xor_max(cm, 32);
-      const float m_new = fmaxf(m_run, cm);
-      const float a = exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= a;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) oacc[n] *= a;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) bias[f] *= a;
-    }
     float p[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        p[u][q] = exp2f(s[u][q] - m_run);
-        l_run += p[u][q];
-      }
+    softmax(s, p);
     // weighted value sum
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -550,38 +559,137 @@ struct PackedWave {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Persistent decomposition.  The work of one (sequence, KV head) unit is its
+// packed 32-token chunks (one work unit each) followed by the 32-token chunks
+// of its fp16 residual window (rw work units each: rw ~ fp16 bytes / packed
+// bytes per token, so that work units stand for equal HBM traffic).  The units
+// in order u = b * Hkv + hkv form one flat work list of `total` units.  Worker
+// wave w of the W launched takes [w * cpw, min((w + 1) * cpw, total)),
+// cpw = ceil(total / W): every wave moves the same number of bytes whatever
+// the mix of lengths.  A packed chunk belongs to the wave whose range holds
+// it; a residual chunk to the wave whose range holds its first work unit.  A
+// wave writes one partial per unit its range meets, at index w + u (distinct
+// over all (w, u) pairs that occur, at most W + units of them); a partial with
+// no tokens has max -inf and sum 0.
+// ---------------------------------------------------------------------------
+constexpr int kPartPad = 4;  // partial row = D values, max, sum, 2 pad floats
+
+struct SeqWork {
+  int n;   // tokens (0 for an invalid length)
+  int nq;  // packed chunks per KV head
+  int nr;  // residual chunks per KV head
+  int w;   // work units per KV head
+};
+
+__device__ __forceinline__ SeqWork seq_work(const DecodeLaunch& L, int b) {
+  SeqWork sw{0, 0, 0, 0};
+  const int n = L.seq_lens[b];
+  if (n <= 0 || n > L.g.C || n > L.max_seq_len) return sw;
+  const int lq = packed_len(n, L.g.R);
+  sw.n = n;
+  sw.nq = lq / kChunk;
+  sw.nr = (n - lq + kChunk - 1) / kChunk;
+  sw.w = sw.nq + sw.nr * L.rw;
+  return sw;
+}
+
+// Total work units over all units, by one wave.
+__device__ __forceinline__ int wave_total_work(const DecodeLaunch& L, int lane) {
+  int s = 0;
+  for (int b = lane; b < L.g.B; b += 64) s += seq_work(L, b).w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return s * L.g.Hkv;
+}
+
+// Sequence b holding flat work unit x, and base = Hkv * (work of sequences < b).
+__device__ __forceinline__ void wave_find_seq(const DecodeLaunch& L, int lane, int x,
+                                              int& b_out, int& base_out) {
+  int base = 0;
+  for (int b0 = 0; b0 < L.g.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int c = (b < L.g.B) ? seq_work(L, b).w * L.g.Hkv : 0;
+    int inc = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += y;
+    }
+    const uint64_t m = __ballot(base + inc > x);
+    if (m) {
+      const int l = __ffsll((unsigned long long)m) - 1;
+      b_out = b0 + l;
+      base_out = base + __shfl(inc - c, l, 64);
+      return;
+    }
+    base += __shfl(inc, 63, 64);
+  }
+  b_out = L.g.B;
+  base_out = base;
+}
+
 template <int D, int BK, int BV, int GQ, int NG>
-__device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split, int t0,
-                               int t1, char* smem) {
+constexpr int kWaveSmem = GQ * D * 4 + (Cfg<D, BK, BV, GQ, NG>::kWaveLds > kChunk * D * 2
+                                            ? Cfg<D, BK, BV, GQ, NG>::kWaveLds
+                                            : kChunk * D * 2);
+
+// The part of unit (b, hkv) in work range [x0, x1) -> partial p.  xu = first
+// work unit of the unit.
+template <int D, int BK, int BV, int GQ, int NG>
+__device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
+                             int xu, int x0, int x1, int p, char* smem, int lane) {
   using C = Cfg<D, BK, BV, GQ, NG>;
   using W = PackedWave<D, BK, BV, GQ, NG>;
   using R = Raw<D, BK, BV, GQ, NG>;
   constexpr int NT = C::NT, SL = C::SL, NF = C::NF;
+  constexpr int QPH = D / 64;  // query values per lane and head
+  constexpr int DP = D + kPartPad;
   const Geom& g = L.g;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t unit = (int64_t)b * g.Hkv + hkv;
+  float* part_base = L.ws + (int64_t)p * GQ * DP;
 
-  float* qfs = reinterpret_cast<float*>(smem);            // [GQ][D] q * 2^-E
-  int* qexp = reinterpret_cast<int*>(qfs + GQ * D);       // [GQ]
-  char* wbase = smem + (GQ * D + 16) * 4 + wave * C::kWaveLds;
+  // packed chunks [pc0, pc1) and residual chunks [rk0, rk1) of this range
+  const int pc0 = max(x0, xu) - xu, pc1 = min(x1, xu + sw.nq) - xu;
+  const int d0 = x0 - xu - sw.nq, d1 = x1 - xu - sw.nq;
+  const int rk0 = d0 <= 0 ? 0 : (d0 + L.rw - 1) / L.rw;
+  const int rk1 = min(sw.nr, d1 <= 0 ? 0 : (d1 + L.rw - 1) / L.rw);
+  if (pc0 >= pc1 && rk0 >= rk1) {  // only part of a residual chunk's weight
+    // an empty partial: zero sums, max -inf (weight 0 in the merge)
+    for (int i = lane; i < GQ * DP; i += 64) {
+      const int c = i % DP;
+      part_base[i] = (c == D) ? kNegInf : 0.0f;
+    }
+    return;
+  }
 
-  for (int i = tid; i < GQ * D; i += kThreads)
-    qfs[i] = h2f(L.q[((int64_t)b * g.Hq + hkv * GQ) * D + i]) * L.scale_log2;
-  __syncthreads();
-  // per-head exponent E with max|qf| < 2^E, so that q * 2^-E * scale fits fp16
-  for (int h = wave; h < GQ; h += kWaves) {
+  float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
+  char* wl = smem + GQ * D * 4;
+
+  // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
+  // that q * 2^-E * scale fits fp16
+  const uint16_t* qg = L.q + ((int64_t)b * g.Hq + hkv * GQ) * D;
+  int eh[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float qv[QPH];
     float mx = 0.0f;
-    for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(qfs[h * D + c]));
+#pragma unroll
+    for (int k = 0; k < QPH; ++k) {
+      qv[k] = h2f(qg[h * D + lane + 64 * k]) * L.scale_log2;
+      mx = fmaxf(mx, fabsf(qv[k]));
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = xor_max(mx, off);
     int e = 0;
     if (mx > 0.0f) (void)frexpf(mx, &e);
-    if (lane == 0) qexp[h] = e;
+    eh[h] = e;
+#pragma unroll
+    for (int k = 0; k < QPH; ++k) qfs[h * D + lane + 64 * k] = ldexpf(qv[k], -e);
   }
-  __syncthreads();
-  for (int i = tid; i < GQ * D; i += kThreads) qfs[i] = ldexpf(qfs[i], -qexp[i / D]);
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   W w;
   w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
@@ -590,36 +698,46 @@ __device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split,
   w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
             unit * (g.C / kVBlock) * NG * kVBlock;
   w.qfs = qfs;
-  w.qB = reinterpret_cast<uint4*>(wbase);
-  w.beta_l = reinterpret_cast<float*>(wbase + C::kQB);
-  const int nchunks = (t1 - t0) / kChunk;
-  const int c_lo = t0 / kChunk + (nchunks * wave) / kWaves;
-  const int c_hi = t0 / kChunk + (nchunks * (wave + 1)) / kWaves;
-  w.c_lo = c_lo;
-  w.c_hi = c_hi;
+  w.qB = reinterpret_cast<uint4*>(wl);
+  w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
+  w.c_lo = pc0;
+  w.c_hi = pc1;
   w.init(lane);
-  const int e_h = qexp[w.hcol];
-  w.kscale = ldexpf(1.0f, e_h + 24);  // codes are the fp16 numbers c * 2^-24
-  w.bscale = ldexpf(1.0f, e_h);
+  int e_mine = 0;
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+    if (w.hcol == h) e_mine = eh[h];
+  w.kscale = ldexpf(1.0f, e_mine + 24);  // codes are the fp16 numbers c * 2^-24
+  w.bscale = ldexpf(1.0f, e_mine);
 
-  // two chunk buffers: the next chunk's loads are in flight while one is
-  // used.  Prefetches past the wave's last chunk re-load that chunk (always in
-  // bounds) instead of being skipped, so no load sits under a branch.
-  R ra, rb;
-  if (c_lo < c_hi) {
-    const int last = c_hi - 1;
-    w.load_kmeta((c_lo * kChunk) / C::G);
-    w.load(c_lo, ra);
-    for (int ch = c_lo; ch < c_hi; ch += 2) {
+  if (pc0 < pc1) {
+    // two chunk buffers: the next chunk's loads are in flight while one is
+    // used.  Prefetches past the last chunk re-load that chunk (always in
+    // bounds) instead of being skipped, so no load sits under a branch.
+    R ra, rb;
+    const int last = pc1 - 1;
+    w.load_kmeta((pc0 * kChunk) / C::G);
+    w.load(pc0, ra);
+    for (int ch = pc0; ch < pc1; ch += 2) {
       w.load(min(ch + 1, last), rb);
       w.process(ch, ra);
-      if (ch + 1 >= c_hi) break;
+      if (ch + 1 >= pc1) break;
       w.load(min(ch + 2, last), ra);
       w.process(ch + 1, rb);
     }
   }
+  const bool resid = rk0 < rk1;
+  if (resid) {
+    w.enter_residual();
+    const uint16_t* kres = L.cache.k_res + unit * g.R * D;
+    const uint16_t* vres = L.cache.v_res + unit * g.R * D;
+    uint16_t* vbuf = reinterpret_cast<uint16_t*>(wl);
+    const int lq = sw.nq * kChunk;
+    for (int k = rk0; k < rk1; ++k)
+      w.process_residual(lq + k * kChunk, sw.n, g.R, kres, vres, vbuf);
+  }
 
-  // ---------------- merge lane groups, then waves ----------------
+  // partial: O (+ value-min term), max, sum of this wave's tokens
   float l_run = w.l_run;
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);
@@ -629,158 +747,303 @@ __device__ void packed_partial(const DecodeLaunch& L, int b, int hkv, int split,
     bias[f] = xor_sum(w.bias[f], 16);
     bias[f] = xor_sum(bias[f], 32);
   }
-  __syncthreads();  // fold buffers are reused for the merge below
-  float* cmb = reinterpret_cast<float*>(smem);  // [kWaves][GQ][D + 2]
-  float* mine = cmb + wave * GQ * (D + 2);
+  float* part = part_base + w.hcol * DP;
+  const float oscale = resid ? 1.0f : 16777216.0f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int gm = C::gam(n);
     if (gm % SL != w.slot) continue;
     const float bsum = bias[gm / SL];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      mine[w.hcol * (D + 2) + 16 * n + 4 * w.lg + q] = w.oacc[n][q] * 16777216.0f + bsum;
+    const float4 v = make_float4(__builtin_fmaf(w.oacc[n][0], oscale, bsum),
+                                 __builtin_fmaf(w.oacc[n][1], oscale, bsum),
+                                 __builtin_fmaf(w.oacc[n][2], oscale, bsum),
+                                 __builtin_fmaf(w.oacc[n][3], oscale, bsum));
+    *reinterpret_cast<float4*>(part + 16 * n + 4 * w.lg) = v;
   }
   if (w.lg == 0 && w.slot == 0) {
-    mine[w.hcol * (D + 2) + D] = w.m_run;
-    mine[w.hcol * (D + 2) + D + 1] = l_run;
+    part[D] = w.m_run;
+    part[D + 1] = l_run;
   }
-  __syncthreads();
-  for (int i = tid; i < GQ * D; i += kThreads) {
-    const int h = i / D, c = i % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, cmb[(v * GQ + h) * (D + 2) + D]);
-    float Ls = 0.0f, acc = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float* sv = cmb + (v * GQ + h) * (D + 2);
-      const float wt = (sv[D] == kNegInf) ? 0.0f : exp2f(sv[D] - M);
-      Ls += sv[D + 1] * wt;
-      acc += sv[c] * wt;
-    }
-    const int64_t bh = (int64_t)b * g.Hq + hkv * GQ + h;
-    float* part = L.ws + (bh * (L.n_split + 1) + split) * (D + 2);
-    part[c] = acc;
-    if (c == 0) {
-      part[D] = M;
-      part[D + 1] = Ls;
-    }
-  }
+  // the next segment of this wave rewrites the LDS buffers
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One wave per workgroup; grid = the number of worker waves.
 template <int D, int BK, int BV, int GQ, int NG>
-constexpr int kSmemBytes() {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  constexpr int packed = (GQ * D + 16) * 4 + kWaves * C::kWaveLds;
-  constexpr int merge = kWaves * GQ * (D + 2) * 4;
-  constexpr int resid = (GQ * D + GQ * kChunk + 3 * GQ) * 4;
-  constexpr int m1 = packed > merge ? packed : merge;
-  return m1 > resid ? m1 : resid;
-}
-
-// grid: (n_split + 1, Hkv, B).  x < n_split: packed tokens of split x;
-// x == n_split: the residual window.
-template <int D, int BK, int BV, int GQ, int NG>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeLaunch L) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D, BK, BV, GQ, NG>()];
-  const Geom& g = L.g;
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int n = L.seq_lens[b];
-  if (n <= 0 || n > g.C || n > L.max_seq_len) return;  // the combine writes 0 / NaN
-  const int lq = packed_len(n, g.R);
-  if (split == L.n_split) {
-    residual_partial<D, GQ>(L, b, hkv, lq, n, L.n_split, reinterpret_cast<float*>(smem));
-    return;
+__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
+  __shared__ __attribute__((aligned(16))) char smem[kWaveSmem<D, BK, BV, GQ, NG>];
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x, nw = gridDim.x;
+  const int total = __builtin_amdgcn_readfirstlane(wave_total_work(L, lane));
+  const int cpw = (total + nw - 1) / nw;
+  const int x0 = w * cpw;
+  const int x1 = min(total, x0 + cpw);
+  int x = x0;
+  while (x < x1) {
+    int b, base;
+    wave_find_seq(L, lane, x, b, base);
+    b = __builtin_amdgcn_readfirstlane(b);
+    base = __builtin_amdgcn_readfirstlane(base);
+    const SeqWork sw = seq_work(L, b);
+    const int hkv = (x - base) / sw.w;
+    const int xu = base + hkv * sw.w;
+    unit_segment<D, BK, BV, GQ, NG>(L, b, hkv, sw, xu, x0, x1, w + b * L.g.Hkv + hkv, smem,
+                                    lane);
+    x = xu + sw.w;
   }
-  const int t0 = split * L.split_tokens;
-  const int t1 = min(lq, t0 + L.split_tokens);
-  if (t0 >= t1) return;  // no packed tokens here: the combine skips this split
-  packed_partial<D, BK, BV, GQ, NG>(L, b, hkv, split, t0, t1, smem);
 }
 
-// Merges the partials of one (sequence, query head).
-template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeLaunch L) {
+// One workgroup per (KV head, sequence): merges the partials of the unit and
+// writes its GQ outputs:
+//   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
+// The unit's partials are contiguous (indices w + u for consecutive waves w),
+// so they stream with independent vector loads.
+template <int D, int GQ>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeLaunch L) {
+  constexpr int DP = D + kPartPad;
+  constexpr int SB = 128;  // partials weighted per pass
+  constexpr int NO = GQ * D / 4;  // float4 outputs of the unit
+  static_assert(kThreads % GQ == 0, "head of a thread must stay fixed");
+  __shared__ int red[2 * kThreads / 64];
+  __shared__ float hred[kThreads];
+  __shared__ float mh[GQ], lh[GQ];
+  __shared__ float wts[SB * GQ];
   const Geom& g = L.g;
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int64_t bh = (int64_t)b * g.Hq + h;
+  const int hkv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int64_t out0 = ((int64_t)b * g.Hq + hkv * GQ) * D;
   const int n = L.seq_lens[b];
   if (n < 0 || n > g.C || n > L.max_seq_len) {
-    L.out[bh * D + c] = 0x7e00;  // NaN: length outside [0, max_seq_len]
+    for (int i = tid; i < GQ * D; i += kThreads) L.out[out0 + i] = 0x7e00;  // NaN
     return;
   }
   if (n == 0) {
-    L.out[bh * D + c] = 0;
+    for (int i = tid; i < GQ * D; i += kThreads) L.out[out0 + i] = 0;
     return;
   }
-  const int lq = packed_len(n, g.R);
-  const int nsp = (lq + L.split_tokens - 1) / L.split_tokens;  // packed splits used
-  const float* part = L.ws + bh * (L.n_split + 1) * (D + 2);
-  const float* res = part + L.n_split * (D + 2);
-  float M = res[D];
-  for (int i = 0; i < nsp; ++i) M = fmaxf(M, part[i * (D + 2) + D]);
-  float w = exp2f(res[D] - M);
-  float Ls = res[D + 1] * w, acc = res[c] * w;
-  for (int i = 0; i < nsp; ++i) {
-    w = exp2f(part[i * (D + 2) + D] - M);
-    Ls += part[i * (D + 2) + D + 1] * w;
-    acc += part[i * (D + 2) + c] * w;
+  // flat position of this unit's work
+  int tot = 0, pre = 0;
+  for (int bb = tid; bb < g.B; bb += kThreads) {
+    const int c = seq_work(L, bb).w;
+    tot += c;
+    if (bb < b) pre += c;
   }
-  L.out[bh * D + c] = f2h(acc / Ls);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    tot += __shfl_xor(tot, off, 64);
+    pre += __shfl_xor(pre, off, 64);
+  }
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = tot;
+    red[kThreads / 64 + (tid >> 6)] = pre;
+  }
+  __syncthreads();
+  tot = 0;
+  pre = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    tot += red[i];
+    pre += red[kThreads / 64 + i];
+  }
+  const int total = tot * g.Hkv;
+  const SeqWork sw = seq_work(L, b);
+  const int xu = pre * g.Hkv + hkv * sw.w;
+  const int cpw = (total + L.n_workers - 1) / L.n_workers;
+  const int w_first = xu / cpw, w_last = (xu + sw.w - 1) / cpw;
+  const int S = w_last - w_first + 1;
+  const float* base = L.ws + (int64_t)(w_first + b * g.Hkv + hkv) * GQ * DP;
+  const int h_t = tid % GQ;  // the head this thread's (s, h) items have
+
+  // pass 1: per-head maximum
+  float m = kNegInf;
+  for (int i = tid; i < S * GQ; i += kThreads) m = fmaxf(m, base[(int64_t)i * DP + D]);
+  hred[tid] = m;
+  __syncthreads();
+  if (tid < GQ) {
+    float mm = kNegInf;
+    for (int j = tid; j < kThreads; j += GQ) mm = fmaxf(mm, hred[j]);
+    mh[tid] = mm;
+  }
+  __syncthreads();
+  // pass 2: weights per block of partials, weighted sums (each thread owns
+  // OPT float4 outputs: item t = tid + j * kThreads -> head t / (D/4))
+  constexpr int OPT = (NO + kThreads - 1) / kThreads;
+  float lsum = 0.0f;
+  float4 acc[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    const int sn = min(SB, S - s0);
+    for (int i = tid; i < SB * GQ; i += kThreads) {
+      float wt = 0.0f;
+      if (i < sn * GQ) {
+        const float* pr = base + ((int64_t)(s0 * GQ + i)) * DP;
+        const float mw = pr[D];
+        if (mw != kNegInf) {
+          wt = exp2f(mw - mh[h_t]);
+          lsum += pr[D + 1] * wt;
+        }
+      }
+      wts[i] = wt;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int t = tid + j * kThreads;
+      if (t < NO) {
+        const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
+        const float* pr = base + (int64_t)s0 * GQ * DP + oh * DP + oc;
+        float4 a = acc[j];
+        int s = 0;
+        for (; s + 4 <= sn; s += 4) {
+          float4 v[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            v[k] = *reinterpret_cast<const float4*>(pr + (int64_t)(s + k) * GQ * DP);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float wt = wts[(s + k) * GQ + oh];
+            a.x += v[k].x * wt;
+            a.y += v[k].y * wt;
+            a.z += v[k].z * wt;
+            a.w += v[k].w * wt;
+          }
+        }
+        for (; s < sn; ++s) {
+          const float4 v = *reinterpret_cast<const float4*>(pr + (int64_t)s * GQ * DP);
+          const float wt = wts[s * GQ + oh];
+          a.x += v.x * wt;
+          a.y += v.y * wt;
+          a.z += v.z * wt;
+          a.w += v.w * wt;
+        }
+        acc[j] = a;
+      }
+    }
+    __syncthreads();
+  }
+  hred[tid] = lsum;
+  __syncthreads();
+  if (tid < GQ) {
+    float ls = 0.0f;
+    for (int j = tid; j < kThreads; j += GQ) ls += hred[j];
+    lh[tid] = ls;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int t = tid + j * kThreads;
+    if (t < NO) {
+      const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
+      const float inv = 1.0f / lh[oh];
+      const int64_t o = out0 + oh * D + oc;
+      L.out[o + 0] = f2h(acc[j].x * inv);
+      L.out[o + 1] = f2h(acc[j].y * inv);
+      L.out[o + 2] = f2h(acc[j].z * inv);
+      L.out[o + 3] = f2h(acc[j].w * inv);
+    }
+  }
 }
 
-template <int D, int BK, int BV, int GQ>
-hipError_t dispatch_ng(const DecodeLaunch& L, dim3 grid, hipStream_t st) {
-  switch (D / L.g.G) {
-    case 1: decode_partial_kernel<D, BK, BV, GQ, 1><<<grid, kThreads, 0, st>>>(L); break;
-    case 2: decode_partial_kernel<D, BK, BV, GQ, 2><<<grid, kThreads, 0, st>>>(L); break;
-    case 4:
-      if constexpr (D == 128) {
-        decode_partial_kernel<D, BK, BV, GQ, 4><<<grid, kThreads, 0, st>>>(L);
-        break;
-      }
-      [[fallthrough]];
-    default: return hipErrorInvalidValue;
+// Worker waves the partial kernel of this instantiation is launched with:
+// resident waves per compute unit (from the kernel's resources) x CUs, cached
+// per device.
+template <int D, int BK, int BV, int GQ, int NG>
+hipError_t workers_of(int cus, int* out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return hipSuccess;
   }
+  int nb = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &nb, decode_partial_kernel<D, BK, BV, GQ, NG>, 64, 0);
+  if (e != hipSuccess) return e;
+  if (nb < 1) nb = 1;
+  const int w = nb * cus;
+  if (dev >= 0 && dev < 64) cache[dev] = w;
+  *out = w;
+  return hipSuccess;
+}
+
+// Op: 0 = launch the partial kernel, 1 = query its worker count.
+template <int D, int BK, int BV, int GQ, int NG>
+hipError_t run(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
+  if (op == 1) return workers_of<D, BK, BV, GQ, NG>(cus, workers);
+  decode_partial_kernel<D, BK, BV, GQ, NG><<<dim3(L.n_workers), 64, 0, st>>>(L);
   return hipGetLastError();
 }
 
+template <int D, int BK, int BV, int GQ>
+hipError_t dispatch_ng(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
+  switch (D / L.g.G) {
+    case 1: return run<D, BK, BV, GQ, 1>(L, op, cus, workers, st);
+    case 2: return run<D, BK, BV, GQ, 2>(L, op, cus, workers, st);
+    case 4:
+      if constexpr (D == 128) return run<D, BK, BV, GQ, 4>(L, op, cus, workers, st);
+      [[fallthrough]];
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D, int BK, int BV>
-hipError_t dispatch_gq(const DecodeLaunch& L, hipStream_t st) {
-  dim3 grid(L.n_split + 1, L.g.Hkv, L.g.B);
+hipError_t dispatch_gq(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
   switch (L.g.Hq / L.g.Hkv) {
-    case 1: return dispatch_ng<D, BK, BV, 1>(L, grid, st);
-    case 2: return dispatch_ng<D, BK, BV, 2>(L, grid, st);
-    case 4: return dispatch_ng<D, BK, BV, 4>(L, grid, st);
-    case 8: return dispatch_ng<D, BK, BV, 8>(L, grid, st);
-    case 16: return dispatch_ng<D, BK, BV, 16>(L, grid, st);
+    case 1: return dispatch_ng<D, BK, BV, 1>(L, op, cus, workers, st);
+    case 2: return dispatch_ng<D, BK, BV, 2>(L, op, cus, workers, st);
+    case 4: return dispatch_ng<D, BK, BV, 4>(L, op, cus, workers, st);
+    case 8: return dispatch_ng<D, BK, BV, 8>(L, op, cus, workers, st);
+    case 16: return dispatch_ng<D, BK, BV, 16>(L, op, cus, workers, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-hipError_t dispatch_bits(const DecodeLaunch& L, hipStream_t st) {
+hipError_t dispatch_bits(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
   const int bk = L.g.bK, bv = L.g.bV;
-  if (bk == 2 && bv == 2) return dispatch_gq<D, 2, 2>(L, st);
-  if (bk == 2 && bv == 4) return dispatch_gq<D, 2, 4>(L, st);
-  if (bk == 4 && bv == 2) return dispatch_gq<D, 4, 2>(L, st);
-  return dispatch_gq<D, 4, 4>(L, st);
+  if (bk == 2 && bv == 2) return dispatch_gq<D, 2, 2>(L, op, cus, workers, st);
+  if (bk == 2 && bv == 4) return dispatch_gq<D, 2, 4>(L, op, cus, workers, st);
+  if (bk == 4 && bv == 2) return dispatch_gq<D, 4, 2>(L, op, cus, workers, st);
+  return dispatch_gq<D, 4, 4>(L, op, cus, workers, st);
+}
+
+hipError_t dispatch(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
+  return L.g.D == 64 ? dispatch_bits<64>(L, op, cus, workers, st)
+                     : dispatch_bits<128>(L, op, cus, workers, st);
+}
+
+template <int D>
+hipError_t combine_gq(const DecodeLaunch& L, hipStream_t st) {
+  dim3 grid(L.g.Hkv, L.g.B);
+  switch (L.g.Hq / L.g.Hkv) {
+    case 1: decode_combine_kernel<D, 1><<<grid, kThreads, 0, st>>>(L); break;
+    case 2: decode_combine_kernel<D, 2><<<grid, kThreads, 0, st>>>(L); break;
+    case 4: decode_combine_kernel<D, 4><<<grid, kThreads, 0, st>>>(L); break;
+    case 8: decode_combine_kernel<D, 8><<<grid, kThreads, 0, st>>>(L); break;
+    case 16: decode_combine_kernel<D, 16><<<grid, kThreads, 0, st>>>(L); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t decode_workers(const Geom& g, int cus, int* workers) {
+  DecodeLaunch L{};
+  L.g = g;
+  return dispatch(L, 1, cus, workers, nullptr);
+}
+
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st) {
-  return L.g.D == 64 ? dispatch_bits<64>(L, st) : dispatch_bits<128>(L, st);
+  return dispatch(L, 0, 0, nullptr, st);
 }
 
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st) {
-  dim3 grid(L.g.Hq, L.g.B);
-  if (L.g.D == 64)
-    decode_combine_kernel<64><<<grid, 64, 0, st>>>(L);
-  else
-    decode_combine_kernel<128><<<grid, 128, 0, st>>>(L);
-  return hipGetLastError();
+  return L.g.D == 64 ? combine_gq<64>(L, st) : combine_gq<128>(L, st);
 }
 
 }  // namespace kvq

@@ -60,12 +60,14 @@ struct DecodeLaunch {
   kvq_cache cache;
   const int32_t* seq_lens;
   int32_t max_seq_len;
-  int32_t n_split;
-  int32_t split_tokens;
-  float scale_log2;  // sm_scale * log2(e)
-  float* ws;         // partials [B][Hq][n_split][D + 2] (n_split > 1)
-  uint16_t* out;     // [B][Hq][D]
+  int32_t n_workers;  // worker waves of the partial kernel
+  int32_t rw;         // work units of a residual chunk (its bytes / a packed chunk's)
+  float scale_log2;   // sm_scale * log2(e)
+  float* ws;          // partials [n_workers + B*Hkv][Hq/Hkv][D + 4]
+  uint16_t* out;      // [B][Hq][D]
 };
+// Worker waves for this geometry's partial kernel on the current device.
+hipError_t decode_workers(const Geom& g, int cus, int* workers);
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st);
 

@@ -127,21 +127,24 @@ def test_decode_parity(case):
     _say(f"  max err {err:.2e}")
 
 
-def test_decode_split_boundaries():
-    """Lengths around split edges (ragged last split, one-token split)."""
-    B, Hq, Hkv, D = 4, 8, 2, 128
-    g0 = kvq.Geom(B, Hq, Hkv, D, 2, 4, 32, 128, 4096)
-    ns, st = kvq.kvq_decode_splits(g0, 4000)
-    _say(f"splits for 4000: {ns} x {st}")
-    lens = [st, st + 1, 2 * st - 1, 4000]
-    g, og = geoms(B, Hq, Hkv, D, 2, 4, 32, 128, 4096)
+def test_decode_worker_boundaries():
+    """Many short sequences (one wave's share spans several units) mixed with
+    long ones (one unit spans many waves), lengths around chunk, group and
+    window edges."""
+    B, Hq, Hkv, D = 24, 8, 2, 128
+    g0 = kvq.Geom(B, Hq, Hkv, D, 2, 4, 32, 128, 8192)
+    nw = kvq.kvq_decode_workers(g0)
+    _say(f"worker waves: {nw}")
+    lens = [1, 31, 32, 33, 127, 128, 129, 160, 161, 255, 256, 257, 383, 384, 385,
+            1000, 4095, 4096, 4097, 5000, 8000, 8191, 129, 300]
+    g, og = geoms(B, Hq, Hkv, D, 2, 4, 32, 128, 8192)
     rng = np.random.default_rng(1)
-    k = rng.standard_normal((B, Hkv, 4000, D)).astype(np.float16)
-    v = rng.standard_normal((B, Hkv, 4000, D)).astype(np.float16)
+    k = rng.standard_normal((B, Hkv, 8191, D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, 8191, D)).astype(np.float16)
     q = (rng.standard_normal((B, Hq, D)) * 3).astype(np.float16)
     cache, oc = prefill_both(g, og, k, v, lens)
-    out, ref = decode_both(g, og, cache, oc, q, lens, max_seq_len=4000)
-    assert_close(out, ref, what="split boundaries")
+    out, ref = decode_both(g, og, cache, oc, q, lens, max_seq_len=8191)
+    assert_close(out, ref, what="worker boundaries")
 
 
 def test_decode_degenerate_lengths():
@@ -232,10 +235,10 @@ def test_append_out_of_range_is_noop():
 # ------------------------------------------------------------ error paths ---
 def test_workspace_errors():
     g = kvq.Geom(4, 32, 8, 128, 2, 4, 32, 128, 65536)
-    ns, st = kvq.kvq_decode_splits(g, 65536)
-    assert ns > 1
+    nw = kvq.kvq_decode_workers(g)
+    assert nw >= 256
     need = kvq.kvq_decode_workspace_bytes(g, 65536)
-    assert need == 4 * 32 * (ns + 1) * 130 * 4  # packed splits + residual partial
+    assert need == (nw + 4 * 8) * 4 * 132 * 4  # (workers + units) x GQ x (D + 4) floats
     cache = kvq.Cache(kvq.Geom(4, 32, 8, 128, 2, 4, 32, 128, 65536))
     q = torch.zeros((4, 32, 128), dtype=torch.float16, device="cuda")
     out = torch.empty_like(q)
