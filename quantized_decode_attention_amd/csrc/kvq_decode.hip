@@ -68,14 +68,26 @@ __device__ __forceinline__ float lo_half(uint32_t v) {
 __device__ __forceinline__ float hi_half(uint32_t v) {
   return (float)__builtin_bit_cast(h2, v)[1];
 }
+// -1.0f that the compiler cannot see as a constant (kept in a register), so
+// that hi * m1 + a stays one mixed-precision fma instead of a conversion and
+// a subtraction.
+__device__ __forceinline__ float opaque_m1() {
+  float x = -1.0f;
+  asm volatile("" : "+v"(x));
+  return x;
+}
 // hi/lo fp16 split of (a, b): a ~= hi.x + lo.x to ~2^-21 relative.  The
-// remainders a - hi.x are exact fp32 subtractions, written as fmas of the fp16
-// half so that the compiler fuses the conversion (v_fma_mix_f32).
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+// remainders a - hi.x are exact fp32 operations, each one v_fma_mix_f32 of
+// the fp16 half (m1 = -1).
+__device__ __forceinline__ void split2(float a, float b, float m1, uint32_t& hi,
+                                       uint32_t& lo) {
   hi = pk_rtz(a, b);
   const h2 hh = __builtin_bit_cast(h2, hi);
-  lo = pk_rtz(__builtin_fmaf((float)hh[0], -1.0f, a), __builtin_fmaf((float)hh[1], -1.0f, b));
+  lo = pk_rtz(__builtin_fmaf((float)hh[0], m1, a), __builtin_fmaf((float)hh[1], m1, b));
 }
+// 2^x on the hardware unit (no range fix-up: results below the fp32 normal
+// range only arise for weights that are negligible next to the running max).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // x * fp16 field of a packed (scale, min) word (+ acc), converted inside the
 // fma (v_fma_mix_f32).  The +0 addend keeps the fma from being folded into a
@@ -208,6 +220,7 @@ struct Raw {
   uint32_t kw[2][C::KW];              // key code words of score tiles 0, 1
   uint32_t vw[C::NT];                 // value code word per channel tile
   uint32_t vmA[C::NF][4], vmB[C::NF][4];  // value (scale, min) of the B elements
+  uint4 kmA[C::IPL], kmB[C::IPL];     // key (scale, min) of the chunk's group
 };
 
 template <int D, int BK, int BV, int GQ, int NG>
@@ -230,7 +243,6 @@ struct PackedWave {
   const float* qfs;
   uint4* qB;
   float* beta_l;
-  int c_lo, c_hi;
   // lane constants
   int lane, col, lg, hcol, slot;
   int koff[2];
@@ -239,17 +251,18 @@ struct PackedWave {
   int kmoff[IPL][2];
   int fitem[IPL];
   float kscale, bscale;
+  float m1;  // -1 in a register (split2)
   // state
   f4 oacc[NT];
   float m_run, l_run;
   float bias[NF];
   uint32_t bq[KP][KC][4];
-  uint4 kmA[IPL], kmB[IPL];  // key (scale, min) for the next fold
   float beta_c;
   int cur_group;
 
   __device__ void init(int lane_) {
     lane = lane_;
+    m1 = opaque_m1();
     col = lane & 15;
     lg = lane >> 4;
     hcol = col / SL;
@@ -297,23 +310,21 @@ struct PackedWave {
       r.vmA[f][0] = a.x; r.vmA[f][1] = a.y; r.vmA[f][2] = a.z; r.vmA[f][3] = a.w;
       r.vmB[f][0] = c.x; r.vmB[f][1] = c.y; r.vmB[f][2] = c.z; r.vmB[f][3] = c.w;
     }
-  }
-
-  // Key meta of group grp for the next fold.
-  __device__ __forceinline__ void load_kmeta(int grp) {
-    const uint32_t* km = kmeta + (int64_t)grp * D;
+    // key meta of the chunk's group, with the chunk's other loads (one
+    // in-order stream, so waiting for a chunk never waits for a later one).
+    // Lanes past the fold items load an in-range row too (kmoff depends on
+    // the item modulo a head's items): no load sits under a branch.
+    const uint32_t* km = kmeta + (int64_t)((ch * kChunk) / G) * D;
 #pragma unroll
     for (int i = 0; i < IPL; ++i) {
-      if (fitem[i] < C::ITEMS) {
-        kmA[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][0]);
-        kmB[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][1]);
-      }
+      r.kmA[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][0]);
+      r.kmB[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][1]);
     }
   }
 
   // q' = q * 2^-E * key scale (hi/lo fp16 fragments in LDS) and beta' =
   // q * 2^-E . key min, for the key group starting in this chunk.
-  __device__ __forceinline__ void fold() {
+  __device__ __forceinline__ void fold(const R& r) {
 #pragma unroll
     for (int i = 0; i < IPL; ++i) {
       const int it = fitem[i];
@@ -323,12 +334,12 @@ struct PackedWave {
         const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][0]);
         const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][1]);
         const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qBv[4] = {qb.x, qb.y, qb.z, qb.w};
-        const uint32_t mA[4] = {kmA[i].x, kmA[i].y, kmA[i].z, kmA[i].w};
-        const uint32_t mB[4] = {kmB[i].x, kmB[i].y, kmB[i].z, kmB[i].w};
+        const uint32_t mA[4] = {r.kmA[i].x, r.kmA[i].y, r.kmA[i].z, r.kmA[i].w};
+        const uint32_t mB[4] = {r.kmB[i].x, r.kmB[i].y, r.kmB[i].z, r.kmB[i].w};
         uint32_t hp[4], lp[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), hp[e], lp[e]);
+          split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), m1, hp[e], lp[e]);
           bpart = mul_hi(qA[e], mA[e], bpart);
           bpart = mul_hi(qBv[e], mB[e], bpart);
         }
@@ -365,7 +376,7 @@ struct PackedWave {
       cm = xor_max(cm, 16);
       cm = xor_max(cm, 32);
       const float m_new = fmaxf(m_run, cm);
-      const float a = exp2f(m_run - m_new);
+      const float a = exp2_hw(m_run - m_new);
       m_run = m_new;
       l_run *= a;
 #pragma unroll
@@ -377,7 +388,7 @@ struct PackedWave {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        p[u][q] = exp2f(s[u][q] - m_run);
+        p[u][q] = exp2_hw(s[u][q] - m_run);
         l_run += p[u][q];
       }
   }
@@ -407,7 +418,7 @@ struct PackedWave {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t hi, lo;
-        split2(qv[2 * i], qv[2 * i + 1], hi, lo);
+        split2(qv[2 * i], qv[2 * i + 1], m1, hi, lo);
         if constexpr (kColSplit) {
           bq[0][kc][i] = (slot & 1) ? lo : hi;
         } else {
@@ -472,7 +483,7 @@ struct PackedWave {
     uint32_t bh[4], bl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], bh[i], bl[i]);
+      split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], m1, bh[i], bl[i]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -497,12 +508,8 @@ struct PackedWave {
     const int grp = (ch * kChunk) / G;
     if (grp != cur_group) {
       cur_group = grp;
-      fold();
+      fold(r);
     }
-    // key meta of the next chunk's group loads while this chunk runs; it is
-    // issued unconditionally (the group index is clamped by the caller's
-    // chunk range) so the memory counters stay exact on every path.
-    load_kmeta(((ch + 1 < c_hi ? ch + 1 : ch) * kChunk) / G);
     // scores: s = 2^(E+24) * (codes x q') + beta
     float s[2][4];
 #pragma unroll
@@ -536,7 +543,7 @@ struct PackedWave {
       for (int i = 0; i < 4; ++i) {
         // elements 2i (run A) and 2i+1 (run B) = score tile i/2, rows 2(i%2), +1
         const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
-        split2(mul_lo(pa, r.vmA[f][i]), mul_lo(pb, r.vmB[f][i]), bh[i], bl[i]);
+        split2(mul_lo(pa, r.vmA[f][i]), mul_lo(pb, r.vmB[f][i]), m1, bh[i], bl[i]);
         bias[f] = mul_hi(pa, r.vmA[f][i], bias[f]);
         bias[f] = mul_hi(pb, r.vmB[f][i], bias[f]);
       }
@@ -700,8 +707,6 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
   w.qfs = qfs;
   w.qB = reinterpret_cast<uint4*>(wl);
   w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
-  w.c_lo = pc0;
-  w.c_hi = pc1;
   w.init(lane);
   int e_mine = 0;
 #pragma unroll
@@ -712,11 +717,11 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
 
   if (pc0 < pc1) {
     // two chunk buffers: the next chunk's loads are in flight while one is
-    // used.  Prefetches past the last chunk re-load that chunk (always in
-    // bounds) instead of being skipped, so no load sits under a branch.
+    // used (a deeper ring measured no faster).  Prefetches past the last
+    // chunk re-load that chunk (always in bounds) instead of being skipped,
+    // so no load sits under a branch.
     R ra, rb;
     const int last = pc1 - 1;
-    w.load_kmeta((pc0 * kChunk) / C::G);
     w.load(pc0, ra);
     for (int ch = pc0; ch < pc1; ch += 2) {
       w.load(min(ch + 1, last), rb);
