@@ -58,30 +58,56 @@
  * over the dequantized values gives the exact low-bit outputs).
  *
  * ---------------------------------------------------------------------------
- * PACKED LAYOUT  (KVQ_LAYOUT_VERSION 1)
+ * PACKED LAYOUT  (KVQ_LAYOUT_VERSION 2)
  * ---------------------------------------------------------------------------
  * Shapes use: B = batch, Hkv = KV heads, D = head_dim, G = group, R = residual,
  * C = capacity (tokens per sequence), bK / bV = key / value bits.
  * All arrays are dense, C-order, little-endian, caller-owned device memory.
  *
- *   k_codes  uint32 [B][Hkv][C][D*bK/32]          token-major rows.
- *            Channel c of a token sits in bits ((c*bK) % 32) .. +bK-1 of word
- *            (c*bK)/32 of the token's row, lowest channel in the lowest bits
- *            (the code order of the 2-bit BQ2_0 block in [KV1] Quantization
- *            Format, where the first of four codes takes the two lowest bits
- *            of a byte; extended here to 4-bit fields).
- *   k_meta   uint16 [B][Hkv][C/G][D][2]           fp16 (scale, min) of key group
- *            j = tokens [jG, jG+G) and channel c; scale first, as the scale field precedes
- *            the min field in the [KV1] BQ2_0 block.
- *   v_codes  uint32 [B][Hkv][C/32][D][bV]         32-token blocks, channel-major
- *            inside a block: word w of channel c in block k holds tokens
- *            32k + tau with (tau*bV)/32 == w, token tau in bits
- *            ((tau*bV) % 32) .. +bV-1 (lowest token in the lowest bits).
- *   v_meta   uint16 [B][Hkv][C/32][D/G][32][2]    fp16 (scale, min) of token t,
- *            channel group gamma = channels [gamma*G, gamma*G+G), stored in
- *            32-token blocks: block t/32, then gamma, then token t % 32.
+ * Packed tokens are stored in blocks of 32 consecutive positions
+ * [32k, 32k + 32); tau = t - 32k is a token's place in its block.  Inside a
+ * block the words are in the order in which a 64-lane wave consumes them, so
+ * that every lane reads one contiguous run of words: lane l = 16 g + i with
+ * lane group g in [0, 4) and i in [0, 16).  Two fixed token orders are used:
+ *   key row i of half u (u in {0, 1}):  tau = 8 (i / 4) + 4 u + (i % 4)
+ *   value element j of lane group g:    tau = 8 g + j,   j in [0, 8)
+ * (the two agree: lane group g's rows 4g..4g+3 of halves 0 and 1 are the
+ * tokens 8g + j).  Inside a field, the code order is the one of the 2-bit
+ * BQ2_0 block in [KV1] Quantization Format: the first code of a byte takes
+ * its lowest bits (extended here to 4-bit fields).
+ *
+ *   k_codes  uint32 [B][Hkv][C/32][64][2][KW],  KW = D*bK/128.
+ *            Entry [k][l][u][w] holds key row i of half u (token tau above) of
+ *            block k, restricted to channel slice g = channels
+ *            [g*D/4, (g+1)*D/4): its word w holds the 32/bK channels
+ *            g*D/4 + w*32/bK + f, channel f of the word in bits f*bK .. +bK-1.
+ *            (A token's natural row of D*bK/32 words is the concatenation of
+ *            its 4 slices, word w of slice g being row word g*KW + w.)
+ *   k_meta   uint16 [B][Hkv][C/G][D/8][8][2]  fp16 (scale, min) of key group
+ *            q = tokens [qG, qG+G); scale first, as the scale field precedes
+ *            the min field in the [KV1] BQ2_0 block.  Entry [q][r][e] is the
+ *            channel that element e of k-chunk r feeds:
+ *              r = g*(D/32) + kc (g in [0,4), kc in [0, D/32)),
+ *              channel = g*D/4 + base + (e / 2) + off * (e % 2)
+ *            with base = 16*(kc/2) + 4*(kc%2), off = 8 for bK = 2 and
+ *                 base = 8*kc,                  off = 4 for bK = 4
+ *            (the channels of key word fields: bits 0..15 of a word hold the
+ *            even elements, bits 16..31 the odd ones).
+ *   v_codes  uint32 [B][Hkv][C/32][64][NW],  NW = D*bV/64.
+ *            bV = 4: entry [k][l][n] (n in [0, D/16)) holds channel 16n + i;
+ *              token tau = 8g + j sits in bits 4*(j/2) + 16*(j%2) .. +3.
+ *            bV = 2: entry [k][l][m] (m in [0, D/32)) holds channels
+ *              16(2m + h) + i for h in {0, 1}; token tau = 8g + j of channel
+ *              16(2m + h) + i sits in bits 8h + 2*(j/2) + 16*(j%2) .. +1.
+ *   v_meta   uint16 [B][Hkv][C/32][4][D/G][8][2]  fp16 (scale, min) of token
+ *            32k + 8g + j and channel group gamma = channels
+ *            [gamma*G, gamma*G + G) at entry [k][g][gamma][j].
  *   k_res,   uint16 [B][Hkv][R][D]                fp16 residual window; position
  *   v_res                                         p lives in slot p % R.
+ *
+ * Version 1 (token-major key rows, channel-major value blocks) is retired:
+ * its per-lane addresses were scattered, and the decode kernel's loads of it
+ * took about 1.2x as long as contiguous ones.
  *
  * Constraints (checked, KVQ_ERR_GEOM / KVQ_ERR_BITS otherwise):
  *   batch >= 1; n_kv_heads >= 1; n_q_heads % n_kv_heads == 0 and
@@ -122,7 +148,7 @@ extern "C" {
 #endif
 
 #define KVQ_ABI_VERSION 1
-#define KVQ_LAYOUT_VERSION 1
+#define KVQ_LAYOUT_VERSION 2
 #define KVQ_VBLOCK 32 /* tokens per v_codes block */
 
 enum {

@@ -65,6 +65,7 @@ def lib():
         L.orc_append.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 9
         L.orc_cache_kv.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 6 + [i64, P, P]
         L.orc_decode_attn.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 8 + [f64, P]
+        L.orc_unpack.argtypes = [ctypes.c_int] * 6 + [i64] + [P] * 8
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -134,10 +135,11 @@ class Cache:
     def __init__(self, g: Geom):
         B, H, C, D = g.batch, g.n_kv_heads, g.capacity, g.head_dim
         self.g = g
-        self.k_codes = np.zeros((B, H, C, D * g.k_bits // 32), np.uint32)
-        self.v_codes = np.zeros((B, H, C // VBLOCK, D, g.v_bits), np.uint32)
-        self.k_meta = np.zeros((B, H, C // g.group, D, 2), np.uint16)
-        self.v_meta = np.zeros((B, H, C // VBLOCK, D // g.group, VBLOCK, 2), np.uint16)
+        blocks = C // VBLOCK
+        self.k_codes = np.zeros((B, H, blocks, 64, 2, D * g.k_bits // 128), np.uint32)
+        self.v_codes = np.zeros((B, H, blocks, 64, D * g.v_bits // 64), np.uint32)
+        self.k_meta = np.zeros((B, H, C // g.group, D // 8, 8, 2), np.uint16)
+        self.v_meta = np.zeros((B, H, blocks, 4, D // g.group, 8, 2), np.uint16)
         self.k_res = np.zeros((B, H, g.residual, D), np.uint16)
         self.v_res = np.zeros((B, H, g.residual, D), np.uint16)
 
@@ -212,6 +214,22 @@ def decode_attn(g: Geom, cache: Cache, q: np.ndarray, seq_lens: np.ndarray,
                           _p(q), *[_p(a) for a in cache.arrays()], _p(sl),
                           float(sm_scale), _p(out))
     return out
+
+
+def unpack(g: Geom, cache: Cache):
+    """The cache's codes and (scale, min) bits in natural order (tests only):
+    k_code, v_code uint8 [B][Hkv][C][D]; k_sm uint16 [B][Hkv][C/G][D][2]
+    (per key group and channel); v_sm uint16 [B][Hkv][C][D/G][2] (per token
+    and channel group)."""
+    B, H, C, D, G = g.batch, g.n_kv_heads, g.capacity, g.head_dim, g.group
+    k_code = np.zeros((B, H, C, D), np.uint8)
+    v_code = np.zeros((B, H, C, D), np.uint8)
+    k_sm = np.zeros((B, H, C // G, D, 2), np.uint16)
+    v_sm = np.zeros((B, H, C, D // G, 2), np.uint16)
+    lib().orc_unpack(B, H, D, g.k_bits, g.v_bits, G, C, _p(cache.k_codes),
+                     _p(cache.v_codes), _p(cache.k_meta), _p(cache.v_meta),
+                     _p(k_code), _p(v_code), _p(k_sm), _p(v_sm))
+    return k_code, v_code, k_sm, v_sm
 
 
 def max_threads() -> int:

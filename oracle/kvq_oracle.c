@@ -52,7 +52,6 @@
 #include <omp.h>
 #endif
 
-#define ORC_VBLOCK 32 /* tokens per value-code block in the packed layout */
 
 /* ------------------------------------------------------------------------ */
 /* fp16 <-> fp32 in software                                                 */
@@ -178,15 +177,23 @@ void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Packed layout (restated from its specification)                          */
+/* Packed layout, version 2 (restated from its specification)               */
 /*                                                                           */
-/* k_codes  u32 [B][Hkv][C][D*bK/32]: token rows, channel c in bits          */
-/*          (c*bK)%32.. of word (c*bK)/32, lowest channel lowest.            */
-/* k_meta   u16 [B][Hkv][C/G][D][2]: (scale, min) per key group and channel. */
-/* v_codes  u32 [B][Hkv][C/32][D][bV]: 32-token blocks; for channel c,       */
-/*          token tau of the block in bits (tau*bV)%32.. of word (tau*bV)/32.*/
-/* v_meta   u16 [B][Hkv][C/32][D/G][32][2]: (scale, min) per token and      */
-/*          channel group, in 32-token blocks (block, group, token).        */
+/* Packed tokens live in blocks of 32 positions; tau = t % 32.  Inside a     */
+/* block, words follow a 64-lane consumer order, lane l = 16 g + i.          */
+/*   key row i of half u holds    tau = 8 (i/4) + 4 u + i % 4                */
+/*   value element j of group g:  tau = 8 g + j                              */
+/* k_codes  u32 [B][Hkv][C/32][64][2][KW], KW = D*bK/128: [k][l][u][w] is    */
+/*          slice g (channels g*D/4 ..) of key row i of half u; its word w   */
+/*          holds channels g*D/4 + w*32/bK + f in bits f*bK.                 */
+/* k_meta   u16 [B][Hkv][C/G][D/8][8][2]: entry [q][r][e] is the channel     */
+/*          key_meta_channel(r, e) of key group q.                           */
+/* v_codes  u32 [B][Hkv][C/32][64][NW], NW = D*bV/64: 4 bits: word n of lane */
+/*          l is channel 16n + i, token 8g + j at bit 4(j/2) + 16(j%2);      */
+/*          2 bits: word m of lane l holds channels 16(2m+h) + i, token      */
+/*          8g + j at bit 8h + 2(j/2) + 16(j%2).                             */
+/* v_meta   u16 [B][Hkv][C/32][4][D/G][8][2]: entry [k][g][gamma][j] is      */
+/*          token 32k + 8g + j, channel group gamma.                         */
 /* k_res, v_res u16 [B][Hkv][R][D]: position p in slot p % R.               */
 /* ------------------------------------------------------------------------ */
 
@@ -199,29 +206,85 @@ static uint32_t get_field(uint32_t word, int bit, int bits) {
   return (word >> bit) & ((1u << bits) - 1u);
 }
 
-/* Key code of token t, channel c of unit (b, h), from the packed rows. */
+/* Index into k_codes of the word holding token t, channel c of a unit, and
+ * the bit at which its code starts. */
+static int64_t key_word(int64_t unit, int64_t C, int D, int bK, int64_t t,
+                        int c, int *bit) {
+  int64_t k = t / 32;
+  int tau = (int)(t % 32);
+  int slice = D / 4; /* channels of a lane group's slice */
+  int g = c / slice, cs = c % slice;
+  int kw = D * bK / 128; /* words per slice */
+  int w = cs * bK / 32;
+  *bit = cs * bK % 32;
+  /* the key row i of half u that holds tau = 8 (i/4) + 4 u + i % 4 */
+  int u = (tau / 4) % 2;
+  int i = 4 * (tau / 8) + tau % 4;
+  int l = 16 * g + i;
+  return (unit * (C / 32) + k) * (int64_t)D * bK + ((int64_t)l * 2 + u) * kw + w;
+}
+
+/* Channel of key-meta entry e (0..7) of k-chunk r (0..D/8-1). */
+static int key_meta_channel(int D, int bK, int r, int e) {
+  int kcs = D / 32; /* k-chunks per slice */
+  int g = r / kcs, kc = r % kcs;
+  int base, off;
+  if (bK == 2) {
+    base = 16 * (kc / 2) + 4 * (kc % 2);
+    off = 8;
+  } else {
+    base = 8 * kc;
+    off = 4;
+  }
+  return g * (D / 4) + base + e / 2 + off * (e % 2);
+}
+
+/* entry_of[c] = position (r*8 + e) of channel c inside a key group's meta. */
+static void key_meta_entries(int D, int bK, int *entry_of) {
+  for (int r = 0; r < D / 8; ++r)
+    for (int e = 0; e < 8; ++e) entry_of[key_meta_channel(D, bK, r, e)] = r * 8 + e;
+}
+
 static uint32_t key_code(const uint32_t *k_codes, int64_t unit, int64_t C,
                          int D, int bK, int64_t t, int c) {
-  int64_t words = (int64_t)D * bK / 32;
-  const uint32_t *row = k_codes + (unit * C + t) * words;
-  return get_field(row[(c * bK) / 32], (c * bK) % 32, bK);
+  int bit;
+  int64_t w = key_word(unit, C, D, bK, t, c, &bit);
+  return get_field(k_codes[w], bit, bK);
+}
+
+/* Index into v_codes of the word holding token t, channel c, and its bit. */
+static int64_t value_word(int64_t unit, int64_t C, int D, int bV, int64_t t,
+                          int c, int *bit) {
+  int64_t k = t / 32;
+  int tau = (int)(t % 32);
+  int g = tau / 8, j = tau % 8;
+  int i = c % 16, n = c / 16;
+  int l = 16 * g + i;
+  int nw = D * bV / 64; /* words per lane */
+  int w;
+  if (bV == 4) {
+    w = n;
+    *bit = 4 * (j / 2) + 16 * (j % 2);
+  } else {
+    w = n / 2;
+    *bit = 8 * (n % 2) + 2 * (j / 2) + 16 * (j % 2);
+  }
+  return (unit * (C / 32) + k) * (int64_t)D * bV + (int64_t)l * nw + w;
+}
+
+static uint32_t value_code(const uint32_t *v_codes, int64_t unit, int64_t C,
+                           int D, int bV, int64_t t, int c) {
+  int bit;
+  int64_t w = value_word(unit, C, D, bV, t, c, &bit);
+  return get_field(v_codes[w], bit, bV);
 }
 
 /* Entry of (scale, min) for token t, channel group gm in v_meta. */
 static int64_t value_meta_index(int64_t unit, int64_t C, int D, int G,
                                 int64_t t, int gm) {
-  int64_t blk = t / ORC_VBLOCK;
-  return ((unit * (C / ORC_VBLOCK) + blk) * (D / G) + gm) * ORC_VBLOCK +
-         t % ORC_VBLOCK;
-}
-
-static uint32_t value_code(const uint32_t *v_codes, int64_t unit, int64_t C,
-                           int D, int bV, int64_t t, int c) {
-  int64_t blk = t / ORC_VBLOCK;
-  int tau = (int)(t % ORC_VBLOCK);
-  const uint32_t *field =
-      v_codes + ((unit * (C / ORC_VBLOCK) + blk) * D + c) * bV;
-  return get_field(field[(tau * bV) / 32], (tau * bV) % 32, bV);
+  int64_t k = t / 32;
+  int tau = (int)(t % 32);
+  return ((unit * (C / 32) + k) * 4 + tau / 8) * (D / G) * 8 + gm * 8 + tau % 8;
 }
 
 /* Quantizes key groups of one unit from a source of token rows src[t*D + c]
@@ -229,21 +292,22 @@ static uint32_t value_code(const uint32_t *v_codes, int64_t unit, int64_t C,
 static void quantize_keys_unit(const uint16_t *src, int64_t pos0, int64_t n_tok,
                                int D, int bK, int G, int64_t C, int64_t unit,
                                uint32_t *k_codes, uint16_t *k_meta) {
-  int64_t words = (int64_t)D * bK / 32;
   uint8_t *codes = (uint8_t *)malloc((size_t)G);
+  int entry_of[128];
+  key_meta_entries(D, bK, entry_of);
   for (int64_t j0 = 0; j0 < n_tok; j0 += G) {
     int64_t j = (pos0 + j0) / G; /* key group index */
     for (int c = 0; c < D; ++c) {
       uint16_t d16, m16;
       /* per channel: the G tokens of the group ([KIVI] keys per channel) */
       orc_quantize_group(src + j0 * D + c, G, D, bK, &d16, &m16, codes, 1);
-      uint16_t *meta = k_meta + ((unit * (C / G) + j) * D + c) * 2;
+      uint16_t *meta = k_meta + ((unit * (C / G) + j) * D + entry_of[c]) * 2;
       meta[0] = d16;
       meta[1] = m16;
       for (int i = 0; i < G; ++i) {
-        int64_t t = pos0 + j0 + i;
-        uint32_t *row = k_codes + (unit * C + t) * words;
-        put_field(&row[(c * bK) / 32], (c * bK) % 32, bK, codes[i]);
+        int bit;
+        int64_t w = key_word(unit, C, D, bK, pos0 + j0 + i, c, &bit);
+        put_field(&k_codes[w], bit, bK, codes[i]);
       }
     }
   }
@@ -268,12 +332,9 @@ static void quantize_values_unit(const uint16_t *src, int64_t pos0,
       meta[0] = d16;
       meta[1] = m16;
       for (int cc = 0; cc < G; ++cc) {
-        int c = gm * G + cc;
-        int64_t blk = t / ORC_VBLOCK;
-        int tau = (int)(t % ORC_VBLOCK);
-        uint32_t *field =
-            v_codes + ((unit * (C / ORC_VBLOCK) + blk) * D + c) * bV;
-        put_field(&field[(tau * bV) / 32], (tau * bV) % 32, bV, codes[cc]);
+        int bit;
+        int64_t w = value_word(unit, C, D, bV, t, gm * G + cc, &bit);
+        put_field(&v_codes[w], bit, bV, codes[cc]);
       }
     }
   }
@@ -351,9 +412,9 @@ void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int R, int64_t C,
  * Dequantize).  The product of a code below 16 and an fp16 scale, plus an fp16
  * min, is exact in fp64. */
 static double dequant_key(const uint32_t *k_codes, const uint16_t *k_meta,
-                          int64_t unit, int64_t C, int D, int bK, int G,
-                          int64_t t, int c) {
-  const uint16_t *meta = k_meta + ((unit * (C / G) + t / G) * D + c) * 2;
+                          const int *entry_of, int64_t unit, int64_t C, int D,
+                          int bK, int G, int64_t t, int c) {
+  const uint16_t *meta = k_meta + ((unit * (C / G) + t / G) * D + entry_of[c]) * 2;
   double scale = orc_half_to_float(meta[0]);
   double minv = orc_half_to_float(meta[1]);
   return (double)key_code(k_codes, unit, C, D, bK, t, c) * scale + minv;
@@ -378,13 +439,15 @@ void orc_cache_kv(int B, int Hkv, int D, int bK, int bV, int G, int R,
                   double *out_k, double *out_v) {
   int64_t units = (int64_t)B * Hkv;
   int64_t lq = orc_packed_len(n, R);
+  int entry_of[128];
+  key_meta_entries(D, bK, entry_of);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u) {
     for (int64_t t = 0; t < n; ++t) {
       for (int c = 0; c < D; ++c) {
         double kv, vv;
         if (t < lq) {
-          kv = dequant_key(k_codes, k_meta, u, C, D, bK, G, t, c);
+          kv = dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c);
           vv = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
         } else {
           kv = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
@@ -416,6 +479,8 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
                      const int32_t *seq_lens, double sm_scale, double *out) {
   int64_t units = (int64_t)B * Hkv;
   int g = Hq / Hkv;
+  int entry_of[128];
+  key_meta_entries(D, bK, entry_of);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u) {
     int b = (int)(u / Hkv);
@@ -430,7 +495,7 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
     for (int64_t t = 0; t < n; ++t) {
       for (int c = 0; c < D; ++c) {
         if (t < lq) {
-          kk[t * D + c] = dequant_key(k_codes, k_meta, u, C, D, bK, G, t, c);
+          kk[t * D + c] = dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c);
           vv[t * D + c] = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
         } else {
           kk[t * D + c] = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
@@ -465,6 +530,35 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
     free(kk);
     free(vv);
     free(s);
+  }
+}
+
+/* The cache's codes and (scale, min) pairs in natural order, for tests:
+ * k_code, v_code u8 [B*Hkv][C][D]; k_sm u16 [B*Hkv][C/G][D][2];
+ * v_sm u16 [B*Hkv][C][D/G][2]. */
+void orc_unpack(int B, int Hkv, int D, int bK, int bV, int G, int64_t C,
+                const uint32_t *k_codes, const uint32_t *v_codes,
+                const uint16_t *k_meta, const uint16_t *v_meta, uint8_t *k_code,
+                uint8_t *v_code, uint16_t *k_sm, uint16_t *v_sm) {
+  int64_t units = (int64_t)B * Hkv;
+  int entry_of[128];
+  key_meta_entries(D, bK, entry_of);
+  for (int64_t u = 0; u < units; ++u) {
+    for (int64_t t = 0; t < C; ++t)
+      for (int c = 0; c < D; ++c) {
+        k_code[(u * C + t) * D + c] = (uint8_t)key_code(k_codes, u, C, D, bK, t, c);
+        v_code[(u * C + t) * D + c] = (uint8_t)value_code(v_codes, u, C, D, bV, t, c);
+      }
+    for (int64_t q = 0; q < C / G; ++q)
+      for (int c = 0; c < D; ++c)
+        for (int x = 0; x < 2; ++x)
+          k_sm[((u * (C / G) + q) * D + c) * 2 + x] =
+              k_meta[((u * (C / G) + q) * D + entry_of[c]) * 2 + x];
+    for (int64_t t = 0; t < C; ++t)
+      for (int gm = 0; gm < D / G; ++gm)
+        for (int x = 0; x < 2; ++x)
+          v_sm[((u * C + t) * (D / G) + gm) * 2 + x] =
+              v_meta[value_meta_index(u, C, D, G, t, gm) * 2 + x];
   }
 }
 

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 ABI_VERSION = 1
-LAYOUT_VERSION = 1
+LAYOUT_VERSION = 2
 VBLOCK = 32
 
 # status codes (include/kvq.h)
@@ -201,10 +201,13 @@ class Cache:
         B, H, C, D = g.batch, g.n_kv_heads, g.capacity, g.head_dim
         self.g = g
         z = dict(device=device)
-        self.k_codes = torch.zeros((B, H, C, D * g.k_bits // 32), dtype=torch.int32, **z)
-        self.v_codes = torch.zeros((B, H, C // VBLOCK, D, g.v_bits), dtype=torch.int32, **z)
-        self.k_meta = torch.zeros((B, H, C // g.group, D, 2), dtype=torch.int16, **z)
-        self.v_meta = torch.zeros((B, H, C // VBLOCK, D // g.group, VBLOCK, 2),
+        blocks = C // VBLOCK
+        self.k_codes = torch.zeros((B, H, blocks, 64, 2, D * g.k_bits // 128),
+                                   dtype=torch.int32, **z)
+        self.v_codes = torch.zeros((B, H, blocks, 64, D * g.v_bits // 64),
+                                   dtype=torch.int32, **z)
+        self.k_meta = torch.zeros((B, H, C // g.group, D // 8, 8, 2), dtype=torch.int16, **z)
+        self.v_meta = torch.zeros((B, H, blocks, 4, D // g.group, 8, 2),
                                   dtype=torch.int16, **z)
         self.k_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
         self.v_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)

@@ -125,23 +125,21 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Token and channel permutations of the MFMA operands.
+// Token order inside a 32-token chunk (the packed layout stores every chunk in
+// this consumer order, so each lane's share is one contiguous run of words).
 //
 // Value side: the A operand of lane (channel c, lane group g) holds 8 codes of
-// channel c; element j is the chunk token tok_v(g, j).  It comes straight from
-// the packed value word(s): 4-bit words hold tokens 8w..8w+7 (nibble e = token
-// 8w+e), and one mask of (w >> 4e) with 0x000F000F yields tokens 8g+e and
-// 8g+4+e as an fp16 pair; 2-bit words hold 16 tokens and (w >> 2s) & 0x00030003
-// yields tokens s and s+8 of the word.
-// Key side: tile u (16 tokens) row r is token tok_v(r / 4, 4u + r % 4), so that
-// the score tile's output registers (lane group g, register r' of tile u) hold
-// exactly the tokens tok_v(g, 4u + r') that the value side wants in element
-// 4u + r' of its B operand: the scores never leave their lanes.
+// channel c; element j is token 8g + j.  A 4-bit word holds them with element
+// 2e in nibble e and element 2e+1 in nibble 4 + e, so (w >> 4e) & 0x000F000F
+// is the fp16 pair (2e, 2e+1); a 2-bit word holds two channel tiles, tile
+// parity h in bits 8h.., and (w >> (8h + 2e)) & 0x00030003 is the pair.
+// Key side: score tile u row r is token 8 (r/4) + 4u + r%4, so the score
+// tile's output registers (lane group g, register q of tile u) hold tokens
+// 8g + 4u + q: exactly element 4u + q of the value side's B operand, and the
+// scores never leave their lanes.
 // ---------------------------------------------------------------------------
-template <int BV>
-__device__ __forceinline__ constexpr int tok_v(int g, int j) {
-  const int e = j >> 1, par = j & 1;
-  return BV == 4 ? 8 * g + 4 * par + e : 16 * (g >> 1) + 8 * par + 4 * (g & 1) + e;
+__device__ __forceinline__ constexpr int key_row_token(int u, int r) {
+  return 8 * (r >> 2) + 4 * u + (r & 3);
 }
 
 // First channel of the two 4-channel runs a key-side B fragment (lane group g,
@@ -177,16 +175,18 @@ __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
   }
 }
 
-template <int KW>
-__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[KW]) {
-  if constexpr (KW == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else if constexpr (KW == 2) {
+// N consecutive words (N = 2, 4 or 8; 8 N-byte aligned up to 16) as wide loads.
+template <int N>
+__device__ __forceinline__ void load_run(const uint32_t* p, uint32_t (&w)[N]) {
+  if constexpr (N == 2) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     w[0] = v.x; w[1] = v.y;
   } else {
-    w[0] = p[0];
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+      w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
   }
 }
 
@@ -200,6 +200,7 @@ struct Cfg {
   static constexpr int G = D / NG;
   static constexpr int KC = D / 32;               // k-chunks of a score tile
   static constexpr int NT = D / 16;               // value channel tiles
+  static constexpr int NW = D * BV / 64;          // value code words per lane
   static constexpr int KW = kKW<D, BK>;           // key words per lane and row
   static constexpr int WR = D * BK / 32;          // words per key row
   static constexpr int SL = 16 / GQ;              // MFMA columns per head
@@ -218,7 +219,7 @@ template <int D, int BK, int BV, int GQ, int NG>
 struct Raw {
   using C = Cfg<D, BK, BV, GQ, NG>;
   uint32_t kw[2][C::KW];              // key code words of score tiles 0, 1
-  uint32_t vw[C::NT];                 // value code word per channel tile
+  uint32_t vw[C::NW];                 // value code words (tile n: word n*BV/4)
   uint32_t vmA[C::NF][4], vmB[C::NF][4];  // value (scale, min) of the B elements
   uint4 kmA[C::IPL], kmB[C::IPL];     // key (scale, min) of the chunk's group
 };
@@ -245,10 +246,10 @@ struct PackedWave {
   float* beta_l;
   // lane constants
   int lane, col, lg, hcol, slot;
-  int koff[2];
-  int voff;
-  int vmoff[NF][2];
-  int kmoff[IPL][2];
+  int kofs, vofs;      // this lane's key / value words inside a chunk
+  int vmofs[NF];       // value meta run of fragment f inside a chunk
+  int kmofs[IPL];      // key meta run of fold item i inside a group
+  int kmoff[IPL][2];   // channels of fold item i (runs A and B)
   int fitem[IPL];
   float kscale, bscale;
   float m1;  // -1 in a register (split2)
@@ -267,21 +268,16 @@ struct PackedWave {
     lg = lane >> 4;
     hcol = col / SL;
     slot = col % SL;
+    kofs = lane * 2 * KW;
+    vofs = lane * C::NW;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      koff[u] = tok_v<BV>(col >> 2, 4 * u + (col & 3)) * WR + lg * KW;
-    voff = col * BV + (BV == 4 ? lg : (lg >> 1));
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int gm = (f * SL + slot) % NG;
-      vmoff[f][0] = gm * kVBlock + tok_v<BV>(lg, 0);
-      vmoff[f][1] = gm * kVBlock + tok_v<BV>(lg, 1);
-    }
+    for (int f = 0; f < NF; ++f) vmofs[f] = (lg * NG + (f * SL + slot) % NG) * 8;
 #pragma unroll
     for (int i = 0; i < IPL; ++i) {
       const int it = lane + 64 * i;
       fitem[i] = it;
       const int r = it % IPH, gg = r / KC, kc = r % KC;
+      kmofs[i] = r * 8;
       kmoff[i][0] = key_run0<D, BK>(gg, kc);
       kmoff[i][1] = kmoff[i][0] + kKeyOff<BK>;
     }
@@ -296,29 +292,41 @@ struct PackedWave {
   }
 
   __device__ __forceinline__ void load(int ch, R& r) const {
-    const uint32_t* kc = kcodes + (int64_t)ch * kChunk * WR;
+    {
+      uint32_t w[2 * KW];
+      load_run<2 * KW>(kcodes + (int64_t)ch * (D * BK) + kofs, w);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) load_words<KW>(kc + koff[u], r.kw[u]);
-    const uint32_t* vc = vcodes + (int64_t)ch * D * BV;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) r.vw[n] = vc[voff + 16 * n * BV];
-    const uint32_t* vm = vmeta + (int64_t)ch * NG * kVBlock;
+      for (int k = 0; k < KW; ++k) {
+        r.kw[0][k] = w[k];
+        r.kw[1][k] = w[KW + k];
+      }
+    }
+    load_run<C::NW>(vcodes + (int64_t)ch * (D * BV) + vofs, r.vw);
+    // value (scale, min) of tokens 8 lg + j: even j feed B elements 2i (run
+    // A), odd j elements 2i + 1 (run B)
+    const uint32_t* vm = vmeta + (int64_t)ch * (4 * NG * 8);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const uint4 a = *reinterpret_cast<const uint4*>(vm + vmoff[f][0]);
-      const uint4 c = *reinterpret_cast<const uint4*>(vm + vmoff[f][1]);
-      r.vmA[f][0] = a.x; r.vmA[f][1] = a.y; r.vmA[f][2] = a.z; r.vmA[f][3] = a.w;
-      r.vmB[f][0] = c.x; r.vmB[f][1] = c.y; r.vmB[f][2] = c.z; r.vmB[f][3] = c.w;
+      uint32_t w[8];
+      load_run<8>(vm + vmofs[f], w);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r.vmA[f][i] = w[2 * i];
+        r.vmB[f][i] = w[2 * i + 1];
+      }
     }
     // key meta of the chunk's group, with the chunk's other loads (one
     // in-order stream, so waiting for a chunk never waits for a later one).
-    // Lanes past the fold items load an in-range row too (kmoff depends on
+    // Entry e of an item is channel run A + e/2 (even e) or run B + e/2 (odd).
+    // Lanes past the fold items load an in-range run too (the run depends on
     // the item modulo a head's items): no load sits under a branch.
     const uint32_t* km = kmeta + (int64_t)((ch * kChunk) / G) * D;
 #pragma unroll
     for (int i = 0; i < IPL; ++i) {
-      r.kmA[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][0]);
-      r.kmB[i] = *reinterpret_cast<const uint4*>(km + kmoff[i][1]);
+      uint32_t w[8];
+      load_run<8>(km + kmofs[i], w);
+      r.kmA[i] = make_uint4(w[0], w[2], w[4], w[6]);
+      r.kmB[i] = make_uint4(w[1], w[3], w[5], w[7]);
     }
   }
 
@@ -451,12 +459,12 @@ struct PackedWave {
         for (int v = 0; v < V4; ++v) dst[v] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    // scores: tile u row r = token tok_v<4>(r/4, 4u + r%4)
+    // scores: tile u row r = token key_row_token(u, r)
     const float kscale_r = bscale;  // keys are real fp16 values here
     float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int tin = t0 + tok_v<4>(col >> 2, 4 * u + (col & 3));
+      const int tin = t0 + key_row_token(u, col);
       const int slot_in = (tin < n_tok ? tin : n_tok - 1) % R;
       const uint4* krow = reinterpret_cast<const uint4*>(kres + (int64_t)slot_in * D);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -474,7 +482,7 @@ struct PackedWave {
           x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
                    __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
         }
-        const bool valid = t0 + tok_v<4>(lg, 4 * u + q) < n_tok;
+        const bool valid = t0 + 8 * lg + 4 * u + q < n_tok;
         s[u][q] = valid ? x * kscale_r : kNegInf;
       }
     }
@@ -492,8 +500,8 @@ struct PackedWave {
       uint32_t a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo16 = vbuf[tok_v<4>(lg, 2 * i) * D + 16 * n + col];
-        const uint32_t hi16 = vbuf[tok_v<4>(lg, 2 * i + 1) * D + 16 * n + col];
+        const uint32_t lo16 = vbuf[(8 * lg + 2 * i) * D + 16 * n + col];
+        const uint32_t hi16 = vbuf[(8 * lg + 2 * i + 1) * D + 16 * n + col];
         a[i] = lo16 | (hi16 << 16);
       }
       oacc[n] = mfma(a, bh, oacc[n]);
@@ -555,9 +563,9 @@ struct PackedWave {
 #pragma unroll
           for (int e = 0; e < 4; ++e) a[e] = (r.vw[n] >> (4 * e)) & 0x000F000Fu;
         } else {
-          const int sh = 8 * (lg & 1);
+          const int sh = 8 * (n & 1);  // tile parity selects the byte
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = (r.vw[n] >> (sh + 2 * e)) & 0x00030003u;
+          for (int e = 0; e < 4; ++e) a[e] = (r.vw[n >> 1] >> (sh + 2 * e)) & 0x00030003u;
         }
         oacc[n] = mfma(a, bh, oacc[n]);
         oacc[n] = mfma(a, bl, oacc[n]);

@@ -53,6 +53,24 @@ __device__ __forceinline__ uint32_t group_code(float x, const GroupParams& p,
   return (uint32_t)r;
 }
 
+// Place of channel c inside a key group's D meta entries: entry 8 r + e is the
+// channel that element e of k-chunk r (lane group g = r / (D/32), chunk
+// kc = r % (D/32)) feeds: g D/4 + base(kc) + e/2 + off (e%2).  Inverse:
+// within its slice, channel cs sits in word cs / (32/BITS) at field s'; the
+// field's half (low / high 16 bits) gives e % 2, its place in the half gives
+// the chunk and e / 2.
+template <int BITS>
+__device__ __forceinline__ int key_meta_entry(int c, int D) {
+  constexpr int per = 32 / BITS;  // fields per word
+  constexpr int hp = per / 2;     // fields per half word
+  const int g = c / (D / 4), cs = c % (D / 4);
+  const int wi = cs / per, sp = cs % per;
+  const int half = sp / hp, s = sp % hp;
+  const int kc = wi * (hp / 4) + s / 4;
+  const int r = g * (D / 32) + kc;
+  return 8 * r + 2 * (s % 4) + half;
+}
+
 // Loads n_halves fp16 values (a multiple of 8, 16-byte aligned) into LDS.
 __device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* src,
                                           int n_halves) {
@@ -79,22 +97,29 @@ __device__ void key_group(const Geom& g, const uint16_t* src, int64_t unit,
       mx = fmaxf(mx, v);
     }
     const GroupParams p = group_params(mn, mx, BITS);
-    meta32[(unit * (g.C / G) + pos / G) * D + c] =
+    meta32[(unit * (g.C / G) + pos / G) * D + key_meta_entry<BITS>(c, D)] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
     for (int t = 0; t < G; ++t)
       codes[t * D + c] = (uint8_t)group_code(h2f(tile[t * D + c]), p, BITS);
   }
   __syncthreads();
+  // words of the natural token rows, stored at their consumer-order places:
+  // row word w' is word w' % KW of slice w' / KW, placed at lane 16 g + i,
+  // half u for the token's key row (i, u) in its 32-token block
   constexpr int kPer = 32 / BITS;  // codes per word
   const int W = D * BITS / 32;     // words per token row
-  uint32_t* rows = k_codes + (unit * g.C + pos) * W;
-  for (int i = threadIdx.x; i < G * W; i += blockDim.x) {
-    const int t = i / W, w = i % W;
-    const uint8_t* cc = codes + t * D + w * kPer;
+  const int KW = W / 4;            // words per slice
+  for (int x = threadIdx.x; x < G * W; x += blockDim.x) {
+    const int t = x / W, wr = x % W;
+    const uint8_t* cc = codes + t * D + wr * kPer;
     uint32_t word = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) word |= (uint32_t)cc[k] << (k * BITS);
-    rows[i] = word;
+    const int p_tok = pos + t, tau = p_tok % kVBlock;
+    const int u = (tau >> 2) & 1, i = 4 * (tau >> 3) + (tau & 3);
+    const int lane = 16 * (wr / KW) + i;
+    k_codes[(unit * (g.C / kVBlock) + p_tok / kVBlock) * (int64_t)(D * BITS) +
+            (2 * lane + u) * KW + wr % KW] = word;
   }
   __syncthreads();  // tile/codes are reused by the caller
 }
@@ -119,21 +144,32 @@ __device__ void value_block(const Geom& g, const uint16_t* src, int64_t unit,
       mx = fmaxf(mx, v);
     }
     const GroupParams p = group_params(mn, mx, BITS);
-    meta32[((unit * (g.C / kVBlock) + pos / kVBlock) * NG + gm) * kVBlock + t] =
+    // entry [block][t / 8][gm][t % 8]
+    meta32[(((unit * (g.C / kVBlock) + pos / kVBlock) * 4 + t / 8) * NG + gm) * 8 + t % 8] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
     for (int c = 0; c < G; ++c)
       codes[t * D + gm * G + c] = (uint8_t)group_code(h2f(row[c]), p, BITS);
   }
   __syncthreads();
-  constexpr int kPer = 32 / BITS;  // tokens per word
-  uint32_t* blk = v_codes + ((unit * (g.C / kVBlock) + pos / kVBlock) * D) * BITS;
-  for (int i = threadIdx.x; i < D * BITS; i += blockDim.x) {
-    const int c = i / BITS, w = i % BITS;
+  // consumer order: lane 16 g + i holds tokens 8g + j; 4 bits: word n is
+  // channel 16n + i, token j at bit 4 (j/2) + 16 (j%2); 2 bits: word m holds
+  // channels 16 (2m + h) + i, token j at bit 8h + 2 (j/2) + 16 (j%2)
+  const int NW = D * BITS / 64;  // words per lane
+  uint32_t* blk = v_codes + (unit * (g.C / kVBlock) + pos / kVBlock) * (int64_t)(D * BITS);
+  for (int x = threadIdx.x; x < 64 * NW; x += blockDim.x) {
+    const int lane = x / NW, w = x % NW;
+    const int gg = lane / 16, i = lane % 16;
     uint32_t word = 0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      word |= (uint32_t)codes[(w * kPer + k) * D + c] << (k * BITS);
-    blk[i] = word;
+    for (int h = 0; h < 4 / BITS; ++h) {
+      const int c = 16 * (w * (4 / BITS) + h) + i;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int bit = 8 * h + BITS * (j / 2) + 16 * (j % 2);
+        word |= (uint32_t)codes[(8 * gg + j) * D + c] << bit;
+      }
+    }
+    blk[x] = word;
   }
   __syncthreads();
 }

@@ -41,7 +41,7 @@ def assert_cache_equal(cache: kvq.Cache, oc: oracle.Cache, lens=None, what=""):
     for b, n in enumerate(np.asarray(lens).tolist()):
         lq = oracle.packed_len(n, g.residual)
         sl = {
-            "k_codes": (slice(b, b + 1), slice(None), slice(0, lq)),
+            "k_codes": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
             "k_meta": (slice(b, b + 1), slice(None), slice(0, lq // g.group)),
             "v_codes": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
             "v_meta": (slice(b, b + 1), slice(None), slice(0, lq // 32)),

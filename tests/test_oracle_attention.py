@@ -120,10 +120,9 @@ def test_cache_reconstructs_inputs(orc):
     kk, vv = orc.cache_kv(g, cache, n)
     np.testing.assert_array_equal(kk[:, :, lq:], k[:, :, lq:].astype(np.float64))
     np.testing.assert_array_equal(vv[:, :, lq:], v[:, :, lq:].astype(np.float64))
-    kscale = cache.k_meta[..., 0].view(np.float16).astype(np.float64)  # [B][H][C/G][D]
-    vscale = cache.v_meta[..., 0].view(np.float16).astype(np.float64)  # [B][H][C/32][D/G][32]
-    vscale = vscale.transpose(0, 1, 2, 4, 3).reshape(vscale.shape[0], vscale.shape[1], -1,
-                                                      vscale.shape[3])      # [B][H][C][D/G]
+    _, _, k_sm, v_sm = orc.unpack(g, cache)
+    kscale = k_sm[..., 0].view(np.float16).astype(np.float64)  # [B][H][C/G][D]
+    vscale = v_sm[..., 0].view(np.float16).astype(np.float64)  # [B][H][C][D/G]
     kbound = np.repeat(kscale[:, :, :lq // 32], 32, axis=2) * 0.5 * (1 + 1e-2)
     vbound = np.repeat(vscale[:, :, :lq], 32, axis=3) * 0.5 * (1 + 1e-2)
     kerr = np.abs(kk[:, :, :lq] - k[:, :, :lq].astype(np.float64))
@@ -202,7 +201,7 @@ def test_appends_equal_bulk_quantization(orc, bK, bV, G, R):
             ref = orc.Cache(gb)
             orc.prefill(gb, ref, k[b:b + 1], v[b:b + 1], n)
             lq = orc.packed_len(n, R)
-            np.testing.assert_array_equal(inc.k_codes[b, :, :lq], ref.k_codes[0, :, :lq])
+            np.testing.assert_array_equal(inc.k_codes[b, :, :lq // 32], ref.k_codes[0, :, :lq // 32])
             np.testing.assert_array_equal(inc.k_meta[b, :, :lq // G], ref.k_meta[0, :, :lq // G])
             np.testing.assert_array_equal(inc.v_codes[b, :, :lq // 32], ref.v_codes[0, :, :lq // 32])
             np.testing.assert_array_equal(inc.v_meta[b, :, :lq // 32], ref.v_meta[0, :, :lq // 32])

@@ -199,8 +199,8 @@ def _golden_layout():
         for line in f:
             if not line.strip() or line.startswith("#"):
                 continue
-            t, bits, idx, word, hexv = [p.strip() for p in line.split("|")]
-            rows.append((t, int(bits), int(idx), int(word), int(hexv, 16)))
+            t, bits, idx, hexv = [p.strip() for p in line.split("|")]
+            rows.append((t, int(bits), int(idx), int(hexv, 16)))
     return rows
 
 
@@ -217,26 +217,27 @@ def _pattern_cache(orc, bits):
 
 
 @pytest.mark.parametrize("row", _golden_layout(),
-                         ids=lambda r: "%s%d_%d_%d" % r[:4])
+                         ids=lambda r: "%s%d_%d" % r[:3])
 def test_layout_worked_examples(orc, row):
-    tensor, bits, idx, word, expect = row
+    tensor, bits, idx, expect = row
     cache = _pattern_cache(orc, bits)
     if tensor == "k":
-        got = int(cache.k_codes[0, 0, idx, word])
-        assert np.all(cache.k_meta[0, 0, 0, :, 0] == 0x3C00)
-        assert np.all(cache.k_meta[0, 0, 0, :, 1] == 0)
+        got = int(cache.k_codes[0, 0, 0].reshape(-1)[idx])
+        assert np.all(cache.k_meta[0, 0, 0, ..., 0] == 0x3C00)
+        assert np.all(cache.k_meta[0, 0, 0, ..., 1] == 0)
     else:
-        got = int(cache.v_codes[0, 0, 0, idx, word])
-        assert np.all(cache.v_meta[0, 0, 0, :, :, 0] == 0x3C00)
+        got = int(cache.v_codes[0, 0, 0].reshape(-1)[idx])
+        assert np.all(cache.v_meta[0, 0, 0, ..., 0] == 0x3C00)
     assert got == expect, hex(got)
 
 
 def test_key_row_is_a_bq2_0_code_array(orc):
-    """At D = 64 and 2 bits, a packed key row's 16 bytes are the qs[] of a BQ2_0
-    block: byte i holds codes 4i..4i+3 with the first in the lowest two bits
-    (KV1 model card, "Quantization Format: KV1.cpp BQ2_0").  The codes come
-    from the group quantizer applied to each channel on its own, so the packer
-    is checked against the page's byte order, not against itself."""
+    """At D = 64 and 2 bits, the four slice words of a key row, in slice order,
+    are the 16 bytes qs[] of a BQ2_0 block: byte i holds codes 4i..4i+3 with the
+    first in the lowest two bits (KV1 model card, "Quantization Format: KV1.cpp
+    BQ2_0").  The codes come from the group quantizer applied to each channel
+    on its own, so the packer is checked against the page's byte order, not
+    against itself."""
     g = orc.Geom(1, 1, 1, 64, 2, 2, 32, 32, 32)
     cache = orc.Cache(g)
     rng = np.random.default_rng(11)
@@ -248,4 +249,84 @@ def test_key_row_is_a_bq2_0_code_array(orc):
         q = per_channel[t].astype(np.int64)
         qs = bytes(int(q[4 * i] | q[4 * i + 1] << 2 | q[4 * i + 2] << 4 | q[4 * i + 3] << 6)
                    for i in range(16))
-        assert cache.k_codes[0, 0, t].tobytes() == qs
+        u, i = (t // 4) % 2, 4 * (t // 8) + t % 4      # key row i of half u
+        row = np.array([cache.k_codes[0, 0, 0, 16 * gg + i, u, 0] for gg in range(4)],
+                       np.uint32)
+        assert row.tobytes() == qs
+
+
+def _spec_pack(g, kc, vc, ksm, vsm):
+    """The version-2 packed arrays of block-aligned natural codes and (scale,
+    min) pairs, written straight from the layout statement (per-element loops,
+    independent of the oracle's C code).  kc, vc [C][D]; ksm [C/G][D][2];
+    vsm [C][D/G][2]."""
+    C, D, G, bK, bV = g.capacity, g.head_dim, g.group, g.k_bits, g.v_bits
+    KW, NW = D * bK // 128, D * bV // 64
+    kw = np.zeros((C // 32, 64, 2, KW), np.uint64)
+    vw = np.zeros((C // 32, 64, NW), np.uint64)
+    km = np.zeros((C // G, D // 8, 8, 2), np.uint16)
+    vm = np.zeros((C // 32, 4, D // G, 8, 2), np.uint16)
+    for t in range(C):
+        k, tau = divmod(t, 32)
+        u, i_k = (tau // 4) % 2, 4 * (tau // 8) + tau % 4
+        gv, j = divmod(tau, 8)
+        for c in range(D):
+            gk, cs = divmod(c, D // 4)
+            kw[k, 16 * gk + i_k, u, cs * bK // 32] |= int(kc[t, c]) << (cs * bK % 32)
+            n, i_v = divmod(c, 16)
+            if bV == 4:
+                vw[k, 16 * gv + i_v, n] |= int(vc[t, c]) << (4 * (j // 2) + 16 * (j % 2))
+            else:
+                bit = 8 * (n % 2) + 2 * (j // 2) + 16 * (j % 2)
+                vw[k, 16 * gv + i_v, n // 2] |= int(vc[t, c]) << bit
+        for gm in range(D // G):
+            vm[k, gv, gm, j] = vsm[t, gm]
+    kcs = D // 32
+    for r in range(D // 8):
+        gk, kcc = divmod(r, kcs)
+        base, off = ((16 * (kcc // 2) + 4 * (kcc % 2), 8) if bK == 2 else (8 * kcc, 4))
+        for e in range(8):
+            km[:, r, e] = ksm[:, gk * (D // 4) + base + e // 2 + off * (e % 2)]
+    return kw.astype(np.uint32), vw.astype(np.uint32), km, vm
+
+
+@pytest.mark.parametrize("D,bK,bV,G", [(64, 2, 2, 32), (64, 4, 4, 64), (128, 2, 4, 32),
+                                       (128, 4, 2, 128), (128, 2, 2, 64)])
+def test_layout_matches_its_statement(orc, D, bK, bV, G):
+    """The oracle's packed arrays equal the layout statement applied to codes
+    and (scale, min) pairs produced group by group by the quantizer (pinned
+    above): a wrong index anywhere in the packer (slice, half, row order,
+    nibble/bit position, meta order) fails here."""
+    C = 128
+    g = orc.Geom(1, 1, 1, D, bK, bV, G, C, C)
+    cache = orc.Cache(g)
+    rng = np.random.default_rng(D + 7 * bK + 3 * bV + G)
+    x = (rng.standard_normal((1, 1, C, D)) * rng.lognormal(0, 1, (1, 1, 1, D))).astype(np.float16)
+    y = rng.standard_normal((1, 1, C, D)).astype(np.float16)
+    orc.quantize_keys(g, cache, x, 0)
+    orc.quantize_values(g, cache, y, 0)
+    kc = np.zeros((C, D), np.uint8)
+    vc = np.zeros((C, D), np.uint8)
+    ksm = np.zeros((C // G, D, 2), np.uint16)
+    vsm = np.zeros((C, D // G, 2), np.uint16)
+    for q in range(C // G):
+        for c in range(D):
+            s, m, codes = orc.quantize_group(np.ascontiguousarray(x[0, 0, q * G:(q + 1) * G, c]), bK)
+            ksm[q, c] = (s, m)
+            kc[q * G:(q + 1) * G, c] = codes
+    for t in range(C):
+        for gm in range(D // G):
+            s, m, codes = orc.quantize_group(np.ascontiguousarray(y[0, 0, t, gm * G:(gm + 1) * G]), bV)
+            vsm[t, gm] = (s, m)
+            vc[t, gm * G:(gm + 1) * G] = codes
+    kw, vw, km, vm = _spec_pack(g, kc, vc, ksm, vsm)
+    np.testing.assert_array_equal(cache.k_codes[0, 0], kw)
+    np.testing.assert_array_equal(cache.v_codes[0, 0], vw)
+    np.testing.assert_array_equal(cache.k_meta[0, 0], km)
+    np.testing.assert_array_equal(cache.v_meta[0, 0], vm)
+    # and the natural-order reader used by other tests inverts it
+    k_code, v_code, k_sm, v_sm = orc.unpack(g, cache)
+    np.testing.assert_array_equal(k_code[0, 0], kc)
+    np.testing.assert_array_equal(v_code[0, 0], vc)
+    np.testing.assert_array_equal(k_sm[0, 0], ksm)
+    np.testing.assert_array_equal(v_sm[0, 0], vsm)
