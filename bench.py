@@ -92,7 +92,7 @@ def cpu_baseline(w, target_seconds: float):
     scale = 1.0 / math.sqrt(w.head_dim)
     steps, nbytes, t_total = 0, 0.0, 0.0
     lens = np.full(bs, n0, np.int32)
-    while t_total < target_seconds and steps < 64:
+    while t_total < target_seconds and steps < 256:
         kn, vn, q = synth.step_token(w, steps, batch=bs)
         t0 = time.perf_counter()
         oracle.append(og, oc, kn, vn, lens)
