@@ -811,18 +811,22 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
 // One workgroup per (KV head, sequence): merges the partials of the unit and
 // writes its GQ outputs:
 //   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
-// The unit's partials are contiguous (indices w + u for consecutive waves w),
-// so they stream with independent vector loads.
+// The unit's partials are contiguous (indices w + u for consecutive waves w).
+// Each thread owns one float4 of the output and a 1/P share of the partials
+// and merges them as a stream (running max, rescale when it grows), so the
+// (m, l, o) loads of a partial do not wait for any reduction; the P shares are
+// then merged through LDS.  Empty partials (m = -inf) carry weight 0.
 template <int D, int GQ>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeLaunch L) {
   constexpr int DP = D + kPartPad;
-  constexpr int SB = 128;  // partials weighted per pass
-  constexpr int NO = GQ * D / 4;  // float4 outputs of the unit
-  static_assert(kThreads % GQ == 0, "head of a thread must stay fixed");
+  constexpr int NO = GQ * D / 4;                          // float4 outputs of the unit
+  constexpr int P = NO >= kThreads ? 1 : kThreads / NO;   // partial shares per output
+  constexpr int OPT = NO >= kThreads ? NO / kThreads : 1;  // outputs per thread
+  constexpr int U = 4;                                     // partials in flight per thread
+  static_assert(NO % kThreads == 0 || kThreads % NO == 0, "outputs tile the workgroup");
   __shared__ int red[2 * kThreads / 64];
-  __shared__ float hred[kThreads];
-  __shared__ float mh[GQ], lh[GQ];
-  __shared__ float wts[SB * GQ];
+  __shared__ float4 s_o[kThreads];
+  __shared__ float2 s_ml[kThreads];
   const Geom& g = L.g;
   const int hkv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t out0 = ((int64_t)b * g.Hq + hkv * GQ) * D;
@@ -866,95 +870,70 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeLaunch L
   const int w_first = xu / cpw, w_last = (xu + sw.w - 1) / cpw;
   const int S = w_last - w_first + 1;
   const float* base = L.ws + (int64_t)(w_first + b * g.Hkv + hkv) * GQ * DP;
-  const int h_t = tid % GQ;  // the head this thread's (s, h) items have
+  const int share = (P > 1) ? tid / NO : 0;
 
-  // pass 1: per-head maximum
-  float m = kNegInf;
-  for (int i = tid; i < S * GQ; i += kThreads) m = fmaxf(m, base[(int64_t)i * DP + D]);
-  hred[tid] = m;
-  __syncthreads();
-  if (tid < GQ) {
-    float mm = kNegInf;
-    for (int j = tid; j < kThreads; j += GQ) mm = fmaxf(mm, hred[j]);
-    mh[tid] = mm;
-  }
-  __syncthreads();
-  // pass 2: weights per block of partials, weighted sums (each thread owns
-  // OPT float4 outputs: item t = tid + j * kThreads -> head t / (D/4))
-  constexpr int OPT = (NO + kThreads - 1) / kThreads;
-  float lsum = 0.0f;
-  float4 acc[OPT];
-#pragma unroll
-  for (int j = 0; j < OPT; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += SB) {
-    const int sn = min(SB, S - s0);
-    for (int i = tid; i < SB * GQ; i += kThreads) {
-      float wt = 0.0f;
-      if (i < sn * GQ) {
-        const float* pr = base + ((int64_t)(s0 * GQ + i)) * DP;
-        const float mw = pr[D];
-        if (mw != kNegInf) {
-          wt = exp2f(mw - mh[h_t]);
-          lsum += pr[D + 1] * wt;
-        }
-      }
-      wts[i] = wt;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int t = tid + j * kThreads;
-      if (t < NO) {
-        const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
-        const float* pr = base + (int64_t)s0 * GQ * DP + oh * DP + oc;
-        float4 a = acc[j];
-        int s = 0;
-        for (; s + 4 <= sn; s += 4) {
-          float4 v[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            v[k] = *reinterpret_cast<const float4*>(pr + (int64_t)(s + k) * GQ * DP);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float wt = wts[(s + k) * GQ + oh];
-            a.x += v[k].x * wt;
-            a.y += v[k].y * wt;
-            a.z += v[k].z * wt;
-            a.w += v[k].w * wt;
-          }
-        }
-        for (; s < sn; ++s) {
-          const float4 v = *reinterpret_cast<const float4*>(pr + (int64_t)s * GQ * DP);
-          const float wt = wts[s * GQ + oh];
-          a.x += v.x * wt;
-          a.y += v.y * wt;
-          a.z += v.z * wt;
-          a.w += v.w * wt;
-        }
-        acc[j] = a;
-      }
-    }
-    __syncthreads();
-  }
-  hred[tid] = lsum;
-  __syncthreads();
-  if (tid < GQ) {
-    float ls = 0.0f;
-    for (int j = tid; j < kThreads; j += GQ) ls += hred[j];
-    lh[tid] = ls;
-  }
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < OPT; ++j) {
-    const int t = tid + j * kThreads;
-    if (t < NO) {
-      const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
-      const float inv = 1.0f / lh[oh];
+    const int t = (P > 1) ? tid % NO : tid + j * kThreads;
+    const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
+    const float* pr = base + oh * DP;
+    float M = kNegInf, Ls = 0.0f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = share; s0 < S; s0 += U * P) {
+      float m[U], l[U];
+      float4 o[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        // a partial past the end re-reads this thread's first one with weight 0
+        const int sk = s0 + k * P;
+        const float* q = pr + (int64_t)(sk < S ? sk : share) * GQ * DP;
+        m[k] = q[D];
+        l[k] = q[D + 1];
+        o[k] = *reinterpret_cast<const float4*>(q + oc);
+        if (sk >= S) m[k] = kNegInf;
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if (m[k] == kNegInf) continue;
+        const float Mn = fmaxf(M, m[k]);
+        const float a = exp2_hw(M - Mn);  // 0 while M is -inf
+        const float c = exp2_hw(m[k] - Mn);
+        M = Mn;
+        Ls = Ls * a + l[k] * c;
+        O.x = O.x * a + o[k].x * c;
+        O.y = O.y * a + o[k].y * c;
+        O.z = O.z * a + o[k].z * c;
+        O.w = O.w * a + o[k].w * c;
+      }
+    }
+    if constexpr (P > 1) {
+      s_o[tid] = O;
+      s_ml[tid] = make_float2(M, Ls);
+      __syncthreads();
+      if (share == 0) {
+#pragma unroll
+        for (int q = 1; q < P; ++q) {
+          const float2 ml = s_ml[tid + q * NO];
+          if (ml.x == kNegInf) continue;
+          const float4 oq = s_o[tid + q * NO];
+          const float Mn = fmaxf(M, ml.x);
+          const float a = exp2_hw(M - Mn), c = exp2_hw(ml.x - Mn);
+          M = Mn;
+          Ls = Ls * a + ml.y * c;
+          O.x = O.x * a + oq.x * c;
+          O.y = O.y * a + oq.y * c;
+          O.z = O.z * a + oq.z * c;
+          O.w = O.w * a + oq.w * c;
+        }
+      }
+    }
+    if (share == 0) {
+      const float inv = 1.0f / Ls;
       const int64_t o = out0 + oh * D + oc;
-      L.out[o + 0] = f2h(acc[j].x * inv);
-      L.out[o + 1] = f2h(acc[j].y * inv);
-      L.out[o + 2] = f2h(acc[j].z * inv);
-      L.out[o + 3] = f2h(acc[j].w * inv);
+      L.out[o + 0] = f2h(O.x * inv);
+      L.out[o + 1] = f2h(O.y * inv);
+      L.out[o + 2] = f2h(O.z * inv);
+      L.out[o + 3] = f2h(O.w * inv);
     }
   }
 }
