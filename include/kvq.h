@@ -58,7 +58,7 @@
  * over the dequantized values gives the exact low-bit outputs).
  *
  * ---------------------------------------------------------------------------
- * PACKED LAYOUT  (KVQ_LAYOUT_VERSION 2)
+ * PACKED LAYOUT  (KVQ_LAYOUT_VERSION 3)
  * ---------------------------------------------------------------------------
  * Shapes use: B = batch, Hkv = KV heads, D = head_dim, G = group, R = residual,
  * C = capacity (tokens per sequence), bK / bV = key / value bits.
@@ -102,12 +102,16 @@
  *   v_meta   uint16 [B][Hkv][C/32][4][D/G][8][2]  fp16 (scale, min) of token
  *            32k + 8g + j and channel group gamma = channels
  *            [gamma*G, gamma*G + G) at entry [k][g][gamma][j].
- *   k_res,   uint16 [B][Hkv][R][D]                fp16 residual window; position
- *   v_res                                         p lives in slot p % R.
+ *   k_res    uint16 [B][Hkv][R][D]     fp16 residual keys; position p lives
+ *            in slot p % R, one row of D channels per slot.
+ *   v_res    uint16 [B][Hkv][R/32][D/16][64][8]  fp16 residual values in the
+ *            value consumer order: entry [k][n][l][j] (l = 16g + i) is slot
+ *            32k + 8g + j, channel 16n + i; position p lives in slot p % R.
  *
- * Version 1 (token-major key rows, channel-major value blocks) is retired:
- * its per-lane addresses were scattered, and the decode kernel's loads of it
- * took about 1.2x as long as contiguous ones.
+ * Earlier versions are retired: version 1 (token-major key rows,
+ * channel-major value blocks) had scattered per-lane addresses and its loads
+ * took about 1.2x as long as contiguous ones; version 2 kept v_res in token
+ * rows, which the decode kernel had to transpose through LDS.
  *
  * Constraints (checked, KVQ_ERR_GEOM / KVQ_ERR_BITS otherwise):
  *   batch >= 1; n_kv_heads >= 1; n_q_heads % n_kv_heads == 0 and
@@ -148,7 +152,7 @@ extern "C" {
 #endif
 
 #define KVQ_ABI_VERSION 1
-#define KVQ_LAYOUT_VERSION 2
+#define KVQ_LAYOUT_VERSION 3
 #define KVQ_VBLOCK 32 /* tokens per v_codes block */
 
 enum {

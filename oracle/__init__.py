@@ -66,6 +66,8 @@ def lib():
         L.orc_cache_kv.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 6 + [i64, P, P]
         L.orc_decode_attn.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 8 + [f64, P]
         L.orc_unpack.argtypes = [ctypes.c_int] * 6 + [i64] + [P] * 8
+        L.orc_residual_store.argtypes = [ctypes.c_int] * 4 + [P, P, i64, i64, P, P]
+        L.orc_value_res_rows.argtypes = [ctypes.c_int] * 4 + [P, P]
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -141,7 +143,7 @@ class Cache:
         self.k_meta = np.zeros((B, H, C // g.group, D // 8, 8, 2), np.uint16)
         self.v_meta = np.zeros((B, H, blocks, 4, D // g.group, 8, 2), np.uint16)
         self.k_res = np.zeros((B, H, g.residual, D), np.uint16)
-        self.v_res = np.zeros((B, H, g.residual, D), np.uint16)
+        self.v_res = np.zeros((B, H, g.residual // 32, D // 16, 64, 8), np.uint16)
 
     def arrays(self):
         return (self.k_codes, self.v_codes, self.k_meta, self.v_meta,
@@ -177,9 +179,21 @@ def prefill(g: Geom, cache: Cache, k: np.ndarray, v: np.ndarray, n: int) -> None
     if lq > 0:
         quantize_keys(g, cache, np.ascontiguousarray(k[:, :, :lq]), 0)
         quantize_values(g, cache, np.ascontiguousarray(v[:, :, :lq]), 0)
-    for t in range(lq, n):
-        cache.k_res[:, :, t % g.residual] = k[:, :, t]
-        cache.v_res[:, :, t % g.residual] = v[:, :, t]
+    if n > lq:
+        kr = np.ascontiguousarray(k[:, :, lq:n])
+        vr = np.ascontiguousarray(v[:, :, lq:n])
+        lib().orc_residual_store(g.batch, g.n_kv_heads, g.head_dim, g.residual, _p(kr),
+                                 _p(vr), lq, n - lq, _p(cache.k_res), _p(cache.v_res))
+
+
+def value_res_rows(g: Geom, v_res: np.ndarray) -> np.ndarray:
+    """A v_res array (any array of the cache's v_res layout and batch) in
+    natural order [B][Hkv][R][D] (tests only)."""
+    B = v_res.shape[0]
+    v_res = np.ascontiguousarray(v_res).view(np.uint16)
+    out = np.zeros((B, g.n_kv_heads, g.residual, g.head_dim), np.uint16)
+    lib().orc_value_res_rows(B, g.n_kv_heads, g.head_dim, g.residual, _p(v_res), _p(out))
+    return out
 
 
 def append(g: Geom, cache: Cache, k_new: np.ndarray, v_new: np.ndarray,

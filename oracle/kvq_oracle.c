@@ -177,7 +177,7 @@ void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Packed layout, version 2 (restated from its specification)               */
+/* Packed layout, version 3 (restated from its specification)               */
 /*                                                                           */
 /* Packed tokens live in blocks of 32 positions; tau = t % 32.  Inside a     */
 /* block, words follow a 64-lane consumer order, lane l = 16 g + i.          */
@@ -194,7 +194,9 @@ void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
 /*          8g + j at bit 8h + 2(j/2) + 16(j%2).                             */
 /* v_meta   u16 [B][Hkv][C/32][4][D/G][8][2]: entry [k][g][gamma][j] is      */
 /*          token 32k + 8g + j, channel group gamma.                         */
-/* k_res, v_res u16 [B][Hkv][R][D]: position p in slot p % R.               */
+/* k_res    u16 [B][Hkv][R][D]: position p in slot p % R, one row per slot. */
+/* v_res    u16 [B][Hkv][R/32][D/16][64][8]: entry [k][n][16g + i][j] is     */
+/*          slot 32k + 8g + j, channel 16n + i; position p in slot p % R.   */
 /* ------------------------------------------------------------------------ */
 
 static void put_field(uint32_t *word, int bit, int bits, uint32_t code) {
@@ -285,6 +287,14 @@ static int64_t value_meta_index(int64_t unit, int64_t C, int D, int G,
   int64_t k = t / 32;
   int tau = (int)(t % 32);
   return ((unit * (C / 32) + k) * 4 + tau / 8) * (D / G) * 8 + gm * 8 + tau % 8;
+}
+
+/* Index inside one unit's v_res of slot s, channel c. */
+static int64_t value_res_index(int D, int s, int c) {
+  int k = s / 32, tau = s % 32;
+  int g = tau / 8, j = tau % 8;
+  int n = c / 16, i = c % 16;
+  return (((int64_t)k * (D / 16) + n) * 64 + 16 * g + i) * 8 + j;
 }
 
 /* Quantizes key groups of one unit from a source of token rows src[t*D + c]
@@ -396,11 +406,15 @@ void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int R, int64_t C,
     if (n > 0 && n % R == 0) {
       /* slots 0..R-1 hold positions n-R .. n-1 in order */
       quantize_keys_unit(kr, n - R, R, D, bK, G, C, u, k_codes, k_meta);
-      quantize_values_unit(vr, n - R, R, D, bV, G, C, u, v_codes, v_meta);
+      uint16_t *rows = (uint16_t *)malloc((size_t)R * D * sizeof(uint16_t));
+      for (int s = 0; s < R; ++s)
+        for (int c = 0; c < D; ++c) rows[s * D + c] = vr[value_res_index(D, s, c)];
+      quantize_values_unit(rows, n - R, R, D, bV, G, C, u, v_codes, v_meta);
+      free(rows);
     }
-    int64_t slot = n % R;
-    memcpy(kr + slot * D, k_new + u * D, (size_t)D * sizeof(uint16_t));
-    memcpy(vr + slot * D, v_new + u * D, (size_t)D * sizeof(uint16_t));
+    int slot = (int)(n % R);
+    memcpy(kr + (int64_t)slot * D, k_new + u * D, (size_t)D * sizeof(uint16_t));
+    for (int c = 0; c < D; ++c) vr[value_res_index(D, slot, c)] = v_new[u * D + c];
   }
 }
 
@@ -451,7 +465,7 @@ void orc_cache_kv(int B, int Hkv, int D, int bK, int bV, int G, int R,
           vv = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
         } else {
           kv = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
-          vv = orc_half_to_float(v_res[(u * R + t % R) * D + c]);
+          vv = orc_half_to_float(v_res[u * R * D + value_res_index(D, (int)(t % R), c)]);
         }
         out_k[(u * n + t) * D + c] = kv;
         out_v[(u * n + t) * D + c] = vv;
@@ -499,7 +513,8 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
           vv[t * D + c] = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
         } else {
           kk[t * D + c] = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
-          vv[t * D + c] = orc_half_to_float(v_res[(u * R + t % R) * D + c]);
+          vv[t * D + c] =
+              orc_half_to_float(v_res[u * R * D + value_res_index(D, (int)(t % R), c)]);
         }
       }
     }
@@ -531,6 +546,32 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
     free(vv);
     free(s);
   }
+}
+
+/* Writes positions [pos0, pos0 + n_tok) of fp16 token rows k, v
+ * [B*Hkv][n_tok][D] into their residual slots p % R. */
+void orc_residual_store(int B, int Hkv, int D, int R, const uint16_t *k,
+                        const uint16_t *v, int64_t pos0, int64_t n_tok,
+                        uint16_t *k_res, uint16_t *v_res) {
+  int64_t units = (int64_t)B * Hkv;
+  for (int64_t u = 0; u < units; ++u)
+    for (int64_t t = 0; t < n_tok; ++t) {
+      int slot = (int)((pos0 + t) % R);
+      for (int c = 0; c < D; ++c) {
+        k_res[(u * R + slot) * D + c] = k[(u * n_tok + t) * D + c];
+        v_res[u * R * D + value_res_index(D, slot, c)] = v[(u * n_tok + t) * D + c];
+      }
+    }
+}
+
+/* The residual window in natural order, for tests: out [B*Hkv][R][D]. */
+void orc_value_res_rows(int B, int Hkv, int D, int R, const uint16_t *v_res,
+                        uint16_t *out) {
+  int64_t units = (int64_t)B * Hkv;
+  for (int64_t u = 0; u < units; ++u)
+    for (int s = 0; s < R; ++s)
+      for (int c = 0; c < D; ++c)
+        out[(u * R + s) * D + c] = v_res[u * R * D + value_res_index(D, s, c)];
 }
 
 /* The cache's codes and (scale, min) pairs in natural order, for tests:

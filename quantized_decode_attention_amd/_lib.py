@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 ABI_VERSION = 1
-LAYOUT_VERSION = 2
+LAYOUT_VERSION = 3
 VBLOCK = 32
 
 # status codes (include/kvq.h)
@@ -210,7 +210,8 @@ class Cache:
         self.v_meta = torch.zeros((B, H, blocks, 4, D // g.group, 8, 2),
                                   dtype=torch.int16, **z)
         self.k_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
-        self.v_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
+        self.v_res = torch.zeros((B, H, g.residual // 32, D // 16, 64, 8),
+                                 dtype=torch.float16, **z)
         sizes = kvq_cache_bytes(g)
         for t, s in zip(self.tensors(), sizes):
             assert t.numel() * t.element_size() == s

@@ -22,13 +22,13 @@
 // 32-token chunk; everything per code is a shift and a mask.
 //
 // Work decomposition: a persistent grid of single-wave workgroups, as many
-// as the GPU keeps resident at once.  The packed 32-token chunks of all
-// (sequence, KV head) units form one flat list; every wave takes an equal
+// as the GPU keeps resident at once.  The 32-token chunks of all (sequence,
+// KV head) units (packed chunks, then the fp16 residual window's chunks, each
+// weighted by its bytes) form one flat list; every wave takes an equal
 // contiguous share of it (so any mix of sequence lengths is balanced) and runs
 // an online softmax over it, writing one partial (max, sum, weighted values)
 // per unit its share touches.  The GQA query heads of a KV head share every
-// load.  The combine kernel (one workgroup per unit) attends over the fp16
-// residual window and merges it with the unit's partials:
+// load.  The combine kernel (one workgroup per unit) merges a unit's partials:
 //   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
 // Scores are kept in log2 units (sm_scale * log2 e folded into q).
 #include "kvq_internal.h"
@@ -439,25 +439,24 @@ struct PackedWave {
   }
 
   // Residual chunk: fp16 tokens t0 + [0, 32) of the window (those >= n_tok
-  // masked), keys straight from the window rows, values transposed through
-  // the wave's LDS buffer vbuf [32][D].
+  // masked).  Keys come straight from the window's slot rows; values are
+  // stored in the value consumer order, so tile n's A operand is one 16-byte
+  // load per lane (slots past n_tok are zeroed in registers: their weight is
+  // 0, and the window may hold anything there).
   __device__ __forceinline__ void process_residual(int t0, int n_tok, int R,
                                                    const uint16_t* kres,
-                                                   const uint16_t* vres, uint16_t* vbuf) {
-    // stage values: lane -> token lane/2, half of the channels
-    {
-      const int tk = lane >> 1, t = t0 + tk;
-      constexpr int V4 = D / 16;  // uint4 per half row
-      uint4* dst = reinterpret_cast<uint4*>(vbuf + tk * D + (lane & 1) * (D / 2));
-      if (t < n_tok) {
-        const uint4* src = reinterpret_cast<const uint4*>(vres + (int64_t)(t % R) * D +
-                                                          (lane & 1) * (D / 2));
+                                                   const uint16_t* vres) {
+    // value operands first: their loads overlap the score MFMAs
+    const uint4* vq = reinterpret_cast<const uint4*>(vres) +
+                      (int64_t)((t0 % R) / kChunk) * (D / 16) * 64 + lane;
+    uint4 va[NT];
 #pragma unroll
-        for (int v = 0; v < V4; ++v) dst[v] = src[v];
-      } else {
+    for (int n = 0; n < NT; ++n) va[n] = vq[n * 64];
+    uint32_t vmask[4];
 #pragma unroll
-        for (int v = 0; v < V4; ++v) dst[v] = make_uint4(0u, 0u, 0u, 0u);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 8 * lg + 2 * i;
+      vmask[i] = (t < n_tok ? 0x0000ffffu : 0u) | (t + 1 < n_tok ? 0xffff0000u : 0u);
     }
     // scores: tile u row r = token key_row_token(u, r)
     const float kscale_r = bscale;  // keys are real fp16 values here
@@ -492,24 +491,13 @@ struct PackedWave {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], m1, bh[i], bl[i]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      uint32_t a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo16 = vbuf[(8 * lg + 2 * i) * D + 16 * n + col];
-        const uint32_t hi16 = vbuf[(8 * lg + 2 * i + 1) * D + 16 * n + col];
-        a[i] = lo16 | (hi16 << 16);
-      }
+      const uint32_t a[4] = {va[n].x & vmask[0], va[n].y & vmask[1], va[n].z & vmask[2],
+                             va[n].w & vmask[3]};
       oacc[n] = mfma(a, bh, oacc[n]);
       oacc[n] = mfma(a, bl, oacc[n]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   __device__ __forceinline__ void process(int ch, const R& r) {
@@ -645,9 +633,7 @@ __device__ __forceinline__ void wave_find_seq(const DecodeLaunch& L, int lane, i
 }
 
 template <int D, int BK, int BV, int GQ, int NG>
-constexpr int kWaveSmem = GQ * D * 4 + (Cfg<D, BK, BV, GQ, NG>::kWaveLds > kChunk * D * 2
-                                            ? Cfg<D, BK, BV, GQ, NG>::kWaveLds
-                                            : kChunk * D * 2);
+constexpr int kWaveSmem = GQ * D * 4 + Cfg<D, BK, BV, GQ, NG>::kWaveLds;
 
 // The part of unit (b, hkv) in work range [x0, x1) -> partial p.  xu = first
 // work unit of the unit.
@@ -681,6 +667,21 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
   float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
   char* wl = smem + GQ * D * 4;
 
+  W w;
+  w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
+  w.kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) + unit * (g.C / C::G) * D;
+  w.vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
+  w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
+            unit * (g.C / kVBlock) * NG * kVBlock;
+  w.qfs = qfs;
+  w.qB = reinterpret_cast<uint4*>(wl);
+  w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
+  w.init(lane);
+  // the first chunk's loads go out before the query's, so the two memory
+  // latencies overlap instead of adding up
+  R ra, rb;
+  if (pc0 < pc1) w.load(pc0, ra);
+
   // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
   // that q * 2^-E * scale fits fp16
   const uint16_t* qg = L.q + ((int64_t)b * g.Hq + hkv * GQ) * D;
@@ -706,16 +707,6 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  W w;
-  w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
-  w.kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) + unit * (g.C / C::G) * D;
-  w.vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
-  w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
-            unit * (g.C / kVBlock) * NG * kVBlock;
-  w.qfs = qfs;
-  w.qB = reinterpret_cast<uint4*>(wl);
-  w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
-  w.init(lane);
   int e_mine = 0;
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
@@ -728,9 +719,7 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
     // used (a deeper ring measured no faster).  Prefetches past the last
     // chunk re-load that chunk (always in bounds) instead of being skipped,
     // so no load sits under a branch.
-    R ra, rb;
     const int last = pc1 - 1;
-    w.load(pc0, ra);
     for (int ch = pc0; ch < pc1; ch += 2) {
       w.load(min(ch + 1, last), rb);
       w.process(ch, ra);
@@ -744,10 +733,8 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
     w.enter_residual();
     const uint16_t* kres = L.cache.k_res + unit * g.R * D;
     const uint16_t* vres = L.cache.v_res + unit * g.R * D;
-    uint16_t* vbuf = reinterpret_cast<uint16_t*>(wl);
     const int lq = sw.nq * kChunk;
-    for (int k = rk0; k < rk1; ++k)
-      w.process_residual(lq + k * kChunk, sw.n, g.R, kres, vres, vbuf);
+    for (int k = rk0; k < rk1; ++k) w.process_residual(lq + k * kChunk, sw.n, g.R, kres, vres);
   }
 
   // partial: O (+ value-min term), max, sum of this wave's tokens

@@ -71,6 +71,30 @@ __device__ __forceinline__ int key_meta_entry(int c, int D) {
   return 8 * r + 2 * (s % 4) + half;
 }
 
+// Place of (slot s, channel c) inside one unit's v_res window: entry
+// [s/32][c/16][16 g + c%16][j] with s % 32 = 8 g + j (the value consumer order).
+__device__ __forceinline__ int64_t value_res_index(int D, int s, int c) {
+  const int k = s / 32, tau = s % 32, gg = tau / 8, j = tau % 8;
+  return (((int64_t)k * (D / 16) + c / 16) * 64 + 16 * gg + c % 16) * 8 + j;
+}
+
+// Token rows [32 blk, 32 blk + 32) of a unit's residual value window, read
+// from its consumer order into LDS rows tile[t * D + c].
+__device__ __forceinline__ void load_value_window(uint16_t* tile, const uint16_t* vres,
+                                                  int blk, int D) {
+  const uint4* src = reinterpret_cast<const uint4*>(vres) + (int64_t)blk * (D / 16) * 64;
+  for (int x = threadIdx.x; x < (D / 16) * 64; x += blockDim.x) {
+    const uint4 w = src[x];  // slots 8g + 0..7 of channel 16n + i
+    const int n = x / 64, l = x % 64, gg = l / 16, c = 16 * n + l % 16;
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[(8 * gg + 2 * e) * D + c] = (uint16_t)(ww[e] & 0xffffu);
+      tile[(8 * gg + 2 * e + 1) * D + c] = (uint16_t)(ww[e] >> 16);
+    }
+  }
+}
+
 // Loads n_halves fp16 values (a multiple of 8, 16-byte aligned) into LDS.
 __device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* src,
                                           int n_halves) {
@@ -126,12 +150,17 @@ __device__ void key_group(const Geom& g, const uint16_t* src, int64_t unit,
 
 // One 32-token value block: token rows at `src`, first position `pos` (a
 // multiple of 32).  Per token: D/G groups of G consecutive channels.
+// With window_blk >= 0, src is the unit's residual value window and the block
+// is its 32-slot chunk window_blk; otherwise src holds 32 token rows.
 template <int BITS>
-__device__ void value_block(const Geom& g, const uint16_t* src, int64_t unit,
-                            int32_t pos, uint32_t* v_codes, uint16_t* v_meta,
-                            uint16_t* tile, uint8_t* codes) {
+__device__ void value_block(const Geom& g, const uint16_t* src, int window_blk,
+                            int64_t unit, int32_t pos, uint32_t* v_codes,
+                            uint16_t* v_meta, uint16_t* tile, uint8_t* codes) {
   const int G = g.G, D = g.D, NG = D / G;
-  load_tile(tile, src, kVBlock * D);
+  if (window_blk >= 0)
+    load_value_window(tile, src, window_blk, D);
+  else
+    load_tile(tile, src, kVBlock * D);
   __syncthreads();
   uint32_t* meta32 = reinterpret_cast<uint32_t*>(v_meta);
   for (int i = threadIdx.x; i < kVBlock * NG; i += blockDim.x) {
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(
   __shared__ uint8_t codes[kVBlock * kMaxD];
   const int64_t unit = (int64_t)blockIdx.z * g.Hkv + blockIdx.y;
   const int blk = blockIdx.x;
-  value_block<BITS>(g, src + unit * src_unit_stride + (int64_t)blk * kVBlock * g.D,
+  value_block<BITS>(g, src + unit * src_unit_stride + (int64_t)blk * kVBlock * g.D, -1,
                     unit, pos0 + blk * kVBlock, v_codes, v_meta, tile, codes);
 }
 
@@ -215,7 +244,15 @@ __global__ __launch_bounds__(kThreads) void residual_copy_kernel(
     const int64_t s = unit * src_unit_stride / 8 + t * vecs_per_row + e;
     const int64_t d = (unit * g.R + slot) * vecs_per_row + e;
     reinterpret_cast<uint4*>(k_res)[d] = reinterpret_cast<const uint4*>(k)[s];
-    reinterpret_cast<uint4*>(v_res)[d] = reinterpret_cast<const uint4*>(v)[s];
+    // values: channels 8e .. 8e+7 of the slot go to their window places
+    const uint4 x = reinterpret_cast<const uint4*>(v)[s];
+    const uint32_t xx[4] = {x.x, x.y, x.z, x.w};
+    uint16_t* vu = v_res + unit * g.R * g.D;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const uint16_t val = (uint16_t)((h & 1) ? (xx[h / 2] >> 16) : (xx[h / 2] & 0xffffu));
+      vu[value_res_index(g.D, (int)slot, (int)(8 * e + h))] = val;
+    }
   }
 }
 
@@ -241,14 +278,14 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
       key_group<BK>(g, kr + (int64_t)j * g.G * g.D, unit, n - g.R + j * g.G,
                     k_codes, k_meta, tile, codes);
     for (int blk = 0; blk < g.R / kVBlock; ++blk)
-      value_block<BV>(g, vr + (int64_t)blk * kVBlock * g.D, unit,
-                      n - g.R + blk * kVBlock, v_codes, v_meta, tile, codes);
+      value_block<BV>(g, vr, blk, unit, n - g.R + blk * kVBlock, v_codes, v_meta, tile,
+                      codes);
     // every read of the window happened before the barriers in the helpers
   }
-  const int64_t slot = n % g.R;
+  const int slot = n % g.R;
   for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
-    kr[slot * g.D + c] = k_new[unit * g.D + c];
-    vr[slot * g.D + c] = v_new[unit * g.D + c];
+    kr[(int64_t)slot * g.D + c] = k_new[unit * g.D + c];
+    vr[value_res_index(g.D, slot, c)] = v_new[unit * g.D + c];
   }
 }
 

@@ -51,10 +51,13 @@ def assert_cache_equal(cache: kvq.Cache, oc: oracle.Cache, lens=None, what=""):
             gg = got[name][idx]
             bad = np.argwhere(gg != o)
             assert bad.size == 0, f"{what} seq {b} {name}: {len(bad)} mismatches, first {bad[0]}"
+        res = {"k_res": (got["k_res"], oc.k_res),
+               "v_res": (oracle.value_res_rows(g, got["v_res"]),
+                         oracle.value_res_rows(g, oc.v_res))}
         for t in range(lq, n):
             s = t % g.residual
-            for name in ("k_res", "v_res"):
-                assert np.array_equal(got[name][b, :, s], getattr(oc, name)[b, :, s]), \
+            for name, (ga, oa) in res.items():
+                assert np.array_equal(ga[b, :, s], oa[b, :, s]), \
                     f"{what} seq {b} {name} slot {s}"
 
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 def test_versions_and_status_strings():
     assert kvq.kvq_abi_version() == kvq.ABI_VERSION == 1
-    assert kvq.kvq_layout_version() == kvq.LAYOUT_VERSION == 2
+    assert kvq.kvq_layout_version() == kvq.LAYOUT_VERSION == 3
     for s in range(-8, 1):
         assert kvq.status_str(s) and kvq.status_str(s) != "unknown status"
     assert kvq.status_str(5) == "unknown status"

@@ -205,6 +205,7 @@ def test_appends_equal_bulk_quantization(orc, bK, bV, G, R):
             np.testing.assert_array_equal(inc.k_meta[b, :, :lq // G], ref.k_meta[0, :, :lq // G])
             np.testing.assert_array_equal(inc.v_codes[b, :, :lq // 32], ref.v_codes[0, :, :lq // 32])
             np.testing.assert_array_equal(inc.v_meta[b, :, :lq // 32], ref.v_meta[0, :, :lq // 32])
+            vrows = orc.value_res_rows(g, inc.v_res)
             for t in range(lq, n):
                 np.testing.assert_array_equal(inc.k_res[b, :, t % R], k[b, :, t].view(np.uint16))
-                np.testing.assert_array_equal(inc.v_res[b, :, t % R], v[b, :, t].view(np.uint16))
+                np.testing.assert_array_equal(vrows[b, :, t % R], v[b, :, t].view(np.uint16))

@@ -330,3 +330,27 @@ def test_layout_matches_its_statement(orc, D, bK, bV, G):
     np.testing.assert_array_equal(v_code[0, 0], vc)
     np.testing.assert_array_equal(k_sm[0, 0], ksm)
     np.testing.assert_array_equal(v_sm[0, 0], vsm)
+
+
+@pytest.mark.parametrize("D,R", [(64, 32), (128, 64), (128, 128)])
+def test_value_residual_layout_matches_its_statement(orc, D, R):
+    """Residual values sit where the layout statement puts them: entry
+    [k][n][16g + i][j] of v_res is slot 32k + 8g + j, channel 16n + i (written
+    per element here, independently of the oracle's C code); residual keys
+    stay in slot rows."""
+    g = orc.Geom(1, 2, 1, D, 2, 2, 32, R, 2 * R)
+    cache = orc.Cache(g)
+    rng = np.random.default_rng(D + R)
+    n = R - 3                                   # all residual, slots 0..n-1
+    k = rng.standard_normal((1, 1, n, D)).astype(np.float16)
+    v = rng.standard_normal((1, 1, n, D)).astype(np.float16)
+    orc.prefill(g, cache, k, v, n)
+    vb = v.view(np.uint16)
+    for s in range(n):
+        kk, tau = divmod(s, 32)
+        gg, j = divmod(tau, 8)
+        for c in range(D):
+            nn, i = divmod(c, 16)
+            assert cache.v_res[0, 0, kk, nn, 16 * gg + i, j] == vb[0, 0, s, c]
+    np.testing.assert_array_equal(cache.k_res[0, 0, :n], k[0, 0].view(np.uint16))
+    np.testing.assert_array_equal(orc.value_res_rows(g, cache.v_res)[0, 0, :n], vb[0, 0])
