@@ -156,22 +156,48 @@ constexpr int kKeyOff = BK == 2 ? 8 : 4;
 template <int D, int BK>
 constexpr int kKW = (D / 4) * BK / 32;
 
+// Key codes to A-operand pairs with one AND per pair: an odd pair (VGPR v
+// odd) is masked where it sits, two bits (2-bit fields) or four bits (4-bit)
+// above its even neighbour, so it comes out as code * 4 (or * 16) * 2^-24.
+// The query fragments carry the inverse: q' of an even channel is scaled by
+// kKeyEvenQ and of an odd channel by kKeyOddQ (channel parity = pair parity,
+// the runs start at multiples of 4), and every pair then contributes
+// kKeyAcc * code * q'.  The factors keep q' inside fp16 for any fp16 keys
+// (a 4-bit scale is at most 8734, a 2-bit one is not scaled up).
+template <int BK> constexpr float kKeyEvenQ = BK == 2 ? 1.0f : 4.0f;
+template <int BK> constexpr float kKeyOddQ = 0.25f;
+template <int BK> constexpr int kKeyAccLog2 = BK == 2 ? 0 : 2;
+
+// Value side, likewise: the odd pairs of a value word (VGPR e odd: tokens
+// 8g + 2e, 8g + 2e + 1 with e odd, i.e. score registers q = 2, 3) come out of
+// their mask as code * 16 (4-bit) or * 4 (2-bit) * 2^-24.  Their softmax
+// weights are taken 4x smaller (2^(s - m - 2)) and the even pairs' weights
+// kValEven times larger, so every pair contributes kValEven * p * code * dV.
+// (4 * 8734 and 43669 stay inside fp16.)
+template <int BV> constexpr float kValEven = BV == 4 ? 4.0f : 1.0f;
+template <int BV> constexpr float kValOdd = 0.25f;
+template <int BV> constexpr float kValEvenLog2 = BV == 4 ? 2.0f : 0.0f;
+constexpr float kValOddLog2 = -2.0f;
+
 template <int D, int BK>
 __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
                                             uint32_t (&a)[D / 32][4]) {
   if constexpr (BK == 2) {
+    // field s of a half: (w >> 4 (s/2)) masked at bits 2 (s%2)
 #pragma unroll
     for (int wi = 0; wi < kKW<D, BK>; ++wi)
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int ri = 8 * wi + s;
-        a[ri >> 2][ri & 3] = (w[wi] >> (2 * s)) & 0x00030003u;
+        a[ri >> 2][ri & 3] = (w[wi] >> (4 * (s >> 1))) & ((s & 1) ? 0x000C000Cu : 0x00030003u);
       }
   } else {
+    // field s of a half: (w >> 8 (s/2)) masked at bits 4 (s%2)
 #pragma unroll
     for (int wi = 0; wi < kKW<D, BK>; ++wi)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[wi][s] = (w[wi] >> (4 * s)) & 0x000F000Fu;
+      for (int s = 0; s < 4; ++s)
+        a[wi][s] = (w[wi] >> (8 * (s >> 1))) & ((s & 1) ? 0x00F000F0u : 0x000F000Fu);
   }
 }
 
@@ -256,7 +282,10 @@ struct PackedWave {
   // state
   f4 oacc[NT];
   float m_run, l_run;
-  float bias[NF];
+  float m_even, m_odd;  // m_run less the classes' log2 factors (packed chunks)
+  float l_odd;          // sum of odd-class weights (scaled by kValOdd)
+  float bias[NF];       // value-min term; odd class kept apart in bias_odd
+  float bias_odd[NF];
   uint32_t bq[KP][KC][4];
   float beta_c;
   int cur_group;
@@ -284,9 +313,15 @@ struct PackedWave {
 #pragma unroll
     for (int n = 0; n < NT; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
     m_run = kNegInf;
+    m_even = kNegInf;
+    m_odd = kNegInf;
     l_run = 0.0f;
+    l_odd = 0.0f;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) bias[f] = 0.0f;
+    for (int f = 0; f < NF; ++f) {
+      bias[f] = 0.0f;
+      bias_odd[f] = 0.0f;
+    }
     beta_c = 0.0f;
     cur_group = -1;
   }
@@ -345,12 +380,20 @@ struct PackedWave {
         const uint32_t mA[4] = {r.kmA[i].x, r.kmA[i].y, r.kmA[i].z, r.kmA[i].w};
         const uint32_t mB[4] = {r.kmB[i].x, r.kmB[i].y, r.kmB[i].z, r.kmB[i].w};
         uint32_t hp[4], lp[4];
+        float bodd = 0.0f;  // odd channels (their q' carries kKeyOddQ)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), m1, hp[e], lp[e]);
-          bpart = mul_hi(qA[e], mA[e], bpart);
-          bpart = mul_hi(qBv[e], mB[e], bpart);
+          if (e & 1) {
+            bodd = mul_hi(qA[e], mA[e], bodd);
+            bodd = mul_hi(qBv[e], mB[e], bodd);
+          } else {
+            bpart = mul_hi(qA[e], mA[e], bpart);
+            bpart = mul_hi(qBv[e], mB[e], bpart);
+          }
         }
+        // beta = q . min with the channel factors taken back out
+        bpart = __builtin_fmaf(bodd, 1.0f / kKeyOddQ<BK>, bpart * (1.0f / kKeyEvenQ<BK>));
         qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
         qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
       }
@@ -377,6 +420,9 @@ struct PackedWave {
   // Online softmax over a chunk's scores (exact running max; rescale only
   // when it grows).  Each lane tests its own 8 scores; the cross-lane maximum
   // is only formed on the (rare) path where some lane sees a larger score.
+  // kPacked: weights carry the value classes' factors (q < 2: kValEven,
+  // q >= 2: kValOdd) and their sums are kept per class; otherwise plain.
+  template <bool kPacked>
   __device__ __forceinline__ void softmax(const float (&s)[2][4], float (&p)[2][4]) {
     float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -386,19 +432,60 @@ struct PackedWave {
       const float m_new = fmaxf(m_run, cm);
       const float a = exp2_hw(m_run - m_new);
       m_run = m_new;
+      m_even = m_new - kValEvenLog2<BV>;
+      m_odd = m_new - kValOddLog2;
       l_run *= a;
+      l_odd *= a;
 #pragma unroll
       for (int n = 0; n < NT; ++n) oacc[n] *= a;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) bias[f] *= a;
+      for (int f = 0; f < NF; ++f) {
+        bias[f] *= a;
+        bias_odd[f] *= a;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        p[u][q] = exp2_hw(s[u][q] - m_run);
-        l_run += p[u][q];
+        if constexpr (kPacked) {
+          p[u][q] = exp2_hw(s[u][q] - (q < 2 ? m_even : m_odd));
+          if (q < 2)
+            l_run += p[u][q];
+          else
+            l_odd += p[u][q];
+        } else {
+          p[u][q] = exp2_hw(s[u][q] - m_run);
+          l_run += p[u][q];
+        }
       }
+  }
+
+  // Packed accumulation to real scale (codes were fp16 numbers c * 2^-24,
+  // pairs carry kValEven) with its value-min term added; class sums folded.
+  // Afterwards the state is plain (as the residual path needs).
+  __device__ __forceinline__ void to_real() {
+    // the value-min term is summed over the four lane groups (token subsets)
+    float btot[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const float bt = __builtin_fmaf(bias_odd[f], 1.0f / kValOdd<BV>,
+                                      bias[f] * (1.0f / kValEven<BV>));
+      btot[f] = xor_sum(xor_sum(bt, 16), 32);
+      bias[f] = 0.0f;
+      bias_odd[f] = 0.0f;
+    }
+    constexpr float oscale = 16777216.0f / kValEven<BV>;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float bsum = btot[C::gam(n) / SL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], oscale, bsum);
+    }
+    l_run = __builtin_fmaf(l_odd, 1.0f / kValOdd<BV>, l_run * (1.0f / kValEven<BV>));
+    l_odd = 0.0f;
+    m_even = m_run;
+    m_odd = m_run;
   }
 
   // Switch to the residual window: bring the packed accumulation to real scale
@@ -406,23 +493,15 @@ struct PackedWave {
   // the key-side B fragments to q * 2^-E in natural channel order (element j of
   // lane group g, k-chunk kc = channel 32 kc + 8 g + j), hi or lo part.
   __device__ __forceinline__ void enter_residual() {
-    // the value-min term is summed over the four lane groups (token subsets)
-    float btot[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) btot[f] = xor_sum(xor_sum(bias[f], 16), 32);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float bsum = btot[C::gam(n) / SL];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], 16777216.0f, bsum);
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) bias[f] = 0.0f;
+    to_real();
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg);
       const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg + 4);
-      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      // channel 32 kc + 8 lg + j: parity of j; the key-side factors come out
+      constexpr float ue = 1.0f / kKeyEvenQ<BK>, uo = 1.0f / kKeyOddQ<BK>;
+      const float qv[8] = {qa.x * ue, qa.y * uo, qa.z * ue, qa.w * uo,
+                           qb.x * ue, qb.y * uo, qb.z * ue, qb.w * uo};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t hi, lo;
@@ -486,7 +565,7 @@ struct PackedWave {
       }
     }
     float p[2][4];
-    softmax(s, p);
+    softmax<false>(s, p);
     uint32_t bh[4], bl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -530,30 +609,36 @@ struct PackedWave {
       }
     }
     float p[2][4];
-    softmax(s, p);
+    softmax<true>(s, p);
     // weighted value sum
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // elements 2i (run A) and 2i+1 (run B) = score tile i/2, rows 2(i%2), +1
+        // elements 2i (run A) and 2i+1 (run B) = score tile i/2, rows 2(i%2), +1;
+        // odd i is the odd class
         const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
         split2(mul_lo(pa, r.vmA[f][i]), mul_lo(pb, r.vmB[f][i]), m1, bh[i], bl[i]);
-        bias[f] = mul_hi(pa, r.vmA[f][i], bias[f]);
-        bias[f] = mul_hi(pb, r.vmB[f][i], bias[f]);
+        float& bacc = (i & 1) ? bias_odd[f] : bias[f];
+        bacc = mul_hi(pa, r.vmA[f][i], bacc);
+        bacc = mul_hi(pb, r.vmB[f][i], bacc);
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         if (C::gam(n) / SL != f) continue;  // compile-time
         uint32_t a[4];
         if constexpr (BV == 4) {
+          // pair e: (w >> 8 (e/2)) masked at bits 4 (e%2)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = (r.vw[n] >> (4 * e)) & 0x000F000Fu;
+          for (int e = 0; e < 4; ++e)
+            a[e] = (r.vw[n] >> (8 * (e >> 1))) & ((e & 1) ? 0x00F000F0u : 0x000F000Fu);
         } else {
-          const int sh = 8 * (n & 1);  // tile parity selects the byte
+          // tile parity selects the byte; pair e: (w' >> 4 (e/2)) at bits 2 (e%2)
+          const uint32_t x = r.vw[n >> 1] >> (8 * (n & 1));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = (r.vw[n >> 1] >> (sh + 2 * e)) & 0x00030003u;
+          for (int e = 0; e < 4; ++e)
+            a[e] = (x >> (4 * (e >> 1))) & ((e & 1) ? 0x000C000Cu : 0x00030003u);
         }
         oacc[n] = mfma(a, bh, oacc[n]);
         oacc[n] = mfma(a, bl, oacc[n]);
@@ -701,7 +786,9 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
     if (mx > 0.0f) (void)frexpf(mx, &e);
     eh[h] = e;
 #pragma unroll
-    for (int k = 0; k < QPH; ++k) qfs[h * D + lane + 64 * k] = ldexpf(qv[k], -e);
+    for (int k = 0; k < QPH; ++k)  // channel lane + 64 k has the parity of lane
+      qfs[h * D + lane + 64 * k] =
+          ldexpf(qv[k], -e) * ((lane & 1) ? kKeyOddQ<BK> : kKeyEvenQ<BK>);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -711,7 +798,8 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
     if (w.hcol == h) e_mine = eh[h];
-  w.kscale = ldexpf(1.0f, e_mine + 24);  // codes are the fp16 numbers c * 2^-24
+  // codes are the fp16 numbers c * 2^-24, pairs carry the key-side factor
+  w.kscale = ldexpf(1.0f, e_mine + 24 - kKeyAccLog2<BK>);
   w.bscale = ldexpf(1.0f, e_mine);
 
   if (pc0 < pc1) {
@@ -737,27 +825,17 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
     for (int k = rk0; k < rk1; ++k) w.process_residual(lq + k * kChunk, sw.n, g.R, kres, vres);
   }
 
-  // partial: O (+ value-min term), max, sum of this wave's tokens
+  // partial: O (value-min term included), max, sum of this wave's tokens
+  if (!resid) w.to_real();
   float l_run = w.l_run;
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);
-  float bias[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    bias[f] = xor_sum(w.bias[f], 16);
-    bias[f] = xor_sum(bias[f], 32);
-  }
   float* part = part_base + w.hcol * DP;
-  const float oscale = resid ? 1.0f : 16777216.0f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int gm = C::gam(n);
     if (gm % SL != w.slot) continue;
-    const float bsum = bias[gm / SL];
-    const float4 v = make_float4(__builtin_fmaf(w.oacc[n][0], oscale, bsum),
-                                 __builtin_fmaf(w.oacc[n][1], oscale, bsum),
-                                 __builtin_fmaf(w.oacc[n][2], oscale, bsum),
-                                 __builtin_fmaf(w.oacc[n][3], oscale, bsum));
+    const float4 v = make_float4(w.oacc[n][0], w.oacc[n][1], w.oacc[n][2], w.oacc[n][3]);
     *reinterpret_cast<float4*>(part + 16 * n + 4 * w.lg) = v;
   }
   if (w.lg == 0 && w.slot == 0) {
