@@ -236,7 +236,7 @@ struct Cfg {
   static constexpr int IPL = (ITEMS + 63) / 64;   // fold items per lane
   // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ]
   static constexpr int kQB = 2 * GQ * 4 * KC * 16;
-  static constexpr int kWaveLds = kQB + 16 * ((GQ * 4 + 15) / 16);
+  static constexpr int kWaveLds = kQB + 16 * ((GQ * 4 + 4 + 15) / 16);  // + spare beta
   static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
 };
 
@@ -372,7 +372,8 @@ struct PackedWave {
     for (int i = 0; i < IPL; ++i) {
       const int it = fitem[i];
       float bpart = 0.0f;
-      if (it < C::ITEMS) {
+      // (when the items fill the wave exactly the test is compile-time true)
+      if (C::ITEMS % 64 == 0 || it < C::ITEMS) {
         const int h = it / IPH, rr = it % IPH, gg = rr / KC, kc = rr % KC;
         const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][0]);
         const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][1]);
@@ -398,7 +399,10 @@ struct PackedWave {
         qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
       }
       bpart = group_sum<IPH>(bpart);
-      if (it < C::ITEMS && (it % IPH) == 0) beta_l[it / IPH] = bpart;
+      // every lane stores (no branch): a head's first item lane its beta, the
+      // others a spare slot
+      const bool lead = (C::ITEMS % 64 == 0 || it < C::ITEMS) && (it % IPH) == 0;
+      beta_l[lead ? it / IPH : GQ] = bpart;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -580,10 +584,15 @@ struct PackedWave {
   }
 
   __device__ __forceinline__ void process(int ch, const R& r) {
-    const int grp = (ch * kChunk) / G;
-    if (grp != cur_group) {
-      cur_group = grp;
-      fold(r);
+    if constexpr (G == kChunk) {
+      fold(r);  // every chunk is a key group: no branch, so the fold can be
+                // scheduled against the previous chunk's value products
+    } else {
+      const int grp = (ch * kChunk) / G;
+      if (grp != cur_group) {
+        cur_group = grp;
+        fold(r);
+      }
     }
     // scores: s = 2^(E+24) * (codes x q') + beta
     float s[2][4];
@@ -808,13 +817,14 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
     // chunk re-load that chunk (always in bounds) instead of being skipped,
     // so no load sits under a branch.
     const int last = pc1 - 1;
-    for (int ch = pc0; ch < pc1; ch += 2) {
-      w.load(min(ch + 1, last), rb);
+    int ch = pc0;
+    for (; ch < last; ch += 2) {  // pairs; ra holds chunk ch on entry
+      w.load(ch + 1, rb);
       w.process(ch, ra);
-      if (ch + 1 >= pc1) break;
       w.load(min(ch + 2, last), ra);
       w.process(ch + 1, rb);
     }
+    if (ch == last) w.process(ch, ra);  // odd count: the last chunk is in ra
   }
   const bool resid = rk0 < rk1;
   if (resid) {
