@@ -16,8 +16,6 @@
 namespace kvq {
 namespace {
 
-constexpr int kMaxG = 128;
-constexpr int kMaxD = 128;
 
 // Scale and min of one group from its fp32 min and max.
 struct GroupParams {
@@ -103,29 +101,39 @@ __device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* src,
   for (int i = threadIdx.x; i < n_halves / 8; i += blockDim.x) d[i] = s[i];
 }
 
-// One key group: G token rows of D channels at `src` (row-major), first
-// position `pos` (a multiple of G).  Per channel: min/max over the G tokens.
+// LDS of one quantizer workgroup: a tile of fp16 token rows and its codes.
+// Keys use G rows, values one 32-token block; sized for the larger.
+__host__ __device__ inline int quant_rows(const Geom& g) { return g.G > kVBlock ? g.G : kVBlock; }
+inline size_t quant_lds_bytes(const Geom& g) { return (size_t)quant_rows(g) * g.D * 3; }
+
+// One key group: G token rows of D channels in `tile` (already loaded),
+// first position `pos` (a multiple of G).  Per channel: min/max over the G
+// tokens, split over kThreads / D threads per channel.
 template <int BITS>
-__device__ void key_group(const Geom& g, const uint16_t* src, int64_t unit,
-                          int32_t pos, uint32_t* k_codes, uint16_t* k_meta,
-                          uint16_t* tile, uint8_t* codes) {
+__device__ void key_group(const Geom& g, int64_t unit, int32_t pos, uint32_t* k_codes,
+                          uint16_t* k_meta, const uint16_t* tile, uint8_t* codes) {
   const int G = g.G, D = g.D;
-  load_tile(tile, src, G * D);
-  __syncthreads();
-  uint32_t* meta32 = reinterpret_cast<uint32_t*>(k_meta);
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float mn = h2f(tile[c]), mx = mn;
-    for (int t = 1; t < G; ++t) {
-      const float v = h2f(tile[t * D + c]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-    const GroupParams p = group_params(mn, mx, BITS);
+  const int tpc = kThreads / D;            // threads per channel (2 or 4)
+  const int c = threadIdx.x / tpc, part = threadIdx.x % tpc;
+  const int tn = G / tpc;                  // tokens of this thread
+  float mn = h2f(tile[(part * tn) * D + c]), mx = mn;
+  for (int t = part * tn + 1; t < (part + 1) * tn; ++t) {
+    const float v = h2f(tile[t * D + c]);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  for (int off = 1; off < tpc; off <<= 1) {  // partners are neighbouring lanes
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  const GroupParams p = group_params(mn, mx, BITS);
+  if (part == 0) {
+    uint32_t* meta32 = reinterpret_cast<uint32_t*>(k_meta);
     meta32[(unit * (g.C / G) + pos / G) * D + key_meta_entry<BITS>(c, D)] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
-    for (int t = 0; t < G; ++t)
-      codes[t * D + c] = (uint8_t)group_code(h2f(tile[t * D + c]), p, BITS);
   }
+  for (int t = part * tn; t < (part + 1) * tn; ++t)
+    codes[t * D + c] = (uint8_t)group_code(h2f(tile[t * D + c]), p, BITS);
   __syncthreads();
   // words of the natural token rows, stored at their consumer-order places:
   // row word w' is word w' % KW of slice w' / KW, placed at lane 16 g + i,
@@ -145,40 +153,40 @@ __device__ void key_group(const Geom& g, const uint16_t* src, int64_t unit,
     k_codes[(unit * (g.C / kVBlock) + p_tok / kVBlock) * (int64_t)(D * BITS) +
             (2 * lane + u) * KW + wr % KW] = word;
   }
-  __syncthreads();  // tile/codes are reused by the caller
 }
 
-// One 32-token value block: token rows at `src`, first position `pos` (a
-// multiple of 32).  Per token: D/G groups of G consecutive channels.
-// With window_blk >= 0, src is the unit's residual value window and the block
-// is its 32-slot chunk window_blk; otherwise src holds 32 token rows.
+// One 32-token value block in `tile` (already loaded), first position `pos`
+// (a multiple of 32).  Per token: D/G groups of G consecutive channels; the
+// 32 * D/G (token, group) items are split over the workgroup's threads.
 template <int BITS>
-__device__ void value_block(const Geom& g, const uint16_t* src, int window_blk,
-                            int64_t unit, int32_t pos, uint32_t* v_codes,
-                            uint16_t* v_meta, uint16_t* tile, uint8_t* codes) {
+__device__ void value_block(const Geom& g, int64_t unit, int32_t pos, uint32_t* v_codes,
+                            uint16_t* v_meta, const uint16_t* tile, uint8_t* codes) {
   const int G = g.G, D = g.D, NG = D / G;
-  if (window_blk >= 0)
-    load_value_window(tile, src, window_blk, D);
-  else
-    load_tile(tile, src, kVBlock * D);
-  __syncthreads();
-  uint32_t* meta32 = reinterpret_cast<uint32_t*>(v_meta);
-  for (int i = threadIdx.x; i < kVBlock * NG; i += blockDim.x) {
-    const int t = i / NG, gm = i % NG;
-    const uint16_t* row = tile + t * D + gm * G;
-    float mn = h2f(row[0]), mx = mn;
-    for (int c = 1; c < G; ++c) {
-      const float v = h2f(row[c]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-    const GroupParams p = group_params(mn, mx, BITS);
+  const int items = kVBlock * NG;                    // 64 .. 128
+  const int tpi = kThreads / items;                  // threads per item (2 .. 8)
+  const int it = threadIdx.x / tpi, part = threadIdx.x % tpi;
+  const int t = it / NG, gm = it % NG;
+  const int cn = G / tpi;                            // channels of this thread
+  const uint16_t* row = tile + t * D + gm * G + part * cn;
+  float mn = h2f(row[0]), mx = mn;
+  for (int c = 1; c < cn; ++c) {
+    const float v = h2f(row[c]);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  for (int off = 1; off < tpi; off <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  const GroupParams p = group_params(mn, mx, BITS);
+  if (part == 0) {
     // entry [block][t / 8][gm][t % 8]
+    uint32_t* meta32 = reinterpret_cast<uint32_t*>(v_meta);
     meta32[(((unit * (g.C / kVBlock) + pos / kVBlock) * 4 + t / 8) * NG + gm) * 8 + t % 8] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
-    for (int c = 0; c < G; ++c)
-      codes[t * D + gm * G + c] = (uint8_t)group_code(h2f(row[c]), p, BITS);
   }
+  for (int c = 0; c < cn; ++c)
+    codes[t * D + gm * G + part * cn + c] = (uint8_t)group_code(h2f(row[c]), p, BITS);
   __syncthreads();
   // consumer order: lane 16 g + i holds tokens 8g + j; 4 bits: word n is
   // channel 16n + i, token j at bit 4 (j/2) + 16 (j%2); 2 bits: word m holds
@@ -200,31 +208,34 @@ __device__ void value_block(const Geom& g, const uint16_t* src, int window_blk,
     }
     blk[x] = word;
   }
-  __syncthreads();
 }
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(
     Geom g, const uint16_t* __restrict__ src, int64_t src_unit_stride,
     int32_t pos0, uint32_t* __restrict__ k_codes, uint16_t* __restrict__ k_meta) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kMaxG * kMaxD];
-  __shared__ uint8_t codes[kMaxG * kMaxD];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* tile = lds;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds + quant_rows(g) * g.D);
   const int64_t unit = (int64_t)blockIdx.z * g.Hkv + blockIdx.y;
   const int j = blockIdx.x;
-  key_group<BITS>(g, src + unit * src_unit_stride + (int64_t)j * g.G * g.D,
-                  unit, pos0 + j * g.G, k_codes, k_meta, tile, codes);
+  load_tile(tile, src + unit * src_unit_stride + (int64_t)j * g.G * g.D, g.G * g.D);
+  __syncthreads();
+  key_group<BITS>(g, unit, pos0 + j * g.G, k_codes, k_meta, tile, codes);
 }
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_values_kernel(
     Geom g, const uint16_t* __restrict__ src, int64_t src_unit_stride,
     int32_t pos0, uint32_t* __restrict__ v_codes, uint16_t* __restrict__ v_meta) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kVBlock * kMaxD];
-  __shared__ uint8_t codes[kVBlock * kMaxD];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* tile = lds;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds + quant_rows(g) * g.D);
   const int64_t unit = (int64_t)blockIdx.z * g.Hkv + blockIdx.y;
   const int blk = blockIdx.x;
-  value_block<BITS>(g, src + unit * src_unit_stride + (int64_t)blk * kVBlock * g.D, -1,
-                    unit, pos0 + blk * kVBlock, v_codes, v_meta, tile, codes);
+  load_tile(tile, src + unit * src_unit_stride + (int64_t)blk * kVBlock * g.D, kVBlock * g.D);
+  __syncthreads();
+  value_block<BITS>(g, unit, pos0 + blk * kVBlock, v_codes, v_meta, tile, codes);
 }
 
 // Copies positions [pos0, pos0 + n_tok) of k and v ([unit][.][D] with the given
@@ -256,7 +267,13 @@ __global__ __launch_bounds__(kThreads) void residual_copy_kernel(
   }
 }
 
-// One workgroup per (KV head, sequence).  Lazy flush, then the residual write.
+// Grid (KV head, sequence, 1 + R/G + R/32).  z = 0 writes the new token to
+// slot n % R when no flush is due.  When one is due (n > 0, n % R == 0: the
+// window holds positions n - R .. n - 1 in slots 0 .. R-1), z = 1 .. R/G
+// quantize the key groups and z = R/G + 1 .. the 32-token value blocks of the
+// window, each in its own workgroup; the workgroups that read slot 0 (key
+// group 0, value block 0) write the new token there after their read, so no
+// workgroup waits for another.  Without a flush, z >= 1 return at once.
 template <int BK, int BV>
 __global__ __launch_bounds__(kThreads) void append_kernel(
     Geom g, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -264,28 +281,42 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     uint32_t* __restrict__ v_codes, uint16_t* __restrict__ k_meta,
     uint16_t* __restrict__ v_meta, uint16_t* __restrict__ k_res,
     uint16_t* __restrict__ v_res) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kMaxG * kMaxD];
-  __shared__ uint8_t codes[kMaxG * kMaxD];
-  const int b = blockIdx.y;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int b = blockIdx.y, z = blockIdx.z;
   const int64_t unit = (int64_t)b * g.Hkv + blockIdx.x;
   const int32_t n = seq_lens[b];
   if (n < 0 || n >= g.C) return;  // caller error: leave the cache untouched
   uint16_t* kr = k_res + unit * g.R * g.D;
   uint16_t* vr = v_res + unit * g.R * g.D;
-  if (n > 0 && n % g.R == 0) {
-    // slots 0..R-1 hold positions n-R .. n-1 in order
-    for (int j = 0; j < g.R / g.G; ++j)
-      key_group<BK>(g, kr + (int64_t)j * g.G * g.D, unit, n - g.R + j * g.G,
-                    k_codes, k_meta, tile, codes);
-    for (int blk = 0; blk < g.R / kVBlock; ++blk)
-      value_block<BV>(g, vr, blk, unit, n - g.R + blk * kVBlock, v_codes, v_meta, tile,
-                      codes);
-    // every read of the window happened before the barriers in the helpers
+  const bool flush = n > 0 && n % g.R == 0;
+  const int nk = g.R / g.G;  // key groups of the window
+  if (!flush) {
+    if (z != 0) return;
+    const int slot = n % g.R;
+    for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
+      kr[(int64_t)slot * g.D + c] = k_new[unit * g.D + c];
+      vr[value_res_index(g.D, slot, c)] = v_new[unit * g.D + c];
+    }
+    return;
   }
-  const int slot = n % g.R;
-  for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
-    kr[(int64_t)slot * g.D + c] = k_new[unit * g.D + c];
-    vr[value_res_index(g.D, slot, c)] = v_new[unit * g.D + c];
+  if (z == 0) return;
+  uint16_t* tile = lds;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds + quant_rows(g) * g.D);
+  if (z <= nk) {
+    const int j = z - 1;
+    load_tile(tile, kr + (int64_t)j * g.G * g.D, g.G * g.D);
+    __syncthreads();
+    if (j == 0)  // slot 0 has been read: the new token goes there
+      for (int c = threadIdx.x; c < g.D; c += blockDim.x) kr[c] = k_new[unit * g.D + c];
+    key_group<BK>(g, unit, n - g.R + j * g.G, k_codes, k_meta, tile, codes);
+  } else {
+    const int blk = z - 1 - nk;
+    load_value_window(tile, vr, blk, g.D);
+    __syncthreads();
+    if (blk == 0)
+      for (int c = threadIdx.x; c < g.D; c += blockDim.x)
+        vr[value_res_index(g.D, 0, c)] = v_new[unit * g.D + c];
+    value_block<BV>(g, unit, n - g.R + blk * kVBlock, v_codes, v_meta, tile, codes);
   }
 }
 
@@ -298,11 +329,11 @@ hipError_t launch_quantize_keys(const Geom& g, const uint16_t* src,
   if (n_tok == 0) return hipSuccess;
   dim3 grid(n_tok / g.G, g.Hkv, g.B);
   if (g.bK == 2)
-    quantize_keys_kernel<2><<<grid, kThreads, 0, st>>>(g, src, src_unit_stride,
-                                                        pos0, k_codes, k_meta);
+    quantize_keys_kernel<2><<<grid, kThreads, quant_lds_bytes(g), st>>>(
+        g, src, src_unit_stride, pos0, k_codes, k_meta);
   else
-    quantize_keys_kernel<4><<<grid, kThreads, 0, st>>>(g, src, src_unit_stride,
-                                                        pos0, k_codes, k_meta);
+    quantize_keys_kernel<4><<<grid, kThreads, quant_lds_bytes(g), st>>>(
+        g, src, src_unit_stride, pos0, k_codes, k_meta);
   return hipGetLastError();
 }
 
@@ -313,10 +344,10 @@ hipError_t launch_quantize_values(const Geom& g, const uint16_t* src,
   if (n_tok == 0) return hipSuccess;
   dim3 grid(n_tok / kVBlock, g.Hkv, g.B);
   if (g.bV == 2)
-    quantize_values_kernel<2><<<grid, kThreads, 0, st>>>(
+    quantize_values_kernel<2><<<grid, kThreads, quant_lds_bytes(g), st>>>(
         g, src, src_unit_stride, pos0, v_codes, v_meta);
   else
-    quantize_values_kernel<4><<<grid, kThreads, 0, st>>>(
+    quantize_values_kernel<4><<<grid, kThreads, quant_lds_bytes(g), st>>>(
         g, src, src_unit_stride, pos0, v_codes, v_meta);
   return hipGetLastError();
 }
@@ -337,9 +368,9 @@ hipError_t launch_residual_copy(const Geom& g, const uint16_t* k,
 hipError_t launch_append(const Geom& g, const uint16_t* k_new,
                          const uint16_t* v_new, const int32_t* seq_lens,
                          const kvq_cache& c, hipStream_t st) {
-  dim3 grid(g.Hkv, g.B);
+  dim3 grid(g.Hkv, g.B, 1 + g.R / g.G + g.R / kVBlock);
 #define KVQ_APPEND(BK, BV)                                                    \
-  append_kernel<BK, BV><<<grid, kThreads, 0, st>>>(                           \
+  append_kernel<BK, BV><<<grid, kThreads, quant_lds_bytes(g), st>>>(          \
       g, k_new, v_new, seq_lens, c.k_codes, c.v_codes, c.k_meta, c.v_meta,    \
       c.k_res, c.v_res)
   if (g.bK == 2 && g.bV == 2) KVQ_APPEND(2, 2);
