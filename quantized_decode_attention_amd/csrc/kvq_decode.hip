@@ -679,9 +679,8 @@ struct SeqWork {
   int w;   // work units per KV head
 };
 
-__device__ __forceinline__ SeqWork seq_work(const DecodeLaunch& L, int b) {
+__device__ __forceinline__ SeqWork seq_work_of(const DecodeLaunch& L, int n) {
   SeqWork sw{0, 0, 0, 0};
-  const int n = L.seq_lens[b];
   if (n <= 0 || n > L.g.C || n > L.max_seq_len) return sw;
   const int lq = packed_len(n, L.g.R);
   sw.n = n;
@@ -691,36 +690,74 @@ __device__ __forceinline__ SeqWork seq_work(const DecodeLaunch& L, int b) {
   return sw;
 }
 
-// Total work units over all units, by one wave.
-__device__ __forceinline__ int wave_total_work(const DecodeLaunch& L, int lane) {
-  int s = 0;
-  for (int b = lane; b < L.g.B; b += 64) s += seq_work(L, b).w;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  return s * L.g.Hkv;
+__device__ __forceinline__ SeqWork seq_work(const DecodeLaunch& L, int b) {
+  return seq_work_of(L, L.seq_lens[b]);
 }
 
-// Sequence b holding flat work unit x, and base = Hkv * (work of sequences < b).
-__device__ __forceinline__ void wave_find_seq(const DecodeLaunch& L, int lane, int x,
-                                              int& b_out, int& base_out) {
-  int base = 0;
-  for (int b0 = 0; b0 < L.g.B; b0 += 64) {
+// Inclusive prefix sum over the wave's 64 lanes: DPP shifts inside each row
+// of 16 lanes, then row broadcasts (lane 15 into the next row, lane 31 into
+// rows 2 and 3); lanes a DPP move does not reach add 0.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// The batch's work layout as one wave sees it: for the first 64 sequences,
+// lane b holds sequence b's work over all its KV heads (c) and the inclusive
+// prefix (inc); total covers the whole batch.
+// uniform: every length equals max_seq_len.
+struct BatchWork {
+  int c, inc, head_total, total;
+  bool uniform;
+};
+
+__device__ __forceinline__ BatchWork batch_work(const DecodeLaunch& L, int lane) {
+  BatchWork bw;
+  const int n = lane < L.g.B ? L.seq_lens[lane] : L.max_seq_len;
+  bw.c = lane < L.g.B ? seq_work_of(L, n).w * L.g.Hkv : 0;
+  bw.inc = wave_scan_incl(bw.c);
+  bw.head_total = __builtin_amdgcn_readlane(bw.inc, 63);
+  bw.total = bw.head_total;
+  bw.uniform = __ballot(n != L.max_seq_len) == 0;
+  for (int b0 = 64; b0 < L.g.B; b0 += 64) {  // batches beyond 64 sequences
+    const int nb = b0 + lane < L.g.B ? L.seq_lens[b0 + lane] : L.max_seq_len;
+    int s = b0 + lane < L.g.B ? seq_work_of(L, nb).w * L.g.Hkv : 0;
+    s = wave_scan_incl(s);
+    bw.total += __builtin_amdgcn_readlane(s, 63);
+    bw.uniform = bw.uniform && __ballot(nb != L.max_seq_len) == 0;
+  }
+  return bw;
+}
+
+// Sequence b holding flat work unit x < total, and base = Hkv * (work of
+// sequences < b).
+__device__ __forceinline__ void wave_find_seq(const DecodeLaunch& L, const BatchWork& bw,
+                                              int lane, int x, int& b_out, int& base_out) {
+  if (x < bw.head_total) {
+    const uint64_t m = __ballot(bw.inc > x);
+    const int l = __ffsll((unsigned long long)m) - 1;
+    b_out = l;
+    base_out = __builtin_amdgcn_readlane(bw.inc - bw.c, l);
+    return;
+  }
+  int base = bw.head_total;
+  for (int b0 = 64; b0 < L.g.B; b0 += 64) {
     const int b = b0 + lane;
     const int c = (b < L.g.B) ? seq_work(L, b).w * L.g.Hkv : 0;
-    int inc = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off, 64);
-      if (lane >= off) inc += y;
-    }
+    const int inc = wave_scan_incl(c);
     const uint64_t m = __ballot(base + inc > x);
     if (m) {
       const int l = __ffsll((unsigned long long)m) - 1;
       b_out = b0 + l;
-      base_out = base + __shfl(inc - c, l, 64);
+      base_out = base + __builtin_amdgcn_readlane(inc - c, l);
       return;
     }
-    base += __shfl(inc, 63, 64);
+    base += __builtin_amdgcn_readlane(inc, 63);
   }
   b_out = L.g.B;
   base_out = base;
@@ -729,53 +766,61 @@ __device__ __forceinline__ void wave_find_seq(const DecodeLaunch& L, int lane, i
 template <int D, int BK, int BV, int GQ, int NG>
 constexpr int kWaveSmem = GQ * D * 4 + Cfg<D, BK, BV, GQ, NG>::kWaveLds;
 
-// The part of unit (b, hkv) in work range [x0, x1) -> partial p.  xu = first
-// work unit of the unit.
-template <int D, int BK, int BV, int GQ, int NG>
-__device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
-                             int xu, int x0, int x1, int p, char* smem, int lane) {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  using W = PackedWave<D, BK, BV, GQ, NG>;
-  using R = Raw<D, BK, BV, GQ, NG>;
-  constexpr int NT = C::NT, SL = C::SL, NF = C::NF;
-  constexpr int QPH = D / 64;  // query values per lane and head
-  constexpr int DP = D + kPartPad;
-  const Geom& g = L.g;
-  const int64_t unit = (int64_t)b * g.Hkv + hkv;
-  float* part_base = L.ws + (int64_t)p * GQ * DP;
+// Packed chunks [pc0, pc1) and residual chunks [rk0, rk1) of unit work
+// starting at xu that fall in the work range [x0, x1).
+struct SegRange {
+  int pc0, pc1, rk0, rk1;
+};
 
-  // packed chunks [pc0, pc1) and residual chunks [rk0, rk1) of this range
-  const int pc0 = max(x0, xu) - xu, pc1 = min(x1, xu + sw.nq) - xu;
+__device__ __forceinline__ SegRange seg_range(const DecodeLaunch& L, const SeqWork& sw, int xu,
+                                              int x0, int x1) {
+  SegRange r;
+  r.pc0 = max(x0, xu) - xu;
+  r.pc1 = min(x1, xu + sw.nq) - xu;
   const int d0 = x0 - xu - sw.nq, d1 = x1 - xu - sw.nq;
-  const int rk0 = d0 <= 0 ? 0 : (d0 + L.rw - 1) / L.rw;
-  const int rk1 = min(sw.nr, d1 <= 0 ? 0 : (d1 + L.rw - 1) / L.rw);
-  if (pc0 >= pc1 && rk0 >= rk1) {  // only part of a residual chunk's weight
-    // an empty partial: zero sums, max -inf (weight 0 in the merge)
-    for (int i = lane; i < GQ * DP; i += 64) {
-      const int c = i % DP;
-      part_base[i] = (c == D) ? kNegInf : 0.0f;
-    }
-    return;
-  }
+  r.rk0 = d0 <= 0 ? 0 : (d0 + L.rw - 1) / L.rw;
+  r.rk1 = min(sw.nr, d1 <= 0 ? 0 : (d1 + L.rw - 1) / L.rw);
+  return r;
+}
 
-  float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
+// Sets up the wave for unit (b, hkv) and issues the loads of the range's first
+// packed chunk into ra (before anything else, so that their latency overlaps
+// the query's).
+template <int D, int BK, int BV, int GQ, int NG>
+__device__ __forceinline__ void seg_begin(const DecodeLaunch& L, int64_t unit, const SegRange& r,
+                                          char* smem, int lane, PackedWave<D, BK, BV, GQ, NG>& w,
+                                          Raw<D, BK, BV, GQ, NG>& ra) {
+  using C = Cfg<D, BK, BV, GQ, NG>;
+  const Geom& g = L.g;
   char* wl = smem + GQ * D * 4;
-
-  W w;
   w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
   w.kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) + unit * (g.C / C::G) * D;
   w.vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
   w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
             unit * (g.C / kVBlock) * NG * kVBlock;
-  w.qfs = qfs;
+  w.qfs = reinterpret_cast<float*>(smem);
   w.qB = reinterpret_cast<uint4*>(wl);
   w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
   w.init(lane);
-  // the first chunk's loads go out before the query's, so the two memory
-  // latencies overlap instead of adding up
-  R ra, rb;
-  if (pc0 < pc1) w.load(pc0, ra);
+  if (r.pc0 < r.pc1) w.load(r.pc0, ra);
+}
 
+// Runs the range of unit (b, hkv) -> partial p, seg_begin having been done.
+template <int D, int BK, int BV, int GQ, int NG>
+__device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
+                        const SegRange& r, int p, char* smem, int lane,
+                        PackedWave<D, BK, BV, GQ, NG>& w, Raw<D, BK, BV, GQ, NG>& ra) {
+  using C = Cfg<D, BK, BV, GQ, NG>;
+  using R = Raw<D, BK, BV, GQ, NG>;
+  constexpr int NT = C::NT, SL = C::SL;
+  constexpr int QPH = D / 64;  // query values per lane and head
+  constexpr int DP = D + kPartPad;
+  const Geom& g = L.g;
+  const int64_t unit = (int64_t)b * g.Hkv + hkv;
+  float* part_base = L.ws + (int64_t)p * GQ * DP;
+  float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
+  const int pc0 = r.pc0, pc1 = r.pc1, rk0 = r.rk0, rk1 = r.rk1;
+  R rb;
   // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
   // that q * 2^-E * scale fits fp16
   const uint16_t* qg = L.q + ((int64_t)b * g.Hq + hkv * GQ) * D;
@@ -858,20 +903,73 @@ __device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWor
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+
+// The part of unit (b, hkv) in work range [x0, x1) -> partial p.  xu = first
+// work unit of the unit.
+template <int D, int BK, int BV, int GQ, int NG>
+__device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
+                             int xu, int x0, int x1, int p, char* smem, int lane) {
+  constexpr int DP = D + kPartPad;
+  const SegRange r = seg_range(L, sw, xu, x0, x1);
+  if (r.pc0 >= r.pc1 && r.rk0 >= r.rk1) {  // only part of a residual chunk's weight
+    // an empty partial: zero sums, max -inf (weight 0 in the merge)
+    float* part_base = L.ws + (int64_t)p * GQ * DP;
+    for (int i = lane; i < GQ * DP; i += 64) {
+      const int c = i % DP;
+      part_base[i] = (c == D) ? kNegInf : 0.0f;
+    }
+    return;
+  }
+  PackedWave<D, BK, BV, GQ, NG> w;
+  Raw<D, BK, BV, GQ, NG> ra;
+  seg_begin<D, BK, BV, GQ, NG>(L, (int64_t)b * L.g.Hkv + hkv, r, smem, lane, w, ra);
+  seg_run<D, BK, BV, GQ, NG>(L, b, hkv, sw, r, p, smem, lane, w, ra);
+}
+
 // One wave per workgroup; grid = the number of worker waves.
 template <int D, int BK, int BV, int GQ, int NG>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
   __shared__ __attribute__((aligned(16))) char smem[kWaveSmem<D, BK, BV, GQ, NG>];
   const int lane = threadIdx.x;
   const int w = blockIdx.x, nw = gridDim.x;
-  const int total = __builtin_amdgcn_readfirstlane(wave_total_work(L, lane));
+  // Speculation: if every length equals max_seq_len (a uniform batch), the
+  // work layout is plain arithmetic, so the first segment's first chunk can
+  // be requested before the lengths are read.  The loads are in bounds
+  // whatever the lengths; they are used only if the lengths confirm it.
+  using PW = PackedWave<D, BK, BV, GQ, NG>;
+  using RW = Raw<D, BK, BV, GQ, NG>;
+  const SeqWork ss = seq_work_of(L, L.max_seq_len);
+  const int per_seq = ss.w * L.g.Hkv;
+  const int cpw_s = (per_seq * L.g.B + nw - 1) / nw;
+  const int x0_s = w * cpw_s, x1_s = min(per_seq * L.g.B, x0_s + cpw_s);
+  bool spec = ss.w > 0 && x0_s < x1_s;
+  int b_s = 0, hkv_s = 0, xu_s = 0;
+  SegRange r_s{0, 0, 0, 0};
+  if (spec) {
+    b_s = x0_s / per_seq;
+    hkv_s = (x0_s - b_s * per_seq) / ss.w;
+    xu_s = b_s * per_seq + hkv_s * ss.w;
+    r_s = seg_range(L, ss, xu_s, x0_s, x1_s);
+    spec = r_s.pc0 < r_s.pc1;
+  }
+  PW ws;
+  RW ra_s;
+  if (spec) seg_begin<D, BK, BV, GQ, NG>(L, (int64_t)b_s * L.g.Hkv + hkv_s, r_s, smem, lane, ws, ra_s);
+
+  const BatchWork bw = batch_work(L, lane);  // one read of the lengths
+  const int total = bw.total;
   const int cpw = (total + nw - 1) / nw;
   const int x0 = w * cpw;
   const int x1 = min(total, x0 + cpw);
   int x = x0;
+  if (spec && bw.uniform) {  // confirmed: the speculative first segment stands
+    seg_run<D, BK, BV, GQ, NG>(L, b_s, hkv_s, ss, r_s, w + b_s * L.g.Hkv + hkv_s, smem, lane,
+                               ws, ra_s);
+    x = xu_s + ss.w;
+  }
   while (x < x1) {
     int b, base;
-    wave_find_seq(L, lane, x, b, base);
+    wave_find_seq(L, bw, lane, x, b, base);
     b = __builtin_amdgcn_readfirstlane(b);
     base = __builtin_amdgcn_readfirstlane(base);
     const SeqWork sw = seq_work(L, b);

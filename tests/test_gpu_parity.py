@@ -147,6 +147,24 @@ def test_decode_worker_boundaries():
     assert_close(out, ref, what="worker boundaries")
 
 
+def test_decode_batch_beyond_one_wave():
+    """More sequences than lanes in a wave (the work layout then spans
+    several 64-sequence blocks), lengths mixed from 1 to a few windows."""
+    B, Hq, Hkv, D = 70, 4, 2, 64
+    rng = np.random.default_rng(70)
+    lens = rng.integers(1, 300, size=B).astype(np.int32)
+    lens[::9] = 1
+    lens[5::11] = 64
+    g, og = geoms(B, Hq, Hkv, D, 2, 2, 32, 32, 320)
+    k = rng.standard_normal((B, Hkv, int(lens.max()), D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, int(lens.max()), D)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    _say(f"batch {B}: lengths {int(lens.min())}..{int(lens.max())}")
+    cache, oc = prefill_both(g, og, k, v, lens)
+    out, ref = decode_both(g, og, cache, oc, q, lens)
+    assert_close(out, ref, what="batch beyond one wave")
+
+
 def test_decode_degenerate_lengths():
     """n = 0 -> zeros; n above max_seq_len -> NaN (no out-of-bounds reads)."""
     g, og = geoms(3, 4, 2, 64, 2, 2, 32, 32, 1024)
