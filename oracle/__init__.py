@@ -22,6 +22,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
+_SRC_BQ2 = os.path.join(_HERE, "bq2_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 VBLOCK = 32  # tokens per value-code block (layout restated in kvq_oracle.c)
@@ -32,7 +33,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         cmd = [
             "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
-            "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC,
+            "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, _SRC_BQ2,
             "-o", _LIB + ".tmp", "-lm",
         ]
         subprocess.run(cmd, check=True)
@@ -68,6 +69,16 @@ def lib():
         L.orc_unpack.argtypes = [ctypes.c_int] * 6 + [i64] + [P] * 8
         L.orc_residual_store.argtypes = [ctypes.c_int] * 4 + [P, P, i64, i64, P, P]
         L.orc_value_res_rows.argtypes = [ctypes.c_int] * 4 + [P, P]
+        L.orc_bq2_hadamard.restype = f64
+        L.orc_bq2_hadamard.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.orc_bq2_rotate.argtypes = [P, P]
+        L.orc_bq2_quantize.argtypes = [P, P, P, P]
+        L.orc_bq2_block.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P]
+        L.orc_bq2_prefill.argtypes = [ctypes.c_int, ctypes.c_int, i64, P, P, i64] + [P] * 6
+        L.orc_bq2_append.argtypes = [ctypes.c_int, ctypes.c_int, i64, P, P, P] + [P] * 6
+        L.orc_bq2_unpack.argtypes = [ctypes.c_int, ctypes.c_int, i64] + [P] * 4
+        L.orc_bq2_cache_kv.argtypes = [ctypes.c_int, ctypes.c_int, i64] + [P] * 6 + [i64, P, P]
+        L.orc_bq2_decode_attn.argtypes = ([ctypes.c_int] * 3 + [i64] + [P] * 8 + [f64, P])
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -244,6 +255,122 @@ def unpack(g: Geom, cache: Cache):
                      _p(cache.v_codes), _p(cache.k_meta), _p(cache.v_meta),
                      _p(k_code), _p(v_code), _p(k_sm), _p(v_sm))
     return k_code, v_code, k_sm, v_sm
+
+
+# --------------------------------------------- rotated 2-bit format (BQ2_0) --
+BQ2_D = 64       # head dim of the format ([KV1] Quantization Format)
+BQ2_SINKS = 4    # positions kept in fp16
+
+
+def bq2_hadamard() -> np.ndarray:
+    """The oracle's normalized 64x64 Sylvester Hadamard matrix (fp64)."""
+    return np.array([[lib().orc_bq2_hadamard(r, c) for c in range(BQ2_D)]
+                     for r in range(BQ2_D)])
+
+
+def bq2_rotate(x: np.ndarray) -> np.ndarray:
+    """fp16 [..., 64] -> fp32 rotated vectors (exact product, one rounding)."""
+    x = _u16(x)
+    flat = x.reshape(-1, BQ2_D)
+    out = np.empty(flat.shape, np.float32)
+    for r in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[r])
+        lib().orc_bq2_rotate(_p(row), _p(out[r]))
+    return out.reshape(x.shape)
+
+
+def bq2_quantize(x: np.ndarray):
+    """One block of 64 fp32 values -> (d bits, m bits, codes uint8[64])."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    assert x.size == BQ2_D
+    codes = np.zeros(BQ2_D, np.uint8)
+    d = ctypes.c_uint16()
+    m = ctypes.c_uint16()
+    lib().orc_bq2_quantize(_p(x), ctypes.byref(d), ctypes.byref(m), _p(codes))
+    return int(d.value), int(m.value), codes
+
+
+def bq2_block(d: int, m: int, codes: np.ndarray) -> bytes:
+    """The page's 20-byte block for (d, m, codes)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.zeros(20, np.uint8)
+    lib().orc_bq2_block(d, m, _p(codes), _p(out))
+    return out.tobytes()
+
+
+@dataclass
+class Bq2Geom:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    capacity: int
+
+
+class Bq2Cache:
+    """Host arrays of the rotated 2-bit format, laid out as bq2_oracle.c states."""
+
+    def __init__(self, g: Bq2Geom):
+        B, H, C = g.batch, g.n_kv_heads, g.capacity
+        self.g = g
+        self.k_codes = np.zeros((B, H, C // 32, 64, 2), np.uint32)
+        self.v_codes = np.zeros((B, H, C // 32, 64, 2), np.uint32)
+        self.k_meta = np.zeros((B, H, C, 2), np.uint16)
+        self.v_meta = np.zeros((B, H, C, 2), np.uint16)
+        self.k_sink = np.zeros((B, H, BQ2_SINKS, BQ2_D), np.uint16)
+        self.v_sink = np.zeros((B, H, BQ2_D, BQ2_SINKS), np.uint16)
+
+    def arrays(self):
+        return (self.k_codes, self.v_codes, self.k_meta, self.v_meta,
+                self.k_sink, self.v_sink)
+
+
+def bq2_prefill(g: Bq2Geom, cache: Bq2Cache, k: np.ndarray, v: np.ndarray, n: int) -> None:
+    """Positions [0, n) from fp16 rows k, v [B][Hkv][n][64] (unrotated)."""
+    k = np.ascontiguousarray(_u16(k)[:, :, :n])
+    v = np.ascontiguousarray(_u16(v)[:, :, :n])
+    lib().orc_bq2_prefill(g.batch, g.n_kv_heads, g.capacity, _p(k), _p(v), n,
+                          *[_p(a) for a in cache.arrays()])
+
+
+def bq2_append(g: Bq2Geom, cache: Bq2Cache, k_new: np.ndarray, v_new: np.ndarray,
+               seq_lens_before: np.ndarray) -> None:
+    k_new = np.ascontiguousarray(_u16(k_new))
+    v_new = np.ascontiguousarray(_u16(v_new))
+    sl = np.ascontiguousarray(seq_lens_before, dtype=np.int32)
+    lib().orc_bq2_append(g.batch, g.n_kv_heads, g.capacity, _p(k_new), _p(v_new), _p(sl),
+                         *[_p(a) for a in cache.arrays()])
+
+
+def bq2_unpack(g: Bq2Geom, cache: Bq2Cache):
+    """Codes in natural order (tests): k_code, v_code uint8 [B][Hkv][C][64]."""
+    shape = (g.batch, g.n_kv_heads, g.capacity, BQ2_D)
+    kc = np.zeros(shape, np.uint8)
+    vc = np.zeros(shape, np.uint8)
+    lib().orc_bq2_unpack(g.batch, g.n_kv_heads, g.capacity, _p(cache.k_codes),
+                         _p(cache.v_codes), _p(kc), _p(vc))
+    return kc, vc
+
+
+def bq2_cache_kv(g: Bq2Geom, cache: Bq2Cache, n: int):
+    """Rotated (K, V) fp64 [B][Hkv][n][64] as the cache represents positions < n."""
+    shape = (g.batch, g.n_kv_heads, n, BQ2_D)
+    ok = np.zeros(shape, np.float64)
+    ov = np.zeros(shape, np.float64)
+    lib().orc_bq2_cache_kv(g.batch, g.n_kv_heads, g.capacity,
+                           *[_p(a) for a in cache.arrays()], n, _p(ok), _p(ov))
+    return ok, ov
+
+
+def bq2_decode_attn(g: Bq2Geom, cache: Bq2Cache, q: np.ndarray, seq_lens: np.ndarray,
+                    sm_scale: float) -> np.ndarray:
+    """fp64 [B][Hq][64] outputs (rotated back); seq_lens include the current token."""
+    q = np.ascontiguousarray(_u16(q))
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.zeros((g.batch, g.n_q_heads, BQ2_D), np.float64)
+    lib().orc_bq2_decode_attn(g.batch, g.n_q_heads, g.n_kv_heads, g.capacity, _p(q),
+                              *[_p(a) for a in cache.arrays()], _p(sl), float(sm_scale),
+                              _p(out))
+    return out
 
 
 def max_threads() -> int:

@@ -57,3 +57,34 @@ def flush_bytes(n_flush_units: int, residual: int, head_dim: int, k_bits: int,
     return n_flush_units * residual * (
         fp16_bytes_per_token(head_dim)
         + packed_bytes_per_token(head_dim, k_bits, v_bits, group))
+
+
+# ---- rotated per-token 2-bit format ([KV1] Quantization Format) ------------
+BQ2_BLOCK_BYTES = 20   # fp16 d, fp16 m, 16 bytes of 2-bit codes per 64 values
+BQ2_SINKS = 4
+
+
+def bq2_bytes_per_token() -> int:
+    """Bytes per position per KV head: one block each for K and V."""
+    return 2 * BQ2_BLOCK_BYTES
+
+
+def bq2_decode_step_bytes(seq_lens, n_q_heads: int, n_kv_heads: int) -> float:
+    """Algorithmic bytes of one decode-attention launch in the rotated format:
+    packed blocks of positions >= 4, fp16 sinks, query in and output out."""
+    D = 64
+    total = 0.0
+    for n in np.asarray(seq_lens).tolist():
+        n = int(n)
+        sinks = min(n, BQ2_SINKS)
+        total += n_kv_heads * ((n - sinks) * bq2_bytes_per_token()
+                               + sinks * fp16_bytes_per_token(D))
+    B = len(np.asarray(seq_lens))
+    total += 2 * 2 * B * n_q_heads * D
+    total += 4 * B
+    return total
+
+
+def bq2_append_bytes(batch: int, n_kv_heads: int) -> int:
+    """One append: new K, V read (fp16) and their blocks written."""
+    return batch * n_kv_heads * (2 * 2 * 64 + bq2_bytes_per_token())

@@ -45,6 +45,7 @@ class Workload:
     outlier_lo: float = 10.0
     outlier_hi: float = 20.0
     steps: int = 1
+    fmt: str = "kivi"               # "kivi" or "bq2" (rotated per-token 2-bit)
 
     def max_context(self) -> int:
         return self.ctx_range[1] if self.ctx_range else self.context
@@ -67,6 +68,11 @@ WORKLOADS = {
     # Full-stack decode: 32 layers, 256 steps from a 4096-token prefix.
     5: Workload("fullstack_32l_gqa_b64_n4096_k4v2_g64_r64_256steps", 5, 64, 32,
                 8, 128, 4, 2, 64, 64, 4096, layers=32, steps=256),
+    # KV1-shaped attention layer (32 query heads, 8 KV heads, head dim 64, 32K
+    # context) in the rotated per-token 2-bit format with 4 fp16 sinks; keys
+    # carry the same channel structure before rotation.
+    6: Workload("kv1_bq2_gqa_b16_n32768_d64", 6, 16, 32, 8, 64, 2, 2, 64, 0, 32768,
+                fmt="bq2"),
 }
 
 
@@ -138,7 +144,8 @@ def step_token(w: Workload, step: int, layer: int = 0, batch: int | None = None)
 
 
 def capacity_for(w: Workload, extra_tokens: int = 0) -> int:
-    """Smallest multiple of R holding the longest context plus extra tokens."""
+    """Smallest multiple of R (of 32 for the rotated format) holding the
+    longest context plus extra tokens."""
     need = w.max_context() + extra_tokens
-    R = w.residual
+    R = w.residual if w.fmt == "kivi" else 32
     return ((need + R - 1) // R) * R
