@@ -298,10 +298,9 @@ int kvq_decode_attn(const kvq_geom *geom, const uint16_t *q,
 /* The two phases of kvq_decode_attn, for callers that time or schedule them
  * apart.  kvq_decode_attn(...) == kvq_decode_partial(...) followed by
  * kvq_decode_combine(...) on the same stream with the same arguments.
- * kvq_decode_partial covers the packed tokens, writing (max, sum, weighted
- * value sum) partials into the workspace, and does not touch out;
- * kvq_decode_combine attends over the residual window, merges it with the
- * partials and writes out. */
+ * kvq_decode_partial covers every token (packed and residual window), writing
+ * (max, sum, weighted value sum) partials into the workspace, and does not
+ * touch out; kvq_decode_combine merges a unit's partials and writes out. */
 int kvq_decode_partial(const kvq_geom *geom, const uint16_t *q,
                        const kvq_cache *cache, const int32_t *seq_lens,
                        int32_t max_seq_len, float sm_scale, void *workspace,

@@ -1,8 +1,9 @@
 """libkvq: KIVI-style quantized KV cache + fused single-token decode attention
-for AMD Instinct MI355X (gfx950).
+for AMD Instinct MI355X (gfx950), and the rotated per-token 2-bit format of
+KV1 (BQ2_0).
 
 The computation lives in libkvq.so (hand-written HIP kernels behind the C ABI
-in include/kvq.h); this package is its thin ctypes binding plus the seeded
+in include/kvq.h and include/kvq_bq2.h); this package is its thin ctypes binding plus the seeded
 synthetic workloads and the byte accounting used by the benchmark.
 """
 from ._lib import (  # noqa: F401
@@ -12,3 +13,8 @@ from ._lib import (  # noqa: F401
     kvq_decode_workspace_bytes, kvq_layout_version, kvq_prefill,
     kvq_quantize_keys_perchannel, kvq_quantize_values_pertoken,
     kvq_validate_geom, last_error, lib, status_str)
+from ._lib import (  # noqa: F401
+    Bq2Cache, Bq2Geom, alloc_bq2_workspace, kvq_bq2_append, kvq_bq2_cache_bytes,
+    kvq_bq2_decode_attn, kvq_bq2_decode_combine, kvq_bq2_decode_partial,
+    kvq_bq2_decode_workers, kvq_bq2_decode_workspace_bytes, kvq_bq2_prefill,
+    kvq_bq2_validate_geom)

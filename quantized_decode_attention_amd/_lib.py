@@ -1,6 +1,7 @@
 """ctypes binding of libkvq (argument marshalling only).
 
-Every function here has the name of a C entry point in include/kvq.h and does
+Every function here has the name of a C entry point in include/kvq.h or
+include/kvq_bq2.h and does
 nothing but check the torch tensors it is handed (device, dtype, contiguity,
 shape), pass their data pointers and the current HIP stream, and turn a
 non-zero status into an exception.  All computation runs in the library's HIP
@@ -40,6 +41,13 @@ EXPORTS = [
     "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append",
     "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
 ]
+EXPORTS_BQ2 = [
+    "kvq_bq2_validate_geom", "kvq_bq2_cache_bytes", "kvq_bq2_decode_workers",
+    "kvq_bq2_decode_workspace_bytes", "kvq_bq2_prefill", "kvq_bq2_append",
+    "kvq_bq2_decode_attn", "kvq_bq2_decode_partial", "kvq_bq2_decode_combine",
+]
+BQ2_HEAD_DIM = 64
+BQ2_SINKS = 4
 
 
 class kvq_geom(ctypes.Structure):
@@ -51,6 +59,15 @@ class kvq_geom(ctypes.Structure):
 class kvq_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res")]
+
+
+class kvq_bq2_geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "n_q_heads", "n_kv_heads", "capacity")]
+
+
+class kvq_bq2_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_codes", "v_codes", "k_meta", "v_meta", "k_sink", "v_sink")]
 
 
 class KvqError(RuntimeError):
@@ -74,6 +91,9 @@ def lib() -> ctypes.CDLL:
         P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         G = ctypes.POINTER(kvq_geom)
         C = ctypes.POINTER(kvq_cache)
+        G2 = ctypes.POINTER(kvq_bq2_geom)
+        C2 = ctypes.POINTER(kvq_bq2_cache)
+        f32 = ctypes.c_float
         sig = {
             "kvq_abi_version": (ctypes.c_int, []),
             "kvq_layout_version": (ctypes.c_int, []),
@@ -90,6 +110,15 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_attn": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_partial": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_combine": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
+            "kvq_bq2_validate_geom": (ctypes.c_int, [G2]),
+            "kvq_bq2_cache_bytes": (ctypes.c_int, [G2, ctypes.POINTER(sz)]),
+            "kvq_bq2_decode_workers": (ctypes.c_int, [G2, ctypes.POINTER(i32)]),
+            "kvq_bq2_decode_workspace_bytes": (ctypes.c_int, [G2, i32, ctypes.POINTER(sz)]),
+            "kvq_bq2_prefill": (ctypes.c_int, [G2, P, P, i32, C2, P]),
+            "kvq_bq2_append": (ctypes.c_int, [G2, P, P, P, C2, P]),
+            "kvq_bq2_decode_attn": (ctypes.c_int, [G2, P, C2, P, i32, f32, P, sz, P, P]),
+            "kvq_bq2_decode_partial": (ctypes.c_int, [G2, P, C2, P, i32, f32, P, sz, P, P]),
+            "kvq_bq2_decode_combine": (ctypes.c_int, [G2, P, C2, P, i32, f32, P, sz, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -324,4 +353,125 @@ def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | 
     n = kvq_decode_workspace_bytes(g, max_seq_len)
     if n == 0:
         return None
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+# ------------------------------------------- rotated per-token 2-bit format --
+@dataclass(frozen=True)
+class Bq2Geom:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    capacity: int
+
+    def c(self) -> kvq_bq2_geom:
+        return kvq_bq2_geom(self.batch, self.n_q_heads, self.n_kv_heads, self.capacity)
+
+
+def kvq_bq2_validate_geom(g: Bq2Geom) -> None:
+    gc = g.c()
+    _check(lib().kvq_bq2_validate_geom(ctypes.byref(gc)), "kvq_bq2_validate_geom")
+
+
+def kvq_bq2_cache_bytes(g: Bq2Geom) -> list[int]:
+    gc = g.c()
+    out = (ctypes.c_size_t * 6)()
+    _check(lib().kvq_bq2_cache_bytes(ctypes.byref(gc), out), "kvq_bq2_cache_bytes")
+    return list(out)
+
+
+def kvq_bq2_decode_workers(g: Bq2Geom) -> int:
+    gc = g.c()
+    nw = ctypes.c_int32()
+    _check(lib().kvq_bq2_decode_workers(ctypes.byref(gc), ctypes.byref(nw)),
+           "kvq_bq2_decode_workers")
+    return nw.value
+
+
+def kvq_bq2_decode_workspace_bytes(g: Bq2Geom, max_seq_len: int) -> int:
+    gc = g.c()
+    out = ctypes.c_size_t()
+    _check(lib().kvq_bq2_decode_workspace_bytes(ctypes.byref(gc), max_seq_len,
+                                                ctypes.byref(out)),
+           "kvq_bq2_decode_workspace_bytes")
+    return out.value
+
+
+class Bq2Cache:
+    """The six buffers of one layer's cache in the rotated format, as torch
+    device tensors laid out as include/kvq_bq2.h specifies."""
+
+    def __init__(self, g: Bq2Geom, device="cuda"):
+        B, H, C = g.batch, g.n_kv_heads, g.capacity
+        self.g = g
+        z = dict(device=device)
+        self.k_codes = torch.zeros((B, H, C // 32, 64, 2), dtype=torch.int32, **z)
+        self.v_codes = torch.zeros((B, H, C // 32, 64, 2), dtype=torch.int32, **z)
+        self.k_meta = torch.zeros((B, H, C, 2), dtype=torch.int16, **z)
+        self.v_meta = torch.zeros((B, H, C, 2), dtype=torch.int16, **z)
+        self.k_sink = torch.zeros((B, H, BQ2_SINKS, BQ2_HEAD_DIM), dtype=torch.float16, **z)
+        self.v_sink = torch.zeros((B, H, BQ2_HEAD_DIM, BQ2_SINKS), dtype=torch.float16, **z)
+        for t, n in zip(self.tensors(), kvq_bq2_cache_bytes(g)):
+            assert t.numel() * t.element_size() == n
+
+    def tensors(self):
+        return (self.k_codes, self.v_codes, self.k_meta, self.v_meta, self.k_sink,
+                self.v_sink)
+
+    def c(self) -> kvq_bq2_cache:
+        for t in self.tensors():
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("cache tensors must be contiguous device tensors")
+        return kvq_bq2_cache(*[t.data_ptr() for t in self.tensors()])
+
+
+def kvq_bq2_prefill(g: Bq2Geom, k: torch.Tensor, v: torch.Tensor, n: int, cache: Bq2Cache,
+                    stream=None) -> None:
+    shape = (g.batch, g.n_kv_heads, n, BQ2_HEAD_DIM)
+    gc, cc = g.c(), cache.c()
+    _check(lib().kvq_bq2_prefill(ctypes.byref(gc), _ptr(k, "k", _F16, shape),
+                                 _ptr(v, "v", _F16, shape), n, ctypes.byref(cc),
+                                 _stream(stream)), "kvq_bq2_prefill")
+
+
+def kvq_bq2_append(g: Bq2Geom, k_new: torch.Tensor, v_new: torch.Tensor,
+                   seq_lens: torch.Tensor, cache: Bq2Cache, stream=None) -> None:
+    shape = (g.batch, g.n_kv_heads, BQ2_HEAD_DIM)
+    gc, cc = g.c(), cache.c()
+    _check(lib().kvq_bq2_append(ctypes.byref(gc), _ptr(k_new, "k_new", _F16, shape),
+                                _ptr(v_new, "v_new", _F16, shape),
+                                _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
+                                ctypes.byref(cc), _stream(stream)), "kvq_bq2_append")
+
+
+def _bq2_decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out):
+    gc, cc = g.c(), cache.c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    shape = (g.batch, g.n_q_heads, BQ2_HEAD_DIM)
+    return (ctypes.byref(gc), _ptr(q, "q", _F16, shape), ctypes.byref(cc),
+            _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(max_seq_len),
+            float(sm_scale), _ptr(workspace, "workspace"), ws_bytes,
+            _ptr(out, "out", _F16, shape)), (gc, cc)
+
+
+def kvq_bq2_decode_attn(g: Bq2Geom, q, cache: Bq2Cache, seq_lens, max_seq_len: int,
+                        sm_scale: float, workspace, out, stream=None) -> None:
+    args, keep = _bq2_decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
+    _check(lib().kvq_bq2_decode_attn(*args, _stream(stream)), "kvq_bq2_decode_attn")
+
+
+def kvq_bq2_decode_partial(g: Bq2Geom, q, cache: Bq2Cache, seq_lens, max_seq_len: int,
+                           sm_scale: float, workspace, out, stream=None) -> None:
+    args, keep = _bq2_decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
+    _check(lib().kvq_bq2_decode_partial(*args, _stream(stream)), "kvq_bq2_decode_partial")
+
+
+def kvq_bq2_decode_combine(g: Bq2Geom, q, cache: Bq2Cache, seq_lens, max_seq_len: int,
+                           sm_scale: float, workspace, out, stream=None) -> None:
+    args, keep = _bq2_decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
+    _check(lib().kvq_bq2_decode_combine(*args, _stream(stream)), "kvq_bq2_decode_combine")
+
+
+def alloc_bq2_workspace(g: Bq2Geom, max_seq_len: int, device="cuda") -> torch.Tensor:
+    n = kvq_bq2_decode_workspace_bytes(g, max_seq_len)
     return torch.empty(n // 4, dtype=torch.float32, device=device)

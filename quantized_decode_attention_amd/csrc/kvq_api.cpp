@@ -179,6 +179,97 @@ int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache
   return KVQ_OK;
 }
 
+
+// ---- rotated per-token 2-bit format (kvq_bq2.h) ---------------------------
+
+int check_bq2_geom(const kvq_bq2_geom* g) {
+  if (!g) return fail(KVQ_ERR_NULL, "geometry is NULL");
+  if (g->batch < 1 || g->n_kv_heads < 1 || g->n_q_heads < 1)
+    return fail(KVQ_ERR_GEOM, "batch and head counts must be >= 1");
+  if (g->n_q_heads % g->n_kv_heads != 0)
+    return fail(KVQ_ERR_GEOM, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                g->n_q_heads, g->n_kv_heads);
+  const int gq = g->n_q_heads / g->n_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4)
+    return fail(KVQ_ERR_GEOM, "query heads per KV head must be 1, 2 or 4 (got %d)", gq);
+  if (g->capacity < 32 || g->capacity % 32 != 0 || g->capacity > (1 << 24))
+    return fail(KVQ_ERR_GEOM, "capacity (%d) must be a positive multiple of 32, <= 2^24",
+                g->capacity);
+  return KVQ_OK;
+}
+
+int check_bq2_cache(const kvq_bq2_cache* c) {
+  if (!c) return fail(KVQ_ERR_NULL, "cache is NULL");
+  const void* p[6] = {c->k_codes, c->v_codes, c->k_meta, c->v_meta, c->k_sink, c->v_sink};
+  static const char* names[6] = {"k_codes", "v_codes", "k_meta", "v_meta", "k_sink", "v_sink"};
+  for (int i = 0; i < 6; ++i) {
+    if (!p[i]) return fail(KVQ_ERR_NULL, "cache.%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(KVQ_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  return KVQ_OK;
+}
+
+int bq2_workers_for(const kvq_bq2_geom* g, int32_t* n_workers) {
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != KVQ_OK) return st;
+  int w = 0;
+  hipError_t e = kvq::bq2_decode_workers(kvq::to_geom(*g), cus, &w);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query");
+  *n_workers = w;
+  return KVQ_OK;
+}
+
+int check_bq2_max_len(const kvq_bq2_geom* g, int32_t max_seq_len) {
+  if (max_seq_len < 1 || max_seq_len > g->capacity)
+    return fail(KVQ_ERR_RANGE, "max_seq_len (%d) must be in [1, capacity=%d]", max_seq_len,
+                g->capacity);
+  return KVQ_OK;
+}
+
+// Partials: at most n_workers + B*Hkv, each [Hq/Hkv][64 + 4] floats.
+size_t bq2_workspace_need(const kvq_bq2_geom* g, int32_t n_workers) {
+  const size_t gq = g->n_q_heads / g->n_kv_heads;
+  return ((size_t)n_workers + (size_t)g->batch * g->n_kv_heads) * gq *
+         (KVQ_BQ2_HEAD_DIM + 4) * sizeof(float);
+}
+
+int bq2_decode_setup(const kvq_bq2_geom* geom, const uint16_t* q, const kvq_bq2_cache* cache,
+                     const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                     void* workspace, size_t workspace_bytes, uint16_t* out,
+                     kvq::Bq2Launch* L) {
+  int st = check_bq2_geom(geom);
+  if (st != KVQ_OK) return st;
+  if ((st = check_bq2_cache(cache)) != KVQ_OK) return st;
+  if ((st = check_ptr(q, "q")) != KVQ_OK) return st;
+  if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
+  if ((st = check_ptr(out, "out")) != KVQ_OK) return st;
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_huge_valf() ||
+      sm_scale == -__builtin_huge_valf())
+    return fail(KVQ_ERR_RANGE, "sm_scale must be finite");
+  if ((st = check_bq2_max_len(geom, max_seq_len)) != KVQ_OK) return st;
+  int32_t n_workers = 0;
+  if ((st = bq2_workers_for(geom, &n_workers)) != KVQ_OK) return st;
+  const size_t need = bq2_workspace_need(geom, n_workers);
+  if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(workspace)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  L->g = kvq::to_geom(*geom);
+  L->q = q;
+  L->cache = *cache;
+  L->seq_lens = seq_lens;
+  L->max_seq_len = max_seq_len;
+  L->n_workers = n_workers;
+  // the sink chunk: 4 fp16 positions (K and V: 1 KB) against a packed chunk's
+  // 32 x 40 bytes, i.e. one work unit
+  L->rw = 1;
+  L->scale_log2 = sm_scale * 1.4426950408889634f;
+  L->ws = static_cast<float*>(workspace);
+  L->out = out;
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +470,134 @@ int kvq_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_cache* ca
   if (st != KVQ_OK) return st;
   return kvq_decode_combine(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
                             workspace_bytes, out, stream);
+}
+
+int kvq_bq2_validate_geom(const kvq_bq2_geom* geom) {
+  try {
+    return check_bq2_geom(geom);
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_cache_bytes(const kvq_bq2_geom* geom, size_t out[6]) {
+  int st = check_bq2_geom(geom);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
+  const size_t units = (size_t)geom->batch * geom->n_kv_heads, C = geom->capacity;
+  out[0] = units * (C / 32) * 64 * 2 * 4;         // k_codes
+  out[1] = units * (C / 32) * 64 * 2 * 4;         // v_codes
+  out[2] = units * C * 2 * 2;                     // k_meta
+  out[3] = units * C * 2 * 2;                     // v_meta
+  out[4] = units * KVQ_BQ2_SINKS * KVQ_BQ2_HEAD_DIM * 2;  // k_sink
+  out[5] = units * KVQ_BQ2_SINKS * KVQ_BQ2_HEAD_DIM * 2;  // v_sink
+  return KVQ_OK;
+}
+
+int kvq_bq2_decode_workers(const kvq_bq2_geom* geom, int32_t* n_workers) {
+  try {
+    int st = check_bq2_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!n_workers) return fail(KVQ_ERR_NULL, "n_workers is NULL");
+    return bq2_workers_for(geom, n_workers);
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_decode_workspace_bytes(const kvq_bq2_geom* geom, int32_t max_seq_len,
+                                   size_t* bytes) {
+  try {
+    int st = check_bq2_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+    if ((st = check_bq2_max_len(geom, max_seq_len)) != KVQ_OK) return st;
+    int32_t nw = 0;
+    if ((st = bq2_workers_for(geom, &nw)) != KVQ_OK) return st;
+    *bytes = bq2_workspace_need(geom, nw);
+    return KVQ_OK;
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_prefill(const kvq_bq2_geom* geom, const uint16_t* k, const uint16_t* v, int32_t n,
+                    const kvq_bq2_cache* cache, void* stream) {
+  try {
+    int st = check_bq2_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_bq2_cache(cache)) != KVQ_OK) return st;
+    if (n < 0 || n > geom->capacity)
+      return fail(KVQ_ERR_RANGE, "n=%d must be in [0, capacity=%d]", n, geom->capacity);
+    if (n == 0) return KVQ_OK;
+    if ((st = check_ptr(k, "k")) != KVQ_OK) return st;
+    if ((st = check_ptr(v, "v")) != KVQ_OK) return st;
+    hipError_t e = kvq::launch_bq2_prefill(kvq::to_geom(*geom), k, v, n, *cache,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "bq2 prefill launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_append(const kvq_bq2_geom* geom, const uint16_t* k_new, const uint16_t* v_new,
+                   const int32_t* seq_lens, const kvq_bq2_cache* cache, void* stream) {
+  try {
+    int st = check_bq2_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_bq2_cache(cache)) != KVQ_OK) return st;
+    if ((st = check_ptr(k_new, "k_new")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_new, "v_new")) != KVQ_OK) return st;
+    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
+    hipError_t e = kvq::launch_bq2_append(kvq::to_geom(*geom), k_new, v_new, seq_lens, *cache,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "bq2 append launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_decode_partial(const kvq_bq2_geom* geom, const uint16_t* q,
+                           const kvq_bq2_cache* cache, const int32_t* seq_lens,
+                           int32_t max_seq_len, float sm_scale, void* workspace,
+                           size_t workspace_bytes, uint16_t* out, void* stream) {
+  try {
+    kvq::Bq2Launch L;
+    int st = bq2_decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                              workspace_bytes, out, &L);
+    if (st != KVQ_OK) return st;
+    hipError_t e = kvq::launch_bq2_decode_partial(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "bq2 decode_partial launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_decode_combine(const kvq_bq2_geom* geom, const uint16_t* q,
+                           const kvq_bq2_cache* cache, const int32_t* seq_lens,
+                           int32_t max_seq_len, float sm_scale, const void* workspace,
+                           size_t workspace_bytes, uint16_t* out, void* stream) {
+  try {
+    kvq::Bq2Launch L;
+    int st = bq2_decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale,
+                              const_cast<void*>(workspace), workspace_bytes, out, &L);
+    if (st != KVQ_OK) return st;
+    hipError_t e = kvq::launch_bq2_decode_combine(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "bq2 decode_combine launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_bq2_decode_attn(const kvq_bq2_geom* geom, const uint16_t* q,
+                        const kvq_bq2_cache* cache, const int32_t* seq_lens,
+                        int32_t max_seq_len, float sm_scale, void* workspace,
+                        size_t workspace_bytes, uint16_t* out, void* stream) {
+  int st = kvq_bq2_decode_partial(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                                  workspace_bytes, out, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_bq2_decode_combine(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                                workspace_bytes, out, stream);
 }
 
 }  // extern "C"

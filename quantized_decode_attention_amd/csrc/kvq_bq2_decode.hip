@@ -1,0 +1,538 @@
+// kvq_bq2_decode.hip — single-token decode attention over the rotated
+// per-token 2-bit cache (KV1's BQ2_0; layout in kvq_bq2.h) on gfx950.
+//
+// [KV1] "Quantization Format: KV1.cpp BQ2_0": the cache holds H k and H v
+// (H the normalized Sylvester Hadamard matrix, H H = I), quantized per
+// position as code * d + m over the 64 channels, positions 0..3 in fp16;
+// scores are unchanged by the rotation and the output is rotated back.  For
+// query head h, with qH = H q in log2 units (sm_scale * log2 e folded in):
+//   s_t = d_t (qH . code_t) + m_t sum_c qH_c
+//   o   = sum_t (p_t dV_t) code_t + (sum_t p_t mV_t) (1, ..., 1)
+//   out = H o / sum_t p_t
+// Both contractions run on v_mfma_f32_16x16x32_f16 with the codes fed as fp16
+// subnormals, as in kvq_decode.hip: the key side multiplies the codes by the
+// rotated query and applies each position's d_t, m_t to the finished score;
+// the value side multiplies the codes by p_t dV_t.
+//
+// Precision of the key side.  The two terms of s_t are large and nearly
+// cancel (the dequantized keys are about zero-mean), so the code product must
+// be accurate to ~2^-20 of its products' magnitude.  The matrix core sums the
+// products of one column exactly only while they span no more than about 20
+// bits (mantissa width plus exponent spread); wider spans lose the low bits of
+// the smallest products, the same bits for every position, which shifts a
+// head's scores uniformly.  So each head's query operand uses four columns:
+// part 0 holds the components within 2^kBigSpan of the head's largest (11-bit
+// values, 2-bit codes: exact sums), part 1 the rest and part 0's remainders,
+// part 2 what part 1 leaves, part 3 zero; a quad of DPP adds recombines them.
+// The value side has the same limit (softmax weights span many binades), so
+// its four columns per head hold the hi and lo parts of the large weights
+// (p >= 2^-kBigSpanV, whose products span few bits) and of the small ones.  The sinks
+// take one more MFMA step on their fp16 vectors.  The work decomposition and
+// the combine (which rotates the merged output back) are shared with the other
+// format (kvq_device.h).
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kD = KVQ_BQ2_HEAD_DIM;
+constexpr int kSinks = KVQ_BQ2_SINKS;
+constexpr float kValEvenB = kValEven<2>, kValOddB = kValOdd<2>;
+constexpr int kQTop = 14;     // the query operand's largest component is below 2^kQTop
+constexpr int kBigSpan = 7;   // part 0 holds components above 2^(kQTop - kBigSpan)
+constexpr int kBigSpanV = 6;  // value weights p >= 2^-kBigSpanV go to the large columns
+
+// Work of a sequence of n positions: the 32-position chunks holding quantized
+// positions (chunk 0 counts when n > 4), one work unit each, then the sink
+// chunk, weighted rw (its fp16 bytes over a packed chunk's).
+__device__ __forceinline__ SeqWork bq2_work_of(const Bq2Launch& L, int n) {
+  SeqWork sw{0, 0, 0, 0};
+  if (n <= 0 || n > L.g.C || n > L.max_seq_len) return sw;
+  sw.n = n;
+  sw.nq = n > kSinks ? (n + kChunk - 1) / kChunk : 0;
+  sw.nr = 1;
+  sw.w = sw.nq + L.rw;
+  return sw;
+}
+
+struct Bq2Work {
+  using Launch = Bq2Launch;
+  static constexpr bool kRotateOut = true;
+  static __device__ __forceinline__ SeqWork work_of(const Bq2Launch& L, int n) {
+    return bq2_work_of(L, n);
+  }
+};
+
+// A lane's share of one 32-position chunk.
+struct Bq2Raw {
+  uint32_t kw[2];  // key code words of score tiles 0, 1
+  uint32_t vw[2];  // value code words (tiles 2m, 2m + 1 in word m)
+  uint4 km[2];     // key (d, m) of positions 8 lg + 4u + q: km[u], component q
+  uint4 vm[2];     // value (d, m) of positions 8 lg + j: vm[j / 4], component j % 4
+};
+
+__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <int GQ>
+struct Bq2Wave {
+  static constexpr int SL = 16 / GQ;  // MFMA columns per head
+  static_assert(SL >= 4, "the key-side operand needs four columns per head");
+
+  const uint32_t* kcodes;
+  const uint32_t* vcodes;
+  const uint32_t* kmeta;
+  const uint32_t* vmeta;
+  int lane, col, lg, hcol, part, kpart;
+  bool vbig;     // this lane's value columns hold the large weights
+  float m1;      // -1 in a register
+  float mpart;   // 0 on hi lanes, -1 on lo lanes: selects the part of a split
+  float qbig;    // 2^(kQTop - kBigSpan): query components at or above go to key part 0
+  float kscale;  // 2^(E - kQTop + 24): code accumulation to log2 units (this lane's head)
+  float sumq;    // sum_c qH_c of this lane's head (log2 units)
+  float qexp;    // 2^(E - kQTop)
+  f4 oacc[4];
+  float m_run, m_even, m_odd;
+  float l_run, l_odd;
+  float bias, bias_odd;  // value-min terms of the two weight classes
+  uint32_t bq[2][4];
+
+  __device__ void init(int lane_) {
+    lane = lane_;
+    col = lane & 15;
+    lg = lane >> 4;
+    hcol = col / SL;
+    part = (col % SL) & 1;
+    kpart = (col % SL) & 3;
+    vbig = kpart < 2;
+    m1 = opaque_m1();
+    qbig = ldexpf(1.0f, kQTop - kBigSpan);
+    mpart = part ? m1 : 0.0f;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
+    m_run = m_even = m_odd = kNegInf;
+    l_run = l_odd = 0.0f;
+    bias = bias_odd = 0.0f;
+  }
+
+  // (a, b) -> the fp16 pair of this lane's part: hi = rtz(a, b), lo = the
+  // remainders (exact fp32 differences).
+  __device__ __forceinline__ uint32_t part_of(float a, float b) const {
+    const uint32_t hi = pk_rtz(a, b);
+    return pk_rtz(__builtin_fmaf(lo_half(hi), mpart, a), __builtin_fmaf(hi_half(hi), mpart, b));
+  }
+
+  // Key-side operand pair of this lane's part (qa, qb: query components; f:
+  // the pair's positional factor): part 0 = fp16 of the large components,
+  // part 1 = fp16 of what remains, part 2 = fp16 of what remains then, part 3
+  // = 0.  Every remainder is an exact fp32 difference.
+  __device__ __forceinline__ uint32_t key_part(float qa, float qb, float f) const {
+    const float a = qa * f, b = qb * f;
+    const uint32_t h0 = pk_rtz(fabsf(qa) >= qbig ? a : 0.0f, fabsf(qb) >= qbig ? b : 0.0f);
+    const float ra = a - lo_half(h0), rb = b - hi_half(h0);
+    const uint32_t h1 = pk_rtz(ra, rb);
+    const uint32_t h2 = pk_rtz(ra - lo_half(h1), rb - hi_half(h1));
+    return kpart == 0 ? h0 : kpart == 1 ? h1 : kpart == 2 ? h2 : 0u;
+  }
+  // Value-side operand pair of this lane's column (x: weights p * dV; p: the
+  // weights; thr: the class's large-weight threshold): the large or the small
+  // weights only, hi or lo part.
+  __device__ __forceinline__ uint32_t value_part(float xa, float xb, float pa, float pb,
+                                                 float thr) const {
+    return part_of((pa >= thr) == vbig ? xa : 0.0f, (pb >= thr) == vbig ? xb : 0.0f);
+  }
+  // Sum of a result over the four columns of a part set (a quad of lanes).
+  __device__ __forceinline__ float key_sum(float x) const {
+    x += dpp<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+    x += dpp<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+    return x;
+  }
+
+  __device__ __forceinline__ void load(int ch, Bq2Raw& r) const {
+    const uint2 k2 = *reinterpret_cast<const uint2*>(kcodes + ch * 128 + 2 * lane);
+    const uint2 v2 = *reinterpret_cast<const uint2*>(vcodes + ch * 128 + 2 * lane);
+    r.kw[0] = k2.x;
+    r.kw[1] = k2.y;
+    r.vw[0] = v2.x;
+    r.vw[1] = v2.y;
+    const uint4* km = reinterpret_cast<const uint4*>(kmeta + ch * kChunk + 8 * lg);
+    const uint4* vm = reinterpret_cast<const uint4*>(vmeta + ch * kChunk + 8 * lg);
+    r.km[0] = km[0];
+    r.km[1] = km[1];
+    r.vm[0] = vm[0];
+    r.vm[1] = vm[1];
+  }
+
+  template <bool kPacked>
+  __device__ __forceinline__ void softmax(const float (&s)[2][4], float (&p)[2][4]) {
+    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    if (__any(cm > m_run)) {
+      cm = xor_max(cm, 16);
+      cm = xor_max(cm, 32);
+      const float m_new = fmaxf(m_run, cm);
+      const float a = exp2_hw(m_run - m_new);
+      m_run = m_new;
+      m_even = kPacked ? m_new - kValEvenLog2<2> : m_new;
+      m_odd = kPacked ? m_new - kValOddLog2 : m_new;
+      l_run *= a;
+      l_odd *= a;
+      bias *= a;
+      bias_odd *= a;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) oacc[n] *= a;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p[u][q] = exp2_hw(s[u][q] - (q < 2 ? m_even : m_odd));
+        if (q < 2 || !kPacked)
+          l_run += p[u][q];
+        else
+          l_odd += p[u][q];
+      }
+  }
+
+  // One chunk of quantized positions.  edge: chunk 0 (positions 0..3 are the
+  // sinks) or a chunk reaching past n; its positions outside [4, n) are
+  // masked (score -inf, value meta 0, so stale memory never reaches a sum).
+  __device__ __forceinline__ void process(int ch, Bq2Raw r, int n) {
+    const bool edge = ch == 0 || (ch + 1) * kChunk > n;
+    if (edge) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t0 = ch * kChunk + 8 * lg + 4 * u;
+        r.vm[u].x = (t0 + 0 >= kSinks && t0 + 0 < n) ? r.vm[u].x : 0u;
+        r.vm[u].y = (t0 + 1 >= kSinks && t0 + 1 < n) ? r.vm[u].y : 0u;
+        r.vm[u].z = (t0 + 2 >= kSinks && t0 + 2 < n) ? r.vm[u].z : 0u;
+        r.vm[u].w = (t0 + 3 >= kSinks && t0 + 3 < n) ? r.vm[u].w : 0u;
+      }
+    }
+    float s[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t w[1] = {r.kw[u]};
+      uint32_t a[2][4];
+      unpack_keys<kD, 2>(w, a);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma(a[0], bq[0], acc);
+      acc = mfma(a[1], bq[1], acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x = key_sum(acc[q]);
+        const uint32_t dm = comp(r.km[u], q);
+        s[u][q] = mul_lo(x * kscale, dm, mul_hi(sumq, dm));
+      }
+    }
+    if (edge) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = ch * kChunk + 8 * lg + 4 * u + q;
+          s[u][q] = (t >= kSinks && t < n) ? s[u][q] : kNegInf;
+        }
+    }
+    float p[2][4];
+    softmax<true>(s, p);
+    // B operand: element j = position 8 lg + j, weight p_j dV_j; pair e holds
+    // j = 2e, 2e + 1 (odd e: the odd weight class)
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ja = 2 * e, jb = 2 * e + 1;
+      const float pa = p[ja >> 2][ja & 3], pb = p[jb >> 2][jb & 3];
+      const uint32_t wa = comp(r.vm[ja >> 2], ja & 3), wb = comp(r.vm[jb >> 2], jb & 3);
+      // odd pairs carry the odd class's factor 1/4 in p
+      const float thr = (e & 1) ? ldexpf(kValOddB, -kBigSpanV) : ldexpf(1.0f, -kBigSpanV);
+      b[e] = value_part(mul_lo(pa, wa), mul_lo(pb, wb), pa, pb, thr);
+      float& bacc = (e & 1) ? bias_odd : bias;
+      bacc = mul_hi(pa, wa, bacc);
+      bacc = mul_hi(pb, wb, bacc);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // tile 2m + h: pair e of token 8 lg + 2e (+1) at bits 8h + 4(e/2) + 2(e%2)
+        const uint32_t x = r.vw[m] >> (8 * h);
+        uint32_t a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a[e] = (x >> (4 * (e >> 1))) & ((e & 1) ? 0x000C000Cu : 0x00030003u);
+        oacc[2 * m + h] = mfma(a, b, oacc[2 * m + h]);
+      }
+  }
+
+  // Packed accumulation to real scale (codes were c * 2^-24, odd pairs carry
+  // their class factor) with the value-min term added once per column pair.
+  __device__ __forceinline__ void to_real() {
+    float bt = __builtin_fmaf(bias_odd, 1.0f / kValOddB, bias * (1.0f / kValEvenB));
+    bt = xor_sum(xor_sum(bt, 16), 32);
+    if (kpart != 0) bt = 0.0f;  // once per head: the four columns are summed
+    constexpr float oscale = 16777216.0f / kValEvenB;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], oscale, bt);
+    l_run = __builtin_fmaf(l_odd, 1.0f / kValOddB, l_run * (1.0f / kValEvenB));
+    l_odd = 0.0f;
+    bias = bias_odd = 0.0f;
+    m_even = m_odd = m_run;
+  }
+
+  // The sinks (positions 0 .. ns-1, ns <= 4) from their fp16 vectors: key
+  // tile 0 rows 0..3 are positions 0..3; the query fragments are rebuilt in
+  // natural channel order (element j of lane group g, k-chunk kc = channel
+  // 32 kc + 8 g + j) from qfs (qH * 2^(kQTop - E)).
+  __device__ __forceinline__ void process_sinks(const uint16_t* ksink, const uint16_t* vsink,
+                                                int ns, const float* qfs) {
+    uint32_t bn[2][4];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * kD + 32 * kc + 8 * lg);
+      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * kD + 32 * kc + 8 * lg + 4);
+      bn[kc][0] = key_part(qa.x, qa.y, 1.0f);
+      bn[kc][1] = key_part(qa.z, qa.w, 1.0f);
+      bn[kc][2] = key_part(qb.x, qb.y, 1.0f);
+      bn[kc][3] = key_part(qb.z, qb.w, 1.0f);
+    }
+    const int i = lane & 15;
+    uint32_t a[2][4];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (i < ns) v = *reinterpret_cast<const uint4*>(ksink + i * kD + 32 * kc + 8 * lg);
+      a[kc][0] = v.x;
+      a[kc][1] = v.y;
+      a[kc][2] = v.z;
+      a[kc][3] = v.w;
+    }
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma(a[0], bn[0], acc);
+    acc = mfma(a[1], bn[1], acc);
+    float s[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // tile 0 row 4 lg + q is position 8 lg + q
+      const float x = key_sum(acc[q]) * qexp;
+      s[0][q] = (lg == 0 && q < ns) ? x : kNegInf;
+      s[1][q] = kNegInf;
+    }
+    float p[2][4];
+    softmax<false>(s, p);
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ja = 2 * e, jb = 2 * e + 1;
+      const float pa = p[ja >> 2][ja & 3], pb = p[jb >> 2][jb & 3];
+      b[e] = value_part(pa, pb, pa, pb, ldexpf(1.0f, -kBigSpanV));
+    }
+    // value tile n: element j of lane group 0 is position j of channel 16n + i
+    const uint32_t keep0 = (ns > 0 ? 0x0000FFFFu : 0u) | (ns > 1 ? 0xFFFF0000u : 0u);
+    const uint32_t keep1 = (ns > 2 ? 0x0000FFFFu : 0u) | (ns > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      uint2 v = make_uint2(0u, 0u);
+      if (lg == 0) v = *reinterpret_cast<const uint2*>(vsink + (16 * n + i) * kSinks);
+      uint32_t av[4] = {v.x & keep0, v.y & keep1, 0u, 0u};
+      oacc[n] = mfma(av, b, oacc[n]);
+    }
+  }
+};
+
+constexpr int kDP = kD + kPartPad;
+
+// Unit (b, hkv), work range [x0, x1) -> partial p.
+template <int GQ>
+__device__ void bq2_segment(const Bq2Launch& L, int b, int hkv, const SeqWork& sw, int xu,
+                            int x0, int x1, int p, float* qfs, int lane) {
+  const SegRange r = seg_range(L, sw, xu, x0, x1);
+  float* part_base = L.ws + (int64_t)p * GQ * kDP;
+  if (r.pc0 >= r.pc1 && r.rk0 >= r.rk1) {  // only part of the sink chunk's weight
+    for (int i = lane; i < GQ * kDP; i += 64) part_base[i] = (i % kDP == kD) ? kNegInf : 0.0f;
+    return;
+  }
+  const Bq2Geom& g = L.g;
+  const int64_t unit = (int64_t)b * g.Hkv + hkv;
+  Bq2Wave<GQ> w;
+  w.init(lane);
+  w.kcodes = L.cache.k_codes + unit * (g.C / kChunk) * 128;
+  w.vcodes = L.cache.v_codes + unit * (g.C / kChunk) * 128;
+  w.kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) + unit * g.C;
+  w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) + unit * g.C;
+  Bq2Raw ra, rb;
+  if (r.pc0 < r.pc1) w.load(r.pc0, ra);  // before the query, to overlap its latency
+
+  // rotated query of the unit's GQ heads: qH = H q (in log2 units), per-head
+  // exponent E with max |qH| < 2^E, qfs = qH * 2^(kQTop - E): the largest
+  // component sits just below 2^kQTop, so the lo parts of the hi/lo split stay
+  // normal fp16 numbers for every component above 2^(kQTop - 25) of the largest
+  // (no key scale is folded into the query here, so fp16 has that headroom)
+  const uint16_t* qg = L.q + ((int64_t)b * g.Hq + hkv * GQ) * kD;
+  int e_mine = 0;
+  float sum_mine = 0.0f;
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float x = h2f(qg[h * kD + lane]);
+#pragma unroll
+    for (int d = 1; d < kD; d <<= 1) {
+      const float y = __shfl_xor(x, d, 64);
+      x = (lane & d) ? (y - x) : (x + y);
+    }
+    x *= 0.125f * L.scale_log2;
+    float mx = fabsf(x), sm = x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      sm += __shfl_xor(sm, off, 64);
+    }
+    int e = 0;
+    if (mx > 0.0f) (void)frexpf(mx, &e);
+    qfs[h * kD + lane] = ldexpf(x, kQTop - e);
+    if (w.hcol == h) {
+      e_mine = e;
+      sum_mine = sm;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  w.kscale = ldexpf(1.0f, e_mine - kQTop + 24 - kKeyAccLog2<2>);
+  w.qexp = ldexpf(1.0f, e_mine - kQTop);
+  w.sumq = sum_mine;
+  // key-side fragments in the key words' channel order: pair v of k-chunk kc
+  // = channels 16 lg + 4 kc + v and + 8; odd pairs come out of their mask 4x
+  // larger, so their query factor is 1/4
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c0 = 16 * w.lg + 4 * kc + v;
+      const float f = (v & 1) ? kKeyOddQ<2> : kKeyEvenQ<2>;
+      w.bq[kc][v] = w.key_part(qfs[w.hcol * kD + c0], qfs[w.hcol * kD + c0 + 8], f);
+    }
+
+  if (r.pc0 < r.pc1) {
+    const int last = r.pc1 - 1;
+    int ch = r.pc0;
+    for (; ch < last; ch += 2) {  // ra holds chunk ch on entry
+      w.load(ch + 1, rb);
+      w.process(ch, ra, sw.n);
+      w.load(min(ch + 2, last), ra);
+      w.process(ch + 1, rb, sw.n);
+    }
+    if (ch == last) w.process(ch, ra, sw.n);
+  }
+  w.to_real();
+  if (r.rk0 < r.rk1)
+    w.process_sinks(L.cache.k_sink + unit * kSinks * kD, L.cache.v_sink + unit * kD * kSinks,
+                    min(sw.n, kSinks), qfs);
+
+  // partial: the four columns summed, max, sum over the four lane groups
+  float l = w.l_run;
+  l = xor_sum(xor_sum(l, 16), 32);
+  float* part = part_base + w.hcol * kDP;
+  const bool writer = (w.col % Bq2Wave<GQ>::SL) == 0;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    f4 o = w.oacc[n];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = w.key_sum(o[q]);
+    if (writer)
+      *reinterpret_cast<float4*>(part + 16 * n + 4 * w.lg) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+  if (writer && w.lg == 0) {
+    part[kD] = w.m_run;
+    part[kD + 1] = l;
+  }
+  // the next segment of this wave rewrites qfs
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave per workgroup; grid = the number of worker waves.
+template <int GQ>
+__global__ __launch_bounds__(64) void bq2_partial_kernel(Bq2Launch L) {
+  __shared__ __attribute__((aligned(16))) float qfs[GQ * kD];
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x, nw = gridDim.x;
+  const BatchWork bw = batch_work<Bq2Work>(L, lane);
+  const int total = bw.total;
+  const int cpw = (total + nw - 1) / nw;
+  const int x0 = w * cpw;
+  const int x1 = min(total, x0 + cpw);
+  int x = x0;
+  while (x < x1) {
+    int b, base;
+    wave_find_seq<Bq2Work>(L, bw, lane, x, b, base);
+    b = __builtin_amdgcn_readfirstlane(b);
+    base = __builtin_amdgcn_readfirstlane(base);
+    const SeqWork sw = bq2_work_of(L, L.seq_lens[b]);
+    const int hkv = (x - base) / sw.w;
+    const int xu = base + hkv * sw.w;
+    bq2_segment<GQ>(L, b, hkv, sw, xu, x0, x1, w + b * L.g.Hkv + hkv, qfs, lane);
+    x = xu + sw.w;
+  }
+}
+
+template <int GQ>
+hipError_t workers_of(int cus, int* out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return hipSuccess;
+  }
+  int nb = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, bq2_partial_kernel<GQ>, 64, 0);
+  if (e != hipSuccess) return e;
+  if (nb < 1) nb = 1;
+  const int w = nb * cus;
+  if (dev >= 0 && dev < 64) cache[dev] = w;
+  *out = w;
+  return hipSuccess;
+}
+
+// op 0: launch the partial kernel; 1: its worker count; 2: launch the combine.
+template <int GQ>
+hipError_t run(const Bq2Launch& L, int op, int cus, int* workers, hipStream_t st) {
+  if (op == 1) return workers_of<GQ>(cus, workers);
+  if (op == 0)
+    bq2_partial_kernel<GQ><<<dim3(L.n_workers), 64, 0, st>>>(L);
+  else
+    decode_combine_kernel<Bq2Work, kD, GQ><<<dim3(L.g.Hkv, L.g.B), kThreads, 0, st>>>(L);
+  return hipGetLastError();
+}
+
+hipError_t dispatch(const Bq2Launch& L, int op, int cus, int* workers, hipStream_t st) {
+  switch (L.g.Hq / L.g.Hkv) {
+    case 1: return run<1>(L, op, cus, workers, st);
+    case 2: return run<2>(L, op, cus, workers, st);
+    case 4: return run<4>(L, op, cus, workers, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t bq2_decode_workers(const Bq2Geom& g, int cus, int* workers) {
+  Bq2Launch L{};
+  L.g = g;
+  return dispatch(L, 1, cus, workers, nullptr);
+}
+
+hipError_t launch_bq2_decode_partial(const Bq2Launch& L, hipStream_t st) {
+  return dispatch(L, 0, 0, nullptr, st);
+}
+
+hipError_t launch_bq2_decode_combine(const Bq2Launch& L, hipStream_t st) {
+  return dispatch(L, 2, 0, nullptr, st);
+}
+
+}  // namespace kvq

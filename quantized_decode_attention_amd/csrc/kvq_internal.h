@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/kvq.h"
+#include "../../include/kvq_bq2.h"
 
 namespace kvq {
 
@@ -70,5 +71,38 @@ struct DecodeLaunch {
 hipError_t decode_workers(const Geom& g, int cus, int* workers);
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st);
+
+// ---- rotated per-token 2-bit format (kvq_bq2.h) ---------------------------
+struct Bq2Geom {
+  int B, Hq, Hkv, C;
+};
+
+inline Bq2Geom to_geom(const kvq_bq2_geom& g) {
+  return Bq2Geom{g.batch, g.n_q_heads, g.n_kv_heads, g.capacity};
+}
+
+// Positions [0, n) of every unit from rows k, v [B][Hkv][n][64].
+hipError_t launch_bq2_prefill(const Bq2Geom& g, const uint16_t* k, const uint16_t* v,
+                              int32_t n, const kvq_bq2_cache& cache, hipStream_t st);
+// One position per sequence (seq_lens[b] = positions held before it).
+hipError_t launch_bq2_append(const Bq2Geom& g, const uint16_t* k_new, const uint16_t* v_new,
+                             const int32_t* seq_lens, const kvq_bq2_cache& cache,
+                             hipStream_t st);
+
+struct Bq2Launch {
+  Bq2Geom g;
+  const uint16_t* q;
+  kvq_bq2_cache cache;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t n_workers;  // worker waves of the partial kernel
+  int32_t rw;         // work units of the sink chunk
+  float scale_log2;   // sm_scale * log2(e)
+  float* ws;          // partials [n_workers + B*Hkv][Hq/Hkv][64 + 4]
+  uint16_t* out;      // [B][Hq][64]
+};
+hipError_t bq2_decode_workers(const Bq2Geom& g, int cus, int* workers);
+hipError_t launch_bq2_decode_partial(const Bq2Launch& L, hipStream_t st);
+hipError_t launch_bq2_decode_combine(const Bq2Launch& L, hipStream_t st);
 
 }  // namespace kvq

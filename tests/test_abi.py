@@ -17,12 +17,13 @@ from quantized_decode_attention_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
+HEADER_BQ2 = os.path.join(ROOT, "include", "kvq_bq2.h")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -32,6 +33,39 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTS) == names
+
+
+def test_exports_every_declared_bq2_symbol():
+    L = kvq.lib()
+    names = _declared(HEADER_BQ2)
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTS_BQ2) == names
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("n_kv_heads", 0), ("n_q_heads", 12), ("n_q_heads", 64), ("n_q_heads", 128),
+    ("capacity", 0), ("capacity", 100), ("capacity", 1 << 25),
+])
+def test_bq2_geometry_validation(field, value):
+    good = dict(batch=2, n_q_heads=32, n_kv_heads=8, capacity=1024)
+    kvq.kvq_bq2_validate_geom(kvq.Bq2Geom(**good))
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_bq2_validate_geom(kvq.Bq2Geom(**{**good, field: value}))
+    assert e.value.status == -2
+
+
+def test_bq2_cache_bytes_and_memory_table():
+    """Per position and KV head: two 20-byte BQ2_0 blocks ([KV1] Quantization
+    Format); 6 layers x 8 KV heads at 32K context give the card's 60 MiB (plus
+    the sinks, 4 fp16 positions per head)."""
+    g = kvq.Bq2Geom(1, 32, 8, 32768)
+    kc, vc, km, vm, ks, vs = kvq.kvq_bq2_cache_bytes(g)
+    assert kc == vc == 8 * 32768 * 16
+    assert km == vm == 8 * 32768 * 4
+    assert ks == vs == 8 * 4 * 64 * 2
+    assert 6 * (kc + vc + km + vm) == 60 * 2**20
 
 
 def test_versions_and_status_strings():
