@@ -11,7 +11,9 @@ one step to the next: the bytes come from HBM, as in a real multi-layer model.
 Default workload: the Llama-3-8B-shaped GQA layer (32 query / 8 KV heads,
 head_dim 128, batch 32, context 8192, 2-bit keys / 4-bit values, G = 32,
 R = 128).  512 steps = 128 tokens per layer, so every layer does exactly one
-residual flush inside the timed region.
+residual flush inside the timed region.  --config 6 runs the KV1-shaped layer
+in the rotated per-token 2-bit format (kvq_bq2_append + kvq_bq2_decode_attn,
+batch 16, context 32768).
 
 Prints one JSON line: effective HBM GB/s of the whole step (algorithmic bytes /
 time), tokens/s, the roofline of the dominant kernel (decode partial: HIP
@@ -41,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=512)
     p.add_argument("--warmup", type=int, default=32)
-    p.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
+    p.add_argument("--config", type=int, default=3, help="workload 1..6 (default 3)")
     p.add_argument("--layers", type=int, default=4, help="rotating layer caches")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -51,23 +53,30 @@ def parse():
     return p.parse_args()
 
 
-def source_hash() -> str:
+# kernel sources whose change invalidates a committed traffic reading
+KERNEL_SOURCES = {
+    "decode_partial": ("kvq_decode.hip", "kvq_device.h", "kvq_quant.hip", "kvq_internal.h"),
+    "bq2_partial": ("kvq_bq2_decode.hip", "kvq_device.h", "kvq_bq2_quant.hip", "kvq_internal.h"),
+}
+
+
+def source_hash(kernel: str = "decode_partial") -> str:
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_quant.hip", "kvq_internal.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "quantized_decode_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM traffic per decode-partial launch from committed rocprofv3 --pmc
+def load_traffic(workload: str, kernel: str = "decode_partial"):
+    """HBM traffic per partial-kernel launch from committed rocprofv3 --pmc
     summaries, if they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_partial_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != source_hash():
+    if d.get("source_hash") != source_hash(kernel):
         return None
     return d.get("bytes_per_launch")
 
@@ -114,6 +123,149 @@ def cpu_baseline(w, target_seconds: float):
     }
 
 
+def cpu_baseline_bq2(w, target_seconds: float):
+    """The oracle of the rotated format on a bounded sample: the first few
+    sequences, one decode step (append + attention) repeated until about
+    target_seconds have passed."""
+    import oracle
+    from quantized_decode_attention_amd import metrics, synth
+
+    bs = min(w.batch, 2)
+    n0 = w.context - 1
+    og = oracle.Bq2Geom(bs, w.n_q_heads, w.n_kv_heads, synth.capacity_for(w, 64))
+    oc = oracle.Bq2Cache(og)
+    oracle.bq2_prefill(og, oc, synth.keys(w, n0, batch=bs), synth.values(w, n0, batch=bs), n0)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    steps, nbytes, t_total = 0, 0.0, 0.0
+    lens = np.full(bs, n0, np.int32)
+    while t_total < target_seconds and steps < 1024:
+        kn, vn, q = synth.step_token(w, steps, batch=bs)
+        t0 = time.perf_counter()
+        oracle.bq2_append(og, oc, kn, vn, lens)
+        _ = oracle.bq2_decode_attn(og, oc, q, lens + 1, scale)
+        t_total += time.perf_counter() - t0
+        nbytes += metrics.bq2_decode_step_bytes(lens + 1, w.n_q_heads, w.n_kv_heads)
+        nbytes += metrics.bq2_append_bytes(bs, w.n_kv_heads)
+        lens += 1
+        steps += 1
+    return {
+        "value": round(nbytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(bs * steps / t_total, 3),
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"{bs} of {w.batch} sequences at context {w.context}, {steps} decode "
+                   f"steps (append + attention), {t_total:.1f} s"),
+    }
+
+
+def run_bq2(a, w, torch, kvq, metrics, synth):
+    """The rotated per-token 2-bit format: kvq_bq2_append then
+    kvq_bq2_decode_partial (timed per launch) and kvq_bq2_decode_combine."""
+    dev = torch.device("cuda:0")
+    L = a.layers
+    total_steps = a.warmup + a.steps
+    per_layer_tokens = -(-total_steps // L)
+    cap = synth.capacity_for(w, per_layer_tokens + 1)
+    g = kvq.Bq2Geom(w.batch, w.n_q_heads, w.n_kv_heads, cap)
+    start = np.full(w.batch, w.context - 1 - (a.warmup + L - 1) // L, np.int32)
+    n0 = int(start[0])
+    print(f"[bench] workload {w.name}: {L} layer caches, capacity {cap}, start len {n0}",
+          file=sys.stderr, flush=True)
+    caches = [kvq.Bq2Cache(g, dev) for _ in range(L)]
+    kd = torch.from_numpy(synth.keys(w, n0)).to(dev)
+    vd = torch.from_numpy(synth.values(w, n0)).to(dev)
+    for c in caches:
+        kvq.kvq_bq2_prefill(g, kd, vd, n0, c)
+    del kd, vd
+    torch.cuda.synchronize()
+    pool = [tuple(torch.from_numpy(x).to(dev) for x in synth.step_token(w, s)) for s in range(8)]
+    lens_host = np.zeros((total_steps, 2, w.batch), np.int32)
+    cur = [start.copy() for _ in range(L)]
+    for s in range(total_steps):
+        l = s % L
+        lens_host[s, 0] = cur[l]
+        lens_host[s, 1] = cur[l] + 1
+        cur[l] = cur[l] + 1
+    lens_dev = torch.from_numpy(lens_host).to(dev)
+    max_len = int(lens_host[:, 1].max())
+    ws = kvq.alloc_bq2_workspace(g, max_len, dev)
+    out = torch.empty((w.batch, w.n_q_heads, 64), dtype=torch.float16, device=dev)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    n_workers = kvq.kvq_bq2_decode_workers(g)
+    dec_bytes = [metrics.bq2_decode_step_bytes(lens_host[s, 1], w.n_q_heads, w.n_kv_heads)
+                 for s in range(total_steps)]
+    step_bytes = [d + metrics.bq2_append_bytes(w.batch, w.n_kv_heads) for d in dec_bytes]
+    stream = torch.cuda.current_stream()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+
+    def step(s, timed_idx=None):
+        kn, vn, q = pool[s % len(pool)]
+        c = caches[s % L]
+        kvq.kvq_bq2_append(g, kn, vn, lens_dev[s, 0], c, stream)
+        if timed_idx is not None:
+            ev_a[timed_idx].record(stream)
+        kvq.kvq_bq2_decode_partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+        if timed_idx is not None:
+            ev_b[timed_idx].record(stream)
+        kvq.kvq_bq2_decode_combine(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+
+    for s in range(a.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed = slice(a.warmup, a.warmup + a.steps)
+    gbs = float(np.sum(step_bytes[timed])) / elapsed / 1e9
+    part_avg_s = float(np.mean([ev_a[i].elapsed_time(ev_b[i]) for i in range(a.steps)])) / 1e3
+    dec_avg_bytes = float(np.mean(dec_bytes[timed]))
+    achieved = dec_avg_bytes / part_avg_s / 1e9
+    return {
+        "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak) + tokens/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed / a.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; keys with per-channel lognormal scales and outlier "
+                "channels before rotation, values and queries N(0,1), fp16)",
+        "config": {
+            "workload": w.name,
+            "format": "rotated per-token 2-bit (KV1 BQ2_0), 4 fp16 sinks",
+            "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim,
+            "context_first_step": int(lens_host[a.warmup, 1].max()),
+            "context_last_step": int(lens_host[-1, 1].max()),
+            "rotating_layer_caches": L, "decode_worker_waves": n_workers,
+            "step": "kvq_bq2_append + kvq_bq2_decode_attn, one layer",
+        },
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(w.batch * a.steps / elapsed, 1),
+        "tokens_per_s_unit": "decoded tokens per second through one layer",
+        "roofline": {
+            "kernel": "bq2_partial",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(w.name, "bq2_partial"),
+            "avg_launch_us": round(part_avg_s * 1e6, 3),
+            "algorithmic_bytes_per_launch": round(dec_avg_bytes),
+        },
+        "gpu": torch.cuda.get_device_name(0),
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -138,6 +290,13 @@ def main():
     w = synth.WORKLOADS[a.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.fmt == "bq2":
+        rec = run_bq2(a, w, torch, kvq, metrics, synth)
+        if not a.no_cpu_baseline:
+            print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+            rec["cpu_baseline"] = cpu_baseline_bq2(w, a.cpu_seconds)
+        print(json.dumps(rec), flush=True)
+        return
     L = a.layers if w.layers == 1 else w.layers
     total_steps = a.warmup + a.steps
     per_layer_tokens = -(-total_steps // L)
