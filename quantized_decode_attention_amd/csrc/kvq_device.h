@@ -236,6 +236,7 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 // uniform: every length equals max_seq_len.
 struct BatchWork {
   int c, inc, head_total, total;
+  int n;  // lane b < 64: length of sequence b
   bool uniform;
 };
 
@@ -243,6 +244,7 @@ template <class Fmt>
 __device__ __forceinline__ BatchWork batch_work(const typename Fmt::Launch& L, int lane) {
   BatchWork bw;
   const int n = lane < L.g.B ? L.seq_lens[lane] : L.max_seq_len;
+  bw.n = n;
   bw.c = lane < L.g.B ? Fmt::work_of(L, n).w * L.g.Hkv : 0;
   bw.inc = wave_scan_incl(bw.c);
   bw.head_total = __builtin_amdgcn_readlane(bw.inc, 63);
