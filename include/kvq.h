@@ -311,6 +311,32 @@ int kvq_decode_combine(const kvq_geom *geom, const uint16_t *q,
                        const void *workspace, size_t workspace_bytes,
                        uint16_t *out, void *stream);
 
+/* ----- several query tokens per sequence ----------------------------------- */
+
+/* Attention of the last T positions of every sequence at once (verification
+ * of T drafted tokens, or a prefill chunk, over the packed cache; [KIVI] core
+ * capabilities: prefill works alongside the quantized cache).  The T tokens
+ * must already be appended.  Query token i (0 <= i < T) sits at position
+ * n - T + i and attends causally: to positions [0, n - T + i] of the cache as
+ * it stands at length n (packed below Lq(n), residual window above),
+ *   out_i = sum_{t <= n-T+i} softmax(s)_t v_t,  s_t = sm_scale * q_i . k_t.
+ * Every cache byte is read once for all T tokens (the T * Hq/Hkv rows of a KV
+ * head are one matrix-core tile).
+ *   q        device fp16 [B][T][Hq][D];  out: device fp16 [B][T][Hq][D].
+ *   seq_lens device int32 [B]: positions per sequence INCLUDING the T tokens.
+ *   T        >= 1, T * Hq/Hkv in {1, 2, 4, 8, 16}, T <= max_seq_len
+ *            (KVQ_ERR_RANGE otherwise).
+ *   workspace at least kvq_decode_multi_workspace_bytes(geom, T, max_seq_len).
+ * T = 1 is kvq_decode_attn.  A row whose query token sees no position (n < T)
+ * gets 0; lengths outside [0, max_seq_len] give NaN as in kvq_decode_attn. */
+int kvq_decode_multi_workspace_bytes(const kvq_geom *geom, int32_t T,
+                                     int32_t max_seq_len, size_t *bytes);
+int kvq_decode_attn_multi(const kvq_geom *geom, const uint16_t *q,
+                          const kvq_cache *cache, const int32_t *seq_lens,
+                          int32_t T, int32_t max_seq_len, float sm_scale,
+                          void *workspace, size_t workspace_bytes,
+                          uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -66,6 +66,8 @@ def lib():
         L.orc_append.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 9
         L.orc_cache_kv.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 6 + [i64, P, P]
         L.orc_decode_attn.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 8 + [f64, P]
+        L.orc_decode_attn_multi.argtypes = ([ctypes.c_int] * 8 + [i64, ctypes.c_int] + [P] * 8
+                                            + [f64, P])
         L.orc_unpack.argtypes = [ctypes.c_int] * 6 + [i64] + [P] * 8
         L.orc_residual_store.argtypes = [ctypes.c_int] * 4 + [P, P, i64, i64, P, P]
         L.orc_value_res_rows.argtypes = [ctypes.c_int] * 4 + [P, P]
@@ -238,6 +240,21 @@ def decode_attn(g: Geom, cache: Cache, q: np.ndarray, seq_lens: np.ndarray,
                           g.k_bits, g.v_bits, g.group, g.residual, g.capacity,
                           _p(q), *[_p(a) for a in cache.arrays()], _p(sl),
                           float(sm_scale), _p(out))
+    return out
+
+
+def decode_attn_multi(g: Geom, cache: Cache, q: np.ndarray, seq_lens: np.ndarray, T: int,
+                      sm_scale: float) -> np.ndarray:
+    """fp64 [B][T][Hq][D]: query token i of the last T attends causally to
+    positions [0, n - T + i]; seq_lens include all T tokens."""
+    q = _u16(q)
+    assert q.shape == (g.batch, T, g.n_q_heads, g.head_dim)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.zeros((g.batch, T, g.n_q_heads, g.head_dim), np.float64)
+    lib().orc_decode_attn_multi(g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, g.k_bits,
+                                g.v_bits, g.group, g.residual, g.capacity, T, _p(q),
+                                *[_p(a) for a in cache.arrays()], _p(sl), float(sm_scale),
+                                _p(out))
     return out
 
 

@@ -548,6 +548,80 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
   }
 }
 
+/*
+ * Attention of the last T positions of each sequence at once ([KIVI] core
+ * capabilities: prefill alongside the quantized cache; the plainest reading is
+ * causal attention of T new tokens).  With n = seq_lens[b] (the T tokens
+ * included), query token i (0 <= i < T) sits at position n - T + i and
+ * attends to positions [0, n - T + i] of the cache at length n: dequantized
+ * below the packed length Lq(n), the fp16 window above, in fp64.
+ * q fp16 [B][T][Hq][D]; out fp64 [B][T][Hq][D]; a token that sees no position
+ * gets 0.
+ */
+void orc_decode_attn_multi(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
+                           int R, int64_t C, int T, const uint16_t *q,
+                           const uint32_t *k_codes, const uint32_t *v_codes,
+                           const uint16_t *k_meta, const uint16_t *v_meta,
+                           const uint16_t *k_res, const uint16_t *v_res,
+                           const int32_t *seq_lens, double sm_scale, double *out) {
+  int64_t units = (int64_t)B * Hkv;
+  int g = Hq / Hkv;
+  int entry_of[128];
+  key_meta_entries(D, bK, entry_of);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    int b = (int)(u / Hkv);
+    int hkv = (int)(u % Hkv);
+    int64_t n = seq_lens[b];
+    if (n > C) n = C;
+    int64_t lq = orc_packed_len(n, R);
+    int64_t nn = n > 0 ? n : 1;
+    double *kk = (double *)malloc((size_t)nn * D * sizeof(double));
+    double *vv = (double *)malloc((size_t)nn * D * sizeof(double));
+    double *s = (double *)malloc((size_t)nn * sizeof(double));
+    for (int64_t t = 0; t < n; ++t)
+      for (int c = 0; c < D; ++c) {
+        if (t < lq) {
+          kk[t * D + c] = dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c);
+          vv[t * D + c] = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
+        } else {
+          kk[t * D + c] = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
+          vv[t * D + c] =
+              orc_half_to_float(v_res[u * R * D + value_res_index(D, (int)(t % R), c)]);
+        }
+      }
+    for (int i = 0; i < T; ++i) {
+      int64_t vis = n - T + i + 1; /* positions this token sees */
+      for (int hh = 0; hh < g; ++hh) {
+        int h = hkv * g + hh;
+        const uint16_t *qh = q + (((int64_t)b * T + i) * Hq + h) * D;
+        double *oh = out + (((int64_t)b * T + i) * Hq + h) * D;
+        for (int c = 0; c < D; ++c) oh[c] = 0.0;
+        if (vis <= 0) continue;
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < vis; ++t) {
+          double dot = 0.0;
+          for (int c = 0; c < D; ++c) dot += (double)orc_half_to_float(qh[c]) * kk[t * D + c];
+          s[t] = sm_scale * dot;
+          if (s[t] > smax) smax = s[t];
+        }
+        double denom = 0.0;
+        for (int64_t t = 0; t < vis; ++t) {
+          s[t] = exp(s[t] - smax);
+          denom += s[t];
+        }
+        for (int64_t t = 0; t < vis; ++t) {
+          double p = s[t] / denom;
+          for (int c = 0; c < D; ++c) oh[c] += p * vv[t * D + c];
+        }
+      }
+    }
+    free(kk);
+    free(vv);
+    free(s);
+  }
+}
+
 /* Writes positions [pos0, pos0 + n_tok) of fp16 token rows k, v
  * [B*Hkv][n_tok][D] into their residual slots p % R. */
 void orc_residual_store(int B, int Hkv, int D, int R, const uint16_t *k,

@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     kvq_quantize_keys_perchannel, kvq_quantize_values_pertoken,
     kvq_validate_geom, last_error, lib, status_str)
 from ._lib import (  # noqa: F401
+    alloc_multi_workspace, kvq_decode_attn_multi, kvq_decode_multi_workspace_bytes)
+from ._lib import (  # noqa: F401
     Bq2Cache, Bq2Geom, alloc_bq2_workspace, kvq_bq2_append, kvq_bq2_cache_bytes,
     kvq_bq2_decode_attn, kvq_bq2_decode_combine, kvq_bq2_decode_partial,
     kvq_bq2_decode_workers, kvq_bq2_decode_workspace_bytes, kvq_bq2_prefill,

@@ -40,6 +40,7 @@ EXPORTS = [
     "kvq_decode_workspace_bytes", "kvq_quantize_keys_perchannel",
     "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append",
     "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
+    "kvq_decode_multi_workspace_bytes", "kvq_decode_attn_multi",
 ]
 EXPORTS_BQ2 = [
     "kvq_bq2_validate_geom", "kvq_bq2_cache_bytes", "kvq_bq2_decode_workers",
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_attn": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_partial": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_combine": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
+            "kvq_decode_multi_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
+            "kvq_decode_attn_multi": (ctypes.c_int, [G, P, C, P, i32, i32, f32, P, sz, P, P]),
             "kvq_bq2_validate_geom": (ctypes.c_int, [G2]),
             "kvq_bq2_cache_bytes": (ctypes.c_int, [G2, ctypes.POINTER(sz)]),
             "kvq_bq2_decode_workers": (ctypes.c_int, [G2, ctypes.POINTER(i32)]),
@@ -347,6 +350,35 @@ def kvq_decode_combine(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.T
                        out: torch.Tensor, stream=None) -> None:
     args, keep = _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
     _check(lib().kvq_decode_combine(*args, _stream(stream)), "kvq_decode_combine")
+
+
+def kvq_decode_multi_workspace_bytes(g: Geom, T: int, max_seq_len: int) -> int:
+    gc = g.c()
+    out = ctypes.c_size_t()
+    _check(lib().kvq_decode_multi_workspace_bytes(ctypes.byref(gc), T, max_seq_len,
+                                                  ctypes.byref(out)),
+           "kvq_decode_multi_workspace_bytes")
+    return out.value
+
+
+def kvq_decode_attn_multi(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,
+                          T: int, max_seq_len: int, sm_scale: float,
+                          workspace: torch.Tensor | None, out: torch.Tensor,
+                          stream=None) -> None:
+    gc = g.c()
+    cc = _cache_arg(cache)
+    shape = (g.batch, T, g.n_q_heads, g.head_dim)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvq_decode_attn_multi(
+        ctypes.byref(gc), _ptr(q, "q", _F16, shape), ctypes.byref(cc),
+        _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(T), int(max_seq_len),
+        float(sm_scale), _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out", _F16, shape),
+        _stream(stream)), "kvq_decode_attn_multi")
+
+
+def alloc_multi_workspace(g: Geom, T: int, max_seq_len: int, device="cuda") -> torch.Tensor:
+    n = kvq_decode_multi_workspace_bytes(g, T, max_seq_len)
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
 
 
 def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:

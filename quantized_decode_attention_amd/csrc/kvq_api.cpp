@@ -108,13 +108,15 @@ int cu_count(int* out) {
   return KVQ_OK;
 }
 
-// Worker waves of the persistent partial kernel (resident waves x CUs).
-int workers_for(const kvq_geom* g, int32_t* n_workers) {
+// Worker waves of the persistent partial kernel (resident waves x CUs) for
+// T query tokens per sequence.
+int workers_for(const kvq_geom* g, int32_t* n_workers, int T = 1) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != KVQ_OK) return st;
   int w = 0;
-  hipError_t e = kvq::decode_workers(kvq::to_geom(*g), cus, &w);
+  hipError_t e = kvq::decode_workers(kvq::to_geom(*g), T * (g->n_q_heads / g->n_kv_heads), cus,
+                                     &w);
   if (e != hipSuccess) return hip_fail(e, "occupancy query");
   *n_workers = w;
   return KVQ_OK;
@@ -128,15 +130,16 @@ int check_max_len(const kvq_geom* g, int32_t max_seq_len) {
 }
 
 // Partials: one per (worker wave, unit) pair that occurs, at most
-// n_workers + B*Hkv, each [Hq/Hkv][head_dim + 4] floats.
-size_t workspace_need(const kvq_geom* g, int32_t n_workers) {
-  const size_t gq = g->n_q_heads / g->n_kv_heads;
+// n_workers + B*Hkv, each [T * Hq/Hkv][head_dim + 4] floats.
+size_t workspace_need(const kvq_geom* g, int32_t n_workers, int T = 1) {
+  const size_t gq = (size_t)T * (g->n_q_heads / g->n_kv_heads);
   return ((size_t)n_workers + (size_t)g->batch * g->n_kv_heads) * gq *
          (g->head_dim + 4) * sizeof(float);
 }
 
-int check_workspace(const kvq_geom* g, int32_t n_workers, const void* ws, size_t bytes) {
-  const size_t need = workspace_need(g, n_workers);
+int check_workspace(const kvq_geom* g, int32_t n_workers, const void* ws, size_t bytes,
+                    int T = 1) {
+  const size_t need = workspace_need(g, n_workers, T);
   if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (bytes < need)
@@ -144,12 +147,24 @@ int check_workspace(const kvq_geom* g, int32_t n_workers, const void* ws, size_t
   return KVQ_OK;
 }
 
+// Query tokens per sequence: T >= 1 with T * Hq/Hkv in {1, 2, 4, 8, 16}.
+int check_tokens(const kvq_geom* g, int32_t T) {
+  const int rows = T * (g->n_q_heads / g->n_kv_heads);
+  if (T < 1 || (rows != 1 && rows != 2 && rows != 4 && rows != 8 && rows != 16))
+    return fail(KVQ_ERR_RANGE,
+                "T=%d query tokens: T * n_q_heads / n_kv_heads must be 1, 2, 4, 8 or 16", T);
+  return KVQ_OK;
+}
+
 int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
                  const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                  void* workspace, size_t workspace_bytes, uint16_t* out,
-                 kvq::DecodeLaunch* L) {
+                 kvq::DecodeLaunch* L, int32_t T = 1) {
   int st = check_geom(geom);
   if (st != KVQ_OK) return st;
+  if ((st = check_tokens(geom, T)) != KVQ_OK) return st;
+  if (T > max_seq_len)
+    return fail(KVQ_ERR_RANGE, "T=%d exceeds max_seq_len=%d", T, max_seq_len);
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if ((st = check_ptr(q, "q")) != KVQ_OK) return st;
   if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
@@ -159,13 +174,16 @@ int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache
     return fail(KVQ_ERR_RANGE, "sm_scale must be finite");
   if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
   int32_t n_workers = 0;
-  if ((st = workers_for(geom, &n_workers)) != KVQ_OK) return st;
-  if ((st = check_workspace(geom, n_workers, workspace, workspace_bytes)) != KVQ_OK) return st;
+  if ((st = workers_for(geom, &n_workers, T)) != KVQ_OK) return st;
+  if ((st = check_workspace(geom, n_workers, workspace, workspace_bytes, T)) != KVQ_OK)
+    return st;
   L->g = kvq::to_geom(*geom);
   L->q = q;
   L->cache = *cache;
   L->seq_lens = seq_lens;
   L->max_seq_len = max_seq_len;
+  L->T = T;
+  L->gq = T * (geom->n_q_heads / geom->n_kv_heads);
   L->n_workers = n_workers;
   {
     // a residual (fp16) chunk moves rw times the bytes of a packed chunk
@@ -456,6 +474,42 @@ int kvq_decode_combine(const kvq_geom* geom, const uint16_t* q, const kvq_cache*
                           const_cast<void*>(workspace), workspace_bytes, out, &L);
     if (st != KVQ_OK) return st;
     hipError_t e = kvq::launch_decode_combine(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_decode_multi_workspace_bytes(const kvq_geom* geom, int32_t T, int32_t max_seq_len,
+                                     size_t* bytes) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+    if ((st = check_tokens(geom, T)) != KVQ_OK) return st;
+    if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
+    int32_t nw = 0;
+    if ((st = workers_for(geom, &nw, T)) != KVQ_OK) return st;
+    *bytes = workspace_need(geom, nw, T);
+    return KVQ_OK;
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_decode_attn_multi(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
+                          const int32_t* seq_lens, int32_t T, int32_t max_seq_len,
+                          float sm_scale, void* workspace, size_t workspace_bytes,
+                          uint16_t* out, void* stream) {
+  try {
+    kvq::DecodeLaunch L;
+    int st = decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
+                          workspace_bytes, out, &L, T);
+    if (st != KVQ_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kvq::launch_decode_partial(L, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+    e = kvq::launch_decode_combine(L, s);
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");

@@ -61,6 +61,9 @@ struct Bq2Work {
   static __device__ __forceinline__ SeqWork work_of(const Bq2Launch& L, int n) {
     return bq2_work_of(L, n);
   }
+  static __device__ __forceinline__ int64_t row(const Bq2Launch& L, int b, int hkv, int j) {
+    return (int64_t)b * L.g.Hq + hkv * (L.g.Hq / L.g.Hkv) + j;
+  }
 };
 
 // A lane's share of one 32-position chunk.

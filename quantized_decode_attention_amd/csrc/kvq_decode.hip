@@ -109,6 +109,7 @@ struct PackedWave {
   uint32_t bq[KP][KC][4];
   float beta_c;
   int cur_group;
+  int hide;  // newest positions this lane's row must not see: T - 1 - its query token
 
   __device__ void init(int lane_) {
     lane = lane_;
@@ -144,6 +145,7 @@ struct PackedWave {
     }
     beta_c = 0.0f;
     cur_group = -1;
+    hide = 0;
   }
 
   __device__ __forceinline__ void load(int ch, R& r) const {
@@ -384,7 +386,7 @@ struct PackedWave {
           x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
                    __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
         }
-        const bool valid = t0 + 8 * lg + 4 * u + q < n_tok;
+        const bool valid = t0 + 8 * lg + 4 * u + q < n_tok - hide;
         s[u][q] = valid ? x * kscale_r : kNegInf;
       }
     }
@@ -403,7 +405,11 @@ struct PackedWave {
     }
   }
 
-  __device__ __forceinline__ void process(int ch, const R& r) {
+  // kMask: positions after last_vis (this lane's row, 32-token chunk ch) get
+  // score -inf (the causal mask of a multi-token query; their codes and meta
+  // are real cache data, so their weight 0 is exact).
+  template <bool kMask = false>
+  __device__ __forceinline__ void process(int ch, const R& r, int last_vis = 0) {
     if constexpr (G == kChunk) {
       fold(r);  // every chunk is a key group: no branch, so the fold can be
                 // scheduled against the previous chunk's value products
@@ -435,6 +441,8 @@ struct PackedWave {
                    __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
         }
         s[u][q] = __builtin_fmaf(x, kscale, beta_c);
+        if constexpr (kMask)
+          s[u][q] = ch * kChunk + 8 * lg + 4 * u + q <= last_vis ? s[u][q] : kNegInf;
       }
     }
     float p[2][4];
@@ -498,9 +506,19 @@ __device__ __forceinline__ SeqWork seq_work(const DecodeLaunch& L, int b) {
   return seq_work_of(L, L.seq_lens[b]);
 }
 
+// Row j of unit (b, hkv) is query token j / (Hq/Hkv) of the last T, head
+// hkv * Hq/Hkv + j % (Hq/Hkv): q and out are [B][T][Hq][D].
+__device__ __forceinline__ int64_t qrow(const DecodeLaunch& L, int b, int hkv, int j) {
+  const int gr = L.g.Hq / L.g.Hkv;
+  return ((int64_t)b * L.T + j / gr) * L.g.Hq + hkv * gr + j % gr;
+}
+
 struct KiviWork {
   using Launch = DecodeLaunch;
   static constexpr bool kRotateOut = false;
+  static __device__ __forceinline__ int64_t row(const DecodeLaunch& L, int b, int hkv, int j) {
+    return qrow(L, b, hkv, j);
+  }
   static __device__ __forceinline__ SeqWork work_of(const DecodeLaunch& L, int n) {
     return seq_work_of(L, n);
   }
@@ -549,15 +567,15 @@ __device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw
   R rb;
   // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
   // that q * 2^-E * scale fits fp16
-  const uint16_t* qg = L.q + ((int64_t)b * g.Hq + hkv * GQ) * D;
   int eh[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
+    const uint16_t* qg = L.q + qrow(L, b, hkv, h) * D;
     float qv[QPH];
     float mx = 0.0f;
 #pragma unroll
     for (int k = 0; k < QPH; ++k) {
-      qv[k] = h2f(qg[h * D + lane + 64 * k]) * L.scale_log2;
+      qv[k] = h2f(qg[lane + 64 * k]) * L.scale_log2;
       mx = fmaxf(mx, fabsf(qv[k]));
     }
 #pragma unroll
@@ -582,12 +600,19 @@ __device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw
   w.kscale = ldexpf(1.0f, e_mine + 24 - kKeyAccLog2<BK>);
   w.bscale = ldexpf(1.0f, e_mine);
 
-  if (pc0 < pc1) {
+  // rows of query token i (of the last T) do not see the newest T - 1 - i
+  // positions; packed chunks holding a position past n - T are processed
+  // apart, with the mask (never for a single query token: the newest packed
+  // position is at most n - 2)
+  w.hide = L.T - 1 - w.hcol / (g.Hq / g.Hkv);
+  const int last_vis = sw.n - 1 - w.hide;
+  const int pm = min(pc1, max(pc0, (sw.n - L.T + 1) / kChunk));
+  if (pc0 < pm) {
     // two chunk buffers: the next chunk's loads are in flight while one is
     // used (a deeper ring measured no faster).  Prefetches past the last
     // chunk re-load that chunk (always in bounds) instead of being skipped,
     // so no load sits under a branch.
-    const int last = pc1 - 1;
+    const int last = pm - 1;
     int ch = pc0;
     for (; ch < last; ch += 2) {  // pairs; ra holds chunk ch on entry
       w.load(ch + 1, rb);
@@ -596,6 +621,10 @@ __device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw
       w.process(ch + 1, rb);
     }
     if (ch == last) w.process(ch, ra);  // odd count: the last chunk is in ra
+  }
+  for (int ch = pm; ch < pc1; ++ch) {  // ra holds chunk pc0 if pm == pc0
+    if (ch != pc0) w.load(ch, ra);
+    w.template process<true>(ch, ra, last_vis);
   }
   const bool resid = rk0 < rk1;
   if (resid) {
@@ -753,7 +782,7 @@ hipError_t dispatch_ng(const DecodeLaunch& L, int op, int cus, int* workers, hip
 
 template <int D, int BK, int BV>
 hipError_t dispatch_gq(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  switch (L.g.Hq / L.g.Hkv) {
+  switch (L.gq) {
     case 1: return dispatch_ng<D, BK, BV, 1>(L, op, cus, workers, st);
     case 2: return dispatch_ng<D, BK, BV, 2>(L, op, cus, workers, st);
     case 4: return dispatch_ng<D, BK, BV, 4>(L, op, cus, workers, st);
@@ -780,7 +809,7 @@ hipError_t dispatch(const DecodeLaunch& L, int op, int cus, int* workers, hipStr
 template <int D>
 hipError_t combine_gq(const DecodeLaunch& L, hipStream_t st) {
   dim3 grid(L.g.Hkv, L.g.B);
-  switch (L.g.Hq / L.g.Hkv) {
+  switch (L.gq) {
     case 1: decode_combine_kernel<KiviWork, D, 1><<<grid, kThreads, 0, st>>>(L); break;
     case 2: decode_combine_kernel<KiviWork, D, 2><<<grid, kThreads, 0, st>>>(L); break;
     case 4: decode_combine_kernel<KiviWork, D, 4><<<grid, kThreads, 0, st>>>(L); break;
@@ -793,9 +822,10 @@ hipError_t combine_gq(const DecodeLaunch& L, hipStream_t st) {
 
 }  // namespace
 
-hipError_t decode_workers(const Geom& g, int cus, int* workers) {
+hipError_t decode_workers(const Geom& g, int gq, int cus, int* workers) {
   DecodeLaunch L{};
   L.g = g;
+  L.gq = gq;
   return dispatch(L, 1, cus, workers, nullptr);
 }
 

@@ -206,8 +206,9 @@ __device__ __forceinline__ void load_run(const uint32_t* p, uint32_t (&w)[N]) {
 // no tokens has max -inf and sum 0.
 // ---------------------------------------------------------------------------
 // A cache format supplies a policy Fmt: Fmt::Launch (its launch record, with
-// g.B, g.Hq, g.Hkv, g.C, seq_lens, max_seq_len, n_workers, rw, ws, out) and
-// Fmt::work_of(L, n), the work of one KV head of a sequence of n tokens.
+// g.B, g.Hq, g.Hkv, g.C, seq_lens, max_seq_len, n_workers, rw, ws, out),
+// Fmt::work_of(L, n), the work of one KV head of a sequence of n tokens, and
+// Fmt::row(L, b, hkv, j), the query / output row of row j of unit (b, hkv).
 // ---------------------------------------------------------------------------
 constexpr int kPartPad = 4;  // partial row = D values, max, sum, 2 pad floats
 
@@ -330,14 +331,14 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
   __shared__ float s_rot[kRotate ? GQ * D : 1];
   const auto& g = L.g;
   const int hkv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int64_t out0 = ((int64_t)b * g.Hq + hkv * GQ) * D;
   const int n = L.seq_lens[b];
   if (n < 0 || n > g.C || n > L.max_seq_len) {
-    for (int i = tid; i < GQ * D; i += kThreads) L.out[out0 + i] = 0x7e00;  // NaN
+    for (int i = tid; i < GQ * D; i += kThreads)
+      L.out[Fmt::row(L, b, hkv, i / D) * D + i % D] = 0x7e00;  // NaN
     return;
   }
   if (n == 0) {
-    for (int i = tid; i < GQ * D; i += kThreads) L.out[out0 + i] = 0;
+    for (int i = tid; i < GQ * D; i += kThreads) L.out[Fmt::row(L, b, hkv, i / D) * D + i % D] = 0;
     return;
   }
   // flat position of this unit's work
@@ -428,8 +429,8 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
         }
       }
     }
-    const float inv = 1.0f / Ls;
-    const int64_t o = out0 + oh * D + oc;
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;  // a row that sees no position: 0
+    const int64_t o = Fmt::row(L, b, hkv, oh) * D + oc;
     if constexpr (kRotate) {
       // out_c = sum_j H[c][j] o_j, H[c][j] = (-1)^popcount(c & j) / 8
       if (share == 0) {

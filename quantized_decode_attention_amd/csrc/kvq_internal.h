@@ -57,18 +57,21 @@ hipError_t launch_append(const Geom& g, const uint16_t* k_new,
 
 struct DecodeLaunch {
   Geom g;
-  const uint16_t* q;
+  const uint16_t* q;  // [B][T][Hq][D]
   kvq_cache cache;
   const int32_t* seq_lens;
   int32_t max_seq_len;
+  int32_t T;          // query tokens per sequence (the last T positions)
+  int32_t gq;         // rows per KV head: T * Hq / Hkv (query token major)
   int32_t n_workers;  // worker waves of the partial kernel
   int32_t rw;         // work units of a residual chunk (its bytes / a packed chunk's)
   float scale_log2;   // sm_scale * log2(e)
-  float* ws;          // partials [n_workers + B*Hkv][Hq/Hkv][D + 4]
-  uint16_t* out;      // [B][Hq][D]
+  float* ws;          // partials [n_workers + B*Hkv][gq][D + 4]
+  uint16_t* out;      // [B][T][Hq][D]
 };
-// Worker waves for this geometry's partial kernel on the current device.
-hipError_t decode_workers(const Geom& g, int cus, int* workers);
+// Worker waves of the partial kernel for gq rows per KV head on the current
+// device.
+hipError_t decode_workers(const Geom& g, int gq, int cus, int* workers);
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st);
 

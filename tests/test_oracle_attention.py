@@ -209,3 +209,42 @@ def test_appends_equal_bulk_quantization(orc, bK, bV, G, R):
             for t in range(lq, n):
                 np.testing.assert_array_equal(inc.k_res[b, :, t % R], k[b, :, t].view(np.uint16))
                 np.testing.assert_array_equal(vrows[b, :, t % R], v[b, :, t].view(np.uint16))
+
+
+# ------------------------------------------- several query tokens at once ----
+@pytest.mark.parametrize("n,T", [(70, 4), (66, 4), (65, 2), (40, 8), (5, 4), (3, 4)])
+def test_multi_token_attention_is_causal_attention_on_the_cache(orc, n, T):
+    """Query token i of the last T sees positions [0, n - T + i] of the cache
+    at length n.  Pinned to torch SDPA with an explicit boolean causal mask on
+    the cache's dequantized K/V (n = 66, T = 4 with R = 32: two of the four
+    new tokens are already flushed, so the mask reaches into packed rows);
+    n < T leaves the first tokens with nothing to see (output 0)."""
+    g, cache, _, _, _ = _tiny_case(orc, n)
+    rng = np.random.default_rng(n * 10 + T)
+    q = rng.standard_normal((g.batch, T, g.n_q_heads, g.head_dim)).astype(np.float16)
+    scale = 0.125
+    out = orc.decode_attn_multi(g, cache, q, np.array([n], np.int32), T, scale)
+    kk, vv = orc.cache_kv(g, cache, n)
+    G = g.n_q_heads // g.n_kv_heads
+    K = torch.from_numpy(kk).repeat_interleave(G, dim=1)          # [B][Hq][n][D]
+    V = torch.from_numpy(vv).repeat_interleave(G, dim=1)
+    for i in range(T):
+        vis = n - T + i + 1
+        if vis <= 0:
+            assert np.all(out[:, i] == 0)
+            continue
+        mask = torch.zeros((1, 1, 1, n), dtype=torch.bool)
+        mask[..., :vis] = True
+        qt = torch.from_numpy(q[:, i].astype(np.float64))[:, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=mask,
+                                                               scale=scale)[:, :, 0].numpy()
+        np.testing.assert_allclose(out[:, i], ref, rtol=0, atol=1e-12)
+
+
+def test_multi_token_last_token_is_single_token_decode(orc):
+    g, cache, _, _, _ = _tiny_case(orc, 97)
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((g.batch, 4, g.n_q_heads, g.head_dim)).astype(np.float16)
+    out = orc.decode_attn_multi(g, cache, q, np.array([97], np.int32), 4, 0.125)
+    one = orc.decode_attn(g, cache, np.ascontiguousarray(q[:, 3]), np.array([97], np.int32), 0.125)
+    np.testing.assert_array_equal(out[:, 3], one)
