@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--config", type=int, default=3, help="workload 1..6 (default 3)")
     p.add_argument("--layers", type=int, default=4, help="rotating layer caches")
+    p.add_argument("--tokens", type=int, default=1,
+                   help="query tokens per sequence per step (T > 1: T appends, then "
+                        "kvq_decode_attn_multi; KIVI-format workloads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -298,9 +301,10 @@ def main():
         print(json.dumps(rec), flush=True)
         return
     L = a.layers if w.layers == 1 else w.layers
+    T = a.tokens
     total_steps = a.warmup + a.steps
-    per_layer_tokens = -(-total_steps // L)
-    cap = synth.capacity_for(w, per_layer_tokens + 1)
+    per_layer_tokens = -(-total_steps // L) * T
+    cap = synth.capacity_for(w, per_layer_tokens + T)
     g = kvq.Geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k_bits, w.v_bits,
                  w.group, w.residual, cap)
 
@@ -308,11 +312,11 @@ def main():
     # each layer attends over the workload's context
     base = synth.seq_lens(w)
     if w.ctx_range is None:
-        start = base - 1 - (a.warmup + L - 1) // L
+        start = base - T - T * ((a.warmup + L - 1) // L)
         if w.cfg == 5:
             start = np.full(w.batch, w.context, np.int32)
     else:
-        start = base - 1
+        start = base - T
     start = np.maximum(start, 1).astype(np.int32)
     nmax0 = int(start.max())
 
@@ -339,30 +343,42 @@ def main():
 
     # per-step inputs (a pool of seeded tokens) and lengths, all on device
     pool = [tuple(torch.from_numpy(x).to(dev) for x in synth.step_token(w, s)) for s in range(8)]
-    lens_host = np.zeros((total_steps, 2, w.batch), np.int32)
+    # lens_host[s, j]: length before append j of step s (j < T); [s, T]: after
+    lens_host = np.zeros((total_steps, T + 1, w.batch), np.int32)
     cur = [start.copy() for _ in range(L)]
     for s in range(total_steps):
         l = s % L
-        lens_host[s, 0] = cur[l]
-        lens_host[s, 1] = cur[l] + 1
-        cur[l] = cur[l] + 1
+        for j in range(T + 1):
+            lens_host[s, j] = cur[l] + j
+        cur[l] = cur[l] + T
     lens_dev = torch.from_numpy(lens_host).to(dev)
-    max_len = int(lens_host[:, 1].max())
-    ws = kvq.alloc_workspace(g, max_len, dev)
-    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    max_len = int(lens_host[:, T].max())
+    if T == 1:
+        ws = kvq.alloc_workspace(g, max_len, dev)
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    else:
+        ws = kvq.alloc_multi_workspace(g, T, max_len, dev)
+        out = torch.empty((w.batch, T, w.n_q_heads, w.head_dim), dtype=torch.float16,
+                          device=dev)
+        qpool = [torch.stack([pool[(s + j) % len(pool)][2] for j in range(T)], 1).contiguous()
+                 for s in range(len(pool))]
     scale = 1.0 / math.sqrt(w.head_dim)
     n_workers = kvq.kvq_decode_workers(g)
 
     # algorithmic bytes of every step
     step_bytes, dec_bytes = [], []
     for s in range(total_steps):
-        before, after = lens_host[s, 0], lens_host[s, 1]
+        after = lens_host[s, T]
         db = metrics.decode_step_bytes(after, w.n_q_heads, w.n_kv_heads, w.head_dim,
                                        w.k_bits, w.v_bits, w.group, w.residual)
-        flushing = int(np.sum((before > 0) & (before % w.residual == 0)))
-        sb = db + metrics.append_bytes(w.batch, w.n_kv_heads, w.head_dim)
-        sb += metrics.flush_bytes(flushing * w.n_kv_heads, w.residual, w.head_dim,
-                                  w.k_bits, w.v_bits, w.group)
+        db += (T - 1) * 4 * w.batch * w.n_q_heads * w.head_dim  # the other tokens' q and out
+        sb = db
+        for j in range(T):
+            before = lens_host[s, j]
+            flushing = int(np.sum((before > 0) & (before % w.residual == 0)))
+            sb += metrics.append_bytes(w.batch, w.n_kv_heads, w.head_dim)
+            sb += metrics.flush_bytes(flushing * w.n_kv_heads, w.residual, w.head_dim,
+                                      w.k_bits, w.v_bits, w.group)
         step_bytes.append(sb)
         dec_bytes.append(db)
 
@@ -372,15 +388,23 @@ def main():
 
     def step(s, timed_idx=None):
         l = s % L
-        kn, vn, q = pool[s % len(pool)]
         c = caches[l]
-        kvq.kvq_append(g, kn, vn, lens_dev[s, 0], c, stream)
+        for j in range(T):
+            kn, vn, _ = pool[(s + j) % len(pool)]
+            kvq.kvq_append(g, kn, vn, lens_dev[s, j], c, stream)
         if timed_idx is not None:
             ev_a[timed_idx].record(stream)
-        kvq.kvq_decode_partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
-        if timed_idx is not None:
-            ev_b[timed_idx].record(stream)
-        kvq.kvq_decode_combine(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+        if T == 1:
+            q = pool[s % len(pool)][2]
+            kvq.kvq_decode_partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+            if timed_idx is not None:
+                ev_b[timed_idx].record(stream)
+            kvq.kvq_decode_combine(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+        else:  # partial + combine in one call: the events bracket both
+            kvq.kvq_decode_attn_multi(g, qpool[s % len(qpool)], c, lens_dev[s, T], T, max_len,
+                                      scale, ws, out, stream)
+            if timed_idx is not None:
+                ev_b[timed_idx].record(stream)
 
     for s in range(a.warmup):
         step(s)
@@ -419,22 +443,25 @@ def main():
             "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "k_bits": w.k_bits, "v_bits": w.v_bits,
             "group": w.group, "residual": w.residual,
-            "context_first_step": int(lens_host[a.warmup, 1].max()),
-            "context_last_step": int(lens_host[-1, 1].max()),
+            "context_first_step": int(lens_host[a.warmup, T].max()),
+            "context_last_step": int(lens_host[-1, T].max()),
             "rotating_layer_caches": L, "decode_worker_waves": n_workers,
-            "step": "kvq_append (+flush when a window fills) + kvq_decode_attn, one layer",
+            "step": ("kvq_append (+flush when a window fills) + kvq_decode_attn, one layer"
+                     if T == 1 else
+                     f"{T} x kvq_append + kvq_decode_attn_multi (T={T}), one layer"),
+            "query_tokens": T,
         },
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "tokens_per_s": round(w.batch * a.steps / elapsed, 1),
+        "tokens_per_s": round(w.batch * T * a.steps / elapsed, 1),
         "tokens_per_s_unit": "decoded tokens per second through one layer",
         "roofline": {
-            "kernel": "decode_partial",
+            "kernel": "decode_partial" if T == 1 else "decode_partial+decode_combine (multi)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
+            "traffic": traffic if T == 1 else None,
             "avg_launch_us": round(part_avg_s * 1e6, 3),
             "algorithmic_bytes_per_launch": round(dec_avg_bytes),
         },
