@@ -3,8 +3,9 @@ for AMD Instinct MI355X (gfx950), and the rotated per-token 2-bit format of
 KV1 (BQ2_0).
 
 The computation lives in libkvq.so (hand-written HIP kernels behind the C ABI
-in include/kvq.h and include/kvq_bq2.h); this package is its thin ctypes binding plus the seeded
-synthetic workloads and the byte accounting used by the benchmark.
+in include/kvq.h, include/kvq_paged.h and include/kvq_bq2.h); this package is
+its thin ctypes binding plus the seeded synthetic workloads and the byte
+accounting used by the benchmark.
 """
 from ._lib import (  # noqa: F401
     ABI_VERSION, LAYOUT_VERSION, Cache, Geom, KvqError, alloc_workspace,
@@ -20,3 +21,7 @@ from ._lib import (  # noqa: F401
     kvq_bq2_decode_attn, kvq_bq2_decode_combine, kvq_bq2_decode_partial,
     kvq_bq2_decode_workers, kvq_bq2_decode_workspace_bytes, kvq_bq2_prefill,
     kvq_bq2_validate_geom)
+from ._lib import (  # noqa: F401
+    PagedCache, alloc_paged_workspace, kvq_paged_append, kvq_paged_cache_bytes,
+    kvq_paged_decode_attn, kvq_paged_decode_attn_multi, kvq_paged_decode_workspace_bytes,
+    kvq_paged_prefill, kvq_paged_validate)

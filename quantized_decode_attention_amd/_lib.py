@@ -47,6 +47,11 @@ EXPORTS_BQ2 = [
     "kvq_bq2_decode_workspace_bytes", "kvq_bq2_prefill", "kvq_bq2_append",
     "kvq_bq2_decode_attn", "kvq_bq2_decode_partial", "kvq_bq2_decode_combine",
 ]
+EXPORTS_PAGED = [
+    "kvq_paged_validate", "kvq_paged_cache_bytes", "kvq_paged_decode_workspace_bytes",
+    "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_decode_attn",
+    "kvq_paged_decode_attn_multi",
+]
 BQ2_HEAD_DIM = 64
 BQ2_SINKS = 4
 
@@ -69,6 +74,12 @@ class kvq_bq2_geom(ctypes.Structure):
 class kvq_bq2_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "k_codes", "v_codes", "k_meta", "v_meta", "k_sink", "v_sink")]
+
+
+class kvq_paged_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res", "block_table")] + [
+        (n, ctypes.c_int32) for n in ("page_size", "max_pages", "num_pages")]
 
 
 class KvqError(RuntimeError):
@@ -95,7 +106,16 @@ def lib() -> ctypes.CDLL:
         G2 = ctypes.POINTER(kvq_bq2_geom)
         C2 = ctypes.POINTER(kvq_bq2_cache)
         f32 = ctypes.c_float
+        CP = ctypes.POINTER(kvq_paged_cache)
         sig = {
+            "kvq_paged_validate": (ctypes.c_int, [G, CP]),
+            "kvq_paged_cache_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
+            "kvq_paged_decode_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
+            "kvq_paged_prefill": (ctypes.c_int, [G, P, P, i32, CP, P]),
+            "kvq_paged_append": (ctypes.c_int, [G, P, P, P, CP, P]),
+            "kvq_paged_decode_attn": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
+            "kvq_paged_decode_attn_multi": (ctypes.c_int, [G, P, CP, P, i32, i32, f32, P, sz, P,
+                                                           P]),
             "kvq_abi_version": (ctypes.c_int, []),
             "kvq_layout_version": (ctypes.c_int, []),
             "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -379,6 +399,143 @@ def kvq_decode_attn_multi(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torc
 def alloc_multi_workspace(g: Geom, T: int, max_seq_len: int, device="cuda") -> torch.Tensor:
     n = kvq_decode_multi_workspace_bytes(g, T, max_seq_len)
     return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+# ------------------------------------------------------------ paged cache --
+class PagedCache:
+    """Page pools, per-sequence residual windows and block table of one layer
+    (include/kvq_paged.h): pools of `num_pages` pages of `page_size` positions
+    for every KV head; block_table is a device int32 [B][max_pages] tensor
+    (entry [b][j]: the pool page holding positions [j P, (j+1) P) of sequence b)."""
+
+    def __init__(self, g: Geom, page_size: int, num_pages: int, block_table: torch.Tensor,
+                 device="cuda"):
+        P, H, D, G = page_size, g.n_kv_heads, g.head_dim, g.group
+        self.g, self.page_size, self.num_pages = g, page_size, num_pages
+        z = dict(device=device)
+        self.k_codes = torch.zeros((num_pages, H, P // VBLOCK, 64, 2, D * g.k_bits // 128),
+                                   dtype=torch.int32, **z)
+        self.v_codes = torch.zeros((num_pages, H, P // VBLOCK, 64, D * g.v_bits // 64),
+                                   dtype=torch.int32, **z)
+        self.k_meta = torch.zeros((num_pages, H, P // G, D // 8, 8, 2), dtype=torch.int16, **z)
+        self.v_meta = torch.zeros((num_pages, H, P // VBLOCK, 4, D // G, 8, 2),
+                                  dtype=torch.int16, **z)
+        self.k_res = torch.zeros((g.batch, H, g.residual, D), dtype=torch.float16, **z)
+        self.v_res = torch.zeros((g.batch, H, g.residual // 32, D // 16, 64, 8),
+                                 dtype=torch.float16, **z)
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                block_table.shape[0] != g.batch or not block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 [batch][max_pages] tensor")
+        self.block_table = block_table
+        self.max_pages = block_table.shape[1]
+        sizes = kvq_paged_cache_bytes(g, page_size, num_pages)
+        for t, n in zip(self.tensors(), sizes):
+            assert t.numel() * t.element_size() == n
+
+    def tensors(self):
+        return (self.k_codes, self.v_codes, self.k_meta, self.v_meta, self.k_res,
+                self.v_res)
+
+    def view(self, b0: int, b1: int) -> "PagedCache":
+        """Sequences [b0, b1) as a paged cache of batch b1 - b0: the same pools,
+        those sequences' residual windows and table rows."""
+        c = PagedCache.__new__(PagedCache)
+        c.g = Geom(b1 - b0, *[getattr(self.g, f) for f in (
+            "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits", "group",
+            "residual", "capacity")])
+        c.page_size, c.num_pages, c.max_pages = self.page_size, self.num_pages, self.max_pages
+        c.k_codes, c.v_codes, c.k_meta, c.v_meta = (self.k_codes, self.v_codes, self.k_meta,
+                                                    self.v_meta)
+        c.k_res, c.v_res = self.k_res[b0:b1], self.v_res[b0:b1]
+        c.block_table = self.block_table[b0:b1]
+        return c
+
+    def c(self) -> kvq_paged_cache:
+        for t in self.tensors() + (self.block_table,):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("paged cache tensors must be contiguous device tensors")
+        return kvq_paged_cache(*[t.data_ptr() for t in self.tensors()],
+                               self.block_table.data_ptr(), self.page_size, self.max_pages,
+                               self.num_pages)
+
+
+def kvq_paged_validate(g: Geom, page_size: int, max_pages: int, num_pages: int) -> None:
+    gc = g.c()
+    cc = kvq_paged_cache(None, None, None, None, None, None, None, page_size, max_pages,
+                         num_pages)
+    _check(lib().kvq_paged_validate(ctypes.byref(gc), ctypes.byref(cc)), "kvq_paged_validate")
+
+
+def kvq_paged_cache_bytes(g: Geom, page_size: int, num_pages: int) -> list[int]:
+    gc = g.c()
+    out = (ctypes.c_size_t * 6)()
+    _check(lib().kvq_paged_cache_bytes(ctypes.byref(gc), page_size, num_pages, out),
+           "kvq_paged_cache_bytes")
+    return list(out)
+
+
+def kvq_paged_decode_workspace_bytes(g: Geom, T: int, max_seq_len: int) -> int:
+    gc = g.c()
+    out = ctypes.c_size_t()
+    _check(lib().kvq_paged_decode_workspace_bytes(ctypes.byref(gc), T, max_seq_len,
+                                                  ctypes.byref(out)),
+           "kvq_paged_decode_workspace_bytes")
+    return out.value
+
+
+def alloc_paged_workspace(g: Geom, T: int, max_seq_len: int, device="cuda") -> torch.Tensor:
+    n = kvq_paged_decode_workspace_bytes(g, T, max_seq_len)
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def kvq_paged_prefill(g: Geom, k: torch.Tensor, v: torch.Tensor, n: int, cache: PagedCache,
+                      stream=None) -> None:
+    shape = (g.batch, g.n_kv_heads, n, g.head_dim)
+    gc = g.c()
+    cc = cache.c()
+    _check(lib().kvq_paged_prefill(ctypes.byref(gc), _ptr(k, "k", _F16, shape),
+                                   _ptr(v, "v", _F16, shape), n, ctypes.byref(cc),
+                                   _stream(stream)), "kvq_paged_prefill")
+
+
+def kvq_paged_append(g: Geom, k_new: torch.Tensor, v_new: torch.Tensor,
+                     seq_lens: torch.Tensor, cache: PagedCache, stream=None) -> None:
+    shape = (g.batch, g.n_kv_heads, g.head_dim)
+    gc = g.c()
+    cc = cache.c()
+    _check(lib().kvq_paged_append(ctypes.byref(gc), _ptr(k_new, "k_new", _F16, shape),
+                                  _ptr(v_new, "v_new", _F16, shape),
+                                  _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
+                                  ctypes.byref(cc), _stream(stream)), "kvq_paged_append")
+
+
+def kvq_paged_decode_attn_multi(g: Geom, q: torch.Tensor, cache: PagedCache,
+                                seq_lens: torch.Tensor, T: int, max_seq_len: int,
+                                sm_scale: float, workspace: torch.Tensor | None,
+                                out: torch.Tensor, stream=None) -> None:
+    gc = g.c()
+    cc = cache.c()
+    shape = (g.batch, T, g.n_q_heads, g.head_dim)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvq_paged_decode_attn_multi(
+        ctypes.byref(gc), _ptr(q, "q", _F16, shape), ctypes.byref(cc),
+        _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(T), int(max_seq_len),
+        float(sm_scale), _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out", _F16, shape),
+        _stream(stream)), "kvq_paged_decode_attn_multi")
+
+
+def kvq_paged_decode_attn(g: Geom, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
+                          max_seq_len: int, sm_scale: float, workspace: torch.Tensor | None,
+                          out: torch.Tensor, stream=None) -> None:
+    gc = g.c()
+    cc = cache.c()
+    shape = (g.batch, g.n_q_heads, g.head_dim)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvq_paged_decode_attn(
+        ctypes.byref(gc), _ptr(q, "q", _F16, shape), ctypes.byref(cc),
+        _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(max_seq_len), float(sm_scale),
+        _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out", _F16, shape),
+        _stream(stream)), "kvq_paged_decode_attn")
 
 
 def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:

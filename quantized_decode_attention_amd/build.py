@@ -26,6 +26,10 @@ SOURCES = {
     # MFMA accumulators in VGPRs: keeps the O tiles out of AGPR<->VGPR copies
     # around the (rare) softmax rescale.
     "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kvq_decode_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kvq_decode_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kvq_decode_paged_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kvq_decode_paged_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "kvq_bq2_quant.hip": ["-ffp-contract=off"],
     "kvq_bq2_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "kvq_api.cpp": [],

@@ -109,14 +109,16 @@ int cu_count(int* out) {
 }
 
 // Worker waves of the persistent partial kernel (resident waves x CUs) for
-// T query tokens per sequence.
-int workers_for(const kvq_geom* g, int32_t* n_workers, int T = 1) {
+// T query tokens per sequence, over a dense cache or a paged one (pc).
+int workers_for(const kvq_geom* g, int32_t* n_workers, int T = 1, bool paged = false) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != KVQ_OK) return st;
   int w = 0;
-  hipError_t e = kvq::decode_workers(kvq::to_geom(*g), T * (g->n_q_heads / g->n_kv_heads), cus,
-                                     &w);
+  kvq::Geom kg = kvq::to_geom(*g);
+  static const int32_t kAnyTable = 0;  // a non-null table selects the paged kernels
+  if (paged) kg.table = &kAnyTable;
+  hipError_t e = kvq::decode_workers(kg, T * (g->n_q_heads / g->n_kv_heads), cus, &w);
   if (e != hipSuccess) return hip_fail(e, "occupancy query");
   *n_workers = w;
   return KVQ_OK;
@@ -156,12 +158,39 @@ int check_tokens(const kvq_geom* g, int32_t T) {
   return KVQ_OK;
 }
 
+// Page parameters of a paged cache (kvq_paged.h); buffers too if `buffers`.
+int check_paged(const kvq_geom* g, const kvq_paged_cache* c, bool buffers) {
+  if (!c) return fail(KVQ_ERR_NULL, "cache is NULL");
+  const int P = c->page_size;
+  if (P < 32 || (P & (P - 1)) != 0 || P < g->group)
+    return fail(KVQ_ERR_GEOM, "page_size (%d) must be a power of two >= 32 and >= group (%d)", P,
+                g->group);
+  if (c->max_pages < 1 || (int64_t)c->max_pages * P < g->capacity)
+    return fail(KVQ_ERR_GEOM, "max_pages (%d) * page_size (%d) must cover capacity (%d)",
+                c->max_pages, P, g->capacity);
+  if (c->num_pages < 1) return fail(KVQ_ERR_GEOM, "num_pages (%d) must be >= 1", c->num_pages);
+  if (!buffers) return KVQ_OK;
+  const void* p[6] = {c->k_codes, c->v_codes, c->k_meta, c->v_meta, c->k_res, c->v_res};
+  static const char* names[6] = {"k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res"};
+  for (int i = 0; i < 6; ++i) {
+    if (!p[i]) return fail(KVQ_ERR_NULL, "cache.%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(KVQ_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  if (!c->block_table) return fail(KVQ_ERR_NULL, "cache.block_table is NULL");
+  if (reinterpret_cast<uintptr_t>(c->block_table) & 3u)
+    return fail(KVQ_ERR_ALIGN, "cache.block_table is not 4-byte aligned");
+  return KVQ_OK;
+}
+
+// Launch parameters of decode over a dense cache, or over a paged one when
+// pc is given (then `cache` is its pool view).
 int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
                  const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                  void* workspace, size_t workspace_bytes, uint16_t* out,
-                 kvq::DecodeLaunch* L, int32_t T = 1) {
+                 kvq::DecodeLaunch* L, int32_t T = 1, const kvq_paged_cache* pc = nullptr) {
   int st = check_geom(geom);
   if (st != KVQ_OK) return st;
+  if (pc && (st = check_paged(geom, pc, true)) != KVQ_OK) return st;
   if ((st = check_tokens(geom, T)) != KVQ_OK) return st;
   if (T > max_seq_len)
     return fail(KVQ_ERR_RANGE, "T=%d exceeds max_seq_len=%d", T, max_seq_len);
@@ -174,10 +203,10 @@ int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache
     return fail(KVQ_ERR_RANGE, "sm_scale must be finite");
   if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
   int32_t n_workers = 0;
-  if ((st = workers_for(geom, &n_workers, T)) != KVQ_OK) return st;
+  if ((st = workers_for(geom, &n_workers, T, pc != nullptr)) != KVQ_OK) return st;
   if ((st = check_workspace(geom, n_workers, workspace, workspace_bytes, T)) != KVQ_OK)
     return st;
-  L->g = kvq::to_geom(*geom);
+  L->g = pc ? kvq::to_geom(*geom, *pc) : kvq::to_geom(*geom);
   L->q = q;
   L->cache = *cache;
   L->seq_lens = seq_lens;
@@ -652,6 +681,134 @@ int kvq_bq2_decode_attn(const kvq_bq2_geom* geom, const uint16_t* q,
   if (st != KVQ_OK) return st;
   return kvq_bq2_decode_combine(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
                                 workspace_bytes, out, stream);
+}
+
+// ---- paged cache (kvq_paged.h) --------------------------------------------
+
+int kvq_paged_validate(const kvq_geom* geom, const kvq_paged_cache* cache) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    return check_paged(geom, cache, false);
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_cache_bytes(const kvq_geom* geom, int32_t page_size, int32_t num_pages,
+                          size_t out[6]) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
+    kvq_paged_cache c{};
+    c.page_size = page_size;
+    c.num_pages = num_pages;
+    c.max_pages = page_size > 0 ? (geom->capacity + page_size - 1) / page_size : 0;
+    if ((st = check_paged(geom, &c, false)) != KVQ_OK) return st;
+    // a pool page is a dense unit of P positions for each of the Hkv heads
+    const size_t H = geom->n_kv_heads, D = geom->head_dim, G = geom->group,
+                 P = page_size, R = geom->residual, N = num_pages;
+    out[0] = N * H * P * (D * geom->k_bits / 32) * 4;          // k_codes
+    out[1] = N * H * (P / KVQ_VBLOCK) * D * geom->v_bits * 4;  // v_codes
+    out[2] = N * H * (P / G) * D * 2 * 2;                      // k_meta
+    out[3] = N * H * P * (D / G) * 2 * 2;                      // v_meta
+    out[4] = (size_t)geom->batch * H * R * D * 2;              // k_res
+    out[5] = (size_t)geom->batch * H * R * D * 2;              // v_res
+    return KVQ_OK;
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_decode_workspace_bytes(const kvq_geom* geom, int32_t T, int32_t max_seq_len,
+                                     size_t* bytes) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+    if ((st = check_tokens(geom, T)) != KVQ_OK) return st;
+    if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
+    int32_t nw = 0;
+    if ((st = workers_for(geom, &nw, T, true)) != KVQ_OK) return st;
+    *bytes = workspace_need(geom, nw, T);
+    return KVQ_OK;
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_prefill(const kvq_geom* geom, const uint16_t* k, const uint16_t* v, int32_t n,
+                      const kvq_paged_cache* cache, void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_paged(geom, cache, true)) != KVQ_OK) return st;
+    if (n < 0 || n > geom->capacity)
+      return fail(KVQ_ERR_RANGE, "n=%d must be in [0, capacity=%d]", n, geom->capacity);
+    if (n == 0) return KVQ_OK;
+    if ((st = check_ptr(k, "k")) != KVQ_OK) return st;
+    if ((st = check_ptr(v, "v")) != KVQ_OK) return st;
+    const kvq::Geom g = kvq::to_geom(*geom, *cache);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int lq = packed_len(n, g.R);
+    const int64_t stride = (int64_t)n * g.D;
+    hipError_t e = kvq::launch_quantize_keys(g, k, stride, 0, lq, cache->k_codes, cache->k_meta, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill quantize_keys launch");
+    e = kvq::launch_quantize_values(g, v, stride, 0, lq, cache->v_codes, cache->v_meta, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill quantize_values launch");
+    e = kvq::launch_residual_copy(g, k + (int64_t)lq * g.D, v + (int64_t)lq * g.D, stride, lq,
+                                  n - lq, cache->k_res, cache->v_res, s);
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "prefill residual copy launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_append(const kvq_geom* geom, const uint16_t* k_new, const uint16_t* v_new,
+                     const int32_t* seq_lens, const kvq_paged_cache* cache, void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_paged(geom, cache, true)) != KVQ_OK) return st;
+    if ((st = check_ptr(k_new, "k_new")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_new, "v_new")) != KVQ_OK) return st;
+    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
+    hipError_t e = kvq::launch_append(kvq::to_geom(*geom, *cache), k_new, v_new, seq_lens,
+                                      kvq::pool_view(*cache), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "append launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_decode_attn_multi(const kvq_geom* geom, const uint16_t* q,
+                                const kvq_paged_cache* cache, const int32_t* seq_lens,
+                                int32_t T, int32_t max_seq_len, float sm_scale, void* workspace,
+                                size_t workspace_bytes, uint16_t* out, void* stream) {
+  try {
+    if (!cache) return fail(KVQ_ERR_NULL, "cache is NULL");
+    const kvq_cache view = kvq::pool_view(*cache);
+    kvq::DecodeLaunch L;
+    int st = decode_setup(geom, q, &view, seq_lens, max_seq_len, sm_scale, workspace,
+                          workspace_bytes, out, &L, T, cache);
+    if (st != KVQ_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kvq::launch_decode_partial(L, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+    e = kvq::launch_decode_combine(L, s);
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_paged_cache* cache,
+                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                          void* workspace, size_t workspace_bytes, uint16_t* out,
+                          void* stream) {
+  return kvq_paged_decode_attn_multi(geom, q, cache, seq_lens, 1, max_seq_len, sm_scale,
+                                     workspace, workspace_bytes, out, stream);
 }
 
 }  // extern "C"

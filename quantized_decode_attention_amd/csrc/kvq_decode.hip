@@ -1,809 +1,17 @@
-// kvq_decode.hip — single-token decode attention over the packed cache plus
-// the fp16 residual window: split-context partial softmax and combine (gfx950).
-//
-// What is computed (KIVI repository page, "Overview": attention with keys
-// quantized per channel and values per token, the recent tokens kept in fp16;
-// KV1-1.2B model card, "Quickstart": attending over the dequantized cache gives
-// the exact low-bit result):
-//   s_t = sm_scale * q . k_t,  out = sum_t softmax(s)_t v_t
-// with k_t = code * scale + min from the key group's per-channel (scale, min)
-// for packed tokens, the fp16 residual for the rest, and v_t likewise from the
-// token's per-group (scale, min).
-//
-// Algebra on the dequantizer (per key group j and value group gamma):
-//   q . k_t = sum_c (q_c scale_jc) code_tc + sum_c q_c min_jc
-//   sum_t p_t v_tc = sum_t (p_t scale_t,gamma) code_tc + sum_t p_t min_t,gamma
-// so both contractions run on the small integer codes.  On gfx950 they are done
-// by v_mfma_f32_16x16x32_f16 with the codes fed as fp16 subnormals (a code c
-// masked out of a packed word *is* the fp16 number c * 2^-24, which the matrix
-// cores multiply exactly) and the fp32 factors (q * scale, p * scale) split into
-// a high and a low fp16 part, two MFMAs accumulating into the same fp32 tile.
-// The scaled-query and weight operands are computed once per key group / per
-// 32-token chunk; everything per code is a shift and a mask.
-//
-// Work decomposition: a persistent grid of single-wave workgroups, as many
-// as the GPU keeps resident at once.  The 32-token chunks of all (sequence,
-// KV head) units (packed chunks, then the fp16 residual window's chunks, each
-// weighted by its bytes) form one flat list; every wave takes an equal
-// contiguous share of it (so any mix of sequence lengths is balanced) and runs
-// an online softmax over it, writing one partial (max, sum, weighted values)
-// per unit its share touches.  The GQA query heads of a KV head share every
-// load.  The combine kernel (one workgroup per unit) merges a unit's partials:
-//   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
-// Scores are kept in log2 units (sm_scale * log2 e folded into q).
-#include "kvq_device.h"
+// kvq_decode.hip — the decode combine kernel and the routing of partial-kernel
+// launches to their translation unit (head dim, dense or paged cache).
+#include "kvq_decode_impl.h"
 
 namespace kvq {
 namespace {
 
-// ---------------------------------------------------------------------------
-// Packed tokens of one split: MFMA path.  NG = head_dim / group is a template
-// parameter, so the key-group length G = D / NG and the value-tile -> group
-// mapping are compile-time constants (no branches around the accumulators).
-// ---------------------------------------------------------------------------
-template <int D, int BK, int BV, int GQ, int NG>
-struct Cfg {
-  static constexpr int G = D / NG;
-  static constexpr int KC = D / 32;               // k-chunks of a score tile
-  static constexpr int NT = D / 16;               // value channel tiles
-  static constexpr int NW = D * BV / 64;          // value code words per lane
-  static constexpr int KW = kKW<D, BK>;           // key words per lane and row
-  static constexpr int WR = D * BK / 32;          // words per key row
-  static constexpr int SL = 16 / GQ;              // MFMA columns per head
-  static constexpr int NF = (NG + SL - 1) / SL;   // value-side B fragments
-  static constexpr int IPH = 4 * KC;              // fold items per head
-  static constexpr int ITEMS = GQ * IPH;          // fold items per key group
-  static constexpr int IPL = (ITEMS + 63) / 64;   // fold items per lane
-  // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ]
-  static constexpr int kQB = 2 * GQ * 4 * KC * 16;
-  static constexpr int kWaveLds = kQB + 16 * ((GQ * 4 + 4 + 15) / 16);  // + spare beta
-  static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
-};
-
-// Loads of one 32-token chunk (a lane's share).
-template <int D, int BK, int BV, int GQ, int NG>
-struct Raw {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  uint32_t kw[2][C::KW];              // key code words of score tiles 0, 1
-  uint32_t vw[C::NW];                 // value code words (tile n: word n*BV/4)
-  uint32_t vmA[C::NF][4], vmB[C::NF][4];  // value (scale, min) of the B elements
-  uint4 kmA[C::IPL], kmB[C::IPL];     // key (scale, min) of the chunk's group
-};
-
-template <int D, int BK, int BV, int GQ, int NG>
-struct PackedWave {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  using R = Raw<D, BK, BV, GQ, NG>;
-  static constexpr int KC = C::KC, NT = C::NT, KW = C::KW, WR = C::WR, SL = C::SL;
-  static constexpr int NF = C::NF, IPH = C::IPH, IPL = C::IPL, G = C::G;
-  // With two or more MFMA columns per head, the hi and lo parts of q' go to
-  // neighbouring columns (one MFMA per k-chunk, one DPP add to recombine);
-  // with one column per head they are two MFMAs into the same accumulator.
-  static constexpr bool kColSplit = SL >= 2;
-  static constexpr int KP = kColSplit ? 1 : 2;  // q' parts held per lane
-
-  // wave-uniform bases
-  const uint32_t* kcodes;
-  const uint32_t* kmeta;
-  const uint32_t* vcodes;
-  const uint32_t* vmeta;
-  const float* qfs;
-  uint4* qB;
-  float* beta_l;
-  // lane constants
-  int lane, col, lg, hcol, slot;
-  int kofs, vofs;      // this lane's key / value words inside a chunk
-  int vmofs[NF];       // value meta run of fragment f inside a chunk
-  int kmofs[IPL];      // key meta run of fold item i inside a group
-  int kmoff[IPL][2];   // channels of fold item i (runs A and B)
-  int fitem[IPL];
-  float kscale, bscale;
-  float m1;  // -1 in a register (split2)
-  // state
-  f4 oacc[NT];
-  float m_run, l_run;
-  float m_even, m_odd;  // m_run less the classes' log2 factors (packed chunks)
-  float l_odd;          // sum of odd-class weights (scaled by kValOdd)
-  float bias[NF];       // value-min term; odd class kept apart in bias_odd
-  float bias_odd[NF];
-  uint32_t bq[KP][KC][4];
-  float beta_c;
-  int cur_group;
-  int hide;  // newest positions this lane's row must not see: T - 1 - its query token
-
-  __device__ void init(int lane_) {
-    lane = lane_;
-    m1 = opaque_m1();
-    col = lane & 15;
-    lg = lane >> 4;
-    hcol = col / SL;
-    slot = col % SL;
-    kofs = lane * 2 * KW;
-    vofs = lane * C::NW;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) vmofs[f] = (lg * NG + (f * SL + slot) % NG) * 8;
-#pragma unroll
-    for (int i = 0; i < IPL; ++i) {
-      const int it = lane + 64 * i;
-      fitem[i] = it;
-      const int r = it % IPH, gg = r / KC, kc = r % KC;
-      kmofs[i] = r * 8;
-      kmoff[i][0] = key_run0<D, BK>(gg, kc);
-      kmoff[i][1] = kmoff[i][0] + kKeyOff<BK>;
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
-    m_run = kNegInf;
-    m_even = kNegInf;
-    m_odd = kNegInf;
-    l_run = 0.0f;
-    l_odd = 0.0f;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      bias[f] = 0.0f;
-      bias_odd[f] = 0.0f;
-    }
-    beta_c = 0.0f;
-    cur_group = -1;
-    hide = 0;
-  }
-
-  __device__ __forceinline__ void load(int ch, R& r) const {
-    {
-      uint32_t w[2 * KW];
-      load_run<2 * KW>(kcodes + (int64_t)ch * (D * BK) + kofs, w);
-#pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        r.kw[0][k] = w[k];
-        r.kw[1][k] = w[KW + k];
-      }
-    }
-    load_run<C::NW>(vcodes + (int64_t)ch * (D * BV) + vofs, r.vw);
-    // value (scale, min) of tokens 8 lg + j: even j feed B elements 2i (run
-    // A), odd j elements 2i + 1 (run B)
-    const uint32_t* vm = vmeta + (int64_t)ch * (4 * NG * 8);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      uint32_t w[8];
-      load_run<8>(vm + vmofs[f], w);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r.vmA[f][i] = w[2 * i];
-        r.vmB[f][i] = w[2 * i + 1];
-      }
-    }
-    // key meta of the chunk's group, with the chunk's other loads (one
-    // in-order stream, so waiting for a chunk never waits for a later one).
-    // Entry e of an item is channel run A + e/2 (even e) or run B + e/2 (odd).
-    // Lanes past the fold items load an in-range run too (the run depends on
-    // the item modulo a head's items): no load sits under a branch.
-    const uint32_t* km = kmeta + (int64_t)((ch * kChunk) / G) * D;
-#pragma unroll
-    for (int i = 0; i < IPL; ++i) {
-      uint32_t w[8];
-      load_run<8>(km + kmofs[i], w);
-      r.kmA[i] = make_uint4(w[0], w[2], w[4], w[6]);
-      r.kmB[i] = make_uint4(w[1], w[3], w[5], w[7]);
-    }
-  }
-
-  // q' = q * 2^-E * key scale (hi/lo fp16 fragments in LDS) and beta' =
-  // q * 2^-E . key min, for the key group starting in this chunk.
-  __device__ __forceinline__ void fold(const R& r) {
-#pragma unroll
-    for (int i = 0; i < IPL; ++i) {
-      const int it = fitem[i];
-      float bpart = 0.0f;
-      // (when the items fill the wave exactly the test is compile-time true)
-      if (C::ITEMS % 64 == 0 || it < C::ITEMS) {
-        const int h = it / IPH, rr = it % IPH, gg = rr / KC, kc = rr % KC;
-        const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][0]);
-        const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][1]);
-        const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qBv[4] = {qb.x, qb.y, qb.z, qb.w};
-        const uint32_t mA[4] = {r.kmA[i].x, r.kmA[i].y, r.kmA[i].z, r.kmA[i].w};
-        const uint32_t mB[4] = {r.kmB[i].x, r.kmB[i].y, r.kmB[i].z, r.kmB[i].w};
-        uint32_t hp[4], lp[4];
-        float bodd = 0.0f;  // odd channels (their q' carries kKeyOddQ)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), m1, hp[e], lp[e]);
-          if (e & 1) {
-            bodd = mul_hi(qA[e], mA[e], bodd);
-            bodd = mul_hi(qBv[e], mB[e], bodd);
-          } else {
-            bpart = mul_hi(qA[e], mA[e], bpart);
-            bpart = mul_hi(qBv[e], mB[e], bpart);
-          }
-        }
-        // beta = q . min with the channel factors taken back out
-        bpart = __builtin_fmaf(bodd, 1.0f / kKeyOddQ<BK>, bpart * (1.0f / kKeyEvenQ<BK>));
-        qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
-        qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
-      }
-      bpart = group_sum<IPH>(bpart);
-      // every lane stores (no branch): a head's first item lane its beta, the
-      // others a spare slot
-      const bool lead = (C::ITEMS % 64 == 0 || it < C::ITEMS) && (it % IPH) == 0;
-      beta_l[lead ? it / IPH : GQ] = bpart;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int p = 0; p < KP; ++p)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int part = kColSplit ? (slot & 1) : p;
-        const uint4 v = qB[((part * GQ + hcol) * 4 + lg) * KC + kc];
-        bq[p][kc][0] = v.x; bq[p][kc][1] = v.y; bq[p][kc][2] = v.z; bq[p][kc][3] = v.w;
-      }
-    beta_c = beta_l[hcol] * bscale;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // Online softmax over a chunk's scores (exact running max; rescale only
-  // when it grows).  Each lane tests its own 8 scores; the cross-lane maximum
-  // is only formed on the (rare) path where some lane sees a larger score.
-  // kPacked: weights carry the value classes' factors (q < 2: kValEven,
-  // q >= 2: kValOdd) and their sums are kept per class; otherwise plain.
-  template <bool kPacked>
-  __device__ __forceinline__ void softmax(const float (&s)[2][4], float (&p)[2][4]) {
-    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    if (__any(cm > m_run)) {
-      cm = xor_max(cm, 16);
-      cm = xor_max(cm, 32);
-      const float m_new = fmaxf(m_run, cm);
-      const float a = exp2_hw(m_run - m_new);
-      m_run = m_new;
-      m_even = m_new - kValEvenLog2<BV>;
-      m_odd = m_new - kValOddLog2;
-      l_run *= a;
-      l_odd *= a;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) oacc[n] *= a;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        bias[f] *= a;
-        bias_odd[f] *= a;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (kPacked) {
-          p[u][q] = exp2_hw(s[u][q] - (q < 2 ? m_even : m_odd));
-          if (q < 2)
-            l_run += p[u][q];
-          else
-            l_odd += p[u][q];
-        } else {
-          p[u][q] = exp2_hw(s[u][q] - m_run);
-          l_run += p[u][q];
-        }
-      }
-  }
-
-  // Packed accumulation to real scale (codes were fp16 numbers c * 2^-24,
-  // pairs carry kValEven) with its value-min term added; class sums folded.
-  // Afterwards the state is plain (as the residual path needs).
-  __device__ __forceinline__ void to_real() {
-    // the value-min term is summed over the four lane groups (token subsets)
-    float btot[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const float bt = __builtin_fmaf(bias_odd[f], 1.0f / kValOdd<BV>,
-                                      bias[f] * (1.0f / kValEven<BV>));
-      btot[f] = xor_sum(xor_sum(bt, 16), 32);
-      bias[f] = 0.0f;
-      bias_odd[f] = 0.0f;
-    }
-    constexpr float oscale = 16777216.0f / kValEven<BV>;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float bsum = btot[C::gam(n) / SL];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], oscale, bsum);
-    }
-    l_run = __builtin_fmaf(l_odd, 1.0f / kValOdd<BV>, l_run * (1.0f / kValEven<BV>));
-    l_odd = 0.0f;
-    m_even = m_run;
-    m_odd = m_run;
-  }
-
-  // Switch to the residual window: bring the packed accumulation to real scale
-  // (codes were fp16 numbers c * 2^-24) with its value-min term added, and set
-  // the key-side B fragments to q * 2^-E in natural channel order (element j of
-  // lane group g, k-chunk kc = channel 32 kc + 8 g + j), hi or lo part.
-  __device__ __forceinline__ void enter_residual() {
-    to_real();
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg);
-      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg + 4);
-      // channel 32 kc + 8 lg + j: parity of j; the key-side factors come out
-      constexpr float ue = 1.0f / kKeyEvenQ<BK>, uo = 1.0f / kKeyOddQ<BK>;
-      const float qv[8] = {qa.x * ue, qa.y * uo, qa.z * ue, qa.w * uo,
-                           qb.x * ue, qb.y * uo, qb.z * ue, qb.w * uo};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t hi, lo;
-        split2(qv[2 * i], qv[2 * i + 1], m1, hi, lo);
-        if constexpr (kColSplit) {
-          bq[0][kc][i] = (slot & 1) ? lo : hi;
-        } else {
-          bq[0][kc][i] = hi;
-          bq[1][kc][i] = lo;
-        }
-      }
-    }
-    cur_group = -1;
-  }
-
-  // Residual chunk: fp16 tokens t0 + [0, 32) of the window (those >= n_tok
-  // masked).  Keys come straight from the window's slot rows; values are
-  // stored in the value consumer order, so tile n's A operand is one 16-byte
-  // load per lane (slots past n_tok are zeroed in registers: their weight is
-  // 0, and the window may hold anything there).
-  __device__ __forceinline__ void process_residual(int t0, int n_tok, int R,
-                                                   const uint16_t* kres,
-                                                   const uint16_t* vres) {
-    // value operands first: their loads overlap the score MFMAs
-    const uint4* vq = reinterpret_cast<const uint4*>(vres) +
-                      (int64_t)((t0 % R) / kChunk) * (D / 16) * 64 + lane;
-    uint4 va[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) va[n] = vq[n * 64];
-    uint32_t vmask[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 8 * lg + 2 * i;
-      vmask[i] = (t < n_tok ? 0x0000ffffu : 0u) | (t + 1 < n_tok ? 0xffff0000u : 0u);
-    }
-    // scores: tile u row r = token key_row_token(u, r)
-    const float kscale_r = bscale;  // keys are real fp16 values here
-    float s[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tin = t0 + key_row_token(u, col);
-      const int slot_in = (tin < n_tok ? tin : n_tok - 1) % R;
-      const uint4* krow = reinterpret_cast<const uint4*>(kres + (int64_t)slot_in * D);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const uint4 kv = krow[4 * kc + lg];
-        const uint32_t a[4] = {kv.x, kv.y, kv.z, kv.w};
-        acc = mfma(a, bq[0][kc], acc);
-        if constexpr (!kColSplit) acc = mfma(a, bq[1][kc], acc);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float x = acc[q];
-        if constexpr (kColSplit) {
-          x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                   __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
-        }
-        const bool valid = t0 + 8 * lg + 4 * u + q < n_tok - hide;
-        s[u][q] = valid ? x * kscale_r : kNegInf;
-      }
-    }
-    float p[2][4];
-    softmax<false>(s, p);
-    uint32_t bh[4], bl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], m1, bh[i], bl[i]);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint32_t a[4] = {va[n].x & vmask[0], va[n].y & vmask[1], va[n].z & vmask[2],
-                             va[n].w & vmask[3]};
-      oacc[n] = mfma(a, bh, oacc[n]);
-      oacc[n] = mfma(a, bl, oacc[n]);
-    }
-  }
-
-  // kMask: positions after last_vis (this lane's row, 32-token chunk ch) get
-  // score -inf (the causal mask of a multi-token query; their codes and meta
-  // are real cache data, so their weight 0 is exact).
-  template <bool kMask = false>
-  __device__ __forceinline__ void process(int ch, const R& r, int last_vis = 0) {
-    if constexpr (G == kChunk) {
-      fold(r);  // every chunk is a key group: no branch, so the fold can be
-                // scheduled against the previous chunk's value products
-    } else {
-      const int grp = (ch * kChunk) / G;
-      if (grp != cur_group) {
-        cur_group = grp;
-        fold(r);
-      }
-    }
-    // scores: s = 2^(E+24) * (codes x q') + beta
-    float s[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      uint32_t a[KC][4];
-      unpack_keys<D, BK>(r.kw[u], a);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        acc = mfma(a[kc], bq[0][kc], acc);
-        if constexpr (!kColSplit) acc = mfma(a[kc], bq[1][kc], acc);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float x = acc[q];
-        if constexpr (kColSplit) {
-          // hi column + lo column (lanes col and col ^ 1 of a quad)
-          x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                   __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
-        }
-        s[u][q] = __builtin_fmaf(x, kscale, beta_c);
-        if constexpr (kMask)
-          s[u][q] = ch * kChunk + 8 * lg + 4 * u + q <= last_vis ? s[u][q] : kNegInf;
-      }
-    }
-    float p[2][4];
-    softmax<true>(s, p);
-    // weighted value sum
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      uint32_t bh[4], bl[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // elements 2i (run A) and 2i+1 (run B) = score tile i/2, rows 2(i%2), +1;
-        // odd i is the odd class
-        const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
-        split2(mul_lo(pa, r.vmA[f][i]), mul_lo(pb, r.vmB[f][i]), m1, bh[i], bl[i]);
-        float& bacc = (i & 1) ? bias_odd[f] : bias[f];
-        bacc = mul_hi(pa, r.vmA[f][i], bacc);
-        bacc = mul_hi(pb, r.vmB[f][i], bacc);
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        if (C::gam(n) / SL != f) continue;  // compile-time
-        uint32_t a[4];
-        if constexpr (BV == 4) {
-          // pair e: (w >> 8 (e/2)) masked at bits 4 (e%2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] = (r.vw[n] >> (8 * (e >> 1))) & ((e & 1) ? 0x00F000F0u : 0x000F000Fu);
-        } else {
-          // tile parity selects the byte; pair e: (w' >> 4 (e/2)) at bits 2 (e%2)
-          const uint32_t x = r.vw[n >> 1] >> (8 * (n & 1));
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] = (x >> (4 * (e >> 1))) & ((e & 1) ? 0x000C000Cu : 0x00030003u);
-        }
-        oacc[n] = mfma(a, bh, oacc[n]);
-        oacc[n] = mfma(a, bl, oacc[n]);
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Work of a sequence in this format: packed 32-token chunks (one work unit
-// each) followed by the 32-token chunks of its fp16 residual window (rw work
-// units each: rw ~ fp16 bytes / packed bytes per token, so that work units
-// stand for equal HBM traffic).  The decomposition itself (kvq_device.h) cuts
-// the flat list of all units' work into equal shares, one per worker wave.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ SeqWork seq_work_of(const DecodeLaunch& L, int n) {
-  SeqWork sw{0, 0, 0, 0};
-  if (n <= 0 || n > L.g.C || n > L.max_seq_len) return sw;
-  const int lq = packed_len(n, L.g.R);
-  sw.n = n;
-  sw.nq = lq / kChunk;
-  sw.nr = (n - lq + kChunk - 1) / kChunk;
-  sw.w = sw.nq + sw.nr * L.rw;
-  return sw;
-}
-
-__device__ __forceinline__ SeqWork seq_work(const DecodeLaunch& L, int b) {
-  return seq_work_of(L, L.seq_lens[b]);
-}
-
-// Row j of unit (b, hkv) is query token j / (Hq/Hkv) of the last T, head
-// hkv * Hq/Hkv + j % (Hq/Hkv): q and out are [B][T][Hq][D].
-__device__ __forceinline__ int64_t qrow(const DecodeLaunch& L, int b, int hkv, int j) {
-  const int gr = L.g.Hq / L.g.Hkv;
-  return ((int64_t)b * L.T + j / gr) * L.g.Hq + hkv * gr + j % gr;
-}
-
-struct KiviWork {
-  using Launch = DecodeLaunch;
-  static constexpr bool kRotateOut = false;
-  static __device__ __forceinline__ int64_t row(const DecodeLaunch& L, int b, int hkv, int j) {
-    return qrow(L, b, hkv, j);
-  }
-  static __device__ __forceinline__ SeqWork work_of(const DecodeLaunch& L, int n) {
-    return seq_work_of(L, n);
-  }
-};
-
-template <int D, int BK, int BV, int GQ, int NG>
-constexpr int kWaveSmem = GQ * D * 4 + Cfg<D, BK, BV, GQ, NG>::kWaveLds;
-
-// Sets up the wave for unit (b, hkv) and issues the loads of the range's first
-// packed chunk into ra (before anything else, so that their latency overlaps
-// the query's).
-template <int D, int BK, int BV, int GQ, int NG>
-__device__ __forceinline__ void seg_begin(const DecodeLaunch& L, int64_t unit, const SegRange& r,
-                                          char* smem, int lane, PackedWave<D, BK, BV, GQ, NG>& w,
-                                          Raw<D, BK, BV, GQ, NG>& ra) {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  const Geom& g = L.g;
-  char* wl = smem + GQ * D * 4;
-  w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
-  w.kmeta = reinterpret_cast<const uint32_t*>(L.cache.k_meta) + unit * (g.C / C::G) * D;
-  w.vcodes = L.cache.v_codes + unit * (g.C / kVBlock) * D * BV;
-  w.vmeta = reinterpret_cast<const uint32_t*>(L.cache.v_meta) +
-            unit * (g.C / kVBlock) * NG * kVBlock;
-  w.qfs = reinterpret_cast<float*>(smem);
-  w.qB = reinterpret_cast<uint4*>(wl);
-  w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
-  w.init(lane);
-  if (r.pc0 < r.pc1) w.load(r.pc0, ra);
-}
-
-// Runs the range of unit (b, hkv) -> partial p, seg_begin having been done.
-template <int D, int BK, int BV, int GQ, int NG>
-__device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
-                        const SegRange& r, int p, char* smem, int lane,
-                        PackedWave<D, BK, BV, GQ, NG>& w, Raw<D, BK, BV, GQ, NG>& ra) {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  using R = Raw<D, BK, BV, GQ, NG>;
-  constexpr int NT = C::NT, SL = C::SL;
-  constexpr int QPH = D / 64;  // query values per lane and head
-  constexpr int DP = D + kPartPad;
-  const Geom& g = L.g;
-  const int64_t unit = (int64_t)b * g.Hkv + hkv;
-  float* part_base = L.ws + (int64_t)p * GQ * DP;
-  float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
-  const int pc0 = r.pc0, pc1 = r.pc1, rk0 = r.rk0, rk1 = r.rk1;
-  R rb;
-  // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
-  // that q * 2^-E * scale fits fp16
-  int eh[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const uint16_t* qg = L.q + qrow(L, b, hkv, h) * D;
-    float qv[QPH];
-    float mx = 0.0f;
-#pragma unroll
-    for (int k = 0; k < QPH; ++k) {
-      qv[k] = h2f(qg[lane + 64 * k]) * L.scale_log2;
-      mx = fmaxf(mx, fabsf(qv[k]));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = xor_max(mx, off);
-    int e = 0;
-    if (mx > 0.0f) (void)frexpf(mx, &e);
-    eh[h] = e;
-#pragma unroll
-    for (int k = 0; k < QPH; ++k)  // channel lane + 64 k has the parity of lane
-      qfs[h * D + lane + 64 * k] =
-          ldexpf(qv[k], -e) * ((lane & 1) ? kKeyOddQ<BK> : kKeyEvenQ<BK>);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  int e_mine = 0;
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
-    if (w.hcol == h) e_mine = eh[h];
-  // codes are the fp16 numbers c * 2^-24, pairs carry the key-side factor
-  w.kscale = ldexpf(1.0f, e_mine + 24 - kKeyAccLog2<BK>);
-  w.bscale = ldexpf(1.0f, e_mine);
-
-  // rows of query token i (of the last T) do not see the newest T - 1 - i
-  // positions; packed chunks holding a position past n - T are processed
-  // apart, with the mask (never for a single query token: the newest packed
-  // position is at most n - 2)
-  w.hide = L.T - 1 - w.hcol / (g.Hq / g.Hkv);
-  const int last_vis = sw.n - 1 - w.hide;
-  const int pm = min(pc1, max(pc0, (sw.n - L.T + 1) / kChunk));
-  if (pc0 < pm) {
-    // two chunk buffers: the next chunk's loads are in flight while one is
-    // used (a deeper ring measured no faster).  Prefetches past the last
-    // chunk re-load that chunk (always in bounds) instead of being skipped,
-    // so no load sits under a branch.
-    const int last = pm - 1;
-    int ch = pc0;
-    for (; ch < last; ch += 2) {  // pairs; ra holds chunk ch on entry
-      w.load(ch + 1, rb);
-      w.process(ch, ra);
-      w.load(min(ch + 2, last), ra);
-      w.process(ch + 1, rb);
-    }
-    if (ch == last) w.process(ch, ra);  // odd count: the last chunk is in ra
-  }
-  for (int ch = pm; ch < pc1; ++ch) {  // ra holds chunk pc0 if pm == pc0
-    if (ch != pc0) w.load(ch, ra);
-    w.template process<true>(ch, ra, last_vis);
-  }
-  const bool resid = rk0 < rk1;
-  if (resid) {
-    w.enter_residual();
-    const uint16_t* kres = L.cache.k_res + unit * g.R * D;
-    const uint16_t* vres = L.cache.v_res + unit * g.R * D;
-    const int lq = sw.nq * kChunk;
-    for (int k = rk0; k < rk1; ++k) w.process_residual(lq + k * kChunk, sw.n, g.R, kres, vres);
-  }
-
-  // partial: O (value-min term included), max, sum of this wave's tokens
-  if (!resid) w.to_real();
-  float l_run = w.l_run;
-  l_run = xor_sum(l_run, 16);
-  l_run = xor_sum(l_run, 32);
-  float* part = part_base + w.hcol * DP;
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int gm = C::gam(n);
-    if (gm % SL != w.slot) continue;
-    const float4 v = make_float4(w.oacc[n][0], w.oacc[n][1], w.oacc[n][2], w.oacc[n][3]);
-    *reinterpret_cast<float4*>(part + 16 * n + 4 * w.lg) = v;
-  }
-  if (w.lg == 0 && w.slot == 0) {
-    part[D] = w.m_run;
-    part[D + 1] = l_run;
-  }
-  // the next segment of this wave rewrites the LDS buffers
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-
-// The part of unit (b, hkv) in work range [x0, x1) -> partial p.  xu = first
-// work unit of the unit.
-template <int D, int BK, int BV, int GQ, int NG>
-__device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
-                             int xu, int x0, int x1, int p, char* smem, int lane) {
-  constexpr int DP = D + kPartPad;
-  const SegRange r = seg_range(L, sw, xu, x0, x1);
-  if (r.pc0 >= r.pc1 && r.rk0 >= r.rk1) {  // only part of a residual chunk's weight
-    // an empty partial: zero sums, max -inf (weight 0 in the merge)
-    float* part_base = L.ws + (int64_t)p * GQ * DP;
-    for (int i = lane; i < GQ * DP; i += 64) {
-      const int c = i % DP;
-      part_base[i] = (c == D) ? kNegInf : 0.0f;
-    }
-    return;
-  }
-  PackedWave<D, BK, BV, GQ, NG> w;
-  Raw<D, BK, BV, GQ, NG> ra;
-  seg_begin<D, BK, BV, GQ, NG>(L, (int64_t)b * L.g.Hkv + hkv, r, smem, lane, w, ra);
-  seg_run<D, BK, BV, GQ, NG>(L, b, hkv, sw, r, p, smem, lane, w, ra);
-}
-
-// One wave per workgroup; grid = the number of worker waves.
-template <int D, int BK, int BV, int GQ, int NG>
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
-  __shared__ __attribute__((aligned(16))) char smem[kWaveSmem<D, BK, BV, GQ, NG>];
-  const int lane = threadIdx.x;
-  const int w = blockIdx.x, nw = gridDim.x;
-  // Speculation: if every length equals max_seq_len (a uniform batch), the
-  // work layout is plain arithmetic, so the first segment's first chunk can
-  // be requested before the lengths are read.  The loads are in bounds
-  // whatever the lengths; they are used only if the lengths confirm it.
-  using PW = PackedWave<D, BK, BV, GQ, NG>;
-  using RW = Raw<D, BK, BV, GQ, NG>;
-  const SeqWork ss = seq_work_of(L, L.max_seq_len);
-  const int per_seq = ss.w * L.g.Hkv;
-  const int cpw_s = (per_seq * L.g.B + nw - 1) / nw;
-  const int x0_s = w * cpw_s, x1_s = min(per_seq * L.g.B, x0_s + cpw_s);
-  bool spec = ss.w > 0 && x0_s < x1_s;
-  int b_s = 0, hkv_s = 0, xu_s = 0;
-  SegRange r_s{0, 0, 0, 0};
-  if (spec) {
-    b_s = x0_s / per_seq;
-    hkv_s = (x0_s - b_s * per_seq) / ss.w;
-    xu_s = b_s * per_seq + hkv_s * ss.w;
-    r_s = seg_range(L, ss, xu_s, x0_s, x1_s);
-    spec = r_s.pc0 < r_s.pc1;
-  }
-  PW ws;
-  RW ra_s;
-  if (spec) seg_begin<D, BK, BV, GQ, NG>(L, (int64_t)b_s * L.g.Hkv + hkv_s, r_s, smem, lane, ws, ra_s);
-
-  const BatchWork bw = batch_work<KiviWork>(L, lane);  // one read of the lengths
-  const int total = bw.total;
-  const int cpw = (total + nw - 1) / nw;
-  const int x0 = w * cpw;
-  const int x1 = min(total, x0 + cpw);
-  int x = x0;
-  if (spec && bw.uniform) {  // confirmed: the speculative first segment stands
-    seg_run<D, BK, BV, GQ, NG>(L, b_s, hkv_s, ss, r_s, w + b_s * L.g.Hkv + hkv_s, smem, lane,
-                               ws, ra_s);
-    x = xu_s + ss.w;
-  }
-  while (x < x1) {
-    int b, base;
-    wave_find_seq<KiviWork>(L, bw, lane, x, b, base);
-    b = __builtin_amdgcn_readfirstlane(b);
-    base = __builtin_amdgcn_readfirstlane(base);
-    const SeqWork sw = seq_work(L, b);
-    const int hkv = (x - base) / sw.w;
-    const int xu = base + hkv * sw.w;
-    unit_segment<D, BK, BV, GQ, NG>(L, b, hkv, sw, xu, x0, x1, w + b * L.g.Hkv + hkv, smem,
-                                    lane);
-    x = xu + sw.w;
-  }
-}
-
-// Worker waves the partial kernel of this instantiation is launched with:
-// resident waves per compute unit (from the kernel's resources) x CUs, cached
-// per device.
-template <int D, int BK, int BV, int GQ, int NG>
-hipError_t workers_of(int cus, int* out) {
-  static int cache[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
-    return hipSuccess;
-  }
-  int nb = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &nb, decode_partial_kernel<D, BK, BV, GQ, NG>, 64, 0);
-  if (e != hipSuccess) return e;
-  if (nb < 1) nb = 1;
-  const int w = nb * cus;
-  if (dev >= 0 && dev < 64) cache[dev] = w;
-  *out = w;
-  return hipSuccess;
-}
-
-// Op: 0 = launch the partial kernel, 1 = query its worker count.
-template <int D, int BK, int BV, int GQ, int NG>
-hipError_t run(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  if (op == 1) return workers_of<D, BK, BV, GQ, NG>(cus, workers);
-  decode_partial_kernel<D, BK, BV, GQ, NG><<<dim3(L.n_workers), 64, 0, st>>>(L);
-  return hipGetLastError();
-}
-
-template <int D, int BK, int BV, int GQ>
-hipError_t dispatch_ng(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  switch (D / L.g.G) {
-    case 1: return run<D, BK, BV, GQ, 1>(L, op, cus, workers, st);
-    case 2: return run<D, BK, BV, GQ, 2>(L, op, cus, workers, st);
-    case 4:
-      if constexpr (D == 128) return run<D, BK, BV, GQ, 4>(L, op, cus, workers, st);
-      [[fallthrough]];
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int D, int BK, int BV>
-hipError_t dispatch_gq(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  switch (L.gq) {
-    case 1: return dispatch_ng<D, BK, BV, 1>(L, op, cus, workers, st);
-    case 2: return dispatch_ng<D, BK, BV, 2>(L, op, cus, workers, st);
-    case 4: return dispatch_ng<D, BK, BV, 4>(L, op, cus, workers, st);
-    case 8: return dispatch_ng<D, BK, BV, 8>(L, op, cus, workers, st);
-    case 16: return dispatch_ng<D, BK, BV, 16>(L, op, cus, workers, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int D>
-hipError_t dispatch_bits(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  const int bk = L.g.bK, bv = L.g.bV;
-  if (bk == 2 && bv == 2) return dispatch_gq<D, 2, 2>(L, op, cus, workers, st);
-  if (bk == 2 && bv == 4) return dispatch_gq<D, 2, 4>(L, op, cus, workers, st);
-  if (bk == 4 && bv == 2) return dispatch_gq<D, 4, 2>(L, op, cus, workers, st);
-  return dispatch_gq<D, 4, 4>(L, op, cus, workers, st);
-}
-
-hipError_t dispatch(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  return L.g.D == 64 ? dispatch_bits<64>(L, op, cus, workers, st)
-                     : dispatch_bits<128>(L, op, cus, workers, st);
+hipError_t partial_entry(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
+  const bool paged = L.g.table != nullptr;
+  if (L.g.D == 64)
+    return paged ? decode_partial_paged_d64(L, op, cus, workers, st)
+                 : decode_partial_d64(L, op, cus, workers, st);
+  return paged ? decode_partial_paged_d128(L, op, cus, workers, st)
+               : decode_partial_d128(L, op, cus, workers, st);
 }
 
 template <int D>
@@ -826,11 +34,11 @@ hipError_t decode_workers(const Geom& g, int gq, int cus, int* workers) {
   DecodeLaunch L{};
   L.g = g;
   L.gq = gq;
-  return dispatch(L, 1, cus, workers, nullptr);
+  return partial_entry(L, 1, cus, workers, nullptr);
 }
 
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st) {
-  return dispatch(L, 0, 0, nullptr, st);
+  return partial_entry(L, 0, 0, nullptr, st);
 }
 
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st) {

@@ -8,6 +8,7 @@
 
 #include "../../include/kvq.h"
 #include "../../include/kvq_bq2.h"
+#include "../../include/kvq_paged.h"
 
 namespace kvq {
 
@@ -23,14 +24,51 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return __half_as_ushort(__float2half_rn(f));
 }
 
-// Geometry as kernels see it (validated on the host).
+// Geometry as kernels see it (validated on the host).  Packed 32-position
+// chunks are addressed through chunk slots (chunk_slot below): with table ==
+// nullptr the cache is dense (kvq.h), otherwise paged (kvq_paged.h) with
+// pages of 32 << cpp_log2 positions.
 struct Geom {
   int B, Hq, Hkv, D, bK, bV, G, R, C;
+  const int32_t* table;  // block table [B][maxp], or nullptr (dense)
+  int cpp_log2;          // log2 of the 32-position chunks per page
+  int maxp;              // table entries per sequence
+  int npages;            // pages in the pools
 };
 
 inline Geom to_geom(const kvq_geom& g) {
   return Geom{g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, g.k_bits,
-              g.v_bits, g.group, g.residual, g.capacity};
+              g.v_bits, g.group, g.residual, g.capacity, nullptr, 0, 0, 0};
+}
+
+inline Geom to_geom(const kvq_geom& g, const kvq_paged_cache& c) {
+  Geom r = to_geom(g);
+  r.table = c.block_table;
+  r.cpp_log2 = __builtin_ctz((unsigned)c.page_size / KVQ_VBLOCK);
+  r.maxp = c.max_pages;
+  r.npages = c.num_pages;
+  return r;
+}
+
+// The dense buffers of kvq_cache standing for a paged cache's pools and
+// residual windows (every launcher addresses packed data by chunk slot).
+inline kvq_cache pool_view(const kvq_paged_cache& c) {
+  return kvq_cache{c.k_codes, c.v_codes, c.k_meta, c.v_meta, c.k_res, c.v_res};
+}
+
+// Slot of 32-position chunk k of unit (b, hkv) = b * Hkv + hkv in the packed
+// buffers: rows of 32 positions, one after the other.  The dense layout is the
+// paged one with a single page of C positions per unit; a paged cache puts the
+// chunk in page table[b][k / chunks per page], whose Hkv units are stored one
+// after the other.  -1 if the table entry is not a page of the pool.  The key
+// group starting at position p (a multiple of G) has meta slot
+// chunk_slot(p / 32) * 32 / G, as every page holds whole key groups.
+__device__ __forceinline__ int64_t chunk_slot(const Geom& g, int64_t unit, int k) {
+  if (g.table == nullptr) return unit * (g.C / KVQ_VBLOCK) + k;
+  const int64_t b = unit / g.Hkv, hkv = unit % g.Hkv;
+  const int pg = g.table[b * g.maxp + (k >> g.cpp_log2)];
+  if (pg < 0 || pg >= g.npages) return -1;
+  return (((int64_t)pg * g.Hkv + hkv) << g.cpp_log2) + (k & ((1 << g.cpp_log2) - 1));
 }
 
 // 64-bit element offsets into the cache buffers.
@@ -70,8 +108,18 @@ struct DecodeLaunch {
   uint16_t* out;      // [B][T][Hq][D]
 };
 // Worker waves of the partial kernel for gq rows per KV head on the current
-// device.
+// device (dense or paged as g.table says).
 hipError_t decode_workers(const Geom& g, int gq, int cus, int* workers);
+// The partial kernels by head dim and cache form: op 0 launches, op 1 puts
+// the worker count in *workers.
+hipError_t decode_partial_d64(const DecodeLaunch& L, int op, int cus, int* workers,
+                              hipStream_t st);
+hipError_t decode_partial_d128(const DecodeLaunch& L, int op, int cus, int* workers,
+                               hipStream_t st);
+hipError_t decode_partial_paged_d64(const DecodeLaunch& L, int op, int cus, int* workers,
+                                    hipStream_t st);
+hipError_t decode_partial_paged_d128(const DecodeLaunch& L, int op, int cus, int* workers,
+                                     hipStream_t st);
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st);
 

@@ -113,6 +113,10 @@ template <int BITS>
 __device__ void key_group(const Geom& g, int64_t unit, int32_t pos, uint32_t* k_codes,
                           uint16_t* k_meta, const uint16_t* tile, uint8_t* codes) {
   const int G = g.G, D = g.D;
+  // slot of the group's first chunk; its other chunks follow it (a page holds
+  // whole key groups).  A table entry outside the pool: nothing is written.
+  const int64_t cs0 = chunk_slot(g, unit, pos / kVBlock);
+  if (cs0 < 0) return;  // uniform over the workgroup
   const int tpc = kThreads / D;            // threads per channel (2 or 4)
   const int c = threadIdx.x / tpc, part = threadIdx.x % tpc;
   const int tn = G / tpc;                  // tokens of this thread
@@ -129,7 +133,7 @@ __device__ void key_group(const Geom& g, int64_t unit, int32_t pos, uint32_t* k_
   const GroupParams p = group_params(mn, mx, BITS);
   if (part == 0) {
     uint32_t* meta32 = reinterpret_cast<uint32_t*>(k_meta);
-    meta32[(unit * (g.C / G) + pos / G) * D + key_meta_entry<BITS>(c, D)] =
+    meta32[cs0 * kVBlock / G * D + key_meta_entry<BITS>(c, D)] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
   }
   for (int t = part * tn; t < (part + 1) * tn; ++t)
@@ -150,8 +154,8 @@ __device__ void key_group(const Geom& g, int64_t unit, int32_t pos, uint32_t* k_
     const int p_tok = pos + t, tau = p_tok % kVBlock;
     const int u = (tau >> 2) & 1, i = 4 * (tau >> 3) + (tau & 3);
     const int lane = 16 * (wr / KW) + i;
-    k_codes[(unit * (g.C / kVBlock) + p_tok / kVBlock) * (int64_t)(D * BITS) +
-            (2 * lane + u) * KW + wr % KW] = word;
+    k_codes[(cs0 + p_tok / kVBlock - pos / kVBlock) * (D * BITS) + (2 * lane + u) * KW +
+            wr % KW] = word;
   }
 }
 
@@ -162,6 +166,8 @@ template <int BITS>
 __device__ void value_block(const Geom& g, int64_t unit, int32_t pos, uint32_t* v_codes,
                             uint16_t* v_meta, const uint16_t* tile, uint8_t* codes) {
   const int G = g.G, D = g.D, NG = D / G;
+  const int64_t cs = chunk_slot(g, unit, pos / kVBlock);
+  if (cs < 0) return;  // a table entry outside the pool: nothing is written
   const int items = kVBlock * NG;                    // 64 .. 128
   const int tpi = kThreads / items;                  // threads per item (2 .. 8)
   const int it = threadIdx.x / tpi, part = threadIdx.x % tpi;
@@ -182,7 +188,7 @@ __device__ void value_block(const Geom& g, int64_t unit, int32_t pos, uint32_t* 
   if (part == 0) {
     // entry [block][t / 8][gm][t % 8]
     uint32_t* meta32 = reinterpret_cast<uint32_t*>(v_meta);
-    meta32[(((unit * (g.C / kVBlock) + pos / kVBlock) * 4 + t / 8) * NG + gm) * 8 + t % 8] =
+    meta32[((cs * 4 + t / 8) * NG + gm) * 8 + t % 8] =
         (uint32_t)p.d16 | ((uint32_t)p.m16 << 16);
   }
   for (int c = 0; c < cn; ++c)
@@ -192,7 +198,7 @@ __device__ void value_block(const Geom& g, int64_t unit, int32_t pos, uint32_t* 
   // channel 16n + i, token j at bit 4 (j/2) + 16 (j%2); 2 bits: word m holds
   // channels 16 (2m + h) + i, token j at bit 8h + 2 (j/2) + 16 (j%2)
   const int NW = D * BITS / 64;  // words per lane
-  uint32_t* blk = v_codes + (unit * (g.C / kVBlock) + pos / kVBlock) * (int64_t)(D * BITS);
+  uint32_t* blk = v_codes + cs * (D * BITS);
   for (int x = threadIdx.x; x < 64 * NW; x += blockDim.x) {
     const int lane = x / NW, w = x % NW;
     const int gg = lane / 16, i = lane % 16;

@@ -18,6 +18,9 @@ from quantized_decode_attention_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
 HEADER_BQ2 = os.path.join(ROOT, "include", "kvq_bq2.h")
+HEADER_PAGED = os.path.join(ROOT, "include", "kvq_paged.h")
+GOOD = dict(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128, k_bits=2, v_bits=4,
+            group=32, residual=128, capacity=1024)
 
 
 def _declared(path=HEADER):
@@ -42,6 +45,73 @@ def test_exports_every_declared_bq2_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTS_BQ2) == names
+
+
+def test_exports_every_declared_paged_symbol():
+    L = kvq.lib()
+    names = _declared(HEADER_PAGED)
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTS_PAGED) == names
+
+
+@pytest.mark.parametrize("page_size,max_pages,num_pages,ok", [
+    (128, 8, 100, True), (32, 32, 1, True), (1024, 1, 4, True), (64, 16, 10, True),
+    (16, 64, 10, False),   # below one 32-position chunk
+    (96, 11, 10, False),   # not a power of two
+    (128, 7, 10, False),   # 7 pages of 128 do not cover capacity 1024
+    (128, 8, 0, False),    # empty pool
+    (0, 8, 10, False),
+])
+def test_paged_validation(page_size, max_pages, num_pages, ok):
+    g = kvq.Geom(**GOOD)
+    if ok:
+        kvq.kvq_paged_validate(g, page_size, max_pages, num_pages)
+        return
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_paged_validate(g, page_size, max_pages, num_pages)
+    assert e.value.status == -2
+
+
+def test_paged_page_smaller_than_key_group():
+    g = kvq.Geom(**{**GOOD, "group": 64, "residual": 128})
+    kvq.kvq_paged_validate(g, 64, 16, 4)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_paged_validate(g, 32, 32, 4)
+    assert e.value.status == -2
+
+
+@pytest.mark.parametrize("geom", [GOOD, {**GOOD, "head_dim": 64, "k_bits": 4, "v_bits": 2,
+                                         "group": 64, "residual": 64}])
+def test_paged_cache_bytes_are_dense_bytes_per_page(geom):
+    """A pool of N pages of P positions takes the bytes of a dense cache of N
+    sequences of capacity P (each page is a dense unit per KV head); the
+    residual windows are per sequence, as in the dense cache."""
+    g = kvq.Geom(**geom)
+    for P, N in [(128, 3), (256, 10), (1024, 2)]:
+        pools = kvq.kvq_paged_cache_bytes(g, P, N)
+        dense_pages = kvq.kvq_cache_bytes(kvq.Geom(**{**geom, "batch": N, "capacity": P}))
+        dense = kvq.kvq_cache_bytes(g)
+        assert pools[:4] == dense_pages[:4]
+        assert pools[4:] == dense[4:]
+
+
+def test_paged_calls_reject_before_launch():
+    """Invalid page parameters or null buffers fail on the host."""
+    g = kvq.Geom(**GOOD)
+    gc = g.c()
+    L = kvq.lib()
+    cc = _lib.kvq_paged_cache(16, 16, 16, 16, 16, 16, None, 128, 8, 4)
+    st = L.kvq_paged_append(ctypes.byref(gc), 16, 16, 16, ctypes.byref(cc), None)
+    assert st == -1 and "block_table" in kvq.last_error()
+    cc = _lib.kvq_paged_cache(16, 16, 16, 16, 16, 16, 16, 100, 8, 4)
+    st = L.kvq_paged_decode_attn(ctypes.byref(gc), 16, ctypes.byref(cc), 16, 1, 1.0, 16, 1 << 30,
+                                 16, None)
+    assert st == -2
+    cc = _lib.kvq_paged_cache(16, 16, 16, 16, 16, 16, 16, 128, 8, 4)
+    st = L.kvq_paged_prefill(ctypes.byref(gc), 16, 16, 2000, ctypes.byref(cc), None)
+    assert st == -6
 
 
 @pytest.mark.parametrize("field,value", [
@@ -75,9 +145,6 @@ def test_versions_and_status_strings():
         assert kvq.status_str(s) and kvq.status_str(s) != "unknown status"
     assert kvq.status_str(5) == "unknown status"
 
-
-GOOD = dict(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128, k_bits=2, v_bits=4,
-            group=32, residual=128, capacity=1024)
 
 
 @pytest.mark.parametrize("field,value,status", [
