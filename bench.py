@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--tokens", type=int, default=1,
                    help="query tokens per sequence per step (T > 1: T appends, then "
                         "kvq_decode_attn_multi; KIVI-format workloads)")
+    p.add_argument("--page-size", type=int, default=0,
+                   help="KIVI workloads: a paged cache with pages of this many positions, "
+                        "handed out in shuffled order (0: the dense cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -323,7 +326,25 @@ def main():
 
     print(f"[bench] workload {w.name}: {L} layer caches, capacity {cap}, "
           f"start len {int(start.min())}..{nmax0}", file=sys.stderr, flush=True)
-    caches = [kvq.Cache(g, dev) for _ in range(L)]
+    P = a.page_size
+    if P:
+        # every layer's pool: B * ceil(cap / P) pages, each sequence's pages
+        # drawn in shuffled order
+        maxp = -(-cap // P)
+        prng = np.random.default_rng(7)
+        caches = []
+        for _ in range(L):
+            table = prng.permutation(w.batch * maxp).astype(np.int32).reshape(w.batch, maxp)
+            caches.append(kvq.PagedCache(g, P, w.batch * maxp, torch.from_numpy(table).to(dev),
+                                         dev))
+        prefill, append = kvq.kvq_paged_prefill, kvq.kvq_paged_append
+        partial, combine = kvq.kvq_paged_decode_partial, kvq.kvq_paged_decode_combine
+        multi = kvq.kvq_paged_decode_attn_multi
+    else:
+        caches = [kvq.Cache(g, dev) for _ in range(L)]
+        prefill, append = kvq.kvq_prefill, kvq.kvq_append
+        partial, combine = kvq.kvq_decode_partial, kvq.kvq_decode_combine
+        multi = kvq.kvq_decode_attn_multi
     # prefill every layer from the same seeded tensors (layer 0's draw)
     k = synth.keys(w, nmax0)
     v = synth.values(w, nmax0)
@@ -332,13 +353,13 @@ def main():
     for c in caches:
         if np.all(start == start[0]):
             n = int(start[0])
-            kvq.kvq_prefill(g, kd[:, :, :n].contiguous(), vd[:, :, :n].contiguous(), n, c)
+            prefill(g, kd[:, :, :n].contiguous(), vd[:, :, :n].contiguous(), n, c)
         else:
             for b in range(w.batch):
                 n = int(start[b])
                 sub = c.view(b, b + 1)
-                kvq.kvq_prefill(sub.g, kd[b:b + 1, :, :n].contiguous(),
-                                vd[b:b + 1, :, :n].contiguous(), n, sub)
+                prefill(sub.g, kd[b:b + 1, :, :n].contiguous(),
+                        vd[b:b + 1, :, :n].contiguous(), n, sub)
     del kd, vd
     torch.cuda.synchronize()
 
@@ -354,17 +375,22 @@ def main():
         cur[l] = cur[l] + T
     lens_dev = torch.from_numpy(lens_host).to(dev)
     max_len = int(lens_host[:, T].max())
-    if T == 1:
+    if P:
+        ws = kvq.alloc_paged_workspace(g, T, max_len, dev)
+    elif T == 1:
         ws = kvq.alloc_workspace(g, max_len, dev)
-        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
     else:
         ws = kvq.alloc_multi_workspace(g, T, max_len, dev)
+    if T == 1:
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    else:
         out = torch.empty((w.batch, T, w.n_q_heads, w.head_dim), dtype=torch.float16,
                           device=dev)
         qpool = [torch.stack([pool[(s + j) % len(pool)][2] for j in range(T)], 1).contiguous()
                  for s in range(len(pool))]
     scale = 1.0 / math.sqrt(w.head_dim)
-    n_workers = kvq.kvq_decode_workers(g)
+    n_workers = (ws.numel() * 4 // (T * (w.n_q_heads // w.n_kv_heads) * (w.head_dim + 4) * 4)
+                 - w.batch * w.n_kv_heads)
 
     # algorithmic bytes of every step
     step_bytes, dec_bytes = [], []
@@ -392,18 +418,18 @@ def main():
         c = caches[l]
         for j in range(T):
             kn, vn, _ = pool[(s + j) % len(pool)]
-            kvq.kvq_append(g, kn, vn, lens_dev[s, j], c, stream)
+            append(g, kn, vn, lens_dev[s, j], c, stream)
         if timed_idx is not None:
             ev_a[timed_idx].record(stream)
         if T == 1:
             q = pool[s % len(pool)][2]
-            kvq.kvq_decode_partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+            partial(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
             if timed_idx is not None:
                 ev_b[timed_idx].record(stream)
-            kvq.kvq_decode_combine(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
+            combine(g, q, c, lens_dev[s, 1], max_len, scale, ws, out, stream)
         else:  # partial + combine in one call: the events bracket both
-            kvq.kvq_decode_attn_multi(g, qpool[s % len(qpool)], c, lens_dev[s, T], T, max_len,
-                                      scale, ws, out, stream)
+            multi(g, qpool[s % len(qpool)], c, lens_dev[s, T], T, max_len, scale, ws, out,
+                  stream)
             if timed_idx is not None:
                 ev_b[timed_idx].record(stream)
 
@@ -423,7 +449,7 @@ def main():
     dec_avg_bytes = float(np.mean(dec_bytes[timed]))
     achieved = dec_avg_bytes / part_avg_s / 1e9
     gbs = total_bytes / elapsed / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name) if T == 1 and not P else None
 
     rec = {
         "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak) + tokens/s",
@@ -451,18 +477,20 @@ def main():
                      if T == 1 else
                      f"{T} x kvq_append + kvq_decode_attn_multi (T={T}), one layer"),
             "query_tokens": T,
+            "cache": f"paged, {P}-position pages in shuffled order" if P else "dense",
         },
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch * T * a.steps / elapsed, 1),
         "tokens_per_s_unit": "decoded tokens per second through one layer",
         "roofline": {
-            "kernel": "decode_partial" if T == 1 else "decode_partial+decode_combine (multi)",
+            "kernel": ("decode_partial" if T == 1 else
+                       "decode_partial+decode_combine (multi)") + (" (paged)" if P else ""),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic if T == 1 else None,
+            "traffic": traffic,
             "avg_launch_us": round(part_avg_s * 1e6, 3),
             "algorithmic_bytes_per_launch": round(dec_avg_bytes),
         },

@@ -101,6 +101,17 @@ int kvq_paged_decode_attn(const kvq_geom *geom, const uint16_t *q,
                           int32_t max_seq_len, float sm_scale, void *workspace,
                           size_t workspace_bytes, uint16_t *out, void *stream);
 
+/* The two phases of kvq_paged_decode_attn (as kvq_decode_partial and
+ * kvq_decode_combine are those of kvq_decode_attn). */
+int kvq_paged_decode_partial(const kvq_geom *geom, const uint16_t *q,
+                             const kvq_paged_cache *cache, const int32_t *seq_lens,
+                             int32_t max_seq_len, float sm_scale, void *workspace,
+                             size_t workspace_bytes, uint16_t *out, void *stream);
+int kvq_paged_decode_combine(const kvq_geom *geom, const uint16_t *q,
+                             const kvq_paged_cache *cache, const int32_t *seq_lens,
+                             int32_t max_seq_len, float sm_scale, const void *workspace,
+                             size_t workspace_bytes, uint16_t *out, void *stream);
+
 /* kvq_decode_attn_multi over the paged cache (T query tokens per sequence,
  * causal over the last T positions; same arguments and rules). */
 int kvq_paged_decode_attn_multi(const kvq_geom *geom, const uint16_t *q,

@@ -23,5 +23,6 @@ from ._lib import (  # noqa: F401
     kvq_bq2_validate_geom)
 from ._lib import (  # noqa: F401
     PagedCache, alloc_paged_workspace, kvq_paged_append, kvq_paged_cache_bytes,
-    kvq_paged_decode_attn, kvq_paged_decode_attn_multi, kvq_paged_decode_workspace_bytes,
-    kvq_paged_prefill, kvq_paged_validate)
+    kvq_paged_decode_attn, kvq_paged_decode_attn_multi, kvq_paged_decode_combine,
+    kvq_paged_decode_partial, kvq_paged_decode_workspace_bytes, kvq_paged_prefill,
+    kvq_paged_validate)

@@ -50,7 +50,7 @@ EXPORTS_BQ2 = [
 EXPORTS_PAGED = [
     "kvq_paged_validate", "kvq_paged_cache_bytes", "kvq_paged_decode_workspace_bytes",
     "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_decode_attn",
-    "kvq_paged_decode_attn_multi",
+    "kvq_paged_decode_partial", "kvq_paged_decode_combine", "kvq_paged_decode_attn_multi",
 ]
 BQ2_HEAD_DIM = 64
 BQ2_SINKS = 4
@@ -114,6 +114,8 @@ def lib() -> ctypes.CDLL:
             "kvq_paged_prefill": (ctypes.c_int, [G, P, P, i32, CP, P]),
             "kvq_paged_append": (ctypes.c_int, [G, P, P, P, CP, P]),
             "kvq_paged_decode_attn": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
+            "kvq_paged_decode_partial": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
+            "kvq_paged_decode_combine": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
             "kvq_paged_decode_attn_multi": (ctypes.c_int, [G, P, CP, P, i32, i32, f32, P, sz, P,
                                                            P]),
             "kvq_abi_version": (ctypes.c_int, []),
@@ -524,18 +526,39 @@ def kvq_paged_decode_attn_multi(g: Geom, q: torch.Tensor, cache: PagedCache,
         _stream(stream)), "kvq_paged_decode_attn_multi")
 
 
-def kvq_paged_decode_attn(g: Geom, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
-                          max_seq_len: int, sm_scale: float, workspace: torch.Tensor | None,
-                          out: torch.Tensor, stream=None) -> None:
+def _paged_call(name, g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out, stream):
     gc = g.c()
     cc = cache.c()
     shape = (g.batch, g.n_q_heads, g.head_dim)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().kvq_paged_decode_attn(
+    _check(getattr(lib(), name)(
         ctypes.byref(gc), _ptr(q, "q", _F16, shape), ctypes.byref(cc),
         _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(max_seq_len), float(sm_scale),
         _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out", _F16, shape),
-        _stream(stream)), "kvq_paged_decode_attn")
+        _stream(stream)), name)
+
+
+def kvq_paged_decode_attn(g: Geom, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
+                          max_seq_len: int, sm_scale: float, workspace: torch.Tensor | None,
+                          out: torch.Tensor, stream=None) -> None:
+    _paged_call("kvq_paged_decode_attn", g, q, cache, seq_lens, max_seq_len, sm_scale,
+                workspace, out, stream)
+
+
+def kvq_paged_decode_partial(g: Geom, q: torch.Tensor, cache: PagedCache,
+                             seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                             workspace: torch.Tensor | None, out: torch.Tensor,
+                             stream=None) -> None:
+    _paged_call("kvq_paged_decode_partial", g, q, cache, seq_lens, max_seq_len, sm_scale,
+                workspace, out, stream)
+
+
+def kvq_paged_decode_combine(g: Geom, q: torch.Tensor, cache: PagedCache,
+                             seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                             workspace: torch.Tensor | None, out: torch.Tensor,
+                             stream=None) -> None:
+    _paged_call("kvq_paged_decode_combine", g, q, cache, seq_lens, max_seq_len, sm_scale,
+                workspace, out, stream)
 
 
 def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:

@@ -803,6 +803,42 @@ int kvq_paged_decode_attn_multi(const kvq_geom* geom, const uint16_t* q,
   }
 }
 
+int kvq_paged_decode_partial(const kvq_geom* geom, const uint16_t* q,
+                             const kvq_paged_cache* cache, const int32_t* seq_lens,
+                             int32_t max_seq_len, float sm_scale, void* workspace,
+                             size_t workspace_bytes, uint16_t* out, void* stream) {
+  try {
+    if (!cache) return fail(KVQ_ERR_NULL, "cache is NULL");
+    const kvq_cache view = kvq::pool_view(*cache);
+    kvq::DecodeLaunch L;
+    int st = decode_setup(geom, q, &view, seq_lens, max_seq_len, sm_scale, workspace,
+                          workspace_bytes, out, &L, 1, cache);
+    if (st != KVQ_OK) return st;
+    hipError_t e = kvq::launch_decode_partial(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_partial launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_decode_combine(const kvq_geom* geom, const uint16_t* q,
+                             const kvq_paged_cache* cache, const int32_t* seq_lens,
+                             int32_t max_seq_len, float sm_scale, const void* workspace,
+                             size_t workspace_bytes, uint16_t* out, void* stream) {
+  try {
+    if (!cache) return fail(KVQ_ERR_NULL, "cache is NULL");
+    const kvq_cache view = kvq::pool_view(*cache);
+    kvq::DecodeLaunch L;
+    int st = decode_setup(geom, q, &view, seq_lens, max_seq_len, sm_scale,
+                          const_cast<void*>(workspace), workspace_bytes, out, &L, 1, cache);
+    if (st != KVQ_OK) return st;
+    hipError_t e = kvq::launch_decode_combine(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 int kvq_paged_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_paged_cache* cache,
                           const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                           void* workspace, size_t workspace_bytes, uint16_t* out,

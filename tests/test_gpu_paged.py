@@ -148,6 +148,14 @@ def test_paged_prefill_and_decode(case):
     out = _decode_paged(g, pc, q, lens, scale)
     ref = oracle.decode_attn(og, oc, q, np.asarray(lens, np.int32), float(np.float32(scale)))
     assert_close(out, ref, what="paged decode")
+    # the two phases called apart give the same bits
+    out2 = torch.empty_like(out)
+    ws = kvq.alloc_paged_workspace(g, 1, max(lens))
+    ld = dev(np.asarray(lens, np.int32))
+    kvq.kvq_paged_decode_partial(g, dev(q), pc, ld, max(lens), scale, ws, out2)
+    kvq.kvq_paged_decode_combine(g, dev(q), pc, ld, max(lens), scale, ws, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     if _same_workers(g, max(lens)):
         dense = _decode_dense(g, cache, q, lens, scale)
         assert torch.equal(out.view(torch.int16), dense.view(torch.int16))
