@@ -54,8 +54,8 @@
  *                                t < Lq, fp16 residual keys for t >= Lq)
  *   out_h = sum_t softmax(s)_t * v_t     (fp32 accumulation, fp16 result)
  * The result equals softmax attention over the dequantized cache ([KV1]
- * Quickstart: quantizing each token once as it enters the cache and attending
- * over the dequantized values gives the exact low-bit outputs).
+ * Quickstart: attention over the cache's dequantized values, each token
+ * quantized a single time on its way in, is the low-bit result).
  *
  * ---------------------------------------------------------------------------
  * PACKED LAYOUT  (KVQ_LAYOUT_VERSION 3)

@@ -16,8 +16,8 @@
  * rotated back by H per head ([KV1] Quantization Format, Hadamard rotation).
  * The rotated vector x is formed exactly and rounded once to fp32.
  * Positions 0..3 of a sequence (attention sinks) keep x rounded to fp16.
- * Every other position is quantized once, when it enters the cache, as one
- * block of 64 values (in fp32, [KV1] Quantization Format):
+ * Every other position becomes one block of 64 values, a single time, at its
+ * append (in fp32, [KV1] Quantization Format):
  *   mn = min x_c (a zero min taken as +0), mx = max x_c
  *   d = fp16(max((mx - mn) / 3, 1e-6))     (IEEE fp32 ops, round to nearest even)
  *   m = fp16(mn)

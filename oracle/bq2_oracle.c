@@ -7,14 +7,14 @@
  * restated below from its written specification.
  *
  * Source: [KV1] "KV1-1.2B-Instruct" model card, sections "Quantization Format:
- * KV1.cpp BQ2_0" (one block per token and KV head over the 64 values of a head:
+ * KV1.cpp BQ2_0" (one block for each position and KV head, covering its 64 channels:
  * fp16 scale d, fp16 min m, sixteen bytes of 2-bit codes with code i of a byte
  * at bit 2i; quantize in fp32 with d = fp16(max((max - min)/3, 1e-6)),
  * m = fp16(min), code = clamp(round half to even((x - m)/d), 0, 3) using the
  * fp16-rounded d and m; dequantize as code * d + m; Q, K and V multiplied by
- * the normalized 64x64 Sylvester Hadamard matrix H (H H = I) after RoPE and
- * before K and V are stored, scores unchanged, the attention output multiplied
- * by H again per head; positions 0-3 keep full-precision K/V), and "Model
+ * the normalized 64x64 Sylvester Hadamard matrix H (H H = I) after RoPE, so
+ * the stored K and V are rotated while q.k is not changed, and each head's
+ * attention output rotated back by H; positions 0-3 keep full-precision K/V), and "Model
  * Overview" (32 query heads, 8 KV heads, head dim 64, 4 fp16 sink tokens).
  *
  * Readings where the page is silent (each listed in the design notes):
@@ -22,7 +22,7 @@
  *     need at most 47 significant bits) and rounded once to fp32, the
  *     precision the format quantizes in;
  *   - sink positions 0-3 store the fp16 rounding of that fp32 rotated vector;
- *   - every other position is quantized once, when it enters the cache (no
+ *   - every other position is quantized a single time, at its append (no
  *     fp16 window);
  *   - a zero min is stored as +0 (as in the group quantizer of kvq_oracle.c);
  *   - the query is rotated exactly in fp64 here, and attention runs in fp64
