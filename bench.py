@@ -61,7 +61,7 @@ def parse():
 
 # kernel sources whose change invalidates a committed traffic reading
 KERNEL_SOURCES = {
-    "decode_partial": ("kvq_decode_impl.h", "kvq_decode_d128.hip", "kvq_device.h",
+    "decode_partial": ("kvq_decode_impl.h", "kvq_decode_inst.hip", "kvq_device.h",
                        "kvq_quant.hip", "kvq_internal.h"),
     "bq2_partial": ("kvq_bq2_decode.hip", "kvq_device.h", "kvq_bq2_quant.hip", "kvq_internal.h"),
 }

@@ -20,8 +20,8 @@
  * Keys are quantized per channel: for every channel, a group of G consecutive
  * tokens shares one (scale, min) pair.  Values are quantized per token: every
  * token's head vector is cut into D/G groups of G consecutive channels, each
- * with its own (scale, min).  Codes have b = 2 or 4 bits, chosen separately for
- * keys and values.  The most recent tokens stay in an fp16 residual window of R
+ * with its own (scale, min).  Codes have b = 2, 4 or 8 bits, chosen separately
+ * for keys and values ([KVQ] Usage: the bit range of a budget goes up to 8).  The most recent tokens stay in an fp16 residual window of R
  * tokens until the window is full; then it is quantized into packed groups.
  * ([KIVI] core capabilities, Overview, Example: k_bits, v_bits, group_size,
  * residual_length; [REC] notes: per-channel keys group outlier channels.)
@@ -80,7 +80,9 @@
  *            Entry [k][l][u][w] holds key row i of half u (token tau above) of
  *            block k, restricted to channel slice g = channels
  *            [g*D/4, (g+1)*D/4): its word w holds the 32/bK channels
- *            g*D/4 + w*32/bK + f, channel f of the word in bits f*bK .. +bK-1.
+ *            g*D/4 + w*32/bK + f, channel f of the word in bits f*bK .. +bK-1
+ *            (bK = 2, 4).  bK = 8: word w = 2 kc + s holds channels
+ *            g*D/4 + 8 kc + 2 s + (0, 1, 4, 5)[f] in byte f.
  *            (A token's natural row of D*bK/32 words is the concatenation of
  *            its 4 slices, word w of slice g being row word g*KW + w.)
  *   k_meta   uint16 [B][Hkv][C/G][D/8][8][2]  fp16 (scale, min) of key group
@@ -90,7 +92,7 @@
  *              r = g*(D/32) + kc (g in [0,4), kc in [0, D/32)),
  *              channel = g*D/4 + base + (e / 2) + off * (e % 2)
  *            with base = 16*(kc/2) + 4*(kc%2), off = 8 for bK = 2 and
- *                 base = 8*kc,                  off = 4 for bK = 4
+ *                 base = 8*kc,                  off = 4 for bK = 4, 8
  *            (the channels of key word fields: bits 0..15 of a word hold the
  *            even elements, bits 16..31 the odd ones).
  *   v_codes  uint32 [B][Hkv][C/32][64][NW],  NW = D*bV/64.
@@ -99,6 +101,9 @@
  *            bV = 2: entry [k][l][m] (m in [0, D/32)) holds channels
  *              16(2m + h) + i for h in {0, 1}; token tau = 8g + j of channel
  *              16(2m + h) + i sits in bits 8h + 2*(j/2) + 16*(j%2) .. +1.
+ *            bV = 8: entries [k][l][2n], [k][l][2n + 1] (n in [0, D/16)) hold
+ *              channel 16n + i; token tau = 8g + j sits in entry 2n + j/4,
+ *              bits 8*((j%4)/2) + 16*(j%2) .. +7.
  *   v_meta   uint16 [B][Hkv][C/32][4][D/G][8][2]  fp16 (scale, min) of token
  *            32k + 8g + j and channel group gamma = channels
  *            [gamma*G, gamma*G + G) at entry [k][g][gamma][j].
@@ -116,7 +121,7 @@
  * Constraints (checked, KVQ_ERR_GEOM / KVQ_ERR_BITS otherwise):
  *   batch >= 1; n_kv_heads >= 1; n_q_heads % n_kv_heads == 0 and
  *   n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; head_dim in {64, 128};
- *   k_bits, v_bits in {2, 4}; group in {32, 64, 128}, group <= head_dim,
+ *   k_bits, v_bits in {2, 4, 8}; group in {32, 64, 128}, group <= head_dim,
  *   head_dim % group == 0; residual % group == 0; capacity % residual == 0;
  *   capacity <= 2^24.
  *
@@ -159,7 +164,7 @@ enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = -1,      /* a required pointer is NULL */
   KVQ_ERR_GEOM = -2,      /* geometry violates the constraints above */
-  KVQ_ERR_BITS = -3,      /* k_bits / v_bits not in {2, 4} */
+  KVQ_ERR_BITS = -3,      /* k_bits / v_bits not in {2, 4, 8} */
   KVQ_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned */
   KVQ_ERR_WORKSPACE = -5, /* workspace missing or too small */
   KVQ_ERR_RANGE = -6,     /* a token range / length argument is out of range */
@@ -173,8 +178,8 @@ typedef struct kvq_geom {
   int32_t n_q_heads;  /* Hq: query heads */
   int32_t n_kv_heads; /* Hkv: KV heads; Hq / Hkv query heads share one */
   int32_t head_dim;   /* D: 64 or 128 */
-  int32_t k_bits;     /* bK: 2 or 4 */
-  int32_t v_bits;     /* bV: 2 or 4 */
+  int32_t k_bits;     /* bK: 2, 4 or 8 */
+  int32_t v_bits;     /* bV: 2, 4 or 8 */
   int32_t group;      /* G: tokens per key group = channels per value group */
   int32_t residual;   /* R: fp16 residual window length, multiple of G */
   int32_t capacity;   /* C: max tokens per sequence, multiple of R */

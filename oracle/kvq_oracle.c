@@ -185,13 +185,17 @@ void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
 /*   value element j of group g:  tau = 8 g + j                              */
 /* k_codes  u32 [B][Hkv][C/32][64][2][KW], KW = D*bK/128: [k][l][u][w] is    */
 /*          slice g (channels g*D/4 ..) of key row i of half u; its word w   */
-/*          holds channels g*D/4 + w*32/bK + f in bits f*bK.                 */
+/*          holds channels g*D/4 + w*32/bK + f in bits f*bK (2, 4 bits);     */
+/*          8 bits: word 2kc + s holds g*D/4 + 8kc + 2s + (0,1,4,5)[f] in    */
+/*          byte f.                                                          */
 /* k_meta   u16 [B][Hkv][C/G][D/8][8][2]: entry [q][r][e] is the channel     */
 /*          key_meta_channel(r, e) of key group q.                           */
 /* v_codes  u32 [B][Hkv][C/32][64][NW], NW = D*bV/64: 4 bits: word n of lane */
 /*          l is channel 16n + i, token 8g + j at bit 4(j/2) + 16(j%2);      */
 /*          2 bits: word m of lane l holds channels 16(2m+h) + i, token      */
-/*          8g + j at bit 8h + 2(j/2) + 16(j%2).                             */
+/*          8g + j at bit 8h + 2(j/2) + 16(j%2).  8 bits: words 2n, 2n+1 of  */
+/*          lane l are channel 16n + i, token 8g + j in word 2n + j/4 at bit */
+/*          8((j%4)/2) + 16(j%2).                                            */
 /* v_meta   u16 [B][Hkv][C/32][4][D/G][8][2]: entry [k][g][gamma][j] is      */
 /*          token 32k + 8g + j, channel group gamma.                         */
 /* k_res    u16 [B][Hkv][R][D]: position p in slot p % R, one row per slot. */
@@ -217,8 +221,19 @@ static int64_t key_word(int64_t unit, int64_t C, int D, int bK, int64_t t,
   int slice = D / 4; /* channels of a lane group's slice */
   int g = c / slice, cs = c % slice;
   int kw = D * bK / 128; /* words per slice */
-  int w = cs * bK / 32;
-  *bit = cs * bK % 32;
+  int w, byte;
+  if (bK == 8) {
+    /* within the 8 channels 8kc .. 8kc+7: p = 2s + (0,1,4,5)[f] */
+    int kc = cs / 8, p = cs % 8;
+    int s = (p % 4) / 2;
+    int f = (p % 2) + 2 * (p / 4);
+    w = 2 * kc + s;
+    byte = f;
+    *bit = 8 * byte;
+  } else {
+    w = cs * bK / 32;
+    *bit = cs * bK % 32;
+  }
   /* the key row i of half u that holds tau = 8 (i/4) + 4 u + i % 4 */
   int u = (tau / 4) % 2;
   int i = 4 * (tau / 8) + tau % 4;
@@ -264,7 +279,10 @@ static int64_t value_word(int64_t unit, int64_t C, int D, int bV, int64_t t,
   int l = 16 * g + i;
   int nw = D * bV / 64; /* words per lane */
   int w;
-  if (bV == 4) {
+  if (bV == 8) {
+    w = 2 * n + j / 4;
+    *bit = 8 * ((j % 4) / 2) + 16 * (j % 2);
+  } else if (bV == 4) {
     w = n;
     *bit = 4 * (j / 2) + 16 * (j % 2);
   } else {

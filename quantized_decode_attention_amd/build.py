@@ -21,25 +21,32 @@ ARCH = ["--offload-arch=gfx950"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(HERE, "..", "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = {
-    "kvq_quant.hip": ["-ffp-contract=off"],
+MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+# (object name, source, extra flags)
+UNITS = [
+    ("kvq_quant", "kvq_quant.hip", ["-ffp-contract=off"]),
     # MFMA accumulators in VGPRs: keeps the O tiles out of AGPR<->VGPR copies
     # around the (rare) softmax rescale.
-    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-    "kvq_decode_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-    "kvq_decode_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-    "kvq_decode_paged_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-    "kvq_decode_paged_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-    "kvq_bq2_quant.hip": ["-ffp-contract=off"],
-    "kvq_bq2_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-    "kvq_api.cpp": [],
-}
+    ("kvq_decode", "kvq_decode.hip", MFMA_VGPR),
+    ("kvq_bq2_quant", "kvq_bq2_quant.hip", ["-ffp-contract=off"]),
+    ("kvq_bq2_decode", "kvq_bq2_decode.hip", MFMA_VGPR),
+    ("kvq_api", "kvq_api.cpp", []),
+]
+# the decode partial kernels: one instantiation set per head dim, key bits and
+# cache form, each its own object (they compile in parallel)
+for _paged in (0, 1):
+    for _d in (64, 128):
+        for _bk in (2, 4, 8):
+            _name = f"decode_partial_{'paged_' if _paged else ''}d{_d}_k{_bk}"
+            UNITS.append((_name, "kvq_decode_inst.hip",
+                          MFMA_VGPR + [f"-DKVQ_D={_d}", f"-DKVQ_BK={_bk}",
+                                       f"-DKVQ_PAGED={_paged}", f"-DKVQ_INST={_name}"]))
 
 
-def _compile(name: str, extra: list[str]) -> str:
-    src = os.path.join(CSRC, name)
+def _compile(name: str, source: str, extra: list[str]) -> str:
+    src = os.path.join(CSRC, source)
     obj = os.path.join(BUILD, name + ".o")
-    lang = ["-x", "hip"] if name.endswith(".hip") else []
+    lang = ["-x", "hip"] if source.endswith(".hip") else []
     cmd = [HIPCC, *ARCH, *COMMON, *extra, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -50,8 +57,8 @@ def _compile(name: str, extra: list[str]) -> str:
 
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
+    with ThreadPoolExecutor(max_workers=min(len(UNITS), os.cpu_count() or 8, 16)) as ex:
+        objs = list(ex.map(lambda u: _compile(*u), UNITS))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)

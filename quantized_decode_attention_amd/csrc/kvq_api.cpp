@@ -34,10 +34,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_geom(const kvq_geom* g) {
   if (!g) return fail(KVQ_ERR_NULL, "geometry is NULL");
-  if (g->k_bits != 2 && g->k_bits != 4)
-    return fail(KVQ_ERR_BITS, "k_bits must be 2 or 4 (got %d)", g->k_bits);
-  if (g->v_bits != 2 && g->v_bits != 4)
-    return fail(KVQ_ERR_BITS, "v_bits must be 2 or 4 (got %d)", g->v_bits);
+  if (g->k_bits != 2 && g->k_bits != 4 && g->k_bits != 8)
+    return fail(KVQ_ERR_BITS, "k_bits must be 2, 4 or 8 (got %d)", g->k_bits);
+  if (g->v_bits != 2 && g->v_bits != 4 && g->v_bits != 8)
+    return fail(KVQ_ERR_BITS, "v_bits must be 2, 4 or 8 (got %d)", g->v_bits);
   if (g->batch < 1 || g->n_kv_heads < 1 || g->n_q_heads < 1)
     return fail(KVQ_ERR_GEOM, "batch and head counts must be >= 1");
   if (g->n_q_heads % g->n_kv_heads != 0)

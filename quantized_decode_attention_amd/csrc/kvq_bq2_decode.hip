@@ -188,7 +188,7 @@ struct Bq2Wave {
       const float a = exp2_hw(m_run - m_new);
       m_run = m_new;
       m_even = kPacked ? m_new - kValEvenLog2<2> : m_new;
-      m_odd = kPacked ? m_new - kValOddLog2 : m_new;
+      m_odd = kPacked ? m_new - kValOddLog2<2> : m_new;
       l_run *= a;
       l_odd *= a;
       bias *= a;

@@ -1,17 +1,23 @@
 // kvq_decode.hip — the decode combine kernel and the routing of partial-kernel
-// launches to their translation unit (head dim, dense or paged cache).
+// launches to their instantiation set (head dim, key bits, dense or paged).
 #include "kvq_decode_impl.h"
 
 namespace kvq {
 namespace {
 
+using SetFn = hipError_t (*)(const DecodeLaunch&, int, int, int*, hipStream_t);
+
 hipError_t partial_entry(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  const bool paged = L.g.table != nullptr;
-  if (L.g.D == 64)
-    return paged ? decode_partial_paged_d64(L, op, cus, workers, st)
-                 : decode_partial_d64(L, op, cus, workers, st);
-  return paged ? decode_partial_paged_d128(L, op, cus, workers, st)
-               : decode_partial_d128(L, op, cus, workers, st);
+  // [paged][head dim 64 / 128][key bits 2 / 4 / 8]
+  static const SetFn sets[2][2][3] = {
+      {{decode_partial_d64_k2, decode_partial_d64_k4, decode_partial_d64_k8},
+       {decode_partial_d128_k2, decode_partial_d128_k4, decode_partial_d128_k8}},
+      {{decode_partial_paged_d64_k2, decode_partial_paged_d64_k4, decode_partial_paged_d64_k8},
+       {decode_partial_paged_d128_k2, decode_partial_paged_d128_k4,
+        decode_partial_paged_d128_k8}}};
+  const int bk = L.g.bK == 2 ? 0 : L.g.bK == 4 ? 1 : L.g.bK == 8 ? 2 : -1;
+  if (bk < 0 || (L.g.D != 64 && L.g.D != 128)) return hipErrorInvalidValue;
+  return sets[L.g.table != nullptr][L.g.D == 128][bk](L, op, cus, workers, st);
 }
 
 template <int D>

@@ -304,7 +304,7 @@ struct PackedWave {
       const float a = exp2_hw(m_run - m_new);
       m_run = m_new;
       m_even = m_new - kValEvenLog2<BV>;
-      m_odd = m_new - kValOddLog2;
+      m_odd = m_new - kValOddLog2<BV>;
       l_run *= a;
       l_odd *= a;
 #pragma unroll
@@ -510,7 +510,12 @@ struct PackedWave {
       for (int n = 0; n < NT; ++n) {
         if (C::gam(n) / SL != f) continue;  // compile-time
         uint32_t a[4];
-        if constexpr (BV == 4) {
+        if constexpr (BV == 8) {
+          // pair e: word 2n + e/2 shifted down by 8 (e%2), bytes 0 and 2
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            a[e] = (r.vw[2 * n + (e >> 1)] >> (8 * (e & 1))) & 0x00FF00FFu;
+        } else if constexpr (BV == 4) {
           // pair e: (w >> 8 (e/2)) masked at bits 4 (e%2)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -848,15 +853,16 @@ hipError_t dispatch_gq(const DecodeLaunch& L, int op, int cus, int* workers, hip
   }
 }
 
-// The partial kernels of one head dim, dense or paged (each translation unit
-// that includes this file instantiates one such set).
-template <int D, bool PG>
-hipError_t dispatch_bits(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
-  const int bk = L.g.bK, bv = L.g.bV;
-  if (bk == 2 && bv == 2) return dispatch_gq<D, 2, 2, PG>(L, op, cus, workers, st);
-  if (bk == 2 && bv == 4) return dispatch_gq<D, 2, 4, PG>(L, op, cus, workers, st);
-  if (bk == 4 && bv == 2) return dispatch_gq<D, 4, 2, PG>(L, op, cus, workers, st);
-  return dispatch_gq<D, 4, 4, PG>(L, op, cus, workers, st);
+// The partial kernels of one head dim, key width and cache form (each
+// translation unit that includes this file instantiates one such set).
+template <int D, int BK, bool PG>
+hipError_t dispatch_bv(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st) {
+  switch (L.g.bV) {
+    case 2: return dispatch_gq<D, BK, 2, PG>(L, op, cus, workers, st);
+    case 4: return dispatch_gq<D, BK, 4, PG>(L, op, cus, workers, st);
+    case 8: return dispatch_gq<D, BK, 8, PG>(L, op, cus, workers, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace

@@ -137,21 +137,24 @@ constexpr int kKW = (D / 4) * BK / 32;
 // kKeyEvenQ and of an odd channel by kKeyOddQ (channel parity = pair parity,
 // the runs start at multiples of 4), and every pair then contributes
 // kKeyAcc * code * q'.  The factors keep q' inside fp16 for any fp16 keys
-// (a 4-bit scale is at most 8734, a 2-bit one is not scaled up).
-template <int BK> constexpr float kKeyEvenQ = BK == 2 ? 1.0f : 4.0f;
-template <int BK> constexpr float kKeyOddQ = 0.25f;
-template <int BK> constexpr int kKeyAccLog2 = BK == 2 ? 0 : 2;
+// (a 4-bit scale is at most 8734, a 2-bit one is not scaled up).  8-bit
+// fields are shifted down to bit 0 of their half before the mask, so every
+// pair is code * 2^-24 and no factor is needed.
+template <int BK> constexpr float kKeyEvenQ = BK == 4 ? 4.0f : 1.0f;
+template <int BK> constexpr float kKeyOddQ = BK == 8 ? 1.0f : 0.25f;
+template <int BK> constexpr int kKeyAccLog2 = BK == 4 ? 2 : 0;
 
 // Value side, likewise: the odd pairs of a value word (VGPR e odd: tokens
 // 8g + 2e, 8g + 2e + 1 with e odd, i.e. score registers q = 2, 3) come out of
 // their mask as code * 16 (4-bit) or * 4 (2-bit) * 2^-24.  Their softmax
 // weights are taken 4x smaller (2^(s - m - 2)) and the even pairs' weights
 // kValEven times larger, so every pair contributes kValEven * p * code * dV.
-// (4 * 8734 and 43669 stay inside fp16.)
+// (4 * 8734 and 43669 stay inside fp16.)  8-bit pairs are all code * 2^-24:
+// both classes keep factor 1.
 template <int BV> constexpr float kValEven = BV == 4 ? 4.0f : 1.0f;
-template <int BV> constexpr float kValOdd = 0.25f;
+template <int BV> constexpr float kValOdd = BV == 8 ? 1.0f : 0.25f;
 template <int BV> constexpr float kValEvenLog2 = BV == 4 ? 2.0f : 0.0f;
-constexpr float kValOddLog2 = -2.0f;
+template <int BV> constexpr float kValOddLog2 = BV == 8 ? 0.0f : -2.0f;
 
 template <int D, int BK>
 __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
@@ -165,13 +168,20 @@ __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
         const int ri = 8 * wi + s;
         a[ri >> 2][ri & 3] = (w[wi] >> (4 * (s >> 1))) & ((s & 1) ? 0x000C000Cu : 0x00030003u);
       }
-  } else {
+  } else if constexpr (BK == 4) {
     // field s of a half: (w >> 8 (s/2)) masked at bits 4 (s%2)
 #pragma unroll
     for (int wi = 0; wi < kKW<D, BK>; ++wi)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         a[wi][s] = (w[wi] >> (8 * (s >> 1))) & ((s & 1) ? 0x00F000F0u : 0x000F000Fu);
+  } else {
+    // k-chunk kc from words 2kc + (s/2): pair s is that word >> 8 (s%2),
+    // bytes 0 and 2 of the result
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[kc][s] = (w[2 * kc + (s >> 1)] >> (8 * (s & 1))) & 0x00FF00FFu;
   }
 }
 

@@ -110,16 +110,18 @@ struct DecodeLaunch {
 // Worker waves of the partial kernel for gq rows per KV head on the current
 // device (dense or paged as g.table says).
 hipError_t decode_workers(const Geom& g, int gq, int cus, int* workers);
-// The partial kernels by head dim and cache form: op 0 launches, op 1 puts
-// the worker count in *workers.
-hipError_t decode_partial_d64(const DecodeLaunch& L, int op, int cus, int* workers,
-                              hipStream_t st);
-hipError_t decode_partial_d128(const DecodeLaunch& L, int op, int cus, int* workers,
-                               hipStream_t st);
-hipError_t decode_partial_paged_d64(const DecodeLaunch& L, int op, int cus, int* workers,
-                                    hipStream_t st);
-hipError_t decode_partial_paged_d128(const DecodeLaunch& L, int op, int cus, int* workers,
-                                     hipStream_t st);
+// The partial kernels by head dim, key bits and cache form (one instantiation
+// set each): op 0 launches, op 1 puts the worker count in *workers.
+#define KVQ_DECODE_SETS(X)                                                          \
+  X(decode_partial_d64_k2) X(decode_partial_d64_k4) X(decode_partial_d64_k8)         \
+  X(decode_partial_d128_k2) X(decode_partial_d128_k4) X(decode_partial_d128_k8)      \
+  X(decode_partial_paged_d64_k2) X(decode_partial_paged_d64_k4)                      \
+  X(decode_partial_paged_d64_k8) X(decode_partial_paged_d128_k2)                     \
+  X(decode_partial_paged_d128_k4) X(decode_partial_paged_d128_k8)
+#define KVQ_DECLARE_SET(name) \
+  hipError_t name(const DecodeLaunch& L, int op, int cus, int* workers, hipStream_t st);
+KVQ_DECODE_SETS(KVQ_DECLARE_SET)
+#undef KVQ_DECLARE_SET
 hipError_t launch_decode_partial(const DecodeLaunch& L, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeLaunch& L, hipStream_t st);
 

@@ -56,17 +56,32 @@ __device__ __forceinline__ uint32_t group_code(float x, const GroupParams& p,
 // kc = r % (D/32)) feeds: g D/4 + base(kc) + e/2 + off (e%2).  Inverse:
 // within its slice, channel cs sits in word cs / (32/BITS) at field s'; the
 // field's half (low / high 16 bits) gives e % 2, its place in the half gives
-// the chunk and e / 2.
+// the chunk and e / 2.  For 8 bits base = 8 kc and off = 4 (as for 4 bits):
+// cs = 8 kc + p gives e = 2 (p % 4) + p / 4.
 template <int BITS>
 __device__ __forceinline__ int key_meta_entry(int c, int D) {
-  constexpr int per = 32 / BITS;  // fields per word
-  constexpr int hp = per / 2;     // fields per half word
   const int g = c / (D / 4), cs = c % (D / 4);
-  const int wi = cs / per, sp = cs % per;
-  const int half = sp / hp, s = sp % hp;
-  const int kc = wi * (hp / 4) + s / 4;
-  const int r = g * (D / 32) + kc;
-  return 8 * r + 2 * (s % 4) + half;
+  if constexpr (BITS == 8) {
+    const int kc = cs / 8, p = cs % 8;
+    return 8 * (g * (D / 32) + kc) + 2 * (p % 4) + p / 4;
+  } else {
+    constexpr int per = 32 / BITS;  // fields per word
+    constexpr int hp = per / 2;     // fields per half word
+    const int wi = cs / per, sp = cs % per;
+    const int half = sp / hp, s = sp % hp;
+    const int kc = wi * (hp / 4) + s / 4;
+    const int r = g * (D / 32) + kc;
+    return 8 * r + 2 * (s % 4) + half;
+  }
+}
+
+// Channel (within its lane group's slice) of field f of slice word ws: 2 and
+// 4 bits in channel order; 8 bits: word 2 kc + s holds 8 kc + 2 s + (0, 1, 4,
+// 5)[f], the order in which the decode kernel's byte masks feed its pairs.
+template <int BITS>
+__device__ __forceinline__ int key_field_channel(int ws, int f) {
+  if constexpr (BITS == 8) return 8 * (ws >> 1) + 2 * (ws & 1) + (f & 1) + 4 * (f >> 1);
+  else return ws * (32 / BITS) + f;
 }
 
 // Place of (slot s, channel c) inside one unit's v_res window: entry
@@ -147,10 +162,11 @@ __device__ void key_group(const Geom& g, int64_t unit, int32_t pos, uint32_t* k_
   const int KW = W / 4;            // words per slice
   for (int x = threadIdx.x; x < G * W; x += blockDim.x) {
     const int t = x / W, wr = x % W;
-    const uint8_t* cc = codes + t * D + wr * kPer;
+    const uint8_t* cc = codes + t * D + (wr / KW) * (D / 4);  // the word's slice
     uint32_t word = 0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) word |= (uint32_t)cc[k] << (k * BITS);
+    for (int k = 0; k < kPer; ++k)
+      word |= (uint32_t)cc[key_field_channel<BITS>(wr % KW, k)] << (k * BITS);
     const int p_tok = pos + t, tau = p_tok % kVBlock;
     const int u = (tau >> 2) & 1, i = 4 * (tau >> 3) + (tau & 3);
     const int lane = 16 * (wr / KW) + i;
@@ -196,20 +212,31 @@ __device__ void value_block(const Geom& g, int64_t unit, int32_t pos, uint32_t* 
   __syncthreads();
   // consumer order: lane 16 g + i holds tokens 8g + j; 4 bits: word n is
   // channel 16n + i, token j at bit 4 (j/2) + 16 (j%2); 2 bits: word m holds
-  // channels 16 (2m + h) + i, token j at bit 8h + 2 (j/2) + 16 (j%2)
+  // channels 16 (2m + h) + i, token j at bit 8h + 2 (j/2) + 16 (j%2); 8 bits:
+  // words 2n, 2n + 1 are channel 16n + i, token j in word 2n + j/4 at bit
+  // 8 ((j%4)/2) + 16 (j%2)
   const int NW = D * BITS / 64;  // words per lane
   uint32_t* blk = v_codes + cs * (D * BITS);
   for (int x = threadIdx.x; x < 64 * NW; x += blockDim.x) {
     const int lane = x / NW, w = x % NW;
     const int gg = lane / 16, i = lane % 16;
     uint32_t word = 0;
+    if constexpr (BITS == 8) {
+      const int c = 16 * (w / 2) + i;
 #pragma unroll
-    for (int h = 0; h < 4 / BITS; ++h) {
-      const int c = 16 * (w * (4 / BITS) + h) + i;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * (w % 2) + jj;
+        word |= (uint32_t)codes[(8 * gg + j) * D + c] << (8 * (jj / 2) + 16 * (jj % 2));
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int bit = 8 * h + BITS * (j / 2) + 16 * (j % 2);
-        word |= (uint32_t)codes[(8 * gg + j) * D + c] << bit;
+      for (int h = 0; h < 4 / BITS; ++h) {
+        const int c = 16 * (w * (4 / BITS) + h) + i;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int bit = 8 * h + BITS * (j / 2) + 16 * (j % 2);
+          word |= (uint32_t)codes[(8 * gg + j) * D + c] << bit;
+        }
       }
     }
     blk[x] = word;
@@ -337,8 +364,11 @@ hipError_t launch_quantize_keys(const Geom& g, const uint16_t* src,
   if (g.bK == 2)
     quantize_keys_kernel<2><<<grid, kThreads, quant_lds_bytes(g), st>>>(
         g, src, src_unit_stride, pos0, k_codes, k_meta);
-  else
+  else if (g.bK == 4)
     quantize_keys_kernel<4><<<grid, kThreads, quant_lds_bytes(g), st>>>(
+        g, src, src_unit_stride, pos0, k_codes, k_meta);
+  else
+    quantize_keys_kernel<8><<<grid, kThreads, quant_lds_bytes(g), st>>>(
         g, src, src_unit_stride, pos0, k_codes, k_meta);
   return hipGetLastError();
 }
@@ -352,8 +382,11 @@ hipError_t launch_quantize_values(const Geom& g, const uint16_t* src,
   if (g.bV == 2)
     quantize_values_kernel<2><<<grid, kThreads, quant_lds_bytes(g), st>>>(
         g, src, src_unit_stride, pos0, v_codes, v_meta);
-  else
+  else if (g.bV == 4)
     quantize_values_kernel<4><<<grid, kThreads, quant_lds_bytes(g), st>>>(
+        g, src, src_unit_stride, pos0, v_codes, v_meta);
+  else
+    quantize_values_kernel<8><<<grid, kThreads, quant_lds_bytes(g), st>>>(
         g, src, src_unit_stride, pos0, v_codes, v_meta);
   return hipGetLastError();
 }
@@ -379,10 +412,19 @@ hipError_t launch_append(const Geom& g, const uint16_t* k_new,
   append_kernel<BK, BV><<<grid, kThreads, quant_lds_bytes(g), st>>>(          \
       g, k_new, v_new, seq_lens, c.k_codes, c.v_codes, c.k_meta, c.v_meta,    \
       c.k_res, c.v_res)
-  if (g.bK == 2 && g.bV == 2) KVQ_APPEND(2, 2);
-  else if (g.bK == 2 && g.bV == 4) KVQ_APPEND(2, 4);
-  else if (g.bK == 4 && g.bV == 2) KVQ_APPEND(4, 2);
-  else KVQ_APPEND(4, 4);
+  const int code = 10 * g.bK + g.bV;
+  switch (code) {
+    case 22: KVQ_APPEND(2, 2); break;
+    case 24: KVQ_APPEND(2, 4); break;
+    case 28: KVQ_APPEND(2, 8); break;
+    case 42: KVQ_APPEND(4, 2); break;
+    case 44: KVQ_APPEND(4, 4); break;
+    case 48: KVQ_APPEND(4, 8); break;
+    case 82: KVQ_APPEND(8, 2); break;
+    case 84: KVQ_APPEND(8, 4); break;
+    case 88: KVQ_APPEND(8, 8); break;
+    default: return hipErrorInvalidValue;
+  }
 #undef KVQ_APPEND
   return hipGetLastError();
 }

@@ -148,7 +148,8 @@ def test_versions_and_status_strings():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("k_bits", 3, -3), ("v_bits", 8, -3), ("batch", 0, -2), ("n_q_heads", 12, -2),
+    ("k_bits", 3, -3), ("v_bits", 16, -3), ("k_bits", 1, -3), ("batch", 0, -2),
+    ("n_q_heads", 12, -2),
     ("n_q_heads", 24, -2), ("head_dim", 96, -2), ("group", 16, -2), ("group", 48, -2),
     ("residual", 48, -2), ("residual", 0, -2), ("capacity", 1000, -2),
     ("capacity", 1 << 25, -2), ("n_kv_heads", 0, -2),

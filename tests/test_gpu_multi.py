@@ -47,6 +47,7 @@ CASES = [
     (64, 4, 2, 32, 32, 2, 2, 16, [16, 17, 33, 47, 48, 64, 100]),
     (128, 4, 4, 32, 64, 16, 2, 2, [2, 65, 66, 97, 160]),
     (64, 2, 2, 64, 64, 2, 1, 8, [8, 64, 65, 70, 71, 72, 129]),
+    (128, 8, 8, 32, 128, 8, 2, 4, [4, 131, 257, 300]),
 ]
 
 

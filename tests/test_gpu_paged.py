@@ -120,6 +120,8 @@ CASES = [
     (2, 16, 2, 128, 4, 4, 128, 128, 2048, 256, [2048, 1500]),
     (3, 2, 2, 64, 2, 2, 32, 32, 256, 32, [256, 33, 100]),
     (2, 32, 8, 128, 2, 4, 32, 128, 1024, 1024, [1024, 700]),
+    (2, 8, 2, 128, 8, 8, 32, 64, 512, 64, [500, 200]),
+    (3, 4, 2, 64, 8, 2, 64, 64, 256, 64, [256, 100, 65]),
 ]
 
 

@@ -32,6 +32,7 @@ QUANT_CASES = [
     # D, bK, bV, G
     (64, 2, 2, 32), (64, 4, 4, 64), (128, 2, 4, 32), (128, 4, 2, 64),
     (128, 4, 4, 128), (128, 2, 2, 64), (64, 2, 4, 64), (128, 2, 2, 128),
+    (64, 8, 8, 32), (128, 8, 4, 64), (128, 2, 8, 128), (128, 8, 2, 32),
 ]
 
 
@@ -104,6 +105,10 @@ DECODE_CASES = [
     (1, 16, 1, 128, 2, 4, 128, 128, [1500]),              # GQA 16, G128
     (2, 4, 2, 64, 2, 2, 32, 32, [1, 32]),                 # all residual
     (4, 4, 2, 64, 2, 2, 32, 32, [33, 64, 65, 31]),        # R, R+1, 2R, 2R+1
+    (2, 32, 8, 128, 8, 8, 32, 128, [3000, 2177]),         # 8-bit keys and values
+    (2, 16, 2, 64, 8, 4, 64, 64, [777, 64]),              # K8V4, D64, GQA 8
+    (3, 8, 2, 128, 4, 8, 128, 128, [1500, 129, 900]),     # K4V8, G128
+    (1, 16, 1, 128, 8, 2, 32, 128, [2000]),               # K8V2, GQA 16
 ]
 
 
@@ -206,7 +211,8 @@ def test_decode_deterministic():
 
 
 # ---------------------------------------------------------- append/flush ----
-@pytest.mark.parametrize("bK,bV,G,R", [(2, 2, 32, 32), (2, 4, 32, 128), (4, 2, 64, 64)])
+@pytest.mark.parametrize("bK,bV,G,R", [(2, 2, 32, 32), (2, 4, 32, 128), (4, 2, 64, 64),
+                                      (8, 8, 32, 64), (8, 2, 64, 64)])
 def test_append_flush_steps(bK, bV, G, R):
     """Several decode steps with appends crossing flushes at different steps per
     sequence: cache bit-exact and outputs within tolerance after every step."""

@@ -75,7 +75,7 @@ def _varlen_cache(orc, g, k, v, lens):
     return cache
 
 
-@pytest.mark.parametrize("bK,bV", [(2, 2), (2, 4), (4, 2), (4, 4)])
+@pytest.mark.parametrize("bK,bV", [(2, 2), (2, 4), (4, 2), (4, 4), (8, 8), (8, 2), (2, 8)])
 def test_attention_matches_torch_sdpa_gqa_varlen(orc, bK, bV):
     n = 200
     g, _, k, v, q = _tiny_case(orc, n, B=3, Hq=8, Hkv=2, bK=bK, bV=bV)
@@ -169,7 +169,8 @@ def test_all_residual_equals_unquantized(orc):
         np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
 
 
-@pytest.mark.parametrize("bK,bV,G,R", [(2, 2, 32, 32), (2, 4, 32, 64), (4, 2, 64, 64)])
+@pytest.mark.parametrize("bK,bV,G,R", [(2, 2, 32, 32), (2, 4, 32, 64), (4, 2, 64, 64), (8, 4, 32, 64),
+                                      (4, 8, 64, 64)])
 def test_appends_equal_bulk_quantization(orc, bK, bV, G, R):
     """Incremental appends (with lazy flushes) leave the same packed state as a
     bulk quantization of the packed prefix, bit for bit, for every length."""

@@ -147,7 +147,7 @@ def _check_group_brute_force(orc, x16: np.ndarray, bits: int):
             assert abs(code - near) == 1
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_brute_force_synthetic_groups(orc, bits):
     w = synth.WORKLOADS[3]
     k = synth.keys(w, 64, batch=1)           # [1][8][64][128]
@@ -168,7 +168,7 @@ def test_reconstruction_bound(orc):
     """|x - xhat| <= scale/2 + (2^b-1)|d32 - scale| (+ fp32 rounding); exact
     minimum; constant groups exact."""
     rng = np.random.default_rng(3)
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         levels = (1 << bits) - 1
         for trial in range(300):
             n = int(rng.choice([32, 64, 128]))
@@ -210,7 +210,11 @@ def _pattern_cache(orc, bits):
     cache = orc.Cache(g)
     t = np.arange(32)[:, None]
     c = np.arange(64)[None, :]
-    x = ((t + c) % (1 << bits)).astype(np.float16)[None, None]
+    if bits == 8:  # z = (t + c) mod 32 -> 0, 8, 16, ..., 240, 255 (z = 31)
+        z = (t + c) % 32
+        x = np.where(z == 31, 255, 8 * z).astype(np.float16)[None, None]
+    else:
+        x = ((t + c) % (1 << bits)).astype(np.float16)[None, None]
     orc.quantize_keys(g, cache, x, 0)
     orc.quantize_values(g, cache, x, 0)
     return cache
@@ -270,11 +274,22 @@ def _spec_pack(g, kc, vc, ksm, vsm):
         k, tau = divmod(t, 32)
         u, i_k = (tau // 4) % 2, 4 * (tau // 8) + tau % 4
         gv, j = divmod(tau, 8)
+        if bK == 8:  # word 2 kc + s of slice gk: byte f is channel 8 kc + 2 s + (0,1,4,5)[f]
+            for gk in range(4):
+                for w in range(KW):
+                    kcc, sw = divmod(w, 2)
+                    for f in range(4):
+                        c = gk * (D // 4) + 8 * kcc + 2 * sw + (0, 1, 4, 5)[f]
+                        kw[k, 16 * gk + i_k, u, w] |= int(kc[t, c]) << (8 * f)
         for c in range(D):
             gk, cs = divmod(c, D // 4)
-            kw[k, 16 * gk + i_k, u, cs * bK // 32] |= int(kc[t, c]) << (cs * bK % 32)
+            if bK != 8:
+                kw[k, 16 * gk + i_k, u, cs * bK // 32] |= int(kc[t, c]) << (cs * bK % 32)
             n, i_v = divmod(c, 16)
-            if bV == 4:
+            if bV == 8:
+                vw[k, 16 * gv + i_v, 2 * n + j // 4] |= \
+                    int(vc[t, c]) << (8 * ((j % 4) // 2) + 16 * (j % 2))
+            elif bV == 4:
                 vw[k, 16 * gv + i_v, n] |= int(vc[t, c]) << (4 * (j // 2) + 16 * (j % 2))
             else:
                 bit = 8 * (n % 2) + 2 * (j // 2) + 16 * (j % 2)
@@ -291,7 +306,8 @@ def _spec_pack(g, kc, vc, ksm, vsm):
 
 
 @pytest.mark.parametrize("D,bK,bV,G", [(64, 2, 2, 32), (64, 4, 4, 64), (128, 2, 4, 32),
-                                       (128, 4, 2, 128), (128, 2, 2, 64)])
+                                       (128, 4, 2, 128), (128, 2, 2, 64), (64, 8, 8, 32),
+                                       (128, 8, 4, 64), (128, 2, 8, 128), (64, 8, 2, 64)])
 def test_layout_matches_its_statement(orc, D, bK, bV, G):
     """The oracle's packed arrays equal the layout statement applied to codes
     and (scale, min) pairs produced group by group by the quantizer (pinned
