@@ -63,13 +63,14 @@ def lib():
         L.orc_quantize_values.argtypes = [ctypes.c_int] * 5 + [i64, P, i64, i64, P, P]
         L.orc_packed_len.restype = i64
         L.orc_packed_len.argtypes = [i64, ctypes.c_int]
-        L.orc_append.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 9
-        L.orc_cache_kv.argtypes = [ctypes.c_int] * 7 + [i64] + [P] * 6 + [i64, P, P]
-        L.orc_decode_attn.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 8 + [f64, P]
-        L.orc_decode_attn_multi.argtypes = ([ctypes.c_int] * 8 + [i64, ctypes.c_int] + [P] * 8
+        L.orc_append.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 9
+        L.orc_cache_kv.argtypes = [ctypes.c_int] * 8 + [i64] + [P] * 6 + [i64, P, P]
+        L.orc_decode_attn.argtypes = [ctypes.c_int] * 9 + [i64] + [P] * 8 + [f64, P]
+        L.orc_decode_attn_multi.argtypes = ([ctypes.c_int] * 9 + [i64, ctypes.c_int] + [P] * 8
                                             + [f64, P])
         L.orc_unpack.argtypes = [ctypes.c_int] * 6 + [i64] + [P] * 8
-        L.orc_residual_store.argtypes = [ctypes.c_int] * 4 + [P, P, i64, i64, P, P]
+        L.orc_key_residual_store.argtypes = [ctypes.c_int] * 4 + [P, i64, i64, P]
+        L.orc_value_residual_store.argtypes = [ctypes.c_int] * 4 + [P, i64, i64, P]
         L.orc_value_res_rows.argtypes = [ctypes.c_int] * 4 + [P, P]
         L.orc_bq2_hadamard.restype = f64
         L.orc_bq2_hadamard.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -141,6 +142,17 @@ class Geom:
     group: int
     residual: int
     capacity: int
+    residual_v: int = 0  # value window length; 0: the same as residual
+
+    @property
+    def rk(self) -> int:
+        """Key window length."""
+        return self.residual
+
+    @property
+    def rv(self) -> int:
+        """Value window length."""
+        return self.residual_v or self.residual
 
 
 class Cache:
@@ -155,8 +167,8 @@ class Cache:
         self.v_codes = np.zeros((B, H, blocks, 64, D * g.v_bits // 64), np.uint32)
         self.k_meta = np.zeros((B, H, C // g.group, D // 8, 8, 2), np.uint16)
         self.v_meta = np.zeros((B, H, blocks, 4, D // g.group, 8, 2), np.uint16)
-        self.k_res = np.zeros((B, H, g.residual, D), np.uint16)
-        self.v_res = np.zeros((B, H, g.residual // 32, D // 16, 64, 8), np.uint16)
+        self.k_res = np.zeros((B, H, g.rk, D), np.uint16)
+        self.v_res = np.zeros((B, H, g.rv // 32, D // 16, 64, 8), np.uint16)
 
     def arrays(self):
         return (self.k_codes, self.v_codes, self.k_meta, self.v_meta,
@@ -185,18 +197,23 @@ def packed_len(n: int, R: int) -> int:
 
 
 def prefill(g: Geom, cache: Cache, k: np.ndarray, v: np.ndarray, n: int) -> None:
-    """State after n single-token appends: [0, Lq) packed, [Lq, n) residual."""
+    """State after n single-token appends: keys [0, Lq(n, Rk)) packed and the
+    rest in the key window; values likewise with Rv."""
     k = _u16(k)
     v = _u16(v)
-    lq = packed_len(n, g.residual)
-    if lq > 0:
-        quantize_keys(g, cache, np.ascontiguousarray(k[:, :, :lq]), 0)
-        quantize_values(g, cache, np.ascontiguousarray(v[:, :, :lq]), 0)
-    if n > lq:
-        kr = np.ascontiguousarray(k[:, :, lq:n])
-        vr = np.ascontiguousarray(v[:, :, lq:n])
-        lib().orc_residual_store(g.batch, g.n_kv_heads, g.head_dim, g.residual, _p(kr),
-                                 _p(vr), lq, n - lq, _p(cache.k_res), _p(cache.v_res))
+    lqk, lqv = packed_len(n, g.rk), packed_len(n, g.rv)
+    if lqk > 0:
+        quantize_keys(g, cache, np.ascontiguousarray(k[:, :, :lqk]), 0)
+    if lqv > 0:
+        quantize_values(g, cache, np.ascontiguousarray(v[:, :, :lqv]), 0)
+    if n > lqk:
+        kr = np.ascontiguousarray(k[:, :, lqk:n])
+        lib().orc_key_residual_store(g.batch, g.n_kv_heads, g.head_dim, g.rk, _p(kr), lqk,
+                                     n - lqk, _p(cache.k_res))
+    if n > lqv:
+        vr = np.ascontiguousarray(v[:, :, lqv:n])
+        lib().orc_value_residual_store(g.batch, g.n_kv_heads, g.head_dim, g.rv, _p(vr), lqv,
+                                       n - lqv, _p(cache.v_res))
 
 
 def value_res_rows(g: Geom, v_res: np.ndarray) -> np.ndarray:
@@ -204,8 +221,8 @@ def value_res_rows(g: Geom, v_res: np.ndarray) -> np.ndarray:
     natural order [B][Hkv][R][D] (tests only)."""
     B = v_res.shape[0]
     v_res = np.ascontiguousarray(v_res).view(np.uint16)
-    out = np.zeros((B, g.n_kv_heads, g.residual, g.head_dim), np.uint16)
-    lib().orc_value_res_rows(B, g.n_kv_heads, g.head_dim, g.residual, _p(v_res), _p(out))
+    out = np.zeros((B, g.n_kv_heads, g.rv, g.head_dim), np.uint16)
+    lib().orc_value_res_rows(B, g.n_kv_heads, g.head_dim, g.rv, _p(v_res), _p(out))
     return out
 
 
@@ -215,7 +232,7 @@ def append(g: Geom, cache: Cache, k_new: np.ndarray, v_new: np.ndarray,
     v_new = _u16(v_new)
     sl = np.ascontiguousarray(seq_lens_before, dtype=np.int32)
     lib().orc_append(g.batch, g.n_kv_heads, g.head_dim, g.k_bits, g.v_bits,
-                     g.group, g.residual, g.capacity, _p(k_new), _p(v_new),
+                     g.group, g.rk, g.rv, g.capacity, _p(k_new), _p(v_new),
                      _p(sl), *[_p(a) for a in cache.arrays()])
 
 
@@ -225,7 +242,7 @@ def cache_kv(g: Geom, cache: Cache, n: int):
     ok = np.zeros(shape, np.float64)
     ov = np.zeros(shape, np.float64)
     lib().orc_cache_kv(g.batch, g.n_kv_heads, g.head_dim, g.k_bits, g.v_bits,
-                       g.group, g.residual, g.capacity,
+                       g.group, g.rk, g.rv, g.capacity,
                        *[_p(a) for a in cache.arrays()], n, _p(ok), _p(ov))
     return ok, ov
 
@@ -237,7 +254,7 @@ def decode_attn(g: Geom, cache: Cache, q: np.ndarray, seq_lens: np.ndarray,
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     out = np.zeros((g.batch, g.n_q_heads, g.head_dim), np.float64)
     lib().orc_decode_attn(g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim,
-                          g.k_bits, g.v_bits, g.group, g.residual, g.capacity,
+                          g.k_bits, g.v_bits, g.group, g.rk, g.rv, g.capacity,
                           _p(q), *[_p(a) for a in cache.arrays()], _p(sl),
                           float(sm_scale), _p(out))
     return out
@@ -252,7 +269,7 @@ def decode_attn_multi(g: Geom, cache: Cache, q: np.ndarray, seq_lens: np.ndarray
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     out = np.zeros((g.batch, T, g.n_q_heads, g.head_dim), np.float64)
     lib().orc_decode_attn_multi(g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, g.k_bits,
-                                g.v_bits, g.group, g.residual, g.capacity, T, _p(q),
+                                g.v_bits, g.group, g.rk, g.rv, g.capacity, T, _p(q),
                                 *[_p(a) for a in cache.arrays()], _p(sl), float(sm_scale),
                                 _p(out))
     return out

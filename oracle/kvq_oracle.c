@@ -198,9 +198,11 @@ void orc_quantize_group(const uint16_t *x, int64_t n, int64_t stride, int bits,
 /*          8((j%4)/2) + 16(j%2).                                            */
 /* v_meta   u16 [B][Hkv][C/32][4][D/G][8][2]: entry [k][g][gamma][j] is      */
 /*          token 32k + 8g + j, channel group gamma.                         */
-/* k_res    u16 [B][Hkv][R][D]: position p in slot p % R, one row per slot. */
-/* v_res    u16 [B][Hkv][R/32][D/16][64][8]: entry [k][n][16g + i][j] is     */
-/*          slot 32k + 8g + j, channel 16n + i; position p in slot p % R.   */
+/* k_res    u16 [B][Hkv][Rk][D]: position p in slot p % Rk, one row per     */
+/*          slot (Rk: the key window).                                      */
+/* v_res    u16 [B][Hkv][Rv/32][D/16][64][8]: entry [k][n][16g + i][j] is    */
+/*          slot 32k + 8g + j, channel 16n + i; position p in slot p % Rv   */
+/*          (Rv: the value window).                                         */
 /* ------------------------------------------------------------------------ */
 
 static void put_field(uint32_t *word, int bit, int bits, uint32_t code) {
@@ -404,11 +406,13 @@ int64_t orc_packed_len(int64_t n, int R) {
 }
 
 /* Appends one token per sequence.  seq_lens[b] = tokens held BEFORE the new
- * one.  If that count n is positive and a multiple of R, positions [n-R, n) are
- * quantized from the residual window first; then the new token goes to slot
- * n % R.  ([KIVI] core capabilities: recent tokens kept in fp16.)
- * k_new, v_new fp16 [B][Hkv][D]. */
-void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int R, int64_t C,
+ * one.  Keys and values each have their own window (Rk, Rv positions; [KVQ]
+ * Usage: a residual length per tensor).  If that count n is positive and a
+ * multiple of Rk, key positions [n-Rk, n) are quantized from the key window
+ * first, and likewise for values with Rv; then the new token goes to key slot
+ * n % Rk and value slot n % Rv.  ([KIVI] core capabilities: recent tokens
+ * kept in fp16.)  k_new, v_new fp16 [B][Hkv][D]. */
+void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int Rk, int Rv, int64_t C,
                 const uint16_t *k_new, const uint16_t *v_new,
                 const int32_t *seq_lens, uint32_t *k_codes, uint32_t *v_codes,
                 uint16_t *k_meta, uint16_t *v_meta, uint16_t *k_res,
@@ -419,20 +423,19 @@ void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int R, int64_t C,
     int b = (int)(u / Hkv);
     int64_t n = seq_lens[b];
     if (n < 0 || n >= C) continue;
-    uint16_t *kr = k_res + u * R * D;
-    uint16_t *vr = v_res + u * R * D;
-    if (n > 0 && n % R == 0) {
-      /* slots 0..R-1 hold positions n-R .. n-1 in order */
-      quantize_keys_unit(kr, n - R, R, D, bK, G, C, u, k_codes, k_meta);
-      uint16_t *rows = (uint16_t *)malloc((size_t)R * D * sizeof(uint16_t));
-      for (int s = 0; s < R; ++s)
+    uint16_t *kr = k_res + u * Rk * D;
+    uint16_t *vr = v_res + u * Rv * D;
+    if (n > 0 && n % Rk == 0) /* key slots 0..Rk-1 hold positions n-Rk .. n-1 */
+      quantize_keys_unit(kr, n - Rk, Rk, D, bK, G, C, u, k_codes, k_meta);
+    if (n > 0 && n % Rv == 0) {
+      uint16_t *rows = (uint16_t *)malloc((size_t)Rv * D * sizeof(uint16_t));
+      for (int s = 0; s < Rv; ++s)
         for (int c = 0; c < D; ++c) rows[s * D + c] = vr[value_res_index(D, s, c)];
-      quantize_values_unit(rows, n - R, R, D, bV, G, C, u, v_codes, v_meta);
+      quantize_values_unit(rows, n - Rv, Rv, D, bV, G, C, u, v_codes, v_meta);
       free(rows);
     }
-    int slot = (int)(n % R);
-    memcpy(kr + (int64_t)slot * D, k_new + u * D, (size_t)D * sizeof(uint16_t));
-    for (int c = 0; c < D; ++c) vr[value_res_index(D, slot, c)] = v_new[u * D + c];
+    memcpy(kr + (n % Rk) * D, k_new + u * D, (size_t)D * sizeof(uint16_t));
+    for (int c = 0; c < D; ++c) vr[value_res_index(D, (int)(n % Rv), c)] = v_new[u * D + c];
   }
 }
 
@@ -441,8 +444,8 @@ void orc_append(int B, int Hkv, int D, int bK, int bV, int G, int R, int64_t C,
 /* ------------------------------------------------------------------------ */
 
 /* Dequantized key of token t < packed length: code * scale + min ([KV1]
- * Dequantize).  The product of a code below 16 and an fp16 scale, plus an fp16
- * min, is exact in fp64. */
+ * Dequantize).  The product of a code below 256 and an fp16 scale, plus an
+ * fp16 min, is exact in fp64. */
 static double dequant_key(const uint32_t *k_codes, const uint16_t *k_meta,
                           const int *entry_of, int64_t unit, int64_t C, int D,
                           int bK, int G, int64_t t, int c) {
@@ -461,35 +464,39 @@ static double dequant_value(const uint32_t *v_codes, const uint16_t *v_meta,
   return (double)value_code(v_codes, unit, C, D, bV, t, c) * scale + minv;
 }
 
+/* Keys and values of positions t < n of unit u as the cache represents them:
+ * a key is dequantized below the key packed length Lq(n, Rk) and the key
+ * window's fp16 above it; a value likewise with Rv.  kk, vv fp64 [n][D]. */
+static void unit_kv(int D, int bK, int bV, int G, int Rk, int Rv, int64_t C,
+                    const int *entry_of, const uint32_t *k_codes, const uint32_t *v_codes,
+                    const uint16_t *k_meta, const uint16_t *v_meta, const uint16_t *k_res,
+                    const uint16_t *v_res, int64_t u, int64_t n, double *kk, double *vv) {
+  int64_t lqk = orc_packed_len(n, Rk), lqv = orc_packed_len(n, Rv);
+  for (int64_t t = 0; t < n; ++t)
+    for (int c = 0; c < D; ++c) {
+      kk[t * D + c] = t < lqk
+                          ? dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c)
+                          : orc_half_to_float(k_res[(u * Rk + t % Rk) * D + c]);
+      vv[t * D + c] =
+          t < lqv ? dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c)
+                  : orc_half_to_float(v_res[u * Rv * D + value_res_index(D, (int)(t % Rv), c)]);
+    }
+}
+
 /* Full-precision key/value of every position t < n of every unit as the cache
- * represents it: dequantized for t < packed length, residual fp16 otherwise.
- * out_k, out_v: fp64 [B*Hkv][n][D]. */
-void orc_cache_kv(int B, int Hkv, int D, int bK, int bV, int G, int R,
+ * represents it (unit_kv).  out_k, out_v: fp64 [B*Hkv][n][D]. */
+void orc_cache_kv(int B, int Hkv, int D, int bK, int bV, int G, int Rk, int Rv,
                   int64_t C, const uint32_t *k_codes, const uint32_t *v_codes,
                   const uint16_t *k_meta, const uint16_t *v_meta,
                   const uint16_t *k_res, const uint16_t *v_res, int64_t n,
                   double *out_k, double *out_v) {
   int64_t units = (int64_t)B * Hkv;
-  int64_t lq = orc_packed_len(n, R);
   int entry_of[128];
   key_meta_entries(D, bK, entry_of);
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t u = 0; u < units; ++u) {
-    for (int64_t t = 0; t < n; ++t) {
-      for (int c = 0; c < D; ++c) {
-        double kv, vv;
-        if (t < lq) {
-          kv = dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c);
-          vv = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
-        } else {
-          kv = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
-          vv = orc_half_to_float(v_res[u * R * D + value_res_index(D, (int)(t % R), c)]);
-        }
-        out_k[(u * n + t) * D + c] = kv;
-        out_v[(u * n + t) * D + c] = vv;
-      }
-    }
-  }
+  for (int64_t u = 0; u < units; ++u)
+    unit_kv(D, bK, bV, G, Rk, Rv, C, entry_of, k_codes, v_codes, k_meta, v_meta, k_res, v_res,
+            u, n, out_k + u * n * D, out_v + u * n * D);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -504,7 +511,7 @@ void orc_cache_kv(int B, int Hkv, int D, int bK, int bV, int G, int R,
  * rest), in fp64.  q fp16 [B][Hq][D]; out fp64 [B][Hq][D].  n == 0 gives 0.
  */
 void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
-                     int R, int64_t C, const uint16_t *q,
+                     int Rk, int Rv, int64_t C, const uint16_t *q,
                      const uint32_t *k_codes, const uint32_t *v_codes,
                      const uint16_t *k_meta, const uint16_t *v_meta,
                      const uint16_t *k_res, const uint16_t *v_res,
@@ -519,23 +526,12 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
     int hkv = (int)(u % Hkv);
     int64_t n = seq_lens[b];
     if (n > C) n = C;
-    int64_t lq = orc_packed_len(n, R);
     /* this unit's keys and values, as the cache represents them */
     double *kk = (double *)malloc((size_t)(n > 0 ? n : 1) * D * sizeof(double));
     double *vv = (double *)malloc((size_t)(n > 0 ? n : 1) * D * sizeof(double));
     double *s = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
-    for (int64_t t = 0; t < n; ++t) {
-      for (int c = 0; c < D; ++c) {
-        if (t < lq) {
-          kk[t * D + c] = dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c);
-          vv[t * D + c] = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
-        } else {
-          kk[t * D + c] = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
-          vv[t * D + c] =
-              orc_half_to_float(v_res[u * R * D + value_res_index(D, (int)(t % R), c)]);
-        }
-      }
-    }
+    unit_kv(D, bK, bV, G, Rk, Rv, C, entry_of, k_codes, v_codes, k_meta, v_meta, k_res, v_res,
+            u, n, kk, vv);
     for (int hh = 0; hh < g; ++hh) {
       int h = hkv * g + hh;
       const uint16_t *qh = q + ((int64_t)b * Hq + h) * D;
@@ -577,7 +573,7 @@ void orc_decode_attn(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
  * gets 0.
  */
 void orc_decode_attn_multi(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
-                           int R, int64_t C, int T, const uint16_t *q,
+                           int Rk, int Rv, int64_t C, int T, const uint16_t *q,
                            const uint32_t *k_codes, const uint32_t *v_codes,
                            const uint16_t *k_meta, const uint16_t *v_meta,
                            const uint16_t *k_res, const uint16_t *v_res,
@@ -592,22 +588,12 @@ void orc_decode_attn_multi(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
     int hkv = (int)(u % Hkv);
     int64_t n = seq_lens[b];
     if (n > C) n = C;
-    int64_t lq = orc_packed_len(n, R);
     int64_t nn = n > 0 ? n : 1;
     double *kk = (double *)malloc((size_t)nn * D * sizeof(double));
     double *vv = (double *)malloc((size_t)nn * D * sizeof(double));
     double *s = (double *)malloc((size_t)nn * sizeof(double));
-    for (int64_t t = 0; t < n; ++t)
-      for (int c = 0; c < D; ++c) {
-        if (t < lq) {
-          kk[t * D + c] = dequant_key(k_codes, k_meta, entry_of, u, C, D, bK, G, t, c);
-          vv[t * D + c] = dequant_value(v_codes, v_meta, u, C, D, bV, G, t, c);
-        } else {
-          kk[t * D + c] = orc_half_to_float(k_res[(u * R + t % R) * D + c]);
-          vv[t * D + c] =
-              orc_half_to_float(v_res[u * R * D + value_res_index(D, (int)(t % R), c)]);
-        }
-      }
+    unit_kv(D, bK, bV, G, Rk, Rv, C, entry_of, k_codes, v_codes, k_meta, v_meta, k_res, v_res,
+            u, n, kk, vv);
     for (int i = 0; i < T; ++i) {
       int64_t vis = n - T + i + 1; /* positions this token sees */
       for (int hh = 0; hh < g; ++hh) {
@@ -640,19 +626,28 @@ void orc_decode_attn_multi(int B, int Hq, int Hkv, int D, int bK, int bV, int G,
   }
 }
 
-/* Writes positions [pos0, pos0 + n_tok) of fp16 token rows k, v
- * [B*Hkv][n_tok][D] into their residual slots p % R. */
-void orc_residual_store(int B, int Hkv, int D, int R, const uint16_t *k,
-                        const uint16_t *v, int64_t pos0, int64_t n_tok,
-                        uint16_t *k_res, uint16_t *v_res) {
+/* Writes positions [pos0, pos0 + n_tok) of fp16 key rows k [B*Hkv][n_tok][D]
+ * into their key-window slots p % Rk. */
+void orc_key_residual_store(int B, int Hkv, int D, int Rk, const uint16_t *k, int64_t pos0,
+                            int64_t n_tok, uint16_t *k_res) {
   int64_t units = (int64_t)B * Hkv;
   for (int64_t u = 0; u < units; ++u)
     for (int64_t t = 0; t < n_tok; ++t) {
-      int slot = (int)((pos0 + t) % R);
-      for (int c = 0; c < D; ++c) {
-        k_res[(u * R + slot) * D + c] = k[(u * n_tok + t) * D + c];
-        v_res[u * R * D + value_res_index(D, slot, c)] = v[(u * n_tok + t) * D + c];
-      }
+      int slot = (int)((pos0 + t) % Rk);
+      for (int c = 0; c < D; ++c) k_res[(u * Rk + slot) * D + c] = k[(u * n_tok + t) * D + c];
+    }
+}
+
+/* Likewise for value rows v into the value window (slots p % Rv, layout
+ * above). */
+void orc_value_residual_store(int B, int Hkv, int D, int Rv, const uint16_t *v, int64_t pos0,
+                              int64_t n_tok, uint16_t *v_res) {
+  int64_t units = (int64_t)B * Hkv;
+  for (int64_t u = 0; u < units; ++u)
+    for (int64_t t = 0; t < n_tok; ++t) {
+      int slot = (int)((pos0 + t) % Rv);
+      for (int c = 0; c < D; ++c)
+        v_res[u * Rv * D + value_res_index(D, slot, c)] = v[(u * n_tok + t) * D + c];
     }
 }
 

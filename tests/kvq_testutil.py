@@ -39,24 +39,24 @@ def assert_cache_equal(cache: kvq.Cache, oc: oracle.Cache, lens=None, what=""):
             assert bad.size == 0, f"{what} {name}: {len(bad)} mismatches, first at {bad[0]}"
         return
     for b, n in enumerate(np.asarray(lens).tolist()):
-        lq = oracle.packed_len(n, g.residual)
+        lqk, lqv = oracle.packed_len(n, g.rk), oracle.packed_len(n, g.rv)
         sl = {
-            "k_codes": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
-            "k_meta": (slice(b, b + 1), slice(None), slice(0, lq // g.group)),
-            "v_codes": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
-            "v_meta": (slice(b, b + 1), slice(None), slice(0, lq // 32)),
+            "k_codes": (slice(b, b + 1), slice(None), slice(0, lqk // 32)),
+            "k_meta": (slice(b, b + 1), slice(None), slice(0, lqk // g.group)),
+            "v_codes": (slice(b, b + 1), slice(None), slice(0, lqv // 32)),
+            "v_meta": (slice(b, b + 1), slice(None), slice(0, lqv // 32)),
         }
         for name, idx in sl.items():
             o = getattr(oc, name)[idx]
             gg = got[name][idx]
             bad = np.argwhere(gg != o)
             assert bad.size == 0, f"{what} seq {b} {name}: {len(bad)} mismatches, first {bad[0]}"
-        res = {"k_res": (got["k_res"], oc.k_res),
+        res = {"k_res": (got["k_res"], oc.k_res, lqk, g.rk),
                "v_res": (oracle.value_res_rows(g, got["v_res"]),
-                         oracle.value_res_rows(g, oc.v_res))}
-        for t in range(lq, n):
-            s = t % g.residual
-            for name, (ga, oa) in res.items():
+                         oracle.value_res_rows(g, oc.v_res), lqv, g.rv)}
+        for name, (ga, oa, lq, R) in res.items():
+            for t in range(lq, n):
+                s = t % R
                 assert np.array_equal(ga[b, :, s], oa[b, :, s]), \
                     f"{what} seq {b} {name} slot {s}"
 

@@ -249,3 +249,93 @@ def test_multi_token_last_token_is_single_token_decode(orc):
     out = orc.decode_attn_multi(g, cache, q, np.array([97], np.int32), 4, 0.125)
     one = orc.decode_attn(g, cache, np.ascontiguousarray(q[:, 3]), np.array([97], np.int32), 0.125)
     np.testing.assert_array_equal(out[:, 3], one)
+
+
+# ------------------------------------- separate key and value windows --------
+def _group_dequant(orc, x16, bits):
+    d, m, codes = orc.quantize_group(np.ascontiguousarray(x16), bits)
+    scale = float(np.array([d], np.uint16).view(np.float16)[0])
+    mn = float(np.array([m], np.uint16).view(np.float16)[0])
+    return codes.astype(np.float64) * scale + mn
+
+
+@pytest.mark.parametrize("Rk,Rv,n", [(32, 128, 200), (128, 32, 200), (64, 96, 300),
+                                     (64, 32, 64), (32, 64, 33)])
+def test_separate_windows_attention_is_sdpa_on_the_mixed_cache(orc, Rk, Rv, n):
+    """With a key window of Rk and a value window of Rv positions ([KVQ] Usage:
+    a residual length per tensor), keys below n - r(n, Rk) are per-channel
+    group dequantized and values below n - r(n, Rv) per-token group
+    dequantized, each with the (pinned) group quantizer; everything else is
+    the fp16 input.  Attention equals SDPA on that reconstruction, built here
+    group by group without the packer."""
+    B, Hq, Hkv, D, bK, bV, G = 2, 4, 2, 64, 2, 4, 32
+    cap = 384
+    g = orc.Geom(B, Hq, Hkv, D, bK, bV, G, Rk, cap, residual_v=Rv)
+    rng = np.random.default_rng(Rk + 3 * Rv + n)
+    k = (rng.standard_normal((B, Hkv, n, D)) * rng.lognormal(0, .5, (1, Hkv, 1, D))).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, n, D)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    cache = orc.Cache(g)
+    orc.prefill(g, cache, k, v, n)
+    lqk = n - ((n - 1) % Rk + 1)
+    lqv = n - ((n - 1) % Rv + 1)
+    kk = k.astype(np.float64)
+    vv = v.astype(np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(lqk // G):
+                for c in range(D):
+                    kk[b, h, j * G:(j + 1) * G, c] = _group_dequant(orc, k[b, h, j * G:(j + 1) * G, c], bK)
+            for t in range(lqv):
+                for gm in range(D // G):
+                    vv[b, h, t, gm * G:(gm + 1) * G] = _group_dequant(orc, v[b, h, t, gm * G:(gm + 1) * G], bV)
+    ck, cv = orc.cache_kv(g, cache, n)
+    np.testing.assert_array_equal(ck, kk)
+    np.testing.assert_array_equal(cv, vv)
+    out = orc.decode_attn(g, cache, q, np.full(B, n), 0.125)
+    ref = _sdpa(q.astype(np.float64), kk, vv, 0.125)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("Rk,Rv", [(32, 64), (64, 32), (32, 96)])
+def test_separate_windows_appends_equal_bulk_quantization(orc, Rk, Rv):
+    """Keys flush every Rk appends and values every Rv appends, each on its own:
+    the packed prefixes and both windows equal a bulk prefill at every length."""
+    B, H, D, bK, bV, G = 2, 2, 64, 4, 2, 32
+    cap = 384
+    steps = 250
+    g = orc.Geom(B, H, H, D, bK, bV, G, Rk, cap, residual_v=Rv)
+    rng = np.random.default_rng(Rk * Rv)
+    k = rng.standard_normal((B, H, steps + 8, D)).astype(np.float16)
+    v = rng.standard_normal((B, H, steps + 8, D)).astype(np.float16)
+    start = np.array([0, 7])
+    inc = orc.Cache(g)
+    for b in range(B):
+        gb = orc.Geom(1, H, H, D, bK, bV, G, Rk, cap, residual_v=Rv)
+        cb = orc.Cache(gb)
+        orc.prefill(gb, cb, k[b:b + 1], v[b:b + 1], int(start[b]))
+        for dst, src in zip(inc.arrays(), cb.arrays()):
+            dst[b] = src[0]
+    lens = start.copy()
+    for step in range(steps):
+        kn = np.stack([k[b, :, lens[b]] for b in range(B)])
+        vn = np.stack([v[b, :, lens[b]] for b in range(B)])
+        orc.append(g, inc, kn, vn, lens.astype(np.int32))
+        lens += 1
+        if step % 7 and step != steps - 1:
+            continue
+        vrows = orc.value_res_rows(g, inc.v_res)
+        for b in range(B):
+            n = int(lens[b])
+            gb = orc.Geom(1, H, H, D, bK, bV, G, Rk, cap, residual_v=Rv)
+            ref = orc.Cache(gb)
+            orc.prefill(gb, ref, k[b:b + 1], v[b:b + 1], n)
+            lqk, lqv = orc.packed_len(n, Rk), orc.packed_len(n, Rv)
+            np.testing.assert_array_equal(inc.k_codes[b, :, :lqk // 32], ref.k_codes[0, :, :lqk // 32])
+            np.testing.assert_array_equal(inc.k_meta[b, :, :lqk // G], ref.k_meta[0, :, :lqk // G])
+            np.testing.assert_array_equal(inc.v_codes[b, :, :lqv // 32], ref.v_codes[0, :, :lqv // 32])
+            np.testing.assert_array_equal(inc.v_meta[b, :, :lqv // 32], ref.v_meta[0, :, :lqv // 32])
+            for t in range(lqk, n):
+                np.testing.assert_array_equal(inc.k_res[b, :, t % Rk], k[b, :, t].view(np.uint16))
+            for t in range(lqv, n):
+                np.testing.assert_array_equal(vrows[b, :, t % Rv], v[b, :, t].view(np.uint16))
