@@ -21,10 +21,14 @@
  * tokens shares one (scale, min) pair.  Values are quantized per token: every
  * token's head vector is cut into D/G groups of G consecutive channels, each
  * with its own (scale, min).  Codes have b = 2, 4 or 8 bits, chosen separately
- * for keys and values ([KVQ] Usage: the bit range of a budget goes up to 8).  The most recent tokens stay in an fp16 residual window of R
- * tokens until the window is full; then it is quantized into packed groups.
- * ([KIVI] core capabilities, Overview, Example: k_bits, v_bits, group_size,
+ * for keys and values ([KVQ] Usage: the bit range of a budget goes up to 8).
+ * The most recent tokens stay in an fp16 residual window of R tokens until the
+ * window is full; then it is quantized into packed groups.  ([KIVI] core
+ * capabilities, Overview, Example: k_bits, v_bits, group_size,
  * residual_length; [REC] notes: per-channel keys group outlier channels.)
+ * Keys and values may have windows of their own length ([KVQ] Usage: a
+ * residual length per tensor): R for keys, Rv for values; everything below
+ * then holds for each tensor with its own window.
  *
  * Group quantizer (affine, asymmetric; [KV1] Quantization Format gives the
  * formula for b = 2 and states that the fp16-rounded scale and min are used for
@@ -51,7 +55,8 @@
  * Decode attention for query head h of sequence b (GQA: the KV head is
  * h / (Hq / Hkv), i.e. consecutive query heads share one KV head):
  *   s_t = sm_scale * q_h . k_t   for the n tokens t < n (dequantized keys for
- *                                t < Lq, fp16 residual keys for t >= Lq)
+ *                                t < Lq, fp16 residual keys for t >= Lq; with
+ *                                Rv, values use their own Lq)
  *   out_h = sum_t softmax(s)_t * v_t     (fp32 accumulation, fp16 result)
  * The result equals softmax attention over the dequantized cache ([KV1]
  * Quickstart: attention over the cache's dequantized values, each token
@@ -109,9 +114,10 @@
  *            [gamma*G, gamma*G + G) at entry [k][g][gamma][j].
  *   k_res    uint16 [B][Hkv][R][D]     fp16 residual keys; position p lives
  *            in slot p % R, one row of D channels per slot.
- *   v_res    uint16 [B][Hkv][R/32][D/16][64][8]  fp16 residual values in the
+ *   v_res    uint16 [B][Hkv][Rv/32][D/16][64][8]  fp16 residual values in the
  *            value consumer order: entry [k][n][l][j] (l = 16g + i) is slot
- *            32k + 8g + j, channel 16n + i; position p lives in slot p % R.
+ *            32k + 8g + j, channel 16n + i; position p lives in slot p % Rv
+ *            (Rv = residual_v, or R when residual_v is 0).
  *
  * Earlier versions are retired: version 1 (token-major key rows,
  * channel-major value blocks) had scattered per-lane addresses and its loads
@@ -123,7 +129,8 @@
  *   n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; head_dim in {64, 128};
  *   k_bits, v_bits in {2, 4, 8}; group in {32, 64, 128}, group <= head_dim,
  *   head_dim % group == 0; residual % group == 0; capacity % residual == 0;
- *   capacity <= 2^24.
+ *   capacity <= 2^24; residual_v == 0, or residual_v % group == 0 and
+ *   capacity % residual_v == 0.
  *
  * ---------------------------------------------------------------------------
  * CONVENTIONS
@@ -156,7 +163,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_LAYOUT_VERSION 3
 #define KVQ_VBLOCK 32 /* tokens per v_codes block */
 
@@ -181,8 +188,10 @@ typedef struct kvq_geom {
   int32_t k_bits;     /* bK: 2, 4 or 8 */
   int32_t v_bits;     /* bV: 2, 4 or 8 */
   int32_t group;      /* G: tokens per key group = channels per value group */
-  int32_t residual;   /* R: fp16 residual window length, multiple of G */
-  int32_t capacity;   /* C: max tokens per sequence, multiple of R */
+  int32_t residual;   /* R: fp16 residual window length, multiple of G (the key
+                         window's when residual_v is set) */
+  int32_t capacity;   /* C: max tokens per sequence, multiple of R (and Rv) */
+  int32_t residual_v; /* Rv: value window length, multiple of G; 0: R */
 } kvq_geom;
 
 /* The six device buffers of one layer's cache (layout above). */

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 LAYOUT_VERSION = 3
 VBLOCK = 32
 
@@ -59,7 +59,7 @@ BQ2_SINKS = 4
 class kvq_geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits",
-        "group", "residual", "capacity")]
+        "group", "residual", "capacity", "residual_v")]
 
 
 class kvq_cache(ctypes.Structure):
@@ -177,11 +177,17 @@ class Geom:
     group: int
     residual: int
     capacity: int
+    residual_v: int = 0  # value window length; 0: the same as residual
+
+    @property
+    def rv(self) -> int:
+        """Value window length."""
+        return self.residual_v or self.residual
 
     def c(self) -> kvq_geom:
         return kvq_geom(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                         self.k_bits, self.v_bits, self.group, self.residual,
-                        self.capacity)
+                        self.capacity, self.residual_v)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -264,7 +270,7 @@ class Cache:
         self.v_meta = torch.zeros((B, H, blocks, 4, D // g.group, 8, 2),
                                   dtype=torch.int16, **z)
         self.k_res = torch.zeros((B, H, g.residual, D), dtype=torch.float16, **z)
-        self.v_res = torch.zeros((B, H, g.residual // 32, D // 16, 64, 8),
+        self.v_res = torch.zeros((B, H, g.rv // 32, D // 16, 64, 8),
                                  dtype=torch.float16, **z)
         sizes = kvq_cache_bytes(g)
         for t, s in zip(self.tensors(), sizes):
@@ -280,7 +286,7 @@ class Cache:
         c = Cache.__new__(Cache)
         c.g = Geom(b1 - b0, *[getattr(self.g, f) for f in (
             "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits", "group",
-            "residual", "capacity")])
+            "residual", "capacity", "residual_v")])
         for name in ("k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res"):
             setattr(c, name, getattr(self, name)[b0:b1])
         return c
@@ -423,7 +429,7 @@ class PagedCache:
         self.v_meta = torch.zeros((num_pages, H, P // VBLOCK, 4, D // G, 8, 2),
                                   dtype=torch.int16, **z)
         self.k_res = torch.zeros((g.batch, H, g.residual, D), dtype=torch.float16, **z)
-        self.v_res = torch.zeros((g.batch, H, g.residual // 32, D // 16, 64, 8),
+        self.v_res = torch.zeros((g.batch, H, g.rv // 32, D // 16, 64, 8),
                                  dtype=torch.float16, **z)
         if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
                 block_table.shape[0] != g.batch or not block_table.is_contiguous():
@@ -444,7 +450,7 @@ class PagedCache:
         c = PagedCache.__new__(PagedCache)
         c.g = Geom(b1 - b0, *[getattr(self.g, f) for f in (
             "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits", "group",
-            "residual", "capacity")])
+            "residual", "capacity", "residual_v")])
         c.page_size, c.num_pages, c.max_pages = self.page_size, self.num_pages, self.max_pages
         c.k_codes, c.v_codes, c.k_meta, c.v_meta = (self.k_codes, self.v_codes, self.k_meta,
                                                     self.v_meta)

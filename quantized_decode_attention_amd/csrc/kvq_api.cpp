@@ -58,6 +58,12 @@ int check_geom(const kvq_geom* g) {
   if (g->capacity < g->residual || g->capacity % g->residual != 0 || g->capacity > (1 << 24))
     return fail(KVQ_ERR_GEOM, "capacity (%d) must be a multiple of residual (%d), <= 2^24",
                 g->capacity, g->residual);
+  if (g->residual_v < 0 || (g->residual_v > 0 && g->residual_v % g->group != 0))
+    return fail(KVQ_ERR_GEOM, "residual_v (%d) must be 0 or a positive multiple of group (%d)",
+                g->residual_v, g->group);
+  if (g->residual_v > 0 && g->capacity % g->residual_v != 0)
+    return fail(KVQ_ERR_GEOM, "capacity (%d) must be a multiple of residual_v (%d)",
+                g->capacity, g->residual_v);
   return KVQ_OK;
 }
 
@@ -359,8 +365,9 @@ int kvq_cache_bytes(const kvq_geom* geom, size_t out[6]) {
   out[1] = B * H * (C / KVQ_VBLOCK) * D * geom->v_bits * 4;      // v_codes
   out[2] = B * H * (C / G) * D * 2 * 2;                          // k_meta
   out[3] = B * H * C * (D / G) * 2 * 2;                          // v_meta
+  const size_t Rv = geom->residual_v > 0 ? geom->residual_v : R;
   out[4] = B * H * R * D * 2;                                    // k_res
-  out[5] = B * H * R * D * 2;                                    // v_res
+  out[5] = B * H * Rv * D * 2;                                   // v_res
   return KVQ_OK;
 }
 
@@ -447,14 +454,18 @@ int kvq_prefill(const kvq_geom* geom, const uint16_t* k, const uint16_t* v, int3
     if ((st = check_ptr(v, "v")) != KVQ_OK) return st;
     const kvq::Geom g = kvq::to_geom(*geom);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int lq = packed_len(n, g.R);
+    const int lqk = packed_len(n, g.R), lqv = packed_len(n, g.Rv);
     const int64_t stride = (int64_t)n * g.D;
-    hipError_t e = kvq::launch_quantize_keys(g, k, stride, 0, lq, cache->k_codes, cache->k_meta, s);
+    hipError_t e =
+        kvq::launch_quantize_keys(g, k, stride, 0, lqk, cache->k_codes, cache->k_meta, s);
     if (e != hipSuccess) return hip_fail(e, "prefill quantize_keys launch");
-    e = kvq::launch_quantize_values(g, v, stride, 0, lq, cache->v_codes, cache->v_meta, s);
+    e = kvq::launch_quantize_values(g, v, stride, 0, lqv, cache->v_codes, cache->v_meta, s);
     if (e != hipSuccess) return hip_fail(e, "prefill quantize_values launch");
-    e = kvq::launch_residual_copy(g, k + (int64_t)lq * g.D, v + (int64_t)lq * g.D, stride, lq,
-                                  n - lq, cache->k_res, cache->v_res, s);
+    e = kvq::launch_residual_copy(g, k + (int64_t)lqk * g.D, stride, lqk, n - lqk,
+                                  cache->k_res, false, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill residual copy launch");
+    e = kvq::launch_residual_copy(g, v + (int64_t)lqv * g.D, stride, lqv, n - lqv,
+                                  cache->v_res, true, s);
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "prefill residual copy launch");
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");
@@ -713,8 +724,9 @@ int kvq_paged_cache_bytes(const kvq_geom* geom, int32_t page_size, int32_t num_p
     out[1] = N * H * (P / KVQ_VBLOCK) * D * geom->v_bits * 4;  // v_codes
     out[2] = N * H * (P / G) * D * 2 * 2;                      // k_meta
     out[3] = N * H * P * (D / G) * 2 * 2;                      // v_meta
+    const size_t Rv = geom->residual_v > 0 ? geom->residual_v : R;
     out[4] = (size_t)geom->batch * H * R * D * 2;              // k_res
-    out[5] = (size_t)geom->batch * H * R * D * 2;              // v_res
+    out[5] = (size_t)geom->batch * H * Rv * D * 2;             // v_res
     return KVQ_OK;
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");
@@ -751,14 +763,18 @@ int kvq_paged_prefill(const kvq_geom* geom, const uint16_t* k, const uint16_t* v
     if ((st = check_ptr(v, "v")) != KVQ_OK) return st;
     const kvq::Geom g = kvq::to_geom(*geom, *cache);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int lq = packed_len(n, g.R);
+    const int lqk = packed_len(n, g.R), lqv = packed_len(n, g.Rv);
     const int64_t stride = (int64_t)n * g.D;
-    hipError_t e = kvq::launch_quantize_keys(g, k, stride, 0, lq, cache->k_codes, cache->k_meta, s);
+    hipError_t e =
+        kvq::launch_quantize_keys(g, k, stride, 0, lqk, cache->k_codes, cache->k_meta, s);
     if (e != hipSuccess) return hip_fail(e, "prefill quantize_keys launch");
-    e = kvq::launch_quantize_values(g, v, stride, 0, lq, cache->v_codes, cache->v_meta, s);
+    e = kvq::launch_quantize_values(g, v, stride, 0, lqv, cache->v_codes, cache->v_meta, s);
     if (e != hipSuccess) return hip_fail(e, "prefill quantize_values launch");
-    e = kvq::launch_residual_copy(g, k + (int64_t)lq * g.D, v + (int64_t)lq * g.D, stride, lq,
-                                  n - lq, cache->k_res, cache->v_res, s);
+    e = kvq::launch_residual_copy(g, k + (int64_t)lqk * g.D, stride, lqk, n - lqk,
+                                  cache->k_res, false, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill residual copy launch");
+    e = kvq::launch_residual_copy(g, v + (int64_t)lqv * g.D, stride, lqv, n - lqv,
+                                  cache->v_res, true, s);
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "prefill residual copy launch");
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");

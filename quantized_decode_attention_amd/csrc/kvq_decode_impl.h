@@ -179,7 +179,7 @@ struct PackedWave {
       return ch;
     } else {
       const int page = ch >> cpp_log2;
-      if (page - tbase >= 64) {  // chunks only move forward inside a range
+      if ((unsigned)(page - tbase) >= 64u) {  // outside the window: move it here
         tbase = page;
         tab = tbase + lane < maxp ? trow[tbase + lane] : 0;
       }
@@ -359,12 +359,12 @@ struct PackedWave {
     m_odd = m_run;
   }
 
-  // Switch to the residual window: bring the packed accumulation to real scale
-  // (codes were fp16 numbers c * 2^-24) with its value-min term added, and set
-  // the key-side B fragments to q * 2^-E in natural channel order (element j of
-  // lane group g, k-chunk kc = channel 32 kc + 8 g + j), hi or lo part.
-  __device__ __forceinline__ void enter_residual() {
-    to_real();
+  // Key-side B fragments for fp16 keys: q * 2^-E in natural channel order
+  // (element j of lane group g, k-chunk kc = channel 32 kc + 8 g + j), hi or
+  // lo part.  (Before the residual window, to_real() brings the packed
+  // accumulation to real scale; the two steps are apart because a mixed chunk
+  // with packed values and fp16 keys needs only this one.)
+  __device__ __forceinline__ void plain_query() {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg);
@@ -388,33 +388,50 @@ struct PackedWave {
     cur_group = -1;
   }
 
-  // Residual chunk: fp16 tokens t0 + [0, 32) of the window (those >= n_tok
-  // masked).  Keys come straight from the window's slot rows; values are
-  // stored in the value consumer order, so tile n's A operand is one 16-byte
-  // load per lane (slots past n_tok are zeroed in registers: their weight is
-  // 0, and the window may hold anything there).
-  __device__ __forceinline__ void process_residual(int t0, int n_tok, int R,
-                                                   const uint16_t* kres,
-                                                   const uint16_t* vres) {
-    // value operands first: their loads overlap the score MFMAs
+  // fp16 windows.  Keys come straight from the key window's slot rows (slot
+  // p % Rk); values are stored in the value consumer order (slot p % Rv), so
+  // tile n's A operand is one 16-byte load per lane.
+  // Value operands of the 32 positions t0 + [0, 32) (t0 a multiple of 32).
+  __device__ __forceinline__ void window_values_load(int t0, int Rv, const uint16_t* vres,
+                                                     uint4 (&va)[NT]) const {
     const uint4* vq = reinterpret_cast<const uint4*>(vres) +
-                      (int64_t)((t0 % R) / kChunk) * (D / 16) * 64 + lane;
-    uint4 va[NT];
+                      (int64_t)((t0 % Rv) / kChunk) * (D / 16) * 64 + lane;
 #pragma unroll
     for (int n = 0; n < NT; ++n) va[n] = vq[n * 64];
+  }
+  // Weighted sum of those values (real-scale accumulators); slots past n_tok
+  // are zeroed in registers: their weight is 0, and the window may hold
+  // anything there.
+  __device__ __forceinline__ void window_values_mma(const uint4 (&va)[NT], int t0, int n_tok,
+                                                    const float (&p)[2][4]) {
     uint32_t vmask[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 8 * lg + 2 * i;
       vmask[i] = (t < n_tok ? 0x0000ffffu : 0u) | (t + 1 < n_tok ? 0xffff0000u : 0u);
     }
+    uint32_t bh[4], bl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], m1, bh[i], bl[i]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint32_t a[4] = {va[n].x & vmask[0], va[n].y & vmask[1], va[n].z & vmask[2],
+                             va[n].w & vmask[3]};
+      oacc[n] = mfma(a, bh, oacc[n]);
+      oacc[n] = mfma(a, bl, oacc[n]);
+    }
+  }
+  // Scores of positions t0 + [0, 32) from the key window (B fragments from
+  // plain_query()); positions this lane's row must not see get -inf.
+  __device__ __forceinline__ void window_scores(int t0, int n_tok, int Rk, const uint16_t* kres,
+                                                float (&s)[2][4]) {
     // scores: tile u row r = token key_row_token(u, r)
     const float kscale_r = bscale;  // keys are real fp16 values here
-    float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tin = t0 + key_row_token(u, col);
-      const int slot_in = (tin < n_tok ? tin : n_tok - 1) % R;
+      const int slot_in = (tin < n_tok ? tin : n_tok - 1) % Rk;
       const uint4* krow = reinterpret_cast<const uint4*>(kres + (int64_t)slot_in * D);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -435,19 +452,46 @@ struct PackedWave {
         s[u][q] = valid ? x * kscale_r : kNegInf;
       }
     }
+  }
+
+  // Residual chunk: fp16 keys and values of positions t0 + [0, 32) (those >=
+  // n_tok masked).
+  __device__ __forceinline__ void process_residual(int t0, int n_tok, int Rk, int Rv,
+                                                   const uint16_t* kres,
+                                                   const uint16_t* vres) {
+    uint4 va[NT];
+    window_values_load(t0, Rv, vres, va);  // first: the loads overlap the score MFMAs
+    float s[2][4];
+    window_scores(t0, n_tok, Rk, kres, s);
     float p[2][4];
     softmax<false>(s, p);
-    uint32_t bh[4], bl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], m1, bh[i], bl[i]);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint32_t a[4] = {va[n].x & vmask[0], va[n].y & vmask[1], va[n].z & vmask[2],
-                             va[n].w & vmask[3]};
-      oacc[n] = mfma(a, bh, oacc[n]);
-      oacc[n] = mfma(a, bl, oacc[n]);
-    }
+    window_values_mma(va, t0, n_tok, p);
+  }
+
+  // Mixed chunk ch with packed keys and fp16 values (the key window is the
+  // shorter one): scores from the codes, weights plain (the accumulators are
+  // at real scale), values from the value window.
+  __device__ __forceinline__ void process_mixed_keys(int ch, const R& r, int n_tok, int Rv,
+                                                     const uint16_t* vres) {
+    uint4 va[NT];
+    window_values_load(ch * kChunk, Rv, vres, va);
+    float s[2][4];
+    packed_scores<true>(ch, r, n_tok - 1 - hide, s);
+    float p[2][4];
+    softmax<false>(s, p);
+    window_values_mma(va, ch * kChunk, n_tok, p);
+  }
+
+  // Mixed chunk ch with fp16 keys and packed values: scores from the key
+  // window (after plain_query()), weights in the packed classes (the
+  // accumulators are still at code scale), values from the codes.
+  __device__ __forceinline__ void process_mixed_values(int ch, const R& r, int n_tok, int Rk,
+                                                       const uint16_t* kres) {
+    float s[2][4];
+    window_scores(ch * kChunk, n_tok, Rk, kres, s);
+    float p[2][4];
+    softmax<true>(s, p);
+    packed_values(r, p);
   }
 
   // kMask: positions after last_vis (this lane's row, 32-token chunk ch) get
@@ -455,6 +499,19 @@ struct PackedWave {
   // are real cache data, so their weight 0 is exact).
   template <bool kMask = false>
   __device__ __forceinline__ void process(int ch, const R& r, int last_vis = 0) {
+    float s[2][4];
+    packed_scores<kMask>(ch, r, last_vis, s);
+    float p[2][4];
+    softmax<true>(s, p);
+    packed_values(r, p);
+  }
+
+  // Scores of packed chunk ch (folding the key group's meta when it starts):
+  // s = 2^(E+24) * (codes x q') + beta; with kMask, positions after last_vis
+  // get -inf.
+  template <bool kMask>
+  __device__ __forceinline__ void packed_scores(int ch, const R& r, int last_vis,
+                                                float (&s)[2][4]) {
     if constexpr (G == kChunk) {
       fold(r);  // every chunk is a key group: no branch, so the fold can be
                 // scheduled against the previous chunk's value products
@@ -465,8 +522,6 @@ struct PackedWave {
         fold(r);
       }
     }
-    // scores: s = 2^(E+24) * (codes x q') + beta
-    float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t a[KC][4];
@@ -490,9 +545,11 @@ struct PackedWave {
           s[u][q] = ch * kChunk + 8 * lg + 4 * u + q <= last_vis ? s[u][q] : kNegInf;
       }
     }
-    float p[2][4];
-    softmax<true>(s, p);
-    // weighted value sum
+  }
+
+  // Weighted sum of a packed chunk's values (code-scale accumulators, weights
+  // in the packed classes) and its value-min term.
+  __device__ __forceinline__ void packed_values(const R& r, const float (&p)[2][4]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       uint32_t bh[4], bl[4];
@@ -541,13 +598,20 @@ struct PackedWave {
 // stand for equal HBM traffic).  The decomposition itself (kvq_device.h) cuts
 // the flat list of all units' work into equal shares, one per worker wave.
 // ---------------------------------------------------------------------------
+// With separate key and value windows the two packed lengths differ: chunks
+// below both are packed, chunks between them mixed (packed for one tensor,
+// in the window for the other; rw work units like a residual chunk), the
+// rest residual.
 __device__ __forceinline__ SeqWork seq_work_of(const DecodeLaunch& L, int n) {
   SeqWork sw{0, 0, 0, 0};
   if (n <= 0 || n > L.g.C || n > L.max_seq_len) return sw;
-  const int lq = packed_len(n, L.g.R);
+  const int lqk = packed_len(n, L.g.R), lqv = packed_len(n, L.g.Rv);
+  const int lo = min(lqk, lqv), hi = max(lqk, lqv);
   sw.n = n;
-  sw.nq = lq / kChunk;
-  sw.nr = (n - lq + kChunk - 1) / kChunk;
+  sw.nq = lo / kChunk;
+  sw.nm = (hi - lo) / kChunk;
+  sw.keys_packed = lqk > lqv;
+  sw.nr = sw.nm + (n - hi + kChunk - 1) / kChunk;
   sw.w = sw.nq + sw.nr * L.rw;
   return sw;
 }
@@ -679,17 +743,39 @@ __device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw
     if (ch != pc0) w.load(ch, ra);
     w.template process<true>(ch, ra, last_vis);
   }
-  const bool resid = rk0 < rk1;
-  if (resid) {
-    w.enter_residual();
-    const uint16_t* kres = L.cache.k_res + unit * g.R * D;
-    const uint16_t* vres = L.cache.v_res + unit * g.R * D;
-    const int lq = sw.nq * kChunk;
-    for (int k = rk0; k < rk1; ++k) w.process_residual(lq + k * kChunk, sw.n, g.R, kres, vres);
+  // chunks past the packed ones: k < nm mixed (chunk nq + k), then residual
+  // (positions (nq + k) * 32 ..); both are in the windows' slots p % Rk, p % Rv
+  const uint16_t* kres = L.cache.k_res + unit * g.R * D;
+  const uint16_t* vres = L.cache.v_res + unit * g.Rv * D;
+  bool real = false;  // accumulators at real scale
+  const int mk1 = min(rk1, sw.nm);
+  if (rk0 < mk1) {
+    if (sw.keys_packed) {
+      w.to_real();
+      real = true;
+      for (int k = rk0; k < mk1; ++k) {
+        w.load(sw.nq + k, ra);
+        w.process_mixed_keys(sw.nq + k, ra, sw.n, g.Rv, vres);
+      }
+    } else {
+      w.plain_query();
+      for (int k = rk0; k < mk1; ++k) {
+        w.load(sw.nq + k, ra);
+        w.process_mixed_values(sw.nq + k, ra, sw.n, g.R, kres);
+      }
+    }
+  }
+  const int r0 = max(rk0, sw.nm);
+  if (r0 < rk1) {
+    if (!real) w.to_real();
+    real = true;
+    if (sw.keys_packed || rk0 >= mk1) w.plain_query();  // unless mixed chunks did it
+    for (int k = r0; k < rk1; ++k)
+      w.process_residual((sw.nq + k) * kChunk, sw.n, g.R, g.Rv, kres, vres);
   }
 
   // partial: O (value-min term included), max, sum of this wave's tokens
-  if (!resid) w.to_real();
+  if (!real) w.to_real();
   float l_run = w.l_run;
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);

@@ -225,8 +225,11 @@ constexpr int kPartPad = 4;  // partial row = D values, max, sum, 2 pad floats
 struct SeqWork {
   int n;   // tokens (0 for an invalid length)
   int nq;  // packed chunks per KV head
-  int nr;  // residual chunks per KV head
+  int nr;  // residual chunks per KV head (rw work units each; the first nm of
+           // them are mixed chunks, packed for one tensor only)
   int w;   // work units per KV head
+  int nm = 0;          // mixed chunks (separate key and value windows)
+  bool keys_packed = false;  // in the mixed chunks: keys packed (else values)
 };
 // Inclusive prefix sum over the wave's 64 lanes: DPP shifts inside each row
 // of 16 lanes, then row broadcasts (lane 15 into the next row, lane 31 into

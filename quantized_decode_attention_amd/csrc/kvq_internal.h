@@ -30,6 +30,7 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 // pages of 32 << cpp_log2 positions.
 struct Geom {
   int B, Hq, Hkv, D, bK, bV, G, R, C;
+  int Rv;                // value window length (R is the key window's)
   const int32_t* table;  // block table [B][maxp], or nullptr (dense)
   int cpp_log2;          // log2 of the 32-position chunks per page
   int maxp;              // table entries per sequence
@@ -38,7 +39,8 @@ struct Geom {
 
 inline Geom to_geom(const kvq_geom& g) {
   return Geom{g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, g.k_bits,
-              g.v_bits, g.group, g.residual, g.capacity, nullptr, 0, 0, 0};
+              g.v_bits, g.group, g.residual, g.capacity,
+              g.residual_v > 0 ? g.residual_v : g.residual, nullptr, 0, 0, 0};
 }
 
 inline Geom to_geom(const kvq_geom& g, const kvq_paged_cache& c) {
@@ -85,10 +87,11 @@ hipError_t launch_quantize_values(const Geom& g, const uint16_t* src,
                                   int64_t src_unit_stride, int32_t pos0,
                                   int32_t n_tok, uint32_t* v_codes,
                                   uint16_t* v_meta, hipStream_t st);
-hipError_t launch_residual_copy(const Geom& g, const uint16_t* k,
-                                const uint16_t* v, int64_t src_unit_stride,
-                                int32_t pos0, int32_t n_tok, uint16_t* k_res,
-                                uint16_t* v_res, hipStream_t st);
+// Positions [pos0, pos0 + n_tok) of key (values = false) or value rows into
+// their window slots.
+hipError_t launch_residual_copy(const Geom& g, const uint16_t* src, int64_t src_unit_stride,
+                                int32_t pos0, int32_t n_tok, uint16_t* window, bool values,
+                                hipStream_t st);
 hipError_t launch_append(const Geom& g, const uint16_t* k_new,
                          const uint16_t* v_new, const int32_t* seq_lens,
                          const kvq_cache& cache, hipStream_t st);

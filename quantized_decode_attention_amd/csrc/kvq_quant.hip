@@ -271,42 +271,48 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(
   value_block<BITS>(g, unit, pos0 + blk * kVBlock, v_codes, v_meta, tile, codes);
 }
 
-// Copies positions [pos0, pos0 + n_tok) of k and v ([unit][.][D] with the given
-// unit stride, first row = position pos0) to residual slots p % R.
+// Copies positions [pos0, pos0 + n_tok) of key rows (values == false; window
+// of R slots, token rows) or value rows (window of Rv slots, value consumer
+// order) src [unit][.][D] (first row = position pos0) to slots p % window.
 __global__ __launch_bounds__(kThreads) void residual_copy_kernel(
-    Geom g, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int64_t src_unit_stride, int32_t pos0, int32_t n_tok,
-    uint16_t* __restrict__ k_res, uint16_t* __restrict__ v_res) {
+    Geom g, const uint16_t* __restrict__ src, int64_t src_unit_stride, int32_t pos0,
+    int32_t n_tok, uint16_t* __restrict__ window, bool values) {
   const int64_t vecs_per_row = g.D / 8;
   const int64_t total = (int64_t)g.B * g.Hkv * n_tok * vecs_per_row;
+  const int W = values ? g.Rv : g.R;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = i % vecs_per_row;
     const int64_t t = (i / vecs_per_row) % n_tok;
     const int64_t unit = i / (vecs_per_row * n_tok);
-    const int64_t slot = (pos0 + t) % g.R;
-    const int64_t s = unit * src_unit_stride / 8 + t * vecs_per_row + e;
-    const int64_t d = (unit * g.R + slot) * vecs_per_row + e;
-    reinterpret_cast<uint4*>(k_res)[d] = reinterpret_cast<const uint4*>(k)[s];
-    // values: channels 8e .. 8e+7 of the slot go to their window places
-    const uint4 x = reinterpret_cast<const uint4*>(v)[s];
-    const uint32_t xx[4] = {x.x, x.y, x.z, x.w};
-    uint16_t* vu = v_res + unit * g.R * g.D;
+    const int64_t slot = (pos0 + t) % W;
+    const uint4 x = reinterpret_cast<const uint4*>(src)[unit * src_unit_stride / 8 +
+                                                        t * vecs_per_row + e];
+    if (!values) {
+      reinterpret_cast<uint4*>(window)[(unit * W + slot) * vecs_per_row + e] = x;
+    } else {
+      // channels 8e .. 8e+7 of the slot go to their window places
+      const uint32_t xx[4] = {x.x, x.y, x.z, x.w};
+      uint16_t* vu = window + unit * W * g.D;
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const uint16_t val = (uint16_t)((h & 1) ? (xx[h / 2] >> 16) : (xx[h / 2] & 0xffffu));
-      vu[value_res_index(g.D, (int)slot, (int)(8 * e + h))] = val;
+      for (int h = 0; h < 8; ++h) {
+        const uint16_t val = (uint16_t)((h & 1) ? (xx[h / 2] >> 16) : (xx[h / 2] & 0xffffu));
+        vu[value_res_index(g.D, (int)slot, (int)(8 * e + h))] = val;
+      }
     }
   }
 }
 
-// Grid (KV head, sequence, 1 + R/G + R/32).  z = 0 writes the new token to
-// slot n % R when no flush is due.  When one is due (n > 0, n % R == 0: the
-// window holds positions n - R .. n - 1 in slots 0 .. R-1), z = 1 .. R/G
-// quantize the key groups and z = R/G + 1 .. the 32-token value blocks of the
-// window, each in its own workgroup; the workgroups that read slot 0 (key
-// group 0, value block 0) write the new token there after their read, so no
-// workgroup waits for another.  Without a flush, z >= 1 return at once.
+// Grid (KV head, sequence, 1 + R/G + Rv/32); keys have a window of R slots,
+// values of Rv (R = Rv unless set apart).  z = 0 writes the new token to key
+// slot n % R when no key flush is due, and to value slot n % Rv when no value
+// flush is due.  A key flush is due when n > 0 and n % R == 0 (the key window
+// holds positions n - R .. n - 1 in slots 0 .. R-1): z = 1 .. R/G quantize
+// its key groups.  A value flush likewise with Rv: z = R/G + 1 .. its 32-token
+// value blocks.  Each in its own workgroup; the workgroup that reads slot 0
+// of a flushing window (key group 0, value block 0) writes the new token
+// there after its read, so no workgroup waits for another.  Workgroups with
+// nothing to do return at once.
 template <int BK, int BV>
 __global__ __launch_bounds__(kThreads) void append_kernel(
     Geom g, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -320,22 +326,23 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   const int32_t n = seq_lens[b];
   if (n < 0 || n >= g.C) return;  // caller error: leave the cache untouched
   uint16_t* kr = k_res + unit * g.R * g.D;
-  uint16_t* vr = v_res + unit * g.R * g.D;
-  const bool flush = n > 0 && n % g.R == 0;
-  const int nk = g.R / g.G;  // key groups of the window
-  if (!flush) {
-    if (z != 0) return;
-    const int slot = n % g.R;
-    for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
-      kr[(int64_t)slot * g.D + c] = k_new[unit * g.D + c];
-      vr[value_res_index(g.D, slot, c)] = v_new[unit * g.D + c];
-    }
+  uint16_t* vr = v_res + unit * g.Rv * g.D;
+  const bool kflush = n > 0 && n % g.R == 0;
+  const bool vflush = n > 0 && n % g.Rv == 0;
+  const int nk = g.R / g.G;  // key groups of the key window
+  if (z == 0) {
+    if (!kflush)
+      for (int c = threadIdx.x; c < g.D; c += blockDim.x)
+        kr[(int64_t)(n % g.R) * g.D + c] = k_new[unit * g.D + c];
+    if (!vflush)
+      for (int c = threadIdx.x; c < g.D; c += blockDim.x)
+        vr[value_res_index(g.D, n % g.Rv, c)] = v_new[unit * g.D + c];
     return;
   }
-  if (z == 0) return;
   uint16_t* tile = lds;
   uint8_t* codes = reinterpret_cast<uint8_t*>(lds + quant_rows(g) * g.D);
   if (z <= nk) {
+    if (!kflush) return;
     const int j = z - 1;
     load_tile(tile, kr + (int64_t)j * g.G * g.D, g.G * g.D);
     __syncthreads();
@@ -343,13 +350,14 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
       for (int c = threadIdx.x; c < g.D; c += blockDim.x) kr[c] = k_new[unit * g.D + c];
     key_group<BK>(g, unit, n - g.R + j * g.G, k_codes, k_meta, tile, codes);
   } else {
+    if (!vflush) return;
     const int blk = z - 1 - nk;
     load_value_window(tile, vr, blk, g.D);
     __syncthreads();
     if (blk == 0)
       for (int c = threadIdx.x; c < g.D; c += blockDim.x)
         vr[value_res_index(g.D, 0, c)] = v_new[unit * g.D + c];
-    value_block<BV>(g, unit, n - g.R + blk * kVBlock, v_codes, v_meta, tile, codes);
+    value_block<BV>(g, unit, n - g.Rv + blk * kVBlock, v_codes, v_meta, tile, codes);
   }
 }
 
@@ -391,23 +399,22 @@ hipError_t launch_quantize_values(const Geom& g, const uint16_t* src,
   return hipGetLastError();
 }
 
-hipError_t launch_residual_copy(const Geom& g, const uint16_t* k,
-                                const uint16_t* v, int64_t src_unit_stride,
-                                int32_t pos0, int32_t n_tok, uint16_t* k_res,
-                                uint16_t* v_res, hipStream_t st) {
+hipError_t launch_residual_copy(const Geom& g, const uint16_t* src, int64_t src_unit_stride,
+                                int32_t pos0, int32_t n_tok, uint16_t* window, bool values,
+                                hipStream_t st) {
   if (n_tok == 0) return hipSuccess;
   const int64_t total = (int64_t)g.B * g.Hkv * n_tok * (g.D / 8);
   const int64_t blocks = (total + kThreads - 1) / kThreads;
   dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
-  residual_copy_kernel<<<grid, kThreads, 0, st>>>(g, k, v, src_unit_stride,
-                                                  pos0, n_tok, k_res, v_res);
+  residual_copy_kernel<<<grid, kThreads, 0, st>>>(g, src, src_unit_stride, pos0, n_tok, window,
+                                                  values);
   return hipGetLastError();
 }
 
 hipError_t launch_append(const Geom& g, const uint16_t* k_new,
                          const uint16_t* v_new, const int32_t* seq_lens,
                          const kvq_cache& c, hipStream_t st) {
-  dim3 grid(g.Hkv, g.B, 1 + g.R / g.G + g.R / kVBlock);
+  dim3 grid(g.Hkv, g.B, 1 + g.R / g.G + g.Rv / kVBlock);
 #define KVQ_APPEND(BK, BV)                                                    \
   append_kernel<BK, BV><<<grid, kThreads, quant_lds_bytes(g), st>>>(          \
       g, k_new, v_new, seq_lens, c.k_codes, c.v_codes, c.k_meta, c.v_meta,    \

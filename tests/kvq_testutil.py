@@ -11,9 +11,10 @@ import quantized_decode_attention_amd as kvq
 NAMES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_res", "v_res")
 
 
-def geoms(B, Hq, Hkv, D, bK, bV, G, R, C):
-    return (kvq.Geom(B, Hq, Hkv, D, bK, bV, G, R, C),
-            oracle.Geom(B, Hq, Hkv, D, bK, bV, G, R, C))
+def geoms(B, Hq, Hkv, D, bK, bV, G, R, C, Rv=0):
+    """Library and oracle geometry; Rv: a value window of its own (0: R)."""
+    return (kvq.Geom(B, Hq, Hkv, D, bK, bV, G, R, C, Rv),
+            oracle.Geom(B, Hq, Hkv, D, bK, bV, G, R, C, residual_v=Rv))
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
@@ -89,7 +90,8 @@ def prefill_both(g, og, k, v, lens):
         sub = cache.view(b, b + 1)
         kvq.kvq_prefill(sub.g, dev(k[b:b + 1, :, :n]), dev(v[b:b + 1, :, :n]), n, sub)
         ob = oracle.Geom(1, og.n_q_heads, og.n_kv_heads, og.head_dim, og.k_bits, og.v_bits,
-                         og.group, og.residual, og.capacity)
+                         og.group, og.residual, og.capacity,
+                         residual_v=og.residual_v)
         c1 = oracle.Cache(ob)
         oracle.prefill(ob, c1, k[b:b + 1, :, :n], v[b:b + 1, :, :n], n)
         for dst, src in zip(oc.arrays(), c1.arrays()):

@@ -139,7 +139,7 @@ def test_bq2_cache_bytes_and_memory_table():
 
 
 def test_versions_and_status_strings():
-    assert kvq.kvq_abi_version() == kvq.ABI_VERSION == 1
+    assert kvq.kvq_abi_version() == kvq.ABI_VERSION == 2
     assert kvq.kvq_layout_version() == kvq.LAYOUT_VERSION == 3
     for s in range(-8, 1):
         assert kvq.status_str(s) and kvq.status_str(s) != "unknown status"
@@ -162,6 +162,28 @@ def test_geometry_validation(field, value, status):
         kvq.kvq_validate_geom(kvq.Geom(**bad))
     assert e.value.status == status
     assert kvq.last_error()
+
+
+@pytest.mark.parametrize("rv,ok", [(0, True), (32, True), (256, True), (64, True),
+                                   (48, False), (-32, False), (384, False)])
+def test_value_window_validation(rv, ok):
+    """residual_v: 0 (the key window's length) or a multiple of group that
+    divides capacity (1024 here)."""
+    g = kvq.Geom(**{**GOOD, "residual_v": rv})
+    if ok:
+        kvq.kvq_validate_geom(g)
+        return
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_validate_geom(g)
+    assert e.value.status == -2
+
+
+def test_value_window_bytes():
+    g = kvq.Geom(**{**GOOD, "residual_v": 256})
+    kc, vc, km, vm, kr, vr = kvq.kvq_cache_bytes(g)
+    assert kr == 2 * 8 * 128 * 128 * 2
+    assert vr == 2 * 8 * 256 * 128 * 2
+    assert kvq.kvq_paged_cache_bytes(g, 128, 4)[4:] == [kr, vr]
 
 
 def test_group_larger_than_head_dim():
