@@ -31,7 +31,8 @@
  * block_table[b][0] = b.
  *
  * Table entries are read for the pages that hold packed positions only
- * (positions below Lq(n), kvq.h): a sequence of n tokens needs entries
+ * (positions below Lq(n), kvq.h; with a separate value window, the larger of
+ * the key and value packed lengths): a sequence of n tokens needs entries
  * [0, ceil(Lq(n) / P)) set; the rest of its row is never read.  An entry that
  * is read and lies outside [0, num_pages) makes decode give NaN for that
  * sequence and makes the writers skip that page (nothing outside the pools is
