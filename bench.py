@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--page-size", type=int, default=0,
                    help="KIVI workloads: a paged cache with pages of this many positions, "
                         "handed out in shuffled order (0: the dense cache)")
+    p.add_argument("--eager", action="store_true",
+                   help="time the steps as launched one by one (default: the timed steps "
+                        "are also captured as one HIP graph, and value is its replay)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -166,6 +169,32 @@ def cpu_baseline_bq2(w, target_seconds: float):
     }
 
 
+def time_steps(a, step, torch):
+    """Times the K steps after the warmup: first launched one by one with the
+    decode-partial events (step(s, i) records them), then, unless --eager, the
+    same K steps captured as one HIP graph (a serving loop's launch form) and
+    replayed: one untimed replay, then the timed one.  Each pass appends the
+    same tokens at the same positions: the same work on the same sizes.
+    Returns (eager seconds, seconds of the run that gives value)."""
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, i)
+    torch.cuda.synchronize()
+    eager = time.perf_counter() - t0
+    if a.eager:
+        return eager, eager
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(a.steps):
+            step(a.warmup + i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    return eager, time.perf_counter() - t0
+
+
 def run_bq2(a, w, torch, kvq, metrics, synth):
     """The rotated per-token 2-bit format: kvq_bq2_append then
     kvq_bq2_decode_partial (timed per launch) and kvq_bq2_decode_combine."""
@@ -203,11 +232,11 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
     dec_bytes = [metrics.bq2_decode_step_bytes(lens_host[s, 1], w.n_q_heads, w.n_kv_heads)
                  for s in range(total_steps)]
     step_bytes = [d + metrics.bq2_append_bytes(w.batch, w.n_kv_heads) for d in dec_bytes]
-    stream = torch.cuda.current_stream()
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
     def step(s, timed_idx=None):
+        stream = torch.cuda.current_stream()  # the capture stream inside a graph capture
         kn, vn, q = pool[s % len(pool)]
         c = caches[s % L]
         kvq.kvq_bq2_append(g, kn, vn, lens_dev[s, 0], c, stream)
@@ -221,13 +250,10 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
     for s in range(a.warmup):
         step(s)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(a.warmup + i, i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager, elapsed = time_steps(a, step, torch)
     timed = slice(a.warmup, a.warmup + a.steps)
     gbs = float(np.sum(step_bytes[timed])) / elapsed / 1e9
+    gbs_eager = float(np.sum(step_bytes[timed])) / elapsed_eager / 1e9
     part_avg_s = float(np.mean([ev_a[i].elapsed_time(ev_b[i]) for i in range(a.steps)])) / 1e3
     dec_avg_bytes = float(np.mean(dec_bytes[timed]))
     achieved = dec_avg_bytes / part_avg_s / 1e9
@@ -254,7 +280,12 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
             "context_last_step": int(lens_host[-1, 1].max()),
             "rotating_layer_caches": L, "decode_worker_waves": n_workers,
             "step": "kvq_bq2_append + kvq_bq2_decode_attn, one layer",
+            "launch": ("kernels launched one by one" if a.eager else
+                       "the timed steps replayed as one HIP graph"),
         },
+        "eager": {"value": round(gbs_eager, 2), "unit": "GB/s",
+                  "ms_per_step": round(elapsed_eager / a.steps * 1e3, 5),
+                  "tokens_per_s": round(w.batch * a.steps / elapsed_eager, 1)},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch * a.steps / elapsed, 1),
         "tokens_per_s_unit": "decoded tokens per second through one layer",
@@ -409,11 +440,11 @@ def main():
         step_bytes.append(sb)
         dec_bytes.append(db)
 
-    stream = torch.cuda.current_stream()
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
     def step(s, timed_idx=None):
+        stream = torch.cuda.current_stream()  # the capture stream inside a graph capture
         l = s % L
         c = caches[l]
         for j in range(T):
@@ -436,11 +467,7 @@ def main():
     for s in range(a.warmup):
         step(s)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(a.warmup + i, i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager, elapsed = time_steps(a, step, torch)
 
     timed = slice(a.warmup, a.warmup + a.steps)
     total_bytes = float(np.sum(step_bytes[timed]))
@@ -449,6 +476,7 @@ def main():
     dec_avg_bytes = float(np.mean(dec_bytes[timed]))
     achieved = dec_avg_bytes / part_avg_s / 1e9
     gbs = total_bytes / elapsed / 1e9
+    gbs_eager = total_bytes / elapsed_eager / 1e9
     traffic = load_traffic(w.name) if T == 1 and not P else None
 
     rec = {
@@ -478,7 +506,12 @@ def main():
                      f"{T} x kvq_append + kvq_decode_attn_multi (T={T}), one layer"),
             "query_tokens": T,
             "cache": f"paged, {P}-position pages in shuffled order" if P else "dense",
+            "launch": ("kernels launched one by one" if a.eager else
+                       "the timed steps replayed as one HIP graph"),
         },
+        "eager": {"value": round(gbs_eager, 2), "unit": "GB/s",
+                  "ms_per_step": round(elapsed_eager / a.steps * 1e3, 5),
+                  "tokens_per_s": round(w.batch * T * a.steps / elapsed_eager, 1)},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch * T * a.steps / elapsed, 1),
         "tokens_per_s_unit": "decoded tokens per second through one layer",

@@ -7,6 +7,7 @@ separate IEEE operations (bit-exact codes).  No fast-math anywhere.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -47,11 +48,25 @@ def _compile(name: str, source: str, extra: list[str]) -> str:
     src = os.path.join(CSRC, source)
     obj = os.path.join(BUILD, name + ".o")
     lang = ["-x", "hip"] if source.endswith(".hip") else []
-    cmd = [HIPCC, *ARCH, *COMMON, *extra, *lang, "-c", src, "-o", obj]
+    # the decode partial kernels keep all their state in registers: a kernel
+    # that needs scratch (a private array or an outlined helper taking the wave
+    # state by reference) runs many times slower, so it fails the build
+    guard = name.startswith("decode_partial")
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if guard else []
+    cmd = [HIPCC, *ARCH, *COMMON, *extra, *remarks, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed on " + name)
+    if guard:
+        func = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                func = m.group(1)
+            m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+            if m and int(m.group(1)) > 0:
+                raise RuntimeError(f"{name}: {func} uses {m.group(1)} bytes/lane of scratch")
     return obj
 
 

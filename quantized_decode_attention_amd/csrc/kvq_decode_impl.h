@@ -668,9 +668,10 @@ __device__ __forceinline__ void seg_begin(const DecodeLaunch& L, int b, int hkv,
 
 // Runs the range of unit (b, hkv) -> partial p, seg_begin having been done.
 template <int D, int BK, int BV, int GQ, int NG, bool PG>
-__device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
-                        const SegRange& r, int p, char* smem, int lane,
-                        PackedWave<D, BK, BV, GQ, NG, PG>& w, Raw<D, BK, BV, GQ, NG>& ra) {
+__device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
+                                        const SegRange& r, int p, char* smem, int lane,
+                                        PackedWave<D, BK, BV, GQ, NG, PG>& w,
+                                        Raw<D, BK, BV, GQ, NG>& ra) {
   using C = Cfg<D, BK, BV, GQ, NG>;
   using R = Raw<D, BK, BV, GQ, NG>;
   constexpr int NT = C::NT, SL = C::SL;
@@ -809,8 +810,9 @@ __device__ void seg_run(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw
 // The part of unit (b, hkv) in work range [x0, x1) -> partial p.  xu = first
 // work unit of the unit.
 template <int D, int BK, int BV, int GQ, int NG, bool PG>
-__device__ void unit_segment(const DecodeLaunch& L, int b, int hkv, const SeqWork& sw,
-                             int xu, int x0, int x1, int p, char* smem, int lane) {
+__device__ __forceinline__ void unit_segment(const DecodeLaunch& L, int b, int hkv,
+                                             const SeqWork& sw, int xu, int x0, int x1, int p,
+                                             char* smem, int lane) {
   constexpr int DP = D + kPartPad;
   const SegRange r = seg_range(L, sw, xu, x0, x1);
   if (r.pc0 >= r.pc1 && r.rk0 >= r.rk1) {  // only part of a residual chunk's weight
