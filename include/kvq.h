@@ -351,27 +351,6 @@ int kvq_decode_attn_multi(const kvq_geom *geom, const uint16_t *q,
                           void *workspace, size_t workspace_bytes,
                           uint16_t *out, void *stream);
 
-/* ----- decode in one kernel ------------------------------------------------ */
-
-/* kvq_decode_attn_multi (T = 1: kvq_decode_attn) in one kernel launch instead
- * of two: the wave that writes the last partial of a (sequence, KV head) unit
- * merges that unit's partials and writes its outputs (the combine's merge,
- * same results up to rounding), so a decode step has one launch fewer.  Same
- * arguments and rules as kvq_decode_attn_multi, except the workspace:
- *   workspace  at least kvq_decode_fused_workspace_bytes(geom, T, max_seq_len)
- *              bytes, 16-byte aligned, holding the partials and one counter
- *              per unit.  It must be ZEROED ONCE before its first use (e.g.
- *              hipMemset at allocation); every call that runs to completion
- *              leaves the counters zero again, so it is reused as is (also
- *              under HIP graph replay).  Calls that overlap on one workspace
- *              race. */
-int kvq_decode_fused_workspace_bytes(const kvq_geom *geom, int32_t T, int32_t max_seq_len,
-                                     size_t *bytes);
-int kvq_decode_attn_fused(const kvq_geom *geom, const uint16_t *q, const kvq_cache *cache,
-                          const int32_t *seq_lens, int32_t T, int32_t max_seq_len,
-                          float sm_scale, void *workspace, size_t workspace_bytes,
-                          uint16_t *out, void *stream);
-
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

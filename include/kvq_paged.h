@@ -121,16 +121,6 @@ int kvq_paged_decode_attn_multi(const kvq_geom *geom, const uint16_t *q,
                                 void *workspace, size_t workspace_bytes, uint16_t *out,
                                 void *stream);
 
-/* kvq_decode_attn_fused over the paged cache (same arguments and rules,
- * including the workspace zeroed once before its first use). */
-int kvq_paged_decode_fused_workspace_bytes(const kvq_geom *geom, int32_t T,
-                                           int32_t max_seq_len, size_t *bytes);
-int kvq_paged_decode_attn_fused(const kvq_geom *geom, const uint16_t *q,
-                                const kvq_paged_cache *cache, const int32_t *seq_lens,
-                                int32_t T, int32_t max_seq_len, float sm_scale,
-                                void *workspace, size_t workspace_bytes, uint16_t *out,
-                                void *stream);
-
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

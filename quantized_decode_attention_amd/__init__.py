@@ -26,5 +26,3 @@ from ._lib import (  # noqa: F401
     kvq_paged_decode_attn, kvq_paged_decode_attn_multi, kvq_paged_decode_combine,
     kvq_paged_decode_partial, kvq_paged_decode_workspace_bytes, kvq_paged_prefill,
     kvq_paged_validate)
-from ._lib import (  # noqa: F401
-    alloc_fused_workspace, kvq_decode_attn_fused, kvq_decode_fused_workspace_bytes)

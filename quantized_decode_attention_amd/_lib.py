@@ -41,7 +41,6 @@ EXPORTS = [
     "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append",
     "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
     "kvq_decode_multi_workspace_bytes", "kvq_decode_attn_multi",
-    "kvq_decode_fused_workspace_bytes", "kvq_decode_attn_fused",
 ]
 EXPORTS_BQ2 = [
     "kvq_bq2_validate_geom", "kvq_bq2_cache_bytes", "kvq_bq2_decode_workers",
@@ -52,7 +51,6 @@ EXPORTS_PAGED = [
     "kvq_paged_validate", "kvq_paged_cache_bytes", "kvq_paged_decode_workspace_bytes",
     "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_decode_attn",
     "kvq_paged_decode_partial", "kvq_paged_decode_combine", "kvq_paged_decode_attn_multi",
-    "kvq_paged_decode_fused_workspace_bytes", "kvq_paged_decode_attn_fused",
 ]
 BQ2_HEAD_DIM = 64
 BQ2_SINKS = 4
@@ -137,12 +135,6 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_combine": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_multi_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
             "kvq_decode_attn_multi": (ctypes.c_int, [G, P, C, P, i32, i32, f32, P, sz, P, P]),
-            "kvq_decode_fused_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
-            "kvq_decode_attn_fused": (ctypes.c_int, [G, P, C, P, i32, i32, f32, P, sz, P, P]),
-            "kvq_paged_decode_fused_workspace_bytes": (ctypes.c_int,
-                                                       [G, i32, i32, ctypes.POINTER(sz)]),
-            "kvq_paged_decode_attn_fused": (ctypes.c_int, [G, P, CP, P, i32, i32, f32, P, sz, P,
-                                                           P]),
             "kvq_bq2_validate_geom": (ctypes.c_int, [G2]),
             "kvq_bq2_cache_bytes": (ctypes.c_int, [G2, ctypes.POINTER(sz)]),
             "kvq_bq2_decode_workers": (ctypes.c_int, [G2, ctypes.POINTER(i32)]),
@@ -410,43 +402,6 @@ def kvq_decode_attn_multi(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torc
         _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(T), int(max_seq_len),
         float(sm_scale), _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out", _F16, shape),
         _stream(stream)), "kvq_decode_attn_multi")
-
-
-def kvq_decode_fused_workspace_bytes(g: Geom, T: int, max_seq_len: int, paged: bool = False) -> int:
-    gc = g.c()
-    out = ctypes.c_size_t()
-    name = ("kvq_paged_decode_fused_workspace_bytes" if paged else
-            "kvq_decode_fused_workspace_bytes")
-    _check(getattr(lib(), name)(ctypes.byref(gc), T, max_seq_len, ctypes.byref(out)), name)
-    return out.value
-
-
-def alloc_fused_workspace(g: Geom, T: int, max_seq_len: int, paged: bool = False,
-                          device="cuda") -> torch.Tensor:
-    """A zeroed workspace for kvq_decode_attn_fused / kvq_paged_decode_attn_fused
-    (it must be zero before its first use; the calls leave it reusable)."""
-    n = kvq_decode_fused_workspace_bytes(g, T, max_seq_len, paged)
-    return torch.zeros(n // 4, dtype=torch.float32, device=device)
-
-
-def kvq_decode_attn_fused(g: Geom, q: torch.Tensor, cache, seq_lens: torch.Tensor, T: int,
-                          max_seq_len: int, sm_scale: float, workspace: torch.Tensor,
-                          out: torch.Tensor, stream=None) -> None:
-    """Decode attention in one kernel over a dense Cache or a PagedCache
-    (q, out [B][T][Hq][D], or [B][Hq][D] when T = 1)."""
-    gc = g.c()
-    shape = (g.batch, T, g.n_q_heads, g.head_dim)
-    if T == 1 and q.dim() == 3:
-        shape = (g.batch, g.n_q_heads, g.head_dim)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    paged = isinstance(cache, PagedCache)
-    cc = cache.c() if paged else _cache_arg(cache)
-    name = "kvq_paged_decode_attn_fused" if paged else "kvq_decode_attn_fused"
-    _check(getattr(lib(), name)(
-        ctypes.byref(gc), _ptr(q, "q", _F16, shape), ctypes.byref(cc),
-        _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(T), int(max_seq_len),
-        float(sm_scale), _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out", _F16, shape),
-        _stream(stream)), name)
 
 
 def alloc_multi_workspace(g: Geom, T: int, max_seq_len: int, device="cuda") -> torch.Tensor:

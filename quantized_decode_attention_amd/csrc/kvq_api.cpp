@@ -145,18 +145,9 @@ size_t workspace_need(const kvq_geom* g, int32_t n_workers, int T = 1) {
          (g->head_dim + 4) * sizeof(float);
 }
 
-// The fused decode's workspace: the partials, then (16-byte aligned) one
-// uint32 counter per (sequence, KV head).
-size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
-size_t fused_workspace_need(const kvq_geom* g, int32_t n_workers, int T) {
-  return align16(workspace_need(g, n_workers, T)) +
-         align16((size_t)g->batch * g->n_kv_heads * sizeof(uint32_t));
-}
-
 int check_workspace(const kvq_geom* g, int32_t n_workers, const void* ws, size_t bytes,
-                    int T = 1, bool fused = false) {
-  const size_t need = fused ? fused_workspace_need(g, n_workers, T)
-                            : workspace_need(g, n_workers, T);
+                    int T = 1) {
+  const size_t need = workspace_need(g, n_workers, T);
   if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (bytes < need)
@@ -202,8 +193,7 @@ int check_paged(const kvq_geom* g, const kvq_paged_cache* c, bool buffers) {
 int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
                  const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                  void* workspace, size_t workspace_bytes, uint16_t* out,
-                 kvq::DecodeLaunch* L, int32_t T = 1, const kvq_paged_cache* pc = nullptr,
-                 bool fused = false) {
+                 kvq::DecodeLaunch* L, int32_t T = 1, const kvq_paged_cache* pc = nullptr) {
   int st = check_geom(geom);
   if (st != KVQ_OK) return st;
   if (pc && (st = check_paged(geom, pc, true)) != KVQ_OK) return st;
@@ -220,11 +210,8 @@ int decode_setup(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache
   if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
   int32_t n_workers = 0;
   if ((st = workers_for(geom, &n_workers, T, pc != nullptr)) != KVQ_OK) return st;
-  if ((st = check_workspace(geom, n_workers, workspace, workspace_bytes, T, fused)) != KVQ_OK)
+  if ((st = check_workspace(geom, n_workers, workspace, workspace_bytes, T)) != KVQ_OK)
     return st;
-  L->counters = fused ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                    align16(workspace_need(geom, n_workers, T)))
-                      : nullptr;
   L->g = pc ? kvq::to_geom(*geom, *pc) : kvq::to_geom(*geom);
   L->q = q;
   L->cache = *cache;
@@ -874,77 +861,6 @@ int kvq_paged_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_pag
                           void* stream) {
   return kvq_paged_decode_attn_multi(geom, q, cache, seq_lens, 1, max_seq_len, sm_scale,
                                      workspace, workspace_bytes, out, stream);
-}
-
-// ---- decode in one kernel (partial and combine fused) ----------------------
-
-int kvq_decode_fused_workspace_bytes(const kvq_geom* geom, int32_t T, int32_t max_seq_len,
-                                     size_t* bytes) {
-  try {
-    int st = check_geom(geom);
-    if (st != KVQ_OK) return st;
-    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
-    if ((st = check_tokens(geom, T)) != KVQ_OK) return st;
-    if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
-    int32_t nw = 0;
-    if ((st = workers_for(geom, &nw, T)) != KVQ_OK) return st;
-    *bytes = fused_workspace_need(geom, nw, T);
-    return KVQ_OK;
-  } catch (...) {
-    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
-  }
-}
-
-int kvq_decode_attn_fused(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
-                          const int32_t* seq_lens, int32_t T, int32_t max_seq_len,
-                          float sm_scale, void* workspace, size_t workspace_bytes,
-                          uint16_t* out, void* stream) {
-  try {
-    kvq::DecodeLaunch L;
-    int st = decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale, workspace,
-                          workspace_bytes, out, &L, T, nullptr, true);
-    if (st != KVQ_OK) return st;
-    hipError_t e = kvq::launch_decode_partial(L, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode (fused) launch");
-  } catch (...) {
-    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
-  }
-}
-
-int kvq_paged_decode_fused_workspace_bytes(const kvq_geom* geom, int32_t T,
-                                           int32_t max_seq_len, size_t* bytes) {
-  try {
-    int st = check_geom(geom);
-    if (st != KVQ_OK) return st;
-    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
-    if ((st = check_tokens(geom, T)) != KVQ_OK) return st;
-    if ((st = check_max_len(geom, max_seq_len)) != KVQ_OK) return st;
-    int32_t nw = 0;
-    if ((st = workers_for(geom, &nw, T, true)) != KVQ_OK) return st;
-    *bytes = fused_workspace_need(geom, nw, T);
-    return KVQ_OK;
-  } catch (...) {
-    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
-  }
-}
-
-int kvq_paged_decode_attn_fused(const kvq_geom* geom, const uint16_t* q,
-                                const kvq_paged_cache* cache, const int32_t* seq_lens,
-                                int32_t T, int32_t max_seq_len, float sm_scale,
-                                void* workspace, size_t workspace_bytes, uint16_t* out,
-                                void* stream) {
-  try {
-    if (!cache) return fail(KVQ_ERR_NULL, "cache is NULL");
-    const kvq_cache view = kvq::pool_view(*cache);
-    kvq::DecodeLaunch L;
-    int st = decode_setup(geom, q, &view, seq_lens, max_seq_len, sm_scale, workspace,
-                          workspace_bytes, out, &L, T, cache, true);
-    if (st != KVQ_OK) return st;
-    hipError_t e = kvq::launch_decode_partial(L, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode (fused) launch");
-  } catch (...) {
-    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
-  }
 }
 
 }  // extern "C"

@@ -830,72 +830,6 @@ __device__ __forceinline__ void unit_segment(const DecodeLaunch& L, int b, int h
   seg_run<D, BK, BV, GQ, NG, PG>(L, b, hkv, sw, r, p, smem, lane, w, ra);
 }
 
-// Fused combine.  Unit (b, hkv) with work [xu, xu + wu) has one partial from
-// each wave w_first .. w_last whose share meets it (at indices w + unit).  A
-// wave that has written its partial counts it (agent-scope atomic after a
-// release fence); the wave that completes the count merges the unit's
-// partials as the combine kernel does and writes its outputs, then resets the
-// counter to 0 for the next call.  No wave waits for another.
-template <int D, int GQ>
-__device__ __forceinline__ void unit_finish(const DecodeLaunch& L, int b, int hkv, int xu, int wu,
-                                            int cpw, int lane) {
-  constexpr int DP = D + kPartPad;
-  const int w_first = xu / cpw, w_last = (xu + wu - 1) / cpw;
-  const int S = w_last - w_first + 1;
-  const int64_t unit = (int64_t)b * L.g.Hkv + hkv;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the partial's stores, all lanes
-  __builtin_amdgcn_wave_barrier();
-  uint32_t old = 0;
-  if (lane == 0)
-    old = __hip_atomic_fetch_add(L.counters + unit, 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  if ((int)old != S - 1) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every partial of the unit
-  const float* base = L.ws + (w_first + unit) * GQ * DP;
-  for (int t = lane; t < GQ * D / 4; t += 64) {
-    const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
-    float M = kNegInf, Ls = 0.0f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < S; ++s) {
-      const float* q = base + (int64_t)s * GQ * DP + oh * DP;
-      const float m = q[D], l = q[D + 1];
-      const float4 o = *reinterpret_cast<const float4*>(q + oc);
-      if (m == kNegInf) continue;  // an empty partial
-      const float Mn = fmaxf(M, m);
-      const float a = exp2_hw(M - Mn), c = exp2_hw(m - Mn);
-      M = Mn;
-      Ls = Ls * a + l * c;
-      O.x = O.x * a + o.x * c;
-      O.y = O.y * a + o.y * c;
-      O.z = O.z * a + o.z * c;
-      O.w = O.w * a + o.w * c;
-    }
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;  // a row that sees no position: 0
-    uint16_t* out = L.out + qrow(L, b, hkv, oh) * D + oc;
-    out[0] = f2h(O.x * inv);
-    out[1] = f2h(O.y * inv);
-    out[2] = f2h(O.z * inv);
-    out[3] = f2h(O.w * inv);
-  }
-  if (lane == 0)
-    __hip_atomic_store(L.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Fused combine: outputs of the sequences no wave works on (length 0: zeros;
-// a length outside [0, max_seq_len] or above capacity: NaN), sequences
-// b = w, w + nw, ...
-template <int D, int GQ>
-__device__ __forceinline__ void empty_outputs(const DecodeLaunch& L, int w, int nw, int lane) {
-  for (int b = w; b < L.g.B; b += nw) {
-    const int n = L.seq_lens[b];
-    if (seq_work_of(L, n).w > 0) continue;
-    const uint16_t v = n == 0 ? 0 : 0x7e00;
-    for (int hkv = 0; hkv < L.g.Hkv; ++hkv)
-      for (int i = lane; i < GQ * D; i += 64) L.out[qrow(L, b, hkv, i / D) * D + i % D] = v;
-  }
-}
-
 // One wave per workgroup; grid = the number of worker waves.
 template <int D, int BK, int BV, int GQ, int NG, bool PG>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
@@ -935,7 +869,6 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
   if (spec && bw.uniform) {  // confirmed: the speculative first segment stands
     seg_run<D, BK, BV, GQ, NG, PG>(L, b_s, hkv_s, ss, r_s, w + b_s * L.g.Hkv + hkv_s, smem, lane,
                                ws, ra_s);
-    if (L.counters) unit_finish<D, GQ>(L, b_s, hkv_s, xu_s, ss.w, cpw, lane);
     x = xu_s + ss.w;
   }
   while (x < x1) {
@@ -948,10 +881,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
     const int xu = base + hkv * sw.w;
     unit_segment<D, BK, BV, GQ, NG, PG>(L, b, hkv, sw, xu, x0, x1, w + b * L.g.Hkv + hkv, smem,
                                     lane);
-    if (L.counters) unit_finish<D, GQ>(L, b, hkv, xu, sw.w, cpw, lane);
     x = xu + sw.w;
   }
-  if (L.counters) empty_outputs<D, GQ>(L, w, nw, lane);
 }
 
 // Worker waves the partial kernel of this instantiation is launched with:

@@ -109,7 +109,6 @@ struct DecodeLaunch {
   float scale_log2;   // sm_scale * log2(e)
   float* ws;          // partials [n_workers + B*Hkv][gq][D + 4]
   uint16_t* out;      // [B][T][Hq][D]
-  uint32_t* counters; // [B*Hkv] partials written per unit (fused combine), or nullptr
 };
 // Worker waves of the partial kernel for gq rows per KV head on the current
 // device (dense or paged as g.table says).

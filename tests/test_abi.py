@@ -50,7 +50,7 @@ def test_exports_every_declared_bq2_symbol():
 def test_exports_every_declared_paged_symbol():
     L = kvq.lib()
     names = _declared(HEADER_PAGED)
-    assert len(names) == 11
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTS_PAGED) == names
