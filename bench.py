@@ -254,9 +254,12 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
     timed = slice(a.warmup, a.warmup + a.steps)
     gbs = float(np.sum(step_bytes[timed])) / elapsed / 1e9
     gbs_eager = float(np.sum(step_bytes[timed])) / elapsed_eager / 1e9
-    part_avg_s = float(np.mean([ev_a[i].elapsed_time(ev_b[i]) for i in range(a.steps)])) / 1e3
+    part_ms = np.array([ev_a[i].elapsed_time(ev_b[i]) for i in range(a.steps)])
+    part_avg_s = float(np.mean(part_ms)) / 1e3
+    part_pct = {f"p{q}_us": round(float(np.percentile(part_ms, q)) * 1e3, 3) for q in (10, 50, 90)}
     dec_avg_bytes = float(np.mean(dec_bytes[timed]))
     achieved = dec_avg_bytes / part_avg_s / 1e9
+    ceiling = kvq.stream_read_gbs()
     return {
         "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak) + tokens/s",
         "value": round(gbs, 2),
@@ -298,8 +301,12 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": load_traffic(w.name, "bq2_partial"),
             "avg_launch_us": round(part_avg_s * 1e6, 3),
+            **part_pct,
             "algorithmic_bytes_per_launch": round(dec_avg_bytes),
+            "frac_of_stream_read": round(achieved / ceiling["gbs"], 4),
         },
+        "stream_read": {**ceiling, "kernel": "kvq_probe_stream_read (plain 16-byte loads, "
+                                              "2 GiB buffer beyond the Infinity Cache)"},
         "gpu": torch.cuda.get_device_name(0),
     }
 
@@ -473,6 +480,8 @@ def main():
     total_bytes = float(np.sum(step_bytes[timed]))
     part_ms = np.array([ev_a[i].elapsed_time(ev_b[i]) for i in range(a.steps)])
     part_avg_s = float(np.mean(part_ms)) / 1e3
+    part_pct = {f"p{q}_us": round(float(np.percentile(part_ms, q)) * 1e3, 3) for q in (10, 50, 90)}
+    ceiling = kvq.stream_read_gbs()
     dec_avg_bytes = float(np.mean(dec_bytes[timed]))
     achieved = dec_avg_bytes / part_avg_s / 1e9
     gbs = total_bytes / elapsed / 1e9
@@ -525,8 +534,12 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(part_avg_s * 1e6, 3),
+            **part_pct,
             "algorithmic_bytes_per_launch": round(dec_avg_bytes),
+            "frac_of_stream_read": round(achieved / ceiling["gbs"], 4),
         },
+        "stream_read": {**ceiling, "kernel": "kvq_probe_stream_read (plain 16-byte loads, "
+                                              "2 GiB buffer beyond the Infinity Cache)"},
         "gpu": torch.cuda.get_device_name(0),
     }
     if not a.no_cpu_baseline:

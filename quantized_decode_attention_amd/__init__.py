@@ -26,3 +26,4 @@ from ._lib import (  # noqa: F401
     kvq_paged_decode_attn, kvq_paged_decode_attn_multi, kvq_paged_decode_combine,
     kvq_paged_decode_partial, kvq_paged_decode_workspace_bytes, kvq_paged_prefill,
     kvq_paged_validate)
+from ._lib import stream_read_gbs  # noqa: F401  (measurement aid)

@@ -14,6 +14,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +53,7 @@ EXPORTS_PAGED = [
     "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_decode_attn",
     "kvq_paged_decode_partial", "kvq_paged_decode_combine", "kvq_paged_decode_attn_multi",
 ]
+EXPORTS_PROBE = ["kvq_probe_stream_read", "kvq_probe_sink_words"]
 BQ2_HEAD_DIM = 64
 BQ2_SINKS = 4
 
@@ -108,6 +110,8 @@ def lib() -> ctypes.CDLL:
         f32 = ctypes.c_float
         CP = ctypes.POINTER(kvq_paged_cache)
         sig = {
+            "kvq_probe_stream_read": (ctypes.c_int, [P, sz, P, P]),
+            "kvq_probe_sink_words": (ctypes.c_int, [ctypes.POINTER(i32)]),
             "kvq_paged_validate": (ctypes.c_int, [G, CP]),
             "kvq_paged_cache_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
             "kvq_paged_decode_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
@@ -565,6 +569,33 @@ def kvq_paged_decode_combine(g: Geom, q: torch.Tensor, cache: PagedCache,
                              stream=None) -> None:
     _paged_call("kvq_paged_decode_combine", g, q, cache, seq_lens, max_seq_len, sm_scale,
                 workspace, out, stream)
+
+
+def stream_read_gbs(nbytes: int = 2 << 30, reps: int = 20, device="cuda") -> dict:
+    """HBM read rate of kvq_probe_stream_read over a buffer of nbytes (well
+    beyond the 256 MB Infinity Cache), HIP events around each of reps reads
+    (a measurement aid: the practical ceiling of a read-only stream)."""
+    words = ctypes.c_int32()
+    _check(lib().kvq_probe_sink_words(ctypes.byref(words)), "kvq_probe_sink_words")
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    sink = torch.zeros(words.value, dtype=torch.int32, device=device)
+    st = torch.cuda.current_stream()
+    times = []
+    for r in range(reps + 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        _check(lib().kvq_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                           ctypes.c_void_p(sink.data_ptr()),
+                                           ctypes.c_void_p(st.cuda_stream)),
+               "kvq_probe_stream_read")
+        b.record(st)
+        b.synchronize()
+        if r >= 2:
+            times.append(a.elapsed_time(b) / 1e3)
+    del buf
+    t = float(np.median(times))
+    return {"gbs": round(nbytes / t / 1e9, 1), "bytes": nbytes, "reps": reps,
+            "median_us": round(t * 1e6, 2)}
 
 
 def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:

@@ -863,4 +863,26 @@ int kvq_paged_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_pag
                                      workspace, workspace_bytes, out, stream);
 }
 
+// ---- measurement aid (kvq_probe.h) ----------------------------------------
+
+int kvq_probe_sink_words(int32_t* words) {
+  if (!words) return fail(KVQ_ERR_NULL, "words is NULL");
+  *words = kvq::probe_sink_words();
+  return KVQ_OK;
+}
+
+int kvq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  try {
+    int st = check_ptr(buf, "buf");
+    if (st != KVQ_OK) return st;
+    if ((st = check_ptr(sink, "sink")) != KVQ_OK) return st;
+    if (bytes == 0 || bytes % 16 != 0)
+      return fail(KVQ_ERR_RANGE, "bytes (%zu) must be a positive multiple of 16", bytes);
+    hipError_t e = kvq::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "stream read launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 }  // extern "C"

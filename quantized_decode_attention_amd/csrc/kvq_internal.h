@@ -9,6 +9,7 @@
 #include "../../include/kvq.h"
 #include "../../include/kvq_bq2.h"
 #include "../../include/kvq_paged.h"
+#include "../../include/kvq_probe.h"
 
 namespace kvq {
 
@@ -160,5 +161,9 @@ struct Bq2Launch {
 hipError_t bq2_decode_workers(const Bq2Geom& g, int cus, int* workers);
 hipError_t launch_bq2_decode_partial(const Bq2Launch& L, hipStream_t st);
 hipError_t launch_bq2_decode_combine(const Bq2Launch& L, hipStream_t st);
+
+// ---- measurement aid (kvq_probe.h) ----------------------------------------
+int probe_sink_words();
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 
 }  // namespace kvq

@@ -19,6 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
 HEADER_BQ2 = os.path.join(ROOT, "include", "kvq_bq2.h")
 HEADER_PAGED = os.path.join(ROOT, "include", "kvq_paged.h")
+HEADER_PROBE = os.path.join(ROOT, "include", "kvq_probe.h")
 GOOD = dict(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128, k_bits=2, v_bits=4,
             group=32, residual=128, capacity=1024)
 
@@ -54,6 +55,20 @@ def test_exports_every_declared_paged_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTS_PAGED) == names
+
+
+def test_exports_every_declared_probe_symbol():
+    L = kvq.lib()
+    names = _declared(HEADER_PROBE)
+    assert sorted(_lib.EXPORTS_PROBE) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_include_headers_are_all_checked():
+    """Every public header's declarations are covered by an export test."""
+    hdrs = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert hdrs == ["kvq.h", "kvq_bq2.h", "kvq_paged.h", "kvq_probe.h"]
 
 
 @pytest.mark.parametrize("page_size,max_pages,num_pages,ok", [
