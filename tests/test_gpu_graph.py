@@ -85,3 +85,62 @@ def test_graph_replays_equal_eager(paged):
         torch.cuda.synchronize()
         for s in range(steps):
             assert torch.equal(outs[s].view(torch.int16), ref[s].view(torch.int16)), (rep, s)
+
+
+def test_graph_replays_equal_eager_bq2():
+    """The rotated 2-bit format's append + decode, captured and replayed."""
+    B, Hq, Hkv, C = 4, 32, 8, 4096
+    g = kvq.Bq2Geom(B, Hq, Hkv, C)
+    rng = np.random.default_rng(42)
+    n0 = np.array([1000, 3, 2047, 3000], np.int32)
+    steps = 5
+    k = rng.standard_normal((B, Hkv, int(n0.max()) + steps, 64)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, int(n0.max()) + steps, 64)).astype(np.float16)
+    qs = [dev(rng.standard_normal((B, Hq, 64)).astype(np.float16)) for _ in range(steps)]
+    kn = [dev(np.ascontiguousarray(k[np.arange(B), :, n0 + s])) for s in range(steps)]
+    vn = [dev(np.ascontiguousarray(v[np.arange(B), :, n0 + s])) for s in range(steps)]
+    before = [dev(n0 + s) for s in range(steps)]
+    after = [dev(n0 + s + 1) for s in range(steps)]
+    msl = int(n0.max()) + steps
+    _say("graph replay bq2")
+
+    def fresh():
+        c = kvq.Bq2Cache(g)
+        for b in range(B):
+            n = int(n0[b])
+            gb = kvq.Bq2Geom(1, Hq, Hkv, C)
+            sub = kvq.Bq2Cache.__new__(kvq.Bq2Cache)
+            for name, t in zip(("k_codes", "v_codes", "k_meta", "v_meta", "k_sink", "v_sink"),
+                               c.tensors()):
+                setattr(sub, name, t[b:b + 1])
+            kvq.kvq_bq2_prefill(gb, dev(k[b:b + 1, :, :n]), dev(v[b:b + 1, :, :n]), n, sub)
+        ws = kvq.alloc_bq2_workspace(g, msl)
+        outs = [torch.empty((B, Hq, 64), dtype=torch.float16, device="cuda") for _ in range(steps)]
+        return c, ws, outs
+
+    def run_steps(c, ws, outs):
+        st = torch.cuda.current_stream()
+        for s in range(steps):
+            kvq.kvq_bq2_append(g, kn[s], vn[s], before[s], c, st)
+            kvq.kvq_bq2_decode_attn(g, qs[s], c, after[s], msl, 0.125, ws, outs[s], st)
+
+    c, ws, outs = fresh()
+    run_steps(c, ws, outs)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    c, ws, outs = fresh()
+    snapshot = [t.clone() for t in c.tensors()]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_steps(c, ws, outs)
+    for rep in range(3):
+        for t, s0 in zip(c.tensors(), snapshot):
+            t.copy_(s0)
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs[s].view(torch.int16), ref[s].view(torch.int16)), (rep, s)
