@@ -65,6 +65,28 @@ def test_exports_every_declared_probe_symbol():
         assert hasattr(L, n), n
 
 
+def test_headers_compile_as_plain_c(tmp_path):
+    """The public headers are C (no C++ in the boundary): a C99 translation
+    unit that includes all of them and takes every entry point's address
+    compiles with gcc -Wall -Werror."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    names = sorted(set(_declared(HEADER) + _declared(HEADER_BQ2) + _declared(HEADER_PAGED) +
+                       _declared(HEADER_PROBE)))
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include "kvq.h"\n#include "kvq_paged.h"\n#include "kvq_bq2.h"\n'
+        '#include "kvq_probe.h"\n'
+        "void *entry_points[] = {\n" + ",\n".join(f"  (void *)&{n}" for n in names) + "\n};\n")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-Wno-pedantic", "-I", os.path.join(ROOT, "include"), "-c", str(src),
+                        "-o", str(tmp_path / "abi.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_include_headers_are_all_checked():
     """Every public header's declarations are covered by an export test."""
     hdrs = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
