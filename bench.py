@@ -524,6 +524,9 @@ def main():
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch * T * a.steps / elapsed, 1),
         "tokens_per_s_unit": "decoded tokens per second through one layer",
+        **({"stack_tokens_per_s": round(w.batch * T * a.steps / L / elapsed, 1),
+            "stack_tokens_per_s_unit": f"decoded tokens per second through all {L} layers"}
+           if w.layers > 1 else {}),
         "roofline": {
             "kernel": ("decode_partial" if T == 1 else
                        "decode_partial+decode_combine (multi)") + (" (paged)" if P else ""),
