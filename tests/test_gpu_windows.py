@@ -148,3 +148,36 @@ def test_equal_windows_set_explicitly_are_the_single_window():
         out, _ = decode_both(g, og, cache, oc, q, lens)
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("Rk,Rv", [(32, 128), (128, 32)])
+def test_windows_paged_multi_token_8bit(Rk, Rv):
+    """The new parts together: 8-bit keys, separate windows, the paged cache in
+    shuffled 32-position pages and T = 4 (causal mask across packed, mixed and
+    window chunks)."""
+    B, Hq, Hkv, D, bK, bV, G, C, P, T = 3, 8, 2, 128, 8, 4, 32, 1024, 32, 4
+    lens = [700, 131, 290]
+    g, og = geoms(B, Hq, Hkv, D, bK, bV, G, Rk, C, Rv)
+    rng = np.random.default_rng(Rk + 3 * Rv + 1)
+    k, v, q = _inputs(rng, B, Hkv, D, max(lens), Hq, T)
+    need = [-(-max(oracle.packed_len(n, Rk), oracle.packed_len(n, Rv)) // P) for n in lens]
+    npages = sum(need) + 4
+    perm = rng.permutation(npages).astype(np.int32)
+    table = np.full((B, C // P), -1, np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[o:o + need[b]]
+        o += need[b]
+    _say(f"windows paged multi 8-bit Rk={Rk} Rv={Rv} pages {need}")
+    pc = kvq.PagedCache(g, P, npages, dev(table))
+    for b, n in enumerate(lens):
+        sub = pc.view(b, b + 1)
+        kvq.kvq_paged_prefill(sub.g, dev(k[b:b + 1, :, :n]), dev(v[b:b + 1, :, :n]), n, sub)
+    _, oc = prefill_both(g, og, k, v, lens)
+    out = torch.empty((B, T, Hq, D), dtype=torch.float16, device="cuda")
+    ws = kvq.alloc_paged_workspace(g, T, max(lens))
+    kvq.kvq_paged_decode_attn_multi(g, dev(q), pc, dev(np.asarray(lens, np.int32)), T,
+                                    max(lens), 0.125, ws, out)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attn_multi(og, oc, q, np.asarray(lens, np.int32), T, 0.125)
+    assert_close(out, ref, what="paged multi 8-bit windows")
