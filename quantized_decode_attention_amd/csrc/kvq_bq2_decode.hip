@@ -587,12 +587,12 @@ __global__ __launch_bounds__(64) void bq2_partial_kernel(Bq2Launch L) {
 
 template <int GQ>
 hipError_t workers_of(int cus, int* out) {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // 0: not queried yet (host threads may race here)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
+  if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) > 0) {
+    *out = cache[dev].load(std::memory_order_relaxed);
     return hipSuccess;
   }
   int nb = 0;
@@ -600,7 +600,7 @@ hipError_t workers_of(int cus, int* out) {
   if (e != hipSuccess) return e;
   if (nb < 1) nb = 1;
   const int w = nb * cus;
-  if (dev >= 0 && dev < 64) cache[dev] = w;
+  if (dev >= 0 && dev < 64) cache[dev].store(w, std::memory_order_relaxed);
   *out = w;
   return hipSuccess;
 }

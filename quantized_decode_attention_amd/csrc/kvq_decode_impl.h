@@ -890,12 +890,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
 // per device.
 template <int D, int BK, int BV, int GQ, int NG, bool PG>
 hipError_t workers_of(int cus, int* out) {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // 0: not queried yet (host threads may race here)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
+  if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) > 0) {
+    *out = cache[dev].load(std::memory_order_relaxed);
     return hipSuccess;
   }
   int nb = 0;
@@ -904,7 +904,7 @@ hipError_t workers_of(int cus, int* out) {
   if (e != hipSuccess) return e;
   if (nb < 1) nb = 1;
   const int w = nb * cus;
-  if (dev >= 0 && dev < 64) cache[dev] = w;
+  if (dev >= 0 && dev < 64) cache[dev].store(w, std::memory_order_relaxed);
   *out = w;
   return hipSuccess;
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kvq.h"
 #include "../../include/kvq_bq2.h"
 #include "../../include/kvq_paged.h"
