@@ -56,3 +56,27 @@ def test_decode_step_bytes_closed_form():
     assert metrics.packed_len(1, 128) == 0
     assert metrics.packed_len(128, 128) == 0
     assert metrics.packed_len(129, 128) == 128
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N with N != 1 prints one JSON line
+    naming the reason and exits with status 2 (before touching any device)."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"]
+
+
+def test_decode_step_bytes_of_the_benchmarked_workload():
+    """Config 3 (B32, 32/8, D128, K2/V4, G32, R128) at n = 8192: per KV head
+    8064 packed tokens of 32 + 64 + 16 + 16 bytes and 128 fp16 tokens of 512
+    bytes, plus q in and out (4 bytes per query value) and the lengths."""
+    n = [8192] * 32
+    got = metrics.decode_step_bytes(n, 32, 8, 128, 2, 4, 32, 128)
+    per_head = 8064 * (32 + 64 + 16 + 16) + 128 * 512
+    assert got == 32 * 8 * per_head + 4 * 32 * 32 * 128 + 4 * 32
