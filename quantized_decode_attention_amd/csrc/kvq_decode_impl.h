@@ -59,9 +59,22 @@ struct Cfg {
   static constexpr int IPH = 4 * KC;              // fold items per head
   static constexpr int ITEMS = GQ * IPH;          // fold items per key group
   static constexpr int IPL = (ITEMS + 63) / 64;   // fold items per lane
-  // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ]
+  // a lane's fold items are lane + 64 i: with IPH dividing 64 they all cover
+  // the same channels (item modulo IPH), so one key-meta load serves them all
+  static_assert(64 % IPH == 0, "fold items of a lane must share their channels");
+  // With two or more value-side fragments (8 or 16 rows per KV head) each lane
+  // group would hold every group's (scale, min) of its 8 tokens in registers,
+  // 16 lanes alike.  Instead each lane loads NG / 2 distinct words of the
+  // chunk's value meta and stages them in LDS; a fragment reads its 8 words
+  // back when its weights are formed.
+  static constexpr bool VL = NF >= 2;
+  static constexpr int VLW = VL ? NG / 2 : 1;  // staged value-meta words per lane
+  // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ] (+ a
+  // spare), the staged value meta [4][NG][8] words
   static constexpr int kQB = 2 * GQ * 4 * KC * 16;
-  static constexpr int kWaveLds = kQB + 16 * ((GQ * 4 + 4 + 15) / 16);  // + spare beta
+  static constexpr int kBetaB = 16 * ((GQ * 4 + 4 + 15) / 16);
+  static constexpr int kVmB = VL ? 4 * NG * 8 * 4 : 0;
+  static constexpr int kWaveLds = kQB + kBetaB + kVmB;
   static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
 };
 
@@ -71,8 +84,10 @@ struct Raw {
   using C = Cfg<D, BK, BV, GQ, NG>;
   uint32_t kw[2][C::KW];              // key code words of score tiles 0, 1
   uint32_t vw[C::NW];                 // value code words (tile n: word n*BV/4)
-  uint32_t vmA[C::NF][4], vmB[C::NF][4];  // value (scale, min) of the B elements
-  uint4 kmA[C::IPL], kmB[C::IPL];     // key (scale, min) of the chunk's group
+  uint32_t vmA[C::VL ? 1 : C::NF][4], vmB[C::VL ? 1 : C::NF][4];  // value (scale, min)
+                                      // of the B elements (direct)
+  uint32_t vml[C::VLW];               // or this lane's share of them (staged)
+  uint4 kmA, kmB;                     // key (scale, min) of the chunk's group
 };
 
 template <int D, int BK, int BV, int GQ, int NG, bool PG>
@@ -95,15 +110,17 @@ struct PackedWave {
   const float* qfs;
   uint4* qB;
   float* beta_l;
+  uint32_t* vm_l;  // staged value meta (8 or 16 rows per KV head)
   // lane constants
   int lane, col, lg, hcol, slot;
   int kofs, vofs;      // this lane's key / value words inside a chunk
   int vmofs[NF];       // value meta run of fragment f inside a chunk
-  int kmofs[IPL];      // key meta run of fold item i inside a group
-  int kmoff[IPL][2];   // channels of fold item i (runs A and B)
+  int kmofs;           // key meta run of this lane's fold items inside a group
+  int kmoff[2];        // channels of those items (runs A and B)
   int fitem[IPL];
   float kscale, bscale;
   float m1;  // -1 in a register (split2)
+  uint32_t m_slot1, m_slot2;  // all ones where bit 0 / bit 1 of slot is set
   // state
   f4 oacc[NT];
   float m_run, l_run;
@@ -128,18 +145,19 @@ struct PackedWave {
     lg = lane >> 4;
     hcol = col / SL;
     slot = col % SL;
+    m_slot1 = 0u - (uint32_t)(slot & 1);
+    m_slot2 = 0u - (uint32_t)((slot >> 1) & 1);
     kofs = lane * 2 * KW;
     vofs = lane * C::NW;
 #pragma unroll
     for (int f = 0; f < NF; ++f) vmofs[f] = (lg * NG + (f * SL + slot) % NG) * 8;
 #pragma unroll
-    for (int i = 0; i < IPL; ++i) {
-      const int it = lane + 64 * i;
-      fitem[i] = it;
-      const int r = it % IPH, gg = r / KC, kc = r % KC;
-      kmofs[i] = r * 8;
-      kmoff[i][0] = key_run0<D, BK>(gg, kc);
-      kmoff[i][1] = kmoff[i][0] + kKeyOff<BK>;
+    for (int i = 0; i < IPL; ++i) fitem[i] = lane + 64 * i;
+    {
+      const int r = lane % IPH, gg = r / KC, kc = r % KC;
+      kmofs = r * 8;
+      kmoff[0] = key_run0<D, BK>(gg, kc);
+      kmoff[1] = kmoff[0] + kKeyOff<BK>;
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) oacc[n] = f4{0.f, 0.f, 0.f, 0.f};
@@ -207,14 +225,21 @@ struct PackedWave {
     // value (scale, min) of tokens 8 lg + j: even j feed B elements 2i (run
     // A), odd j elements 2i + 1 (run B)
     const uint32_t* vm = vmeta + sl * (4 * NG * 8);
+    if constexpr (C::VL) {
+      if constexpr (C::VLW == 1)
+        r.vml[0] = vm[lane];
+      else
+        load_run<C::VLW>(vm + lane * C::VLW, r.vml);
+    } else {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      uint32_t w[8];
-      load_run<8>(vm + vmofs[f], w);
+      for (int f = 0; f < NF; ++f) {
+        uint32_t w[8];
+        load_run<8>(vm + vmofs[f], w);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r.vmA[f][i] = w[2 * i];
-        r.vmB[f][i] = w[2 * i + 1];
+        for (int i = 0; i < 4; ++i) {
+          r.vmA[f][i] = w[2 * i];
+          r.vmB[f][i] = w[2 * i + 1];
+        }
       }
     }
     // key meta of the chunk's group, with the chunk's other loads (one
@@ -223,12 +248,25 @@ struct PackedWave {
     // Lanes past the fold items load an in-range run too (the run depends on
     // the item modulo a head's items): no load sits under a branch.
     const uint32_t* km = kmeta + (sl * kChunk) / G * D;
-#pragma unroll
-    for (int i = 0; i < IPL; ++i) {
+    {
       uint32_t w[8];
-      load_run<8>(km + kmofs[i], w);
-      r.kmA[i] = make_uint4(w[0], w[2], w[4], w[6]);
-      r.kmB[i] = make_uint4(w[1], w[3], w[5], w[7]);
+      load_run<8>(km + kmofs, w);
+      r.kmA = make_uint4(w[0], w[2], w[4], w[6]);
+      r.kmB = make_uint4(w[1], w[3], w[5], w[7]);
+    }
+  }
+
+  // Staged value meta: this lane's words of the chunk to LDS (before the
+  // scores, so that the write is long done when packed_values reads them).
+  __device__ __forceinline__ void stage_vmeta(const R& r) {
+    if constexpr (C::VL) {
+      if constexpr (C::VLW == 1)
+        vm_l[lane] = r.vml[0];
+      else
+        *reinterpret_cast<uint2*>(vm_l + 2 * lane) = make_uint2(r.vml[0], r.vml[1]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 
@@ -242,11 +280,11 @@ struct PackedWave {
       // (when the items fill the wave exactly the test is compile-time true)
       if (C::ITEMS % 64 == 0 || it < C::ITEMS) {
         const int h = it / IPH, rr = it % IPH, gg = rr / KC, kc = rr % KC;
-        const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][0]);
-        const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[i][1]);
+        const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[0]);
+        const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[1]);
         const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qBv[4] = {qb.x, qb.y, qb.z, qb.w};
-        const uint32_t mA[4] = {r.kmA[i].x, r.kmA[i].y, r.kmA[i].z, r.kmA[i].w};
-        const uint32_t mB[4] = {r.kmB[i].x, r.kmB[i].y, r.kmB[i].z, r.kmB[i].w};
+        const uint32_t mA[4] = {r.kmA.x, r.kmA.y, r.kmA.z, r.kmA.w};
+        const uint32_t mB[4] = {r.kmB.x, r.kmB.y, r.kmB.z, r.kmB.w};
         uint32_t hp[4], lp[4];
         float bodd = 0.0f;  // odd channels (their q' carries kKeyOddQ)
 #pragma unroll
@@ -288,48 +326,136 @@ struct PackedWave {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // Online softmax over a chunk's scores (exact running max; rescale only
-  // when it grows).  Each lane tests its own 8 scores; the cross-lane maximum
-  // is only formed on the (rare) path where some lane sees a larger score.
-  // kPacked: weights carry the value classes' factors (q < 2: kValEven,
-  // q >= 2: kValOdd) and their sums are kept per class; otherwise plain.
-  template <bool kPacked>
-  __device__ __forceinline__ void softmax(const float (&s)[2][4], float (&p)[2][4]) {
-    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    if (__any(cm > m_run)) {
-      cm = xor_max(cm, 16);
-      cm = xor_max(cm, 32);
-      const float m_new = fmaxf(m_run, cm);
-      const float a = exp2_hw(m_run - m_new);
-      m_run = m_new;
-      m_even = m_new - kValEvenLog2<BV>;
-      m_odd = m_new - kValOddLog2<BV>;
-      l_run *= a;
-      l_odd *= a;
+  // Scores.  A lane of column col and lane group lg holds, in the two score
+  // tiles' accumulators, rows 4 lg + q of tile u: position j = 4 u + q of its
+  // 8 positions 8 lg + j of the chunk.  With two or more columns per head
+  // (kColSplit) the hi and lo parts of q' sit in neighbouring columns and are
+  // added across the lane pair.
+  //
+  // With 2 or 4 columns per head (kShare) the lanes of a head, which sit in
+  // one quad, would all hold the same 8 scores.  Each takes NS = 8 / SL of
+  // them instead (positions NS * slot + k) for the maximum, the exponentials
+  // and the sums, and the weights of all 8 are gathered back from the quad
+  // with DPP moves.  The running sums are then per lane and summed over the
+  // quad at the end.
+  static constexpr bool kShare = SL == 2 || SL == 4;
+  static constexpr int NS = kShare ? 8 / SL : 8;  // scores a lane works on
+
+  // a where mask bits are set, else b (v_bfi_b32; a select between two
+  // elements of one array could otherwise become an indexed private array)
+  static __device__ __forceinline__ float bit_sel(uint32_t mask, float a, float b) {
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    return __builtin_bit_cast(float, ub ^ ((ua ^ ub) & mask));
+  }
+  static __device__ __forceinline__ float pair_add(float x) { return x + dpp<0xB1>(x); }
+
+  // offset (in the lane group's 8 positions) of this lane's score k
+  __device__ __forceinline__ int pos_of(int k) const { return kShare ? NS * slot + k : k; }
+
+  // This lane's raw dot products (hi + lo) from the score tiles.
+  __device__ __forceinline__ void lane_scores(const f4 (&acc)[2], float (&x)[NS]) const {
+    if constexpr (SL == 4) {
+      // the lane pair (slot 0, 1 or 2, 3) shares tile slot / 2: add hi + lo
+      // on it, then each lane keeps rows 2 (slot % 2) + k
+      float f[4];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) oacc[n] *= a;
+      for (int q = 0; q < 4; ++q) f[q] = pair_add(bit_sel(m_slot2, acc[1][q], acc[0][q]));
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        bias[f] *= a;
-        bias_odd[f] *= a;
-      }
+      for (int k = 0; k < 2; ++k) x[k] = bit_sel(m_slot1, f[2 + k], f[k]);
+    } else if constexpr (SL == 2) {  // lane slot keeps tile slot
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = bit_sel(m_slot1, pair_add(acc[1][q]), pair_add(acc[0][q]));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[4 * u + q] = kColSplit ? pair_add(acc[u][q]) : acc[u][q];
     }
+  }
+
+  // Online softmax over a chunk's scores (exact running max; rescale only
+  // when it grows).  Each lane tests its own scores; the cross-lane maximum
+  // is only formed on the (rare) path where some lane sees a larger score.
+  // kPacked: weights carry the value classes' factors (rows q < 2: kValEven,
+  // q >= 2: kValOdd) and their sums are kept per class; otherwise plain.
+  // p receives the weights of all 8 positions.
+  __device__ __forceinline__ void rescale(float cm) {
+    if constexpr (kShare) {
+      cm = xor_max(cm, 1);
+      if constexpr (SL == 4) cm = xor_max(cm, 2);
+    }
+    cm = xor_max(cm, 16);
+    cm = xor_max(cm, 32);
+    const float m_new = fmaxf(m_run, cm);
+    const float a = exp2_hw(m_run - m_new);
+    m_run = m_new;
+    m_even = m_new - kValEvenLog2<BV>;
+    m_odd = m_new - kValOddLog2<BV>;
+    l_run *= a;
+    l_odd *= a;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int n = 0; n < NT; ++n) oacc[n] *= a;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (kPacked) {
-          p[u][q] = exp2_hw(s[u][q] - (q < 2 ? m_even : m_odd));
-          if (q < 2)
-            l_run += p[u][q];
+    for (int f = 0; f < NF; ++f) {
+      bias[f] *= a;
+      bias_odd[f] *= a;
+    }
+  }
+
+  template <bool kPacked>
+  __device__ __forceinline__ void softmax(const float (&s)[NS], float (&p)[2][4]) {
+    float cm = s[0];
+#pragma unroll
+    for (int k = 1; k < NS; ++k) cm = fmaxf(cm, s[k]);
+    if (__any(cm > m_run)) rescale(cm);
+    float pm[NS];
+    if constexpr (kPacked && SL == 4) {  // a lane's two rows share a class
+      const bool odd = slot & 1;
+      const float mref = odd ? m_odd : m_even;
+      pm[0] = exp2_hw(s[0] - mref);
+      pm[1] = exp2_hw(s[1] - mref);
+      const float add = pm[0] + pm[1];
+      l_run += odd ? 0.0f : add;
+      l_odd += odd ? add : 0.0f;
+    } else {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        if constexpr (kPacked) {  // row (k % 4) < 2: even class
+          pm[k] = exp2_hw(s[k] - ((k & 3) < 2 ? m_even : m_odd));
+          if ((k & 3) < 2)
+            l_run += pm[k];
           else
-            l_odd += p[u][q];
+            l_odd += pm[k];
         } else {
-          p[u][q] = exp2_hw(s[u][q] - m_run);
-          l_run += p[u][q];
+          pm[k] = exp2_hw(s[k] - m_run);
+          l_run += pm[k];
         }
       }
+    }
+    if constexpr (SL == 4) {
+      // position j = 4 u + q from quad lane j / 2 (quad_perm control: the
+      // source of quad positions 0..3, 2 bits each)
+      p[0][0] = dpp<0x00>(pm[0]);
+      p[0][1] = dpp<0x00>(pm[1]);
+      p[0][2] = dpp<0x55>(pm[0]);
+      p[0][3] = dpp<0x55>(pm[1]);
+      p[1][0] = dpp<0xAA>(pm[0]);
+      p[1][1] = dpp<0xAA>(pm[1]);
+      p[1][2] = dpp<0xFF>(pm[0]);
+      p[1][3] = dpp<0xFF>(pm[1]);
+    } else if constexpr (SL == 2) {
+      // tile u from the head's lane of slot u: quad positions (0, 1) or (2, 3)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p[0][q] = dpp<0xA0>(pm[q]);
+        p[1][q] = dpp<0xF5>(pm[q]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[u][q] = pm[4 * u + q];
+    }
   }
 
   // Packed accumulation to real scale (codes were fp16 numbers c * 2^-24,
@@ -425,32 +551,30 @@ struct PackedWave {
   // Scores of positions t0 + [0, 32) from the key window (B fragments from
   // plain_query()); positions this lane's row must not see get -inf.
   __device__ __forceinline__ void window_scores(int t0, int n_tok, int Rk, const uint16_t* kres,
-                                                float (&s)[2][4]) {
+                                                float (&s)[NS]) {
     // scores: tile u row r = token key_row_token(u, r)
     const float kscale_r = bscale;  // keys are real fp16 values here
+    f4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tin = t0 + key_row_token(u, col);
       const int slot_in = (tin < n_tok ? tin : n_tok - 1) % Rk;
       const uint4* krow = reinterpret_cast<const uint4*>(kres + (int64_t)slot_in * D);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const uint4 kv = krow[4 * kc + lg];
         const uint32_t a[4] = {kv.x, kv.y, kv.z, kv.w};
-        acc = mfma(a, bq[0][kc], acc);
-        if constexpr (!kColSplit) acc = mfma(a, bq[1][kc], acc);
+        acc[u] = mfma(a, bq[0][kc], acc[u]);
+        if constexpr (!kColSplit) acc[u] = mfma(a, bq[1][kc], acc[u]);
       }
+    }
+    float x[NS];
+    lane_scores(acc, x);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float x = acc[q];
-        if constexpr (kColSplit) {
-          x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                   __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
-        }
-        const bool valid = t0 + 8 * lg + 4 * u + q < n_tok - hide;
-        s[u][q] = valid ? x * kscale_r : kNegInf;
-      }
+    for (int k = 0; k < NS; ++k) {
+      const bool valid = t0 + 8 * lg + pos_of(k) < n_tok - hide;
+      s[k] = valid ? x[k] * kscale_r : kNegInf;
     }
   }
 
@@ -461,7 +585,7 @@ struct PackedWave {
                                                    const uint16_t* vres) {
     uint4 va[NT];
     window_values_load(t0, Rv, vres, va);  // first: the loads overlap the score MFMAs
-    float s[2][4];
+    float s[NS];
     window_scores(t0, n_tok, Rk, kres, s);
     float p[2][4];
     softmax<false>(s, p);
@@ -475,7 +599,7 @@ struct PackedWave {
                                                      const uint16_t* vres) {
     uint4 va[NT];
     window_values_load(ch * kChunk, Rv, vres, va);
-    float s[2][4];
+    float s[NS];
     packed_scores<true>(ch, r, n_tok - 1 - hide, s);
     float p[2][4];
     softmax<false>(s, p);
@@ -487,7 +611,8 @@ struct PackedWave {
   // accumulators are still at code scale), values from the codes.
   __device__ __forceinline__ void process_mixed_values(int ch, const R& r, int n_tok, int Rk,
                                                        const uint16_t* kres) {
-    float s[2][4];
+    stage_vmeta(r);
+    float s[NS];
     window_scores(ch * kChunk, n_tok, Rk, kres, s);
     float p[2][4];
     softmax<true>(s, p);
@@ -499,7 +624,8 @@ struct PackedWave {
   // are real cache data, so their weight 0 is exact).
   template <bool kMask = false>
   __device__ __forceinline__ void process(int ch, const R& r, int last_vis = 0) {
-    float s[2][4];
+    stage_vmeta(r);
+    float s[NS];
     packed_scores<kMask>(ch, r, last_vis, s);
     float p[2][4];
     softmax<true>(s, p);
@@ -511,7 +637,7 @@ struct PackedWave {
   // get -inf.
   template <bool kMask>
   __device__ __forceinline__ void packed_scores(int ch, const R& r, int last_vis,
-                                                float (&s)[2][4]) {
+                                                float (&s)[NS]) {
     if constexpr (G == kChunk) {
       fold(r);  // every chunk is a key group: no branch, so the fold can be
                 // scheduled against the previous chunk's value products
@@ -522,28 +648,25 @@ struct PackedWave {
         fold(r);
       }
     }
+    f4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t a[KC][4];
       unpack_keys<D, BK>(r.kw[u], a);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        acc = mfma(a[kc], bq[0][kc], acc);
-        if constexpr (!kColSplit) acc = mfma(a[kc], bq[1][kc], acc);
+        acc[u] = mfma(a[kc], bq[0][kc], acc[u]);
+        if constexpr (!kColSplit) acc[u] = mfma(a[kc], bq[1][kc], acc[u]);
       }
+    }
+    float x[NS];
+    lane_scores(acc, x);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float x = acc[q];
-        if constexpr (kColSplit) {
-          // hi column + lo column (lanes col and col ^ 1 of a quad)
-          x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                   __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
-        }
-        s[u][q] = __builtin_fmaf(x, kscale, beta_c);
-        if constexpr (kMask)
-          s[u][q] = ch * kChunk + 8 * lg + 4 * u + q <= last_vis ? s[u][q] : kNegInf;
-      }
+    for (int k = 0; k < NS; ++k) {
+      s[k] = __builtin_fmaf(x[k], kscale, beta_c);
+      if constexpr (kMask)
+        s[k] = ch * kChunk + 8 * lg + pos_of(k) <= last_vis ? s[k] : kNegInf;
     }
   }
 
@@ -552,16 +675,29 @@ struct PackedWave {
   __device__ __forceinline__ void packed_values(const R& r, const float (&p)[2][4]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
+      uint32_t mA[4], mB[4];
+      if constexpr (C::VL) {
+        const uint4* st = reinterpret_cast<const uint4*>(vm_l + vmofs[f]);
+        const uint4 x = st[0], y = st[1];
+        mA[0] = x.x; mA[1] = x.z; mA[2] = y.x; mA[3] = y.z;
+        mB[0] = x.y; mB[1] = x.w; mB[2] = y.y; mB[3] = y.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mA[i] = r.vmA[f][i];
+          mB[i] = r.vmB[f][i];
+        }
+      }
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // elements 2i (run A) and 2i+1 (run B) = score tile i/2, rows 2(i%2), +1;
         // odd i is the odd class
         const float pa = p[i >> 1][2 * (i & 1)], pb = p[i >> 1][2 * (i & 1) + 1];
-        split2(mul_lo(pa, r.vmA[f][i]), mul_lo(pb, r.vmB[f][i]), m1, bh[i], bl[i]);
+        split2(mul_lo(pa, mA[i]), mul_lo(pb, mB[i]), m1, bh[i], bl[i]);
         float& bacc = (i & 1) ? bias_odd[f] : bias[f];
-        bacc = mul_hi(pa, r.vmA[f][i], bacc);
-        bacc = mul_hi(pb, r.vmB[f][i], bacc);
+        bacc = mul_hi(pa, mA[i], bacc);
+        bacc = mul_hi(pb, mB[i], bacc);
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -587,6 +723,11 @@ struct PackedWave {
         oacc[n] = mfma(a, bh, oacc[n]);
         oacc[n] = mfma(a, bl, oacc[n]);
       }
+    }
+    if constexpr (C::VL) {  // the next chunk restages after these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 };
@@ -661,6 +802,7 @@ __device__ __forceinline__ void seg_begin(const DecodeLaunch& L, int b, int hkv,
   w.qfs = reinterpret_cast<float*>(smem);
   w.qB = reinterpret_cast<uint4*>(wl);
   w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
+  w.vm_l = reinterpret_cast<uint32_t*>(wl + C::kQB + C::kBetaB);
   w.init(lane);
   if constexpr (PG) w.set_table(g, b, hkv, r.pc0 >> g.cpp_log2);
   if (r.pc0 < r.pc1) w.load(r.pc0, ra);
@@ -778,6 +920,10 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   // partial: O (value-min term included), max, sum of this wave's tokens
   if (!real) w.to_real();
   float l_run = w.l_run;
+  if constexpr (PackedWave<D, BK, BV, GQ, NG, PG>::kShare) {  // per-lane sums
+    l_run = xor_sum(l_run, 1);
+    if constexpr (SL == 4) l_run = xor_sum(l_run, 2);
+  }
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);
   if constexpr (PG) {
