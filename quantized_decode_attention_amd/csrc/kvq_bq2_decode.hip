@@ -70,8 +70,8 @@ struct Bq2Work {
 struct Bq2Raw {
   uint32_t kw[2];  // key code words of score tiles 0, 1
   uint32_t vw[2];  // value code words (tiles 2m, 2m + 1 in word m)
-  uint4 km[2];     // key (d, m) of positions 8 lg + 4u + q: km[u], component q
-  uint4 vm[2];     // value (d, m) of positions 8 lg + j: vm[j / 4], component j % 4
+  uint32_t km[2];  // key (d, m) of this lane's positions 8 lg + 2 i + k (i: quad position)
+  uint32_t vm[2];  // value (d, m) of the same positions
 };
 
 // A lane's share of a unit's sink vectors, fetched with the first chunk:
@@ -81,10 +81,6 @@ struct Bq2Sinks {
   uint4 k[2];  // channels 32 kc + 8 g .. + 7 of key row min(i, 3)
   uint2 v[4];  // positions 0..3 of channel 16 n + i
 };
-
-__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
 
 template <int GQ>
 struct Bq2Wave {
@@ -97,6 +93,7 @@ struct Bq2Wave {
   const uint32_t* vmeta;
   int lane, col, lg, hcol, part, kpart;
   bool vbig;     // this lane's value columns hold the large weights
+  uint32_t m_q1, m_q2;  // all ones where bit 0 / bit 1 of the lane's quad position is set
   float m1;      // -1 in a register
   float mpart;   // 0 on hi lanes, -1 on lo lanes: selects the part of a split
   float qbig;    // 2^(kQTop - kBigSpan): query components at or above go to key part 0
@@ -117,6 +114,8 @@ struct Bq2Wave {
     part = (col % SL) & 1;
     kpart = (col % SL) & 3;
     vbig = kpart < 2;
+    m_q1 = 0u - (uint32_t)(lane & 1);
+    m_q2 = 0u - (uint32_t)((lane >> 1) & 1);
     m1 = opaque_m1();
     qbig = ldexpf(1.0f, kQTop - kBigSpan);
     mpart = part ? m1 : 0.0f;
@@ -167,21 +166,27 @@ struct Bq2Wave {
     r.kw[1] = k2.y;
     r.vw[0] = v2.x;
     r.vw[1] = v2.y;
-    const uint4* km = reinterpret_cast<const uint4*>(kmeta + ch * kChunk + 8 * lg);
-    const uint4* vm = reinterpret_cast<const uint4*>(vmeta + ch * kChunk + 8 * lg);
-    r.km[0] = km[0];
-    r.km[1] = km[1];
-    r.vm[0] = vm[0];
-    r.vm[1] = vm[1];
+    const uint2 km = *reinterpret_cast<const uint2*>(kmeta + ch * kChunk + 8 * lg + 2 * (lane & 3));
+    const uint2 vm = *reinterpret_cast<const uint2*>(vmeta + ch * kChunk + 8 * lg + 2 * (lane & 3));
+    r.km[0] = km.x;
+    r.km[1] = km.y;
+    r.vm[0] = vm.x;
+    r.vm[1] = vm.y;
   }
 
   // Scores arrive as s / sc (sc > 0 per lane: a power of two), the running
-  // max is kept in log2 units; p = 2^(s - m) = 2^(fma(s/sc, sc, -m)).
+  // max is kept in log2 units; p = 2^(s - m) = 2^(fma(s/sc, sc, -m)).  The
+  // four lanes of a quad (one head's columns) hold the same 8 code products
+  // after the quad sum, so each works on positions 2 i, 2 i + 1 of the lane
+  // group (i its quad position; x: their scores, pm: their weights) for the
+  // maximum, the exponentials and the sums, which are per lane and summed
+  // over the quad at the end.  Callers gather the 8 weights from the quad.
   template <bool kPacked>
-  __device__ __forceinline__ void softmax(const float (&s)[2][4], float sc, float (&p)[2][4]) {
-    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * sc;
+  __device__ __forceinline__ void softmax(const float (&x)[2], float sc, float (&pm)[2]) {
+    float cm = fmaxf(x[0], x[1]) * sc;
     if (__any(cm > m_run)) {
+      cm = xor_max(cm, 1);
+      cm = xor_max(cm, 2);
       cm = xor_max(cm, 16);
       cm = xor_max(cm, 32);
       const float m_new = fmaxf(m_run, cm);
@@ -196,16 +201,18 @@ struct Bq2Wave {
 #pragma unroll
       for (int n = 0; n < 4; ++n) oacc[n] *= a;
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        p[u][q] = exp2_hw(__builtin_fmaf(s[u][q], sc, -(q < 2 ? m_even : m_odd)));
-        if (q < 2 || !kPacked)
-          l_run += p[u][q];
-        else
-          l_odd += p[u][q];
-      }
+    // the lane's two positions are rows 2 (i % 2) + k: one weight class
+    const bool odd = lane & 1;
+    const float mref = odd ? m_odd : m_even;
+    pm[0] = exp2_hw(__builtin_fmaf(x[0], sc, -mref));
+    pm[1] = exp2_hw(__builtin_fmaf(x[1], sc, -mref));
+    const float add = pm[0] + pm[1];
+    if constexpr (kPacked) {
+      l_run += odd ? 0.0f : add;
+      l_odd += odd ? add : 0.0f;
+    } else {
+      l_run += add;
+    }
   }
 
   // One chunk of quantized positions.  kEdge: chunk 0 (positions 0..3 are
@@ -215,15 +222,12 @@ struct Bq2Wave {
   __device__ __forceinline__ void process(int ch, Bq2Raw r, int n) {
     if constexpr (kEdge) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t0 = ch * kChunk + 8 * lg + 4 * u;
-        r.vm[u].x = (t0 + 0 >= kSinks && t0 + 0 < n) ? r.vm[u].x : 0u;
-        r.vm[u].y = (t0 + 1 >= kSinks && t0 + 1 < n) ? r.vm[u].y : 0u;
-        r.vm[u].z = (t0 + 2 >= kSinks && t0 + 2 < n) ? r.vm[u].z : 0u;
-        r.vm[u].w = (t0 + 3 >= kSinks && t0 + 3 < n) ? r.vm[u].w : 0u;
+      for (int k = 0; k < 2; ++k) {
+        const int t = ch * kChunk + 8 * lg + 2 * (lane & 3) + k;
+        r.vm[k] = (t >= kSinks && t < n) ? r.vm[k] : 0u;
       }
     }
-    float s[2][4];
+    float xs[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint32_t w[1] = {r.kw[u]};
@@ -233,24 +237,37 @@ struct Bq2Wave {
       acc = mfma(a[0], bq[0], acc);
       acc = mfma(a[1], bq[1], acc);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // s / kscale = d (qH . code) 2^-(E - kQTop + 24) + m sum qH / kscale
-        const float x = key_sum(acc[q]);
-        const uint32_t dm = comp(r.km[u], q);
-        s[u][q] = mul_lo(x, dm, mul_hi(sumq_k, dm));
+      for (int q = 0; q < 4; ++q) xs[u][q] = key_sum(acc[q]);
+    }
+    // this lane's positions 8 lg + 2 i + k:
+    // s / kscale = d (qH . code) 2^-(E - kQTop + 24) + m sum qH / kscale
+    float s[2];
+    quad_pick2(m_q1, m_q2, xs, s);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      s[k] = mul_lo(s[k], r.km[k], mul_hi(sumq_k, r.km[k]));
+      if constexpr (kEdge) {
+        const int t = ch * kChunk + 8 * lg + 2 * (lane & 3) + k;
+        s[k] = (t >= kSinks && t < n) ? s[k] : kNegInf;
       }
     }
-    if constexpr (kEdge) {
+    float pm[2];
+    softmax<true>(s, kscale, pm);
+    // this lane's positions: weighted value scales p dV and the value-min term
+    // (per lane, in the positions' class: odd quad positions are the odd class)
+    float ym[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = ch * kChunk + 8 * lg + 4 * u + q;
-          s[u][q] = (t >= kSinks && t < n) ? s[u][q] : kNegInf;
-        }
+    for (int k = 0; k < 2; ++k) ym[k] = mul_lo(pm[k], r.vm[k]);
+    {
+      const float bm = mul_hi(pm[1], r.vm[1], mul_hi(pm[0], r.vm[0]));
+      const bool odd = lane & 1;
+      bias += odd ? 0.0f : bm;
+      bias_odd += odd ? bm : 0.0f;
     }
-    float p[2][4];
-    softmax<true>(s, kscale, p);
+    // all 8 positions of the lane group back from the quad
+    float p[2][4], y[2][4];
+    quad_gather2(pm, p);
+    quad_gather2(ym, y);
     // B operand: element j = position 8 lg + j, weight p_j dV_j; pair e holds
     // j = 2e, 2e + 1 (odd e: the odd weight class)
     uint32_t b[4];
@@ -258,13 +275,9 @@ struct Bq2Wave {
     for (int e = 0; e < 4; ++e) {
       const int ja = 2 * e, jb = 2 * e + 1;
       const float pa = p[ja >> 2][ja & 3], pb = p[jb >> 2][jb & 3];
-      const uint32_t wa = comp(r.vm[ja >> 2], ja & 3), wb = comp(r.vm[jb >> 2], jb & 3);
       // odd pairs carry the odd class's factor 1/4 in p
       const float thr = (e & 1) ? ldexpf(kValOddB, -kBigSpanV) : ldexpf(1.0f, -kBigSpanV);
-      b[e] = value_part(mul_lo(pa, wa), mul_lo(pb, wb), pa, pb, thr);
-      float& bacc = (e & 1) ? bias_odd : bias;
-      bacc = mul_hi(pa, wa, bacc);
-      bacc = mul_hi(pb, wb, bacc);
+      b[e] = value_part(y[ja >> 2][ja & 3], y[jb >> 2][jb & 3], pa, pb, thr);
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -284,6 +297,7 @@ struct Bq2Wave {
   // their class factor) with the value-min term added once per column pair.
   __device__ __forceinline__ void to_real() {
     float bt = __builtin_fmaf(bias_odd, 1.0f / kValOddB, bias * (1.0f / kValEvenB));
+    bt = xor_sum(xor_sum(bt, 1), 2);  // per-lane terms: the quad, then the lane groups
     bt = xor_sum(xor_sum(bt, 16), 32);
     if (kpart != 0) bt = 0.0f;  // once per head: the four columns are summed
     constexpr float oscale = 16777216.0f / kValEvenB;
@@ -336,16 +350,19 @@ struct Bq2Wave {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mfma(a[0], bn[0], acc);
     acc = mfma(a[1], bn[1], acc);
-    float s[2][4];
+    float s8[2][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // tile 0 row 4 lg + q is position 8 lg + q
       const float x = key_sum(acc[q]) * qexp;
-      s[0][q] = (lg == 0 && q < ns) ? x : kNegInf;
-      s[1][q] = kNegInf;
+      s8[0][q] = (lg == 0 && q < ns) ? x : kNegInf;
+      s8[1][q] = kNegInf;
     }
-    float p[2][4];
-    softmax<false>(s, 1.0f, p);
+    float s[2];
+    quad_pick2(m_q1, m_q2, s8, s);
+    float pm[2], p[2][4];
+    softmax<false>(s, 1.0f, pm);
+    quad_gather2(pm, p);
     uint32_t b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -396,7 +413,7 @@ __device__ void bq2_run(const Bq2Launch& L, int b, int hkv, const SeqWork& sw, c
                         const Bq2Sinks& sk) {
   const Bq2Geom& g = L.g;
   float* part_base = L.ws + (int64_t)p * GQ * kDP;
-  Bq2Raw rb;
+  Bq2Raw rb, rc, rd;
 
   // rotated query of the unit's GQ heads: qH = H q (in log2 units), per-head
   // exponent E with max |qH| < 2^E, qfs = qH * 2^(kQTop - E): the largest
@@ -474,15 +491,27 @@ __device__ void bq2_run(const Bq2Launch& L, int b, int hkv, const SeqWork& sw, c
     const bool tail = sw.nq * kChunk > sw.n;
     const int end = (tail && hi == sw.nq && hi - 1 >= lo) ? hi - 1 : hi;
     if (lo < end) {
+      // four chunk buffers: the loads of the next three chunks are in flight
+      // while one is used (a chunk here is only 1.25 KB, 8 registers a lane).
+      // Prefetches past the last chunk re-load that chunk (always in bounds)
+      // instead of being skipped, so no load sits under a branch.
       const int last = end - 1;
       int ch = lo;
-      for (; ch < last; ch += 2) {  // ra holds chunk ch on entry
-        w.load(ch + 1, rb);
+      w.load(min(ch + 1, last), rb);
+      w.load(min(ch + 2, last), rc);
+      for (; ch + 3 <= last; ch += 4) {  // ra, rb, rc hold chunks ch .. ch + 2 on entry
+        w.load(ch + 3, rd);
         w.template process<false>(ch, ra, sw.n);
-        w.load(min(ch + 2, last), ra);
+        w.load(min(ch + 4, last), ra);
         w.template process<false>(ch + 1, rb, sw.n);
+        w.load(min(ch + 5, last), rb);
+        w.template process<false>(ch + 2, rc, sw.n);
+        w.load(min(ch + 6, last), rc);
+        w.template process<false>(ch + 3, rd, sw.n);
       }
-      if (ch == last) w.template process<false>(ch, ra, sw.n);
+      if (ch <= last) w.template process<false>(ch, ra, sw.n);
+      if (ch + 1 <= last) w.template process<false>(ch + 1, rb, sw.n);
+      if (ch + 2 <= last) w.template process<false>(ch + 2, rc, sw.n);
     }
     if (end < hi) {
       w.load(end, ra);
@@ -493,7 +522,8 @@ __device__ void bq2_run(const Bq2Launch& L, int b, int hkv, const SeqWork& sw, c
   if (r.rk0 < r.rk1) w.process_sinks(sk, min(sw.n, kSinks), qfs);
 
   // partial: the four columns summed, max, sum over the four lane groups
-  float l = w.l_run;
+  float l = w.l_run;  // per lane: summed over the quad, then the lane groups
+  l = xor_sum(xor_sum(l, 1), 2);
   l = xor_sum(xor_sum(l, 16), 32);
   float* part = part_base + w.hcol * kDP;
   const bool writer = (w.col % Bq2Wave<GQ>::SL) == 0;
@@ -534,7 +564,7 @@ __device__ void bq2_segment(const Bq2Launch& L, int b, int hkv, const SeqWork& s
 
 // One wave per workgroup; grid = the number of worker waves.
 template <int GQ>
-__global__ __launch_bounds__(64) void bq2_partial_kernel(Bq2Launch L) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void bq2_partial_kernel(Bq2Launch L) {
   __shared__ __attribute__((aligned(16))) float qfs[GQ * kD];
   const int lane = threadIdx.x;
   const int w = blockIdx.x, nw = gridDim.x;

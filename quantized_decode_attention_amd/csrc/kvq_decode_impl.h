@@ -341,12 +341,6 @@ struct PackedWave {
   static constexpr bool kShare = SL == 2 || SL == 4;
   static constexpr int NS = kShare ? 8 / SL : 8;  // scores a lane works on
 
-  // a where mask bits are set, else b (v_bfi_b32; a select between two
-  // elements of one array could otherwise become an indexed private array)
-  static __device__ __forceinline__ float bit_sel(uint32_t mask, float a, float b) {
-    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
-    return __builtin_bit_cast(float, ub ^ ((ua ^ ub) & mask));
-  }
   static __device__ __forceinline__ float pair_add(float x) { return x + dpp<0xB1>(x); }
 
   // offset (in the lane group's 8 positions) of this lane's score k
@@ -433,16 +427,7 @@ struct PackedWave {
       }
     }
     if constexpr (SL == 4) {
-      // position j = 4 u + q from quad lane j / 2 (quad_perm control: the
-      // source of quad positions 0..3, 2 bits each)
-      p[0][0] = dpp<0x00>(pm[0]);
-      p[0][1] = dpp<0x00>(pm[1]);
-      p[0][2] = dpp<0x55>(pm[0]);
-      p[0][3] = dpp<0x55>(pm[1]);
-      p[1][0] = dpp<0xAA>(pm[0]);
-      p[1][1] = dpp<0xAA>(pm[1]);
-      p[1][2] = dpp<0xFF>(pm[0]);
-      p[1][3] = dpp<0xFF>(pm[1]);
+      quad_gather2(pm, p);  // position j = 4 u + q from quad lane j / 2
     } else if constexpr (SL == 2) {
       // tile u from the head's lane of slot u: quad positions (0, 1) or (2, 3)
 #pragma unroll

@@ -82,6 +82,37 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
                                                            kCtrl, 0xF, 0xF, true));
 }
+// a where mask bits are set, else b (a bitwise merge: one VALU op; a select
+// between two elements of one array could otherwise become an indexed private
+// array)
+__device__ __forceinline__ float bit_sel(uint32_t mask, float a, float b) {
+  const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+  return __builtin_bit_cast(float, ub ^ ((ua ^ ub) & mask));
+}
+
+// Quad sharing of a lane group's 8 positions j = 4 u + q (two score tiles u,
+// rows q) when the four lanes of a quad hold the same 8 values: quad lane i
+// (masks m1, m2: all ones where bit 0 / bit 1 of i is set) takes positions
+// 2 i and 2 i + 1, and gets all 8 results back from the quad.
+__device__ __forceinline__ void quad_pick2(uint32_t m1, uint32_t m2, const float (&s)[2][4],
+                                           float (&x)[2]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    x[k] = bit_sel(m2, bit_sel(m1, s[1][2 + k], s[1][k]), bit_sel(m1, s[0][2 + k], s[0][k]));
+}
+__device__ __forceinline__ void quad_gather2(const float (&x)[2], float (&p)[2][4]) {
+  // position j from quad lane j / 2 (quad_perm control: the source of quad
+  // positions 0..3, 2 bits each)
+  p[0][0] = dpp<0x00>(x[0]);
+  p[0][1] = dpp<0x00>(x[1]);
+  p[0][2] = dpp<0x55>(x[0]);
+  p[0][3] = dpp<0x55>(x[1]);
+  p[1][0] = dpp<0xAA>(x[0]);
+  p[1][1] = dpp<0xAA>(x[1]);
+  p[1][2] = dpp<0xFF>(x[0]);
+  p[1][3] = dpp<0xFF>(x[1]);
+}
+
 // Sum over aligned groups of n lanes (n = 8 or 16).  Rotations act on whole
 // 16-lane rows, so they serve n = 16; for n = 8 the 4-apart step is a lane
 // shuffle.
