@@ -146,7 +146,7 @@ struct PackedWave {
     hcol = col / SL;
     slot = col % SL;
     m_slot1 = 0u - (uint32_t)(slot & 1);
-    m_slot2 = 0u - (uint32_t)((slot >> 1) & 1);
+    m_slot2 = 0u - (uint32_t)((slot >> 1) & 1);  // (from 4 columns per head: the quad position's bits)
     kofs = lane * 2 * KW;
     vofs = lane * C::NW;
 #pragma unroll
@@ -332,25 +332,30 @@ struct PackedWave {
   // (kColSplit) the hi and lo parts of q' sit in neighbouring columns and are
   // added across the lane pair.
   //
-  // With 2 or 4 columns per head (kShare) the lanes of a head, which sit in
-  // one quad, would all hold the same 8 scores.  Each takes NS = 8 / SL of
-  // them instead (positions NS * slot + k) for the maximum, the exponentials
-  // and the sums, and the weights of all 8 are gathered back from the quad
-  // with DPP moves.  The running sums are then per lane and summed over the
-  // quad at the end.
-  static constexpr bool kShare = SL == 2 || SL == 4;
-  static constexpr int NS = kShare ? 8 / SL : 8;  // scores a lane works on
+  // With two or more columns per head (kShare) the lanes of a quad belong to
+  // one head (a head's columns are consecutive and, from 4 up, 4-aligned)
+  // and would all hold the same 8 scores.  Each takes NS of them instead for
+  // the maximum, the exponentials and the sums: positions 2 i + k for quad
+  // position i with 4 or more columns per head (NS = 2; other quads of the
+  // same head do the same work), 4 slot + k with 2 (NS = 4).  The weights of
+  // all 8 are gathered back from the quad with DPP moves.  The running sums
+  // are then per lane and summed over the quad at the end.
+  static constexpr bool kShare = SL >= 2;
+  static constexpr bool kQuad = SL >= 4;
+  static constexpr int NS = kQuad ? 2 : kShare ? 4 : 8;  // scores a lane works on
 
   static __device__ __forceinline__ float pair_add(float x) { return x + dpp<0xB1>(x); }
 
   // offset (in the lane group's 8 positions) of this lane's score k
-  __device__ __forceinline__ int pos_of(int k) const { return kShare ? NS * slot + k : k; }
+  __device__ __forceinline__ int pos_of(int k) const {
+    return kQuad ? 2 * (slot & 3) + k : kShare ? 4 * slot + k : k;
+  }
 
   // This lane's raw dot products (hi + lo) from the score tiles.
   __device__ __forceinline__ void lane_scores(const f4 (&acc)[2], float (&x)[NS]) const {
-    if constexpr (SL == 4) {
-      // the lane pair (slot 0, 1 or 2, 3) shares tile slot / 2: add hi + lo
-      // on it, then each lane keeps rows 2 (slot % 2) + k
+    if constexpr (kQuad) {
+      // the lane pair (quad positions 0, 1 or 2, 3) shares tile i / 2: add
+      // hi + lo on it, then each lane keeps rows 2 (i % 2) + k
       float f[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) f[q] = pair_add(bit_sel(m_slot2, acc[1][q], acc[0][q]));
@@ -376,7 +381,7 @@ struct PackedWave {
   __device__ __forceinline__ void rescale(float cm) {
     if constexpr (kShare) {
       cm = xor_max(cm, 1);
-      if constexpr (SL == 4) cm = xor_max(cm, 2);
+      if constexpr (kQuad) cm = xor_max(cm, 2);
     }
     cm = xor_max(cm, 16);
     cm = xor_max(cm, 32);
@@ -403,7 +408,7 @@ struct PackedWave {
     for (int k = 1; k < NS; ++k) cm = fmaxf(cm, s[k]);
     if (__any(cm > m_run)) rescale(cm);
     float pm[NS];
-    if constexpr (kPacked && SL == 4) {  // a lane's two rows share a class
+    if constexpr (kPacked && kQuad) {  // a lane's two rows share a class
       const bool odd = slot & 1;
       const float mref = odd ? m_odd : m_even;
       pm[0] = exp2_hw(s[0] - mref);
@@ -426,7 +431,7 @@ struct PackedWave {
         }
       }
     }
-    if constexpr (SL == 4) {
+    if constexpr (kQuad) {
       quad_gather2(pm, p);  // position j = 4 u + q from quad lane j / 2
     } else if constexpr (SL == 2) {
       // tile u from the head's lane of slot u: quad positions (0, 1) or (2, 3)
@@ -907,7 +912,7 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   float l_run = w.l_run;
   if constexpr (PackedWave<D, BK, BV, GQ, NG, PG>::kShare) {  // per-lane sums
     l_run = xor_sum(l_run, 1);
-    if constexpr (SL == 4) l_run = xor_sum(l_run, 2);
+    if constexpr (PackedWave<D, BK, BV, GQ, NG, PG>::kQuad) l_run = xor_sum(l_run, 2);
   }
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);
