@@ -94,6 +94,7 @@ struct Bq2Wave {
   int lane, col, lg, hcol, part, kpart;
   bool vbig;     // this lane's value columns hold the large weights
   uint32_t m_q1, m_q2;  // all ones where bit 0 / bit 1 of the lane's quad position is set
+  uint32_t m_vbig;      // all ones on lanes whose value columns take the large weights
   float m1;      // -1 in a register
   float mpart;   // 0 on hi lanes, -1 on lo lanes: selects the part of a split
   float qbig;    // 2^(kQTop - kBigSpan): query components at or above go to key part 0
@@ -116,6 +117,7 @@ struct Bq2Wave {
     vbig = kpart < 2;
     m_q1 = 0u - (uint32_t)(lane & 1);
     m_q2 = 0u - (uint32_t)((lane >> 1) & 1);
+    m_vbig = vbig ? ~0u : 0u;
     m1 = opaque_m1();
     qbig = ldexpf(1.0f, kQTop - kBigSpan);
     mpart = part ? m1 : 0.0f;
@@ -264,20 +266,31 @@ struct Bq2Wave {
       bias += odd ? 0.0f : bm;
       bias_odd += odd ? bm : 0.0f;
     }
-    // all 8 positions of the lane group back from the quad
-    float p[2][4], y[2][4];
-    quad_gather2(pm, p);
-    quad_gather2(ym, y);
-    // B operand: element j = position 8 lg + j, weight p_j dV_j; pair e holds
-    // j = 2e, 2e + 1 (odd e: the odd weight class)
+    // the lane's products split by weight size (the large-weight columns
+    // take p >= the class threshold; odd quad positions are the odd class,
+    // whose p carries the factor 1/4): one of each pair is the product, the
+    // other 0.  All 8 positions of the lane group come back from the quad.
+    float yb[2], ys[2];
+    {
+      const float thr = (lane & 1) ? ldexpf(kValOddB, -kBigSpanV) : ldexpf(1.0f, -kBigSpanV);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const bool big = pm[k] >= thr;
+        yb[k] = big ? ym[k] : 0.0f;
+        ys[k] = big ? 0.0f : ym[k];
+      }
+    }
+    float Yb[2][4], Ys[2][4];
+    quad_gather2(yb, Yb);
+    quad_gather2(ys, Ys);
+    // B operand: element j = position 8 lg + j, weight p_j dV_j (the part of
+    // this lane's columns); pair e holds j = 2e, 2e + 1
     uint32_t b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ja = 2 * e, jb = 2 * e + 1;
-      const float pa = p[ja >> 2][ja & 3], pb = p[jb >> 2][jb & 3];
-      // odd pairs carry the odd class's factor 1/4 in p
-      const float thr = (e & 1) ? ldexpf(kValOddB, -kBigSpanV) : ldexpf(1.0f, -kBigSpanV);
-      b[e] = value_part(y[ja >> 2][ja & 3], y[jb >> 2][jb & 3], pa, pb, thr);
+      b[e] = part_of(bit_sel(m_vbig, Yb[ja >> 2][ja & 3], Ys[ja >> 2][ja & 3]),
+                     bit_sel(m_vbig, Yb[jb >> 2][jb & 3], Ys[jb >> 2][jb & 3]));
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
