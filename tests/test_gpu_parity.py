@@ -99,6 +99,7 @@ DECODE_CASES = [
     (1, 2, 2, 64, 2, 2, 32, 32, [256]),                   # config 1
     (2, 8, 8, 128, 2, 2, 32, 128, [1000, 700]),           # MHA
     (2, 32, 8, 128, 2, 4, 32, 128, [3000, 2177]),         # GQA 4, K2V4
+    (2, 16, 8, 128, 2, 4, 32, 128, [2600, 1111]),         # GQA 2, D128 (8 columns per head)
     (3, 32, 8, 128, 2, 2, 64, 128, [5000, 129, 4097]),    # varlen, G64
     (2, 16, 8, 128, 4, 2, 64, 64, [4100, 4160]),          # K4V2 G64 R64
     (2, 16, 2, 64, 4, 4, 64, 64, [777, 64]),              # GQA 8, D64
