@@ -287,6 +287,23 @@ int kvq_append(const kvq_geom *geom, const uint16_t *k_new,
                const uint16_t *v_new, const int32_t *seq_lens,
                const kvq_cache *cache, void *stream);
 
+/* Appends T tokens per sequence in one call: the new tokens of a multi-token
+ * decode step, before kvq_decode_attn_multi ([KIVI] core capabilities, as
+ * kvq_append).  The cache ends bit-identical to T kvq_append calls, token t
+ * with k_new[:, t], v_new[:, t] and lengths seq_lens + t (a window that fills
+ * part-way is flushed before the token that finds it full).
+ *   T             host int32, >= 1.
+ *   k_new, v_new  device fp16 [B][T][Hkv][D]: the new tokens, oldest first.
+ *   seq_lens      device int32 [B]: tokens each sequence holds BEFORE the
+ *                 first of them.  Not modified.
+ * A sequence with n = seq_lens[b] < 0 or n + T > capacity is left untouched
+ * (no write), which is the caller's error.  One workgroup per (sequence, KV
+ * head) does its tokens in order, so a call that flushes takes longer than
+ * one that does not. */
+int kvq_append_tokens(const kvq_geom *geom, int32_t T, const uint16_t *k_new,
+                      const uint16_t *v_new, const int32_t *seq_lens,
+                      const kvq_cache *cache, void *stream);
+
 /* Single-token decode attention over the packed cache plus the residual window
  * (split-context partial softmax over the packed tokens, then a combine that
  * also covers the fp16 residual window; GQA heads of one KV head are processed

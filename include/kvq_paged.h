@@ -94,6 +94,11 @@ int kvq_paged_prefill(const kvq_geom *geom, const uint16_t *k, const uint16_t *v
 int kvq_paged_append(const kvq_geom *geom, const uint16_t *k_new, const uint16_t *v_new,
                      const int32_t *seq_lens, const kvq_paged_cache *cache, void *stream);
 
+/* kvq_append_tokens into the paged cache (same arguments and rules). */
+int kvq_paged_append_tokens(const kvq_geom *geom, int32_t T, const uint16_t *k_new,
+                            const uint16_t *v_new, const int32_t *seq_lens,
+                            const kvq_paged_cache *cache, void *stream);
+
 /* kvq_decode_attn over the paged cache: same arguments, rules and results
  * as over a dense cache holding the same positions (the split of the work may
  * differ, and with it the rounding of the partial sums). */

@@ -9,7 +9,7 @@ accounting used by the benchmark.
 """
 from ._lib import (  # noqa: F401
     ABI_VERSION, LAYOUT_VERSION, Cache, Geom, KvqError, alloc_workspace,
-    kvq_abi_version, kvq_append, kvq_cache_bytes, kvq_decode_attn,
+    kvq_abi_version, kvq_append, kvq_append_tokens, kvq_cache_bytes, kvq_decode_attn,
     kvq_decode_combine, kvq_decode_partial, kvq_decode_workers,
     kvq_decode_workspace_bytes, kvq_layout_version, kvq_prefill,
     kvq_quantize_keys_perchannel, kvq_quantize_values_pertoken,
@@ -22,7 +22,8 @@ from ._lib import (  # noqa: F401
     kvq_bq2_decode_workers, kvq_bq2_decode_workspace_bytes, kvq_bq2_prefill,
     kvq_bq2_validate_geom)
 from ._lib import (  # noqa: F401
-    PagedCache, alloc_paged_workspace, kvq_paged_append, kvq_paged_cache_bytes,
+    PagedCache, alloc_paged_workspace, kvq_paged_append, kvq_paged_append_tokens,
+    kvq_paged_cache_bytes,
     kvq_paged_decode_attn, kvq_paged_decode_attn_multi, kvq_paged_decode_combine,
     kvq_paged_decode_partial, kvq_paged_decode_workspace_bytes, kvq_paged_prefill,
     kvq_paged_validate)

@@ -39,7 +39,7 @@ EXPORTS = [
     "kvq_abi_version", "kvq_layout_version", "kvq_status_str", "kvq_last_error",
     "kvq_validate_geom", "kvq_cache_bytes", "kvq_decode_workers",
     "kvq_decode_workspace_bytes", "kvq_quantize_keys_perchannel",
-    "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append",
+    "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append", "kvq_append_tokens",
     "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
     "kvq_decode_multi_workspace_bytes", "kvq_decode_attn_multi",
 ]
@@ -50,7 +50,7 @@ EXPORTS_BQ2 = [
 ]
 EXPORTS_PAGED = [
     "kvq_paged_validate", "kvq_paged_cache_bytes", "kvq_paged_decode_workspace_bytes",
-    "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_decode_attn",
+    "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_append_tokens", "kvq_paged_decode_attn",
     "kvq_paged_decode_partial", "kvq_paged_decode_combine", "kvq_paged_decode_attn_multi",
 ]
 EXPORTS_PROBE = ["kvq_probe_stream_read", "kvq_probe_sink_words"]
@@ -117,6 +117,7 @@ def lib() -> ctypes.CDLL:
             "kvq_paged_decode_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
             "kvq_paged_prefill": (ctypes.c_int, [G, P, P, i32, CP, P]),
             "kvq_paged_append": (ctypes.c_int, [G, P, P, P, CP, P]),
+            "kvq_paged_append_tokens": (ctypes.c_int, [G, ctypes.c_int32, P, P, P, CP, P]),
             "kvq_paged_decode_attn": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
             "kvq_paged_decode_partial": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
             "kvq_paged_decode_combine": (ctypes.c_int, [G, P, CP, P, i32, f32, P, sz, P, P]),
@@ -134,6 +135,7 @@ def lib() -> ctypes.CDLL:
             "kvq_quantize_values_pertoken": (ctypes.c_int, [G, P, i32, i32, P, P, P]),
             "kvq_prefill": (ctypes.c_int, [G, P, P, i32, C, P]),
             "kvq_append": (ctypes.c_int, [G, P, P, P, C, P]),
+            "kvq_append_tokens": (ctypes.c_int, [G, ctypes.c_int32, P, P, P, C, P]),
             "kvq_decode_attn": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_partial": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_combine": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
@@ -352,6 +354,18 @@ def kvq_append(g: Geom, k_new: torch.Tensor, v_new: torch.Tensor,
                             ctypes.byref(cc), _stream(stream)), "kvq_append")
 
 
+def kvq_append_tokens(g: Geom, T: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                      seq_lens: torch.Tensor, cache: Cache, stream=None) -> None:
+    """T new tokens per sequence, k_new / v_new [B][T][Hkv][D], in one launch."""
+    shape = (g.batch, T, g.n_kv_heads, g.head_dim)
+    gc = g.c()
+    cc = _cache_arg(cache)
+    _check(lib().kvq_append_tokens(ctypes.byref(gc), T, _ptr(k_new, "k_new", _F16, shape),
+                                   _ptr(v_new, "v_new", _F16, shape),
+                                   _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
+                                   ctypes.byref(cc), _stream(stream)), "kvq_append_tokens")
+
+
 def _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out):
     gc = g.c()
     cc = _cache_arg(cache)
@@ -519,6 +533,18 @@ def kvq_paged_append(g: Geom, k_new: torch.Tensor, v_new: torch.Tensor,
                                   _ptr(v_new, "v_new", _F16, shape),
                                   _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
                                   ctypes.byref(cc), _stream(stream)), "kvq_paged_append")
+
+
+def kvq_paged_append_tokens(g: Geom, T: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                            seq_lens: torch.Tensor, cache: PagedCache, stream=None) -> None:
+    shape = (g.batch, T, g.n_kv_heads, g.head_dim)
+    gc = g.c()
+    cc = cache.c()
+    _check(lib().kvq_paged_append_tokens(ctypes.byref(gc), T, _ptr(k_new, "k_new", _F16, shape),
+                                         _ptr(v_new, "v_new", _F16, shape),
+                                         _ptr(seq_lens, "seq_lens", _I32, (g.batch,)),
+                                         ctypes.byref(cc), _stream(stream)),
+           "kvq_paged_append_tokens")
 
 
 def kvq_paged_decode_attn_multi(g: Geom, q: torch.Tensor, cache: PagedCache,

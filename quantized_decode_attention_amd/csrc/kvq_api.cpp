@@ -489,6 +489,25 @@ int kvq_append(const kvq_geom* geom, const uint16_t* k_new, const uint16_t* v_ne
   }
 }
 
+int kvq_append_tokens(const kvq_geom* geom, int32_t T, const uint16_t* k_new,
+                      const uint16_t* v_new, const int32_t* seq_lens, const kvq_cache* cache,
+                      void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(cache)) != KVQ_OK) return st;
+    if (T < 1) return fail(KVQ_ERR_RANGE, "T must be >= 1 (got %d)", T);
+    if ((st = check_ptr(k_new, "k_new")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_new, "v_new")) != KVQ_OK) return st;
+    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
+    hipError_t e = kvq::launch_append_tokens(kvq::to_geom(*geom), T, k_new, v_new, seq_lens,
+                                             *cache, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "append_tokens launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 int kvq_decode_partial(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                        void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
@@ -793,6 +812,26 @@ int kvq_paged_append(const kvq_geom* geom, const uint16_t* k_new, const uint16_t
     hipError_t e = kvq::launch_append(kvq::to_geom(*geom, *cache), k_new, v_new, seq_lens,
                                       kvq::pool_view(*cache), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "append launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int kvq_paged_append_tokens(const kvq_geom* geom, int32_t T, const uint16_t* k_new,
+                            const uint16_t* v_new, const int32_t* seq_lens,
+                            const kvq_paged_cache* cache, void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    if ((st = check_paged(geom, cache, true)) != KVQ_OK) return st;
+    if (T < 1) return fail(KVQ_ERR_RANGE, "T must be >= 1 (got %d)", T);
+    if ((st = check_ptr(k_new, "k_new")) != KVQ_OK) return st;
+    if ((st = check_ptr(v_new, "v_new")) != KVQ_OK) return st;
+    if ((st = check_lens(seq_lens)) != KVQ_OK) return st;
+    hipError_t e =
+        kvq::launch_append_tokens(kvq::to_geom(*geom, *cache), T, k_new, v_new, seq_lens,
+                                  kvq::pool_view(*cache), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "append_tokens launch");
   } catch (...) {
     return fail(KVQ_ERR_INTERNAL, "unexpected exception");
   }

@@ -98,6 +98,11 @@ hipError_t launch_residual_copy(const Geom& g, const uint16_t* src, int64_t src_
 hipError_t launch_append(const Geom& g, const uint16_t* k_new,
                          const uint16_t* v_new, const int32_t* seq_lens,
                          const kvq_cache& cache, hipStream_t st);
+// T new tokens per sequence ([B][T][Hkv][D]) in one launch: the same result
+// as T launch_append calls with seq_lens + t.
+hipError_t launch_append_tokens(const Geom& g, int T, const uint16_t* k_new,
+                                const uint16_t* v_new, const int32_t* seq_lens,
+                                const kvq_cache& c, hipStream_t st);
 
 struct DecodeLaunch {
   Geom g;

@@ -361,6 +361,55 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   }
 }
 
+// T tokens per sequence in one launch (the new tokens of a multi-token decode
+// step): one workgroup per (sequence, KV head) appends them in order, each as
+// append_kernel would, so the cache ends bit-identical to T single appends.
+// A token that arrives for a full window first quantizes the whole window
+// here, one key group or value block after another through the LDS tile
+// (the window then holds every earlier token of this call, written above).
+template <int BK, int BV>
+__global__ __launch_bounds__(kThreads) void append_tokens_kernel(
+    Geom g, int T, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ seq_lens, uint32_t* __restrict__ k_codes,
+    uint32_t* __restrict__ v_codes, uint16_t* __restrict__ k_meta,
+    uint16_t* __restrict__ v_meta, uint16_t* __restrict__ k_res,
+    uint16_t* __restrict__ v_res) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int b = blockIdx.y, hkv = blockIdx.x;
+  const int64_t unit = (int64_t)b * g.Hkv + hkv;
+  const int32_t n = seq_lens[b];
+  if (n < 0 || n > g.C - T) return;  // caller error: leave the cache untouched
+  uint16_t* kr = k_res + unit * g.R * g.D;
+  uint16_t* vr = v_res + unit * g.Rv * g.D;
+  uint16_t* tile = lds;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(lds + quant_rows(g) * g.D);
+  for (int t = 0; t < T; ++t) {
+    const int32_t pos = n + t;
+    const int64_t src = (((int64_t)b * T + t) * g.Hkv + hkv) * g.D;  // [B][T][Hkv][D]
+    if (pos > 0 && pos % g.R == 0) {
+      for (int j = 0; j < g.R / g.G; ++j) {
+        load_tile(tile, kr + (int64_t)j * g.G * g.D, g.G * g.D);
+        __syncthreads();
+        key_group<BK>(g, unit, pos - g.R + j * g.G, k_codes, k_meta, tile, codes);
+        __syncthreads();
+      }
+    }
+    if (pos > 0 && pos % g.Rv == 0) {
+      for (int blk = 0; blk < g.Rv / kVBlock; ++blk) {
+        load_value_window(tile, vr, blk, g.D);
+        __syncthreads();
+        value_block<BV>(g, unit, pos - g.Rv + blk * kVBlock, v_codes, v_meta, tile, codes);
+        __syncthreads();
+      }
+    }
+    for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
+      kr[(int64_t)(pos % g.R) * g.D + c] = k_new[src + c];
+      vr[value_res_index(g.D, pos % g.Rv, c)] = v_new[src + c];
+    }
+    __syncthreads();  // a later token's flush reads these slots
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_keys(const Geom& g, const uint16_t* src,
@@ -433,6 +482,31 @@ hipError_t launch_append(const Geom& g, const uint16_t* k_new,
     default: return hipErrorInvalidValue;
   }
 #undef KVQ_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_append_tokens(const Geom& g, int T, const uint16_t* k_new,
+                                const uint16_t* v_new, const int32_t* seq_lens,
+                                const kvq_cache& c, hipStream_t st) {
+  dim3 grid(g.Hkv, g.B);
+#define KVQ_APPEND_T(BK, BV)                                                  \
+  append_tokens_kernel<BK, BV><<<grid, kThreads, quant_lds_bytes(g), st>>>(   \
+      g, T, k_new, v_new, seq_lens, c.k_codes, c.v_codes, c.k_meta, c.v_meta, \
+      c.k_res, c.v_res)
+  const int code = 10 * g.bK + g.bV;
+  switch (code) {
+    case 22: KVQ_APPEND_T(2, 2); break;
+    case 24: KVQ_APPEND_T(2, 4); break;
+    case 28: KVQ_APPEND_T(2, 8); break;
+    case 42: KVQ_APPEND_T(4, 2); break;
+    case 44: KVQ_APPEND_T(4, 4); break;
+    case 48: KVQ_APPEND_T(4, 8); break;
+    case 82: KVQ_APPEND_T(8, 2); break;
+    case 84: KVQ_APPEND_T(8, 4); break;
+    case 88: KVQ_APPEND_T(8, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KVQ_APPEND_T
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ def test_exports_every_declared_bq2_symbol():
 def test_exports_every_declared_paged_symbol():
     L = kvq.lib()
     names = _declared(HEADER_PAGED)
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.EXPORTS_PAGED) == names
@@ -272,6 +272,11 @@ def test_invalid_arguments_are_rejected_before_launch():
     # prefill length out of range
     c = _lib.kvq_cache(*([0x10000] * 6))
     assert L.kvq_prefill(ctypes.byref(g), fake, fake, 1025, ctypes.byref(c), None) == -6
+    # a T-token append needs T >= 1, and the usual pointers
+    assert L.kvq_append_tokens(ctypes.byref(g), 0, fake, fake, fake, ctypes.byref(c), None) == -6
+    assert "T must be" in kvq.last_error()
+    assert L.kvq_append_tokens(ctypes.byref(g), 4, None, fake, fake, ctypes.byref(c), None) == -1
+    assert L.kvq_append_tokens(ctypes.byref(g), 4, fake, odd, fake, ctypes.byref(c), None) == -4
     # bad geometry is reported first
     bad = kvq.Geom(**{**GOOD, "k_bits": 3}).c()
     assert L.kvq_decode_attn(ctypes.byref(bad), fake, ctypes.byref(c), fake, 8, 0.1,
