@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--config", type=int, default=3, help="workload 1..6 (default 3)")
     p.add_argument("--layers", type=int, default=4, help="rotating layer caches")
     p.add_argument("--tokens", type=int, default=1,
-                   help="query tokens per sequence per step (T > 1: T appends, then "
+                   help="query tokens per sequence per step (T > 1: kvq_append_tokens, then "
                         "kvq_decode_attn_multi; KIVI-format workloads)")
     p.add_argument("--page-size", type=int, default=0,
                    help="KIVI workloads: a paged cache with pages of this many positions, "
@@ -376,11 +376,13 @@ def main():
             caches.append(kvq.PagedCache(g, P, w.batch * maxp, torch.from_numpy(table).to(dev),
                                          dev))
         prefill, append = kvq.kvq_paged_prefill, kvq.kvq_paged_append
+        append_tokens = kvq.kvq_paged_append_tokens
         partial, combine = kvq.kvq_paged_decode_partial, kvq.kvq_paged_decode_combine
         multi = kvq.kvq_paged_decode_attn_multi
     else:
         caches = [kvq.Cache(g, dev) for _ in range(L)]
         prefill, append = kvq.kvq_prefill, kvq.kvq_append
+        append_tokens = kvq.kvq_append_tokens
         partial, combine = kvq.kvq_decode_partial, kvq.kvq_decode_combine
         multi = kvq.kvq_decode_attn_multi
     # prefill every layer from the same seeded tensors (layer 0's draw)
@@ -403,6 +405,10 @@ def main():
 
     # per-step inputs (a pool of seeded tokens) and lengths, all on device
     pool = [tuple(torch.from_numpy(x).to(dev) for x in synth.step_token(w, s)) for s in range(8)]
+    # T > 1: the T new tokens of step s as [B][T][Hkv][D] (pool entries s .. s + T - 1)
+    tpool = [(torch.stack([pool[(s + j) % len(pool)][0] for j in range(T)], 1).contiguous(),
+              torch.stack([pool[(s + j) % len(pool)][1] for j in range(T)], 1).contiguous())
+             for s in range(len(pool))] if T > 1 else None
     # lens_host[s, j]: length before append j of step s (j < T); [s, T]: after
     lens_host = np.zeros((total_steps, T + 1, w.batch), np.int32)
     cur = [start.copy() for _ in range(L)]
@@ -454,9 +460,12 @@ def main():
         stream = torch.cuda.current_stream()  # the capture stream inside a graph capture
         l = s % L
         c = caches[l]
-        for j in range(T):
-            kn, vn, _ = pool[(s + j) % len(pool)]
-            append(g, kn, vn, lens_dev[s, j], c, stream)
+        if T == 1:
+            kn, vn, _ = pool[s % len(pool)]
+            append(g, kn, vn, lens_dev[s, 0], c, stream)
+        else:  # the T new tokens in one launch
+            kt, vt = tpool[s % len(tpool)]
+            append_tokens(g, T, kt, vt, lens_dev[s, 0], c, stream)
         if timed_idx is not None:
             ev_a[timed_idx].record(stream)
         if T == 1:
@@ -512,7 +521,7 @@ def main():
             "rotating_layer_caches": L, "decode_worker_waves": n_workers,
             "step": ("kvq_append (+flush when a window fills) + kvq_decode_attn, one layer"
                      if T == 1 else
-                     f"{T} x kvq_append + kvq_decode_attn_multi (T={T}), one layer"),
+                     f"kvq_append_tokens (T={T}) + kvq_decode_attn_multi, one layer"),
             "query_tokens": T,
             "cache": f"paged, {P}-position pages in shuffled order" if P else "dense",
             "launch": ("kernels launched one by one" if a.eager else
