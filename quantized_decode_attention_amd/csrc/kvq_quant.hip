@@ -381,6 +381,22 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(
   if (n < 0 || n > g.C - T) return;  // caller error: leave the cache untouched
   uint16_t* kr = k_res + unit * g.R * g.D;
   uint16_t* vr = v_res + unit * g.Rv * g.D;
+  // the first position of the call that finds a window full (a multiple of
+  // the window length, above 0): with none, every token is a plain copy, done
+  // at once
+  const int32_t p1 = n > 0 ? n : 1;
+  const bool kflush = (p1 + g.R - 1) / g.R * g.R < n + T;
+  const bool vflush = (p1 + g.Rv - 1) / g.Rv * g.Rv < n + T;
+  if (!kflush && !vflush) {
+    for (int i = threadIdx.x; i < T * g.D; i += blockDim.x) {
+      const int t = i / g.D, c = i % g.D;
+      const int32_t pos = n + t;
+      const int64_t src = (((int64_t)b * T + t) * g.Hkv + hkv) * g.D + c;
+      kr[(int64_t)(pos % g.R) * g.D + c] = k_new[src];
+      vr[value_res_index(g.D, pos % g.Rv, c)] = v_new[src];
+    }
+    return;
+  }
   uint16_t* tile = lds;
   uint8_t* codes = reinterpret_cast<uint8_t*>(lds + quant_rows(g) * g.D);
   for (int t = 0; t < T; ++t) {
