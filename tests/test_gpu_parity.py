@@ -96,7 +96,7 @@ def test_quantize_synthetic_configs_bitexact():
 # ---------------------------------------------------------------- decode ----
 DECODE_CASES = [
     # B, Hq, Hkv, D, bK, bV, G, R, lens
-    (1, 2, 2, 64, 2, 2, 32, 32, [256]),                   # config 1
+    (1, 2, 2, 64, 2, 2, 32, 32, [256]),                   # tiny: B1, 2 heads, D64
     (2, 8, 8, 128, 2, 2, 32, 128, [1000, 700]),           # MHA
     (2, 32, 8, 128, 2, 4, 32, 128, [3000, 2177]),         # GQA 4, K2V4
     (2, 16, 8, 128, 2, 4, 32, 128, [2600, 1111]),         # GQA 2, D128 (8 columns per head)

@@ -73,7 +73,7 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_decode_step_bytes_of_the_benchmarked_workload():
-    """Config 3 (B32, 32/8, D128, K2/V4, G32, R128) at n = 8192: per KV head
+    """The Llama-3-8B GQA workload (B32, 32/8, D128, K2/V4, G32, R128) at n = 8192: per KV head
     8064 packed tokens of 32 + 64 + 16 + 16 bytes and 128 fp16 tokens of 512
     bytes, plus q in and out (4 bytes per query value) and the lengths."""
     n = [8192] * 32

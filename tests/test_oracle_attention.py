@@ -45,7 +45,7 @@ def _tiny_case(orc, n, B=1, Hq=4, Hkv=2, D=64, bK=2, bV=4, G=32, R=32, seed=5):
     return g, cache, k, v, q
 
 
-def test_attention_matches_torch_sdpa_config1(orc):
+def test_attention_matches_torch_sdpa_tiny(orc):
     w = synth.WORKLOADS[1]
     g = _geom(orc, w, 288)
     k = synth.keys(w, w.context)
