@@ -45,6 +45,20 @@ for _paged in (0, 1):
                                        f"-DKVQ_PAGED={_paged}", f"-DKVQ_INST={_name}"]))
 
 
+def scratch_kernels(remarks: str) -> list[tuple[str, int]]:
+    """(kernel, bytes per lane) of every decode partial kernel (either format)
+    that the compiler's resource-usage remarks report with scratch."""
+    out, func = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            func = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0 and func and "partial" in func:
+            out.append((func, int(m.group(1))))
+    return out
+
+
 def _compile(name: str, source: str, extra: list[str]) -> str:
     src = os.path.join(CSRC, source)
     obj = os.path.join(BUILD, name + ".o")
@@ -61,14 +75,10 @@ def _compile(name: str, source: str, extra: list[str]) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed on " + name)
     if guard:
-        func = None
-        for line in r.stderr.splitlines():
-            m = re.search(r"Function Name: (\S+)", line)
-            if m:
-                func = m.group(1)
-            m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
-            if m and int(m.group(1)) > 0 and func and "partial" in func:
-                raise RuntimeError(f"{name}: {func} uses {m.group(1)} bytes/lane of scratch")
+        bad = scratch_kernels(r.stderr)
+        if bad:
+            func, nbytes = bad[0]
+            raise RuntimeError(f"{name}: {func} uses {nbytes} bytes/lane of scratch")
     return obj
 
 

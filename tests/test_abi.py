@@ -285,3 +285,21 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert L.kvq_decode_attn(ctypes.byref(g), fake, ctypes.byref(c), fake, 8,
                              float("nan"), None, 0, fake, None) == -6
     assert L.kvq_cache_bytes(None, None) == -1
+
+
+def test_build_scratch_guard_reads_the_resource_remarks():
+    """The build rejects a decode partial kernel (either format) that the
+    compiler reports with scratch; other kernels and zero scratch pass."""
+    from quantized_decode_attention_amd import build
+    remarks = "\n".join([
+        "x.hip:1:1: remark: Function Name: _ZN3kvq12_GLOBAL__N_121decode_partial_kernelILi128E",
+        "x.hip:1:1: remark:     VGPRs: 201",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0",
+        "x.hip:2:1: remark: Function Name: _ZN3kvq12_GLOBAL__N_118bq2_partial_kernelILi4E",
+        "x.hip:2:1: remark:     ScratchSize [bytes/lane]: 28",
+        "x.hip:3:1: remark: Function Name: _ZN3kvq12_GLOBAL__N_121decode_combine_kernel",
+        "x.hip:3:1: remark:     ScratchSize [bytes/lane]: 16",
+    ])
+    assert build.scratch_kernels(remarks) == [
+        ("_ZN3kvq12_GLOBAL__N_118bq2_partial_kernelILi4E", 28)]
+    assert build.scratch_kernels(remarks.replace(": 28", ": 0")) == []
