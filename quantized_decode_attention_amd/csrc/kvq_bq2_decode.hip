@@ -98,7 +98,7 @@ struct Bq2Wave {
   float m1;      // -1 in a register
   float mpart;   // 0 on hi lanes, -1 on lo lanes: selects the part of a split
   float qbig;    // 2^(kQTop - kBigSpan): query components at or above go to key part 0
-  float kscale;  // 2^(E - kQTop + 24): code accumulation to log2 units (this lane's head)
+  float kscale;  // 2^(E - kQTop + 24 - L): code accumulation to log2 units (this lane's head)
   float sumq_k;  // sum_c qH_c of this lane's head (log2 units) / kscale
   float qexp;    // 2^(E - kQTop)
   f4 oacc[4];
@@ -128,11 +128,12 @@ struct Bq2Wave {
     bias = bias_odd = 0.0f;
   }
 
-  // (a, b) -> the fp16 pair of this lane's part: hi = rtz(a, b), lo = the
-  // remainders (exact fp32 differences).
+  // (a, b) -> the fp16 pair of this lane's part: hi = rne(a, b), lo = the
+  // remainders (exact fp32 differences) rounded to nearest (part 0 rounds
+  // a - 0 * hi, i.e. is hi itself).
   __device__ __forceinline__ uint32_t part_of(float a, float b) const {
-    const uint32_t hi = pk_rtz(a, b);
-    return pk_rtz(__builtin_fmaf(lo_half(hi), mpart, a), __builtin_fmaf(hi_half(hi), mpart, b));
+    const uint32_t hi = pk_rne(a, b);
+    return pk_rne(__builtin_fmaf(lo_half(hi), mpart, a), __builtin_fmaf(hi_half(hi), mpart, b));
   }
 
   // Key-side operand pair of this lane's part (qa, qb: query components; f:
@@ -141,10 +142,10 @@ struct Bq2Wave {
   // = 0.  Every remainder is an exact fp32 difference.
   __device__ __forceinline__ uint32_t key_part(float qa, float qb, float f) const {
     const float a = qa * f, b = qb * f;
-    const uint32_t h0 = pk_rtz(fabsf(qa) >= qbig ? a : 0.0f, fabsf(qb) >= qbig ? b : 0.0f);
+    const uint32_t h0 = pk_rne(fabsf(qa) >= qbig ? a : 0.0f, fabsf(qb) >= qbig ? b : 0.0f);
     const float ra = a - lo_half(h0), rb = b - hi_half(h0);
-    const uint32_t h1 = pk_rtz(ra, rb);
-    const uint32_t h2 = pk_rtz(ra - lo_half(h1), rb - hi_half(h1));
+    const uint32_t h1 = pk_rne(ra, rb);
+    const uint32_t h2 = pk_rne(ra - lo_half(h1), rb - hi_half(h1));
     return kpart == 0 ? h0 : kpart == 1 ? h1 : kpart == 2 ? h2 : 0u;
   }
   // Value-side operand pair of this lane's column (x: weights p * dV; p: the
@@ -297,23 +298,20 @@ struct Bq2Wave {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // tile 2m + h: pair e of token 8 lg + 2e (+1) at bits 8h + 4(e/2) + 2(e%2)
-        const uint32_t x = r.vw[m] >> (8 * h);
         uint32_t a[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a[e] = (x >> (4 * (e >> 1))) & ((e & 1) ? 0x000C000Cu : 0x00030003u);
+        unpack_value_tile<2>(r.vw, 2 * m + h, a);
         oacc[2 * m + h] = mfma(a, b, oacc[2 * m + h]);
       }
   }
 
-  // Packed accumulation to real scale (codes were c * 2^-24, odd pairs carry
+  // Packed accumulation to real scale (codes were c * 2^(L-24), odd pairs carry
   // their class factor) with the value-min term added once per column pair.
   __device__ __forceinline__ void to_real() {
     float bt = __builtin_fmaf(bias_odd, 1.0f / kValOddB, bias * (1.0f / kValEvenB));
     bt = xor_sum(xor_sum(bt, 1), 2);  // per-lane terms: the quad, then the lane groups
     bt = xor_sum(xor_sum(bt, 16), 32);
     if (kpart != 0) bt = 0.0f;  // once per head: the four columns are summed
-    constexpr float oscale = 16777216.0f / kValEvenB;
+    constexpr float oscale = 16777216.0f / float(1 << kCodeLift<2>) / kValEvenB;
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -477,7 +475,7 @@ __device__ void bq2_run(const Bq2Launch& L, int b, int hkv, const SeqWork& sw, c
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  w.kscale = ldexpf(1.0f, e_mine - kQTop + 24 - kKeyAccLog2<2>);
+  w.kscale = ldexpf(1.0f, e_mine - kQTop + 24 - kKeyAccLog2<2> - kCodeLift<2>);
   w.qexp = ldexpf(1.0f, e_mine - kQTop);
   w.sumq_k = sum_mine / w.kscale;  // exact: kscale is a power of two
   // key-side fragments in the key words' channel order: pair v of k-chunk kc

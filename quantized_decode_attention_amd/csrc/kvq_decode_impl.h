@@ -15,9 +15,10 @@
 //   sum_t p_t v_tc = sum_t (p_t scale_t,gamma) code_tc + sum_t p_t min_t,gamma
 // so both contractions run on the small integer codes.  On gfx950 they are done
 // by v_mfma_f32_16x16x32_f16 with the codes fed as fp16 subnormals (a code c
-// masked out of a packed word *is* the fp16 number c * 2^-24, which the matrix
-// cores multiply exactly) and the fp32 factors (q * scale, p * scale) split into
-// a high and a low fp16 part, two MFMAs accumulating into the same fp32 tile.
+// shifted to the top of an fp16 mantissa and masked out of a packed word *is*
+// the fp16 number c * 2^(L - 24), which the matrix cores multiply exactly)
+// and the fp32 factors (q * scale, p * scale) split into a high and a low fp16
+// part, two MFMAs accumulating into the same fp32 tile.
 // The scaled-query and weight operands are computed once per key group / per
 // 32-token chunk; everything per code is a shift and a mask.
 //
@@ -30,7 +31,8 @@
 // per unit its share touches.  The GQA query heads of a KV head share every
 // load.  The combine kernel (one workgroup per unit) merges a unit's partials:
 //   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
-// Scores are kept in log2 units (sm_scale * log2 e folded into q).
+// Scores are kept in log2 units (sm_scale * log2 e applied to the finished
+// dot products).
 //
 // A paged cache (block table, kvq_paged.h) differs only in where a packed
 // chunk sits: its slot comes from the sequence's table row, of which each lane
@@ -90,6 +92,9 @@ struct Raw {
   uint4 kmA, kmB;                     // key (scale, min) of the chunk's group
 };
 
+constexpr float kPlainLog2 = 14.0f;
+constexpr float kPlain = 16384.0f;
+
 template <int D, int BK, int BV, int GQ, int NG, bool PG>
 struct PackedWave {
   using C = Cfg<D, BK, BV, GQ, NG>;
@@ -125,6 +130,7 @@ struct PackedWave {
   f4 oacc[NT];
   float m_run, l_run;
   float m_even, m_odd;  // m_run less the classes' log2 factors (packed chunks)
+  float m_plain;        // m_run - kPlainLog2 (fp16 window weights)
   float l_odd;          // sum of odd-class weights (scaled by kValOdd)
   float bias[NF];       // value-min term; odd class kept apart in bias_odd
   float bias_odd[NF];
@@ -164,6 +170,7 @@ struct PackedWave {
     m_run = kNegInf;
     m_even = kNegInf;
     m_odd = kNegInf;
+    m_plain = kNegInf;
     l_run = 0.0f;
     l_odd = 0.0f;
 #pragma unroll
@@ -390,6 +397,7 @@ struct PackedWave {
     m_run = m_new;
     m_even = m_new - kValEvenLog2<BV>;
     m_odd = m_new - kValOddLog2<BV>;
+    m_plain = m_new - kPlainLog2;
     l_run *= a;
     l_odd *= a;
 #pragma unroll
@@ -426,7 +434,7 @@ struct PackedWave {
           else
             l_odd += pm[k];
         } else {
-          pm[k] = exp2_hw(s[k] - m_run);
+          pm[k] = exp2_hw(s[k] - m_plain);
           l_run += pm[k];
         }
       }
@@ -448,28 +456,33 @@ struct PackedWave {
     }
   }
 
-  // Packed accumulation to real scale (codes were fp16 numbers c * 2^-24,
+  // Packed accumulation to real scale (codes were fp16 numbers c * 2^(L-24),
   // pairs carry kValEven) with its value-min term added; class sums folded.
-  // Afterwards the state is plain (as the residual path needs).
+  // Afterwards the state is plain (as the residual path needs), in units of
+  // kPlain: the fp16 window's weights are 2^(s - m + kPlainLog2), so that
+  // their hi/lo fp16 split keeps the lo part out of the subnormals down to
+  // weights of 2^-17 (a small weight times a large fp16 value would otherwise
+  // carry an absolute error of 2^-25 |v|).  Partials and sums share the
+  // factor, so the combine's ratios are unchanged.
   __device__ __forceinline__ void to_real() {
     // the value-min term is summed over the four lane groups (token subsets)
     float btot[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const float bt = __builtin_fmaf(bias_odd[f], 1.0f / kValOdd<BV>,
-                                      bias[f] * (1.0f / kValEven<BV>));
+      const float bt = __builtin_fmaf(bias_odd[f], kPlain / kValOdd<BV>,
+                                      bias[f] * (kPlain / kValEven<BV>));
       btot[f] = xor_sum(xor_sum(bt, 16), 32);
       bias[f] = 0.0f;
       bias_odd[f] = 0.0f;
     }
-    constexpr float oscale = 16777216.0f / kValEven<BV>;
+    constexpr float oscale = 16777216.0f / float(1 << kCodeLift<BV>) / kValEven<BV> * kPlain;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const float bsum = btot[C::gam(n) / SL];
 #pragma unroll
       for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], oscale, bsum);
     }
-    l_run = __builtin_fmaf(l_odd, 1.0f / kValOdd<BV>, l_run * (1.0f / kValEven<BV>));
+    l_run = __builtin_fmaf(l_odd, kPlain / kValOdd<BV>, l_run * (kPlain / kValEven<BV>));
     l_odd = 0.0f;
     m_even = m_run;
     m_odd = m_run;
@@ -693,23 +706,7 @@ struct PackedWave {
       for (int n = 0; n < NT; ++n) {
         if (C::gam(n) / SL != f) continue;  // compile-time
         uint32_t a[4];
-        if constexpr (BV == 8) {
-          // pair e: word 2n + e/2 shifted down by 8 (e%2), bytes 0 and 2
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] = (r.vw[2 * n + (e >> 1)] >> (8 * (e & 1))) & 0x00FF00FFu;
-        } else if constexpr (BV == 4) {
-          // pair e: (w >> 8 (e/2)) masked at bits 4 (e%2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] = (r.vw[n] >> (8 * (e >> 1))) & ((e & 1) ? 0x00F000F0u : 0x000F000Fu);
-        } else {
-          // tile parity selects the byte; pair e: (w' >> 4 (e/2)) at bits 2 (e%2)
-          const uint32_t x = r.vw[n >> 1] >> (8 * (n & 1));
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] = (x >> (4 * (e >> 1))) & ((e & 1) ? 0x000C000Cu : 0x00030003u);
-        }
+        unpack_value_tile<BV>(r.vw, n, a);
         oacc[n] = mfma(a, bh, oacc[n]);
         oacc[n] = mfma(a, bl, oacc[n]);
       }
@@ -816,7 +813,10 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   const int pc0 = r.pc0, pc1 = r.pc1, rk0 = r.rk0, rk1 = r.rk1;
   R rb;
   // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
-  // that q * 2^-E * scale fits fp16
+  // that q * 2^-E * key scale fits fp16.  The softmax scale (sm_scale log2 e)
+  // is not folded into q: it multiplies the finished scores (kscale, bscale),
+  // so q * 2^-E stays the fp16 query exactly, q' = q 2^-E scale is an exact
+  // 22-bit product and its hi/lo split is exact too.
   int eh[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
@@ -825,7 +825,7 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
     float mx = 0.0f;
 #pragma unroll
     for (int k = 0; k < QPH; ++k) {
-      qv[k] = h2f(qg[lane + 64 * k]) * L.scale_log2;
+      qv[k] = h2f(qg[lane + 64 * k]);
       mx = fmaxf(mx, fabsf(qv[k]));
     }
 #pragma unroll
@@ -846,9 +846,10 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
     if (w.hcol == h) e_mine = eh[h];
-  // codes are the fp16 numbers c * 2^-24, pairs carry the key-side factor
-  w.kscale = ldexpf(1.0f, e_mine + 24 - kKeyAccLog2<BK>);
-  w.bscale = ldexpf(1.0f, e_mine);
+  // codes are the fp16 numbers c * 2^(L - 24), pairs carry the key-side
+  // factor; scores in log2 units
+  w.kscale = ldexpf(L.scale_log2, e_mine + 24 - kKeyAccLog2<BK> - kCodeLift<BK>);
+  w.bscale = ldexpf(L.scale_log2, e_mine);
 
   // rows of query token i (of the last T) do not see the newest T - 1 - i
   // positions; packed chunks holding a position past n - T are processed

@@ -30,11 +30,15 @@ __device__ __forceinline__ f4 mfma(const uint32_t (&a)[4], const uint32_t (&b)[4
                                                 __builtin_bit_cast(h8, bv), c, 0, 0, 0);
 }
 
-// Two floats -> packed fp16 pair, rounded toward zero (hi part of a hi/lo
-// split; the lo part carries the remainder, so the rounding mode of the split
-// does not matter).
-__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+// Two floats -> packed fp16 pair, rounded to nearest even (v_cvt_pk_f16_f32,
+// the same rate as the round-toward-zero form).  Both parts of a hi/lo split
+// are rounded to nearest: the lo part's rounding errors are then half an ulp
+// of it, of either sign, so a weighted sum over many tokens carries no
+// systematic bias (with truncation every weight came out up to 2^-22 low,
+// which over a long context of large values exceeded the tolerance).
+__device__ __forceinline__ uint32_t pk_rne(float a, float b) {
+  const h2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float lo_half(uint32_t v) {
   return (float)__builtin_bit_cast(h2, v)[0];
@@ -50,14 +54,14 @@ __device__ __forceinline__ float opaque_m1() {
   asm volatile("" : "+v"(x));
   return x;
 }
-// hi/lo fp16 split of (a, b): a ~= hi.x + lo.x to ~2^-21 relative.  The
+// hi/lo fp16 split of (a, b): a ~= hi.x + lo.x to ~2^-23 relative.  The
 // remainders a - hi.x are exact fp32 operations, each one v_fma_mix_f32 of
 // the fp16 half (m1 = -1).
 __device__ __forceinline__ void split2(float a, float b, float m1, uint32_t& hi,
                                        uint32_t& lo) {
-  hi = pk_rtz(a, b);
+  hi = pk_rne(a, b);
   const h2 hh = __builtin_bit_cast(h2, hi);
-  lo = pk_rtz(__builtin_fmaf((float)hh[0], m1, a), __builtin_fmaf((float)hh[1], m1, b));
+  lo = pk_rne(__builtin_fmaf((float)hh[0], m1, a), __builtin_fmaf((float)hh[1], m1, b));
 }
 // 2^x on the hardware unit (no range fix-up: results below the fp32 normal
 // range only arise for weights that are negligible next to the running max).
@@ -135,9 +139,9 @@ __device__ __forceinline__ float group_sum(float x) {
 //
 // Value side: the A operand of lane (channel c, lane group g) holds 8 codes of
 // channel c; element j is token 8g + j.  A 4-bit word holds them with element
-// 2e in nibble e and element 2e+1 in nibble 4 + e, so (w >> 4e) & 0x000F000F
-// is the fp16 pair (2e, 2e+1); a 2-bit word holds two channel tiles, tile
-// parity h in bits 8h.., and (w >> (8h + 2e)) & 0x00030003 is the pair.
+// 2e in nibble e and element 2e+1 in nibble 4 + e of the word, i.e. nibble e
+// of its two halves form the fp16 pair (2e, 2e+1); a 2-bit word holds two
+// channel tiles, tile parity h in bits 8h.. of each half (unpack_value_tile).
 // Key side: score tile u row r is token 8 (r/4) + 4u + r%4, so the score
 // tile's output registers (lane group g, register q of tile u) hold tokens
 // 8g + 4u + q: exactly element 4u + q of the value side's B operand, and the
@@ -161,58 +165,127 @@ constexpr int kKeyOff = BK == 2 ? 8 : 4;
 template <int D, int BK>
 constexpr int kKW = (D / 4) * BK / 32;
 
-// Key codes to A-operand pairs with one AND per pair: an odd pair (VGPR v
-// odd) is masked where it sits, two bits (2-bit fields) or four bits (4-bit)
-// above its even neighbour, so it comes out as code * 4 (or * 16) * 2^-24.
-// The query fragments carry the inverse: q' of an even channel is scaled by
-// kKeyEvenQ and of an odd channel by kKeyOddQ (channel parity = pair parity,
-// the runs start at multiples of 4), and every pair then contributes
-// kKeyAcc * code * q'.  The factors keep q' inside fp16 for any fp16 keys
-// (a 4-bit scale is at most 8734, a 2-bit one is not scaled up).  8-bit
-// fields are shifted down to bit 0 of their half before the mask, so every
-// pair is code * 2^-24 and no factor is needed.
-template <int BK> constexpr float kKeyEvenQ = BK == 4 ? 4.0f : 1.0f;
-template <int BK> constexpr float kKeyOddQ = BK == 8 ? 1.0f : 0.25f;
-template <int BK> constexpr int kKeyAccLog2 = BK == 4 ? 2 : 0;
+// Where a code sits inside its fp16 operand.  The matrix core aligns the 32
+// products of an instruction by their operands' nominal exponents before it
+// sums them, and keeps about 27 bits below the largest (measured on gfx950:
+// one wave, exact fp64 sums; C is added with fp32 rounding).  A subnormal's
+// nominal exponent is that of the smallest normal number, 2^-14, whatever its
+// value, so a code at the bottom of the mantissa (c * 2^-24) wastes nearly ten
+// of those bits: products about 18 binades below an instruction's largest
+// already lose bits, which a cache whose scales differ by 2^15 between the
+// tokens (values) or channels (keys) of one chunk reaches.  So every field is
+// moved to the top of the mantissa: a pair comes out as code * 2^(L - 24) *
+// (its class factor below), L = kCodeLift (2-bit fields at bits 6 and 8,
+// 4-bit ones all at bits 6..9, 8-bit ones at bits 2..9), and the 2^L is
+// taken back out by the power-of-two scale applied to the finished sums.
+// (A 4-bit field at bits 2..5 would still sit 2^4 below the nominal exponent,
+// and up to 32 products truncated one way against the largest cost about
+// 2^-18 of it: measured on caches with large value scales.)
+template <int B> constexpr int kCodeLift = B == 8 ? 2 : 6;
 
-// Value side, likewise: the odd pairs of a value word (VGPR e odd: tokens
-// 8g + 2e, 8g + 2e + 1 with e odd, i.e. score registers q = 2, 3) come out of
-// their mask as code * 16 (4-bit) or * 4 (2-bit) * 2^-24.  Their softmax
-// weights are taken 4x smaller (2^(s - m - 2)) and the even pairs' weights
-// kValEven times larger, so every pair contributes kValEven * p * code * dV.
-// (4 * 8734 and 43669 stay inside fp16.)  8-bit pairs are all code * 2^-24:
-// both classes keep factor 1.
-template <int BV> constexpr float kValEven = BV == 4 ? 4.0f : 1.0f;
-template <int BV> constexpr float kValOdd = BV == 8 ? 1.0f : 0.25f;
-template <int BV> constexpr float kValEvenLog2 = BV == 4 ? 2.0f : 0.0f;
-template <int BV> constexpr float kValOddLog2 = BV == 8 ? 0.0f : -2.0f;
+// Key codes to A-operand pairs with one AND per pair: a 2-bit odd pair
+// (VGPR v odd) sits two bits above its even neighbour (the two share one
+// shift), so it comes out as code * 4 * 2^(L - 24); 4-bit and 8-bit pairs all
+// come out as code * 2^(L - 24).  The query fragments carry the inverse and a
+// headroom factor: q' of an even channel is scaled by kKeyEvenQ and of an odd
+// channel by kKeyOddQ (channel parity = pair parity, the runs start at
+// multiples of 4), and every pair then contributes kKeyAcc * 2^L * code * q'.
+// The factors keep q' inside fp16 for any fp16 keys (a scale is at most
+// 43669 at 2 bits, 8734 at 4 and 514 at 8) and as large as that allows, so
+// that the lo fp16 part of q' stays out of the subnormals for small key
+// scales (a lo part in the subnormals has an absolute step that large codes
+// magnify).
+template <int BK> constexpr float kKeyEvenQ = BK == 4 ? 4.0f : BK == 8 ? 64.0f : 1.0f;
+template <int BK> constexpr float kKeyOddQ = BK == 4 ? 4.0f : BK == 8 ? 64.0f : 0.25f;
+template <int BK> constexpr int kKeyAccLog2 = BK == 4 ? 2 : BK == 8 ? 6 : 0;
+
+// Value side, likewise: at 2 bits the odd pairs of a value word (VGPR e odd:
+// tokens 8g + 2e, 8g + 2e + 1 with e odd, i.e. score registers q = 2, 3) come
+// out of their mask as code * 4 * 2^(L - 24); their softmax weights are taken
+// 4x smaller (2^(s - m - 2)), so every pair contributes 2^L * p * code * dV.
+// 4-bit and 8-bit pairs all come out as code * 2^(L - 24) and both classes'
+// weights carry a headroom factor (4 at 4 bits, 64 at 8: 4 * 8734 and
+// 64 * 514 stay inside fp16), which keeps the lo parts of p dV normal.
+template <int BV> constexpr float kValEven = BV == 4 ? 4.0f : BV == 8 ? 64.0f : 1.0f;
+template <int BV> constexpr float kValOdd = BV == 4 ? 4.0f : BV == 8 ? 64.0f : 0.25f;
+template <int BV> constexpr float kValEvenLog2 = BV == 4 ? 2.0f : BV == 8 ? 6.0f : 0.0f;
+template <int BV> constexpr float kValOddLog2 = BV == 4 ? 2.0f : BV == 8 ? 6.0f : -2.0f;
+
+// A word shifted left (k > 0) or right (k < 0) by |k| bits.
+template <int K>
+__device__ __forceinline__ uint32_t shl(uint32_t w) {
+  if constexpr (K >= 0)
+    return w << K;
+  else
+    return w >> (-K);
+}
+// Masks of the lifted fields in both halves of a word: even and odd pairs.
+template <int B> constexpr uint32_t kMaskEven = B == 2 ? 0x00C000C0u : B == 4 ? 0x03C003C0u
+                                                                               : 0x03FC03FCu;
+template <int B> constexpr uint32_t kMaskOdd = B == 2 ? 0x03000300u : B == 4 ? 0x03C003C0u
+                                                                              : 0x03FC03FCu;
 
 template <int D, int BK>
 __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
                                             uint32_t (&a)[D / 32][4]) {
   if constexpr (BK == 2) {
-    // field s of a half: (w >> 4 (s/2)) masked at bits 2 (s%2)
+    // field s of a half (bits 2s) to bit 6 (even s) or 8 (odd s): fields
+    // 2j, 2j + 1 share the shift 6 - 4j
 #pragma unroll
-    for (int wi = 0; wi < kKW<D, BK>; ++wi)
+    for (int wi = 0; wi < kKW<D, BK>; ++wi) {
+      const uint32_t x[4] = {shl<6>(w[wi]), shl<2>(w[wi]), shl<-2>(w[wi]), shl<-6>(w[wi])};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int ri = 8 * wi + s;
-        a[ri >> 2][ri & 3] = (w[wi] >> (4 * (s >> 1))) & ((s & 1) ? 0x000C000Cu : 0x00030003u);
+        a[ri >> 2][ri & 3] = x[s >> 1] & ((s & 1) ? kMaskOdd<2> : kMaskEven<2>);
       }
+    }
   } else if constexpr (BK == 4) {
-    // field s of a half: (w >> 8 (s/2)) masked at bits 4 (s%2)
+    // nibble s of a half (bits 4s) to bits 6..9
 #pragma unroll
-    for (int wi = 0; wi < kKW<D, BK>; ++wi)
+    for (int wi = 0; wi < kKW<D, BK>; ++wi) {
+      const uint32_t x[4] = {shl<6>(w[wi]), shl<2>(w[wi]), shl<-2>(w[wi]), shl<-6>(w[wi])};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        a[wi][s] = (w[wi] >> (8 * (s >> 1))) & ((s & 1) ? 0x00F000F0u : 0x000F000Fu);
+      for (int s = 0; s < 4; ++s) a[wi][s] = x[s] & kMaskEven<4>;
+    }
   } else {
-    // k-chunk kc from words 2kc + (s/2): pair s is that word >> 8 (s%2),
-    // bytes 0 and 2 of the result
+    // k-chunk kc from words 2kc + (s/2): pair s is bytes 0, 2 (s even) or
+    // 1, 3 (s odd) of that word, moved to bits 2..9 of each half
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[kc][s] = (w[2 * kc + (s >> 1)] >> (8 * (s & 1))) & 0x00FF00FFu;
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t wv = w[2 * kc + (s >> 1)];
+        a[kc][s] = ((s & 1) ? shl<-6>(wv) : shl<2>(wv)) & kMaskEven<8>;
+      }
+  }
+}
+
+// The A operand of value channel tile n (pairs e = 0..3: tokens 2e, 2e + 1 of
+// the lane group) from a lane's value code words vw (layout 3):
+//   bV = 4: word n, token pair e in nibble e of each half -> bits 6..9;
+//   bV = 2: word n/2, tile parity h = n % 2, pair e at bits 8h + 2e -> bit 6
+//           (even e) or 8 (odd e); pairs 2j, 2j + 1 share the shift 6 - 4j - 8h;
+//   bV = 8: words 2n + e/2, pair e in bytes (0, 2) or (1, 3) -> bits 2..9.
+template <int BV, int NW>
+__device__ __forceinline__ void unpack_value_tile(const uint32_t (&vw)[NW], int n,
+                                                  uint32_t (&a)[4]) {
+  if constexpr (BV == 4) {
+    const uint32_t x[4] = {shl<6>(vw[n]), shl<2>(vw[n]), shl<-2>(vw[n]), shl<-6>(vw[n])};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = x[e] & kMaskEven<4>;
+  } else if constexpr (BV == 2) {
+    const uint32_t w = vw[n >> 1];
+    const uint32_t x0 = (n & 1) ? shl<-2>(w) : shl<6>(w);
+    const uint32_t x1 = (n & 1) ? shl<-6>(w) : shl<2>(w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = (e < 2 ? x0 : x1) & ((e & 1) ? kMaskOdd<2> : kMaskEven<2>);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = vw[2 * n + (e >> 1)];
+      a[e] = ((e & 1) ? shl<-6>(w) : shl<2>(w)) & kMaskEven<8>;
+    }
   }
 }
 
