@@ -30,18 +30,25 @@ def packed_len(n: int, residual: int) -> int:
 
 
 def decode_step_bytes(seq_lens, n_q_heads: int, n_kv_heads: int, head_dim: int,
-                      k_bits: int, v_bits: int, group: int, residual: int) -> float:
+                      k_bits: int, v_bits: int, group: int, residual: int,
+                      residual_v: int | None = None) -> float:
     """Algorithmic bytes of one decode-attention launch over sequences of the
-    given lengths (current token included)."""
-    per_packed = packed_bytes_per_token(head_dim, k_bits, v_bits, group)
+    given lengths (current token included).  residual is the key window;
+    residual_v the value window (default: the same)."""
+    D, G = head_dim, group
+    Rk = residual
+    Rv = residual if residual_v is None else residual_v
+    key_tok = D * k_bits / 8 + 4 * D / G      # codes + (scale, min) per channel / G
+    val_tok = D * v_bits / 8 + 4 * D / G      # codes + (scale, min) per group of G
     total = 0.0
     for n in np.asarray(seq_lens).tolist():
-        lq = packed_len(int(n), residual)
-        r = int(n) - lq
-        total += n_kv_heads * (lq * per_packed + r * fp16_bytes_per_token(head_dim))
+        n = int(n)
+        lk, lv = packed_len(n, Rk), packed_len(n, Rv)
+        total += n_kv_heads * (lk * key_tok + (n - lk) * 2 * D
+                               + lv * val_tok + (n - lv) * 2 * D)
     B = len(np.asarray(seq_lens))
-    total += 2 * 2 * B * n_q_heads * head_dim      # q in, out
-    total += 4 * B                                  # seq_lens
+    total += 2 * 2 * B * n_q_heads * D       # q in, out
+    total += 4 * B                            # seq_lens
     return total
 
 
@@ -51,12 +58,16 @@ def append_bytes(batch: int, n_kv_heads: int, head_dim: int) -> int:
 
 
 def flush_bytes(n_flush_units: int, residual: int, head_dim: int, k_bits: int,
-                v_bits: int, group: int) -> float:
-    """Bytes of flushing R residual tokens of n units: fp16 window read, packed
-    rows written."""
-    return n_flush_units * residual * (
-        fp16_bytes_per_token(head_dim)
-        + packed_bytes_per_token(head_dim, k_bits, v_bits, group))
+                v_bits: int, group: int, residual_v: int | None = None) -> float:
+    """Bytes of flushing full residual windows of n units: the fp16 window
+    read, the packed rows written.  With separate windows (residual for keys,
+    residual_v for values) this counts one flush of each."""
+    D, G = head_dim, group
+    Rk = residual
+    Rv = residual if residual_v is None else residual_v
+    key_tok = D * k_bits / 8 + 4 * D / G
+    val_tok = D * v_bits / 8 + 4 * D / G
+    return n_flush_units * (Rk * (2 * D + key_tok) + Rv * (2 * D + val_tok))
 
 
 # ---- rotated per-token 2-bit format ([KV1] Quantization Format) ------------

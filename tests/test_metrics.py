@@ -80,3 +80,21 @@ def test_decode_step_bytes_of_the_benchmarked_workload():
     got = metrics.decode_step_bytes(n, 32, 8, 128, 2, 4, 32, 128)
     per_head = 8064 * (32 + 64 + 16 + 16) + 128 * 512
     assert got == 32 * 8 * per_head + 4 * 32 * 32 * 128 + 4 * 32
+
+
+def test_separate_key_and_value_windows():
+    """Key window 128, value window 64 at n = 8192 (B32, 32/8, D128, K2/V4,
+    G32): keys hold 8064 packed + 128 fp16 tokens, values 8128 packed + 64 fp16
+    tokens.  Packed key token: 32 code bytes + 4 * 128 / 32 meta bytes; packed
+    value token: 64 code bytes + 16 meta bytes; an fp16 K or V row is 256
+    bytes."""
+    n = [8192] * 32
+    got = metrics.decode_step_bytes(n, 32, 8, 128, 2, 4, 32, 128, residual_v=64)
+    per_head = 8064 * 48 + 128 * 256 + 8128 * 80 + 64 * 256
+    assert got == 32 * 8 * per_head + 4 * 32 * 32 * 128 + 4 * 32
+    # one window each: the same as the single-window call
+    assert metrics.decode_step_bytes(n, 32, 8, 128, 2, 4, 32, 128, residual_v=128) == \
+        metrics.decode_step_bytes(n, 32, 8, 128, 2, 4, 32, 128)
+    # flushing one unit: 128 key rows read (256 B) and packed (48 B), 64 value rows (256 + 80 B)
+    assert metrics.flush_bytes(1, 128, 128, 2, 4, 32, residual_v=64) == 128 * 304 + 64 * 336
+    assert metrics.flush_bytes(3, 128, 128, 2, 4, 32) == 3 * 128 * (512 + 128)
