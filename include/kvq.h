@@ -342,6 +342,28 @@ int kvq_decode_combine(const kvq_geom *geom, const uint16_t *q,
                        const void *workspace, size_t workspace_bytes,
                        uint16_t *out, void *stream);
 
+/* kvq_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as kvq_decode_attn (the same kernels, bit for
+ * bit), but the split partials go to a static device array of the library,
+ * KVQ_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first call on a
+ * device until the process ends.  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.
+ *   A geometry whose partials need more than KVQ_NOALLOC_SCRATCH_BYTES
+ *   (kvq_decode_workspace_bytes) fails with KVQ_ERR_WORKSPACE before any
+ *   launch; use kvq_decode_attn with a workspace for it.
+ *   Nothing in the array needs to start at zero: every partial the combine
+ *   reads is written by the same call's partial kernel first, and the array
+ *   keeps the last call's contents.
+ *   Every call on one GPU shares that GPU's array: calls on one stream are
+ *   ordered, but calls that overlap on one GPU (two streams, two threads, two
+ *   captured graphs replayed concurrently) race and give wrong results. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int kvq_decode_attn_noalloc(const kvq_geom *geom, const uint16_t *q,
+                            const kvq_cache *cache, const int32_t *seq_lens,
+                            int32_t max_seq_len, float sm_scale, uint16_t *out,
+                            void *stream);
+
 /* ----- several query tokens per sequence ----------------------------------- */
 
 /* Attention of the last T positions of every sequence at once (verification

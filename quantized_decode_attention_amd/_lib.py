@@ -34,6 +34,7 @@ KVQ_ERR_WORKSPACE = -5
 KVQ_ERR_RANGE = -6
 KVQ_ERR_HIP = -7
 KVQ_ERR_INTERNAL = -8
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = [
     "kvq_abi_version", "kvq_layout_version", "kvq_status_str", "kvq_last_error",
@@ -41,7 +42,7 @@ EXPORTS = [
     "kvq_decode_workspace_bytes", "kvq_quantize_keys_perchannel",
     "kvq_quantize_values_pertoken", "kvq_prefill", "kvq_append", "kvq_append_tokens",
     "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_combine",
-    "kvq_decode_multi_workspace_bytes", "kvq_decode_attn_multi",
+    "kvq_decode_multi_workspace_bytes", "kvq_decode_attn_multi", "kvq_decode_attn_noalloc",
 ]
 EXPORTS_BQ2 = [
     "kvq_bq2_validate_geom", "kvq_bq2_cache_bytes", "kvq_bq2_decode_workers",
@@ -139,6 +140,7 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_attn": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_partial": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
             "kvq_decode_combine": (ctypes.c_int, [G, P, C, P, i32, ctypes.c_float, P, sz, P, P]),
+            "kvq_decode_attn_noalloc": (ctypes.c_int, [G, P, C, P, i32, f32, P, P]),
             "kvq_decode_multi_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
             "kvq_decode_attn_multi": (ctypes.c_int, [G, P, C, P, i32, i32, f32, P, sz, P, P]),
             "kvq_bq2_validate_geom": (ctypes.c_int, [G2]),
@@ -382,6 +384,19 @@ def kvq_decode_attn(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tens
                     out: torch.Tensor, stream=None) -> None:
     args, keep = _decode_args(g, q, cache, seq_lens, max_seq_len, sm_scale, workspace, out)
     _check(lib().kvq_decode_attn(*args, _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_decode_attn_noalloc(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,
+                            max_seq_len: int, sm_scale: float, out: torch.Tensor,
+                            stream=None) -> None:
+    """kvq_decode_attn with the library's static partials buffer (no workspace)."""
+    gc = g.c()
+    cc = _cache_arg(cache)
+    _check(lib().kvq_decode_attn_noalloc(
+        ctypes.byref(gc), _ptr(q, "q", _F16, (g.batch, g.n_q_heads, g.head_dim)),
+        ctypes.byref(cc), _ptr(seq_lens, "seq_lens", _I32, (g.batch,)), int(max_seq_len),
+        float(sm_scale), _ptr(out, "out", _F16, (g.batch, g.n_q_heads, g.head_dim)),
+        _stream(stream)), "kvq_decode_attn_noalloc")
 
 
 def kvq_decode_partial(g: Geom, q: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,

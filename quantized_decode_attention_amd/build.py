@@ -33,6 +33,7 @@ UNITS = [
     ("kvq_bq2_decode", "kvq_bq2_decode.hip", MFMA_VGPR),
     ("kvq_api", "kvq_api.cpp", []),
     ("kvq_probe", "kvq_probe.hip", []),
+    ("kvq_noalloc", "kvq_noalloc.hip", []),
 ]
 # the decode partial kernels: one instantiation set per head dim, key bits and
 # cache form, each its own object (they compile in parallel)

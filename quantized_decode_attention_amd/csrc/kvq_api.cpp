@@ -585,6 +585,37 @@ int kvq_decode_attn(const kvq_geom* geom, const uint16_t* q, const kvq_cache* ca
                             workspace_bytes, out, stream);
 }
 
+int kvq_decode_attn_noalloc(const kvq_geom* geom, const uint16_t* q, const kvq_cache* cache,
+                            const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                            uint16_t* out, void* stream) {
+  try {
+    int st = check_geom(geom);
+    if (st != KVQ_OK) return st;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    hipError_t e = kvq::noalloc_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    int32_t n_workers = 0;
+    if ((st = workers_for(geom, &n_workers)) != KVQ_OK) return st;
+    const size_t need = workspace_need(geom, n_workers);
+    if (need > ws_bytes)
+      return fail(KVQ_ERR_WORKSPACE,
+                  "kvq_decode_attn_noalloc: this geometry's partials need %zu bytes, beyond "
+                  "the library's %zu-byte static buffer (use kvq_decode_attn with a workspace)",
+                  need, ws_bytes);
+    kvq::DecodeLaunch L;
+    st = decode_setup(geom, q, cache, seq_lens, max_seq_len, sm_scale, ws, ws_bytes, out, &L);
+    if (st != KVQ_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    e = kvq::launch_decode_partial(L, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+    e = kvq::launch_decode_combine(L, s);
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "decode_combine launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 int kvq_bq2_validate_geom(const kvq_bq2_geom* geom) {
   try {
     return check_bq2_geom(geom);

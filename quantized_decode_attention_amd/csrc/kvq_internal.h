@@ -169,6 +169,10 @@ hipError_t bq2_decode_workers(const Bq2Geom& g, int cus, int* workers);
 hipError_t launch_bq2_decode_partial(const Bq2Launch& L, hipStream_t st);
 hipError_t launch_bq2_decode_combine(const Bq2Launch& L, hipStream_t st);
 
+// ---- kvq_decode_attn_noalloc's partials (kvq_noalloc.hip) -----------------
+// This device's copy of the library's static partials array and its size.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // ---- measurement aid (kvq_probe.h) ----------------------------------------
 int probe_sink_words();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);

@@ -303,3 +303,11 @@ def test_build_scratch_guard_reads_the_resource_remarks():
     assert build.scratch_kernels(remarks) == [
         ("_ZN3kvq12_GLOBAL__N_118bq2_partial_kernelILi4E", 28)]
     assert build.scratch_kernels(remarks.replace(": 28", ": 0")) == []
+
+
+def test_noalloc_buffer_size_matches_the_header():
+    """The binding's copy of KVQ_NOALLOC_SCRATCH_BYTES is the header's."""
+    text = open(HEADER).read()
+    m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "KVQ_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
