@@ -68,6 +68,9 @@ def parse():
                         "least 10 replays)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--probe-sweep", action="store_true",
+                   help="only sweep the plain stream-read probe over waves per SIMD, loads "
+                        "in flight per lane and nontemporal loads; prints one JSON line")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (5 times); used to "
                         "calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -665,6 +668,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
+
+    if a.probe_sweep:
+        shapes = [(wps, loads, nt) for nt in (0, 1) for wps in (1, 2, 3, 4, 8)
+                  for loads in (1, 2, 4, 8, 16) if not (loads == 16 and wps > 3)]
+        res = kvq.stream_read_sweep(shapes)
+        best = max(res, key=lambda r: r["gbs"])
+        print(json.dumps({"probe": "kvq_probe_stream_read_sweep, 2 GiB buffer",
+                          "best": best, "default_probe": kvq.stream_read_gbs(),
+                          "sweep": res}), flush=True)
         return
 
     w = synth.WORKLOADS[a.config]

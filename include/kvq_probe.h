@@ -24,6 +24,18 @@ int kvq_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *s
 /* Entries sink must hold. */
 int kvq_probe_sink_words(int32_t *words);
 
+/* The same read in a chosen launch shape, for sweeping the read rate against
+ * the bytes a wave keeps in flight: waves_per_simd x 4 x (compute units)
+ * single-wave workgroups (1 <= waves_per_simd <= 8), each reading one
+ * contiguous share in batches of loads_per_lane (1, 2, 4, 8 or 16) 16-byte
+ * loads per lane, with the next batch requested before the current one is
+ * used; nontemporal != 0 makes them nontemporal loads.  Waves beyond what
+ * the GPU keeps resident run after the first ones finish.  Status codes and
+ * sink as kvq_probe_stream_read. */
+int kvq_probe_stream_read_sweep(const void *buf, size_t bytes, uint32_t *sink,
+                                int32_t waves_per_simd, int32_t loads_per_lane,
+                                int32_t nontemporal, void *stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -54,7 +54,7 @@ EXPORTS_PAGED = [
     "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_append_tokens", "kvq_paged_decode_attn",
     "kvq_paged_decode_partial", "kvq_paged_decode_combine", "kvq_paged_decode_attn_multi",
 ]
-EXPORTS_PROBE = ["kvq_probe_stream_read", "kvq_probe_sink_words"]
+EXPORTS_PROBE = ["kvq_probe_stream_read", "kvq_probe_sink_words", "kvq_probe_stream_read_sweep"]
 BQ2_HEAD_DIM = 64
 BQ2_SINKS = 4
 
@@ -113,6 +113,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "kvq_probe_stream_read": (ctypes.c_int, [P, sz, P, P]),
             "kvq_probe_sink_words": (ctypes.c_int, [ctypes.POINTER(i32)]),
+            "kvq_probe_stream_read_sweep": (ctypes.c_int, [P, sz, P, i32, i32, i32, P]),
             "kvq_paged_validate": (ctypes.c_int, [G, CP]),
             "kvq_paged_cache_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
             "kvq_paged_decode_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
@@ -637,6 +638,37 @@ def stream_read_gbs(nbytes: int = 2 << 30, reps: int = 20, device="cuda") -> dic
     t = float(np.median(times))
     return {"gbs": round(nbytes / t / 1e9, 1), "bytes": nbytes, "reps": reps,
             "median_us": round(t * 1e6, 2)}
+
+
+def stream_read_sweep(shapes, nbytes: int = 2 << 30, reps: int = 10, device="cuda") -> list:
+    """HBM read rate of kvq_probe_stream_read_sweep for each (waves_per_simd,
+    loads_per_lane, nontemporal) in shapes: the median of reps reads of nbytes
+    (HIP events around each).  A measurement aid."""
+    words = ctypes.c_int32()
+    _check(lib().kvq_probe_sink_words(ctypes.byref(words)), "kvq_probe_sink_words")
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    sink = torch.zeros(words.value, dtype=torch.int32, device=device)
+    st = torch.cuda.current_stream()
+    out = []
+    for wps, loads, nt in shapes:
+        times = []
+        for r in range(reps + 2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            _check(lib().kvq_probe_stream_read_sweep(
+                ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                int(wps), int(loads), int(nt), ctypes.c_void_p(st.cuda_stream)),
+                "kvq_probe_stream_read_sweep")
+            b.record(st)
+            b.synchronize()
+            if r >= 2:
+                times.append(a.elapsed_time(b) / 1e3)
+        t = float(np.median(times))
+        out.append({"waves_per_simd": wps, "loads_per_lane": loads, "nontemporal": bool(nt),
+                    "bytes_in_flight_per_wave": [64 * 16 * loads, 2 * 64 * 16 * loads],
+                    "gbs": round(nbytes / t / 1e9, 1), "median_us": round(t * 1e6, 2)})
+    del buf
+    return out
 
 
 def alloc_workspace(g: Geom, max_seq_len: int, device="cuda") -> torch.Tensor | None:

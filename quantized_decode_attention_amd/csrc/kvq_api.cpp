@@ -955,4 +955,32 @@ int kvq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* s
   }
 }
 
+int kvq_probe_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink,
+                                int32_t waves_per_simd, int32_t loads_per_lane,
+                                int32_t nontemporal, void* stream) {
+  try {
+    int st = check_ptr(buf, "buf");
+    if (st != KVQ_OK) return st;
+    if ((st = check_ptr(sink, "sink")) != KVQ_OK) return st;
+    if (bytes == 0 || bytes % 16 != 0)
+      return fail(KVQ_ERR_RANGE, "bytes (%zu) must be a positive multiple of 16", bytes);
+    if (waves_per_simd < 1 || waves_per_simd > 8)
+      return fail(KVQ_ERR_RANGE, "waves_per_simd (%d) must be in [1, 8]", waves_per_simd);
+    const int L = loads_per_lane;
+    if (L != 1 && L != 2 && L != 4 && L != 8 && L != 16)
+      return fail(KVQ_ERR_RANGE, "loads_per_lane (%d) must be 1, 2, 4, 8 or 16", L);
+    int cus = 0;
+    if ((st = cu_count(&cus)) != KVQ_OK) return st;
+    const int waves = waves_per_simd * 4 * cus;
+    if (waves > kvq::probe_sink_words())
+      return fail(KVQ_ERR_RANGE, "%d waves exceed the sink's %d words", waves,
+                  kvq::probe_sink_words());
+    hipError_t e = kvq::launch_stream_read_sweep(buf, bytes, sink, waves, L, nontemporal != 0,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "stream read sweep launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 }  // extern "C"

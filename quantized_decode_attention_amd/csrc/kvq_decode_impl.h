@@ -64,33 +64,52 @@ struct Cfg {
   // a lane's fold items are lane + 64 i: with IPH dividing 64 they all cover
   // the same channels (item modulo IPH), so one key-meta load serves them all
   static_assert(64 % IPH == 0, "fold items of a lane must share their channels");
-  // With two or more value-side fragments (8 or 16 rows per KV head) each lane
-  // group would hold every group's (scale, min) of its 8 tokens in registers,
-  // 16 lanes alike.  Instead each lane loads NG / 2 distinct words of the
-  // chunk's value meta and stages them in LDS; a fragment reads its 8 words
-  // back when its weights are formed.
   static constexpr bool VL = NF >= 2;
-  static constexpr int VLW = VL ? NG / 2 : 1;  // staged value-meta words per lane
+  // A chunk's LDS slot, the destination of its direct loads: key codes, value
+  // codes, value meta, then the key meta of the chunk's key group, each in the
+  // cache's byte order, so every lane reads back exactly the words it would
+  // have loaded (byte offsets kSlot*).  A ring of kRing slots per wave: while
+  // one chunk is used, the loads of the next kRing - 1 are in flight.
+  static constexpr int KB = 4 * D * BK, VB = 4 * D * BV, VMB = 128 * NG, KMB = 4 * D;
+  static constexpr int kSlotV = KB, kSlotVM = KB + VB, kSlotKM = KB + VB + VMB;
+  static constexpr int kSlot = KB + VB + VMB + KMB;
+  static constexpr int NI = (KB + 1023) / 1024 + (VB + 1023) / 1024 + (VMB + 1023) / 1024 +
+                            (KMB + 1023) / 1024;  // direct loads per chunk
+  static_assert(NI <= 20, "vmcnt must hold the ring's loads");
   // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ] (+ a
-  // spare), the staged value meta [4][NG][8] words
-  static constexpr int kQB = 2 * GQ * 4 * KC * 16;
-  static constexpr int kBetaB = 16 * ((GQ * 4 + 4 + 15) / 16);
-  static constexpr int kVmB = VL ? 4 * NG * 8 * 4 : 0;
-  static constexpr int kWaveLds = kQB + kBetaB + kVmB;
+  // spare), two chunk slots
+  // With one MFMA column per row (16 rows per KV head) every lane forms its
+  // own q' fragments and no staging is needed.
+  static constexpr bool kDirectFold = SL == 1;
+  static constexpr int kQB = kDirectFold ? 0 : 2 * GQ * 4 * KC * 16;
+  static constexpr int kBetaB = kDirectFold ? 0 : 16 * ((GQ * 4 + 4 + 15) / 16);
+  static constexpr int kRing = 2;
+  static constexpr int kWaveLds = kQB + kBetaB + kRing * kSlot;
   static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
 };
 
-// Loads of one 32-token chunk (a lane's share).
+// The LDS slot a 32-token chunk is loaded into (Cfg::kSlot bytes).
 template <int D, int BK, int BV, int GQ, int NG>
 struct Raw {
-  using C = Cfg<D, BK, BV, GQ, NG>;
-  uint32_t kw[2][C::KW];              // key code words of score tiles 0, 1
-  uint32_t vw[C::NW];                 // value code words (tile n: word n*BV/4)
-  uint32_t vmA[C::VL ? 1 : C::NF][4], vmB[C::VL ? 1 : C::NF][4];  // value (scale, min)
-                                      // of the B elements (direct)
-  uint32_t vml[C::VLW];               // or this lane's share of them (staged)
-  uint4 kmA, kmB;                     // key (scale, min) of the chunk's group
+  uint32_t* s;
 };
+
+// N consecutive words from LDS (N = 1, 2, 4, 8 or 16; 4 N-byte aligned up to 16).
+template <int N>
+__device__ __forceinline__ void lds_words(const uint32_t* p, uint32_t (&w)[N]) {
+  if constexpr (N == 1) {
+    w[0] = p[0];
+  } else if constexpr (N == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+      w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
+  }
+}
 
 constexpr float kPlainLog2 = 14.0f;
 constexpr float kPlain = 16384.0f;
@@ -115,9 +134,10 @@ struct PackedWave {
   const float* qfs;
   uint4* qB;
   float* beta_l;
-  uint32_t* vm_l;  // staged value meta (8 or 16 rows per KV head)
+  uint32_t* ring;  // the wave's chunk slots
   // lane constants
   int lane, col, lg, hcol, slot;
+  uint32_t lane16;     // 16 * lane: a lane's piece of a direct load
   int kofs, vofs;      // this lane's key / value words inside a chunk
   int vmofs[NF];       // value meta run of fragment f inside a chunk
   int kmofs;           // key meta run of this lane's fold items inside a group
@@ -146,6 +166,7 @@ struct PackedWave {
 
   __device__ void init(int lane_) {
     lane = lane_;
+    lane16 = 16u * (uint32_t)lane_;
     m1 = opaque_m1();
     col = lane & 15;
     lg = lane >> 4;
@@ -217,69 +238,96 @@ struct PackedWave {
     }
   }
 
+  // Issues chunk ch's direct loads into slot r: the codes nontemporal (they
+  // stream through once), the meta plain (a key group's meta is read by each
+  // of its chunks).  Earlier reads of the slot are finished first.
   __device__ __forceinline__ void load(int ch, R& r) {
     const int64_t sl = slot_of(ch);
-    {
-      uint32_t w[2 * KW];
-      load_run<2 * KW>(kcodes + sl * (D * BK) + kofs, w);
-#pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        r.kw[0][k] = w[k];
-        r.kw[1][k] = w[KW + k];
-      }
-    }
-    load_run<C::NW>(vcodes + sl * (D * BV) + vofs, r.vw);
-    // value (scale, min) of tokens 8 lg + j: even j feed B elements 2i (run
-    // A), odd j elements 2i + 1 (run B)
-    const uint32_t* vm = vmeta + sl * (4 * NG * 8);
-    if constexpr (C::VL) {
-      if constexpr (C::VLW == 1)
-        r.vml[0] = vm[lane];
-      else
-        load_run<C::VLW>(vm + lane * C::VLW, r.vml);
-    } else {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        uint32_t w[8];
-        load_run<8>(vm + vmofs[f], w);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          r.vmA[f][i] = w[2 * i];
-          r.vmB[f][i] = w[2 * i + 1];
-        }
-      }
-    }
-    // key meta of the chunk's group, with the chunk's other loads (one
-    // in-order stream, so waiting for a chunk never waits for a later one).
-    // Entry e of an item is channel run A + e/2 (even e) or run B + e/2 (odd).
-    // Lanes past the fold items load an in-range run too (the run depends on
-    // the item modulo a head's items): no load sits under a branch.
-    const uint32_t* km = kmeta + (sl * kChunk) / G * D;
-    {
-      uint32_t w[8];
-      load_run<8>(km + kmofs, w);
-      r.kmA = make_uint4(w[0], w[2], w[4], w[6]);
-      r.kmB = make_uint4(w[1], w[3], w[5], w[7]);
-    }
+    const char* kc = reinterpret_cast<const char*>(kcodes + sl * (D * BK));
+    const char* vc = reinterpret_cast<const char*>(vcodes + sl * (D * BV));
+    const char* vm = reinterpret_cast<const char*>(vmeta + sl * (4 * NG * 8));
+    const char* km = reinterpret_cast<const char*>(kmeta + (sl * kChunk) / G * D);
+    const uint32_t base = lds_addr(r.s);
+    lds_dma_begin();
+    lds_copy<C::KB, true>(kc, base, lane16, lane);
+    lds_copy<C::VB, true>(vc, base + C::kSlotV, lane16, lane);
+    lds_copy<C::VMB, false>(vm, base + C::kSlotVM, lane16, lane);
+    lds_copy<C::KMB, false>(km, base + C::kSlotKM, lane16, lane);
   }
 
-  // Staged value meta: this lane's words of the chunk to LDS (before the
-  // scores, so that the write is long done when packed_values reads them).
-  __device__ __forceinline__ void stage_vmeta(const R& r) {
-    if constexpr (C::VL) {
-      if constexpr (C::VLW == 1)
-        vm_l[lane] = r.vml[0];
-      else
-        *reinterpret_cast<uint2*>(vm_l + 2 * lane) = make_uint2(r.vml[0], r.vml[1]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+  // Waits until every chunk loaded but the last `ahead` is in its slot.
+  template <int ahead>
+  __device__ __forceinline__ void wait_chunks() const {
+    wait_vm<ahead * C::NI>();
   }
+  // Slot i of the ring (0 <= i < kRing).
+  __device__ __forceinline__ R slot_at(int i) const { return R{ring + i * (C::kSlot / 4)}; }
 
   // q' = q * 2^-E * key scale (hi/lo fp16 fragments in LDS) and beta' =
   // q * 2^-E . key min, for the key group starting in this chunk.
+  // One fold item: channel runs A (qa, ma) and B (qb, mb) of 4 pairs each ->
+  // the hi and lo fp16 pairs of q' and this item's part of beta.
+  __device__ __forceinline__ float fold_item(const float4& qa, const float4& qb, const uint4& ma,
+                                             const uint4& mb, uint32_t (&hp)[4],
+                                             uint32_t (&lp)[4]) const {
+    const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qBv[4] = {qb.x, qb.y, qb.z, qb.w};
+    const uint32_t mA[4] = {ma.x, ma.y, ma.z, ma.w};
+    const uint32_t mB[4] = {mb.x, mb.y, mb.z, mb.w};
+    float beven = 0.0f, bodd = 0.0f;  // odd channels (their q' carries kKeyOddQ)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), m1, hp[e], lp[e]);
+      if (e & 1) {
+        bodd = mul_hi(qA[e], mA[e], bodd);
+        bodd = mul_hi(qBv[e], mB[e], bodd);
+      } else {
+        beven = mul_hi(qA[e], mA[e], beven);
+        beven = mul_hi(qBv[e], mB[e], beven);
+      }
+    }
+    // beta = q . min with the channel factors taken back out
+    return __builtin_fmaf(bodd, 1.0f / kKeyOddQ<BK>, beven * (1.0f / kKeyEvenQ<BK>));
+  }
+
+  // Direct form (one column per row): lane (row hcol, lane group lg) forms the
+  // items (hcol, lg, kc) it consumes itself; beta sums over the lane groups.
+  __device__ __forceinline__ void fold_direct(const R& r) {
+    float bsum = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int rr = lg * KC + kc;  // the item's run in the group's meta
+      uint32_t w[8];
+      lds_words<8>(r.s + C::kSlotKM / 4 + rr * 8, w);
+      const int ca = key_run0<D, BK>(lg, kc), cb = ca + kKeyOff<BK>;
+      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + ca);
+      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * D + cb);
+      uint32_t hp[4], lp[4];
+      bsum += fold_item(qa, qb, make_uint4(w[0], w[2], w[4], w[6]),
+                        make_uint4(w[1], w[3], w[5], w[7]), hp, lp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bq[0][kc][i] = hp[i];
+        bq[1][kc][i] = lp[i];
+      }
+    }
+    beta_c = xor_sum(xor_sum(bsum, 16), 32) * bscale;
+  }
+
   __device__ __forceinline__ void fold(const R& r) {
+    if constexpr (C::kDirectFold) {
+      fold_direct(r);
+      return;
+    }
+    // key meta of the group: entry e of an item is channel run A + e/2 (even
+    // e) or run B + e/2 (odd); lanes past the fold items read an in-range run
+    // too (the run depends on the item modulo a head's items)
+    uint4 kmA, kmB;
+    {
+      uint32_t w[8];
+      lds_words<8>(r.s + C::kSlotKM / 4 + kmofs, w);
+      kmA = make_uint4(w[0], w[2], w[4], w[6]);
+      kmB = make_uint4(w[1], w[3], w[5], w[7]);
+    }
 #pragma unroll
     for (int i = 0; i < IPL; ++i) {
       const int it = fitem[i];
@@ -289,24 +337,8 @@ struct PackedWave {
         const int h = it / IPH, rr = it % IPH, gg = rr / KC, kc = rr % KC;
         const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[0]);
         const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[1]);
-        const float qA[4] = {qa.x, qa.y, qa.z, qa.w}, qBv[4] = {qb.x, qb.y, qb.z, qb.w};
-        const uint32_t mA[4] = {r.kmA.x, r.kmA.y, r.kmA.z, r.kmA.w};
-        const uint32_t mB[4] = {r.kmB.x, r.kmB.y, r.kmB.z, r.kmB.w};
         uint32_t hp[4], lp[4];
-        float bodd = 0.0f;  // odd channels (their q' carries kKeyOddQ)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          split2(mul_lo(qA[e], mA[e]), mul_lo(qBv[e], mB[e]), m1, hp[e], lp[e]);
-          if (e & 1) {
-            bodd = mul_hi(qA[e], mA[e], bodd);
-            bodd = mul_hi(qBv[e], mB[e], bodd);
-          } else {
-            bpart = mul_hi(qA[e], mA[e], bpart);
-            bpart = mul_hi(qBv[e], mB[e], bpart);
-          }
-        }
-        // beta = q . min with the channel factors taken back out
-        bpart = __builtin_fmaf(bodd, 1.0f / kKeyOddQ<BK>, bpart * (1.0f / kKeyEvenQ<BK>));
+        bpart = fold_item(qa, qb, kmA, kmB, hp, lp);
         qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
         qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
       }
@@ -614,7 +646,6 @@ struct PackedWave {
   // accumulators are still at code scale), values from the codes.
   __device__ __forceinline__ void process_mixed_values(int ch, const R& r, int n_tok, int Rk,
                                                        const uint16_t* kres) {
-    stage_vmeta(r);
     float s[NS];
     window_scores(ch * kChunk, n_tok, Rk, kres, s);
     float p[2][4];
@@ -627,7 +658,6 @@ struct PackedWave {
   // are real cache data, so their weight 0 is exact).
   template <bool kMask = false>
   __device__ __forceinline__ void process(int ch, const R& r, int last_vis = 0) {
-    stage_vmeta(r);
     float s[NS];
     packed_scores<kMask>(ch, r, last_vis, s);
     float p[2][4];
@@ -651,11 +681,21 @@ struct PackedWave {
         fold(r);
       }
     }
+    uint32_t kw[2][KW];
+    {
+      uint32_t w[2 * KW];
+      lds_words<2 * KW>(r.s + kofs, w);
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        kw[0][k] = w[k];
+        kw[1][k] = w[KW + k];
+      }
+    }
     f4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t a[KC][4];
-      unpack_keys<D, BK>(r.kw[u], a);
+      unpack_keys<D, BK>(kw[u], a);
       acc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
@@ -676,20 +716,18 @@ struct PackedWave {
   // Weighted sum of a packed chunk's values (code-scale accumulators, weights
   // in the packed classes) and its value-min term.
   __device__ __forceinline__ void packed_values(const R& r, const float (&p)[2][4]) {
+    uint32_t vw[C::NW];
+    lds_words<C::NW>(r.s + C::kSlotV / 4 + vofs, vw);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
+      // value (scale, min) of tokens 8 lg + j: even j feed B elements 2i
+      // (run A), odd j elements 2i + 1 (run B)
       uint32_t mA[4], mB[4];
-      if constexpr (C::VL) {
-        const uint4* st = reinterpret_cast<const uint4*>(vm_l + vmofs[f]);
+      {
+        const uint4* st = reinterpret_cast<const uint4*>(r.s + C::kSlotVM / 4 + vmofs[f]);
         const uint4 x = st[0], y = st[1];
         mA[0] = x.x; mA[1] = x.z; mA[2] = y.x; mA[3] = y.z;
         mB[0] = x.y; mB[1] = x.w; mB[2] = y.y; mB[3] = y.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          mA[i] = r.vmA[f][i];
-          mB[i] = r.vmB[f][i];
-        }
       }
       uint32_t bh[4], bl[4];
 #pragma unroll
@@ -706,15 +744,10 @@ struct PackedWave {
       for (int n = 0; n < NT; ++n) {
         if (C::gam(n) / SL != f) continue;  // compile-time
         uint32_t a[4];
-        unpack_value_tile<BV>(r.vw, n, a);
+        unpack_value_tile<BV>(vw, n, a);
         oacc[n] = mfma(a, bh, oacc[n]);
         oacc[n] = mfma(a, bl, oacc[n]);
       }
-    }
-    if constexpr (C::VL) {  // the next chunk restages after these reads
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 };
@@ -789,8 +822,9 @@ __device__ __forceinline__ void seg_begin(const DecodeLaunch& L, int b, int hkv,
   w.qfs = reinterpret_cast<float*>(smem);
   w.qB = reinterpret_cast<uint4*>(wl);
   w.beta_l = reinterpret_cast<float*>(wl + C::kQB);
-  w.vm_l = reinterpret_cast<uint32_t*>(wl + C::kQB + C::kBetaB);
+  w.ring = reinterpret_cast<uint32_t*>(wl + C::kQB + C::kBetaB);
   w.init(lane);
+  ra.s = w.ring;
   if constexpr (PG) w.set_table(g, b, hkv, r.pc0 >> g.cpp_log2);
   if (r.pc0 < r.pc1) w.load(r.pc0, ra);
 }
@@ -811,7 +845,7 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   float* part_base = L.ws + (int64_t)p * GQ * DP;
   float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
   const int pc0 = r.pc0, pc1 = r.pc1, rk0 = r.rk0, rk1 = r.rk1;
-  R rb;
+  constexpr int kRing = C::kRing;
   // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
   // that q * 2^-E * key scale fits fp16.  The softmax scale (sm_scale log2 e)
   // is not folded into q: it multiplies the finished scores (kscale, bscale),
@@ -859,22 +893,58 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   const int last_vis = sw.n - 1 - w.hide;
   const int pm = min(pc1, max(pc0, (sw.n - L.T + 1) / kChunk));
   if (pc0 < pm) {
-    // two chunk buffers: the next chunk's loads are in flight while one is
-    // used (a deeper ring measured no faster).  Prefetches past the last
-    // chunk re-load that chunk (always in bounds) instead of being skipped,
-    // so no load sits under a branch.
+    // chunk pc0 + i in ring slot i % kRing (seg_begin loaded pc0 into slot
+    // 0); while one is used, up to kRing - 1 later ones are in flight
     const int last = pm - 1;
-    int ch = pc0;
-    for (; ch < last; ch += 2) {  // pairs; ra holds chunk ch on entry
-      w.load(ch + 1, rb);
-      w.process(ch, ra);
-      w.load(min(ch + 2, last), ra);
-      w.process(ch + 1, rb);
+    if constexpr (kRing == 2) {
+      // pairs, so that the compiler can schedule one chunk's fold against the
+      // previous chunk's value products; ra holds chunk ch on entry
+      R rb = w.slot_at(1);
+      int ch = pc0;
+      for (; ch < last; ch += 2) {
+        w.load(ch + 1, rb);
+        w.template wait_chunks<1>();
+        w.process(ch, ra);
+        if (ch + 2 <= last) {
+          w.load(ch + 2, ra);
+          w.template wait_chunks<1>();
+        } else {
+          w.template wait_chunks<0>();
+        }
+        w.process(ch + 1, rb);
+      }
+      if (ch == last) {  // odd count: the last chunk is in ra
+        w.template wait_chunks<0>();
+        w.process(ch, ra);
+      }
+    } else {
+#pragma unroll
+      for (int k = 1; k < kRing - 1; ++k)
+        if (pc0 + k <= last) {
+          R rk = w.slot_at(k);
+          w.load(pc0 + k, rk);
+        }
+      int ch = pc0, si = 0;
+      for (; ch + kRing - 1 <= last; ++ch) {  // steady: kRing - 1 chunks ahead
+        R rn = w.slot_at(si == 0 ? kRing - 1 : si - 1);
+        w.load(ch + kRing - 1, rn);
+        w.template wait_chunks<kRing - 1>();
+        w.process(ch, w.slot_at(si));
+        si = si + 1 == kRing ? 0 : si + 1;
+      }
+      for (; ch <= last; ++ch) {  // the chunks already in flight
+        if (kRing == 3 && ch < last)
+          w.template wait_chunks<1>();
+        else
+          w.template wait_chunks<0>();
+        w.process(ch, w.slot_at(si));
+        si = si + 1 == kRing ? 0 : si + 1;
+      }
     }
-    if (ch == last) w.process(ch, ra);  // odd count: the last chunk is in ra
   }
   for (int ch = pm; ch < pc1; ++ch) {  // ra holds chunk pc0 if pm == pc0
     if (ch != pc0) w.load(ch, ra);
+    w.template wait_chunks<0>();
     w.template process<true>(ch, ra, last_vis);
   }
   // chunks past the packed ones: k < nm mixed (chunk nq + k), then residual
@@ -889,12 +959,14 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
       real = true;
       for (int k = rk0; k < mk1; ++k) {
         w.load(sw.nq + k, ra);
+        w.template wait_chunks<0>();
         w.process_mixed_keys(sw.nq + k, ra, sw.n, g.Rv, vres);
       }
     } else {
       w.plain_query();
       for (int k = rk0; k < mk1; ++k) {
         w.load(sw.nq + k, ra);
+        w.template wait_chunks<0>();
         w.process_mixed_values(sw.nq + k, ra, sw.n, g.R, kres);
       }
     }
@@ -1020,6 +1092,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
                                     lane);
     x = xu + sw.w;
   }
+  wait_vm<0>();  // no direct load into this wave's LDS outlives it
 }
 
 // Worker waves the partial kernel of this instantiation is launched with:

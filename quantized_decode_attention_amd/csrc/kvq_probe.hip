@@ -31,9 +31,84 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4*
   if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kProbeThreads / 64) + threadIdx.x / 64] = acc;
 }
 
+// The sweep form: single-wave workgroups, each reading one contiguous share in
+// batches of U 16-byte loads per lane (64 U loads per wave), two batches in
+// flight (the next batch is requested before the current one is folded), with
+// plain or nontemporal loads.  An index past the share is clamped to its last
+// unit (a cached re-read), so no load sits under a branch.
+template <int U, bool NT>
+__device__ __forceinline__ void batch_load(const uint4* buf, int64_t i, int64_t b1, int lane,
+                                           uint4 (&v)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int64_t k = i + 64 * u + lane;
+    k = k < b1 ? k : b1 - 1;
+    if constexpr (NT) {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf) + k);
+      v[u] = make_uint4(t.x, t.y, t.z, t.w);
+    } else {
+      v[u] = buf[k];
+    }
+  }
+}
+
+template <int U>
+__device__ __forceinline__ uint32_t batch_fold(const uint4 (&v)[U]) {
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  return acc;
+}
+
+template <int U, bool NT>
+__global__ __launch_bounds__(64) void stream_read_sweep_kernel(const uint4* buf, int64_t n16,
+                                                               uint32_t* sink) {
+  constexpr int64_t kBatch = 64 * U;
+  const int64_t per = ((n16 + gridDim.x - 1) / gridDim.x + kBatch - 1) / kBatch * kBatch;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  const int lane = threadIdx.x;
+  uint32_t acc = 0;
+  uint4 ra[U], rb[U];
+  int64_t i = b0;
+  if (i < b1) batch_load<U, NT>(buf, i, b1, lane, ra);
+  for (; i < b1; i += 2 * kBatch) {  // ra holds batch i on entry
+    batch_load<U, NT>(buf, i + kBatch, b1, lane, rb);
+    acc ^= batch_fold<U>(ra);
+    batch_load<U, NT>(buf, i + 2 * kBatch, b1, lane, ra);
+    acc ^= batch_fold<U>(rb);
+  }
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  if (lane == 0) sink[blockIdx.x] = acc;
+}
+
+template <int U>
+hipError_t sweep_launch(const void* buf, size_t bytes, uint32_t* sink, int waves, bool nt,
+                        hipStream_t st) {
+  const uint4* b = static_cast<const uint4*>(buf);
+  if (nt)
+    stream_read_sweep_kernel<U, true><<<waves, 64, 0, st>>>(b, (int64_t)(bytes / 16), sink);
+  else
+    stream_read_sweep_kernel<U, false><<<waves, 64, 0, st>>>(b, (int64_t)(bytes / 16), sink);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int probe_sink_words() { return kProbeBlocks * (kProbeThreads / 64); }
+
+hipError_t launch_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink, int waves,
+                                    int loads, bool nontemporal, hipStream_t st) {
+  switch (loads) {
+    case 1: return sweep_launch<1>(buf, bytes, sink, waves, nontemporal, st);
+    case 2: return sweep_launch<2>(buf, bytes, sink, waves, nontemporal, st);
+    case 4: return sweep_launch<4>(buf, bytes, sink, waves, nontemporal, st);
+    case 8: return sweep_launch<8>(buf, bytes, sink, waves, nontemporal, st);
+    case 16: return sweep_launch<16>(buf, bytes, sink, waves, nontemporal, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
   stream_read_kernel<<<kProbeBlocks, kProbeThreads, 0, st>>>(
