@@ -4,9 +4,10 @@
 A step is one pass of the whole decode hot path for one attention layer over a
 batch of sequences: kvq_append (the new token; a residual flush when a window
 is full) then kvq_decode_attn (split partials + combine).  Steps rotate over
---layers independent layer caches (default 4, about 1.1 GB for the default
-workload) so the 256 MB Infinity Cache cannot serve a layer's packed cache from
-one step to the next: the bytes come from HBM, as in a real multi-layer model.
+--layers independent layer caches (by default as many as keep at least 1 GB
+of decode bytes in rotation, and at least 4: 4 for the default workload) so the
+256 MB Infinity Cache cannot serve a layer's cache from one step to the next:
+the bytes come from HBM, as in a real multi-layer model.
 
 Every timed step runs at the workload's context.  A steady step appends at
 position context - 1 and attends over the context; a flush step appends into a
@@ -52,7 +53,9 @@ def parse():
     p.add_argument("--steps", type=int, default=128)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--config", type=int, default=3, help="workload 1..6 (default 3)")
-    p.add_argument("--layers", type=int, default=4, help="rotating layer caches")
+    p.add_argument("--layers", type=int, default=0,
+                   help="rotating layer caches (0: enough for 1 GB of decode bytes, at "
+                        "least 4, at most 16)")
     p.add_argument("--tokens", type=int, default=1,
                    help="query tokens per sequence per step (T > 1: kvq_append_tokens, then "
                         "kvq_decode_attn_multi; KIVI-format workloads)")
@@ -63,6 +66,9 @@ def parse():
                    help="time the steps as launched one by one (default: the timed steps "
                         "are also captured as one HIP graph, and value is the median of "
                         "its replays)")
+    p.add_argument("--eager-launches", type=int, default=1024,
+                   help="at least this many eager steps of each kind carry the per-launch "
+                        "kernel events (fewer for a profiled run)")
     p.add_argument("--min-seconds", type=float, default=0.3,
                    help="graph replays continue until they cover this much time (and at "
                         "least 10 replays)")
@@ -242,6 +248,27 @@ def cpu_baseline_bq2(w, target_seconds: float):
     return _baseline_record(w, bs, w.context, steps, nbytes, t_total, threads, one)
 
 
+ROTATION_BYTES = 1e9  # decode bytes kept in rotation: four times the Infinity Cache
+
+
+def rotating_layers(a, step_bytes: float) -> int:
+    """--layers, or enough layer caches that one pass over them reads at least
+    ROTATION_BYTES (4 to 16)."""
+    if a.layers:
+        return a.layers
+    return int(min(16, max(4, math.ceil(ROTATION_BYTES / step_bytes))))
+
+
+def stream_ceiling(kvq) -> dict:
+    """The read rate of the stream probe in the shape that reads fastest (one
+    wave per SIMD, four nontemporal 16-byte loads per lane in flight, two
+    batches deep): the practical ceiling of a read-only stream."""
+    r = kvq.stream_read_sweep([(1, 4, 1)], reps=20)[0]
+    return {"gbs": r["gbs"], "median_us": r["median_us"], "bytes": 2 << 30,
+            "kernel": "kvq_probe_stream_read_sweep (1 wave per SIMD, 4 nontemporal 16-byte "
+                      "loads per lane in flight, 2 GiB buffer beyond the Infinity Cache)"}
+
+
 def steady_and_flush_lengths(base: np.ndarray, T: int, R: int):
     """Lengths before the first append of the two kinds of decode step at the
     workload's contexts `base` (current tokens included).
@@ -303,16 +330,19 @@ def eager_per_step(step, K: int, passes: int, torch):
     return np.array(per_step), np.array([a.elapsed_time(b) for a, b in evs])
 
 
-def measure(a, step, torch, label: str):
+def measure(a, step, torch, label: str, kernel=None):
     """Warmup, eager passes with per-launch kernel events, then (unless
     --eager) the K steps captured as one HIP graph and replayed.  Every step
     of a kind does the same work at the same lengths, so passes and replays
-    repeat it exactly."""
+    repeat it exactly.  kernel(i), if given, launches only step i's dominant
+    kernel: K of them are captured as a graph of their own and replayed, so
+    that its average launch is timed as it runs inside the step graph (back to
+    back, HIP events around each replay) rather than launched one by one."""
     K = a.steps
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    passes = max(2, -(-1024 // K))
+    passes = max(2, -(-a.eager_launches // K))
     eager, kern_ms = eager_per_step(step, K, passes, torch)
     print(f"[bench] {label}: {passes} eager passes of {K} steps, "
           f"{np.median(eager) * 1e6:.2f} us per step", file=sys.stderr, flush=True)
@@ -332,11 +362,26 @@ def measure(a, step, torch, label: str):
                                                       np.percentile(host, 10)))
     print(f"[bench] {label}: {len(host)} graph replays of {K} steps, "
           f"{res['step_s'] * 1e6:.2f} us per step", file=sys.stderr, flush=True)
+    if kernel is not None:
+        kg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(kg):
+            for i in range(K):
+                kernel(i)
+        _, kgpu = replay_per_step(kg, K, torch, a.min_seconds)
+        del kg
+        res.update(kernel_graph_s=float(np.median(kgpu)), kernel_replays=len(kgpu))
+        print(f"[bench] {label}: {len(kgpu)} replays of {K} back-to-back kernel launches, "
+              f"{res['kernel_graph_s'] * 1e6:.2f} us per launch", file=sys.stderr, flush=True)
     return res
 
 
-def kernel_roofline(kernel: str, kern_ms, dec_bytes: float, traffic, ceiling: dict):
-    avg_s = float(np.mean(kern_ms)) / 1e3
+def kernel_roofline(kernel: str, m: dict, dec_bytes: float, traffic, ceiling: dict):
+    """The dominant kernel against the HBM roofline: its algorithmic bytes per
+    launch over its average launch as timed in a graph of back-to-back launches
+    (or, with --eager, over the per-launch events of the eager passes)."""
+    kern_ms = m["kernel_ms"]
+    eager_avg_s = float(np.mean(kern_ms)) / 1e3
+    avg_s = m.get("kernel_graph_s", eager_avg_s)
     achieved = dec_bytes / avg_s / 1e9
     return {
         "kernel": kernel,
@@ -347,8 +392,13 @@ def kernel_roofline(kernel: str, kern_ms, dec_bytes: float, traffic, ceiling: di
         "frac": round(achieved / PEAK_HBM_GBS, 4),
         "traffic": traffic,
         "avg_launch_us": round(avg_s * 1e6, 3),
-        **{f"p{q}_us": round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)},
-        "launches": int(len(kern_ms)),
+        "launch_timing": ("HIP events around replays of a graph of back-to-back launches "
+                          "(median replay / launches)" if "kernel_graph_s" in m else
+                          "HIP events around each eager launch"),
+        "eager_launches": {
+            "avg_us": round(eager_avg_s * 1e6, 3), "launches": int(len(kern_ms)),
+            **{f"p{q}_us": round(float(np.percentile(kern_ms, q)) * 1e3, 3)
+               for q in (10, 50, 90)}},
         "algorithmic_bytes_per_launch": round(dec_bytes),
         "frac_of_stream_read": round(achieved / ceiling["gbs"], 4),
     }
@@ -361,18 +411,14 @@ DTYPE_NOTE = ("codes enter v_mfma_f32_16x16x32_f16 as exact fp16 operands agains
               "softmax and the split combine in fp32; fp16 out")
 
 
-def stream_read_entry(ceiling: dict) -> dict:
-    return {**ceiling, "kernel": "kvq_probe_stream_read (plain 16-byte loads, "
-                                 "2 GiB buffer beyond the Infinity Cache)"}
-
-
 def run_bq2(a, w, torch, kvq, metrics, synth):
     """The rotated per-token 2-bit format: kvq_bq2_append then
     kvq_bq2_decode_partial (timed per launch) and kvq_bq2_decode_combine, every
     step appending at position context - 1 and attending over the context
     (the format has no window to flush)."""
     dev = torch.device("cuda:0")
-    L = a.layers
+    L = rotating_layers(a, metrics.bq2_decode_step_bytes(np.full(w.batch, w.context),
+                                                         w.n_q_heads, w.n_kv_heads))
     cap = synth.capacity_for(w, 1)
     g = kvq.Bq2Geom(w.batch, w.n_q_heads, w.n_kv_heads, cap)
     n0 = w.context - 1
@@ -409,8 +455,12 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
             ev[1].record(stream)
         kvq.kvq_bq2_decode_combine(g, q, c, after, max_len, scale, ws, out, stream)
 
-    m = measure(a, step, torch, "steady steps")
-    ceiling = kvq.stream_read_gbs()
+    def kernel(i):
+        kvq.kvq_bq2_decode_partial(g, pool[i % len(pool)][2], caches[i % L], after, max_len,
+                                   scale, ws, out, torch.cuda.current_stream())
+
+    m = measure(a, step, torch, "steady steps", kernel)
+    ceiling = stream_ceiling(kvq)
     t = m["step_s"]
     gbs = step_bytes / t / 1e9
     return {
@@ -448,9 +498,9 @@ def run_bq2(a, w, torch, kvq, metrics, synth):
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch / t, 1),
         "tokens_per_s_unit": "decoded tokens per second through one layer",
-        "roofline": kernel_roofline("bq2_partial", m["kernel_ms"], dec_bytes,
+        "roofline": kernel_roofline("bq2_partial", m, dec_bytes,
                                     load_traffic(w.name, "bq2_partial"), ceiling),
-        "stream_read": stream_read_entry(ceiling),
+        "stream_read": ceiling,
         "gpu": torch.cuda.get_device_name(0),
     }
 
@@ -460,8 +510,10 @@ def run_kivi(a, w, torch, kvq, metrics, synth):
     steady_and_flush_lengths) timed apart, the flush amortized at one step in
     R / T per layer cache, as a decode loop at these contexts sees it."""
     dev = torch.device("cuda:0")
-    L = a.layers if w.layers == 1 else w.layers
     T, R = a.tokens, w.residual
+    L = w.layers if w.layers > 1 else rotating_layers(
+        a, metrics.decode_step_bytes(synth.seq_lens(w), w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                     w.k_bits, w.v_bits, w.group, R))
     if T >= R:
         raise SystemExit(f"--tokens must be below the window ({R})")
     base = synth.seq_lens(w)
@@ -559,6 +611,15 @@ def run_kivi(a, w, torch, kvq, metrics, synth):
                     ev[1].record(stream)
         return step
 
+    def kernel(i):  # the steady step's dominant kernel alone
+        before, after, msl = lens["steady"]
+        stream = torch.cuda.current_stream()
+        c = caches[i % L]
+        if T == 1:
+            partial(g, pool[i % len(pool)][2], c, after, msl, scale, ws, out, stream)
+        else:
+            multi(g, tpool[i % len(tpool)][2], c, after, T, msl, scale, ws, out, stream)
+
     def step_bytes(n_before, flushing):
         after = n_before + T
         db = metrics.decode_step_bytes(after, w.n_q_heads, w.n_kv_heads, w.head_dim,
@@ -572,14 +633,14 @@ def run_kivi(a, w, torch, kvq, metrics, synth):
 
     dec_s, b_s = step_bytes(n_s, False)
     dec_f, b_f = step_bytes(n_f, True)
-    ms = measure(a, make_step("steady"), torch, "steady steps")
+    ms = measure(a, make_step("steady"), torch, "steady steps", kernel)
     mf = measure(a, make_step("flush"), torch, "flush steps")
     F = R / T  # steps per layer cache between its flushes
     t = ((F - 1) * ms["step_s"] + mf["step_s"]) / F
     nbytes = ((F - 1) * b_s + b_f) / F
     t_eager = ((F - 1) * ms["eager_s"] + mf["eager_s"]) / F
     gbs = nbytes / t / 1e9
-    ceiling = kvq.stream_read_gbs()
+    ceiling = stream_ceiling(kvq)
     traffic = load_traffic(w.name) if T == 1 and not P else None
 
     def kind_entry(m, b, n_before, flushes):
@@ -642,8 +703,8 @@ def run_kivi(a, w, torch, kvq, metrics, synth):
            if w.layers > 1 else {}),
         "roofline": kernel_roofline(
             ("decode_partial" if T == 1 else "decode_partial+decode_combine (multi)")
-            + (" (paged)" if P else ""), ms["kernel_ms"], dec_s, traffic, ceiling),
-        "stream_read": stream_read_entry(ceiling),
+            + (" (paged)" if P else ""), ms, dec_s, traffic, ceiling),
+        "stream_read": ceiling,
         "gpu": torch.cuda.get_device_name(0),
     }
     return rec
@@ -671,7 +732,7 @@ def main():
         return
 
     if a.probe_sweep:
-        shapes = [(wps, loads, nt) for nt in (0, 1) for wps in (1, 2, 3, 4, 8)
+        shapes = [(wps, loads, nt) for nt in (0, 1, 2, 3) for wps in (1, 2, 3, 4, 8)
                   for loads in (1, 2, 4, 8, 16) if not (loads == 16 and wps > 3)]
         res = kvq.stream_read_sweep(shapes)
         best = max(res, key=lambda r: r["gbs"])

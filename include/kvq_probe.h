@@ -29,7 +29,10 @@ int kvq_probe_sink_words(int32_t *words);
  * single-wave workgroups (1 <= waves_per_simd <= 8), each reading one
  * contiguous share in batches of loads_per_lane (1, 2, 4, 8 or 16) 16-byte
  * loads per lane, with the next batch requested before the current one is
- * used; nontemporal != 0 makes them nontemporal loads.  Waves beyond what
+ * used.  nontemporal selects the load: 0 plain, 1 nontemporal, 2 nontemporal
+ * direct loads into LDS (global_load_lds_dwordx4, each batch read back from
+ * LDS), 3 plain direct loads into LDS (KVQ_ERR_RANGE otherwise; for 2 and 3
+ * bytes must be a multiple of 1024).  Waves beyond what
  * the GPU keeps resident run after the first ones finish.  Status codes and
  * sink as kvq_probe_stream_read. */
 int kvq_probe_stream_read_sweep(const void *buf, size_t bytes, uint32_t *sink,

@@ -664,7 +664,8 @@ def stream_read_sweep(shapes, nbytes: int = 2 << 30, reps: int = 10, device="cud
             if r >= 2:
                 times.append(a.elapsed_time(b) / 1e3)
         t = float(np.median(times))
-        out.append({"waves_per_simd": wps, "loads_per_lane": loads, "nontemporal": bool(nt),
+        out.append({"waves_per_simd": wps, "loads_per_lane": loads,
+                    "load": ("plain", "nontemporal", "lds nontemporal", "lds plain")[nt],
                     "bytes_in_flight_per_wave": [64 * 16 * loads, 2 * 64 * 16 * loads],
                     "gbs": round(nbytes / t / 1e9, 1), "median_us": round(t * 1e6, 2)})
     del buf

@@ -975,7 +975,12 @@ int kvq_probe_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink,
     if (waves > kvq::probe_sink_words())
       return fail(KVQ_ERR_RANGE, "%d waves exceed the sink's %d words", waves,
                   kvq::probe_sink_words());
-    hipError_t e = kvq::launch_stream_read_sweep(buf, bytes, sink, waves, L, nontemporal != 0,
+    if (nontemporal < 0 || nontemporal > 3)
+      return fail(KVQ_ERR_RANGE, "nontemporal (%d) must be in [0, 3]", nontemporal);
+    if (nontemporal >= 2 && bytes % 1024 != 0)  // whole 1 KB direct loads
+      return fail(KVQ_ERR_RANGE, "bytes (%zu) must be a multiple of 1024 for direct loads",
+                  bytes);
+    hipError_t e = kvq::launch_stream_read_sweep(buf, bytes, sink, waves, L, nontemporal,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVQ_OK : hip_fail(e, "stream read sweep launch");
   } catch (...) {

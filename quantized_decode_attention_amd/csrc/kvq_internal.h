@@ -177,6 +177,6 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 int probe_sink_words();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink, int waves,
-                                    int loads, bool nontemporal, hipStream_t st);
+                                    int loads, int mode, hipStream_t st);
 
 }  // namespace kvq

@@ -1,7 +1,7 @@
 // kvq_probe.hip — a plain streaming read (measurement aid, kvq_probe.h):
 // every wave reads a contiguous share of the buffer with 16-byte loads, four
 // in flight per lane, and folds them into one word so that none is dropped.
-#include "kvq_internal.h"
+#include "kvq_device.h"
 
 namespace kvq {
 namespace {
@@ -83,14 +83,65 @@ __global__ __launch_bounds__(64) void stream_read_sweep_kernel(const uint4* buf,
   if (lane == 0) sink[blockIdx.x] = acc;
 }
 
+// The same share read with direct loads into LDS (global_load_lds_dwordx4, as
+// the decode kernel streams its chunks): batches of U 1 KB loads into one half
+// of a per-wave ring, two batches in flight, each batch read back from LDS
+// once it is in.  Loads past the share are clamped to its last 16 bytes.
+template <int U, bool NT>
+__global__ __launch_bounds__(64) void stream_read_lds_kernel(const uint4* buf, int64_t n16,
+                                                             uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint4 ring[2][U][64];
+  constexpr int64_t kBatch = 64 * U;
+  const int64_t per = ((n16 + gridDim.x - 1) / gridDim.x + kBatch - 1) / kBatch * kBatch;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  const int lane = threadIdx.x;
+  const uint32_t lane16 = 16u * lane;
+  uint32_t acc = 0;
+  auto issue = [&](int64_t i, int half) {
+    lds_dma_begin();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // the instruction's 64 pieces; a piece past the share re-reads its last
+      const int64_t k0 = i + 64 * u;
+      const uint4* g = buf + (k0 < b1 ? k0 : b1 - 64 > b0 ? b1 - 64 : b0);
+      lds_dma16<NT>(g, lds_addr(&ring[half][u][0]), lane16);
+    }
+  };
+  int64_t i = b0;
+  if (i < b1) issue(i, 0);
+  int half = 0;
+  for (; i < b1; i += kBatch) {
+    if (i + kBatch < b1) {
+      issue(i + kBatch, half ^ 1);
+      wait_vm<U>();
+    } else {
+      wait_vm<0>();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint4 v = ring[half][u][lane];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    half ^= 1;
+  }
+  wait_vm<0>();
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  if (lane == 0) sink[blockIdx.x] = acc;
+}
+
+// mode: 0 plain loads, 1 nontemporal, 2 direct-to-LDS nontemporal, 3 direct-to-LDS plain
 template <int U>
-hipError_t sweep_launch(const void* buf, size_t bytes, uint32_t* sink, int waves, bool nt,
+hipError_t sweep_launch(const void* buf, size_t bytes, uint32_t* sink, int waves, int mode,
                         hipStream_t st) {
   const uint4* b = static_cast<const uint4*>(buf);
-  if (nt)
-    stream_read_sweep_kernel<U, true><<<waves, 64, 0, st>>>(b, (int64_t)(bytes / 16), sink);
-  else
-    stream_read_sweep_kernel<U, false><<<waves, 64, 0, st>>>(b, (int64_t)(bytes / 16), sink);
+  const int64_t n16 = (int64_t)(bytes / 16);
+  switch (mode) {
+    case 0: stream_read_sweep_kernel<U, false><<<waves, 64, 0, st>>>(b, n16, sink); break;
+    case 1: stream_read_sweep_kernel<U, true><<<waves, 64, 0, st>>>(b, n16, sink); break;
+    case 2: stream_read_lds_kernel<U, true><<<waves, 64, 0, st>>>(b, n16, sink); break;
+    default: stream_read_lds_kernel<U, false><<<waves, 64, 0, st>>>(b, n16, sink); break;
+  }
   return hipGetLastError();
 }
 
@@ -99,13 +150,13 @@ hipError_t sweep_launch(const void* buf, size_t bytes, uint32_t* sink, int waves
 int probe_sink_words() { return kProbeBlocks * (kProbeThreads / 64); }
 
 hipError_t launch_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink, int waves,
-                                    int loads, bool nontemporal, hipStream_t st) {
+                                    int loads, int mode, hipStream_t st) {
   switch (loads) {
-    case 1: return sweep_launch<1>(buf, bytes, sink, waves, nontemporal, st);
-    case 2: return sweep_launch<2>(buf, bytes, sink, waves, nontemporal, st);
-    case 4: return sweep_launch<4>(buf, bytes, sink, waves, nontemporal, st);
-    case 8: return sweep_launch<8>(buf, bytes, sink, waves, nontemporal, st);
-    case 16: return sweep_launch<16>(buf, bytes, sink, waves, nontemporal, st);
+    case 1: return sweep_launch<1>(buf, bytes, sink, waves, mode, st);
+    case 2: return sweep_launch<2>(buf, bytes, sink, waves, mode, st);
+    case 4: return sweep_launch<4>(buf, bytes, sink, waves, mode, st);
+    case 8: return sweep_launch<8>(buf, bytes, sink, waves, mode, st);
+    case 16: return sweep_launch<16>(buf, bytes, sink, waves, mode, st);
     default: return hipErrorInvalidValue;
   }
 }
