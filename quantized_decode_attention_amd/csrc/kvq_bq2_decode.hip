@@ -652,6 +652,8 @@ hipError_t run(const Bq2Launch& L, int op, int cus, int* workers, hipStream_t st
   if (op == 1) return workers_of<GQ>(cus, workers);
   if (op == 0)
     bq2_partial_kernel<GQ><<<dim3(L.n_workers), 64, 0, st>>>(L);
+  else if (L.g.B * L.g.Hkv < kCombineRowUnits && GQ > 1)
+    decode_combine_kernel<Bq2Work, kD, GQ, 1><<<dim3(L.g.Hkv * GQ, L.g.B), kThreads, 0, st>>>(L);
   else
     decode_combine_kernel<Bq2Work, kD, GQ><<<dim3(L.g.Hkv, L.g.B), kThreads, 0, st>>>(L);
   return hipGetLastError();

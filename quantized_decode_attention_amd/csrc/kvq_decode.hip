@@ -20,18 +20,25 @@ hipError_t partial_entry(const DecodeLaunch& L, int op, int cus, int* workers, h
   return sets[L.g.table != nullptr][L.g.D == 128][bk](L, op, cus, workers, st);
 }
 
+template <int D, int GQ>
+hipError_t combine_rows(const DecodeLaunch& L, hipStream_t st) {
+  if (L.g.B * L.g.Hkv < kCombineRowUnits && GQ > 1)
+    decode_combine_kernel<KiviWork, D, GQ, 1><<<dim3(L.g.Hkv * GQ, L.g.B), kThreads, 0, st>>>(L);
+  else
+    decode_combine_kernel<KiviWork, D, GQ><<<dim3(L.g.Hkv, L.g.B), kThreads, 0, st>>>(L);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t combine_gq(const DecodeLaunch& L, hipStream_t st) {
-  dim3 grid(L.g.Hkv, L.g.B);
   switch (L.gq) {
-    case 1: decode_combine_kernel<KiviWork, D, 1><<<grid, kThreads, 0, st>>>(L); break;
-    case 2: decode_combine_kernel<KiviWork, D, 2><<<grid, kThreads, 0, st>>>(L); break;
-    case 4: decode_combine_kernel<KiviWork, D, 4><<<grid, kThreads, 0, st>>>(L); break;
-    case 8: decode_combine_kernel<KiviWork, D, 8><<<grid, kThreads, 0, st>>>(L); break;
-    case 16: decode_combine_kernel<KiviWork, D, 16><<<grid, kThreads, 0, st>>>(L); break;
+    case 1: return combine_rows<D, 1>(L, st);
+    case 2: return combine_rows<D, 2>(L, st);
+    case 4: return combine_rows<D, 4>(L, st);
+    case 8: return combine_rows<D, 8>(L, st);
+    case 16: return combine_rows<D, 16>(L, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace

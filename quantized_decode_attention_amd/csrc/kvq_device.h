@@ -485,18 +485,22 @@ __device__ __forceinline__ SegRange seg_range(const Launch& L, const SeqWork& sw
   r.rk1 = min(sw.nr, d1 <= 0 ? 0 : (d1 + L.rw - 1) / L.rw);
   return r;
 }
-// One workgroup per (KV head, sequence): merges the partials of the unit and
-// writes its GQ outputs:
+// One workgroup per RS rows of a (KV head, sequence) unit (RS = GQ: the whole
+// unit; RS = 1: one row, for launches with few units, where a unit's many
+// partials would otherwise be streamed by few workgroups); blockIdx.x =
+// hkv * (GQ / RS) + row group.  Merges the unit's partials for those rows and
+// writes their outputs:
 //   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
 // The unit's partials are contiguous (indices w + u for consecutive waves w).
 // Each thread owns one float4 of the output and a 1/P share of the partials
 // and merges them as a stream (running max, rescale when it grows), so the
 // (m, l, o) loads of a partial do not wait for any reduction; the P shares are
 // then merged through LDS.  Empty partials (m = -inf) carry weight 0.
-template <class Fmt, int D, int GQ>
+template <class Fmt, int D, int GQ, int RS = GQ>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::Launch L) {
+  static_assert(RS == GQ || RS == 1, "whole units or single rows");
   constexpr int DP = D + kPartPad;
-  constexpr int NO = GQ * D / 4;                          // float4 outputs of the unit
+  constexpr int NO = RS * D / 4;                          // float4 outputs of the workgroup
   constexpr int P = NO >= kThreads ? 1 : kThreads / NO;   // partial shares per output
   constexpr int OPT = NO >= kThreads ? NO / kThreads : 1;  // outputs per thread
   constexpr int U = 4;                                     // partials in flight per thread
@@ -506,17 +510,19 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
   __shared__ int red[2 * kThreads / 64];
   __shared__ float4 s_o[kThreads];
   __shared__ float2 s_ml[kThreads];
-  __shared__ float s_rot[kRotate ? GQ * D : 1];
+  __shared__ float s_rot[kRotate ? RS * D : 1];
   const auto& g = L.g;
-  const int hkv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int hkv = blockIdx.x / (GQ / RS), row0 = (blockIdx.x % (GQ / RS)) * RS;
+  const int b = blockIdx.y, tid = threadIdx.x;
   const int n = L.seq_lens[b];
   if (n < 0 || n > g.C || n > L.max_seq_len) {
-    for (int i = tid; i < GQ * D; i += kThreads)
-      L.out[Fmt::row(L, b, hkv, i / D) * D + i % D] = 0x7e00;  // NaN
+    for (int i = tid; i < RS * D; i += kThreads)
+      L.out[Fmt::row(L, b, hkv, row0 + i / D) * D + i % D] = 0x7e00;  // NaN
     return;
   }
   if (n == 0) {
-    for (int i = tid; i < GQ * D; i += kThreads) L.out[Fmt::row(L, b, hkv, i / D) * D + i % D] = 0;
+    for (int i = tid; i < RS * D; i += kThreads)
+      L.out[Fmt::row(L, b, hkv, row0 + i / D) * D + i % D] = 0;
     return;
   }
   // flat position of this unit's work
@@ -555,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
 #pragma unroll
   for (int j = 0; j < OPT; ++j) {
     const int t = (P > 1) ? tid % NO : tid + j * kThreads;
-    const int oh = t / (D / 4), oc = (t % (D / 4)) * 4;
+    const int ol = t / (D / 4), oh = row0 + ol, oc = (t % (D / 4)) * 4;
     const float* pr = base + oh * DP;
     float M = kNegInf, Ls = 0.0f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -612,10 +618,10 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
     if constexpr (kRotate) {
       // out_c = sum_j H[c][j] o_j, H[c][j] = (-1)^popcount(c & j) / 8
       if (share == 0) {
-        s_rot[oh * D + oc + 0] = O.x * inv;
-        s_rot[oh * D + oc + 1] = O.y * inv;
-        s_rot[oh * D + oc + 2] = O.z * inv;
-        s_rot[oh * D + oc + 3] = O.w * inv;
+        s_rot[ol * D + oc + 0] = O.x * inv;
+        s_rot[ol * D + oc + 1] = O.y * inv;
+        s_rot[ol * D + oc + 2] = O.z * inv;
+        s_rot[ol * D + oc + 3] = O.w * inv;
       }
       __syncthreads();
       if (share == 0) {
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
           const int c = oc + e;
           float acc = 0.0f;
           for (int j = 0; j < D; ++j) {
-            const float r = s_rot[oh * D + j];
+            const float r = s_rot[ol * D + j];
             acc += (__builtin_popcount(c & j) & 1) ? -r : r;
           }
           L.out[o + e] = f2h(acc * 0.125f);
@@ -638,5 +644,8 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
     }
   }
 }
+// Units of a launch below which the combine takes one row per workgroup.
+constexpr int kCombineRowUnits = 128;
+
 }  // namespace
 }  // namespace kvq
