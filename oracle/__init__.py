@@ -24,8 +24,23 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _SRC_BQ2 = os.path.join(_HERE, "bq2_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a separately built library (the sanitizer test loads an instrumented build)
+_LIB_OVERRIDE = os.environ.get("KVQ_ORACLE_LIB")
 
 VBLOCK = 32  # tokens per value-code block (layout restated in kvq_oracle.c)
+
+
+def build_sanitized(out: str) -> str:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code, gcc; any report aborts), for tests that run the oracle under
+    them."""
+    cmd = [
+        "gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+        "-fno-sanitize-recover=all", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+        "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, _SRC_BQ2, "-o", out, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 def build(force: bool = True) -> str:
@@ -47,9 +62,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.orc_half_to_float.restype = ctypes.c_float
