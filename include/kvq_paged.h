@@ -30,13 +30,16 @@
  * So a dense kvq.h cache is this layout with P = capacity, num_pages = B and
  * block_table[b][0] = b.
  *
- * Table entries are read for the pages that hold packed positions only
- * (positions below Lq(n), kvq.h; with a separate value window, the larger of
- * the key and value packed lengths): a sequence of n tokens needs entries
- * [0, ceil(Lq(n) / P)) set; the rest of its row is never read.  An entry that
- * is read and lies outside [0, num_pages) makes decode give NaN for that
- * sequence and makes the writers skip that page (nothing outside the pools is
- * read or written).  Pages may be shared by several sequences for reading (a
+ * A sequence of n tokens needs valid entries [0, ceil(Lq(n) / P)) of its
+ * row (Lq(n) as in kvq.h; with a separate value window, the larger of the key
+ * and value packed lengths): only the pages they name are used.  Decode may
+ * read any entry of the row, [0, max_pages) (it loads windows of 64 entries,
+ * and its first chunk is requested before the lengths are known), so every
+ * entry must be readable memory; entries past the needed ones need not hold
+ * valid page numbers, and their values do not affect any result.  A needed
+ * entry outside [0, num_pages) makes decode give NaN for that sequence and
+ * makes the writers skip that page (nothing outside the pools is read or
+ * written).  Pages may be shared by several sequences for reading (a
  * common prefix); a call that writes a page (the flush of an append, a
  * prefill) must be the only one using it.
  *

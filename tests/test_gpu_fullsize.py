@@ -113,28 +113,32 @@ def test_one_step_full_size(cfg, samples):
         _say(f"    max err {err:.2e}")
 
 
-def test_full_stack_layer_through_flushes():
-    """The full-stack workload's geometry at its full batch, one layer: 65 decode
-    steps from a 4096-token prefix, so both the flush at n = 4096 (first step)
-    and at n = 4160 (step 65) happen; sampled outputs at steps 1, 2, 64, 65 and
-    the packed state after the last step."""
+@pytest.mark.parametrize("layer", [0, 15, 31])
+def test_full_stack_layer_through_flushes(layer):
+    """The full-stack workload (32 layers, 256 decode steps from a 4096-token
+    prefix, K4/V2, G = R = 64) at its full batch, layers 0, 15 and 31 (each
+    layer its own seeded keys, values and tokens): all 256 steps, so the
+    flushes at n = 4096 (step 1), 4160, 4224 and 4288 all happen; sampled
+    outputs on both sides of every flush and at the last step, for sequences
+    0, 37 and 63, and their packed state after the last step."""
     w = synth.WORKLOADS[5]
-    steps = 65
+    steps = w.steps
     start = np.full(w.batch, w.context, np.int32)
     cap = synth.capacity_for(w, steps + 1)
     g = kvq.Geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k_bits, w.v_bits,
                  w.group, w.residual, cap)
-    _say(f"full-stack layer 0 ({w.name}): {steps} steps, workers {kvq.kvq_decode_workers(g)}")
-    k = synth.keys(w, w.context)
-    v = synth.values(w, w.context)
+    _say(f"full-stack layer {layer} ({w.name}): {steps} steps, workers "
+         f"{kvq.kvq_decode_workers(g)}")
+    k = synth.keys(w, w.context, layer=layer)
+    v = synth.values(w, w.context, layer=layer)
     cache = kvq.Cache(g)
     _gpu_prefill(g, cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), start)
-    toks = [synth.step_token(w, s) for s in range(steps)]
+    toks = [synth.step_token(w, s, layer=layer) for s in range(steps)]
     msl = w.context + steps
     ws = kvq.alloc_workspace(g, msl)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device="cuda")
     scale = 1.0 / math.sqrt(w.head_dim)
-    check_at = (1, 2, 64, 65)
+    check_at = (1, 2, 64, 65, 128, 129, 192, 193, 256)
     outs = {}
     lens = start.copy()
     for s in range(steps):
@@ -149,7 +153,7 @@ def test_full_stack_layer_through_flushes():
                           w.v_bits, w.group, w.residual, cap)
     got = cache_np(cache, oracle.Cache(og_full))
     for b in (0, 37, 63):
-        _say(f"  oracle sequence {b}")
+        _say(f"  layer {layer}: oracle sequence {b}")
         og, oc = _oracle_seq(w, cap, k, v, b, w.context)
         n = w.context
         for s in range(steps):
@@ -159,5 +163,6 @@ def test_full_stack_layer_through_flushes():
             if s + 1 in check_at:
                 ref = oracle.decode_attn(og, oc, q[b:b + 1], np.array([n], np.int32),
                                          float(np.float32(scale)))
-                assert_close(outs[s + 1][b:b + 1], ref, what=f"cfg5 seq {b} step {s + 1}")
-        _check_seq_cache(got, oc, w, b, n, "cfg5")
+                assert_close(outs[s + 1][b:b + 1], ref,
+                             what=f"cfg5 layer {layer} seq {b} step {s + 1}")
+        _check_seq_cache(got, oc, w, b, n, f"cfg5 layer {layer}")
