@@ -231,14 +231,13 @@ struct Bq2Wave {
       }
     }
     float xs[2][4];
+    uint32_t ka[2][2][4];
+    unpack_keys_2x64(r.kw, ka);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint32_t w[1] = {r.kw[u]};
-      uint32_t a[2][4];
-      unpack_keys<kD, 2>(w, a);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(a[0], bq[0], acc);
-      acc = mfma(a[1], bq[1], acc);
+      acc = mfma(ka[u][0], bq[0], acc);
+      acc = mfma(ka[u][1], bq[1], acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) xs[u][q] = key_sum(acc[q]);
     }
@@ -293,15 +292,11 @@ struct Bq2Wave {
       b[e] = part_of(bit_sel(m_vbig, Yb[ja >> 2][ja & 3], Ys[ja >> 2][ja & 3]),
                      bit_sel(m_vbig, Yb[jb >> 2][jb & 3], Ys[jb >> 2][jb & 3]));
     }
+    // tile 2m + h: pair e of token 8 lg + 2e (+1) at bits 8h + 4(e/2) + 2(e%2)
+    uint32_t va[4][4];
+    unpack_values_2x64(r.vw, va);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // tile 2m + h: pair e of token 8 lg + 2e (+1) at bits 8h + 4(e/2) + 2(e%2)
-        uint32_t a[4];
-        unpack_value_tile<2>(r.vw, 2 * m + h, a);
-        oacc[2 * m + h] = mfma(a, b, oacc[2 * m + h]);
-      }
+    for (int n = 0; n < 4; ++n) oacc[n] = mfma(va[n], b, oacc[n]);
   }
 
   // Packed accumulation to real scale (codes were c * 2^(L-24), odd pairs carry

@@ -43,6 +43,12 @@
 namespace kvq {
 namespace {
 
+// Row stride (floats) of the scaled query in LDS: D + 4, so that rows sit 4
+// banks apart and the lanes of different rows reading the same channels hit
+// different banks (a stride of D would put all rows on one bank).
+template <int D>
+constexpr int kQS = D + 4;
+
 // ---------------------------------------------------------------------------
 // Packed tokens of one split: MFMA path.  NG = head_dim / group is a template
 // parameter, so the key-group length G = D / NG and the value-tile -> group
@@ -299,8 +305,8 @@ struct PackedWave {
       uint32_t w[8];
       lds_words<8>(r.s + C::kSlotKM / 4 + rr * 8, w);
       const int ca = key_run0<D, BK>(lg, kc), cb = ca + kKeyOff<BK>;
-      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + ca);
-      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * D + cb);
+      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * kQS<D> + ca);
+      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * kQS<D> + cb);
       uint32_t hp[4], lp[4];
       bsum += fold_item(qa, qb, make_uint4(w[0], w[2], w[4], w[6]),
                         make_uint4(w[1], w[3], w[5], w[7]), hp, lp);
@@ -335,8 +341,8 @@ struct PackedWave {
       // (when the items fill the wave exactly the test is compile-time true)
       if (C::ITEMS % 64 == 0 || it < C::ITEMS) {
         const int h = it / IPH, rr = it % IPH, gg = rr / KC, kc = rr % KC;
-        const float4 qa = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[0]);
-        const float4 qb = *reinterpret_cast<const float4*>(qfs + h * D + kmoff[1]);
+        const float4 qa = *reinterpret_cast<const float4*>(qfs + h * kQS<D> + kmoff[0]);
+        const float4 qb = *reinterpret_cast<const float4*>(qfs + h * kQS<D> + kmoff[1]);
         uint32_t hp[4], lp[4];
         bpart = fold_item(qa, qb, kmA, kmB, hp, lp);
         qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
@@ -528,8 +534,8 @@ struct PackedWave {
   __device__ __forceinline__ void plain_query() {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg);
-      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * D + 32 * kc + 8 * lg + 4);
+      const float4 qa = *reinterpret_cast<const float4*>(qfs + hcol * kQS<D> + 32 * kc + 8 * lg);
+      const float4 qb = *reinterpret_cast<const float4*>(qfs + hcol * kQS<D> + 32 * kc + 8 * lg + 4);
       // channel 32 kc + 8 lg + j: parity of j; the key-side factors come out
       constexpr float ue = 1.0f / kKeyEvenQ<BK>, uo = 1.0f / kKeyOddQ<BK>;
       const float qv[8] = {qa.x * ue, qa.y * uo, qa.z * ue, qa.w * uo,
@@ -800,7 +806,7 @@ struct KiviWork {
 };
 
 template <int D, int BK, int BV, int GQ, int NG>
-constexpr int kWaveSmem = GQ * D * 4 + Cfg<D, BK, BV, GQ, NG>::kWaveLds;
+constexpr int kWaveSmem = GQ * kQS<D> * 4 + Cfg<D, BK, BV, GQ, NG>::kWaveLds;
 
 // Sets up the wave for unit (b, hkv) and issues the loads of the range's first
 // packed chunk into ra (before anything else, so that their latency overlaps
@@ -811,7 +817,7 @@ __device__ __forceinline__ void seg_begin(const DecodeLaunch& L, int b, int hkv,
                                           Raw<D, BK, BV, GQ, NG>& ra) {
   using C = Cfg<D, BK, BV, GQ, NG>;
   const Geom& g = L.g;
-  char* wl = smem + GQ * D * 4;
+  char* wl = smem + GQ * kQS<D> * 4;
   // dense: the unit's rows (chunk slot = chunk); paged: the pools
   const int64_t unit = PG ? 0 : (int64_t)b * g.Hkv + hkv;
   w.kcodes = L.cache.k_codes + unit * g.C * C::WR;
@@ -843,7 +849,7 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   const Geom& g = L.g;
   const int64_t unit = (int64_t)b * g.Hkv + hkv;
   float* part_base = L.ws + (int64_t)p * GQ * DP;
-  float* qfs = reinterpret_cast<float*>(smem);  // [GQ][D] q * 2^-E_h
+  float* qfs = reinterpret_cast<float*>(smem);  // [GQ][kQS] q * 2^-E_h
   const int pc0 = r.pc0, pc1 = r.pc1, rk0 = r.rk0, rk1 = r.rk1;
   constexpr int kRing = C::kRing;
   // query of the unit's GQ heads; per-head exponent E with max|q| < 2^E so
@@ -869,7 +875,7 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
     eh[h] = e;
 #pragma unroll
     for (int k = 0; k < QPH; ++k)  // channel lane + 64 k has the parity of lane
-      qfs[h * D + lane + 64 * k] =
+      qfs[h * kQS<D> + lane + 64 * k] =
           ldexpf(qv[k], -e) * ((lane & 1) ? kKeyOddQ<BK> : kKeyEvenQ<BK>);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

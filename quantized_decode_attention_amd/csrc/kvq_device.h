@@ -225,6 +225,62 @@ template <int B> constexpr uint32_t kMaskEven = B == 2 ? 0x00C000C0u : B == 4 ? 
 template <int B> constexpr uint32_t kMaskOdd = B == 2 ? 0x03000300u : B == 4 ? 0x03C003C0u
                                                                               : 0x03FC03FCu;
 
+// Two words shifted left (K > 0) or right (K < 0) by |K| <= 6 bits as one
+// 64-bit shift (which issues at the rate of a 32-bit one).  The bits that
+// cross between the two words land in bits [0, K) of the high word or
+// [32 - |K|, 32) of the low one, which the 2-bit field masks clear (they
+// cover bits 6..9 and 22..25).  Written as the instruction itself: seeing the
+// masks, the compiler would otherwise split it back into 32-bit shifts.
+template <int K>
+__device__ __forceinline__ void shl_pair(uint32_t lo, uint32_t hi, uint32_t& out_lo,
+                                         uint32_t& out_hi) {
+  static_assert(K >= -6 && K <= 6, "fields stay clear of the crossing bits");
+  const uint64_t v = ((uint64_t)hi << 32) | lo;
+  uint64_t r;
+  if constexpr (K >= 0)
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(K), "v"(v));
+  else
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(-K), "v"(v));
+  out_lo = (uint32_t)r;
+  out_hi = (uint32_t)(r >> 32);
+}
+
+// 2-bit codes of a 64-channel head: the two score tiles' A operands from a
+// lane's two key words (tile u: word u) and the four value tiles' from its two
+// value words (tiles 2w, 2w + 1 share word w), each pair of words shifted
+// together: the results of unpack_keys<64, 2> per word and unpack_value_tile<2>
+// per tile with half the shifts.
+__device__ __forceinline__ void unpack_keys_2x64(const uint32_t (&w)[2],
+                                                 uint32_t (&a)[2][2][4]) {
+  uint32_t x[4][2];
+  shl_pair<6>(w[0], w[1], x[0][0], x[0][1]);
+  shl_pair<2>(w[0], w[1], x[1][0], x[1][1]);
+  shl_pair<-2>(w[0], w[1], x[2][0], x[2][1]);
+  shl_pair<-6>(w[0], w[1], x[3][0], x[3][1]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      a[u][f >> 2][f & 3] = x[f >> 1][u] & ((f & 1) ? kMaskOdd<2> : kMaskEven<2>);
+}
+__device__ __forceinline__ void unpack_values_2x64(const uint32_t (&vw)[2],
+                                                   uint32_t (&a)[4][4]) {
+  uint32_t l6[2], l2[2], r2[2], r6[2];
+  shl_pair<6>(vw[0], vw[1], l6[0], l6[1]);
+  shl_pair<2>(vw[0], vw[1], l2[0], l2[1]);
+  shl_pair<-2>(vw[0], vw[1], r2[0], r2[1]);
+  shl_pair<-6>(vw[0], vw[1], r6[0], r6[1]);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int wi = n >> 1;
+    const uint32_t x0 = (n & 1) ? r2[wi] : l6[wi];
+    const uint32_t x1 = (n & 1) ? r6[wi] : l2[wi];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      a[n][e] = (e < 2 ? x0 : x1) & ((e & 1) ? kMaskOdd<2> : kMaskEven<2>);
+  }
+}
+
 template <int D, int BK>
 __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
                                             uint32_t (&a)[D / 32][4]) {
