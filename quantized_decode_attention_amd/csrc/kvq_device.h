@@ -563,10 +563,12 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
   static_assert(NO % kThreads == 0 || kThreads % NO == 0, "outputs tile the workgroup");
   constexpr bool kRotate = Fmt::kRotateOut;  // out = H o per head (64 channels)
   static_assert(!kRotate || (D == 64 && OPT == 1), "rotation covers one 64-channel head");
+  // (a row's 16 float4 outputs sit in 16 consecutive lanes of the first wave:
+  // the rotation's lane exchanges stay inside them)
+  static_assert(!kRotate || NO % 16 == 0, "a row's outputs are whole 16-lane groups");
   __shared__ int red[2 * kThreads / 64];
   __shared__ float4 s_o[kThreads];
   __shared__ float2 s_ml[kThreads];
-  __shared__ float s_rot[kRotate ? RS * D : 1];
   const auto& g = L.g;
   const int hkv = blockIdx.x / (GQ / RS), row0 = (blockIdx.x % (GQ / RS)) * RS;
   const int b = blockIdx.y, tid = threadIdx.x;
@@ -672,25 +674,37 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;  // a row that sees no position: 0
     const int64_t o = Fmt::row(L, b, hkv, oh) * D + oc;
     if constexpr (kRotate) {
-      // out_c = sum_j H[c][j] o_j, H[c][j] = (-1)^popcount(c & j) / 8
+      // out_c = sum_j H[c][j] o_j / 8, H[c][j] = (-1)^popcount(c & j): the fast
+      // Walsh-Hadamard transform, six butterfly stages (a, b) -> (a + b, a - b)
+      // over channel bits 0..5.  Lane i of a row's 16 holds channels 4 i .. 4 i
+      // + 3, so bits 0 and 1 pair values inside a lane and bits 2..5 pair lanes
+      // i and i ^ 2^(bit - 2).
       if (share == 0) {
-        s_rot[ol * D + oc + 0] = O.x * inv;
-        s_rot[ol * D + oc + 1] = O.y * inv;
-        s_rot[ol * D + oc + 2] = O.z * inv;
-        s_rot[ol * D + oc + 3] = O.w * inv;
-      }
-      __syncthreads();
-      if (share == 0) {
+        float x[4] = {O.x * inv, O.y * inv, O.z * inv, O.w * inv};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = oc + e;
-          float acc = 0.0f;
-          for (int j = 0; j < D; ++j) {
-            const float r = s_rot[ol * D + j];
-            acc += (__builtin_popcount(c & j) & 1) ? -r : r;
+        for (int sb = 0; sb < 2; ++sb) {  // channel bits 0, 1: inside the lane
+          const int sp = 1 << sb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (e & sp) continue;
+            const float a = x[e], bb = x[e + sp];
+            x[e] = a + bb;
+            x[e + sp] = a - bb;
           }
-          L.out[o + e] = f2h(acc * 0.125f);
         }
+        const int i = t % (D / 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {  // channel bits 2..5: across lanes
+          const int m = 1 << k;
+          const bool upper = (i & m) != 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __shfl_xor(x[e], m, 64);
+            x[e] = upper ? p - x[e] : x[e] + p;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.out[o + e] = f2h(x[e] * 0.125f);
       }
     } else if (share == 0) {
       L.out[o + 0] = f2h(O.x * inv);
