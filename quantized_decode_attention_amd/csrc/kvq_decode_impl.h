@@ -82,12 +82,18 @@ struct Cfg {
   static constexpr int NI = (KB + 1023) / 1024 + (VB + 1023) / 1024 + (VMB + 1023) / 1024 +
                             (KMB + 1023) / 1024;  // direct loads per chunk
   static_assert(NI <= 20, "vmcnt must hold the ring's loads");
-  // LDS (bytes) per wave: q' fragments [2][GQ][4][KC] x 16 B, beta [GQ] (+ a
+  // LDS (bytes) per wave: q' fragments (16 B slots, below), beta [GQ] (+ a
   // spare), two chunk slots
   // With one MFMA column per row (16 rows per KV head) every lane forms its
   // own q' fragments and no staging is needed.
   static constexpr bool kDirectFold = SL == 1;
-  static constexpr int kQB = kDirectFold ? 0 : 2 * GQ * 4 * KC * 16;
+  // q' fragment slots: one block of 4 KC slots (lane group, k-chunk) per head
+  // and part, the two parts of a head adjacent, each block padded by a slot.
+  // The 16 lanes of a fragment read differ only in head and part, so the
+  // padding puts their slots on distinct banks (unpadded they all share one).
+  static constexpr int kQBlk = 4 * KC + 1;
+  static constexpr int qb_slot(int part, int h, int r) { return (2 * h + part) * kQBlk + r; }
+  static constexpr int kQB = kDirectFold ? 0 : 2 * GQ * kQBlk * 16;
   static constexpr int kBetaB = kDirectFold ? 0 : 16 * ((GQ * 4 + 4 + 15) / 16);
   static constexpr int kRing = 2;
   static constexpr int kWaveLds = kQB + kBetaB + kRing * kSlot;
@@ -345,8 +351,8 @@ struct PackedWave {
         const float4 qb = *reinterpret_cast<const float4*>(qfs + h * kQS<D> + kmoff[1]);
         uint32_t hp[4], lp[4];
         bpart = fold_item(qa, qb, kmA, kmB, hp, lp);
-        qB[((0 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
-        qB[((1 * GQ + h) * 4 + gg) * KC + kc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+        qB[C::qb_slot(0, h, gg * KC + kc)] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+        qB[C::qb_slot(1, h, gg * KC + kc)] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
       }
       bpart = group_sum<IPH>(bpart);
       // every lane stores (no branch): a head's first item lane its beta, the
@@ -362,7 +368,7 @@ struct PackedWave {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const int part = kColSplit ? (slot & 1) : p;
-        const uint4 v = qB[((part * GQ + hcol) * 4 + lg) * KC + kc];
+        const uint4 v = qB[C::qb_slot(part, hcol, lg * KC + kc)];
         bq[p][kc][0] = v.x; bq[p][kc][1] = v.y; bq[p][kc][2] = v.z; bq[p][kc][3] = v.w;
       }
     beta_c = beta_l[hcol] * bscale;
