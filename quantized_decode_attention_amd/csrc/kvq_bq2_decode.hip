@@ -163,18 +163,10 @@ struct Bq2Wave {
   }
 
   __device__ __forceinline__ void load(int ch, Bq2Raw& r) const {
-    const uint2 k2 = *reinterpret_cast<const uint2*>(kcodes + ch * 128 + 2 * lane);
-    const uint2 v2 = *reinterpret_cast<const uint2*>(vcodes + ch * 128 + 2 * lane);
-    r.kw[0] = k2.x;
-    r.kw[1] = k2.y;
-    r.vw[0] = v2.x;
-    r.vw[1] = v2.y;
-    const uint2 km = *reinterpret_cast<const uint2*>(kmeta + ch * kChunk + 8 * lg + 2 * (lane & 3));
-    const uint2 vm = *reinterpret_cast<const uint2*>(vmeta + ch * kChunk + 8 * lg + 2 * (lane & 3));
-    r.km[0] = km.x;
-    r.km[1] = km.y;
-    r.vm[0] = vm.x;
-    r.vm[1] = vm.y;
+    load_run<2>(kcodes + ch * 128 + 2 * lane, r.kw);
+    load_run<2>(vcodes + ch * 128 + 2 * lane, r.vw);
+    load_run<2>(kmeta + ch * kChunk + 8 * lg + 2 * (lane & 3), r.km);
+    load_run<2>(vmeta + ch * kChunk + 8 * lg + 2 * (lane & 3), r.vm);
   }
 
   // Scores arrive as s / sc (sc > 0 per lane: a power of two), the running

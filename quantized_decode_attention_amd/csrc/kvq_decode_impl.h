@@ -250,9 +250,12 @@ struct PackedWave {
     }
   }
 
-  // Issues chunk ch's direct loads into slot r: the codes nontemporal (they
-  // stream through once), the meta plain (a key group's meta is read by each
-  // of its chunks).  Earlier reads of the slot are finished first.
+  // Issues chunk ch's direct loads into slot r, nontemporal wherever the bytes
+  // are read once per step (codes, value meta, and the key meta when a key
+  // group is one chunk): loads that do not allocate in the caches stream HBM
+  // faster.  A key group longer than a chunk has its meta read by each of its
+  // chunks, so that one is loaded plain.  Earlier reads of the slot are
+  // finished first.
   __device__ __forceinline__ void load(int ch, R& r) {
     const int64_t sl = slot_of(ch);
     const char* kc = reinterpret_cast<const char*>(kcodes + sl * (D * BK));
@@ -263,8 +266,8 @@ struct PackedWave {
     lds_dma_begin();
     lds_copy<C::KB, true>(kc, base, lane16, lane);
     lds_copy<C::VB, true>(vc, base + C::kSlotV, lane16, lane);
-    lds_copy<C::VMB, false>(vm, base + C::kSlotVM, lane16, lane);
-    lds_copy<C::KMB, false>(km, base + C::kSlotKM, lane16, lane);
+    lds_copy<C::VMB, true>(vm, base + C::kSlotVM, lane16, lane);
+    lds_copy<C::KMB, G == kChunk>(km, base + C::kSlotKM, lane16, lane);
   }
 
   // Waits until every chunk loaded but the last `ahead` is in its slot.
@@ -274,6 +277,36 @@ struct PackedWave {
   }
   // Slot i of the ring (0 <= i < kRing).
   __device__ __forceinline__ R slot_at(int i) const { return R{ring + i * (C::kSlot / 4)}; }
+
+  // A chunk's code words and value meta as this lane uses them.  They are read
+  // from the slot when the chunk's turn comes, before the key-group fold, so
+  // that the LDS latency of these reads overlaps the fold and the scores
+  // instead of following the fold's barrier and the softmax.
+  struct Words {
+    uint32_t kw[2][KW];   // key code words of the two score tiles
+    uint32_t vw[C::NW];   // value code words
+    uint32_t vmA[NF][4];  // value (scale, min) of tokens 8 lg + 2 i (run A)
+    uint32_t vmB[NF][4];  // ... and 8 lg + 2 i + 1 (run B)
+  };
+  __device__ __forceinline__ void read_words(const R& r, Words& cw) const {
+    uint32_t w[2 * KW];
+    lds_words<2 * KW>(r.s + kofs, w);
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      cw.kw[0][k] = w[k];
+      cw.kw[1][k] = w[KW + k];
+    }
+    lds_words<C::NW>(r.s + C::kSlotV / 4 + vofs, cw.vw);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      // value meta of tokens 8 lg + j: even j feed B elements 2i (run A), odd
+      // j elements 2i + 1 (run B)
+      const uint4* st = reinterpret_cast<const uint4*>(r.s + C::kSlotVM / 4 + vmofs[f]);
+      const uint4 x = st[0], y = st[1];
+      cw.vmA[f][0] = x.x; cw.vmA[f][1] = x.z; cw.vmA[f][2] = y.x; cw.vmA[f][3] = y.z;
+      cw.vmB[f][0] = x.y; cw.vmB[f][1] = x.w; cw.vmB[f][2] = y.y; cw.vmB[f][3] = y.w;
+    }
+  }
 
   // q' = q * 2^-E * key scale (hi/lo fp16 fragments in LDS) and beta' =
   // q * 2^-E . key min, for the key group starting in this chunk.
@@ -646,8 +679,10 @@ struct PackedWave {
                                                      const uint16_t* vres) {
     uint4 va[NT];
     window_values_load(ch * kChunk, Rv, vres, va);
+    Words cw;
+    read_words(r, cw);
     float s[NS];
-    packed_scores<true>(ch, r, n_tok - 1 - hide, s);
+    packed_scores<true>(ch, r, cw, n_tok - 1 - hide, s);
     float p[2][4];
     softmax<false>(s, p);
     window_values_mma(va, ch * kChunk, n_tok, p);
@@ -658,11 +693,13 @@ struct PackedWave {
   // accumulators are still at code scale), values from the codes.
   __device__ __forceinline__ void process_mixed_values(int ch, const R& r, int n_tok, int Rk,
                                                        const uint16_t* kres) {
+    Words cw;
+    read_words(r, cw);
     float s[NS];
     window_scores(ch * kChunk, n_tok, Rk, kres, s);
     float p[2][4];
     softmax<true>(s, p);
-    packed_values(r, p);
+    packed_values(cw, p);
   }
 
   // kMask: positions after last_vis (this lane's row, 32-token chunk ch) get
@@ -670,19 +707,21 @@ struct PackedWave {
   // are real cache data, so their weight 0 is exact).
   template <bool kMask = false>
   __device__ __forceinline__ void process(int ch, const R& r, int last_vis = 0) {
+    Words cw;
+    read_words(r, cw);
     float s[NS];
-    packed_scores<kMask>(ch, r, last_vis, s);
+    packed_scores<kMask>(ch, r, cw, last_vis, s);
     float p[2][4];
     softmax<true>(s, p);
-    packed_values(r, p);
+    packed_values(cw, p);
   }
 
   // Scores of packed chunk ch (folding the key group's meta when it starts):
   // s = 2^(E+24) * (codes x q') + beta; with kMask, positions after last_vis
   // get -inf.
   template <bool kMask>
-  __device__ __forceinline__ void packed_scores(int ch, const R& r, int last_vis,
-                                                float (&s)[NS]) {
+  __device__ __forceinline__ void packed_scores(int ch, const R& r, const Words& cw,
+                                                int last_vis, float (&s)[NS]) {
     if constexpr (G == kChunk) {
       fold(r);  // every chunk is a key group: no branch, so the fold can be
                 // scheduled against the previous chunk's value products
@@ -693,21 +732,11 @@ struct PackedWave {
         fold(r);
       }
     }
-    uint32_t kw[2][KW];
-    {
-      uint32_t w[2 * KW];
-      lds_words<2 * KW>(r.s + kofs, w);
-#pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        kw[0][k] = w[k];
-        kw[1][k] = w[KW + k];
-      }
-    }
     f4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t a[KC][4];
-      unpack_keys<D, BK>(kw[u], a);
+      unpack_keys<D, BK>(cw.kw[u], a);
       acc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
@@ -727,20 +756,11 @@ struct PackedWave {
 
   // Weighted sum of a packed chunk's values (code-scale accumulators, weights
   // in the packed classes) and its value-min term.
-  __device__ __forceinline__ void packed_values(const R& r, const float (&p)[2][4]) {
-    uint32_t vw[C::NW];
-    lds_words<C::NW>(r.s + C::kSlotV / 4 + vofs, vw);
+  __device__ __forceinline__ void packed_values(const Words& cw, const float (&p)[2][4]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      // value (scale, min) of tokens 8 lg + j: even j feed B elements 2i
-      // (run A), odd j elements 2i + 1 (run B)
-      uint32_t mA[4], mB[4];
-      {
-        const uint4* st = reinterpret_cast<const uint4*>(r.s + C::kSlotVM / 4 + vmofs[f]);
-        const uint4 x = st[0], y = st[1];
-        mA[0] = x.x; mA[1] = x.z; mA[2] = y.x; mA[3] = y.z;
-        mB[0] = x.y; mB[1] = x.w; mB[2] = y.y; mB[3] = y.w;
-      }
+      const uint32_t(&mA)[4] = cw.vmA[f];
+      const uint32_t(&mB)[4] = cw.vmB[f];
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -756,7 +776,7 @@ struct PackedWave {
       for (int n = 0; n < NT; ++n) {
         if (C::gam(n) / SL != f) continue;  // compile-time
         uint32_t a[4];
-        unpack_value_tile<BV>(vw, n, a);
+        unpack_value_tile<BV>(cw.vw, n, a);
         oacc[n] = mfma(a, bh, oacc[n]);
         oacc[n] = mfma(a, bl, oacc[n]);
       }
