@@ -1077,41 +1077,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeLaunch L) {
   __shared__ __attribute__((aligned(16))) char smem[kWaveSmem<D, BK, BV, GQ, NG>];
   const int lane = threadIdx.x;
   const int w = blockIdx.x, nw = gridDim.x;
-  // Speculation: if every length equals max_seq_len (a uniform batch), the
-  // work layout is plain arithmetic, so the first segment's first chunk can
-  // be requested before the lengths are read.  The loads are in bounds
-  // whatever the lengths; they are used only if the lengths confirm it.
-  using PW = PackedWave<D, BK, BV, GQ, NG, PG>;
-  using RW = Raw<D, BK, BV, GQ, NG>;
-  const SeqWork ss = seq_work_of(L, L.max_seq_len);
-  const int per_seq = ss.w * L.g.Hkv;
-  const int cpw_s = (per_seq * L.g.B + nw - 1) / nw;
-  const int x0_s = w * cpw_s, x1_s = min(per_seq * L.g.B, x0_s + cpw_s);
-  bool spec = ss.w > 0 && x0_s < x1_s;
-  int b_s = 0, hkv_s = 0, xu_s = 0;
-  SegRange r_s{0, 0, 0, 0};
-  if (spec) {
-    b_s = x0_s / per_seq;
-    hkv_s = (x0_s - b_s * per_seq) / ss.w;
-    xu_s = b_s * per_seq + hkv_s * ss.w;
-    r_s = seg_range(L, ss, xu_s, x0_s, x1_s);
-    spec = r_s.pc0 < r_s.pc1;
-  }
-  PW ws;
-  RW ra_s;
-  if (spec) seg_begin<D, BK, BV, GQ, NG, PG>(L, b_s, hkv_s, r_s, smem, lane, ws, ra_s);
-
   const BatchWork bw = batch_work<KiviWork>(L, lane);  // one read of the lengths
   const int total = bw.total;
   const int cpw = (total + nw - 1) / nw;
   const int x0 = w * cpw;
   const int x1 = min(total, x0 + cpw);
   int x = x0;
-  if (spec && bw.uniform) {  // confirmed: the speculative first segment stands
-    seg_run<D, BK, BV, GQ, NG, PG>(L, b_s, hkv_s, ss, r_s, w + b_s * L.g.Hkv + hkv_s, smem, lane,
-                               ws, ra_s);
-    x = xu_s + ss.w;
-  }
   while (x < x1) {
     int b, base;
     wave_find_seq<KiviWork>(L, bw, lane, x, b, base);

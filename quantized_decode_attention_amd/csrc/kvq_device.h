@@ -468,11 +468,9 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 // The batch's work layout as one wave sees it: for the first 64 sequences,
 // lane b holds sequence b's work over all its KV heads (c) and the inclusive
 // prefix (inc); total covers the whole batch.
-// uniform: every length equals max_seq_len.
 struct BatchWork {
   int c, inc, head_total, total;
   int n;  // lane b < 64: length of sequence b
-  bool uniform;
 };
 
 template <class Fmt>
@@ -484,13 +482,11 @@ __device__ __forceinline__ BatchWork batch_work(const typename Fmt::Launch& L, i
   bw.inc = wave_scan_incl(bw.c);
   bw.head_total = __builtin_amdgcn_readlane(bw.inc, 63);
   bw.total = bw.head_total;
-  bw.uniform = __ballot(n != L.max_seq_len) == 0;
   for (int b0 = 64; b0 < L.g.B; b0 += 64) {  // batches beyond 64 sequences
     const int nb = b0 + lane < L.g.B ? L.seq_lens[b0 + lane] : L.max_seq_len;
     int s = b0 + lane < L.g.B ? Fmt::work_of(L, nb).w * L.g.Hkv : 0;
     s = wave_scan_incl(s);
     bw.total += __builtin_amdgcn_readlane(s, 63);
-    bw.uniform = bw.uniform && __ballot(nb != L.max_seq_len) == 0;
   }
   return bw;
 }
