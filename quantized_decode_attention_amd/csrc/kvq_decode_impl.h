@@ -98,6 +98,7 @@ struct Cfg {
   static constexpr int kRing = 2;
   static constexpr int kWaveLds = kQB + kBetaB + kRing * kSlot;
   static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
+  static_assert(G >= 32, "value tiles 2k and 2k + 1 share a group");
 };
 
 // The LDS slot a 32-token chunk is loaded into (Cfg::kSlot bytes).
@@ -772,13 +773,27 @@ struct PackedWave {
         bacc = mul_hi(pa, mA[i], bacc);
         bacc = mul_hi(pb, mB[i], bacc);
       }
+      if constexpr (BV != 4) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        if (C::gam(n) / SL != f) continue;  // compile-time
-        uint32_t a[4];
-        unpack_value_tile<BV>(cw.vw, n, a);
-        oacc[n] = mfma(a, bh, oacc[n]);
-        oacc[n] = mfma(a, bl, oacc[n]);
+        for (int n = 0; n < NT; ++n) {
+          if (C::gam(n) / SL != f) continue;  // compile-time
+          uint32_t a[4];
+          unpack_value_tile<BV>(cw.vw, n, a);
+          oacc[n] = mfma(a, bh, oacc[n]);
+          oacc[n] = mfma(a, bl, oacc[n]);
+        }
+      } else {
+        // 4-bit tiles in pairs (a group holds at least two 16-channel tiles)
+#pragma unroll
+        for (int n = 0; n < NT; n += 2) {
+          if (C::gam(n) / SL != f) continue;  // compile-time
+          uint32_t a0[4], a1[4];
+          unpack_value_tiles2<BV>(cw.vw, n, a0, a1);
+          oacc[n] = mfma(a0, bh, oacc[n]);
+          oacc[n + 1] = mfma(a1, bh, oacc[n + 1]);
+          oacc[n] = mfma(a0, bl, oacc[n]);
+          oacc[n + 1] = mfma(a1, bl, oacc[n + 1]);
+        }
       }
     }
   }

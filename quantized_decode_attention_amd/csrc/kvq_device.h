@@ -284,36 +284,54 @@ __device__ __forceinline__ void unpack_values_2x64(const uint32_t (&vw)[2],
 template <int D, int BK>
 __device__ __forceinline__ void unpack_keys(const uint32_t (&w)[kKW<D, BK>],
                                             uint32_t (&a)[D / 32][4]) {
-  if constexpr (BK == 2) {
-    // field s of a half (bits 2s) to bit 6 (even s) or 8 (odd s): fields
-    // 2j, 2j + 1 share the shift 6 - 4j
+  constexpr int KW = kKW<D, BK>;
+  if constexpr (BK == 2 || BK == 4) {
+    // 2 bits: field s of a half (bits 2s) to bit 6 (even s) or 8 (odd s):
+    // fields 2j, 2j + 1 share the shift 6 - 4j.  4 bits: nibble s of a half
+    // (bits 4s) to bits 6..9.  Words are shifted in pairs (one 64-bit shift
+    // for two words) where there are two.
 #pragma unroll
-    for (int wi = 0; wi < kKW<D, BK>; ++wi) {
-      const uint32_t x[4] = {shl<6>(w[wi]), shl<2>(w[wi]), shl<-2>(w[wi]), shl<-6>(w[wi])};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int ri = 8 * wi + s;
-        a[ri >> 2][ri & 3] = x[s >> 1] & ((s & 1) ? kMaskOdd<2> : kMaskEven<2>);
+    for (int wp = 0; wp < KW; wp += 2) {
+      constexpr int NP = KW >= 2 ? 2 : 1;
+      uint32_t x[4][NP];
+      if constexpr (NP == 2) {
+        shl_pair<6>(w[wp], w[wp + 1], x[0][0], x[0][1]);
+        shl_pair<2>(w[wp], w[wp + 1], x[1][0], x[1][1]);
+        shl_pair<-2>(w[wp], w[wp + 1], x[2][0], x[2][1]);
+        shl_pair<-6>(w[wp], w[wp + 1], x[3][0], x[3][1]);
+      } else {
+        x[0][0] = shl<6>(w[wp]);
+        x[1][0] = shl<2>(w[wp]);
+        x[2][0] = shl<-2>(w[wp]);
+        x[3][0] = shl<-6>(w[wp]);
       }
-    }
-  } else if constexpr (BK == 4) {
-    // nibble s of a half (bits 4s) to bits 6..9
 #pragma unroll
-    for (int wi = 0; wi < kKW<D, BK>; ++wi) {
-      const uint32_t x[4] = {shl<6>(w[wi]), shl<2>(w[wi]), shl<-2>(w[wi]), shl<-6>(w[wi])};
+      for (int k = 0; k < NP; ++k) {
+        const int wi = wp + k;
+        if constexpr (BK == 2) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[wi][s] = x[s] & kMaskEven<4>;
+          for (int s = 0; s < 8; ++s) {
+            const int ri = 8 * wi + s;
+            a[ri >> 2][ri & 3] = x[s >> 1][k] & ((s & 1) ? kMaskOdd<2> : kMaskEven<2>);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) a[wi][s] = x[s][k] & kMaskEven<4>;
+        }
+      }
     }
   } else {
     // k-chunk kc from words 2kc + (s/2): pair s is bytes 0, 2 (s even) or
-    // 1, 3 (s odd) of that word, moved to bits 2..9 of each half
+    // 1, 3 (s odd) of that word, moved to bits 2..9 of each half (the two
+    // words of a k-chunk shifted together)
 #pragma unroll
-    for (int kc = 0; kc < D / 32; ++kc)
+    for (int kc = 0; kc < D / 32; ++kc) {
+      uint32_t l2[2], r6[2];
+      shl_pair<2>(w[2 * kc], w[2 * kc + 1], l2[0], l2[1]);
+      shl_pair<-6>(w[2 * kc], w[2 * kc + 1], r6[0], r6[1]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t wv = w[2 * kc + (s >> 1)];
-        a[kc][s] = ((s & 1) ? shl<-6>(wv) : shl<2>(wv)) & kMaskEven<8>;
-      }
+      for (int s = 0; s < 4; ++s) a[kc][s] = ((s & 1) ? r6[s >> 1] : l2[s >> 1]) & kMaskEven<8>;
+    }
   }
 }
 
@@ -337,11 +355,31 @@ __device__ __forceinline__ void unpack_value_tile(const uint32_t (&vw)[NW], int 
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = (e < 2 ? x0 : x1) & ((e & 1) ? kMaskOdd<2> : kMaskEven<2>);
   } else {
+    // the tile's two words shifted together
+    uint32_t l2[2], r6[2];
+    shl_pair<2>(vw[2 * n], vw[2 * n + 1], l2[0], l2[1]);
+    shl_pair<-6>(vw[2 * n], vw[2 * n + 1], r6[0], r6[1]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = vw[2 * n + (e >> 1)];
-      a[e] = ((e & 1) ? shl<-6>(w) : shl<2>(w)) & kMaskEven<8>;
-    }
+    for (int e = 0; e < 4; ++e) a[e] = ((e & 1) ? r6[e >> 1] : l2[e >> 1]) & kMaskEven<8>;
+  }
+}
+
+// 4-bit value tiles n and n + 1 (n even) at once, their code words shifted in
+// pairs (one 64-bit shift for two words); the same operands as
+// unpack_value_tile.
+template <int BV, int NW>
+__device__ __forceinline__ void unpack_value_tiles2(const uint32_t (&vw)[NW], int n,
+                                                    uint32_t (&a0)[4], uint32_t (&a1)[4]) {
+  static_assert(BV == 4, "4-bit tiles (2-bit tiles share one word, 8-bit ones pair inside)");
+  uint32_t x[4][2];
+  shl_pair<6>(vw[n], vw[n + 1], x[0][0], x[0][1]);
+  shl_pair<2>(vw[n], vw[n + 1], x[1][0], x[1][1]);
+  shl_pair<-2>(vw[n], vw[n + 1], x[2][0], x[2][1]);
+  shl_pair<-6>(vw[n], vw[n + 1], x[3][0], x[3][1]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a0[e] = x[e][0] & kMaskEven<4>;
+    a1[e] = x[e][1] & kMaskEven<4>;
   }
 }
 
