@@ -63,7 +63,18 @@ struct Cfg {
   static constexpr int KW = kKW<D, BK>;           // key words per lane and row
   static constexpr int WR = D * BK / 32;          // words per key row
   static constexpr int SL = 16 / GQ;              // MFMA columns per head
-  static constexpr int NF = (NG + SL - 1) / SL;   // value-side B fragments
+  // Value side.  When half of a head's MFMA columns can hold all its value
+  // groups (kVSplit: at least four columns, NG <= SL / 2), column bit 0
+  // selects the hi or lo fp16 part of the weights and the other bits a value
+  // group (VH groups per fragment), so a value tile takes one MFMA and the
+  // parts are added once, when the partial is written; otherwise each column
+  // of a head is a group (VH = SL) and the hi and lo parts are two MFMAs into
+  // one accumulator.  (With more groups than that the split would need a
+  // second weight fragment, whose VALU work costs more than the MFMAs saved:
+  // 54.0 against 52.8 us at four groups and four columns per head.)
+  static constexpr bool kVSplit = SL >= 4 && NG <= SL / 2;
+  static constexpr int VH = kVSplit ? SL / 2 : SL;
+  static constexpr int NF = (NG + VH - 1) / VH;   // value-side B fragments
   static constexpr int IPH = 4 * KC;              // fold items per head
   static constexpr int ITEMS = GQ * IPH;          // fold items per key group
   static constexpr int IPL = (ITEMS + 63) / 64;   // fold items per lane
@@ -98,6 +109,7 @@ struct Cfg {
   static constexpr int kRing = 2;
   static constexpr int kWaveLds = kQB + kBetaB + kRing * kSlot;
   static constexpr int gam(int n) { return (16 * n) / G; }  // group of value tile n
+  static constexpr int frag(int n) { return gam(n) / VH; }  // its value-side fragment
   static_assert(G >= 32, "value tiles 2k and 2k + 1 share a group");
 };
 
@@ -150,6 +162,7 @@ struct PackedWave {
   uint32_t* ring;  // the wave's chunk slots
   // lane constants
   int lane, col, lg, hcol, slot;
+  int gsel;            // value group selector of this lane's column (within a fragment)
   uint32_t lane16;     // 16 * lane: a lane's piece of a direct load
   int kofs, vofs;      // this lane's key / value words inside a chunk
   int vmofs[NF];       // value meta run of fragment f inside a chunk
@@ -189,8 +202,9 @@ struct PackedWave {
     m_slot2 = 0u - (uint32_t)((slot >> 1) & 1);  // (from 4 columns per head: the quad position's bits)
     kofs = lane * 2 * KW;
     vofs = lane * C::NW;
+    gsel = C::kVSplit ? slot >> 1 : slot;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) vmofs[f] = (lg * NG + (f * SL + slot) % NG) * 8;
+    for (int f = 0; f < NF; ++f) vmofs[f] = (lg * NG + (f * C::VH + gsel) % NG) * 8;
 #pragma unroll
     for (int i = 0; i < IPL; ++i) fitem[i] = lane + 64 * i;
     {
@@ -556,7 +570,8 @@ struct PackedWave {
     constexpr float oscale = 16777216.0f / float(1 << kCodeLift<BV>) / kValEven<BV> * kPlain;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const float bsum = btot[C::gam(n) / SL];
+      // (split columns: the value-min term goes to the hi part's column only)
+      const float bsum = C::kVSplit ? bit_sel(m_slot1, 0.0f, btot[C::frag(n)]) : btot[C::frag(n)];
 #pragma unroll
       for (int q = 0; q < 4; ++q) oacc[n][q] = __builtin_fmaf(oacc[n][q], oscale, bsum);
     }
@@ -621,12 +636,16 @@ struct PackedWave {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       split2(p[i >> 1][2 * (i & 1)], p[i >> 1][2 * (i & 1) + 1], m1, bh[i], bl[i]);
+    if constexpr (C::kVSplit) {  // this lane's column takes the hi or the lo part
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bh[i] ^= (bl[i] ^ bh[i]) & m_slot1;
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const uint32_t a[4] = {va[n].x & vmask[0], va[n].y & vmask[1], va[n].z & vmask[2],
                              va[n].w & vmask[3]};
       oacc[n] = mfma(a, bh, oacc[n]);
-      oacc[n] = mfma(a, bl, oacc[n]);
+      if constexpr (!C::kVSplit) oacc[n] = mfma(a, bl, oacc[n]);
     }
   }
   // Scores of positions t0 + [0, 32) from the key window (B fragments from
@@ -773,26 +792,32 @@ struct PackedWave {
         bacc = mul_hi(pa, mA[i], bacc);
         bacc = mul_hi(pb, mB[i], bacc);
       }
+      if constexpr (C::kVSplit) {  // this lane's column takes the hi or the lo part
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bh[i] ^= (bl[i] ^ bh[i]) & m_slot1;
+      }
       if constexpr (BV != 4) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          if (C::gam(n) / SL != f) continue;  // compile-time
+          if (C::frag(n) != f) continue;  // compile-time
           uint32_t a[4];
           unpack_value_tile<BV>(cw.vw, n, a);
           oacc[n] = mfma(a, bh, oacc[n]);
-          oacc[n] = mfma(a, bl, oacc[n]);
+          if constexpr (!C::kVSplit) oacc[n] = mfma(a, bl, oacc[n]);
         }
       } else {
         // 4-bit tiles in pairs (a group holds at least two 16-channel tiles)
 #pragma unroll
         for (int n = 0; n < NT; n += 2) {
-          if (C::gam(n) / SL != f) continue;  // compile-time
+          if (C::frag(n) != f) continue;  // compile-time
           uint32_t a0[4], a1[4];
           unpack_value_tiles2<BV>(cw.vw, n, a0, a1);
           oacc[n] = mfma(a0, bh, oacc[n]);
           oacc[n + 1] = mfma(a1, bh, oacc[n + 1]);
-          oacc[n] = mfma(a0, bl, oacc[n]);
-          oacc[n + 1] = mfma(a1, bl, oacc[n + 1]);
+          if constexpr (!C::kVSplit) {
+            oacc[n] = mfma(a0, bl, oacc[n]);
+            oacc[n + 1] = mfma(a1, bl, oacc[n + 1]);
+          }
         }
       }
     }
@@ -884,7 +909,7 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
                                         Raw<D, BK, BV, GQ, NG>& ra) {
   using C = Cfg<D, BK, BV, GQ, NG>;
   using R = Raw<D, BK, BV, GQ, NG>;
-  constexpr int NT = C::NT, SL = C::SL;
+  constexpr int NT = C::NT;
   constexpr int QPH = D / 64;  // query values per lane and head
   constexpr int DP = D + kPartPad;
   const Geom& g = L.g;
@@ -1047,10 +1072,14 @@ __device__ __forceinline__ void seg_run(const DecodeLaunch& L, int b, int hkv, c
   float* part = part_base + w.hcol * DP;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const int gm = C::gam(n);
-    if (gm % SL != w.slot) continue;
-    const float4 v = make_float4(w.oacc[n][0], w.oacc[n][1], w.oacc[n][2], w.oacc[n][3]);
-    *reinterpret_cast<float4*>(part + 16 * n + 4 * w.lg) = v;
+    f4 o = w.oacc[n];
+    if constexpr (C::kVSplit) {  // hi + lo parts: neighbouring columns
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = PackedWave<D, BK, BV, GQ, NG, PG>::pair_add(o[q]);
+      if (w.slot & 1) continue;
+    }
+    if (C::gam(n) % C::VH != w.gsel) continue;
+    *reinterpret_cast<float4*>(part + 16 * n + 4 * w.lg) = make_float4(o[0], o[1], o[2], o[3]);
   }
   if (w.lg == 0 && w.slot == 0) {
     part[D] = w.m_run;
