@@ -66,6 +66,27 @@ struct Bq2Work {
   }
 };
 
+// Words in the global address space, and p as such a pointer made wave-uniform
+// (its value in the first active lane): address arithmetic on it stays in
+// scalar registers, and a load from it plus a lane offset takes the
+// scalar-base + vector-offset form (no 64-bit vector add per load).  Only for
+// pointers into global memory that are the same in every lane.
+typedef __attribute__((address_space(1))) const uint32_t gword;
+__device__ __forceinline__ gword* wave_uniform(const uint32_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((uint32_t)v));
+  return reinterpret_cast<gword*>(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+// Two consecutive words (8-byte aligned) from global memory as one
+// nontemporal load.
+__device__ __forceinline__ void load_pair_nt(gword* p, uint32_t (&w)[2]) {
+  typedef __attribute__((address_space(1))) const unsigned int __attribute__((ext_vector_type(2))) gu2;
+  const auto v = __builtin_nontemporal_load((gu2*)p);
+  w[0] = v.x;
+  w[1] = v.y;
+}
+
 // A lane's share of one 32-position chunk.
 struct Bq2Raw {
   uint32_t kw[2];  // key code words of score tiles 0, 1
@@ -163,10 +184,12 @@ struct Bq2Wave {
   }
 
   __device__ __forceinline__ void load(int ch, Bq2Raw& r) const {
-    load_run<2>(kcodes + ch * 128 + 2 * lane, r.kw);
-    load_run<2>(vcodes + ch * 128 + 2 * lane, r.vw);
-    load_run<2>(kmeta + ch * kChunk + 8 * lg + 2 * (lane & 3), r.km);
-    load_run<2>(vmeta + ch * kChunk + 8 * lg + 2 * (lane & 3), r.vm);
+    // chunk bases wave-uniform, lane offsets apart
+    const int lm = 8 * lg + 2 * (lane & 3);
+    load_pair_nt(wave_uniform(kcodes + ch * 128) + 2 * lane, r.kw);
+    load_pair_nt(wave_uniform(vcodes + ch * 128) + 2 * lane, r.vw);
+    load_pair_nt(wave_uniform(kmeta + ch * kChunk) + lm, r.km);
+    load_pair_nt(wave_uniform(vmeta + ch * kChunk) + lm, r.vm);
   }
 
   // Scores arrive as s / sc (sc > 0 per lane: a power of two), the running
