@@ -77,6 +77,11 @@ def parse():
     p.add_argument("--probe-sweep", action="store_true",
                    help="only sweep the plain stream-read probe over waves per SIMD, loads "
                         "in flight per lane and nontemporal loads; prints one JSON line")
+    p.add_argument("--probe-chunks", action="store_true",
+                   help="only run the chunk-stream probe: the decode partial kernel's loads for "
+                        "the --config workload (its 32-token chunk pieces, one chunk per work "
+                        "unit) without the arithmetic, then with 16..192 dependent FMAs per "
+                        "chunk; prints one JSON line")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (5 times); used to "
                         "calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -743,6 +748,25 @@ def main():
 
     w = synth.WORKLOADS[a.config]
     torch.cuda.set_device(torch.device("cuda:0"))
+    if a.probe_chunks:
+        if w.fmt != "kivi":
+            print(json.dumps({"error": "--probe-chunks takes a KIVI-format workload"}))
+            sys.exit(2)
+        # a packed 32-token chunk's pieces, as the partial kernel loads them: key
+        # codes, value codes, value meta, and the key group's meta (a chunk's share)
+        D, ng = w.head_dim, w.head_dim // w.group
+        pieces = [32 * D * w.k_bits // 8, 32 * D * w.v_bits // 8, 32 * ng * 4,
+                  D * 4 * 32 // w.group]
+        pieces = [max(512, (b + 511) // 512 * 512) for b in pieces]
+        n_chunks = w.batch * w.n_kv_heads * w.context // 32
+        res = kvq.chunk_stream(pieces, n_chunks, [0, 16, 32, 64, 96, 128, 192])
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        for r in res:
+            r["us_per_chunk_and_wave"] = round(r["median_us"] * 2 * 4 * cus / n_chunks, 3)
+        print(json.dumps({"probe": "kvq_probe_chunk_stream", "workload": w.name,
+                          "piece_bytes": pieces, "n_chunks": n_chunks,
+                          "waves": 2 * 4 * cus, "rows": res}), flush=True)
+        return
     if w.fmt == "bq2":
         rec = run_bq2(a, w, torch, kvq, metrics, synth)
     else:

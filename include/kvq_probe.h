@@ -39,6 +39,24 @@ int kvq_probe_stream_read_sweep(const void *buf, size_t bytes, uint32_t *sink,
                                 int32_t waves_per_simd, int32_t loads_per_lane,
                                 int32_t nontemporal, void *stream);
 
+/* The decode partial kernel's load stream without its arithmetic, for
+ * telling a kernel bound by its loads from one bound by its instructions:
+ * n_chunks chunks of four pieces, piece i of chunk c being bytes_i bytes at
+ * buf_i + c * bytes_i (buf_i device memory of n_chunks * bytes_i bytes,
+ * 16-byte aligned, owned by the caller and only read; each bytes_i a
+ * multiple of 512, the four summing to at most 4096), each chunk brought into
+ * a per-wave ring of two LDS slots with nontemporal direct loads
+ * (global_load_lds_dwordx4, 1 KB per instruction, a 512-byte rest with half
+ * the lanes), the next chunk requested before the current one is read back,
+ * then spin dependent fp32 multiply-adds (0 <= spin <= 4096) standing in for
+ * the per-chunk arithmetic.  2 x 4 x (compute units) single-wave workgroups,
+ * each a contiguous share of the chunks.  Returns KVQ_ERR_RANGE for sizes
+ * outside these bounds; status codes and sink as kvq_probe_stream_read. */
+int kvq_probe_chunk_stream(const void *buf_a, const void *buf_b, const void *buf_c,
+                           const void *buf_d, int64_t n_chunks, int32_t bytes_a,
+                           int32_t bytes_b, int32_t bytes_c, int32_t bytes_d, int32_t spin,
+                           uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

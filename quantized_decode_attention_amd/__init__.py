@@ -28,4 +28,4 @@ from ._lib import (  # noqa: F401
     kvq_paged_decode_partial, kvq_paged_decode_workspace_bytes, kvq_paged_prefill,
     kvq_paged_validate)
 from ._lib import kvq_decode_attn_noalloc  # noqa: F401
-from ._lib import stream_read_gbs, stream_read_sweep  # noqa: F401  (measurement aids)
+from ._lib import chunk_stream, stream_read_gbs, stream_read_sweep  # noqa: F401  (measurement aids)

@@ -54,7 +54,8 @@ EXPORTS_PAGED = [
     "kvq_paged_prefill", "kvq_paged_append", "kvq_paged_append_tokens", "kvq_paged_decode_attn",
     "kvq_paged_decode_partial", "kvq_paged_decode_combine", "kvq_paged_decode_attn_multi",
 ]
-EXPORTS_PROBE = ["kvq_probe_stream_read", "kvq_probe_sink_words", "kvq_probe_stream_read_sweep"]
+EXPORTS_PROBE = ["kvq_probe_stream_read", "kvq_probe_sink_words", "kvq_probe_stream_read_sweep",
+                 "kvq_probe_chunk_stream"]
 BQ2_HEAD_DIM = 64
 BQ2_SINKS = 4
 
@@ -114,6 +115,8 @@ def lib() -> ctypes.CDLL:
             "kvq_probe_stream_read": (ctypes.c_int, [P, sz, P, P]),
             "kvq_probe_sink_words": (ctypes.c_int, [ctypes.POINTER(i32)]),
             "kvq_probe_stream_read_sweep": (ctypes.c_int, [P, sz, P, i32, i32, i32, P]),
+            "kvq_probe_chunk_stream": (ctypes.c_int, [P, P, P, P, ctypes.c_int64, i32, i32, i32,
+                                                      i32, i32, P, P]),
             "kvq_paged_validate": (ctypes.c_int, [G, CP]),
             "kvq_paged_cache_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
             "kvq_paged_decode_workspace_bytes": (ctypes.c_int, [G, i32, i32, ctypes.POINTER(sz)]),
@@ -669,6 +672,50 @@ def stream_read_sweep(shapes, nbytes: int = 2 << 30, reps: int = 10, device="cud
                     "bytes_in_flight_per_wave": [64 * 16 * loads, 2 * 64 * 16 * loads],
                     "gbs": round(nbytes / t / 1e9, 1), "median_us": round(t * 1e6, 2)})
     del buf
+    return out
+
+
+def chunk_stream(piece_bytes, n_chunks: int, spins, copies: int = 4, reps: int = 20,
+                 device="cuda") -> list:
+    """Rate of kvq_probe_chunk_stream (the decode partial kernel's load stream
+    without its arithmetic) for chunks of the four given piece sizes, for each
+    spin (dependent multiply-adds per chunk).  Launches run back to back in
+    rounds of 2 x copies, rotating over copies buffer sets so that the Infinity
+    Cache holds none of a launch's bytes, with HIP events around each round
+    (as the decode kernel is timed); the median round / launches is reported.
+    A measurement aid."""
+    words = ctypes.c_int32()
+    _check(lib().kvq_probe_sink_words(ctypes.byref(words)), "kvq_probe_sink_words")
+    sets = [[torch.ones(n_chunks * b // 4, dtype=torch.int32, device=device) for b in piece_bytes]
+            for _ in range(copies)]
+    sink = torch.zeros(words.value, dtype=torch.int32, device=device)
+    st = torch.cuda.current_stream()
+
+    def launch(k, spin):
+        _check(lib().kvq_probe_chunk_stream(
+            *[ctypes.c_void_p(x.data_ptr()) for x in sets[k % copies]], int(n_chunks),
+            *[int(x) for x in piece_bytes], int(spin), ctypes.c_void_p(sink.data_ptr()),
+            ctypes.c_void_p(st.cuda_stream)), "kvq_probe_chunk_stream")
+
+    out = []
+    per_round = 2 * copies
+    for spin in spins:
+        for k in range(copies):
+            launch(k, spin)
+        times = []
+        for r in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for k in range(per_round):
+                launch(k, spin)
+            b.record(st)
+            b.synchronize()
+            times.append(a.elapsed_time(b) / 1e3 / per_round)
+        t = float(np.median(times))
+        nbytes = n_chunks * sum(piece_bytes)
+        out.append({"spin": spin, "median_us": round(t * 1e6, 2),
+                    "gbs": round(nbytes / t / 1e9, 1)})
+    del sets
     return out
 
 

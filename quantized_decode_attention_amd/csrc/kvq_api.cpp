@@ -941,6 +941,43 @@ int kvq_probe_sink_words(int32_t* words) {
   return KVQ_OK;
 }
 
+int kvq_probe_chunk_stream(const void* buf_a, const void* buf_b, const void* buf_c,
+                           const void* buf_d, int64_t n_chunks, int32_t bytes_a,
+                           int32_t bytes_b, int32_t bytes_c, int32_t bytes_d, int32_t spin,
+                           uint32_t* sink, void* stream) {
+  try {
+    const void* const bufs[4] = {buf_a, buf_b, buf_c, buf_d};
+    const int32_t bytes[4] = {bytes_a, bytes_b, bytes_c, bytes_d};
+    static const char* const names[4] = {"buf_a", "buf_b", "buf_c", "buf_d"};
+    int st = KVQ_OK;
+    int64_t total = 0;
+    for (int p = 0; p < 4; ++p) {
+      if ((st = check_ptr(bufs[p], names[p])) != KVQ_OK) return st;
+      if (bytes[p] < 0 || bytes[p] % 512 != 0)
+        return fail(KVQ_ERR_RANGE, "piece %d bytes (%d) must be a multiple of 512", p, bytes[p]);
+      total += bytes[p];
+    }
+    if ((st = check_ptr(sink, "sink")) != KVQ_OK) return st;
+    if (total <= 0 || total > 4096)
+      return fail(KVQ_ERR_RANGE, "a chunk's pieces (%lld bytes) must sum to 1..4096 bytes",
+                  (long long)total);
+    if (n_chunks <= 0) return fail(KVQ_ERR_RANGE, "n_chunks (%lld) must be positive",
+                                   (long long)n_chunks);
+    if (spin < 0 || spin > 4096) return fail(KVQ_ERR_RANGE, "spin (%d) must be in [0, 4096]", spin);
+    int cus = 0;
+    if ((st = cu_count(&cus)) != KVQ_OK) return st;
+    const int waves = 2 * 4 * cus;
+    if (waves > kvq::probe_sink_words())
+      return fail(KVQ_ERR_RANGE, "%d waves exceed the sink's %d words", waves,
+                  kvq::probe_sink_words());
+    hipError_t e = kvq::launch_chunk_stream(bufs, n_chunks, bytes, spin, waves, sink,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "chunk stream launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 int kvq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   try {
     int st = check_ptr(buf, "buf");

@@ -145,9 +145,88 @@ hipError_t sweep_launch(const void* buf, size_t bytes, uint32_t* sink, int waves
   return hipGetLastError();
 }
 
+// The decode partial kernel's chunk stream alone (kvq_probe_chunk_stream): a
+// chunk's loads (up to 8 direct 1 KB loads, listed by the host: source,
+// per-chunk stride, LDS offset, half-wave or full) go into one of two LDS
+// slots, the next chunk is requested before the current one is read back, and
+// spin dependent multiply-adds stand in for the arithmetic.  NI = loads per
+// chunk (vmcnt takes an immediate: the launch picks the instantiation).
+struct ChunkLoads {
+  const char* src[8];
+  int64_t stride[8];
+  uint32_t dst[8];
+  int32_t half[8];
+};
+
+template <int NI>
+__global__ __launch_bounds__(64) void chunk_stream_kernel(ChunkLoads cl, int64_t n_chunks,
+                                                          int spin, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) char ring[2][4096];
+  const int lane = threadIdx.x;
+  const uint32_t lane16 = 16u * lane;
+  const int64_t per = (n_chunks + gridDim.x - 1) / gridDim.x;
+  const int64_t c0 = (int64_t)blockIdx.x * per;
+  const int64_t c1 = c0 + per < n_chunks ? c0 + per : n_chunks;
+  auto issue = [&](int64_t c, int s) {
+    lds_dma_begin();
+    const uint32_t base = lds_addr(&ring[s][0]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(base + cl.dst[i]));
+      if (!cl.half[i] || lane < 32) lds_dma16<true>(cl.src[i] + c * cl.stride[i], d, lane16);
+    }
+  };
+  float x = (float)lane;
+  uint32_t acc = 0;
+  if (c0 < c1) issue(c0, 0);
+  for (int64_t c = c0; c < c1; ++c) {
+    const int s = (int)((c - c0) & 1);
+    if (c + 1 < c1) {
+      issue(c + 1, s ^ 1);
+      wait_vm<NI>();
+    } else {
+      wait_vm<0>();
+    }
+    acc ^= reinterpret_cast<const uint32_t*>(&ring[s][0])[lane];
+    for (int i = 0; i < spin; ++i) x = __builtin_fmaf(x, 0.999f, 0.5f);
+  }
+  wait_vm<0>();
+  acc ^= __builtin_bit_cast(uint32_t, x);
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  if (lane == 0) sink[blockIdx.x] = acc;
+}
+
 }  // namespace
 
 int probe_sink_words() { return kProbeBlocks * (kProbeThreads / 64); }
+
+hipError_t launch_chunk_stream(const void* const (&bufs)[4], int64_t n_chunks,
+                               const int32_t (&bytes)[4], int spin, int waves, uint32_t* sink,
+                               hipStream_t st) {
+  ChunkLoads cl{};
+  int ni = 0;
+  uint32_t dst = 0;
+  for (int p = 0; p < 4; ++p) {
+    for (int o = 0; o < bytes[p]; o += 1024) {
+      if (ni == 8) return hipErrorInvalidValue;
+      cl.src[ni] = static_cast<const char*>(bufs[p]) + o;
+      cl.stride[ni] = bytes[p];
+      cl.dst[ni] = dst + o;
+      cl.half[ni] = o + 1024 > bytes[p];  // a 512-byte rest: half the lanes
+      ++ni;
+    }
+    dst += bytes[p];
+  }
+  switch (ni) {
+#define KVQ_CHUNK_CASE(N) \
+    case N: chunk_stream_kernel<N><<<waves, 64, 0, st>>>(cl, n_chunks, spin, sink); break;
+    KVQ_CHUNK_CASE(1) KVQ_CHUNK_CASE(2) KVQ_CHUNK_CASE(3) KVQ_CHUNK_CASE(4)
+    KVQ_CHUNK_CASE(5) KVQ_CHUNK_CASE(6) KVQ_CHUNK_CASE(7) KVQ_CHUNK_CASE(8)
+#undef KVQ_CHUNK_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink, int waves,
                                     int loads, int mode, hipStream_t st) {

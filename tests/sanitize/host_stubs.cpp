@@ -48,5 +48,9 @@ hipError_t launch_stream_read(const void*, size_t, uint32_t*, hipStream_t) {
 hipError_t launch_stream_read_sweep(const void*, size_t, uint32_t*, int, int, int, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_chunk_stream(const void* const (&)[4], int64_t, const int32_t (&)[4], int, int,
+                               uint32_t*, hipStream_t) {
+  return hipErrorNoDevice;
+}
 
 }  // namespace kvq
