@@ -941,6 +941,15 @@ int kvq_probe_sink_words(int32_t* words) {
   return KVQ_OK;
 }
 
+extern "C++" {
+namespace kvq {
+// The chunk-stream probe's launcher (kvq_probe.hip).
+hipError_t launch_chunk_stream(const void* const (&bufs)[4], int64_t n_chunks,
+                               const int32_t (&bytes)[4], int spin, int waves, uint32_t* sink,
+                               hipStream_t st);
+}  // namespace kvq
+}
+
 int kvq_probe_chunk_stream(const void* buf_a, const void* buf_b, const void* buf_c,
                            const void* buf_d, int64_t n_chunks, int32_t bytes_a,
                            int32_t bytes_b, int32_t bytes_c, int32_t bytes_d, int32_t spin,

@@ -178,8 +178,5 @@ int probe_sink_words();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_stream_read_sweep(const void* buf, size_t bytes, uint32_t* sink, int waves,
                                     int loads, int mode, hipStream_t st);
-hipError_t launch_chunk_stream(const void* const (&bufs)[4], int64_t n_chunks,
-                               const int32_t (&bytes)[4], int spin, int waves, uint32_t* sink,
-                               hipStream_t st);
 
 }  // namespace kvq
