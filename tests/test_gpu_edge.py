@@ -466,6 +466,7 @@ MULTI = [
     (8, 2, 128, 2, 4, 32, 128, 4, [300, 257, 385, 131]),   # 16 rows per KV head
     (4, 2, 64, 4, 2, 64, 64, 4, [320, 129, 66, 200]),      # 8 rows
     (8, 4, 128, 8, 8, 32, 32, 2, [300, 33, 185, 64]),      # 4 rows, 8-bit
+    (8, 8, 128, 2, 2, 32, 64, 2, [300, 129, 66, 200]),     # MHA, 2 rows: split value columns
 ]
 
 

@@ -48,6 +48,10 @@ CASES = [
     (128, 4, 4, 32, 64, 16, 2, 2, [2, 65, 66, 97, 160]),
     (64, 2, 2, 64, 64, 2, 1, 8, [8, 64, 65, 70, 71, 72, 129]),
     (128, 8, 8, 32, 128, 8, 2, 4, [4, 131, 257, 300]),
+    # MHA with several query tokens: 2 or 4 rows per KV head, so the value
+    # weights' hi and lo parts take neighbouring MFMA columns
+    (128, 2, 4, 32, 128, 4, 4, 2, [2, 64, 129, 200]),
+    (128, 4, 2, 64, 64, 4, 4, 4, [4, 65, 130, 191]),
 ]
 
 
