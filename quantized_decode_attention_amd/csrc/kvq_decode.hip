@@ -24,6 +24,11 @@ template <int D, int GQ>
 hipError_t combine_rows(const DecodeLaunch& L, hipStream_t st) {
   if (L.g.B * L.g.Hkv < kCombineRowUnits && GQ > 1)
     decode_combine_kernel<KiviWork, D, GQ, 1><<<dim3(L.g.Hkv * GQ, L.g.B), kThreads, 0, st>>>(L);
+  else if constexpr (GQ * D > 4 * kThreads)  // more outputs than threads: groups of rows,
+    // two threads per output (16 rows at D = 128: four workgroups of four rows
+    // per unit; T = 4 partial + combine 95.7 -> 94.5 us on one box)
+    decode_combine_kernel<KiviWork, D, GQ, 2 * kThreads / D>
+        <<<dim3(L.g.Hkv * (GQ * D / (2 * kThreads)), L.g.B), kThreads, 0, st>>>(L);
   else
     decode_combine_kernel<KiviWork, D, GQ><<<dim3(L.g.Hkv, L.g.B), kThreads, 0, st>>>(L);
   return hipGetLastError();

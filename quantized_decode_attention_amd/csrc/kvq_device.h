@@ -577,7 +577,8 @@ __device__ __forceinline__ SegRange seg_range(const Launch& L, const SeqWork& sw
 }
 // One workgroup per RS rows of a (KV head, sequence) unit (RS = GQ: the whole
 // unit; RS = 1: one row, for launches with few units, where a unit's many
-// partials would otherwise be streamed by few workgroups); blockIdx.x =
+// partials would otherwise be streamed by few workgroups; in between for units
+// with more outputs than a workgroup has threads); blockIdx.x =
 // hkv * (GQ / RS) + row group.  Merges the unit's partials for those rows and
 // writes their outputs:
 //   M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
@@ -588,7 +589,7 @@ __device__ __forceinline__ SegRange seg_range(const Launch& L, const SeqWork& sw
 // then merged through LDS.  Empty partials (m = -inf) carry weight 0.
 template <class Fmt, int D, int GQ, int RS = GQ>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(typename Fmt::Launch L) {
-  static_assert(RS == GQ || RS == 1, "whole units or single rows");
+  static_assert(GQ % RS == 0, "whole row groups of a unit");
   constexpr int DP = D + kPartPad;
   constexpr int NO = RS * D / 4;                          // float4 outputs of the workgroup
   constexpr int P = NO >= kThreads ? 1 : kThreads / NO;   // partial shares per output
